@@ -1,0 +1,13 @@
+"""CPU oracle for the KLA forward path (float64).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call, link or execute anything
+under ``oracle/``. The library ``delta_rule_recurrence_kla_amd`` never touches
+it, and the two share no code.
+
+  kla_ref.py   plain NumPy token-by-token recurrence (the definition)
+  kla_ref.c    the same recurrence in plain C, OpenMP over heads
+  cref.py      ctypes loader for the C build
+  build.py     gcc build of kla_ref.c into oracle/libkla_ref.so
+"""
+from . import kla_ref  # noqa: F401
