@@ -1,0 +1,199 @@
+"""Python binding of libkla, the MI355X (gfx950) KLA forward hot path.
+
+Argument marshalling only: tensors are checked for dtype/shape/device, their
+device pointers and the current HIP stream are handed to the C ABI declared in
+include/kla.h, and a non-OK status raises RuntimeError with kla_last_error().
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback. PyTorch provides device memory and streams.
+
+    out, S = chunk_fwd(q, k, v, log_alpha, eta, eps, init_state=None)
+    out = decode_step(q, k, v, log_alpha, eta, state, eps)     # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = ["chunk_fwd", "decode_step", "plan", "version", "last_error", "timing_enable",
+           "timing_collect", "lib_path", "load", "KLAError", "PATHS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "libkla.so")
+_lib = None
+
+KLA_OK, KLA_ERR_INVALID_ARG, KLA_ERR_UNSUPPORTED, KLA_ERR_HIP, KLA_ERR_OOM = range(5)
+PATHS = {"auto": 0, "sequential": 1, "scan": 2}
+_PATH_NAMES = {v: k for k, v in PATHS.items()}
+_STATUS_NAMES = {0: "KLA_OK", 1: "KLA_ERR_INVALID_ARG", 2: "KLA_ERR_UNSUPPORTED", 3: "KLA_ERR_HIP", 4: "KLA_ERR_OOM"}
+
+
+class KLAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class KernelTiming(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkla.so (built in tree by delta_rule_recurrence_kla_amd.build). Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libkla.so is not built ({_LIB_PATH}); run "
+                           "`python -m delta_rule_recurrence_kla_amd.build` first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kla_chunk_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
+    lib.kla_chunk_fwd_f32.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
+    lib.kla_chunk_fwd_ex.argtypes = [I, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.kla_plan.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(S)]
+    lib.kla_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
+    lib.kla_decode_step_f32.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
+    for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_plan", "kla_decode_step",
+               "kla_decode_step_f32", "kla_timing_enable"):
+        getattr(lib, fn).restype = I
+    lib.kla_timing_enable.argtypes = [I]
+    lib.kla_timing_collect.argtypes = [ctypes.POINTER(KernelTiming), I]
+    lib.kla_timing_collect.restype = I
+    lib.kla_last_error.restype = ctypes.c_char_p
+    lib.kla_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().kla_last_error().decode()
+
+
+def version() -> str:
+    return load().kla_version().decode()
+
+
+def _check(status: int):
+    if status != KLA_OK:
+        raise KLAError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, shape, dtypes, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def chunk_fwd(q, k, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk: int = 64,
+              path: str = "auto", segments: int = 0, out=None, final_state=None,
+              want_final: bool = True, stream=None) -> Tuple[object, Optional[object]]:
+    """Chunkwise KLA prefill. q, k [B,T,H,dk] and v [B,T,H,dv] in bf16 (or all fp32);
+    log_alpha, eta fp32 [B,T,H]; init_state fp32 [B,H,dk,dv] or None.
+    Returns (out fp32 [B,T,H,dv], final_state fp32 [B,H,dk,dv] or None)."""
+    import torch
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype == torch.bfloat16:
+        dtype = 0
+    elif q.dtype == torch.float32:
+        dtype = 1
+    else:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    _need(q, "q", (B, T, H, dk), (q.dtype,), dev)
+    _need(k, "k", (B, T, H, dk), (q.dtype,), dev)
+    _need(v, "v", (B, T, H, dv), (q.dtype,), dev)
+    _need(log_alpha, "log_alpha", (B, T, H), (torch.float32,), dev)
+    _need(eta, "eta", (B, T, H), (torch.float32,), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (B, H, dk, dv), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, T, H, dv), (torch.float32,), dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (B, H, dk, dv), (torch.float32,), dev)
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    st = lib.kla_chunk_fwd_ex(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(eta), float(eps),
+                              _ptr(init_state), _ptr(out), _ptr(final_state), B, T, H, dk, dv, chunk,
+                              PATHS[path], int(segments), _stream(stream))
+    _check(st)
+    return out, final_state
+
+
+def decode_step(q, k, v, log_alpha, eta, state, eps: float = 1e-6, out=None, stream=None):
+    """One decode step for N x H states (updated in place). q, k [N,H,dk], v [N,H,dv] in bf16
+    (or all fp32); log_alpha, eta fp32 [N,H]; state fp32 [N,H,dk,dv]. Returns out fp32 [N,H,dv]."""
+    import torch
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype == torch.bfloat16:
+        fn = lib.kla_decode_step
+    elif q.dtype == torch.float32:
+        fn = lib.kla_decode_step_f32
+    else:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    _need(k, "k", (N, H, dk), (q.dtype,), dev)
+    _need(v, "v", (N, H, dv), (q.dtype,), dev)
+    _need(q, "q", (N, H, dk), (q.dtype,), dev)
+    _need(log_alpha, "log_alpha", (N, H), (torch.float32,), dev)
+    _need(eta, "eta", (N, H), (torch.float32,), dev)
+    _need(state, "state", (N, H, dk, dv), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    _need(out, "out", (N, H, dv), (torch.float32,), dev)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(eta), float(eps), _ptr(state), _ptr(out),
+              N, H, dk, dv, _stream(stream)))
+    return out
+
+
+def plan(B: int, T: int, H: int, dk: int, dv: int, chunk: int = 64, path: str = "auto",
+         segments: int = 0, num_cus: int = 256):
+    """Host-only: (path name, segments, workspace bytes) the library would use."""
+    lib = load()
+    p, s, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _check(lib.kla_plan(B, T, H, dk, dv, chunk, PATHS[path], segments, num_cus,
+                        ctypes.byref(p), ctypes.byref(s), ctypes.byref(w)))
+    return _PATH_NAMES[p.value], s.value, w.value
+
+
+def timing_enable(enable: bool = True):
+    _check(load().kla_timing_enable(1 if enable else 0))
+
+
+def timing_collect(max_kernels: int = 16):
+    """{kernel name: (launches, total ms)} for launches timed since the last collect."""
+    arr = (KernelTiming * max_kernels)()
+    n = load().kla_timing_collect(arr, max_kernels)
+    if n < 0:
+        raise KLAError(KLA_ERR_HIP, last_error())
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(min(n, max_kernels))}

@@ -1,0 +1,367 @@
+// libkla host side: the C ABI declared in include/kla.h.
+//
+// Every entry point validates its arguments before any HIP call, plans the
+// launch, takes a stream-ordered workspace when it needs one, enqueues the
+// kernels on the caller's stream and returns. No exception crosses the ABI.
+#include "kla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kla_launch.h"
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int kRecBytes = 33280;  // per-chunk record of the prep kernel (kla_device.h)
+constexpr int kMaxGridYZ = 65535;
+
+thread_local std::string g_err;
+
+kla_status fail(kla_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+// ---------------------------------------------------------------------------
+// timing hook
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct TimingState {
+  bool enabled = false;
+  std::vector<TimedLaunch> rec;
+};
+thread_local TimingState g_timing;
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
+  if (!g_timing.enabled) return launch();
+  TimedLaunch t{name, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&t.start);
+  if (e == hipSuccess) e = hipEventCreate(&t.stop);
+  if (e == hipSuccess) e = hipEventRecord(t.start, stream);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(t.stop, stream);
+  if (e == hipSuccess) g_timing.rec.push_back(t);
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// device bookkeeping: keep freed workspace in the stream-ordered pool between calls
+std::once_flag g_pool_once[64];
+
+void keep_pool_warm() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  std::call_once(g_pool_once[dev], [dev] {
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+      uint64_t thr = UINT64_MAX;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+  });
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// ---------------------------------------------------------------------------
+// validation and planning
+bool supported_dk(int dk) { return dk == 64 || dk == 128 || dk == 256; }
+bool supported_dv(int dv) { return dv == 64 || dv == 128; }
+
+kla_status check_prefill_sizes(kla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk) {
+  if (dtype != KLA_DTYPE_BF16 && dtype != KLA_DTYPE_F32) return fail(KLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 1 || H < 1 || T < 0) return fail(KLA_ERR_INVALID_ARG, "sizes must satisfy B >= 1, H >= 1, T >= 0 (got B=%d T=%d H=%d)", B, T, H);
+  if (dk < 1 || dv < 1 || chunk < 1) return fail(KLA_ERR_INVALID_ARG, "dk, dv and chunk must be positive");
+  if (!supported_dk(dk)) return fail(KLA_ERR_UNSUPPORTED, "dk=%d not supported (64, 128, 256)", dk);
+  if (!supported_dv(dv)) return fail(KLA_ERR_UNSUPPORTED, "dv=%d not supported (64, 128)", dv);
+  if (chunk != kChunk) return fail(KLA_ERR_UNSUPPORTED, "chunk=%d not supported (64)", chunk);
+  if (dtype == KLA_DTYPE_F32 && dk > 128) return fail(KLA_ERR_UNSUPPORTED, "fp32 prefill supports dk <= 128 (got %d)", dk);
+  if (static_cast<long long>(B) * H > kMaxGridYZ) return fail(KLA_ERR_UNSUPPORTED, "B*H=%lld exceeds %d", static_cast<long long>(B) * H, kMaxGridYZ);
+  return KLA_OK;
+}
+
+struct Plan {
+  kla_path path;
+  int segs;        // scan segments (1 for sequential)
+  int seg_chunks;  // chunks per segment
+  size_t rec_off, rec_bytes, maps_off, maps_bytes, starts_off, starts_bytes, total;
+};
+
+Plan make_plan(int B, int T, int H, int dk, int dv, kla_path path, int segments, int cus) {
+  Plan p{};
+  const int nc = (T + kChunk - 1) / kChunk;
+  const long long bh = static_cast<long long>(B) * H;
+  const long long seq_wgs = bh * (dv / 64);
+  kla_path chosen = path;
+  int segs = 1;
+  if (nc >= 2 && path != KLA_PATH_SEQUENTIAL) {
+    // cost in chunk steps: rounds of workgroups (one per CU) times chunks per walk
+    auto rounds = [cus](long long wgs) { return (wgs + cus - 1) / cus; };
+    const double seq_cost = static_cast<double>(rounds(seq_wgs)) * nc;
+    double best = 1e300;
+    int best_g = 1;
+    const int gmax = std::min(nc, 256);
+    for (int g = 2; g <= gmax; ++g) {
+      const int L = (nc + g - 1) / g;
+      const int G = (nc + L - 1) / L;
+      if (G < 2) continue;
+      const long long wg1 = bh * (G - 1) * ((dk + dv) / 64);
+      const long long wg3 = bh * G * (dv / 64);
+      // a map walk skips the output products (about 0.6 of an output walk), plus the serial fold
+      const double cost = 0.6 * rounds(wg1) * L + rounds(wg3) * L + 0.25 * G;
+      if (cost < best) {
+        best = cost;
+        best_g = G;
+      }
+    }
+    if (path == KLA_PATH_SCAN) {
+      segs = segments > 0 ? std::min(segments, nc) : best_g;
+      chosen = KLA_PATH_SCAN;
+    } else if (best_g >= 2 && best < 0.8 * seq_cost) {
+      segs = best_g;
+      chosen = KLA_PATH_SCAN;
+    } else {
+      chosen = KLA_PATH_SEQUENTIAL;
+    }
+  } else {
+    chosen = KLA_PATH_SEQUENTIAL;
+  }
+  int seg_chunks = nc;
+  if (chosen == KLA_PATH_SCAN) {
+    segs = std::max(segs, 1);
+    seg_chunks = (nc + segs - 1) / segs;
+    segs = (nc + seg_chunks - 1) / seg_chunks;  // no empty segment
+    if (segs < 2) {
+      chosen = KLA_PATH_SEQUENTIAL;
+      segs = 1;
+      seg_chunks = nc;
+    }
+  }
+  p.path = chosen;
+  p.segs = segs;
+  p.seg_chunks = seg_chunks;
+  p.rec_off = 0;
+  p.rec_bytes = align256(static_cast<size_t>(bh) * nc * kRecBytes);
+  p.maps_off = p.rec_off + p.rec_bytes;
+  p.maps_bytes = chosen == KLA_PATH_SCAN ? align256(static_cast<size_t>(bh) * (segs - 1) * dk * (dk + dv) * 4) : 0;
+  p.starts_off = p.maps_off + p.maps_bytes;
+  p.starts_bytes = chosen == KLA_PATH_SCAN ? align256(static_cast<size_t>(bh) * segs * dk * dv * 4) : 0;
+  p.total = p.starts_off + p.starts_bytes;
+  return p;
+}
+
+kla_status hip_fail(hipError_t e, const char* what) {
+  return fail(KLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+kla_status chunk_fwd_impl(kla_dtype dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* eta, float eps, const float* init_state, float* out, float* final_state,
+                          int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
+                          hipStream_t stream) {
+  kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
+  if (st != KLA_OK) return st;
+  if (path != KLA_PATH_AUTO && path != KLA_PATH_SEQUENTIAL && path != KLA_PATH_SCAN)
+    return fail(KLA_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (segments < 0) return fail(KLA_ERR_INVALID_ARG, "segments must be >= 0");
+  if (T > 0 && (!q || !k || !v || !log_alpha || !eta || !out))
+    return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta and out must be non-null when T > 0");
+  const size_t state_n = static_cast<size_t>(B) * H * dk * dv;
+
+  if (T == 0) {
+    if (final_state && final_state != init_state) {
+      hipError_t e = timed("kla_copy_or_zero", stream, [&] { return kla::launch_copy_or_zero(init_state, final_state, state_n, stream); });
+      if (e != hipSuccess) return hip_fail(e, "launch");
+    }
+    return KLA_OK;
+  }
+
+  if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
+    if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
+  }
+
+  const Plan p = make_plan(B, T, H, dk, dv, path, segments, device_cus());
+  const kla::Dims d{B, T, H, dk, dv, (T + kChunk - 1) / kChunk};
+  const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
+
+  keep_pool_warm();
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, p.total, stream);
+  if (e != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return fail(KLA_ERR_OOM, "hipMallocAsync(%zu bytes) failed: %s", p.total, hipGetErrorString(e));
+  }
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* rec = base + p.rec_off;
+  float* maps = reinterpret_cast<float*>(base + p.maps_off);
+  float* starts = reinterpret_cast<float*>(base + p.starts_off);
+
+  e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, rec, stream); });
+  if (e == hipSuccess) {
+    if (p.path == KLA_PATH_SEQUENTIAL) {
+      e = timed("kla_state_seq", stream, [&] {
+        return kla::launch_state_seq(mode, d, q, k, v, rec, init_state, out, final_state, stream);
+      });
+    } else {
+      e = timed("kla_scan_maps", stream, [&] {
+        return kla::launch_scan_maps(mode, d, k, v, rec, p.seg_chunks, p.segs, maps, stream);
+      });
+      if (e == hipSuccess)
+        e = timed("kla_scan_starts", stream, [&] { return kla::launch_scan_starts(d, maps, init_state, p.segs, starts, stream); });
+      if (e == hipSuccess)
+        e = timed("kla_scan_apply", stream, [&] {
+          return kla::launch_scan_apply(mode, d, q, k, v, rec, p.seg_chunks, p.segs, starts, out, final_state, stream);
+        });
+    }
+  }
+  hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
+  return KLA_OK;
+}
+
+kla_status decode_impl(kla_dtype dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* eta, float eps, float* state, float* out, int N, int H, int dk, int dv,
+                       hipStream_t stream) {
+  if (dtype != KLA_DTYPE_BF16 && dtype != KLA_DTYPE_F32) return fail(KLA_ERR_INVALID_ARG, "unknown dtype");
+  if (N < 0 || H < 1) return fail(KLA_ERR_INVALID_ARG, "sizes must satisfy N >= 0, H >= 1 (got N=%d H=%d)", N, H);
+  if (dk < 1 || dv < 1) return fail(KLA_ERR_INVALID_ARG, "dk and dv must be positive");
+  if (!supported_dk(dk)) return fail(KLA_ERR_UNSUPPORTED, "dk=%d not supported (64, 128, 256)", dk);
+  if (!supported_dv(dv)) return fail(KLA_ERR_UNSUPPORTED, "dv=%d not supported (64, 128)", dv);
+  if (static_cast<long long>(N) * H > 2147483647LL) return fail(KLA_ERR_UNSUPPORTED, "N*H too large");
+  if (N == 0) return KLA_OK;
+  if (!q || !k || !v || !log_alpha || !eta || !state || !out)
+    return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta, state and out must be non-null");
+  const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
+  hipError_t e = timed("kla_decode", stream, [&] {
+    return kla::launch_decode(mode, N, H, dk, dv, q, k, v, log_alpha, eta, eps, state, out, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return KLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kla_status kla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* eta,
+                         float eps, const float* init_state, float* out, float* final_state, int B, int T, int H,
+                         int dk, int dv, int chunk, hipStream_t stream) {
+  return chunk_fwd_impl(KLA_DTYPE_BF16, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv,
+                        chunk, KLA_PATH_AUTO, 0, stream);
+}
+
+kla_status kla_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* log_alpha,
+                             const float* eta, float eps, const float* init_state, float* out, float* final_state,
+                             int B, int T, int H, int dk, int dv, int chunk, hipStream_t stream) {
+  return chunk_fwd_impl(KLA_DTYPE_F32, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv,
+                        chunk, KLA_PATH_AUTO, 0, stream);
+}
+
+kla_status kla_chunk_fwd_ex(kla_dtype dtype, const void* q, const void* k, const void* v, const float* log_alpha,
+                            const float* eta, float eps, const float* init_state, float* out, float* final_state,
+                            int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
+                            hipStream_t stream) {
+  return chunk_fwd_impl(dtype, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv, chunk,
+                        path, segments, stream);
+}
+
+kla_status kla_plan(int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments, int num_cus,
+                    kla_path* chosen_path, int* chosen_segments, size_t* workspace_bytes) {
+  kla_status st = check_prefill_sizes(KLA_DTYPE_BF16, B, T, H, dk, dv, chunk);
+  if (st != KLA_OK) return st;
+  if (path != KLA_PATH_AUTO && path != KLA_PATH_SEQUENTIAL && path != KLA_PATH_SCAN)
+    return fail(KLA_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (segments < 0) return fail(KLA_ERR_INVALID_ARG, "segments must be >= 0");
+  const int cus = num_cus > 0 ? num_cus : device_cus();
+  Plan p{};
+  if (T > 0) p = make_plan(B, T, H, dk, dv, path, segments, cus);
+  else p.path = KLA_PATH_SEQUENTIAL, p.segs = 1;
+  if (chosen_path) *chosen_path = p.path;
+  if (chosen_segments) *chosen_segments = p.segs;
+  if (workspace_bytes) *workspace_bytes = p.total;
+  return KLA_OK;
+}
+
+kla_status kla_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const float* eta,
+                           float eps, float* state, float* out, int N, int H, int dk, int dv, hipStream_t stream) {
+  return decode_impl(KLA_DTYPE_BF16, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
+}
+
+kla_status kla_decode_step_f32(const float* q, const float* k, const float* v, const float* log_alpha,
+                               const float* eta, float eps, float* state, float* out, int N, int H, int dk, int dv,
+                               hipStream_t stream) {
+  return decode_impl(KLA_DTYPE_F32, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
+}
+
+const char* kla_last_error(void) { return g_err.c_str(); }
+
+const char* kla_version(void) { return "kla-mi355x 0.1.0 (gfx950)"; }
+
+kla_status kla_timing_enable(int enable) {
+  g_timing.enabled = enable != 0;
+  return KLA_OK;
+}
+
+int kla_timing_collect(kla_kernel_timing* out, int max) {
+  struct Acc {
+    const char* name;
+    int n;
+    double ms;
+  };
+  std::vector<Acc> acc;
+  bool err = false;
+  for (auto& t : g_timing.rec) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) {
+      err = true;
+    } else {
+      auto it = std::find_if(acc.begin(), acc.end(), [&](const Acc& a) { return std::strcmp(a.name, t.name) == 0; });
+      if (it == acc.end()) acc.push_back({t.name, 1, ms});
+      else {
+        it->n += 1;
+        it->ms += ms;
+      }
+    }
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_timing.rec.clear();
+  if (err) {
+    fail(KLA_ERR_HIP, "timing events could not be read");
+    return -1;
+  }
+  for (int i = 0; i < static_cast<int>(acc.size()) && i < max && out; ++i) {
+    std::snprintf(out[i].name, sizeof out[i].name, "%s", acc[i].name);
+    out[i].launches = acc[i].n;
+    out[i].total_ms = acc[i].ms;
+  }
+  return static_cast<int>(acc.size());
+}
+
+}  // extern "C"

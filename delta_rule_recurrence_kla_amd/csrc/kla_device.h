@@ -1,0 +1,190 @@
+// Device-side building blocks shared by the KLA kernels (gfx950 / CDNA4).
+//
+// Matrix products run on the 16x16 MFMA tiles of one 64-lane wavefront:
+//   bf16 mode: v_mfma_f32_16x16x32_bf16 (fp32 accumulate)
+//   fp32 mode: v_mfma_f32_16x16x4_f32
+// Lane l of a wave is split into a column index ln = l % 16 and a lane group
+// gq = l / 16. A 16x16 accumulator tile holds D[4*gq + i][ln], i = 0..3.
+//
+// Contraction order. A 32-wide contraction block is consumed by lane group gq
+// as 8 values whose contraction indices are kslot(gq, j):
+//     j = 0..3  ->  4*gq + j
+//     j = 4..7  -> 16 + 4*gq + (j - 4)
+// These are exactly the rows that two stacked 16x16 accumulator tiles hold in a
+// lane, so the result of one product (rows = contraction index of the next
+// product) feeds the next product's B operand straight from registers, with no
+// LDS round trip. Operands read from LDS use the same order. The sum is the
+// same for any order in which both operands agree.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int MODE_BF16 = 0;  // q, k, v in bf16; derived operands split into hi + lo bf16
+constexpr int MODE_F32 = 1;   // q, k, v in fp32; fp32 MFMA throughout
+
+constexpr int CHUNK = 64;     // tokens per chunk
+
+// Per-chunk record written by the prep kernel and read by the state kernels.
+//   [0, 16384)      T' = (I + A)^-1 diag(beta): 64 rows of 256 bytes
+//   [16384, 32768)  P  = (Q K^T) masked by the inclusive decay mask: 64 rows of 256 bytes
+//   [32768, 33024)  exp(g_r), 64 floats (g = chunk-local inclusive cumsum of log alpha)
+//   [33024, 33280)  exp(g_C - g_r), 64 floats
+// A 256-byte row holds 64 fp32 values (fp32 mode) or 64 hi bf16 then 64 lo bf16 (bf16 mode).
+constexpr int REC_T_OFF = 0;
+constexpr int REC_P_OFF = 16384;
+constexpr int REC_EG_OFF = 32768;
+constexpr int REC_EGC_OFF = 33024;
+constexpr int REC_BYTES = 33280;
+
+// LDS row pitch of a derived 64x64 matrix: 256 bytes of data + 16 bytes of padding.
+constexpr int DROW_BYTES = 272;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ int kslot(int gq, int j) {
+  return j < 4 ? 4 * gq + j : 12 + 4 * gq + j;
+}
+
+struct F8 {
+  float v[8];
+};
+
+struct S8 {  // hi + lo bf16 split of 8 fp32 values
+  bf16x8 h, l;
+};
+
+__device__ __forceinline__ F8 frag_from_acc(const f32x4& a, const f32x4& b) {
+  F8 r;
+  r.v[0] = a[0]; r.v[1] = a[1]; r.v[2] = a[2]; r.v[3] = a[3];
+  r.v[4] = b[0]; r.v[5] = b[1]; r.v[6] = b[2]; r.v[7] = b[3];
+  return r;
+}
+
+__device__ __forceinline__ S8 split8(const F8& x) {
+  S8 s;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    __bf16 h = static_cast<__bf16>(x.v[j]);  // round to nearest even
+    s.h[j] = h;
+    s.l[j] = static_cast<__bf16>(x.v[j] - static_cast<float>(h));  // exact residual, rounded
+  }
+  return s;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// Mode traits: storage type of q/k/v and the three kinds of product
+//   xx: exact input x exact input
+//   xd: exact input x derived (fp32 value carried as hi + lo in bf16 mode)
+//   dd: derived x derived
+// ---------------------------------------------------------------------------
+template <int MODE>
+struct Tr;
+
+template <>
+struct Tr<MODE_BF16> {
+  using in_t = uint16_t;  // bf16 bit pattern
+  using XF = bf16x8;      // exact operand fragment
+  using DF = S8;          // derived operand fragment
+
+  // Exact operand from a row-major LDS matrix with pitch `ld` elements:
+  // row = row0 + ln, contraction columns k0 + kslot(gq, 0..7).
+  static __device__ __forceinline__ XF ldx(const in_t* base, int ld, int row0, int k0, int lane) {
+    const in_t* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    uint2 a = *reinterpret_cast<const uint2*>(p);
+    uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+    union {
+      uint4 u;
+      bf16x8 v;
+    } cv;
+    cv.u = make_uint4(a.x, a.y, b.x, b.y);
+    return cv.v;
+  }
+  // Derived operand from a 64x64 matrix stored with DROW_BYTES rows (hi at byte 0, lo at byte 128).
+  static __device__ __forceinline__ DF ldd(const uint8_t* base, int row0, int k0, int lane) {
+    const uint8_t* p = base + (row0 + (lane & 15)) * DROW_BYTES + 2 * (k0 + 4 * (lane >> 4));
+    uint2 a = *reinterpret_cast<const uint2*>(p);
+    uint2 b = *reinterpret_cast<const uint2*>(p + 32);
+    uint2 c = *reinterpret_cast<const uint2*>(p + 128);
+    uint2 d = *reinterpret_cast<const uint2*>(p + 160);
+    union {
+      uint4 u;
+      bf16x8 v;
+    } h, l;
+    h.u = make_uint4(a.x, a.y, b.x, b.y);
+    l.u = make_uint4(c.x, c.y, d.x, d.y);
+    DF r;
+    r.h = h.v;
+    r.l = l.v;
+    return r;
+  }
+  static __device__ __forceinline__ DF mk(const F8& x) { return split8(x); }
+  static __device__ __forceinline__ f32x4 mma_xx(f32x4 c, const XF& a, const XF& b) {
+    return mfma_bf16(a, b, c);
+  }
+  static __device__ __forceinline__ f32x4 mma_xd(f32x4 c, const XF& a, const DF& b) {
+    c = mfma_bf16(a, b.h, c);
+    return mfma_bf16(a, b.l, c);
+  }
+  static __device__ __forceinline__ f32x4 mma_dd(f32x4 c, const DF& a, const DF& b) {
+    c = mfma_bf16(a.h, b.h, c);
+    c = mfma_bf16(a.h, b.l, c);
+    return mfma_bf16(a.l, b.h, c);
+  }
+  static __device__ __forceinline__ float to_f32(in_t x) { return bf16_bits_to_f32(x); }
+};
+
+template <>
+struct Tr<MODE_F32> {
+  using in_t = float;
+  using XF = F8;
+  using DF = F8;
+
+  static __device__ __forceinline__ XF ldx(const in_t* base, int ld, int row0, int k0, int lane) {
+    const in_t* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 16);
+    F8 r;
+    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+    r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+    return r;
+  }
+  static __device__ __forceinline__ DF ldd(const uint8_t* base, int row0, int k0, int lane) {
+    const float* p = reinterpret_cast<const float*>(base + (row0 + (lane & 15)) * DROW_BYTES) + k0 +
+                     4 * (lane >> 4);
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 16);
+    F8 r;
+    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+    r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+    return r;
+  }
+  static __device__ __forceinline__ DF mk(const F8& x) { return x; }
+  static __device__ __forceinline__ f32x4 mma8(f32x4 c, const F8& a, const F8& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ f32x4 mma_xx(f32x4 c, const XF& a, const XF& b) { return mma8(c, a, b); }
+  static __device__ __forceinline__ f32x4 mma_xd(f32x4 c, const XF& a, const DF& b) { return mma8(c, a, b); }
+  static __device__ __forceinline__ f32x4 mma_dd(f32x4 c, const DF& a, const DF& b) { return mma8(c, a, b); }
+  static __device__ __forceinline__ float to_f32(in_t x) { return x; }
+};
+
+}  // namespace kla

@@ -1,0 +1,46 @@
+// Host-side launchers of the KLA kernels (internal to libkla; not part of the C ABI).
+// Every launcher only enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kla {
+
+// Per-launch size bundle shared by the prefill kernels.
+struct Dims {
+  int B, T, H, dk, dv;
+  int nc;  // number of 64-token chunks, ceil(T / 64)
+};
+
+// Chunk prep: one workgroup per (b, h, chunk); writes one record per chunk.
+hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
+                       const float* eta, float eps, uint8_t* rec, hipStream_t stream);
+
+// Sequential inter-chunk state + output: one workgroup per (b, h, 64-column group of dv).
+// init may be null (zero state); fin may be null (not written).
+hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* k, const void* v,
+                            const uint8_t* rec, const float* init, float* out, float* fin,
+                            hipStream_t stream);
+
+// Scan path.
+//  phase 1: affine map [M | N] of each of the first `segs - 1` segments of `seg_chunks` chunks
+//  phase 2: start state of every segment, sequentially over segments
+//  phase 3: state + output inside every segment from its start state
+hipError_t launch_scan_maps(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
+                            int seg_chunks, int segs, float* maps, hipStream_t stream);
+hipError_t launch_scan_starts(const Dims& d, const float* maps, const float* init, int segs,
+                              float* starts, hipStream_t stream);
+hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void* k, const void* v,
+                             const uint8_t* rec, int seg_chunks, int segs, const float* starts,
+                             float* out, float* fin, hipStream_t stream);
+
+// Copy (or zero when src is null) n floats; used for T == 0 and as a graph-safe fill.
+hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);
+
+// Single-token decode for N x H states, in place.
+hipError_t launch_decode(int mode, int N, int H, int dk, int dv, const void* q, const void* k,
+                         const void* v, const float* log_alpha, const float* eta, float eps,
+                         float* state, float* out, hipStream_t stream);
+
+}  // namespace kla

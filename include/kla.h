@@ -1,0 +1,161 @@
+/*
+ * kla.h - C ABI of libkla: the forward hot path of Kaczmarz Linear Attention
+ * (KLA) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (KLA page, "KLA update rule"; decay gate kept from Gated
+ * DeltaNet, KLA page "Implementation"), for every batch b, head h and token t,
+ * with a dk x dv fp32 state S per (b, h):
+ *
+ *     beta_t = eta_t / (||k_t||^2 + eps)        Kaczmarz step size
+ *     S~     = exp(log_alpha_t) * S_{t-1}       decayed previous state
+ *     e_t    = v_t - S~^T k_t                   residual
+ *     S_t    = S~ + beta_t k_t e_t^T            the write: for eta_t = 1, eps = 0 it is the
+ *                                               orthogonal projection of S~ onto S^T k_t = v_t
+ *                                               (KLA page, "Theoretical derivation")
+ *     o_t    = S_t^T q_t                        readout after the write, no query scaling
+ *
+ * The pages do not state the readout or where the decay applies; the reading
+ * above is the one this library implements. If ||k_t||^2 + eps == 0 the write is
+ * skipped (beta_t = 0).
+ *
+ * Conventions shared by every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller. The library
+ *    never keeps a pointer after the call returns.
+ *  - Layouts are dense and row-major: q, k [B,T,H,dk]; v [B,T,H,dv];
+ *    log_alpha, eta [B,T,H]; states [B,H,dk,dv] with dv fastest;
+ *    out [B,T,H,dv]. bf16 arrays are IEEE bfloat16 bit patterns.
+ *  - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *    without waiting. Faults during execution surface at the caller's next
+ *    synchronisation.
+ *  - Arguments are validated before anything is enqueued; on any non-OK return
+ *    nothing has been enqueued except as stated for KLA_ERR_HIP, and
+ *    kla_last_error() describes the problem. Nothing aborts or throws.
+ *  - Supported sizes: dk in {64, 128, 256}, dv in {64, 128}, chunk == 64.
+ *    The fp32 prefill entry points support dk in {64, 128}. Other sizes give
+ *    KLA_ERR_UNSUPPORTED. T need not be a multiple of the chunk.
+ *  - Calls on different streams may run concurrently; the library holds no
+ *    mutable global state apart from the per-thread error text and the
+ *    per-thread timing record.
+ */
+#ifndef KLA_H_
+#define KLA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KLA_OK = 0,
+  KLA_ERR_INVALID_ARG = 1, /* null pointer, negative size, ... */
+  KLA_ERR_UNSUPPORTED = 2, /* valid but not implemented (dk, dv, chunk, dtype) */
+  KLA_ERR_HIP = 3,         /* a HIP call failed (launch, event, ...) */
+  KLA_ERR_OOM = 4          /* the stream-ordered workspace allocation failed */
+} kla_status;
+
+typedef enum { KLA_DTYPE_BF16 = 0, KLA_DTYPE_F32 = 1 } kla_dtype;
+
+typedef enum {
+  KLA_PATH_AUTO = 0,       /* let the library choose */
+  KLA_PATH_SEQUENTIAL = 1, /* one walk over all chunks per (b, h, 64 dv columns) */
+  KLA_PATH_SCAN = 2        /* segments composed by an associative scan over affine chunk maps */
+} kla_path;
+
+/*
+ * Chunkwise-parallel prefill (the chunkwise solver of Gated DeltaNet with
+ * B = Diag(beta_1..beta_C), KLA page "Implementation"; inter-chunk propagation
+ * optionally by associative scan, KATA page section 2.3 and HLA page section 4).
+ * Computes out and the end state of the recurrence above over T tokens.
+ *
+ *   q, k, v        bf16 device arrays, layouts above
+ *   log_alpha, eta fp32 device arrays [B,T,H]; alpha_t = exp(log_alpha_t)
+ *   eps            fp32 stabiliser added to ||k_t||^2
+ *   init_state     fp32 [B,H,dk,dv], or NULL for a zero start state
+ *   out            fp32 [B,T,H,dv] (required unless T == 0)
+ *   final_state    fp32 [B,H,dk,dv], or NULL to skip; may alias init_state
+ *   B, T, H        sizes (B, H >= 1; T >= 0); dk, dv, chunk as supported
+ * The workspace (about 33 KB per chunk per head) is taken from the device's
+ * stream-ordered pool on `stream` and released on it before return.
+ * With T == 0, final_state receives init_state (or zeros) and out is untouched.
+ */
+kla_status kla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* eta, float eps, const float* init_state, float* out,
+                         float* final_state, int B, int T, int H, int dk, int dv, int chunk,
+                         hipStream_t stream);
+
+/* Same as kla_chunk_fwd with fp32 q, k, v; all products in fp32 (dk in {64, 128}). */
+kla_status kla_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* log_alpha,
+                             const float* eta, float eps, const float* init_state, float* out,
+                             float* final_state, int B, int T, int H, int dk, int dv, int chunk,
+                             hipStream_t stream);
+
+/*
+ * kla_chunk_fwd with the input dtype and the inter-chunk path chosen by the
+ * caller. `segments` is the number of scan segments for KLA_PATH_SCAN
+ * (0 = library choice; clamped to the number of chunks); ignored otherwise.
+ * Results of both paths agree to rounding.
+ */
+kla_status kla_chunk_fwd_ex(kla_dtype dtype, const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* eta, float eps,
+                            const float* init_state, float* out, float* final_state, int B, int T,
+                            int H, int dk, int dv, int chunk, kla_path path, int segments,
+                            hipStream_t stream);
+
+/*
+ * Host-only planning query: which path and segment count kla_chunk_fwd_ex would
+ * use for these sizes, and the workspace bytes it would allocate. `num_cus` is
+ * the compute-unit count to plan for (0 = ask the current HIP device, 256 if
+ * there is none). Makes no allocation and enqueues nothing.
+ */
+kla_status kla_plan(int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
+                    int num_cus, kla_path* chosen_path, int* chosen_segments,
+                    size_t* workspace_bytes);
+
+/*
+ * One recurrent decode step for N x H states, updated in place (KLA page,
+ * "KLA update rule", one token; the state keeps a constant size per head).
+ *   q, k   bf16 [N,H,dk];  v bf16 [N,H,dv]
+ *   log_alpha, eta  fp32 [N,H]
+ *   state  fp32 [N,H,dk,dv], read and overwritten with S_t
+ *   out    fp32 [N,H,dv], o_t = S_t^T q_t
+ * Needs no workspace.
+ */
+kla_status kla_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* eta, float eps, float* state, float* out, int N, int H,
+                           int dk, int dv, hipStream_t stream);
+
+/* Same as kla_decode_step with fp32 q, k, v. */
+kla_status kla_decode_step_f32(const float* q, const float* k, const float* v,
+                               const float* log_alpha, const float* eta, float eps, float* state,
+                               float* out, int N, int H, int dk, int dv, hipStream_t stream);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char* kla_last_error(void);
+
+/* Library version string. */
+const char* kla_version(void);
+
+/*
+ * Measurement hook. While enabled on the calling thread, every kernel the
+ * library enqueues from that thread is bracketed by a pair of HIP events on
+ * the same stream. kla_timing_collect waits for those events, writes up to
+ * `max` per-kernel totals (name, launches, summed milliseconds) and clears the
+ * record; it returns the number of distinct kernels recorded, or -1 on a HIP
+ * error. Timing adds two event records per launch and is off by default.
+ */
+typedef struct {
+  char name[32];
+  int launches;
+  double total_ms;
+} kla_kernel_timing;
+
+kla_status kla_timing_enable(int enable);
+int kla_timing_collect(kla_kernel_timing* out, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KLA_H_ */

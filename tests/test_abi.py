@@ -1,0 +1,116 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/kla.h declares, rejects bad arguments before touching HIP, and
+plans paths and workspaces as documented. No call here reaches a kernel."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kla.h")
+
+kla = pytest.importorskip("delta_rule_recurrence_kla_amd")
+if not os.path.exists(kla.lib_path()):
+    pytest.skip("libkla.so not built", allow_module_level=True)
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_decode_step",
+              "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
+              "kla_timing_enable", "kla_timing_collect"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kla.load()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kla.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (kla_\w+)$", out, flags=re.M))
+    assert set(_declared_functions()) <= exported
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in kla.version()
+    assert isinstance(kla.last_error(), str)
+
+
+def _chunk(lib, dtype=0, q=FAKE, out=FAKE, B=1, T=64, H=1, dk=64, dv=64, chunk=64, path=0, segs=0):
+    return lib.kla_chunk_fwd_ex(dtype, q, FAKE, FAKE, FAKE, FAKE, 1e-6, None, out, None,
+                                B, T, H, dk, dv, chunk, path, segs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1), (dict(q=None), 1), (dict(out=None), 1),
+    (dict(dk=96), 2), (dict(dv=256), 2), (dict(chunk=32), 2), (dict(dtype=7), 1),
+    (dict(dtype=1, dk=256), 2), (dict(path=5), 1), (dict(segs=-1), 1), (dict(B=70000, H=1), 2),
+])
+def test_prefill_validation(kw, status):
+    lib = kla.load()
+    assert _chunk(lib, **kw) == status
+    assert kla.last_error() != ""
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(N=-1), 1), (dict(H=0), 1), (dict(dk=100), 2), (dict(dv=32), 2), (dict(q=None), 1),
+    (dict(state=None), 1),
+])
+def test_decode_validation(args, status):
+    lib = kla.load()
+    a = dict(q=FAKE, state=FAKE, N=4, H=2, dk=128, dv=128)
+    a.update(args)
+    st = lib.kla_decode_step(a["q"], FAKE, FAKE, FAKE, FAKE, 1e-6, a["state"], FAKE,
+                             a["N"], a["H"], a["dk"], a["dv"], None)
+    assert st == status
+
+
+def test_decode_zero_sequences_is_a_no_op():
+    lib = kla.load()
+    assert lib.kla_decode_step(None, None, None, None, None, 1e-6, None, None, 0, 4, 128, 128, None) == 0
+
+
+def test_forced_workspace_failure(monkeypatch):
+    """The OOM path returns KLA_ERR_OOM before any HIP call (forced from the host)."""
+    monkeypatch.setenv("KLA_TEST_FAIL_ALLOC", "1")
+    lib = kla.load()
+    assert _chunk(lib) == 4
+    assert "KLA_TEST_FAIL_ALLOC" in kla.last_error()
+
+
+def test_plan_paths():
+    # 0.4B-LM-shaped layer: B*H = 128 heads x 2 column groups fill 256 CUs -> sequential
+    p, s, w = kla.plan(8, 4096, 16, 128, 128, num_cus=256)
+    assert p == "sequential" and s == 1
+    assert w >= 8 * 16 * 64 * 33280
+    # long context with 16 heads under-fills the chip -> scan with several segments
+    p, s, w = kla.plan(1, 131072, 16, 128, 128, num_cus=256)
+    assert p == "scan" and 4 <= s <= 64
+    # explicit choices are honoured; segments are clamped so that none is empty
+    assert kla.plan(1, 131072, 16, 128, 128, path="sequential", num_cus=256)[:2] == ("sequential", 1)
+    p, s, _ = kla.plan(1, 64 * 10, 1, 64, 64, path="scan", segments=4, num_cus=256)
+    assert p == "scan" and s == 4
+    p, s, _ = kla.plan(1, 64 * 10, 1, 64, 64, path="scan", segments=100, num_cus=256)
+    assert p == "scan" and s == 10
+    # a single chunk cannot be split
+    assert kla.plan(1, 64, 1, 64, 64, path="scan", num_cus=256)[:2] == ("sequential", 1)
+    assert kla.plan(2, 0, 2, 64, 64, num_cus=256)[1:] == (1, 0)
+
+
+def test_plan_workspace_bytes():
+    _, s, w = kla.plan(1, 64 * 10, 2, 128, 64, path="scan", segments=5, num_cus=256)
+    rec = 2 * 10 * 33280
+    maps = 2 * 4 * 128 * (128 + 64) * 4
+    starts = 2 * 5 * 128 * 64 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert w == up(rec) + up(maps) + up(starts)

@@ -1,0 +1,265 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: max|err| <= 1e-4 * RMS(ref) for fp32 inputs and <= 2e-2 * RMS(ref) for bf16
+inputs, on the outputs and on the end state, element by element. Small cases
+span several chunks and a ragged tail; full-size workloads are compared on
+sampled heads that the C oracle computes over the whole sequence.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import cref, kla_ref
+from tests.gpu_common import TOL, assert_close, err_over_rms, upload, upload_prefill
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import delta_rule_recurrence_kla_amd as kla  # noqa: E402
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_prefill(wl, path="auto", segments=0, init=None):
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    if init is not None:
+        s0 = init
+    out, fin = kla.chunk_fwd(q, k, v, la, eta, wl.eps, init_state=s0, chunk=wl.chunk, path=path, segments=segments)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), fin.cpu().numpy()
+
+
+def oracle_prefill(wl):
+    o, S = cref.forward(wl.q, wl.k, wl.v, wl.log_alpha, wl.eta, wl.eps, wl.init_state)
+    B, T, H, dv = wl.B, wl.T, wl.H, wl.dv
+    return o.reshape(B, H, T, dv).transpose(0, 2, 1, 3), S.reshape(B, H, wl.dk, dv)
+
+
+# ---------------------------------------------------------------------------
+# decode
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (256, 128), (128, 64), (64, 128), (256, 64)])
+def test_decode_small(dtype, dk, dv):
+    log(f"decode small dtype={dtype} dk={dk} dv={dv}")
+    N, H, steps = 3, 5, 6
+    S0 = W.make_decode_state(N, H, dk, dv, std=0.5, seed=3)
+    S_dev = upload(S0, "f32")
+    S_ref = S0.astype(np.float64)
+    for s in range(steps):
+        st = W.make_decode_step(s, N, H, dk, dv, dtype=dtype, seed=3)
+        o = kla.decode_step(upload(st.q, dtype), upload(st.k, dtype), upload(st.v, dtype),
+                            upload(st.log_alpha, "f32"), upload(st.eta, "f32"), S_dev, st.eps)
+        o_ref, S_ref = kla_ref.decode_step(S_ref, st.q, st.k, st.v, st.log_alpha, st.eta, st.eps)
+        assert_close(o.cpu().numpy(), o_ref, 1e-5, f"decode out step {s}")
+    assert_close(S_dev.cpu().numpy(), S_ref, 1e-5, "decode state")
+
+
+def test_decode_full_size_sampled():
+    """Batched recurrent decode at its full shape (256 sequences x 16 heads, dk=dv=128),
+    256 successive steps, sampled heads checked against the C oracle at every step."""
+    cfg = W.DECODE_CONFIG
+    N, H, dk, dv = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"]
+    steps = 256
+    log(f"decode full size N={N} H={H} steps={steps}")
+    S0 = W.make_decode_state(N, H, dk, dv, std=cfg["state_std"], seed=0)
+    S_dev = upload(S0, "f32")
+    rng = np.random.default_rng(123)
+    heads = [(int(a), int(b)) for a, b in zip(rng.integers(0, N, 48), rng.integers(0, H, 48))]
+    heads = sorted(set(heads))
+    S_ref = np.stack([S0[a, h] for a, h in heads]).astype(np.float64)
+    worst = 0.0
+    for s in range(steps):
+        st = W.make_decode_step(s, N, H, dk, dv, dtype="bf16", seed=0)
+        o = kla.decode_step(upload(st.q, "bf16"), upload(st.k, "bf16"), upload(st.v, "bf16"),
+                            upload(st.log_alpha, "f32"), upload(st.eta, "f32"), S_dev, st.eps)
+        o_ref = cref.decode_step(S_ref, st.q, st.k, st.v, st.log_alpha, st.eta, st.eps, heads=heads)
+        og = o.cpu().numpy()
+        got = np.stack([og[a, h] for a, h in heads])
+        worst = max(worst, err_over_rms(got, o_ref))
+        assert worst <= TOL["bf16"], f"step {s}: {worst}"
+    Sg = S_dev.cpu().numpy()
+    assert_close(np.stack([Sg[a, h] for a, h in heads]), S_ref, TOL["bf16"], "decode end state")
+    log(f"decode full size worst max|err|/RMS = {worst:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# prefill, small cases
+def test_prefill_tiny_fp32_config():
+    """Tiny CPU-checkable forward: B=1, H=2, T=256, dk=dv=64, fp32, seed 0, all outputs."""
+    wl = W.make_prefill("tiny_f32", seed=0)
+    log("prefill tiny fp32")
+    o, S = run_prefill(wl)
+    o_ref, S_ref = kla_ref.forward(wl.q, wl.k, wl.v, wl.log_alpha, wl.eta, wl.eps)
+    e1 = assert_close(o, o_ref, TOL["f32"], "out")
+    e2 = assert_close(S, S_ref, TOL["f32"], "final state")
+    log(f"tiny fp32: out {e1:.2e} state {e2:.2e}")
+
+
+SMALL = [(64, 64), (128, 128), (256, 128), (128, 64), (64, 128), (256, 64)]
+
+
+@pytest.mark.parametrize("dk,dv", SMALL)
+@pytest.mark.parametrize("T", [64, 200, 1000])
+@pytest.mark.parametrize("path", ["sequential", "scan"])
+def test_prefill_small_bf16(dk, dv, T, path):
+    log(f"prefill bf16 dk={dk} dv={dv} T={T} path={path}")
+    wl = W.make_prefill("lm_layer_4k", seed=T + dk, B=2, T=T, H=2, dk=dk, dv=dv, init_std=0.3)
+    o, S = run_prefill(wl, path=path, segments=3)
+    o_ref, S_ref = oracle_prefill(wl)
+    assert_close(o, o_ref, TOL["bf16"] / 10, "out")
+    assert_close(S, S_ref, TOL["bf16"] / 10, "final state")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("T", [100, 640])
+@pytest.mark.parametrize("path", ["sequential", "scan"])
+def test_prefill_small_fp32(dk, dv, T, path):
+    log(f"prefill fp32 dk={dk} dv={dv} T={T} path={path}")
+    wl = W.make_prefill("tiny_f32", seed=T + dv, B=2, T=T, H=3, dk=dk, dv=dv, init_std=0.2)
+    o, S = run_prefill(wl, path=path, segments=4)
+    o_ref, S_ref = oracle_prefill(wl)
+    assert_close(o, o_ref, TOL["f32"], "out")
+    assert_close(S, S_ref, TOL["f32"], "final state")
+
+
+def test_prefill_psd_recipe_small():
+    log("prefill psd small")
+    wl = W.make_prefill("psd_lift_8k", seed=5, B=1, T=700, H=2)
+    o, S = run_prefill(wl)
+    o_ref, S_ref = oracle_prefill(wl)
+    assert_close(o, o_ref, TOL["bf16"] / 10, "out")
+    assert_close(S, S_ref, TOL["bf16"] / 10, "final state")
+
+
+# ---------------------------------------------------------------------------
+# invariants
+def test_zero_length_copies_init():
+    wl = W.make_prefill("lm_layer_4k", seed=1, B=2, T=0, H=3, init_std=1.0)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    out, fin = kla.chunk_fwd(q, k, v, la, eta, wl.eps, init_state=s0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(fin.cpu().numpy(), wl.init_state)
+    _, fin0 = kla.chunk_fwd(q, k, v, la, eta, wl.eps)
+    torch.cuda.synchronize()
+    assert np.all(fin0.cpu().numpy() == 0)
+
+
+def test_split_prefill_equals_whole():
+    """prefill(T) == prefill(T1) then prefill(T - T1) from its end state."""
+    wl = W.make_prefill("lm_layer_4k", seed=2, B=2, T=640, H=2, init_std=0.1)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    o, S = kla.chunk_fwd(q, k, v, la, eta, wl.eps, init_state=s0)
+    T1 = 300
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    o1, S1 = kla.chunk_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(la, 0, T1), sl(eta, 0, T1), wl.eps, init_state=s0)
+    o2, S2 = kla.chunk_fwd(sl(q, T1, 640), sl(k, T1, 640), sl(v, T1, 640), sl(la, T1, 640), sl(eta, T1, 640),
+                           wl.eps, init_state=S1)
+    torch.cuda.synchronize()
+    on = o.cpu().numpy()
+    assert_close(np.concatenate([o1.cpu().numpy(), o2.cpu().numpy()], 1), on, 2e-4, "split out")
+    assert_close(S2.cpu().numpy(), S.cpu().numpy(), 2e-4, "split state")
+
+
+def test_prefill_then_decode_equals_longer_prefill():
+    """Decode continues from the prefill's end state: prefill(T) + 5 decode steps ==
+    prefill(T + 5) on the last 5 outputs."""
+    wl = W.make_prefill("lm_layer_4k", seed=4, B=2, T=133, H=2)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    o, S = kla.chunk_fwd(q, k, v, la, eta, wl.eps)
+    T1 = 128
+    sl = lambda x: x[:, :T1].contiguous()
+    _, St = kla.chunk_fwd(sl(q), sl(k), sl(v), sl(la), sl(eta), wl.eps)
+    outs = []
+    for t in range(T1, 133):
+        outs.append(kla.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                                    la[:, t].contiguous(), eta[:, t].contiguous(), St, wl.eps))
+    torch.cuda.synchronize()
+    dec = np.stack([x.cpu().numpy() for x in outs], 1)
+    assert_close(dec, o.cpu().numpy()[:, T1:], 2e-4, "decode after prefill")
+    assert_close(St.cpu().numpy(), S.cpu().numpy(), 2e-4, "state after decode")
+
+
+def test_sequential_equals_scan():
+    wl = W.make_prefill("long_131k", seed=6, B=1, T=64 * 37 + 5, H=3, init_std=0.2)
+    o1, S1 = run_prefill(wl, path="sequential")
+    for segs in (2, 5, 37):
+        o2, S2 = run_prefill(wl, path="scan", segments=segs)
+        assert_close(o2, o1, 1e-3, f"scan({segs}) out")
+        assert_close(S2, S1, 1e-3, f"scan({segs}) state")
+
+
+def test_causality_and_determinism():
+    wl = W.make_prefill("lm_layer_4k", seed=7, B=1, T=500, H=2)
+    q, k, v, la, eta, _ = upload_prefill(wl)
+    o_a, S_a = kla.chunk_fwd(q, k, v, la, eta, wl.eps)
+    o_b, S_b = kla.chunk_fwd(q, k, v, la, eta, wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(S_a, S_b), "two runs differ"
+    t = 300
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[:, t + 1:] += 1
+    k2[:, t + 1:] *= 2
+    v2[:, t + 1:] -= 3
+    o_c, _ = kla.chunk_fwd(q2, k2, v2, la, eta, wl.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c[:, : t + 1], o_a[:, : t + 1]), "outputs up to t changed"
+    assert not torch.equal(o_c[:, t + 1:], o_a[:, t + 1:])
+
+
+def test_final_state_may_alias_init():
+    wl = W.make_prefill("lm_layer_4k", seed=8, B=2, T=300, H=2, init_std=0.3)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    o_ref, S_ref = kla.chunk_fwd(q, k, v, la, eta, wl.eps, init_state=s0.clone())
+    o, _ = kla.chunk_fwd(q, k, v, la, eta, wl.eps, init_state=s0, final_state=s0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(s0, S_ref)
+
+
+def test_exact_projection_self_check():
+    """q = k with eta = 1: o_t = S_t^T k_t = v_t - (1 - beta_t ||k_t||^2) e_t, i.e. v_t up to eps
+    (KLA page, "Theoretical derivation"); checked on PSD-lifted keys without the oracle."""
+    wl = W.make_prefill("psd_lift_8k", seed=9, B=1, T=2048, H=4)
+    q, k, v, la, eta, _ = upload_prefill(wl)
+    o, _ = kla.chunk_fwd(k, k, v, la, eta, 0.0)
+    torch.cuda.synchronize()
+    e = err_over_rms(o.cpu().numpy(), wl.v)
+    assert e < 2e-2, e
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled heads
+def _full_size(name, n_heads, path="auto"):
+    wl = W.make_prefill(name, seed=0)
+    log(f"full size {name}: B={wl.B} T={wl.T} H={wl.H} dk={wl.dk} dv={wl.dv} path={path}")
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    out, fin = kla.chunk_fwd(q, k, v, la, eta, wl.eps, init_state=s0, path=path)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(99)
+    heads = sorted({(int(rng.integers(wl.B)), int(rng.integers(wl.H))) for _ in range(n_heads)})
+    o_ref, S_ref = cref.forward(wl.q, wl.k, wl.v, wl.log_alpha, wl.eta, wl.eps, wl.init_state, heads=heads)
+    got_o = np.stack([out[b, :, h].cpu().numpy() for b, h in heads])
+    got_S = np.stack([fin[b, h].cpu().numpy() for b, h in heads])
+    e1 = assert_close(got_o, o_ref, TOL[wl.dtype], f"{name} out")
+    e2 = assert_close(got_S, S_ref, TOL[wl.dtype], f"{name} state")
+    log(f"{name}: out {e1:.2e} state {e2:.2e} on {len(heads)} heads")
+    return out
+
+
+def test_full_lm_layer_4k():
+    _full_size("lm_layer_4k", 12)
+
+
+def test_full_psd_lift_8k():
+    _full_size("psd_lift_8k", 6)
+
+
+def test_full_long_131k():
+    _full_size("long_131k", 3)
