@@ -22,7 +22,7 @@
 namespace {
 
 constexpr int kChunk = 64;
-constexpr int kRecBytes = 33280;  // per-chunk record of the prep kernel (kla_device.h)
+constexpr int kRecBytes = 33536;  // per-chunk record of the prep kernel (kla_device.h)
 constexpr int kMaxGridYZ = 65535;
 
 thread_local std::string g_err;
@@ -103,6 +103,8 @@ kla_status check_prefill_sizes(kla_dtype dtype, int B, int T, int H, int dk, int
   if (chunk != kChunk) return fail(KLA_ERR_UNSUPPORTED, "chunk=%d not supported (64)", chunk);
   if (dtype == KLA_DTYPE_F32 && dk > 128) return fail(KLA_ERR_UNSUPPORTED, "fp32 prefill supports dk <= 128 (got %d)", dk);
   if (static_cast<long long>(B) * H > kMaxGridYZ) return fail(KLA_ERR_UNSUPPORTED, "B*H=%lld exceeds %d", static_cast<long long>(B) * H, kMaxGridYZ);
+  // kernels address one chunk (64 tokens of every head) with 32-bit buffer offsets below 2^30
+  if (64LL * H * std::max(dk, dv) * 4 >= (1LL << 30)) return fail(KLA_ERR_UNSUPPORTED, "H=%d too large for dk=%d, dv=%d", H, dk, dv);
   return KLA_OK;
 }
 

@@ -24,6 +24,10 @@ namespace kla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Raw 16- and 8-byte vectors. Native vector types (not the uint4 struct) keep register
+// copies out of memory: a conditional struct copy lowers to a select of addresses.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MODE_BF16 = 0;  // q, k, v in bf16; derived operands split into hi + lo bf16
 constexpr int MODE_F32 = 1;   // q, k, v in fp32; fp32 MFMA throughout
@@ -35,15 +39,40 @@ constexpr int CHUNK = 64;     // tokens per chunk
 //   [16384, 32768)  P  = (Q K^T) masked by the inclusive decay mask: 64 rows of 256 bytes
 //   [32768, 33024)  exp(g_r), 64 floats (g = chunk-local inclusive cumsum of log alpha)
 //   [33024, 33280)  exp(g_C - g_r), 64 floats
+//   [33280, 33536)  g_r, 64 floats
 // A 256-byte row holds 64 fp32 values (fp32 mode) or 64 hi bf16 then 64 lo bf16 (bf16 mode).
 constexpr int REC_T_OFF = 0;
 constexpr int REC_P_OFF = 16384;
 constexpr int REC_EG_OFF = 32768;
 constexpr int REC_EGC_OFF = 33024;
-constexpr int REC_BYTES = 33280;
+constexpr int REC_G_OFF = 33280;
+constexpr int REC_BYTES = 33536;
 
 // LDS row pitch of a derived 64x64 matrix: 256 bytes of data + 16 bytes of padding.
 constexpr int DROW_BYTES = 272;
+
+// ---------------------------------------------------------------------------
+// Buffer resources. A raw buffer access is bounds-checked against num_records on
+// its per-lane offset (the scalar offset is not checked): out-of-range loads return
+// zero and out-of-range stores are dropped. Resources are built per chunk with the
+// chunk's first row as base and num_records ending at token T, so the ragged last
+// chunk needs no branches.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int BUF_FLAGS = 0x00020000;  // raw (untyped) dword access
+
+// num_records is capped below BUF_OOB, an offset that is therefore always out of range;
+// the host keeps every in-chunk offset below it.
+constexpr int BUF_OOB = 0x40000000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= BUF_OOB ? BUF_OOB - 1 : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, BUF_FLAGS);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+__device__ __forceinline__ void bstore_f32(float x, rsrc_t r, int voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -51,6 +80,17 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 
 __device__ __forceinline__ int kslot(int gq, int j) {
   return j < 4 ? 4 * gq + j : 12 + 4 * gq + j;
+}
+
+// 32-bit word i (compile-time after unrolling) of a 16-byte vector, without taking its address
+// (an address would force the vector out of registers).
+__device__ __forceinline__ uint32_t u4word(const u32x4& v, int i) { return v[i]; }
+
+// Element j of a 16-byte vector holding bf16 (ELEM_BYTES = 2) or fp32 (4) values, as raw bits.
+template <int ELEM_BYTES>
+__device__ __forceinline__ uint32_t u4elem(const u32x4& v, int j) {
+  if constexpr (ELEM_BYTES == 2) return (u4word(v, j >> 1) >> (16 * (j & 1))) & 0xFFFFu;
+  else return u4word(v, j);
 }
 
 struct F8 {
@@ -107,31 +147,20 @@ struct Tr<MODE_BF16> {
   // row = row0 + ln, contraction columns k0 + kslot(gq, 0..7).
   static __device__ __forceinline__ XF ldx(const in_t* base, int ld, int row0, int k0, int lane) {
     const in_t* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
-    uint2 a = *reinterpret_cast<const uint2*>(p);
-    uint2 b = *reinterpret_cast<const uint2*>(p + 16);
-    union {
-      uint4 u;
-      bf16x8 v;
-    } cv;
-    cv.u = make_uint4(a.x, a.y, b.x, b.y);
-    return cv.v;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
   }
   // Derived operand from a 64x64 matrix stored with DROW_BYTES rows (hi at byte 0, lo at byte 128).
   static __device__ __forceinline__ DF ldd(const uint8_t* base, int row0, int k0, int lane) {
     const uint8_t* p = base + (row0 + (lane & 15)) * DROW_BYTES + 2 * (k0 + 4 * (lane >> 4));
-    uint2 a = *reinterpret_cast<const uint2*>(p);
-    uint2 b = *reinterpret_cast<const uint2*>(p + 32);
-    uint2 c = *reinterpret_cast<const uint2*>(p + 128);
-    uint2 d = *reinterpret_cast<const uint2*>(p + 160);
-    union {
-      uint4 u;
-      bf16x8 v;
-    } h, l;
-    h.u = make_uint4(a.x, a.y, b.x, b.y);
-    l.u = make_uint4(c.x, c.y, d.x, d.y);
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 32);
+    const u32x2 c = *reinterpret_cast<const u32x2*>(p + 128);
+    const u32x2 d = *reinterpret_cast<const u32x2*>(p + 160);
     DF r;
-    r.h = h.v;
-    r.l = l.v;
+    r.h = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
+    r.l = __builtin_bit_cast(bf16x8, __builtin_shufflevector(c, d, 0, 1, 2, 3));
     return r;
   }
   static __device__ __forceinline__ DF mk(const F8& x) { return split8(x); }

@@ -13,7 +13,7 @@ struct Dims {
   int nc;  // number of 64-token chunks, ceil(T / 64)
 };
 
-// Chunk prep: one workgroup per (b, h, chunk); writes one record per chunk.
+// Chunk prep: one wavefront per (b, h, chunk); writes one record per chunk.
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
                        const float* eta, float eps, uint8_t* rec, hipStream_t stream);
 

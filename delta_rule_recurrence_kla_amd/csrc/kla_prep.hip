@@ -1,22 +1,32 @@
 // Chunk prep kernel of the chunkwise KLA forward.
 //
 // For each 64-token chunk of one (batch, head) it computes, in this order:
-//   n_r    = ||k_r||^2                            (fp32)
-//   beta_r = eta_r / (n_r + eps)                  Kaczmarz step size: KLA page, "KLA update rule"
-//   g_r    = sum_{j<=r} log_alpha_j               chunk-local decay exponents
-//   A      = strict_lower(beta_r e^{g_r-g_i} (k_r . k_i))
-//   T      = (I + A)^-1                           blocked fp32 inverse of a unit lower-triangular matrix
+//   G      = K K^T, QK = Q K^T                     (MFMA; q, k enter exactly)
+//   n_r    = ||k_r||^2 = G_rr
+//   beta_r = eta_r / (n_r + eps)                   Kaczmarz step size: KLA page, "KLA update rule"
+//   g_r    = sum_{j<=r} log_alpha_j                chunk-local decay exponents
+//   P      = QK masked by e^{g_r-g_i} for i <= r   (diagonal included: o_t reads S_t after the write)
+//   A      = strict_lower(beta_r e^{g_r-g_i} G)
+//   T      = (I + A)^-1                            blocked inverse of a unit lower-triangular matrix
 //   T'     = T diag(beta)
-//   P      = (q_r . k_i) e^{g_r-g_i} for i <= r   (diagonal included: o_t reads S_t after the write)
-// and stores T', P, e^{g_r} and e^{g_C-g_r} as the chunk's record.
+// and stores T', P, e^{g_r}, e^{g_C-g_r} and g_r as the chunk's record.
 //
 // Why this is the chunk's whole job: writing u_i = beta_i e_i and unrolling the
 // per-token update of the KLA page ("KLA update rule": S_t = S~ + beta_t k_t e_t^T,
 // e_t = v_t - S~^T k_t, S~ = alpha_t S_{t-1}) inside a chunk that starts from S_0 gives
 //   (I + A) U = diag(beta) (V - diag(e^g) K S_0),   so U = T' (V - diag(e^g) K S_0),
-// the chunkwise solver that the KLA page ("Implementation") keeps from Gated DeltaNet
-// with only B = Diag(beta_1..beta_C) changed. Everything above depends on the chunk's
-// own inputs only, so all chunks of all heads run in parallel.
+// and o_r = e^{g_r} S_0^T q_r + sum_{i<=r} P_ri u_i. This is the chunkwise solver that
+// the KLA page ("Implementation") keeps from Gated DeltaNet with only
+// B = Diag(beta_1..beta_C) changed. None of it depends on the state, so every chunk of
+// every head is prepared in parallel.
+//
+// One wavefront prepares one chunk and never waits on another wave: K and Q enter
+// MFMA straight from global memory in fragment layout, the inverse runs as MFMA
+// products over 16x16 blocks, and LDS serves only as the wave's own staging area
+// (to turn accumulator tiles into coalesced record rows and into A operands).
+//
+// The inverse, by block rows (D_I = (I + A_II)^-1, found by forward substitution):
+//   T_II = D_I,   T_IJ = -D_I X_IJ,   X_IJ = sum_{C=J}^{I-1} A_IC T_CJ   (J < I).
 //
 // Tokens past T in the last chunk enter as identity steps: k = q = 0, log_alpha = 0,
 // eta = 0, so their rows and columns of T' and P are zero.
@@ -25,202 +35,262 @@
 
 namespace kla {
 
+namespace {
+
+constexpr int SP = 68;  // fp32 pitch of a wave's 64 x 64 staging matrix (272-byte rows)
+
+__device__ __forceinline__ int tix(int mt, int nt) { return mt * (mt + 1) / 2 + nt; }  // lower tiles
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// 8 fp32 values of a staged matrix in contraction-slot order: row r, columns c0 + kslot(gq, j).
+// `second` = false zeroes slots 4..7 (a 16-deep contraction).
+__device__ __forceinline__ F8 stage_frag(const float* m, int pitch, int r, int c0, int gq, bool second) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(m + r * pitch + c0 + 4 * gq);
+  f32x4 b = zero4();
+  if (second) b = *reinterpret_cast<const f32x4*>(m + r * pitch + c0 + 16 + 4 * gq);
+  return frag_from_acc(a, b);
+}
+
+}  // namespace
+
 template <int MODE, int DK>
-__global__ __launch_bounds__(256) void prep_kernel(const typename Tr<MODE>::in_t* __restrict__ q,
-                                                   const typename Tr<MODE>::in_t* __restrict__ k,
+__global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                    const float* __restrict__ log_alpha,
                                                    const float* __restrict__ eta, float eps,
-                                                   uint8_t* __restrict__ rec, int T, int H, int nc) {
+                                                   uint8_t* __restrict__ rec, int T, int H, int nc, int nchunks) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
-  constexpr int VEC = 16 / static_cast<int>(sizeof(in_t));  // elements per 16-byte access
-  constexpr int LD = DK + VEC;  // row pitch in elements: a 16-byte pad keeps rows 16-byte aligned
-  constexpr int LPR = DK / VEC;                             // lanes per row
-  constexpr int RPI = 256 / LPR;                            // rows per iteration
-  static_assert(LPR <= 64 && 256 % LPR == 0 && CHUNK % RPI == 0, "load shape");
+  using XF = typename TR::XF;
+  using DF = typename TR::DF;
+  constexpr int SZ = static_cast<int>(sizeof(in_t));
 
-  __shared__ __align__(16) in_t sK[CHUNK * LD];
-  __shared__ __align__(16) in_t sQ[CHUNK * LD];
-  __shared__ float sA[CHUNK][CHUNK + 1];
-  __shared__ float sT[CHUNK][CHUNK + 1];
-  __shared__ float sY[3][16][17];
-  __shared__ float sg[CHUNK], sbeta[CHUNK], snk[CHUNK];
+  __shared__ __align__(16) float sStage[4][64 * SP];
+  __shared__ __align__(16) float sD[4][4 * 16 * 20];  // diagonal-block inverses, 16 x 16 with pitch 20
+  __shared__ __align__(16) float sVec[4][2][64];      // n (then beta), g
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gq = lane >> 4, ln = lane & 15;
-  const int c = blockIdx.x, bh = blockIdx.y;
+  const int id = blockIdx.x * 4 + w;
+  if (id >= nchunks) return;  // only wave-level synchronisation below
+  const int bh = id / nc, c = id - bh * nc;
   const int b = bh / H, h = bh - b * H;
   const int t0 = c * CHUNK;
-  uint8_t* R = rec + (static_cast<size_t>(bh) * nc + c) * REC_BYTES;
+  float* st = sStage[w];
+  float* sDw = sD[w];
+  float* sNB = sVec[w][0];
+  float* sGv = sVec[w][1];
 
-  // 1. chunk of K and Q into LDS (zero past T), and key norms
+  // ---- G = K K^T and QK = Q K^T on the lower 10 tiles, operands straight from memory ----
+  const int rowK = H * DK * SZ;
+  const size_t chunk_off = (static_cast<size_t>(b) * T + t0) * rowK;
+  const long long avail = static_cast<long long>(T - t0) * rowK;
+  const rsrc_t rk = make_rsrc(static_cast<const uint8_t*>(kv) + chunk_off, avail);
+  const rsrc_t rq = make_rsrc(static_cast<const uint8_t*>(qv) + chunk_off, avail);
+  f32x4 G[10], QK[10];
 #pragma unroll
-  for (int it = 0; it < CHUNK / RPI; ++it) {
-    const int r = it * RPI + tid / LPR;
-    const int cv = (tid % LPR) * VEC;
-    const int t = t0 + r;
-    uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-    if (t < T) {
-      const size_t off = ((static_cast<size_t>(b) * T + t) * H + h) * DK + cv;
-      kv = *reinterpret_cast<const uint4*>(k + off);
-      qv = *reinterpret_cast<const uint4*>(q + off);
-    }
-    *reinterpret_cast<uint4*>(sK + r * LD + cv) = kv;
-    *reinterpret_cast<uint4*>(sQ + r * LD + cv) = qv;
-    const in_t* e = reinterpret_cast<const in_t*>(&kv);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      const float x = TR::to_f32(e[j]);
-      s += x * x;
-    }
-#pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    if (tid % LPR == 0) snk[r] = s;
-  }
-  __syncthreads();
+  for (int i = 0; i < 10; ++i) G[i] = QK[i] = zero4();
 
-  // 2. gates: lane = token of the chunk
-  if (w == 0) {
-    const int t = t0 + lane;
-    float la = 0.f, et = 0.f;
-    if (t < T) {
-      const size_t gi = (static_cast<size_t>(b) * T + t) * H + h;
-      la = log_alpha[gi];
-      et = eta[gi];
-    }
-    float g = la;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float y = __shfl_up(g, o);
-      if (lane >= o) g += y;
-    }
-    const float denom = snk[lane] + eps;
-    sg[lane] = g;
-    sbeta[lane] = denom != 0.f ? et / denom : 0.f;
-    const float gC = __shfl(g, 63);
-    reinterpret_cast<float*>(R + REC_EG_OFF)[lane] = expf(g);
-    reinterpret_cast<float*>(R + REC_EGC_OFF)[lane] = expf(gC - g);
-  }
-  __syncthreads();
-
-  // 3. K K^T and Q K^T, one 16-row strip per wave, lower-triangular tiles only
+  for (int kb = 0; kb < DK / 32; ++kb) {
+    XF kf[4], qf[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    f32x4 ag = zero4(), ap = zero4();
-    if (nt <= w) {
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        const auto xk = TR::ldx(sK, LD, 16 * w, 32 * kb, lane);
-        const auto xq = TR::ldx(sQ, LD, 16 * w, 32 * kb, lane);
-        const auto yk = TR::ldx(sK, LD, 16 * nt, 32 * kb, lane);
-        ag = TR::mma_xx(ag, xk, yk);
-        ap = TR::mma_xx(ap, xq, yk);
-      }
-    }
-    const int cc = 16 * nt + ln;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * gq + i;
-      const float dec = cc <= r ? expf(sg[r] - sg[cc]) : 0.f;
-      sA[r][cc] = cc < r ? sbeta[r] * dec * ag[i] : 0.f;
-      const float pv = dec * ap[i];
+    for (int x = 0; x < 4; ++x) {
+      const int off = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 4 * gq) * SZ;
       if constexpr (MODE == MODE_BF16) {
-        const __bf16 hi = static_cast<__bf16>(pv);
-        const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
-        __bf16* row = reinterpret_cast<__bf16*>(R + REC_P_OFF + r * 256);
-        row[cc] = hi;
-        row[64 + cc] = lo;
+        const u32x2 k0 = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
+        const u32x2 k1 = __builtin_amdgcn_raw_buffer_load_b64(rk, off + 16 * SZ, 0, 0);
+        const u32x2 q0 = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
+        const u32x2 q1 = __builtin_amdgcn_raw_buffer_load_b64(rq, off + 16 * SZ, 0, 0);
+        kf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3));
+        qf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3));
       } else {
-        reinterpret_cast<float*>(R + REC_P_OFF + r * 256)[cc] = pv;
+        const f32x4 k0 = __builtin_bit_cast(f32x4, bload16(rk, off));
+        const f32x4 k1 = __builtin_bit_cast(f32x4, bload16(rk, off + 16 * SZ));
+        const f32x4 q0 = __builtin_bit_cast(f32x4, bload16(rq, off));
+        const f32x4 q1 = __builtin_bit_cast(f32x4, bload16(rq, off + 16 * SZ));
+        kf[x] = frag_from_acc(k0, k1);
+        qf[x] = frag_from_acc(q0, q1);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt <= mt; ++nt) {
+        G[tix(mt, nt)] = TR::mma_xx(G[tix(mt, nt)], kf[mt], kf[nt]);
+        QK[tix(mt, nt)] = TR::mma_xx(QK[tix(mt, nt)], qf[mt], kf[nt]);
       }
     }
   }
-  __syncthreads();
 
-  // 4a. inverses of the four 16x16 diagonal blocks of I + A, by forward substitution;
-  //     lane (blk, j) produces column j of block blk
-  if (w == 0) {
-    const int blk = lane >> 4, j = lane & 15;
+  // ---- key norms from the diagonal of G; gates; beta; decay exponents ----
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const f32x4 d = G[tix(x, x)];
+    const int i = ln & 3;
+    const float v = i == 0 ? d[0] : i == 1 ? d[1] : i == 2 ? d[2] : d[3];
+    if ((ln >> 2) == gq) sNB[16 * x + ln] = v;  // G[16x+ln][16x+ln]
+  }
+  const int t = t0 + lane;
+  float la = 0.f, et = 0.f;
+  if (t < T) {
+    const size_t gi = (static_cast<size_t>(b) * T + t) * H + h;
+    la = log_alpha[gi];
+    et = eta[gi];
+  }
+  float g = la;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(g, o);
+    if (lane >= o) g += y;
+  }
+  const float gC = __shfl(g, 63);
+  wave_sync();
+  const float denom = sNB[lane] + eps;
+  const float beta = denom != 0.f ? et / denom : 0.f;
+  wave_sync();
+  sNB[lane] = beta;
+  sGv[lane] = g;
+  uint8_t* R = rec + static_cast<size_t>(id) * REC_BYTES;
+  const rsrc_t rr = make_rsrc(R, REC_BYTES);
+  bstore_f32(__expf(g), rr, REC_EG_OFF + 4 * lane);
+  bstore_f32(__expf(gC - g), rr, REC_EGC_OFF + 4 * lane);
+  bstore_f32(g, rr, REC_G_OFF + 4 * lane);
+  wave_sync();
+
+  // Copies the staged 64 x 256-byte image (pitch 272 bytes) to the record at byte offset dst.
+  auto flush_stage = [&](int dst) __attribute__((always_inline)) {
+    wave_sync();
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(st);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int p = lane + 64 * j;  // 16-byte piece: row p >> 4, column piece p & 15
+      const u32x4 x = *reinterpret_cast<const u32x4*>(sb + (p >> 4) * 272 + 16 * (p & 15));
+      __builtin_amdgcn_raw_buffer_store_b128(x, rr, dst + 16 * p, 0, 0);
+    }
+    wave_sync();
+  };
+  // Writes one element of a derived 64 x 64 matrix into the staged record image.
+  auto stage_put = [&](int r, int cc, float v) __attribute__((always_inline)) {
+    uint8_t* row = reinterpret_cast<uint8_t*>(st) + r * 272;
+    if constexpr (MODE == MODE_BF16) {
+      const __bf16 hi = static_cast<__bf16>(v);
+      reinterpret_cast<__bf16*>(row)[cc] = hi;
+      reinterpret_cast<__bf16*>(row)[64 + cc] = static_cast<__bf16>(v - static_cast<float>(hi));
+    } else {
+      reinterpret_cast<float*>(row)[cc] = v;
+    }
+  };
+
+  // ---- P = QK masked by the inclusive decay mask -> record ----
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(sGv + 16 * mt + 4 * gq);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int cc = 16 * nt + ln;
+      const float gc = sGv[cc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * gq + i;
+        float v = 0.f;
+        if (nt <= mt) v = cc <= r ? __expf(fminf(gr[i] - gc, 0.f)) * QK[tix(mt, nt)][i] : 0.f;
+        stage_put(r, cc, v);
+      }
+    }
+  }
+  flush_stage(REC_P_OFF);
+
+  // ---- A = strict_lower(beta_r e^{g_r - g_i} G) into the stage as fp32 ----
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const f32x4 gr = *reinterpret_cast<const f32x4*>(sGv + 16 * mt + 4 * gq);
+    const f32x4 br = *reinterpret_cast<const f32x4*>(sNB + 16 * mt + 4 * gq);
+#pragma unroll
+    for (int nt = 0; nt <= mt; ++nt) {
+      const int cc = 16 * nt + ln;
+      const float gc = sGv[cc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * gq + i;
+        st[r * SP + cc] = cc < r ? br[i] * __expf(fminf(gr[i] - gc, 0.f)) * G[tix(mt, nt)][i] : 0.f;
+      }
+    }
+  }
+  wave_sync();
+
+  // ---- diagonal blocks D_blk = (I + A_blk,blk)^-1; lane (gq, ln) = (block, column) ----
+  {
+    const int blk = gq, j = ln;
+    const float* Ab = st + (16 * blk) * SP + 16 * blk;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float s = r == j ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s -= sA[16 * blk + r][16 * blk + i] * x[i];
+      for (int i = 0; i < r; ++i) s -= Ab[r * SP + i] * x[i];
       x[r] = s;
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sT[16 * blk + r][16 * blk + j] = x[r];
+    for (int r = 0; r < 16; ++r) sDw[blk * 320 + r * 20 + j] = x[r];
   }
-  __syncthreads();
+  wave_sync();
 
-  // 4b. off-diagonal blocks by distance from the diagonal:
-  //     T_IJ = -T_II * sum_{C=J}^{I-1} A_IC T_CJ
+  // ---- off-diagonal blocks by block rows; tiles of T in accumulator layout ----
+  f32x4 Tt[10];
 #pragma unroll
-  for (int d = 1; d <= 3; ++d) {
-    const int nblk = 4 - d;
-    for (int o = tid; o < nblk * 256; o += 256) {
-      const int bi = o >> 8, r = (o >> 4) & 15, s = o & 15;
-      const int I = d + bi, J = bi;
-      float y = 0.f;
-      for (int C = J; C < I; ++C) {
+  for (int I = 0; I < 4; ++I) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) y += sA[16 * I + r][16 * C + u] * sT[16 * C + u][16 * J + s];
-      }
-      sY[bi][r][s] = y;
-    }
-    __syncthreads();
-    for (int o = tid; o < nblk * 256; o += 256) {
-      const int bi = o >> 8, r = (o >> 4) & 15, s = o & 15;
-      const int I = d + bi, J = bi;
-      float t = 0.f;
-      for (int u = 0; u <= r; ++u) t += sT[16 * I + r][16 * I + u] * sY[bi][u][s];
-      sT[16 * I + r][16 * J + s] = -t;
-    }
-    __syncthreads();
+    for (int i = 0; i < 4; ++i) Tt[tix(I, I)][i] = sDw[I * 320 + (4 * gq + i) * 20 + ln];
   }
+#pragma unroll
+  for (int I = 1; I < 4; ++I) {
+    // D_I as an A operand: row ln, contraction columns 4gq .. 4gq+3 (a 16-deep contraction)
+    const DF dI = TR::mk(frag_from_acc(*reinterpret_cast<const f32x4*>(sDw + I * 320 + ln * 20 + 4 * gq), zero4()));
+#pragma unroll
+    for (int J = 0; J < I; ++J) {
+      f32x4 X = zero4();
+#pragma unroll
+      for (int C0 = J; C0 < I; C0 += 2) {
+        const bool two = C0 + 1 < I;
+        const DF a = TR::mk(stage_frag(st, SP, 16 * I + ln, 16 * C0, gq, two));
+        const DF bb = TR::mk(frag_from_acc(Tt[tix(C0, J)], two ? Tt[tix(C0 + 1, J)] : zero4()));
+        X = TR::mma_dd(X, a, bb);
+      }
+      const DF xb = TR::mk(frag_from_acc(X, zero4()));
+      Tt[tix(I, J)] = -TR::mma_dd(zero4(), dI, xb);
+    }
+  }
+  wave_sync();
 
-  // 5. T' = T diag(beta), lower triangle incl. diagonal; 16 columns per thread
-  {
-    const int r = tid >> 2, c0 = (tid & 3) * 16;
-    float tv[16];
+  // ---- T' = T diag(beta) -> record ----
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int cc = c0 + j;
-      tv[j] = cc <= r ? sT[r][cc] * sbeta[cc] : 0.f;
-    }
-    if constexpr (MODE == MODE_BF16) {
-      union {
-        uint4 u[2];
-        __bf16 e[16];
-      } hi, lo;
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        hi.e[j] = static_cast<__bf16>(tv[j]);
-        lo.e[j] = static_cast<__bf16>(tv[j] - static_cast<float>(hi.e[j]));
+    for (int nt = 0; nt < 4; ++nt) {
+      const int cc = 16 * nt + ln;
+      const float bc = sNB[cc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * gq + i;
+        float v = 0.f;
+        if (nt <= mt) v = cc <= r ? Tt[tix(mt, nt)][i] * bc : 0.f;
+        stage_put(r, cc, v);
       }
-      uint4* ph = reinterpret_cast<uint4*>(R + REC_T_OFF + r * 256 + 2 * c0);
-      uint4* pl = reinterpret_cast<uint4*>(R + REC_T_OFF + r * 256 + 128 + 2 * c0);
-      ph[0] = hi.u[0];
-      ph[1] = hi.u[1];
-      pl[0] = lo.u[0];
-      pl[1] = lo.u[1];
-    } else {
-      float4* p = reinterpret_cast<float4*>(R + REC_T_OFF + r * 256 + 4 * c0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = make_float4(tv[4 * j], tv[4 * j + 1], tv[4 * j + 2], tv[4 * j + 3]);
     }
   }
+  flush_stage(REC_T_OFF);
 }
 
 template <int MODE, int DK>
 static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, const float* la, const float* eta,
                                 float eps, uint8_t* rec, hipStream_t stream) {
-  using in_t = typename Tr<MODE>::in_t;
-  dim3 grid(d.nc, d.B * d.H);
-  hipLaunchKernelGGL((prep_kernel<MODE, DK>), grid, dim3(256), 0, stream, static_cast<const in_t*>(q),
-                     static_cast<const in_t*>(k), la, eta, eps, rec, d.T, d.H, d.nc);
+  const int nchunks = d.B * d.H * d.nc;
+  hipLaunchKernelGGL((prep_kernel<MODE, DK>), dim3((nchunks + 3) / 4), dim3(256), 0, stream, q, k, la, eta, eps, rec,
+                     d.T, d.H, d.nc, nchunks);
   return hipGetLastError();
 }
 

@@ -41,36 +41,66 @@ struct StateArgs {
   int fin_ld;
   int fin_segs;
   int fin_last_only;     // write only from the last segment, into slot 0
+  int ncg;               // column groups per (segment, head)
+  int nseg;              // segments in the grid
 };
 
-template <int MODE, int DK, int NW, bool WITH_OUT, bool AUG>
-__global__ __launch_bounds__(NW * 64) void state_kernel(StateArgs a) {
+// Workgroup id -> (column group, unit), unit = bh * nseg + seg. The column groups of one
+// unit read the same K, Q and T'; workgroup ids are dealt to the 8 XCDs round-robin, so
+// ids that differ by a multiple of 8 share an L2. When the grid divides evenly, the
+// groups of a unit get such ids.
+__device__ __forceinline__ void decode_wg(int L, int ncg, int nunits, int& cg, int& unit) {
+  if ((ncg * nunits) % (8 * ncg) == 0) {
+    const int xcd = L & 7, slot = L >> 3;
+    cg = slot % ncg;
+    unit = (slot / ncg) * 8 + xcd;
+  } else {
+    cg = L % ncg;
+    unit = L / ncg;
+  }
+}
+
+// Packs 16-bit element `half` (0 = low, 1 = high) of words lo and hi into one word (lo first).
+__device__ __forceinline__ uint32_t pack_halves(uint32_t lo, uint32_t hi, int half) {
+  return __builtin_amdgcn_perm(hi, lo, half ? 0x07060302u : 0x05040100u);
+}
+
+template <int MODE, int DK, bool WITH_OUT, bool AUG>
+__global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
   using DF = typename TR::DF;
-  constexpr int NT = NW * 64;
-  constexpr int NCOLS = NW * 16;
-  constexpr int VEC = 16 / static_cast<int>(sizeof(in_t));
-  constexpr int LDK = DK + VEC;      // [token][key] pitch
-  constexpr int LDT = CHUNK + VEC;   // [key][token] pitch
-  constexpr int LDV = NCOLS + VEC;   // [token][column] pitch
+  constexpr int NT = 256;
+  constexpr int NCOLS = 64;                    // 4 waves x 16 columns
+  constexpr int SZ = static_cast<int>(sizeof(in_t));
+  constexpr int VEC = 16 / SZ;                 // elements per 16-byte access
+  constexpr int LDK = DK + VEC;                // [token][key] pitch (16-byte aligned rows)
+  constexpr int LDT = CHUNK + 4;               // [key][token] and [column][token] pitch
+  constexpr int KCB = DK / VEC;                // 16-byte column blocks of a key row
+  constexpr int KBLK = 16 * KCB;               // (4 tokens x 16 bytes) blocks of a chunk's K
+  constexpr int KPT = (KBLK + NT - 1) / NT;    // such blocks per thread
+  constexpr int VCB = NCOLS / VEC;             // 16-byte column blocks of a value row
+  constexpr int VBLK = 16 * VCB;               // (4 tokens x 16 bytes) blocks of a chunk's V
+  constexpr int VPT = (VBLK + NT - 1) / NT;
+  constexpr int TPT = CHUNK * 16 / NT;         // T' (and P) vectors per thread
   static_assert(!AUG || DK % NCOLS == 0, "identity/value columns must not share a workgroup");
+  static_assert((KCB & (KCB - 1)) == 0 && (VCB & (VCB - 1)) == 0, "shape");
 
   __shared__ __align__(16) in_t sK[CHUNK * LDK];
   __shared__ __align__(16) in_t sKt[DK * LDT];
   __shared__ __align__(16) in_t sQ[WITH_OUT ? CHUNK * LDK : VEC];
-  __shared__ __align__(16) in_t sV[CHUNK * LDV];
+  __shared__ __align__(16) in_t sVt[NCOLS * LDT];
   __shared__ __align__(16) uint8_t sTP[CHUNK * DROW_BYTES];
   __shared__ __align__(16) uint8_t sPP[WITH_OUT ? CHUNK * DROW_BYTES : 16];
-  __shared__ float sEG[CHUNK], sEGC[CHUNK];
-
-  const in_t* __restrict__ gq_ = static_cast<const in_t*>(a.q);
-  const in_t* __restrict__ gk_ = static_cast<const in_t*>(a.k);
-  const in_t* __restrict__ gv_ = static_cast<const in_t*>(a.v);
+  __shared__ __align__(16) float sTail[3 * CHUNK];  // e^{g}, e^{g_C - g}, g
+  const float* sEG = sTail;
+  const float* sEGC = sTail + CHUNK;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, ln = lane & 15;
-  const int cg = blockIdx.x, seg = blockIdx.y, bh = blockIdx.z;
+  int cg, unit;
+  decode_wg(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
+  const int bh = unit / a.nseg, seg = unit - bh * a.nseg;
   const int H = a.H, T = a.T, DV = a.DV;
   const int b = bh / H, h = bh - b * H;
   const int col0 = cg * NCOLS;            // first (augmented) column of the workgroup
@@ -80,6 +110,116 @@ __global__ __launch_bounds__(NW * 64) void state_kernel(StateArgs a) {
   const int vcol = vcol0 + 16 * w + ln;
   const int c_begin = seg * a.seg_chunks;
   const int c_end = min(a.nc, c_begin + a.seg_chunks);
+
+  // byte strides between consecutive tokens, and this batch's first rows
+  const int rowK = H * DK * SZ, rowV = H * DV * SZ, rowO = H * DV * 4;
+  const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
+  const uint8_t* qb_ = static_cast<const uint8_t*>(a.q) + static_cast<size_t>(b) * T * rowK;
+  const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
+  uint8_t* ob_ = reinterpret_cast<uint8_t*>(a.out) + static_cast<size_t>(b) * T * rowO;
+
+  // per-lane byte offsets inside a chunk (token 0 of the chunk = offset 0)
+  auto kblk = [&](int blk, int& rb, int& cb) __attribute__((always_inline)) {
+    rb = (blk & 3) | ((blk / (4 * KCB)) << 2);
+    cb = (blk >> 2) & (KCB - 1);
+  };
+  auto vblk = [&](int blk, int& rb, int& cb) __attribute__((always_inline)) {
+    rb = (blk & 3) | ((blk / (4 * VCB)) << 2);
+    cb = (blk >> 2) & (VCB - 1);
+  };
+
+  // ---- prefetch registers: the next chunk's inputs, loaded while the current one is computed ----
+  u32x4 pk[KPT][4];
+  u32x4 pq[WITH_OUT ? KPT : 1][4];
+  u32x4 pv[VPT][4];
+  u32x4 pt[TPT];
+  u32x4 pp[WITH_OUT ? TPT : 1];
+  u32x4 ptail = {0u, 0u, 0u, 0u};
+
+  auto issue_loads = [&](int c) __attribute__((always_inline)) {
+    const int t0 = c * CHUNK;
+    const long long rem = static_cast<long long>(T - t0);
+    const rsrc_t rk = make_rsrc(kb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
+    const rsrc_t rq = make_rsrc(qb_ + static_cast<size_t>(t0) * rowK, WITH_OUT ? rem * rowK : 0);
+    const rsrc_t rv = make_rsrc(vb_ + static_cast<size_t>(t0) * rowV, ident ? 0 : rem * rowV);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int blk = tid + NT * u;
+      int rb, cb;
+      kblk(blk, rb, cb);
+      const int off = blk < KBLK ? 4 * rb * rowK + h * DK * SZ + 16 * cb : BUF_OOB;
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4) {
+        pk[u][u4] = bload16(rk, off + u4 * rowK);
+        if constexpr (WITH_OUT) pq[u][u4] = bload16(rq, off + u4 * rowK);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int blk = tid + NT * u;
+      int rb, cb;
+      vblk(blk, rb, cb);
+      const int off = blk < VBLK ? 4 * rb * rowV + (h * DV + vcol0) * SZ + 16 * cb : BUF_OOB;
+#pragma unroll
+      for (int u4 = 0; u4 < 4; ++u4) pv[u][u4] = bload16(rv, off + u4 * rowV);
+    }
+    const uint8_t* R = a.rec + (static_cast<size_t>(bh) * a.nc + c) * REC_BYTES;
+    const rsrc_t rr = make_rsrc(R, REC_BYTES);
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      pt[u] = bload16(rr, REC_T_OFF + 16 * (tid + NT * u));
+      if constexpr (WITH_OUT) pp[u] = bload16(rr, REC_P_OFF + 16 * (tid + NT * u));
+    }
+    if (tid < 3 * CHUNK / 4) ptail = bload16(rr, REC_EG_OFF + 16 * tid);
+  };
+
+  // 4 tokens x VEC elements -> VEC rows of a transposed [element][token] LDS matrix
+  auto store_transposed = [&](in_t* dst, const u32x4 (&blk4)[4], int row0, int tok0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      if constexpr (MODE == MODE_BF16) {
+        const u32x2 pair = {pack_halves(blk4[0][j >> 1], blk4[1][j >> 1], j & 1),
+                            pack_halves(blk4[2][j >> 1], blk4[3][j >> 1], j & 1)};
+        *reinterpret_cast<u32x2*>(dst + (row0 + j) * LDT + tok0) = pair;
+      } else {
+        const u32x4 col4 = {blk4[0][j], blk4[1][j], blk4[2][j], blk4[3][j]};
+        *reinterpret_cast<u32x4*>(dst + (row0 + j) * LDT + tok0) = col4;
+      }
+    }
+  };
+
+  auto store_lds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int blk = tid + NT * u;
+      if (blk < KBLK) {
+        int rb, cb;
+        kblk(blk, rb, cb);
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) {
+          *reinterpret_cast<u32x4*>(sK + (4 * rb + u4) * LDK + VEC * cb) = pk[u][u4];
+          if constexpr (WITH_OUT) *reinterpret_cast<u32x4*>(sQ + (4 * rb + u4) * LDK + VEC * cb) = pq[u][u4];
+        }
+        store_transposed(sKt, pk[u], VEC * cb, 4 * rb);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int blk = tid + NT * u;
+      if (blk < VBLK) {
+        int rb, cb;
+        vblk(blk, rb, cb);
+        store_transposed(sVt, pv[u], VEC * cb, 4 * rb);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int vid = tid + NT * u;
+      *reinterpret_cast<u32x4*>(sTP + (vid >> 4) * DROW_BYTES + 16 * (vid & 15)) = pt[u];
+      if constexpr (WITH_OUT) *reinterpret_cast<u32x4*>(sPP + (vid >> 4) * DROW_BYTES + 16 * (vid & 15)) = pp[u];
+    }
+    if (tid < 3 * CHUNK / 4) reinterpret_cast<u32x4*>(sTail)[tid] = ptail;
+  };
 
   // start state
   f32x4 S[DK / 16];
@@ -98,48 +238,16 @@ __global__ __launch_bounds__(NW * 64) void state_kernel(StateArgs a) {
     }
   }
 
+  if (c_begin < c_end) {
+    issue_loads(c_begin);
+    store_lds();
+  }
+  __syncthreads();
+
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * CHUNK;
-    const uint8_t* R = a.rec + (static_cast<size_t>(bh) * a.nc + c) * REC_BYTES;
-
-    // ---- chunk inputs into LDS ----
-    for (int idx = tid; idx < CHUNK * DK / VEC; idx += NT) {
-      const int r = idx / (DK / VEC), cv = (idx % (DK / VEC)) * VEC;
-      const int t = t0 + r;
-      uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-      if (t < T) {
-        const size_t off = ((static_cast<size_t>(b) * T + t) * H + h) * DK + cv;
-        x = *reinterpret_cast<const uint4*>(gk_ + off);
-        if constexpr (WITH_OUT) y = *reinterpret_cast<const uint4*>(gq_ + off);
-      }
-      *reinterpret_cast<uint4*>(sK + r * LDK + cv) = x;
-      if constexpr (WITH_OUT) *reinterpret_cast<uint4*>(sQ + r * LDK + cv) = y;
-      const in_t* e = reinterpret_cast<const in_t*>(&x);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) sKt[(cv + j) * LDT + r] = e[j];
-    }
-    if (!ident) {
-      for (int idx = tid; idx < CHUNK * NCOLS / VEC; idx += NT) {
-        const int r = idx / (NCOLS / VEC), cv = (idx % (NCOLS / VEC)) * VEC;
-        const int t = t0 + r;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (t < T) x = *reinterpret_cast<const uint4*>(gv_ + ((static_cast<size_t>(b) * T + t) * H + h) * DV + vcol0 + cv);
-        *reinterpret_cast<uint4*>(sV + r * LDV + cv) = x;
-      }
-    }
-    for (int idx = tid; idx < CHUNK * 16; idx += NT) {
-      const int r = idx >> 4, j = idx & 15;
-      *reinterpret_cast<uint4*>(sTP + r * DROW_BYTES + 16 * j) =
-          *reinterpret_cast<const uint4*>(R + REC_T_OFF + r * 256 + 16 * j);
-      if constexpr (WITH_OUT)
-        *reinterpret_cast<uint4*>(sPP + r * DROW_BYTES + 16 * j) =
-            *reinterpret_cast<const uint4*>(R + REC_P_OFF + r * 256 + 16 * j);
-    }
-    if (tid < CHUNK) {
-      sEG[tid] = reinterpret_cast<const float*>(R + REC_EG_OFF)[tid];
-      sEGC[tid] = reinterpret_cast<const float*>(R + REC_EGC_OFF)[tid];
-    }
-    __syncthreads();
+    const bool more = c + 1 < c_end;
+    if (more) issue_loads(c + 1);
 
     // ---- S as B operand (contraction over keys) ----
     DF Sb[DK / 32];
@@ -153,55 +261,68 @@ __global__ __launch_bounds__(NW * 64) void state_kernel(StateArgs a) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, TR::ldx(sK, LDK, 16 * mt, 32 * kb, lane), Sb[kb]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 16 * mt + 4 * gq + i;
-        const float vv = ident ? 0.f : TR::to_f32(sV[tok * LDV + 16 * w + ln]);
-        Rr[mt][i] = vv - sEG[tok] * acc[i];
+      const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + 16 * mt + 4 * gq);
+      float vv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (!ident) {
+        const in_t* vp = sVt + (16 * w + ln) * LDT + 16 * mt + 4 * gq;
+        if constexpr (MODE == MODE_BF16) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(vp);
+          vv[0] = __uint_as_float(x[0] << 16);
+          vv[1] = __uint_as_float(x[0] & 0xFFFF0000u);
+          vv[2] = __uint_as_float(x[1] << 16);
+          vv[3] = __uint_as_float(x[1] & 0xFFFF0000u);
+        } else {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(vp);
+          vv[0] = x[0]; vv[1] = x[1]; vv[2] = x[2]; vv[3] = x[3];
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Rr[mt][i] = vv[i] - eg[i] * acc[i];
     }
     DF Rb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Rb[kb] = TR::mk(frag_from_acc(Rr[2 * kb], Rr[2 * kb + 1]));
 
-    // ---- U = T' R ----
+    // ---- U = T' R  (T' is lower triangular: rows 0..31 need only tokens 0..31) ----
     f32x4 U[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       U[mt] = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) U[mt] = TR::mma_dd(U[mt], TR::ldd(sTP, 16 * mt, 32 * kb, lane), Rb[kb]);
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], TR::ldd(sTP, 16 * mt, 32 * kb, lane), Rb[kb]);
     }
 
     // ---- O = diag(e^g) Q S + P U ----
     if constexpr (WITH_OUT) {
-      DF Ub[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) Ub[kb] = TR::mk(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
+      f32x4 O[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, TR::ldx(sQ, LDK, 16 * mt, 32 * kb, lane), Sb[kb]);
+        O[mt] = acc * *reinterpret_cast<const f32x4*>(sEG + 16 * mt + 4 * gq);
+      }
+
+      DF Ub[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= sEG[16 * mt + 4 * gq + i];
+      for (int kb = 0; kb < 2; ++kb) Ub[kb] = TR::mk(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
+      const rsrc_t ro = make_rsrc(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
+      const int obase = 4 * gq * rowO + (h * DV + vcol) * 4;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc = TR::mma_dd(acc, TR::ldd(sPP, 16 * mt, 32 * kb, lane), Ub[kb]);
+      for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * mt + 4 * gq + i;
-          if (t < T) a.out[((static_cast<size_t>(b) * T + t) * H + h) * DV + vcol] = acc[i];
-        }
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb == 0 || mt >= 2) O[mt] = TR::mma_dd(O[mt], TR::ldd(sPP, 16 * mt, 32 * kb, lane), Ub[kb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bstore_f32(O[mt][i], ro, obase + (16 * mt + i) * rowO);
       }
     }
 
     // ---- S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
     const float gC = sEG[CHUNK - 1];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) U[mt][i] *= sEGC[16 * mt + 4 * gq + i];
-    }
+    for (int mt = 0; mt < 4; ++mt) U[mt] *= *reinterpret_cast<const f32x4*>(sEGC + 16 * mt + 4 * gq);
     DF Ud[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Ud[kb] = TR::mk(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
@@ -211,11 +332,13 @@ __global__ __launch_bounds__(NW * 64) void state_kernel(StateArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], TR::ldx(sKt, LDT, 16 * mt, 32 * kb, lane), Ud[kb]);
     }
+    __syncthreads();  // every read of this chunk's LDS is done
+    if (more) store_lds();
     __syncthreads();
   }
 
   // end state
-  if (a.fin && (!a.fin_last_only || seg == static_cast<int>(gridDim.y) - 1)) {
+  if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
     float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
 #pragma unroll
     for (int mt = 0; mt < DK / 16; ++mt) {
@@ -274,26 +397,26 @@ __global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __rest
 }
 
 // ---------------------------------------------------------------------------
-constexpr int NW_STATE = 4;  // 4 waves = 64 columns per workgroup
+constexpr int NCOLS_STATE = 64;  // state columns per workgroup (4 waves x 16)
 
 template <int MODE, int DK, bool WITH_OUT, bool AUG>
-static hipError_t launch_state_t(dim3 grid, const StateArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((state_kernel<MODE, DK, NW_STATE, WITH_OUT, AUG>), grid, dim3(NW_STATE * 64), 0, stream, a);
+static hipError_t launch_state_t(int nwg, const StateArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((state_kernel<MODE, DK, WITH_OUT, AUG>), dim3(nwg), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool WITH_OUT, bool AUG>
-static hipError_t dispatch_state(int mode, int dk, dim3 grid, const StateArgs& a, hipStream_t stream) {
+static hipError_t dispatch_state(int mode, int dk, int nwg, const StateArgs& a, hipStream_t stream) {
   if (mode == MODE_BF16) {
     switch (dk) {
-      case 64: return launch_state_t<MODE_BF16, 64, WITH_OUT, AUG>(grid, a, stream);
-      case 128: return launch_state_t<MODE_BF16, 128, WITH_OUT, AUG>(grid, a, stream);
-      case 256: return launch_state_t<MODE_BF16, 256, WITH_OUT, AUG>(grid, a, stream);
+      case 64: return launch_state_t<MODE_BF16, 64, WITH_OUT, AUG>(nwg, a, stream);
+      case 128: return launch_state_t<MODE_BF16, 128, WITH_OUT, AUG>(nwg, a, stream);
+      case 256: return launch_state_t<MODE_BF16, 256, WITH_OUT, AUG>(nwg, a, stream);
     }
   } else {
     switch (dk) {
-      case 64: return launch_state_t<MODE_F32, 64, WITH_OUT, AUG>(grid, a, stream);
-      case 128: return launch_state_t<MODE_F32, 128, WITH_OUT, AUG>(grid, a, stream);
+      case 64: return launch_state_t<MODE_F32, 64, WITH_OUT, AUG>(nwg, a, stream);
+      case 128: return launch_state_t<MODE_F32, 128, WITH_OUT, AUG>(nwg, a, stream);
     }
   }
   return hipErrorInvalidValue;
@@ -302,17 +425,17 @@ static hipError_t dispatch_state(int mode, int dk, dim3 grid, const StateArgs& a
 hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* k, const void* v,
                             const uint8_t* rec, const float* init, float* out, float* fin,
                             hipStream_t stream) {
-  StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out, fin, d.dv, 1, 0};
-  dim3 grid(d.dv / (16 * NW_STATE), 1, d.B * d.H);
-  return dispatch_state<true, false>(mode, d.dk, grid, a, stream);
+  const int ncg = d.dv / NCOLS_STATE;
+  StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out, fin, d.dv, 1, 0, ncg, 1};
+  return dispatch_state<true, false>(mode, d.dk, ncg * d.B * d.H, a, stream);
 }
 
 hipError_t launch_scan_maps(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
                             int seg_chunks, int segs, float* maps, hipStream_t stream) {
+  const int ncg = (d.dk + d.dv) / NCOLS_STATE;
   StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv,
-              segs - 1, 0};
-  dim3 grid((d.dk + d.dv) / (16 * NW_STATE), segs - 1, d.B * d.H);
-  return dispatch_state<false, true>(mode, d.dk, grid, a, stream);
+              segs - 1, 0, ncg, segs - 1};
+  return dispatch_state<false, true>(mode, d.dk, ncg * (segs - 1) * d.B * d.H, a, stream);
 }
 
 hipError_t launch_scan_starts(const Dims& d, const float* maps, const float* init, int segs, float* starts,
@@ -330,9 +453,9 @@ hipError_t launch_scan_starts(const Dims& d, const float* maps, const float* ini
 hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void* k, const void* v,
                              const uint8_t* rec, int seg_chunks, int segs, const float* starts, float* out,
                              float* fin, hipStream_t stream) {
-  StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, starts, segs, out, fin, d.dv, 1, 1};
-  dim3 grid(d.dv / (16 * NW_STATE), segs, d.B * d.H);
-  return dispatch_state<true, false>(mode, d.dk, grid, a, stream);
+  const int ncg = d.dv / NCOLS_STATE;
+  StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, starts, segs, out, fin, d.dv, 1, 1, ncg, segs};
+  return dispatch_state<true, false>(mode, d.dk, ncg * segs * d.B * d.H, a, stream);
 }
 
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream) {

@@ -92,7 +92,7 @@ def test_plan_paths():
     # 0.4B-LM-shaped layer: B*H = 128 heads x 2 column groups fill 256 CUs -> sequential
     p, s, w = kla.plan(8, 4096, 16, 128, 128, num_cus=256)
     assert p == "sequential" and s == 1
-    assert w >= 8 * 16 * 64 * 33280
+    assert w >= 8 * 16 * 64 * 33536
     # long context with 16 heads under-fills the chip -> scan with several segments
     p, s, w = kla.plan(1, 131072, 16, 128, 128, num_cus=256)
     assert p == "scan" and 4 <= s <= 64
@@ -109,7 +109,7 @@ def test_plan_paths():
 
 def test_plan_workspace_bytes():
     _, s, w = kla.plan(1, 64 * 10, 2, 128, 64, path="scan", segments=5, num_cus=256)
-    rec = 2 * 10 * 33280
+    rec = 2 * 10 * 33536
     maps = 2 * 4 * 128 * (128 + 64) * 4
     starts = 2 * 5 * 128 * 64 * 4
     up = lambda x: (x + 255) // 256 * 256
