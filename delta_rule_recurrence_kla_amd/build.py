@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kla_prep.hip", "kla_state.hip", "kla_decode.hip", "kla_api.cpp"]
+SOURCES = ["kla_prep.hip", "kla_state.hip", "kla_state_dma.hip", "kla_decode.hip", "kla_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
 

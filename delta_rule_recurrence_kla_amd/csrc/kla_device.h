@@ -74,6 +74,27 @@ __device__ __forceinline__ void bstore_f32(float x, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// LDS row swizzle. Rows of RB bytes are split into 16-byte pieces; logical piece p of
+// row r is stored at piece p ^ swz<RB>(r). With it, the two read patterns used on
+// these rows are free of bank conflicts: an MFMA operand fragment (16 rows, one
+// column block each) and a transposed read (4 consecutive rows x 32 bytes per group
+// of 16 lanes). Chunk records are written in this layout so that they can be copied
+// into LDS unchanged.
+template <int RB>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (RB >= 256) {
+    return ((row & 7) << 1) | ((row >> 3) & 1);
+  } else {
+    const int x = (row >> 1) & 7;
+    return ((x & 3) << 1) | (x >> 2);
+  }
+}
+template <int RB>
+__device__ __forceinline__ int swz_off(int row, int byte) {
+  return row * RB + (((byte >> 4) ^ swz<RB>(row)) << 4) + (byte & 15);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

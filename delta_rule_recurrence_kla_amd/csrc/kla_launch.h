@@ -35,6 +35,13 @@ hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void*
                              const uint8_t* rec, int seg_chunks, int segs, const float* starts,
                              float* out, float* fin, hipStream_t stream);
 
+// DMA-fed state kernel (kla_state_dma.hip): bf16 inputs with dk in {64, 128}.
+bool state_dma_supported(int mode, int dk);
+hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
+                            const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
+                            int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
+                            int ncg, int nseg, hipStream_t stream);
+
 // Copy (or zero when src is null) n floats; used for T == 0 and as a graph-safe fill.
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);
 

@@ -9,7 +9,8 @@
 //   A      = strict_lower(beta_r e^{g_r-g_i} G)
 //   T      = (I + A)^-1                            blocked inverse of a unit lower-triangular matrix
 //   T'     = T diag(beta)
-// and stores T', P, e^{g_r}, e^{g_C-g_r} and g_r as the chunk's record.
+// and stores T', P, e^{g_r}, e^{g_C-g_r} and g_r as the chunk's record (matrix rows in the
+// swizzled LDS layout of kla_device.h).
 //
 // Why this is the chunk's whole job: writing u_i = beta_i e_i and unrolling the
 // per-token update of the KLA page ("KLA update rule": S_t = S~ + beta_t k_t e_t^T,
@@ -37,7 +38,9 @@ namespace kla {
 
 namespace {
 
-constexpr int SP = 68;  // fp32 pitch of a wave's 64 x 64 staging matrix (272-byte rows)
+constexpr int AP = 20;        // fp32 pitch of a packed 16 x 16 block of A (80-byte rows)
+constexpr int ABLK = 16 * AP;  // floats per packed block
+constexpr int DP = 17;        // fp32 pitch of a 16 x 16 diagonal-block inverse
 
 __device__ __forceinline__ int tix(int mt, int nt) { return mt * (mt + 1) / 2 + nt; }  // lower tiles
 
@@ -46,12 +49,12 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// 8 fp32 values of a staged matrix in contraction-slot order: row r, columns c0 + kslot(gq, j).
-// `second` = false zeroes slots 4..7 (a 16-deep contraction).
-__device__ __forceinline__ F8 stage_frag(const float* m, int pitch, int r, int c0, int gq, bool second) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(m + r * pitch + c0 + 4 * gq);
+// 8 fp32 values of block row I of A in contraction-slot order: row ln of blocks (I, C0) and
+// (I, C0 + 1), columns 4gq .. 4gq+3 of each. `second` = false zeroes slots 4..7.
+__device__ __forceinline__ F8 a_frag(const float* sA, int I, int C0, int ln, int gq, bool second) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(sA + tix(I, C0) * ABLK + ln * AP + 4 * gq);
   f32x4 b = zero4();
-  if (second) b = *reinterpret_cast<const f32x4*>(m + r * pitch + c0 + 16 + 4 * gq);
+  if (second) b = *reinterpret_cast<const f32x4*>(sA + tix(I, C0 + 1) * ABLK + ln * AP + 4 * gq);
   return frag_from_acc(a, b);
 }
 
@@ -68,9 +71,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
   using DF = typename TR::DF;
   constexpr int SZ = static_cast<int>(sizeof(in_t));
 
-  __shared__ __align__(16) float sStage[4][64 * SP];
-  __shared__ __align__(16) float sD[4][4 * 16 * 20];  // diagonal-block inverses, 16 x 16 with pitch 20
-  __shared__ __align__(16) float sVec[4][2][64];      // n (then beta), g
+  // per wave: the 10 lower 16x16 blocks of A; a 16-row staging strip (272-byte rows) that
+  // also holds the diagonal-block inverses during the inverse; n (then beta) and g
+  __shared__ __align__(16) float sAbuf[4][10 * ABLK];
+  __shared__ __align__(16) float sStage[4][16 * 68];
+  __shared__ __align__(16) float sVec[4][2][64];
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gq = lane >> 4, ln = lane & 15;
@@ -79,8 +84,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
   const int bh = id / nc, c = id - bh * nc;
   const int b = bh / H, h = bh - b * H;
   const int t0 = c * CHUNK;
+  float* sA = sAbuf[w];
   float* st = sStage[w];
-  float* sDw = sD[w];
+  float* sDw = st;  // diagonal-block inverses D_I at I * 16 * DP
   float* sNB = sVec[w][0];
   float* sGv = sVec[w][1];
 
@@ -161,19 +167,20 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
   bstore_f32(g, rr, REC_G_OFF + 4 * lane);
   wave_sync();
 
-  // Copies the staged 64 x 256-byte image (pitch 272 bytes) to the record at byte offset dst.
-  auto flush_stage = [&](int dst) __attribute__((always_inline)) {
+  // Copies the staged strip (16 rows of 256 bytes, pitch 272) to record rows 16*mt .. 16*mt+15 at byte dst.
+  auto flush_strip = [&](int dst, int mt) __attribute__((always_inline)) {
     wave_sync();
     const uint8_t* sb = reinterpret_cast<const uint8_t*>(st);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int p = lane + 64 * j;  // 16-byte piece: row p >> 4, column piece p & 15
+    for (int j = 0; j < 4; ++j) {
+      const int p = lane + 64 * j;  // 16-byte piece: strip row p >> 4, column piece p & 15
       const u32x4 x = *reinterpret_cast<const u32x4*>(sb + (p >> 4) * 272 + 16 * (p & 15));
-      __builtin_amdgcn_raw_buffer_store_b128(x, rr, dst + 16 * p, 0, 0);
+      const int row = 16 * mt + (p >> 4);
+      __builtin_amdgcn_raw_buffer_store_b128(x, rr, dst + swz_off<256>(row, 16 * (p & 15)), 0, 0);
     }
     wave_sync();
   };
-  // Writes one element of a derived 64 x 64 matrix into the staged record image.
+  // Writes one element of a derived 64 x 64 matrix into the strip (row r of the strip).
   auto stage_put = [&](int r, int cc, float v) __attribute__((always_inline)) {
     uint8_t* row = reinterpret_cast<uint8_t*>(st) + r * 272;
     if constexpr (MODE == MODE_BF16) {
@@ -198,11 +205,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
         const int r = 16 * mt + 4 * gq + i;
         float v = 0.f;
         if (nt <= mt) v = cc <= r ? __expf(fminf(gr[i] - gc, 0.f)) * QK[tix(mt, nt)][i] : 0.f;
-        stage_put(r, cc, v);
+        stage_put(4 * gq + i, cc, v);
       }
     }
+    flush_strip(REC_P_OFF, mt);
   }
-  flush_stage(REC_P_OFF);
 
   // ---- A = strict_lower(beta_r e^{g_r - g_i} G) into the stage as fp32 ----
 #pragma unroll
@@ -216,26 +223,29 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * gq + i;
-        st[r * SP + cc] = cc < r ? br[i] * __expf(fminf(gr[i] - gc, 0.f)) * G[tix(mt, nt)][i] : 0.f;
+        sA[tix(mt, nt) * ABLK + (4 * gq + i) * AP + ln] =
+            cc < r ? br[i] * __expf(fminf(gr[i] - gc, 0.f)) * G[tix(mt, nt)][i] : 0.f;
       }
     }
   }
   wave_sync();
 
   // ---- diagonal blocks D_blk = (I + A_blk,blk)^-1; lane (gq, ln) = (block, column) ----
+  // column-oriented forward substitution: once x_i is final, fold it into every later row
   {
     const int blk = gq, j = ln;
-    const float* Ab = st + (16 * blk) * SP + 16 * blk;
+    const float* Ab = sA + tix(blk, blk) * ABLK;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = r == j ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = r == j ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s -= Ab[r * SP + i] * x[i];
-      x[r] = s;
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int r = i + 1; r < 16; ++r) x[r] -= Ab[r * AP + i] * x[i];
     }
+    wave_sync();  // the P strip flush has finished with the staging area
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sDw[blk * 320 + r * 20 + j] = x[r];
+    for (int r = 0; r < 16; ++r) sDw[blk * 16 * DP + r * DP + j] = x[r];
   }
   wave_sync();
 
@@ -244,19 +254,21 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
 #pragma unroll
   for (int I = 0; I < 4; ++I) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Tt[tix(I, I)][i] = sDw[I * 320 + (4 * gq + i) * 20 + ln];
+    for (int i = 0; i < 4; ++i) Tt[tix(I, I)][i] = sDw[I * 16 * DP + (4 * gq + i) * DP + ln];
   }
 #pragma unroll
   for (int I = 1; I < 4; ++I) {
     // D_I as an A operand: row ln, contraction columns 4gq .. 4gq+3 (a 16-deep contraction)
-    const DF dI = TR::mk(frag_from_acc(*reinterpret_cast<const f32x4*>(sDw + I * 320 + ln * 20 + 4 * gq), zero4()));
+    const float* dr = sDw + I * 16 * DP + ln * DP + 4 * gq;
+    const f32x4 drow = {dr[0], dr[1], dr[2], dr[3]};
+    const DF dI = TR::mk(frag_from_acc(drow, zero4()));
 #pragma unroll
     for (int J = 0; J < I; ++J) {
       f32x4 X = zero4();
 #pragma unroll
       for (int C0 = J; C0 < I; C0 += 2) {
         const bool two = C0 + 1 < I;
-        const DF a = TR::mk(stage_frag(st, SP, 16 * I + ln, 16 * C0, gq, two));
+        const DF a = TR::mk(a_frag(sA, I, C0, ln, gq, two));
         const DF bb = TR::mk(frag_from_acc(Tt[tix(C0, J)], two ? Tt[tix(C0 + 1, J)] : zero4()));
         X = TR::mma_dd(X, a, bb);
       }
@@ -278,11 +290,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
         const int r = 16 * mt + 4 * gq + i;
         float v = 0.f;
         if (nt <= mt) v = cc <= r ? Tt[tix(mt, nt)][i] * bc : 0.f;
-        stage_put(r, cc, v);
+        stage_put(4 * gq + i, cc, v);
       }
     }
+    flush_strip(REC_T_OFF, mt);
   }
-  flush_stage(REC_T_OFF);
 }
 
 template <int MODE, int DK>

@@ -215,8 +215,9 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int vid = tid + NT * u;
-      *reinterpret_cast<u32x4*>(sTP + (vid >> 4) * DROW_BYTES + 16 * (vid & 15)) = pt[u];
-      if constexpr (WITH_OUT) *reinterpret_cast<u32x4*>(sPP + (vid >> 4) * DROW_BYTES + 16 * (vid & 15)) = pp[u];
+      const int row = vid >> 4, piece = (vid & 15) ^ swz<256>(vid >> 4);  // record rows are swizzled
+      *reinterpret_cast<u32x4*>(sTP + row * DROW_BYTES + 16 * piece) = pt[u];
+      if constexpr (WITH_OUT) *reinterpret_cast<u32x4*>(sPP + row * DROW_BYTES + 16 * piece) = pp[u];
     }
     if (tid < 3 * CHUNK / 4) reinterpret_cast<u32x4*>(sTail)[tid] = ptail;
   };
@@ -426,6 +427,9 @@ hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* 
                             const uint8_t* rec, const float* init, float* out, float* fin,
                             hipStream_t stream) {
   const int ncg = d.dv / NCOLS_STATE;
+  if (state_dma_supported(mode, d.dk))
+    return launch_state_dma(true, false, d.dk, ncg * d.B * d.H, q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out,
+                            fin, d.dv, 1, 0, ncg, 1, stream);
   StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out, fin, d.dv, 1, 0, ncg, 1};
   return dispatch_state<true, false>(mode, d.dk, ncg * d.B * d.H, a, stream);
 }
@@ -433,6 +437,9 @@ hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* 
 hipError_t launch_scan_maps(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
                             int seg_chunks, int segs, float* maps, hipStream_t stream) {
   const int ncg = (d.dk + d.dv) / NCOLS_STATE;
+  if (state_dma_supported(mode, d.dk))
+    return launch_state_dma(false, true, d.dk, ncg * (segs - 1) * d.B * d.H, nullptr, k, v, rec, d.T, d.H, d.dv, d.nc,
+                            seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv, segs - 1, 0, ncg, segs - 1, stream);
   StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv,
               segs - 1, 0, ncg, segs - 1};
   return dispatch_state<false, true>(mode, d.dk, ncg * (segs - 1) * d.B * d.H, a, stream);
@@ -454,6 +461,9 @@ hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void*
                              const uint8_t* rec, int seg_chunks, int segs, const float* starts, float* out,
                              float* fin, hipStream_t stream) {
   const int ncg = d.dv / NCOLS_STATE;
+  if (state_dma_supported(mode, d.dk))
+    return launch_state_dma(true, false, d.dk, ncg * segs * d.B * d.H, q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks,
+                            starts, segs, out, fin, d.dv, 1, 1, ncg, segs, stream);
   StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, starts, segs, out, fin, d.dv, 1, 1, ncg, segs};
   return dispatch_state<true, false>(mode, d.dk, ncg * segs * d.B * d.H, a, stream);
 }

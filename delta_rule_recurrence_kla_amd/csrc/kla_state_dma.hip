@@ -1,0 +1,328 @@
+// Inter-chunk state and output kernel, bf16 inputs, dk in {64, 128}: the DMA-fed variant.
+//
+// Same mathematics as state_kernel in kla_state.hip (see there; KLA page, "KLA update
+// rule" and "Implementation"):
+//   R  = V - diag(e^g) K S,   U = T' R,   O = diag(e^g) Q S + P U,
+//   S <- e^{g_C} S + K^T diag(e^{g_C - g}) U,
+// with one workgroup per (b, h, 64 state columns), one wave per 16 columns, and the
+// state held in MFMA accumulator registers for the whole walk over the chunks.
+//
+// What differs is how a chunk's operands reach LDS and registers:
+//  * every input of chunk c+1 (rows of K, Q, V and the chunk record) is copied into
+//    the other half of a double-buffered LDS area by buffer_load ... lds while chunk
+//    c is computed, so no registers hold prefetched data and a chunk needs a single
+//    workgroup barrier;
+//  * rows land in the swizzled layout of kla_device.h: the DMA picks, per lane, the
+//    source piece that belongs at its fixed destination;
+//  * K^T operands and the accumulator-layout view of V come from transposed LDS reads
+//    (ds_read_b64_tr_b16) of the row-major rows, so no transposed copies are built.
+#include "kla_device.h"
+#include "kla_launch.h"
+
+namespace kla {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+struct StateDmaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* rec;
+  int T, H, DV, nc;
+  int seg_chunks;
+  const float* init;
+  int init_segs;
+  float* out;
+  float* fin;
+  int fin_ld;
+  int fin_segs;
+  int fin_last_only;
+  int ncg;
+  int nseg;
+};
+
+namespace {
+
+// Transposed read: with X a row-major bf16 matrix of RB-byte swizzled rows, lane (gq, ln)
+// receives X[r0 + 4gq + j][c0 + ln] for j = 0..3 (c0 a multiple of 16 elements).
+template <int RB>
+__device__ __forceinline__ u32x2 tr_rows4(const uint8_t* X, int r0, int c0, int lane) {
+  const int gq = lane >> 4, ln = lane & 15;
+  const int off = swz_off<RB>(r0 + 4 * gq + (ln >> 2), 2 * (c0 + 4 * (ln & 3)));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand fragment of a row-major bf16 matrix: row row0 + ln, contraction columns
+// k0 + kslot(gq, 0..7).
+template <int RB>
+__device__ __forceinline__ bf16x8 frag_rows(const uint8_t* X, int row0, int k0, int lane) {
+  const int row = row0 + (lane & 15), byte = 2 * (k0 + 4 * (lane >> 4));
+  const u32x2 a = *reinterpret_cast<const u32x2*>(X + swz_off<RB>(row, byte));
+  const u32x2 b = *reinterpret_cast<const u32x2*>(X + swz_off<RB>(row, byte + 32));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
+}
+
+// MFMA operand fragment of the transpose of a row-major bf16 matrix: element
+// [m = m0 + ln][k = k0 + kslot(gq, j)] = X[k][m].
+template <int RB>
+__device__ __forceinline__ bf16x8 frag_cols(const uint8_t* X, int m0, int k0, int lane) {
+  const u32x2 a = tr_rows4<RB>(X, k0, m0, lane);
+  const u32x2 b = tr_rows4<RB>(X, k0 + 16, m0, lane);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
+}
+
+// Derived (hi + lo) operand fragment of a 64 x 64 record matrix (256-byte swizzled rows).
+__device__ __forceinline__ S8 frag_rec(const uint8_t* M, int row0, int k0, int lane) {
+  const int row = row0 + (lane & 15), byte = 2 * (k0 + 4 * (lane >> 4));
+  const u32x2 a = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte));
+  const u32x2 b = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte + 32));
+  const u32x2 c = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte + 128));
+  const u32x2 d = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte + 160));
+  S8 r;
+  r.h = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
+  r.l = __builtin_bit_cast(bf16x8, __builtin_shufflevector(c, d, 0, 1, 2, 3));
+  return r;
+}
+
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void decode_wg_dma(int L, int ncg, int nunits, int& cg, int& unit) {
+  if ((ncg * nunits) % (8 * ncg) == 0) {
+    const int xcd = L & 7, slot = L >> 3;
+    cg = slot % ncg;
+    unit = (slot / ncg) * 8 + xcd;
+  } else {
+    cg = L % ncg;
+    unit = L / ncg;
+  }
+}
+
+}  // namespace
+
+template <int DK, bool WITH_OUT, bool AUG>
+__global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
+  using TR = Tr<MODE_BF16>;
+  constexpr int NCOLS = 64;
+  constexpr int KRB = DK * 2;                 // bytes of a key row
+  constexpr int VRB = NCOLS * 2;              // bytes of a value row (this workgroup's columns)
+  constexpr int KBYTES = CHUNK * KRB;
+  constexpr int VBYTES = CHUNK * VRB;
+  constexpr int RECB = 33 * 1024;             // record image (33536 bytes) rounded up to whole DMA blocks
+  constexpr int K_OFF = 0;
+  constexpr int Q_OFF = K_OFF + KBYTES;
+  constexpr int V_OFF = Q_OFF + (WITH_OUT ? KBYTES : 0);
+  constexpr int R_OFF = V_OFF + VBYTES;
+  constexpr int BUF = R_OFF + RECB;           // one buffer
+  static_assert(KRB == 128 || KRB == 256, "dk must be 64 or 128");
+  static_assert(!AUG || DK % NCOLS == 0, "identity/value columns must not share a workgroup");
+
+  __shared__ __align__(1024) uint8_t lds[2 * BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gq = lane >> 4, ln = lane & 15;
+  int cg, unit;
+  decode_wg_dma(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
+  const int bh = unit / a.nseg, seg = unit - bh * a.nseg;
+  const int H = a.H, T = a.T, DV = a.DV;
+  const int b = bh / H, h = bh - b * H;
+  const int col0 = cg * NCOLS;
+  const int col = col0 + 16 * w + ln;
+  const bool ident = AUG && col0 < DK;
+  const int vcol0 = AUG ? col0 - DK : col0;
+  const int vcol = vcol0 + 16 * w + ln;
+  const int c_begin = seg * a.seg_chunks;
+  const int c_end = min(a.nc, c_begin + a.seg_chunks);
+
+  const int rowK = H * DK * 2, rowV = H * DV * 2, rowO = H * DV * 4;
+  const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
+  const uint8_t* qb_ = static_cast<const uint8_t*>(a.q) + static_cast<size_t>(b) * T * rowK;
+  const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
+  uint8_t* ob_ = reinterpret_cast<uint8_t*>(a.out) + static_cast<size_t>(b) * T * rowO;
+
+  // per-lane source offsets of the DMA blocks (chunk-relative); rows land swizzled
+  constexpr int KPR = KRB / 16, KRPB = 1024 / KRB;  // pieces per key row, key rows per block
+  constexpr int VPR = VRB / 16, VRPB = 1024 / VRB;
+  auto k_src = [&](int blk) __attribute__((always_inline)) {
+    const int row = blk * KRPB + lane / KPR;
+    return row * rowK + h * DK * 2 + 16 * ((lane % KPR) ^ swz<KRB>(row));
+  };
+  auto v_src = [&](int blk) __attribute__((always_inline)) {
+    const int row = blk * VRPB + lane / VPR;
+    return row * rowV + (h * DV + vcol0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row));
+  };
+
+  auto issue_dma = [&](int c, int bi) __attribute__((always_inline)) {
+    uint8_t* B = lds + bi * BUF;
+    const int t0 = c * CHUNK;
+    const long long rem = static_cast<long long>(T - t0);
+    const rsrc_t rk = make_rsrc(kb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
+#pragma unroll
+    for (int m = w; m < KBYTES / 1024; m += 4) dma16(rk, B + K_OFF + 1024 * m, k_src(m));
+    if constexpr (WITH_OUT) {
+      const rsrc_t rq = make_rsrc(qb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
+#pragma unroll
+      for (int m = w; m < KBYTES / 1024; m += 4) dma16(rq, B + Q_OFF + 1024 * m, k_src(m));
+    }
+    if (!ident) {
+      const rsrc_t rv = make_rsrc(vb_ + static_cast<size_t>(t0) * rowV, rem * rowV);
+#pragma unroll
+      for (int m = w; m < VBYTES / 1024; m += 4) dma16(rv, B + V_OFF + 1024 * m, v_src(m));
+    }
+    const rsrc_t rr = make_rsrc(a.rec + (static_cast<size_t>(bh) * a.nc + c) * REC_BYTES, REC_BYTES);
+#pragma unroll
+    for (int m = w; m < RECB / 1024; m += 4) {
+      const bool p_block = m >= REC_P_OFF / 1024 && m < REC_EG_OFF / 1024;
+      if (WITH_OUT || !p_block) dma16(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
+    }
+  };
+
+  // start state
+  f32x4 S[DK / 16];
+#pragma unroll
+  for (int mt = 0; mt < DK / 16; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mt + 4 * gq + i;
+      float s0 = 0.f;
+      if constexpr (AUG) {
+        s0 = (ident && r == col) ? 1.f : 0.f;
+      } else {
+        if (a.init) s0 = a.init[(static_cast<size_t>(bh) * a.init_segs + seg) * DK * DV + r * DV + col];
+      }
+      S[mt][i] = s0;
+    }
+  }
+
+  int bi = 0;
+  if (c_begin < c_end) issue_dma(c_begin, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  __syncthreads();
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int t0 = c * CHUNK;
+    if (c + 1 < c_end) issue_dma(c + 1, bi ^ 1);
+    const uint8_t* B = lds + bi * BUF;
+    const uint8_t* sK = B + K_OFF;
+    const uint8_t* sQ = B + Q_OFF;
+    const uint8_t* sV = B + V_OFF;
+    const uint8_t* sR = B + R_OFF;
+    const float* sEG = reinterpret_cast<const float*>(sR + REC_EG_OFF);
+    const float* sEGC = reinterpret_cast<const float*>(sR + REC_EGC_OFF);
+
+    // ---- S as B operand ----
+    S8 Sb[DK / 32];
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) Sb[kb] = split8(frag_from_acc(S[2 * kb], S[2 * kb + 1]));
+
+    // ---- R = V - diag(e^g) K S ----
+    f32x4 Rr[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, frag_rows<KRB>(sK, 16 * mt, 32 * kb, lane), Sb[kb]);
+      const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + 16 * mt + 4 * gq);
+      f32x4 vv = zero4();
+      if (!ident) {
+        const u32x2 x = tr_rows4<VRB>(sV, 16 * mt, 16 * w, lane);
+        vv[0] = __uint_as_float(x[0] << 16);
+        vv[1] = __uint_as_float(x[0] & 0xFFFF0000u);
+        vv[2] = __uint_as_float(x[1] << 16);
+        vv[3] = __uint_as_float(x[1] & 0xFFFF0000u);
+      }
+      Rr[mt] = vv - eg * acc;
+    }
+    S8 Rb[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) Rb[kb] = split8(frag_from_acc(Rr[2 * kb], Rr[2 * kb + 1]));
+
+    // ---- U = T' R (lower triangular: rows 0..31 need only tokens 0..31) ----
+    f32x4 U[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      U[mt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], frag_rec(sR + REC_T_OFF, 16 * mt, 32 * kb, lane), Rb[kb]);
+    }
+
+    // ---- O = diag(e^g) Q S + P U ----
+    if constexpr (WITH_OUT) {
+      S8 Ub[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) Ub[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
+      const rsrc_t ro = make_rsrc(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
+      const int obase = 4 * gq * rowO + (h * DV + vcol) * 4;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, frag_rows<KRB>(sQ, 16 * mt, 32 * kb, lane), Sb[kb]);
+        acc *= *reinterpret_cast<const f32x4*>(sEG + 16 * mt + 4 * gq);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, frag_rec(sR + REC_P_OFF, 16 * mt, 32 * kb, lane), Ub[kb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bstore_f32(acc[i], ro, obase + (16 * mt + i) * rowO);
+      }
+    }
+
+    // ---- S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
+    const float gC = sEG[CHUNK - 1];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) U[mt] *= *reinterpret_cast<const f32x4*>(sEGC + 16 * mt + 4 * gq);
+    S8 Ud[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) Ud[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
+#pragma unroll
+    for (int mt = 0; mt < DK / 16; ++mt) {
+      S[mt] *= gC;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], frag_cols<KRB>(sK, 16 * mt, 32 * kb, lane), Ud[kb]);
+    }
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies for chunk c+1 have landed
+    __syncthreads();                     // ... and every wave's; all reads of this buffer are done
+    bi ^= 1;
+  }
+
+  if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
+    float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
+#pragma unroll
+    for (int mt = 0; mt < DK / 16; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) F[(16 * mt + 4 * gq + i) * a.fin_ld + col] = S[mt][i];
+    }
+  }
+}
+
+template <int DK, bool WITH_OUT, bool AUG>
+static hipError_t launch_dma_t(int nwg, const StateDmaArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((state_dma_kernel<DK, WITH_OUT, AUG>), dim3(nwg), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 64 || dk == 128); }
+
+hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
+                            const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
+                            int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
+                            int ncg, int nseg, hipStream_t stream) {
+  const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, seg_chunks, init, init_segs, out, fin, fin_ld, fin_segs,
+                       fin_last_only, ncg, nseg};
+  if (dk == 64) {
+    if (with_out) return launch_dma_t<64, true, false>(nwg, a, stream);
+    if (aug) return launch_dma_t<64, false, true>(nwg, a, stream);
+  } else if (dk == 128) {
+    if (with_out) return launch_dma_t<128, true, false>(nwg, a, stream);
+    if (aug) return launch_dma_t<128, false, true>(nwg, a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kla
