@@ -24,6 +24,7 @@ namespace kla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 // Raw 16- and 8-byte vectors. Native vector types (not the uint4 struct) keep register
 // copies out of memory: a conditional struct copy lowers to a select of addresses.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -130,13 +131,21 @@ __device__ __forceinline__ F8 frag_from_acc(const f32x4& a, const f32x4& b) {
 }
 
 __device__ __forceinline__ S8 split8(const F8& x) {
-  S8 s;
+  // hi = round-to-nearest-even bf16 of x; lo = bf16 of the exact residual x - hi.
+  // Vector conversions make the compiler pair values into v_cvt_pk_bf16_f32.
+  f32x8 v;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    __bf16 h = static_cast<__bf16>(x.v[j]);  // round to nearest even
-    s.h[j] = h;
-    s.l[j] = static_cast<__bf16>(x.v[j] - static_cast<float>(h));  // exact residual, rounded
+  for (int j = 0; j < 8; ++j) v[j] = x.v[j];
+  S8 s;
+  s.h = __builtin_convertvector(v, bf16x8);
+  const u32x4 hw = __builtin_bit_cast(u32x4, s.h);
+  f32x8 hf;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    hf[2 * m] = __uint_as_float(hw[m] << 16);
+    hf[2 * m + 1] = __uint_as_float(hw[m] & 0xFFFF0000u);
   }
+  s.l = __builtin_convertvector(v - hf, bf16x8);
   return s;
 }
 

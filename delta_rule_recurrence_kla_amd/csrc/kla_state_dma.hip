@@ -121,7 +121,11 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   static_assert(KRB == 128 || KRB == 256, "dk must be 64 or 128");
   static_assert(!AUG || DK % NCOLS == 0, "identity/value columns must not share a workgroup");
 
-  __shared__ __align__(1024) uint8_t lds[2 * BUF];
+  // Two separate buffers (not one array indexed by parity): the compiler must see that the
+  // copies into one buffer cannot alias the reads of the other, or it waits for the copies
+  // before the first read and the overlap is lost.
+  __shared__ __align__(1024) uint8_t lds0[BUF];
+  __shared__ __align__(1024) uint8_t lds1[BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, ln = lane & 15;
@@ -156,8 +160,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     return row * rowV + (h * DV + vcol0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row));
   };
 
-  auto issue_dma = [&](int c, int bi) __attribute__((always_inline)) {
-    uint8_t* B = lds + bi * BUF;
+  auto issue_dma = [&](int c, uint8_t* B) __attribute__((always_inline)) {
     const int t0 = c * CHUNK;
     const long long rem = static_cast<long long>(T - t0);
     const rsrc_t rk = make_rsrc(kb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
@@ -198,15 +201,10 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     }
   }
 
-  int bi = 0;
-  if (c_begin < c_end) issue_dma(c_begin, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-  __syncthreads();
-
-  for (int c = c_begin; c < c_end; ++c) {
+  // one chunk computed from buffer B while chunk c+1 is copied into buffer D
+  auto chunk = [&](int c, const uint8_t* B, uint8_t* D) __attribute__((always_inline)) {
     const int t0 = c * CHUNK;
-    if (c + 1 < c_end) issue_dma(c + 1, bi ^ 1);
-    const uint8_t* B = lds + bi * BUF;
+    if (c + 1 < c_end) issue_dma(c + 1, D);
     const uint8_t* sK = B + K_OFF;
     const uint8_t* sQ = B + Q_OFF;
     const uint8_t* sV = B + V_OFF;
@@ -287,8 +285,15 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies for chunk c+1 have landed
-    __syncthreads();                     // ... and every wave's; all reads of this buffer are done
-    bi ^= 1;
+    __syncthreads();                     // ... and every wave's; all reads of buffer B are done
+  };
+
+  if (c_begin < c_end) issue_dma(c_begin, lds0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+  __syncthreads();
+  for (int c = c_begin; c < c_end; c += 2) {
+    chunk(c, lds0, lds1);
+    if (c + 1 < c_end) chunk(c + 1, lds1, lds0);
   }
 
   if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
