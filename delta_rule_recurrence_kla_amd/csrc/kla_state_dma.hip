@@ -15,7 +15,12 @@
 //  * rows land in the swizzled layout of kla_device.h: the DMA picks, per lane, the
 //    source piece that belongs at its fixed destination;
 //  * K^T operands and the accumulator-layout view of V come from transposed LDS reads
-//    (ds_read_b64_tr_b16) of the row-major rows, so no transposed copies are built.
+//    (ds_read_b64_tr_b16) of the row-major rows, so no transposed copies are built;
+//  * rows of every 64-row tile (tokens, and state rows) are taken in the permuted order
+//    tok(m, r) = 32(m >> 1) + 8(r >> 2) + 4(m & 1) + (r & 3) for MFMA tile m, tile row r.
+//    An accumulator pair (tiles 2a, 2a + 1) then gives each lane eight consecutive
+//    indices 32a + 8(lane >> 4) + 0..7 as the contraction slots of the next product, so
+//    every row-major operand fragment is one contiguous 16-byte LDS read.
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -45,46 +50,9 @@ struct StateDmaArgs {
 
 namespace {
 
-// Transposed read: with X a row-major bf16 matrix of RB-byte swizzled rows, lane (gq, ln)
-// receives X[r0 + 4gq + j][c0 + ln] for j = 0..3 (c0 a multiple of 16 elements).
-template <int RB>
-__device__ __forceinline__ u32x2 tr_rows4(const uint8_t* X, int r0, int c0, int lane) {
-  const int gq = lane >> 4, ln = lane & 15;
-  const int off = swz_off<RB>(r0 + 4 * gq + (ln >> 2), 2 * (c0 + 4 * (ln & 3)));
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + off));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-// MFMA operand fragment of a row-major bf16 matrix: row row0 + ln, contraction columns
-// k0 + kslot(gq, 0..7).
-template <int RB>
-__device__ __forceinline__ bf16x8 frag_rows(const uint8_t* X, int row0, int k0, int lane) {
-  const int row = row0 + (lane & 15), byte = 2 * (k0 + 4 * (lane >> 4));
-  const u32x2 a = *reinterpret_cast<const u32x2*>(X + swz_off<RB>(row, byte));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(X + swz_off<RB>(row, byte + 32));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
-}
-
-// MFMA operand fragment of the transpose of a row-major bf16 matrix: element
-// [m = m0 + ln][k = k0 + kslot(gq, j)] = X[k][m].
-template <int RB>
-__device__ __forceinline__ bf16x8 frag_cols(const uint8_t* X, int m0, int k0, int lane) {
-  const u32x2 a = tr_rows4<RB>(X, k0, m0, lane);
-  const u32x2 b = tr_rows4<RB>(X, k0 + 16, m0, lane);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
-}
-
-// Derived (hi + lo) operand fragment of a 64 x 64 record matrix (256-byte swizzled rows).
-__device__ __forceinline__ S8 frag_rec(const uint8_t* M, int row0, int k0, int lane) {
-  const int row = row0 + (lane & 15), byte = 2 * (k0 + 4 * (lane >> 4));
-  const u32x2 a = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte));
-  const u32x2 b = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte + 32));
-  const u32x2 c = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte + 128));
-  const u32x2 d = *reinterpret_cast<const u32x2*>(M + swz_off<256>(row, byte + 160));
-  S8 r;
-  r.h = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3));
-  r.l = __builtin_bit_cast(bf16x8, __builtin_shufflevector(c, d, 0, 1, 2, 3));
-  return r;
+// Row of 64-row tile block m (16-row MFMA tile m of four) taken by tile row r.
+__device__ __forceinline__ int tok(int m, int r) {
+  return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
 }
 
 __device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds_dst, int voff) {
@@ -148,16 +116,66 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
   uint8_t* ob_ = reinterpret_cast<uint8_t*>(a.out) + static_cast<size_t>(b) * T * rowO;
 
-  // per-lane source offsets of the DMA blocks (chunk-relative); rows land swizzled
+  // per-lane source offsets of this wave's DMA blocks (chunk-relative; blocks w, w + 4, ...);
+  // rows land swizzled
   constexpr int KPR = KRB / 16, KRPB = 1024 / KRB;  // pieces per key row, key rows per block
   constexpr int VPR = VRB / 16, VRPB = 1024 / VRB;
-  auto k_src = [&](int blk) __attribute__((always_inline)) {
-    const int row = blk * KRPB + lane / KPR;
-    return row * rowK + h * DK * 2 + 16 * ((lane % KPR) ^ swz<KRB>(row));
+  constexpr int NKB = KBYTES / 4096, NVB = VBYTES / 4096;  // blocks per wave
+  int kS[NKB], vS[NVB];
+#pragma unroll
+  for (int i = 0; i < NKB; ++i) {
+    const int row = (w + 4 * i) * KRPB + lane / KPR;
+    kS[i] = row * rowK + h * DK * 2 + 16 * ((lane % KPR) ^ swz<KRB>(row));
+  }
+#pragma unroll
+  for (int i = 0; i < NVB; ++i) {
+    const int row = (w + 4 * i) * VRPB + lane / VPR;
+    vS[i] = row * rowV + (h * DV + vcol0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row));
+  }
+
+  // Per-lane LDS offsets of the operand reads. Both swizzles ignore row bits 2 and 5, the
+  // bits that a tile index adds to a permuted row (tok(m, r) = tok(0, r) + 32(m >> 1) +
+  // 4(m & 1)), so every read below is one of these lane offsets plus a constant.
+  int oK[DK / 32], oT[DK / 32], oR[2][2];
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb) {
+    oK[kb] = swz_off<KRB>(tok(0, ln), 64 * kb + 16 * gq);                   // K, Q rows
+    oT[kb] = swz_off<KRB>(8 * gq + (ln >> 2), 2 * (32 * kb + 8 * (ln & 3)));  // K^T blocks
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) oR[kb][hl] = swz_off<256>(tok(0, ln), 128 * hl + 64 * kb + 16 * gq);
+  }
+  const int oV = swz_off<VRB>(8 * gq + (ln >> 2), 2 * (16 * w + 4 * (ln & 3)));
+  auto mrow = [](int m) { return 32 * (m >> 1) + 4 * (m & 1); };
+
+  // Operand fragments. ds_read_b64_tr_b16: lane (gq, ln) supplies the address of an 8-byte
+  // block and receives, for j = 0..3, element (ln & 3) of the block of lane 4j + (ln >> 2)
+  // of its 16-lane group.
+  //  fragK:  row tok(m, ln) of K or Q, contraction columns 32 kb + 8 gq + 0..7 (one 16-byte read)
+  //  fragKT: element [tok(m, ln)][32 kb + 8 gq + j] = K[32 kb + 8 gq + j][tok(m, ln)]
+  //          (lane blocks: row 32 kb + 8 gq + (ln >> 2) (+4), columns 32(m >> 1) + 8(ln & 3) + 4(m & 1))
+  //  fragR:  hi and lo halves of record row tok(m, ln), columns 32 kb + 8 gq + 0..7
+  //  trV:    lane (gq, ln) gets V[tok(m, 4 gq + j)][16 w + ln], j = 0..3 (accumulator layout)
+  auto fragK = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oK[kb] + mrow(m) * KRB));
   };
-  auto v_src = [&](int blk) __attribute__((always_inline)) {
-    const int row = blk * VRPB + lane / VPR;
-    return row * rowV + (h * DV + vcol0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row));
+  auto fragKT = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    const uint8_t* p = X + oT[m >> 1] + 32 * kb * KRB + 8 * (m & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * KRB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto fragR = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    S8 r;
+    r.h = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oR[kb][0] + mrow(m) * 256));
+    r.l = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oR[kb][1] + mrow(m) * 256));
+    return r;
+  };
+  auto trV = [&](const uint8_t* X, int m) __attribute__((always_inline)) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + oV + mrow(m) * VRB));
+    return __builtin_bit_cast(u32x2, v);
   };
 
   auto issue_dma = [&](int c, uint8_t* B) __attribute__((always_inline)) {
@@ -165,16 +183,16 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     const long long rem = static_cast<long long>(T - t0);
     const rsrc_t rk = make_rsrc(kb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
 #pragma unroll
-    for (int m = w; m < KBYTES / 1024; m += 4) dma16(rk, B + K_OFF + 1024 * m, k_src(m));
+    for (int i = 0; i < NKB; ++i) dma16(rk, B + K_OFF + 1024 * (w + 4 * i), kS[i]);
     if constexpr (WITH_OUT) {
       const rsrc_t rq = make_rsrc(qb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
 #pragma unroll
-      for (int m = w; m < KBYTES / 1024; m += 4) dma16(rq, B + Q_OFF + 1024 * m, k_src(m));
+      for (int i = 0; i < NKB; ++i) dma16(rq, B + Q_OFF + 1024 * (w + 4 * i), kS[i]);
     }
     if (!ident) {
       const rsrc_t rv = make_rsrc(vb_ + static_cast<size_t>(t0) * rowV, rem * rowV);
 #pragma unroll
-      for (int m = w; m < VBYTES / 1024; m += 4) dma16(rv, B + V_OFF + 1024 * m, v_src(m));
+      for (int i = 0; i < NVB; ++i) dma16(rv, B + V_OFF + 1024 * (w + 4 * i), vS[i]);
     }
     const rsrc_t rr = make_rsrc(a.rec + (static_cast<size_t>(bh) * a.nc + c) * REC_BYTES, REC_BYTES);
 #pragma unroll
@@ -190,7 +208,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   for (int mt = 0; mt < DK / 16; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * mt + 4 * gq + i;
+      const int r = tok(mt, 4 * gq + i);
       float s0 = 0.f;
       if constexpr (AUG) {
         s0 = (ident && r == col) ? 1.f : 0.f;
@@ -201,10 +219,27 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     }
   }
 
+  // Output rows of a chunk are stored at the start of the next chunk (or after the last):
+  // vmcnt counts stores as well as the copies, so a store issued just before the
+  // end-of-chunk wait would put its write latency on every chunk.
+  f32x4 Ohold[4];
+  auto store_out = [&](int c) __attribute__((always_inline)) {
+    const int t0 = c * CHUNK;
+    const rsrc_t ro = make_rsrc(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
+    const int obase = (h * DV + vcol) * 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bstore_f32(Ohold[mt][i], ro, obase + (tok(mt, 4 * gq) + i) * rowO);
+    }
+  };
+
   // one chunk computed from buffer B while chunk c+1 is copied into buffer D
   auto chunk = [&](int c, const uint8_t* B, uint8_t* D) __attribute__((always_inline)) {
-    const int t0 = c * CHUNK;
     if (c + 1 < c_end) issue_dma(c + 1, D);
+    if constexpr (WITH_OUT) {
+      if (c > c_begin) store_out(c - 1);
+    }
     const uint8_t* sK = B + K_OFF;
     const uint8_t* sQ = B + Q_OFF;
     const uint8_t* sV = B + V_OFF;
@@ -223,11 +258,11 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     for (int mt = 0; mt < 4; ++mt) {
       f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, frag_rows<KRB>(sK, 16 * mt, 32 * kb, lane), Sb[kb]);
-      const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + 16 * mt + 4 * gq);
+      for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, fragK(sK, mt, kb), Sb[kb]);
+      const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tok(mt, 4 * gq));
       f32x4 vv = zero4();
       if (!ident) {
-        const u32x2 x = tr_rows4<VRB>(sV, 16 * mt, 16 * w, lane);
+        const u32x2 x = trV(sV, mt);
         vv[0] = __uint_as_float(x[0] << 16);
         vv[1] = __uint_as_float(x[0] & 0xFFFF0000u);
         vv[2] = __uint_as_float(x[1] << 16);
@@ -246,7 +281,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       U[mt] = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], frag_rec(sR + REC_T_OFF, 16 * mt, 32 * kb, lane), Rb[kb]);
+        if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], fragR(sR + REC_T_OFF, mt, kb), Rb[kb]);
     }
 
     // ---- O = diag(e^g) Q S + P U ----
@@ -254,26 +289,23 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       S8 Ub[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) Ub[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
-      const rsrc_t ro = make_rsrc(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
-      const int obase = 4 * gq * rowO + (h * DV + vcol) * 4;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, frag_rows<KRB>(sQ, 16 * mt, 32 * kb, lane), Sb[kb]);
-        acc *= *reinterpret_cast<const f32x4*>(sEG + 16 * mt + 4 * gq);
+        for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, fragK(sQ, mt, kb), Sb[kb]);
+        acc *= *reinterpret_cast<const f32x4*>(sEG + tok(mt, 4 * gq));
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, frag_rec(sR + REC_P_OFF, 16 * mt, 32 * kb, lane), Ub[kb]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bstore_f32(acc[i], ro, obase + (16 * mt + i) * rowO);
+          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, fragR(sR + REC_P_OFF, mt, kb), Ub[kb]);
+        Ohold[mt] = acc;
       }
     }
 
     // ---- S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
     const float gC = sEG[CHUNK - 1];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) U[mt] *= *reinterpret_cast<const f32x4*>(sEGC + 16 * mt + 4 * gq);
+    for (int mt = 0; mt < 4; ++mt) U[mt] *= *reinterpret_cast<const f32x4*>(sEGC + tok(mt, 4 * gq));
     S8 Ud[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Ud[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
@@ -281,7 +313,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     for (int mt = 0; mt < DK / 16; ++mt) {
       S[mt] *= gC;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], frag_cols<KRB>(sK, 16 * mt, 32 * kb, lane), Ud[kb]);
+      for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], fragKT(sK, mt, kb), Ud[kb]);
     }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies for chunk c+1 have landed
@@ -295,13 +327,16 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     chunk(c, lds0, lds1);
     if (c + 1 < c_end) chunk(c + 1, lds1, lds0);
   }
+  if constexpr (WITH_OUT) {
+    if (c_begin < c_end) store_out(c_end - 1);
+  }
 
   if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
     float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
 #pragma unroll
     for (int mt = 0; mt < DK / 16; ++mt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) F[(16 * mt + 4 * gq + i) * a.fin_ld + col] = S[mt][i];
+      for (int i = 0; i < 4; ++i) F[(tok(mt, 4 * gq) + i) * a.fin_ld + col] = S[mt][i];
     }
   }
 }
