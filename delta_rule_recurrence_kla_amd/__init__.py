@@ -24,6 +24,7 @@ _lib = None
 
 KLA_OK, KLA_ERR_INVALID_ARG, KLA_ERR_UNSUPPORTED, KLA_ERR_HIP, KLA_ERR_OOM = range(5)
 PATHS = {"auto": 0, "sequential": 1, "scan": 2}
+DTYPES = {"bf16": 0, "f32": 1}
 _PATH_NAMES = {v: k for k, v in PATHS.items()}
 _STATUS_NAMES = {0: "KLA_OK", 1: "KLA_ERR_INVALID_ARG", 2: "KLA_ERR_UNSUPPORTED", 3: "KLA_ERR_HIP", 4: "KLA_ERR_OOM"}
 
@@ -55,7 +56,7 @@ def load():
     lib.kla_chunk_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_f32.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_ex.argtypes = [I, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
-    lib.kla_plan.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(S)]
+    lib.kla_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(S)]
     lib.kla_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_f32.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_plan", "kla_decode_step",
@@ -177,11 +178,11 @@ def decode_step(q, k, v, log_alpha, eta, state, eps: float = 1e-6, out=None, str
 
 
 def plan(B: int, T: int, H: int, dk: int, dv: int, chunk: int = 64, path: str = "auto",
-         segments: int = 0, num_cus: int = 256):
+         segments: int = 0, num_cus: int = 256, dtype: str = "bf16"):
     """Host-only: (path name, segments, workspace bytes) the library would use."""
     lib = load()
     p, s, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
-    _check(lib.kla_plan(B, T, H, dk, dv, chunk, PATHS[path], segments, num_cus,
+    _check(lib.kla_plan(DTYPES[dtype], B, T, H, dk, dv, chunk, PATHS[path], segments, num_cus,
                         ctypes.byref(p), ctypes.byref(s), ctypes.byref(w)))
     return _PATH_NAMES[p.value], s.value, w.value
 

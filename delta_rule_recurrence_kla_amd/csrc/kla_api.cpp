@@ -22,7 +22,6 @@
 namespace {
 
 constexpr int kChunk = 64;
-constexpr int kRecBytes = 33536;  // per-chunk record of the prep kernel (kla_device.h)
 constexpr int kMaxGridYZ = 65535;
 
 thread_local std::string g_err;
@@ -115,7 +114,7 @@ struct Plan {
   size_t rec_off, rec_bytes, maps_off, maps_bytes, starts_off, starts_bytes, total;
 };
 
-Plan make_plan(int B, int T, int H, int dk, int dv, kla_path path, int segments, int cus) {
+Plan make_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, kla_path path, int segments, int cus) {
   Plan p{};
   const int nc = (T + kChunk - 1) / kChunk;
   const long long bh = static_cast<long long>(B) * H;
@@ -169,7 +168,8 @@ Plan make_plan(int B, int T, int H, int dk, int dv, kla_path path, int segments,
   p.segs = segs;
   p.seg_chunks = seg_chunks;
   p.rec_off = 0;
-  p.rec_bytes = align256(static_cast<size_t>(bh) * nc * kRecBytes);
+  const int rec_bytes = kla::record_bytes(dtype == KLA_DTYPE_BF16 ? 0 : 1, dk);  // per chunk
+  p.rec_bytes = align256(static_cast<size_t>(bh) * nc * rec_bytes);
   p.maps_off = p.rec_off + p.rec_bytes;
   p.maps_bytes = chosen == KLA_PATH_SCAN ? align256(static_cast<size_t>(bh) * (segs - 1) * dk * (dk + dv) * 4) : 0;
   p.starts_off = p.maps_off + p.maps_bytes;
@@ -207,7 +207,7 @@ kla_status chunk_fwd_impl(kla_dtype dtype, const void* q, const void* k, const v
     if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
   }
 
-  const Plan p = make_plan(B, T, H, dk, dv, path, segments, device_cus());
+  const Plan p = make_plan(dtype, B, T, H, dk, dv, path, segments, device_cus());
   const kla::Dims d{B, T, H, dk, dv, (T + kChunk - 1) / kChunk};
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
 
@@ -293,16 +293,17 @@ kla_status kla_chunk_fwd_ex(kla_dtype dtype, const void* q, const void* k, const
                         path, segments, stream);
 }
 
-kla_status kla_plan(int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments, int num_cus,
-                    kla_path* chosen_path, int* chosen_segments, size_t* workspace_bytes) {
-  kla_status st = check_prefill_sizes(KLA_DTYPE_BF16, B, T, H, dk, dv, chunk);
+kla_status kla_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
+                    int num_cus, kla_path* chosen_path, int* chosen_segments, size_t* workspace_bytes) {
+  if (dtype != KLA_DTYPE_BF16 && dtype != KLA_DTYPE_F32) return fail(KLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
   if (st != KLA_OK) return st;
   if (path != KLA_PATH_AUTO && path != KLA_PATH_SEQUENTIAL && path != KLA_PATH_SCAN)
     return fail(KLA_ERR_INVALID_ARG, "unknown path %d", (int)path);
   if (segments < 0) return fail(KLA_ERR_INVALID_ARG, "segments must be >= 0");
   const int cus = num_cus > 0 ? num_cus : device_cus();
   Plan p{};
-  if (T > 0) p = make_plan(B, T, H, dk, dv, path, segments, cus);
+  if (T > 0) p = make_plan(dtype, B, T, H, dk, dv, path, segments, cus);
   else p.path = KLA_PATH_SEQUENTIAL, p.segs = 1;
   if (chosen_path) *chosen_path = p.path;
   if (chosen_segments) *chosen_segments = p.segs;

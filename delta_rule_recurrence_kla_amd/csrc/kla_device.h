@@ -49,6 +49,20 @@ constexpr int REC_EGC_OFF = 33024;
 constexpr int REC_G_OFF = 33280;
 constexpr int REC_BYTES = 33536;
 
+// Compact per-chunk record, for the state kernel that forms P itself (bf16, dk <= 128):
+//   [0, 4096)       T' rows 0..31, 128 bytes each: hi of columns 0..31, then lo
+//   [4096, 12288)   T' rows 32..63, 256 bytes each: hi of columns 0..63, then lo
+//   [12288, 13056)  exp(g_r), exp(g_C - g_r), g_r as above
+// T' is lower triangular, so its upper-right 32 x 32 quadrant (zero) is left out. Rows
+// 0..31 are swizzled as 128-byte rows (swz<128>), rows 32..63 as 256-byte rows numbered
+// from 0 (swz<256> of row - 32).
+constexpr int CREC_TOP_OFF = 0;
+constexpr int CREC_BOT_OFF = 4096;
+constexpr int CREC_EG_OFF = 12288;
+constexpr int CREC_EGC_OFF = 12544;
+constexpr int CREC_G_OFF = 12800;
+constexpr int CREC_BYTES = 13056;
+
 // LDS row pitch of a derived 64x64 matrix: 256 bytes of data + 16 bytes of padding.
 constexpr int DROW_BYTES = 272;
 
@@ -67,6 +81,20 @@ constexpr int BUF_OOB = 0x40000000;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long bytes) {
   const int n = bytes <= 0 ? 0 : (bytes >= BUF_OOB ? BUF_OOB - 1 : static_cast<int>(bytes));
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, BUF_FLAGS);
+}
+// The same for a base and size that are uniform across the wave but that the compiler
+// cannot prove uniform (they depend on the wave index): the values are passed through
+// readfirstlane, so the descriptor lives in scalar registers. Without this, every buffer
+// instruction using the descriptor is wrapped in a loop over the distinct values of the
+// wave's lanes (readfirstlane, compare, exec mask), which costs about a hundred cycles per
+// instruction.
+__device__ __forceinline__ rsrc_t make_rsrc_wu(const void* base, long long bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  const int n = bytes <= 0 ? 0 : (bytes >= BUF_OOB ? BUF_OOB - 1 : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(n), BUF_FLAGS);
 }
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);

@@ -37,6 +37,9 @@ hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void*
 
 // DMA-fed state kernel (kla_state_dma.hip): bf16 inputs with dk in {64, 128}.
 bool state_dma_supported(int mode, int dk);
+// Bytes of one chunk record: compact (no P, T' without its zero quadrant) when the DMA-fed
+// state kernel consumes it, else the full record.
+int record_bytes(int mode, int dk);
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,

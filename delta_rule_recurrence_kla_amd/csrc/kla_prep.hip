@@ -10,7 +10,9 @@
 //   T      = (I + A)^-1                            blocked inverse of a unit lower-triangular matrix
 //   T'     = T diag(beta)
 // and stores T', P, e^{g_r}, e^{g_C-g_r} and g_r as the chunk's record (matrix rows in the
-// swizzled LDS layout of kla_device.h).
+// swizzled LDS layout of kla_device.h). The compact variant (COMPACT = true) is for the
+// state kernel that forms P itself: it neither reads Q nor stores P, and stores T' without
+// its zero upper-right quadrant.
 //
 // Why this is the chunk's whole job: writing u_i = beta_i e_i and unrolling the
 // per-token update of the KLA page ("KLA update rule": S_t = S~ + beta_t k_t e_t^T,
@@ -60,7 +62,7 @@ __device__ __forceinline__ F8 a_frag(const float* sA, int I, int C0, int ln, int
 
 }  // namespace
 
-template <int MODE, int DK>
+template <int MODE, int DK, bool COMPACT>
 __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                    const float* __restrict__ log_alpha,
                                                    const float* __restrict__ eta, float eps,
@@ -94,8 +96,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
   const int rowK = H * DK * SZ;
   const size_t chunk_off = (static_cast<size_t>(b) * T + t0) * rowK;
   const long long avail = static_cast<long long>(T - t0) * rowK;
-  const rsrc_t rk = make_rsrc(static_cast<const uint8_t*>(kv) + chunk_off, avail);
-  const rsrc_t rq = make_rsrc(static_cast<const uint8_t*>(qv) + chunk_off, avail);
+  const rsrc_t rk = make_rsrc_wu(static_cast<const uint8_t*>(kv) + chunk_off, avail);
+  const rsrc_t rq = make_rsrc_wu(static_cast<const uint8_t*>(qv) + chunk_off, avail);
   f32x4 G[10], QK[10];
 #pragma unroll
   for (int i = 0; i < 10; ++i) G[i] = QK[i] = zero4();
@@ -109,10 +111,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
       if constexpr (MODE == MODE_BF16) {
         const u32x2 k0 = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
         const u32x2 k1 = __builtin_amdgcn_raw_buffer_load_b64(rk, off + 16 * SZ, 0, 0);
-        const u32x2 q0 = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
-        const u32x2 q1 = __builtin_amdgcn_raw_buffer_load_b64(rq, off + 16 * SZ, 0, 0);
         kf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3));
-        qf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3));
+        if constexpr (!COMPACT) {
+          const u32x2 q0 = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
+          const u32x2 q1 = __builtin_amdgcn_raw_buffer_load_b64(rq, off + 16 * SZ, 0, 0);
+          qf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3));
+        }
       } else {
         const f32x4 k0 = __builtin_bit_cast(f32x4, bload16(rk, off));
         const f32x4 k1 = __builtin_bit_cast(f32x4, bload16(rk, off + 16 * SZ));
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
 #pragma unroll
       for (int nt = 0; nt <= mt; ++nt) {
         G[tix(mt, nt)] = TR::mma_xx(G[tix(mt, nt)], kf[mt], kf[nt]);
-        QK[tix(mt, nt)] = TR::mma_xx(QK[tix(mt, nt)], qf[mt], kf[nt]);
+        if constexpr (!COMPACT) QK[tix(mt, nt)] = TR::mma_xx(QK[tix(mt, nt)], qf[mt], kf[nt]);
       }
     }
   }
@@ -160,23 +164,39 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
   wave_sync();
   sNB[lane] = beta;
   sGv[lane] = g;
-  uint8_t* R = rec + static_cast<size_t>(id) * REC_BYTES;
-  const rsrc_t rr = make_rsrc(R, REC_BYTES);
-  bstore_f32(__expf(g), rr, REC_EG_OFF + 4 * lane);
-  bstore_f32(__expf(gC - g), rr, REC_EGC_OFF + 4 * lane);
-  bstore_f32(g, rr, REC_G_OFF + 4 * lane);
+  constexpr int RB = COMPACT ? CREC_BYTES : REC_BYTES;
+  uint8_t* R = rec + static_cast<size_t>(id) * RB;
+  const rsrc_t rr = make_rsrc_wu(R, RB);
+  bstore_f32(__expf(g), rr, (COMPACT ? CREC_EG_OFF : REC_EG_OFF) + 4 * lane);
+  bstore_f32(__expf(gC - g), rr, (COMPACT ? CREC_EGC_OFF : REC_EGC_OFF) + 4 * lane);
+  bstore_f32(g, rr, (COMPACT ? CREC_G_OFF : REC_G_OFF) + 4 * lane);
   wave_sync();
 
   // Copies the staged strip (16 rows of 256 bytes, pitch 272) to record rows 16*mt .. 16*mt+15 at byte dst.
   auto flush_strip = [&](int dst, int mt) __attribute__((always_inline)) {
     wave_sync();
     const uint8_t* sb = reinterpret_cast<const uint8_t*>(st);
+    if (COMPACT && mt < 2) {
+      // rows 0..31 of the compact T': pieces 0..3 (hi of columns 0..31) and 8..11 (lo)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = lane + 64 * j;  // 16-byte piece: strip row p >> 4, column piece p & 15
-      const u32x4 x = *reinterpret_cast<const u32x4*>(sb + (p >> 4) * 272 + 16 * (p & 15));
-      const int row = 16 * mt + (p >> 4);
-      __builtin_amdgcn_raw_buffer_store_b128(x, rr, dst + swz_off<256>(row, 16 * (p & 15)), 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const int p = lane + 64 * j;  // strip row p >> 3, compact piece p & 7
+        const int cp = p & 7, sp = cp < 4 ? cp : cp + 4;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sb + (p >> 3) * 272 + 16 * sp);
+        const int row = 16 * mt + (p >> 3);
+        __builtin_amdgcn_raw_buffer_store_b128(x, rr, CREC_TOP_OFF + swz_off<128>(row, 16 * cp), 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = lane + 64 * j;  // 16-byte piece: strip row p >> 4, column piece p & 15
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sb + (p >> 4) * 272 + 16 * (p & 15));
+        const int row = 16 * mt + (p >> 4);
+        if constexpr (COMPACT)
+          __builtin_amdgcn_raw_buffer_store_b128(x, rr, CREC_BOT_OFF + swz_off<256>(row - 32, 16 * (p & 15)), 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b128(x, rr, dst + swz_off<256>(row, 16 * (p & 15)), 0, 0);
+      }
     }
     wave_sync();
   };
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
 
   // ---- P = QK masked by the inclusive decay mask -> record ----
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < (COMPACT ? 0 : 4); ++mt) {
     const f32x4 gr = *reinterpret_cast<const f32x4*>(sGv + 16 * mt + 4 * gq);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -301,10 +321,16 @@ template <int MODE, int DK>
 static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, const float* la, const float* eta,
                                 float eps, uint8_t* rec, hipStream_t stream) {
   const int nchunks = d.B * d.H * d.nc;
-  hipLaunchKernelGGL((prep_kernel<MODE, DK>), dim3((nchunks + 3) / 4), dim3(256), 0, stream, q, k, la, eta, eps, rec,
-                     d.T, d.H, d.nc, nchunks);
+  if (state_dma_supported(MODE, DK))
+    hipLaunchKernelGGL((prep_kernel<MODE, DK, true>), dim3((nchunks + 3) / 4), dim3(256), 0, stream, q, k, la, eta, eps,
+                       rec, d.T, d.H, d.nc, nchunks);
+  else
+    hipLaunchKernelGGL((prep_kernel<MODE, DK, false>), dim3((nchunks + 3) / 4), dim3(256), 0, stream, q, k, la, eta,
+                       eps, rec, d.T, d.H, d.nc, nchunks);
   return hipGetLastError();
 }
+
+int record_bytes(int mode, int dk) { return state_dma_supported(mode, dk) ? CREC_BYTES : REC_BYTES; }
 
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
                        const float* eta, float eps, uint8_t* rec, hipStream_t stream) {

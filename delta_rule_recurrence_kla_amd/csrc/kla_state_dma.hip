@@ -16,6 +16,10 @@
 //    source piece that belongs at its fixed destination;
 //  * K^T operands and the accumulator-layout view of V come from transposed LDS reads
 //    (ds_read_b64_tr_b16) of the row-major rows, so no transposed copies are built;
+//  * P = tril(e^{g_r - g_i} Q K^T) is formed here from the Q and K rows already in LDS
+//    (twelve 16 x 16 tiles, three per wave, shared through LDS), so the chunk record
+//    carries only T' (without its zero quadrant) and the gates: 12.75 KB instead of
+//    33.5 KB per chunk, the larger part of what the kernel streams in;
 //  * rows of every 64-row tile (tokens, and state rows) are taken in the permuted order
 //    tok(m, r) = 32(m >> 1) + 8(r >> 2) + 4(m & 1) + (r & 3) for MFMA tile m, tile row r.
 //    An accumulator pair (tiles 2a, 2a + 1) then gives each lane eight consecutive
@@ -27,6 +31,7 @@
 namespace kla {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   constexpr int VRB = NCOLS * 2;              // bytes of a value row (this workgroup's columns)
   constexpr int KBYTES = CHUNK * KRB;
   constexpr int VBYTES = CHUNK * VRB;
-  constexpr int RECB = 33 * 1024;             // record image (33536 bytes) rounded up to whole DMA blocks
+  constexpr int RECB = 13 * 1024;             // compact record (13056 bytes) rounded up to whole DMA blocks
   constexpr int K_OFF = 0;
   constexpr int Q_OFF = K_OFF + KBYTES;
   constexpr int V_OFF = Q_OFF + (WITH_OUT ? KBYTES : 0);
@@ -94,8 +99,10 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   // before the first read and the overlap is lost.
   __shared__ __align__(1024) uint8_t lds0[BUF];
   __shared__ __align__(1024) uint8_t lds1[BUF];
+  __shared__ __align__(1024) uint8_t ldsP[WITH_OUT ? CREC_EG_OFF : 16];  // P of the chunk, compact T' layout
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a scalar
   const int gq = lane >> 4, ln = lane & 15;
   int cg, unit;
   decode_wg_dma(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
@@ -136,16 +143,17 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   // Per-lane LDS offsets of the operand reads. Both swizzles ignore row bits 2 and 5, the
   // bits that a tile index adds to a permuted row (tok(m, r) = tok(0, r) + 32(m >> 1) +
   // 4(m & 1)), so every read below is one of these lane offsets plus a constant.
-  int oK[DK / 32], oT[DK / 32], oR[2][2];
+  int oK[DK / 32], oT[DK / 32], oRt[2], oRb[2][2];
 #pragma unroll
   for (int kb = 0; kb < DK / 32; ++kb) {
     oK[kb] = swz_off<KRB>(tok(0, ln), 64 * kb + 16 * gq);                   // K, Q rows
     oT[kb] = swz_off<KRB>(8 * gq + (ln >> 2), 2 * (32 * kb + 8 * (ln & 3)));  // K^T blocks
   }
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int hl = 0; hl < 2; ++hl) {
+    oRt[hl] = CREC_TOP_OFF + swz_off<128>(tok(0, ln), 64 * hl + 16 * gq);
 #pragma unroll
-    for (int hl = 0; hl < 2; ++hl) oR[kb][hl] = swz_off<256>(tok(0, ln), 128 * hl + 64 * kb + 16 * gq);
+    for (int kb = 0; kb < 2; ++kb) oRb[kb][hl] = CREC_BOT_OFF + swz_off<256>(tok(0, ln), 128 * hl + 64 * kb + 16 * gq);
   }
   const int oV = swz_off<VRB>(8 * gq + (ln >> 2), 2 * (16 * w + 4 * (ln & 3)));
   auto mrow = [](int m) { return 32 * (m >> 1) + 4 * (m & 1); };
@@ -156,7 +164,8 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   //  fragK:  row tok(m, ln) of K or Q, contraction columns 32 kb + 8 gq + 0..7 (one 16-byte read)
   //  fragKT: element [tok(m, ln)][32 kb + 8 gq + j] = K[32 kb + 8 gq + j][tok(m, ln)]
   //          (lane blocks: row 32 kb + 8 gq + (ln >> 2) (+4), columns 32(m >> 1) + 8(ln & 3) + 4(m & 1))
-  //  fragR:  hi and lo halves of record row tok(m, ln), columns 32 kb + 8 gq + 0..7
+  //  fragR:  hi and lo halves of row tok(m, ln) of a lower-triangular matrix in the compact
+  //          record layout (T', or P), columns 32 kb + 8 gq + 0..7 (kb = 0 when m < 2)
   //  trV:    lane (gq, ln) gets V[tok(m, 4 gq + j)][16 w + ln], j = 0..3 (accumulator layout)
   auto fragK = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oK[kb] + mrow(m) * KRB));
@@ -168,9 +177,11 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   auto fragR = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    const uint8_t* p = m < 2 ? X + oRt[0] + 4 * (m & 1) * 128 : X + oRb[kb][0] + 4 * (m & 1) * 256;
+    const int lo = m < 2 ? oRt[1] - oRt[0] : oRb[kb][1] - oRb[kb][0];
     S8 r;
-    r.h = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oR[kb][0] + mrow(m) * 256));
-    r.l = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oR[kb][1] + mrow(m) * 256));
+    r.h = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+    r.l = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + lo));
     return r;
   };
   auto trV = [&](const uint8_t* X, int m) __attribute__((always_inline)) {
@@ -178,28 +189,41 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     return __builtin_bit_cast(u32x2, v);
   };
 
-  auto issue_dma = [&](int c, uint8_t* B) __attribute__((always_inline)) {
+  // Copies of chunk c into buffer B, one 1 KB block per slot. A wave cannot issue past a
+  // memory instruction that the memory pipeline has not yet accepted, and the pipeline of a
+  // CU accepts a 1 KB copy only every few dozen cycles; if all four waves issued their
+  // copies (and output stores) at once, each would wait until the pipeline had taken all
+  // of them. So each wave issues its share at its own point of the chunk (wave w at issue
+  // point w), and the pipeline serves one wave while the other three compute.
+  // Slot order: record blocks w, w+4, w+8, w+12 (those below 13), K blocks, Q blocks, V blocks.
+  constexpr int NSLOT = 4 + NKB + (WITH_OUT ? NKB : 0) + NVB;
+  auto copy_slot = [&](int sl, int c, uint8_t* B) __attribute__((always_inline)) {
     const int t0 = c * CHUNK;
-    const long long rem = static_cast<long long>(T - t0);
-    const rsrc_t rk = make_rsrc(kb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
-#pragma unroll
-    for (int i = 0; i < NKB; ++i) dma16(rk, B + K_OFF + 1024 * (w + 4 * i), kS[i]);
-    if constexpr (WITH_OUT) {
-      const rsrc_t rq = make_rsrc(qb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
-#pragma unroll
-      for (int i = 0; i < NKB; ++i) dma16(rq, B + Q_OFF + 1024 * (w + 4 * i), kS[i]);
+    if (sl < 4) {
+      const int m = wu + 4 * sl;
+      if (m < RECB / 1024) {
+        const rsrc_t rr = make_rsrc_wu(a.rec + (static_cast<size_t>(bh) * a.nc + c) * CREC_BYTES, CREC_BYTES);
+        dma16(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
+      }
+    } else if (sl < 4 + NKB) {
+      const int i = sl - 4;
+      const rsrc_t rk = make_rsrc_wu(kb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
+      dma16(rk, B + K_OFF + 1024 * (wu + 4 * i), kS[i]);
+    } else if (WITH_OUT && sl < 4 + 2 * NKB) {
+      const int i = sl - 4 - NKB;
+      const rsrc_t rq = make_rsrc_wu(qb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
+      dma16(rq, B + Q_OFF + 1024 * (wu + 4 * i), kS[i]);
+    } else if (sl < NSLOT) {
+      const int i = sl - (NSLOT - NVB);
+      if (!ident) {
+        const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV, static_cast<long long>(T - t0) * rowV);
+        dma16(rv, B + V_OFF + 1024 * (wu + 4 * i), vS[i]);
+      }
     }
-    if (!ident) {
-      const rsrc_t rv = make_rsrc(vb_ + static_cast<size_t>(t0) * rowV, rem * rowV);
+  };
+  auto issue_dma = [&](int c, uint8_t* B) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < NVB; ++i) dma16(rv, B + V_OFF + 1024 * (w + 4 * i), vS[i]);
-    }
-    const rsrc_t rr = make_rsrc(a.rec + (static_cast<size_t>(bh) * a.nc + c) * REC_BYTES, REC_BYTES);
-#pragma unroll
-    for (int m = w; m < RECB / 1024; m += 4) {
-      const bool p_block = m >= REC_P_OFF / 1024 && m < REC_EG_OFF / 1024;
-      if (WITH_OUT || !p_block) dma16(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
-    }
+    for (int sl = 0; sl < NSLOT; ++sl) copy_slot(sl, c, B);
   };
 
   // start state
@@ -219,33 +243,89 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     }
   }
 
-  // Output rows of a chunk are stored at the start of the next chunk (or after the last):
-  // vmcnt counts stores as well as the copies, so a store issued just before the
-  // end-of-chunk wait would put its write latency on every chunk.
+  // The output is computed transposed: tile mt of O^T holds, in lane (gq, ln), token
+  // tok(mt, ln) and this wave's columns 16 w + 4 gq + 0..3, stored as one 16-byte write.
+  // A chunk's output is stored during the next chunk (or after the last): vmcnt counts
+  // stores as well as the copies, so a store issued just before the end-of-chunk wait
+  // would put its write latency on every chunk.
   f32x4 Ohold[4];
-  auto store_out = [&](int c) __attribute__((always_inline)) {
+  auto store_out = [&](int c, int mt) __attribute__((always_inline)) {
     const int t0 = c * CHUNK;
-    const rsrc_t ro = make_rsrc(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
-    const int obase = (h * DV + vcol) * 4;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bstore_f32(Ohold[mt][i], ro, obase + (tok(mt, 4 * gq) + i) * rowO);
-    }
+    const rsrc_t ro = make_rsrc_wu(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
+    const int obase = (h * DV + vcol0 + 16 * w + 4 * gq) * 4;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Ohold[mt]), ro, obase + tok(mt, ln) * rowO, 0, 0);
   };
 
   // one chunk computed from buffer B while chunk c+1 is copied into buffer D
   auto chunk = [&](int c, const uint8_t* B, uint8_t* D) __attribute__((always_inline)) {
-    if (c + 1 < c_end) issue_dma(c + 1, D);
-    if constexpr (WITH_OUT) {
-      if (c > c_begin) store_out(c - 1);
-    }
+    const bool more = c + 1 < c_end;
+    // issue point pt: the wave with w == pt issues its copies of chunk c+1 and stores its
+    // output of chunk c-1
+    auto issue_point = [&](int pt) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (wu == pt) {
+        if (more) {
+#pragma unroll
+          for (int sl = 0; sl < NSLOT; ++sl) copy_slot(sl, c + 1, D);
+        }
+        if constexpr (WITH_OUT) {
+          if (c > c_begin) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) store_out(c - 1, mt);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    issue_point(0);
     const uint8_t* sK = B + K_OFF;
     const uint8_t* sQ = B + Q_OFF;
     const uint8_t* sV = B + V_OFF;
     const uint8_t* sR = B + R_OFF;
-    const float* sEG = reinterpret_cast<const float*>(sR + REC_EG_OFF);
-    const float* sEGC = reinterpret_cast<const float*>(sR + REC_EGC_OFF);
+    const float* sEG = reinterpret_cast<const float*>(sR + CREC_EG_OFF);
+    const float* sEGC = reinterpret_cast<const float*>(sR + CREC_EGC_OFF);
+
+    // ---- P = tril(e^{g_r - g_i} Q K^T) into ldsP (rows r = query tokens, columns i = key tokens) ----
+    // Twelve 16 x 16 tiles pair key tile mi with query tile mj (permuted token order) where
+    // the half of mi does not exceed the half of mj; wave w computes three of them. A tile is
+    // D = K_mi Q_mj^T, so a lane holds four consecutive key tokens of one query token and
+    // writes 8 bytes of hi and 8 of lo. The products and the mask are those of the full
+    // record's P: fp32 sums of exact bf16 products, then e^{min(g_r - g_i, 0)} for i <= r.
+    if constexpr (WITH_OUT) {
+      const float* sG = reinterpret_cast<const float*>(sR + CREC_G_OFF);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int mi = (w >> 1) + (j == 2 ? 2 : 0), mj = (w & 1) + (j >= 1 ? 2 : 0);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) acc = mfma_bf16(fragK(sK, mi, kb), fragK(sQ, mj, kb), acc);
+        const int r = tok(mj, ln), i0 = tok(mi, 4 * gq);
+        const float gr = sG[r];
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = i0 + e <= r ? __expf(fminf(gr - gi[e], 0.f)) * acc[e] : 0.f;
+        const bf16x4 ph = __builtin_convertvector(pv, bf16x4);
+        const u32x2 hw = __builtin_bit_cast(u32x2, ph);
+        f32x4 hf;
+        hf[0] = __uint_as_float(hw[0] << 16);
+        hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
+        hf[2] = __uint_as_float(hw[1] << 16);
+        hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
+        const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv - hf, bf16x4));
+        int oh, ol;
+        if (mj < 2) {
+          oh = CREC_TOP_OFF + swz_off<128>(r, 2 * i0);
+          ol = CREC_TOP_OFF + swz_off<128>(r, 64 + 2 * i0);
+        } else {
+          oh = CREC_BOT_OFF + swz_off<256>(r - 32, 2 * i0);
+          ol = CREC_BOT_OFF + swz_off<256>(r - 32, 128 + 2 * i0);
+        }
+        *reinterpret_cast<u32x2*>(ldsP + oh) = hw;
+        *reinterpret_cast<u32x2*>(ldsP + ol) = lw;
+      }
+    }
+    if constexpr (WITH_OUT) issue_point(1);
 
     // ---- S as B operand ----
     S8 Sb[DK / 32];
@@ -269,7 +349,9 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
         vv[3] = __uint_as_float(x[1] & 0xFFFF0000u);
       }
       Rr[mt] = vv - eg * acc;
+      if (mt == 1) issue_point(WITH_OUT ? 2 : 1);
     }
+    issue_point(WITH_OUT ? 3 : 2);
     S8 Rb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Rb[kb] = split8(frag_from_acc(Rr[2 * kb], Rr[2 * kb + 1]));
@@ -281,23 +363,33 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       U[mt] = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], fragR(sR + REC_T_OFF, mt, kb), Rb[kb]);
+        if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], fragR(sR, mt, kb), Rb[kb]);
+      if (!WITH_OUT && mt == 1) issue_point(3);
     }
 
     // ---- O = diag(e^g) Q S + P U ----
     if constexpr (WITH_OUT) {
+      // every wave's tiles of P are in LDS (an LDS-only barrier: the copies of chunk c+1
+      // stay in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       S8 Ub[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) Ub[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
+      // O^T = S^T Q^T (times e^g per token) + U^T P^T: the same fragments as O = Q S + P U
+      // with the two operands of every product exchanged
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, fragK(sQ, mt, kb), Sb[kb]);
-        acc *= *reinterpret_cast<const f32x4*>(sEG + tok(mt, 4 * gq));
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const bf16x8 qf = fragK(sQ, mt, kb);
+          acc = mfma_bf16(Sb[kb].h, qf, acc);
+          acc = mfma_bf16(Sb[kb].l, qf, acc);
+        }
+        acc *= sEG[tok(mt, ln)];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, fragR(sR + REC_P_OFF, mt, kb), Ub[kb]);
+          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
         Ohold[mt] = acc;
       }
     }
@@ -328,7 +420,10 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     if (c + 1 < c_end) chunk(c + 1, lds1, lds0);
   }
   if constexpr (WITH_OUT) {
-    if (c_begin < c_end) store_out(c_end - 1);
+    if (c_begin < c_end) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) store_out(c_end - 1, mt);
+    }
   }
 
   if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {

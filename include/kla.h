@@ -105,13 +105,14 @@ kla_status kla_chunk_fwd_ex(kla_dtype dtype, const void* q, const void* k, const
 
 /*
  * Host-only planning query: which path and segment count kla_chunk_fwd_ex would
- * use for these sizes, and the workspace bytes it would allocate. `num_cus` is
- * the compute-unit count to plan for (0 = ask the current HIP device, 256 if
- * there is none). Makes no allocation and enqueues nothing.
+ * use for these sizes and input dtype, and the workspace bytes it would allocate
+ * (the per-chunk record is smaller for bf16 with dk <= 128). `num_cus` is the
+ * compute-unit count to plan for (0 = ask the current HIP device, 256 if there is
+ * none). Makes no allocation and enqueues nothing.
  */
-kla_status kla_plan(int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
-                    int num_cus, kla_path* chosen_path, int* chosen_segments,
-                    size_t* workspace_bytes);
+kla_status kla_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk,
+                    kla_path path, int segments, int num_cus, kla_path* chosen_path,
+                    int* chosen_segments, size_t* workspace_bytes);
 
 /*
  * One recurrent decode step for N x H states, updated in place (KLA page,

@@ -92,7 +92,8 @@ def test_plan_paths():
     # 0.4B-LM-shaped layer: B*H = 128 heads x 2 column groups fill 256 CUs -> sequential
     p, s, w = kla.plan(8, 4096, 16, 128, 128, num_cus=256)
     assert p == "sequential" and s == 1
-    assert w >= 8 * 16 * 64 * 33536
+    assert w >= 8 * 16 * 64 * 13056                      # compact bf16 record
+    assert kla.plan(8, 4096, 16, 128, 128, num_cus=256, dtype="f32")[2] >= 8 * 16 * 64 * 33536
     # long context with 16 heads under-fills the chip -> scan with several segments
     p, s, w = kla.plan(1, 131072, 16, 128, 128, num_cus=256)
     assert p == "scan" and 4 <= s <= 64
@@ -107,10 +108,13 @@ def test_plan_paths():
     assert kla.plan(2, 0, 2, 64, 64, num_cus=256)[1:] == (1, 0)
 
 
-def test_plan_workspace_bytes():
-    _, s, w = kla.plan(1, 64 * 10, 2, 128, 64, path="scan", segments=5, num_cus=256)
-    rec = 2 * 10 * 33536
-    maps = 2 * 4 * 128 * (128 + 64) * 4
-    starts = 2 * 5 * 128 * 64 * 4
+@pytest.mark.parametrize("dtype,dk,rec_bytes", [("bf16", 128, 13056), ("bf16", 256, 33536), ("f32", 128, 33536)])
+def test_plan_workspace_bytes(dtype, dk, rec_bytes):
+    """Workspace = chunk records + segment maps + segment start states, each 256-byte aligned.
+    bf16 with dk <= 128 uses the compact record (no P, T' without its zero quadrant)."""
+    _, s, w = kla.plan(1, 64 * 10, 2, dk, 64, path="scan", segments=5, num_cus=256, dtype=dtype)
+    rec = 2 * 10 * rec_bytes
+    maps = 2 * 4 * dk * (dk + 64) * 4
+    starts = 2 * 5 * dk * 64 * 4
     up = lambda x: (x + 255) // 256 * 256
     assert w == up(rec) + up(maps) + up(starts)
