@@ -259,11 +259,15 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   // one chunk computed from buffer B while chunk c+1 is copied into buffer D
   auto chunk = [&](int c, const uint8_t* B, uint8_t* D) __attribute__((always_inline)) {
     const bool more = c + 1 < c_end;
-    // issue point pt: the wave with w == pt issues its copies of chunk c+1 and stores its
-    // output of chunk c-1
+    // Issue points: START (chunk start), R_MID (after R tile 1), R_END (after R), U_MID (after
+    // U tile 1). At its point a wave issues its copies of chunk c+1 and stores its output of
+    // chunk c-1. With output: waves 0 and 1 at START, 2 at R_MID, 3 at R_END (no point
+    // separates the P tiles from R, so the two interleave). Without: wave w at point w.
+    enum { START = 0, R_MID = 1, R_END = 2, U_MID = 3 };
+    const int my_point = WITH_OUT ? (wu <= 1 ? START : wu == 2 ? R_MID : R_END) : wu;
     auto issue_point = [&](int pt) __attribute__((always_inline)) {
       __builtin_amdgcn_sched_barrier(0);
-      if (wu == pt) {
+      if (my_point == pt) {
         if (more) {
 #pragma unroll
           for (int sl = 0; sl < NSLOT; ++sl) copy_slot(sl, c + 1, D);
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    issue_point(0);
+    issue_point(START);
     const uint8_t* sK = B + K_OFF;
     const uint8_t* sQ = B + Q_OFF;
     const uint8_t* sV = B + V_OFF;
@@ -287,45 +291,42 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
 
     // ---- P = tril(e^{g_r - g_i} Q K^T) into ldsP (rows r = query tokens, columns i = key tokens) ----
     // Twelve 16 x 16 tiles pair key tile mi with query tile mj (permuted token order) where
-    // the half of mi does not exceed the half of mj; wave w computes three of them. A tile is
-    // D = K_mi Q_mj^T, so a lane holds four consecutive key tokens of one query token and
-    // writes 8 bytes of hi and 8 of lo. The products and the mask are those of the full
-    // record's P: fp32 sums of exact bf16 products, then e^{min(g_r - g_i, 0)} for i <= r.
-    if constexpr (WITH_OUT) {
-      const float* sG = reinterpret_cast<const float*>(sR + CREC_G_OFF);
+    // the half of mi does not exceed the half of mj; wave w computes three of them (tile j
+    // right after R tile j, so that the two interleave). A tile is D = K_mi Q_mj^T, so a
+    // lane holds four consecutive key tokens of one query token and writes 8 bytes of hi and
+    // 8 of lo. The products and the mask are those of the full record's P: fp32 sums of
+    // exact bf16 products, then e^{min(g_r - g_i, 0)} for i <= r.
+    const float* sG = reinterpret_cast<const float*>(sR + CREC_G_OFF);
+    auto ptile = [&](int j) __attribute__((always_inline)) {
+      const int mi = (w >> 1) + (j == 2 ? 2 : 0), mj = (w & 1) + (j >= 1 ? 2 : 0);
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int mi = (w >> 1) + (j == 2 ? 2 : 0), mj = (w & 1) + (j >= 1 ? 2 : 0);
-        f32x4 acc = zero4();
+      for (int kb = 0; kb < DK / 32; ++kb) acc = mfma_bf16(fragK(sK, mi, kb), fragK(sQ, mj, kb), acc);
+      const int r = tok(mj, ln), i0 = tok(mi, 4 * gq);
+      const float gr = sG[r];
+      const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);
+      f32x4 pv;
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) acc = mfma_bf16(fragK(sK, mi, kb), fragK(sQ, mj, kb), acc);
-        const int r = tok(mj, ln), i0 = tok(mi, 4 * gq);
-        const float gr = sG[r];
-        const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = i0 + e <= r ? __expf(fminf(gr - gi[e], 0.f)) * acc[e] : 0.f;
-        const bf16x4 ph = __builtin_convertvector(pv, bf16x4);
-        const u32x2 hw = __builtin_bit_cast(u32x2, ph);
-        f32x4 hf;
-        hf[0] = __uint_as_float(hw[0] << 16);
-        hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
-        hf[2] = __uint_as_float(hw[1] << 16);
-        hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
-        const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv - hf, bf16x4));
-        int oh, ol;
-        if (mj < 2) {
-          oh = CREC_TOP_OFF + swz_off<128>(r, 2 * i0);
-          ol = CREC_TOP_OFF + swz_off<128>(r, 64 + 2 * i0);
-        } else {
-          oh = CREC_BOT_OFF + swz_off<256>(r - 32, 2 * i0);
-          ol = CREC_BOT_OFF + swz_off<256>(r - 32, 128 + 2 * i0);
-        }
-        *reinterpret_cast<u32x2*>(ldsP + oh) = hw;
-        *reinterpret_cast<u32x2*>(ldsP + ol) = lw;
+      for (int e = 0; e < 4; ++e) pv[e] = i0 + e <= r ? __expf(fminf(gr - gi[e], 0.f)) * acc[e] : 0.f;
+      const bf16x4 ph = __builtin_convertvector(pv, bf16x4);
+      const u32x2 hw = __builtin_bit_cast(u32x2, ph);
+      f32x4 hf;
+      hf[0] = __uint_as_float(hw[0] << 16);
+      hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
+      hf[2] = __uint_as_float(hw[1] << 16);
+      hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
+      const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv - hf, bf16x4));
+      int oh, ol;
+      if (j == 0) {  // query tile mj < 2: rows 0..31
+        oh = CREC_TOP_OFF + swz_off<128>(r, 2 * i0);
+        ol = CREC_TOP_OFF + swz_off<128>(r, 64 + 2 * i0);
+      } else {
+        oh = CREC_BOT_OFF + swz_off<256>(r - 32, 2 * i0);
+        ol = CREC_BOT_OFF + swz_off<256>(r - 32, 128 + 2 * i0);
       }
-    }
-    if constexpr (WITH_OUT) issue_point(1);
+      *reinterpret_cast<u32x2*>(ldsP + oh) = hw;
+      *reinterpret_cast<u32x2*>(ldsP + ol) = lw;
+    };
 
     // ---- S as B operand ----
     S8 Sb[DK / 32];
@@ -349,9 +350,12 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
         vv[3] = __uint_as_float(x[1] & 0xFFFF0000u);
       }
       Rr[mt] = vv - eg * acc;
-      if (mt == 1) issue_point(WITH_OUT ? 2 : 1);
+      if constexpr (WITH_OUT) {
+        if (mt < 3) ptile(mt);
+      }
+      if (mt == 1) issue_point(R_MID);
     }
-    issue_point(WITH_OUT ? 3 : 2);
+    issue_point(R_END);
     S8 Rb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Rb[kb] = split8(frag_from_acc(Rr[2 * kb], Rr[2 * kb + 1]));
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], fragR(sR, mt, kb), Rb[kb]);
-      if (!WITH_OUT && mt == 1) issue_point(3);
+      if (!WITH_OUT && mt == 1) issue_point(U_MID);
     }
 
     // ---- O = diag(e^g) Q S + P U ----
