@@ -48,17 +48,26 @@ struct TimingState {
 };
 thread_local TimingState g_timing;
 
+thread_local kla::LaunchEvents g_launch_events;
+}  // namespace
+
+kla::LaunchEvents& kla::launch_events() { return g_launch_events; }
+
+namespace {
+
+// Each launcher enqueues one kernel. With timing on, that launch stamps a pair of events
+// from its own dispatch (kla::launch_kernel), so the recorded interval is the kernel alone.
 template <class F>
 hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
+  (void)stream;
   if (!g_timing.enabled) return launch();
   TimedLaunch t{name, nullptr, nullptr};
   hipError_t e = hipEventCreate(&t.start);
   if (e == hipSuccess) e = hipEventCreate(&t.stop);
-  if (e == hipSuccess) e = hipEventRecord(t.start, stream);
   if (e != hipSuccess) return e;
+  g_launch_events = {t.start, t.stop};
   e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(t.stop, stream);
+  g_launch_events = {};
   if (e == hipSuccess) g_timing.rec.push_back(t);
   return e;
 }
@@ -339,11 +348,21 @@ int kla_timing_collect(kla_kernel_timing* out, int max) {
   };
   std::vector<Acc> acc;
   bool err = false;
+  const TimedLaunch* prev = nullptr;
   for (auto& t : g_timing.rec) {
     float ms = 0.f;
     if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) {
       err = true;
     } else {
+      // A dispatch can take its start stamp while it still waits for the kernel before it
+      // on the stream; the kernel runs only from that kernel's end, so the overlap is not
+      // counted (launches timed from one thread go to one stream in order).
+      float overlap = 0.f;
+      if (prev && hipEventElapsedTime(&overlap, t.start, prev->stop) == hipSuccess && overlap > 0.f)
+        ms -= std::min(overlap, ms);
+    }
+    prev = &t;
+    if (!err) {
       auto it = std::find_if(acc.begin(), acc.end(), [&](const Acc& a) { return std::strcmp(a.name, t.name) == 0; });
       if (it == acc.end()) acc.push_back({t.name, 1, ms});
       else {
@@ -351,6 +370,8 @@ int kla_timing_collect(kla_kernel_timing* out, int max) {
         it->ms += ms;
       }
     }
+  }
+  for (auto& t : g_timing.rec) {
     (void)hipEventDestroy(t.start);
     (void)hipEventDestroy(t.stop);
   }

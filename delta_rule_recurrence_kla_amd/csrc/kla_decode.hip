@@ -114,9 +114,8 @@ template <int MODE, int DK, int DV>
 static hipError_t launch_decode_t(int N, int H, const void* q, const void* k, const void* v, const float* la,
                                   const float* eta, float eps, float* state, float* out, hipStream_t stream) {
   using in_t = typename Tr<MODE>::in_t;
-  hipLaunchKernelGGL((decode_kernel<MODE, DK, DV>), dim3(N * H), dim3(256), 0, stream, static_cast<const in_t*>(q),
-                     static_cast<const in_t*>(k), static_cast<const in_t*>(v), la, eta, eps, state, out);
-  return hipGetLastError();
+  return launch_kernel(decode_kernel<MODE, DK, DV>, dim3(N * H), dim3(256), stream, static_cast<const in_t*>(q),
+                       static_cast<const in_t*>(k), static_cast<const in_t*>(v), la, eta, eps, state, out);
 }
 
 template <int MODE>

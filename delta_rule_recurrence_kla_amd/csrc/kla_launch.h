@@ -2,10 +2,29 @@
 // Every launcher only enqueues on `stream` and returns hipGetLastError().
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace kla {
+
+// Events the next kernel launch stamps with its own start and end (set by the library's
+// timing hook, null otherwise). hipExtLaunchKernelGGL takes both timestamps from the
+// kernel's dispatch, so the interval is the kernel's execution alone, as a profiler's
+// kernel trace reports it.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+// Every kernel of the library is launched through this (arguments are converted to the
+// kernel's parameter types); returns the launch status.
+template <class F, class... A>
+inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
+  const LaunchEvents& ev = launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  return hipGetLastError();
+}
 
 // Per-launch size bundle shared by the prefill kernels.
 struct Dims {

@@ -322,12 +322,10 @@ static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, con
                                 float eps, uint8_t* rec, hipStream_t stream) {
   const int nchunks = d.B * d.H * d.nc;
   if (state_dma_supported(MODE, DK))
-    hipLaunchKernelGGL((prep_kernel<MODE, DK, true>), dim3((nchunks + 3) / 4), dim3(256), 0, stream, q, k, la, eta, eps,
+    return launch_kernel(prep_kernel<MODE, DK, true>, dim3((nchunks + 3) / 4), dim3(256), stream, q, k, la, eta, eps,
+                         rec, d.T, d.H, d.nc, nchunks);
+  return launch_kernel(prep_kernel<MODE, DK, false>, dim3((nchunks + 3) / 4), dim3(256), stream, q, k, la, eta, eps,
                        rec, d.T, d.H, d.nc, nchunks);
-  else
-    hipLaunchKernelGGL((prep_kernel<MODE, DK, false>), dim3((nchunks + 3) / 4), dim3(256), 0, stream, q, k, la, eta,
-                       eps, rec, d.T, d.H, d.nc, nchunks);
-  return hipGetLastError();
 }
 
 int record_bytes(int mode, int dk) { return state_dma_supported(mode, dk) ? CREC_BYTES : REC_BYTES; }

@@ -402,8 +402,7 @@ constexpr int NCOLS_STATE = 64;  // state columns per workgroup (4 waves x 16)
 
 template <int MODE, int DK, bool WITH_OUT, bool AUG>
 static hipError_t launch_state_t(int nwg, const StateArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((state_kernel<MODE, DK, WITH_OUT, AUG>), dim3(nwg), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(state_kernel<MODE, DK, WITH_OUT, AUG>, dim3(nwg), dim3(256), stream, a);
 }
 
 template <bool WITH_OUT, bool AUG>
@@ -449,12 +448,11 @@ hipError_t launch_scan_starts(const Dims& d, const float* maps, const float* ini
                               hipStream_t stream) {
   dim3 grid(d.dv / 16, d.B * d.H);
   switch (d.dk) {
-    case 64: hipLaunchKernelGGL(scan_starts_kernel<64>, grid, dim3(256), 0, stream, maps, init, starts, d.dv, segs); break;
-    case 128: hipLaunchKernelGGL(scan_starts_kernel<128>, grid, dim3(256), 0, stream, maps, init, starts, d.dv, segs); break;
-    case 256: hipLaunchKernelGGL(scan_starts_kernel<256>, grid, dim3(256), 0, stream, maps, init, starts, d.dv, segs); break;
+    case 64: return launch_kernel(scan_starts_kernel<64>, grid, dim3(256), stream, maps, init, starts, d.dv, segs);
+    case 128: return launch_kernel(scan_starts_kernel<128>, grid, dim3(256), stream, maps, init, starts, d.dv, segs);
+    case 256: return launch_kernel(scan_starts_kernel<256>, grid, dim3(256), stream, maps, init, starts, d.dv, segs);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void* k, const void* v,
@@ -471,9 +469,8 @@ hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void*
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const size_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(copy_or_zero_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
-                     stream, src, dst, n);
-  return hipGetLastError();
+  return launch_kernel(copy_or_zero_kernel, dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256),
+                       stream, src, dst, n);
 }
 
 }  // namespace kla

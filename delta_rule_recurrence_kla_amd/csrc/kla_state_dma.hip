@@ -442,8 +442,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
 
 template <int DK, bool WITH_OUT, bool AUG>
 static hipError_t launch_dma_t(int nwg, const StateDmaArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((state_dma_kernel<DK, WITH_OUT, AUG>), dim3(nwg), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel(state_dma_kernel<DK, WITH_OUT, AUG>, dim3(nwg), dim3(256), stream, a);
 }
 
 bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 64 || dk == 128); }

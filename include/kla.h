@@ -140,11 +140,13 @@ const char* kla_version(void);
 
 /*
  * Measurement hook. While enabled on the calling thread, every kernel the
- * library enqueues from that thread is bracketed by a pair of HIP events on
- * the same stream. kla_timing_collect waits for those events, writes up to
- * `max` per-kernel totals (name, launches, summed milliseconds) and clears the
- * record; it returns the number of distinct kernels recorded, or -1 on a HIP
- * error. Timing adds two event records per launch and is off by default.
+ * library enqueues from that thread stamps a pair of HIP events from its own
+ * dispatch (hipExtLaunchKernelGGL). kla_timing_collect waits for those events,
+ * writes up to `max` per-kernel totals (name, launches, summed milliseconds)
+ * and clears the record; it returns the number of distinct kernels recorded,
+ * or -1 on a HIP error. A kernel's time runs from the later of its start stamp
+ * and the end of the previous timed kernel to its end, which assumes the timed
+ * launches of a thread share one stream. Off by default.
  */
 typedef struct {
   char name[32];
