@@ -98,9 +98,35 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
   const long long avail = static_cast<long long>(T - t0) * rowK;
   const rsrc_t rk = make_rsrc_wu(static_cast<const uint8_t*>(kv) + chunk_off, avail);
   const rsrc_t rq = make_rsrc_wu(static_cast<const uint8_t*>(qv) + chunk_off, avail);
+  // gates first: their loads then overlap the key loads
+  const int t = t0 + lane;
+  float la = 0.f, et = 0.f;
+  if (t < T) {
+    const size_t gi = (static_cast<size_t>(b) * T + t) * H + h;
+    la = log_alpha[gi];
+    et = eta[gi];
+  }
   f32x4 G[10], QK[10];
 #pragma unroll
   for (int i = 0; i < 10; ++i) G[i] = QK[i] = zero4();
+
+  // Compact bf16 variant: every key fragment of the chunk is loaded before the first
+  // product, so the wave waits for one memory round trip instead of one per 32 columns.
+  constexpr bool PRELOAD = COMPACT && MODE == MODE_BF16 && DK <= 128;
+  XF kall[PRELOAD ? DK / 32 : 1][4];
+  if constexpr (PRELOAD) {
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int off = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 4 * gq) * SZ;
+        const u32x2 k0 = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
+        const u32x2 k1 = __builtin_amdgcn_raw_buffer_load_b64(rk, off + 16 * SZ, 0, 0);
+        kall[kb][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
+  }
 
 #pragma unroll
   for (int kb = 0; kb < DK / 32; ++kb) {
@@ -108,7 +134,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int off = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 4 * gq) * SZ;
-      if constexpr (MODE == MODE_BF16) {
+      if constexpr (PRELOAD) {
+        kf[x] = kall[kb][x];
+      } else if constexpr (MODE == MODE_BF16) {
         const u32x2 k0 = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
         const u32x2 k1 = __builtin_amdgcn_raw_buffer_load_b64(rk, off + 16 * SZ, 0, 0);
         kf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3));
@@ -143,13 +171,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
     const int i = ln & 3;
     const float v = i == 0 ? d[0] : i == 1 ? d[1] : i == 2 ? d[2] : d[3];
     if ((ln >> 2) == gq) sNB[16 * x + ln] = v;  // G[16x+ln][16x+ln]
-  }
-  const int t = t0 + lane;
-  float la = 0.f, et = 0.f;
-  if (t < T) {
-    const size_t gi = (static_cast<size_t>(b) * T + t) * H + h;
-    la = log_alpha[gi];
-    et = eta[gi];
   }
   float g = la;
 #pragma unroll
