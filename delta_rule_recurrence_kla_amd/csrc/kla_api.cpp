@@ -62,8 +62,9 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
   (void)stream;
   if (!g_timing.enabled) return launch();
   TimedLaunch t{name, nullptr, nullptr};
-  hipError_t e = hipEventCreate(&t.start);
-  if (e == hipSuccess) e = hipEventCreate(&t.stop);
+  // no system-scope fences around the stamps: they would add a cache flush to every launch
+  hipError_t e = hipEventCreateWithFlags(&t.start, hipEventDisableSystemFence);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&t.stop, hipEventDisableSystemFence);
   if (e != hipSuccess) return e;
   g_launch_events = {t.start, t.stop};
   e = launch();
