@@ -26,11 +26,18 @@ ARCH = "gfx950"
 SOURCES = ["kla_prep.hip", "kla_state.hip", "kla_state_dma.hip", "kla_decode.hip", "kla_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+# The two prefill kernels are latency-bound chains of MFMA, LDS and VALU work run at one wave
+# per SIMD; LLVM's iterative ILP scheduler orders them better than the default occupancy
+# scheduler (measured: state kernel about 7% and prep about 5% faster on gfx950).
+PER_FILE = {
+    "kla_state_dma.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "kla_prep.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
