@@ -172,13 +172,32 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
     const float v = i == 0 ? d[0] : i == 1 ? d[1] : i == 2 ? d[2] : d[3];
     if ((ln >> 2) == gq) sNB[16 * x + ln] = v;  // G[16x+ln][16x+ln]
   }
+  // inclusive cumsum over the 64 lanes: DPP row shifts by 1, 2, 4, 8 within rows of 16 lanes
+  // (lanes shifted in from outside a row read 0), then lane 15 of each row added to the next
+  // row (rows 1 and 3) and lane 31 to rows 2 and 3
   float g = la;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float y = __shfl_up(g, o);
-    if (lane >= o) g += y;
-  }
-  const float gC = __shfl(g, 63);
+  auto dpp = [](float x, auto ctrl_c, auto rows_c, auto bound_c) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl_c)::value,
+                                                      decltype(rows_c)::value, 0xf, decltype(bound_c)::value));
+  };
+  using shr1 = std::integral_constant<int, 0x111>;
+  using shr2 = std::integral_constant<int, 0x112>;
+  using shr4 = std::integral_constant<int, 0x114>;
+  using shr8 = std::integral_constant<int, 0x118>;
+  using bc15 = std::integral_constant<int, 0x142>;
+  using bc31 = std::integral_constant<int, 0x143>;
+  using all_rows = std::integral_constant<int, 0xf>;
+  using rows13 = std::integral_constant<int, 0xa>;
+  using rows23 = std::integral_constant<int, 0xc>;
+  using zero_oob = std::integral_constant<bool, true>;
+  using keep_oob = std::integral_constant<bool, false>;
+  g += dpp(g, shr1{}, all_rows{}, zero_oob{});
+  g += dpp(g, shr2{}, all_rows{}, zero_oob{});
+  g += dpp(g, shr4{}, all_rows{}, zero_oob{});
+  g += dpp(g, shr8{}, all_rows{}, zero_oob{});
+  g += dpp(g, bc15{}, rows13{}, keep_oob{});
+  g += dpp(g, bc31{}, rows23{}, keep_oob{});
+  const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 63));
   wave_sync();
   const float denom = sNB[lane] + eps;
   const float beta = denom != 0.f ? et / denom : 0.f;
