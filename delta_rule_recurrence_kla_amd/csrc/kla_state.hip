@@ -349,43 +349,54 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   }
 }
 
-// Start state of every segment: X_0 = init (or 0), X_{s+1} = M_s X_s + N_s.
-// One workgroup per (b, h, 16-column tile of dv); fp32 throughout.
+// Start state of every segment: X_0 = init (or 0), X_{s+1} = M_s X_s + N_s (the fold of the
+// segment maps; the associative scan of the KATA page, 2.3, and the HLA page, 4).
+// One workgroup per (b, h, 16-column tile of dv), four waves, each owning DK/64 row tiles of
+// 16 rows. The products run on the fp32 MFMA (v_mfma_f32_16x16x4_f32, full fp32 products).
+// The contraction is taken in the order k = 16 kk + 4 gq + s (s = 0..3 over four MFMAs), so a
+// lane's A operands for four MFMAs are one 16-byte load of a row of M and its B operands one
+// 16-byte LDS read of X^T, kept in LDS with a padded row pitch. X^T is double-buffered: one
+// barrier per segment step.
 template <int DK>
 __global__ __launch_bounds__(256) void scan_starts_kernel(const float* __restrict__ maps,
                                                           const float* __restrict__ init,
                                                           float* __restrict__ starts, int DV, int segs) {
-  __shared__ float X[DK][16];
-  const int tid = threadIdx.x;
-  const int ct = blockIdx.x, bh = blockIdx.y;
-  const int c0 = ct * 16;
+  constexpr int XP = DK + 4;  // padded pitch of X^T rows (floats)
+  __shared__ __align__(16) float XT[2][16 * XP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int gq = lane >> 4, ln = lane & 15;
+  const int c0 = blockIdx.x * 16, bh = blockIdx.y;
   const int LDM = DK + DV;
   for (int o = tid; o < DK * 16; o += 256) {
     const int r = o >> 4, j = o & 15;
     const float x = init ? init[static_cast<size_t>(bh) * DK * DV + r * DV + c0 + j] : 0.f;
-    X[r][j] = x;
+    XT[0][j * XP + r] = x;
     starts[(static_cast<size_t>(bh) * segs) * DK * DV + r * DV + c0 + j] = x;
   }
   __syncthreads();
   for (int s = 0; s + 1 < segs; ++s) {
     const float* M = maps + (static_cast<size_t>(bh) * (segs - 1) + s) * DK * LDM;
-    float y[DK * 16 / 256];
+    const float* X = XT[s & 1];
+    float* Xn = XT[(s + 1) & 1];
+    float* out = starts + (static_cast<size_t>(bh) * segs + s + 1) * DK * DV;
 #pragma unroll
-    for (int q = 0; q < DK * 16 / 256; ++q) {
-      const int o = tid + 256 * q;
-      const int r = o >> 4, j = o & 15;
-      const float* Mr = M + static_cast<size_t>(r) * LDM;
-      float acc = Mr[DK + c0 + j];
-      for (int u = 0; u < DK; ++u) acc += Mr[u] * X[u][j];
-      y[q] = acc;
-    }
-    __syncthreads();
+    for (int u = 0; u < DK / 64; ++u) {
+      const int mt = w + 4 * u;
+      f32x4 acc;
 #pragma unroll
-    for (int q = 0; q < DK * 16 / 256; ++q) {
-      const int o = tid + 256 * q;
-      const int r = o >> 4, j = o & 15;
-      X[r][j] = y[q];
-      starts[(static_cast<size_t>(bh) * segs + s + 1) * DK * DV + r * DV + c0 + j] = y[q];
+      for (int i = 0; i < 4; ++i) acc[i] = M[static_cast<size_t>(16 * mt + 4 * gq + i) * LDM + DK + c0 + ln];  // N
+      const float* Mrow = M + static_cast<size_t>(16 * mt + ln) * LDM + 4 * gq;
+      const float* Xrow = X + ln * XP + 4 * gq;
+#pragma unroll 4
+      for (int kk = 0; kk < DK / 16; ++kk) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(Mrow + 16 * kk);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(Xrow + 16 * kk);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[q], b4[q], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[static_cast<size_t>(16 * mt + 4 * gq + i) * DV + c0 + ln] = acc[i];
+      *reinterpret_cast<f32x4*>(Xn + ln * XP + 16 * mt + 4 * gq) = acc;  // X^T[col][rows 16mt + 4gq + 0..3]
     }
     __syncthreads();
   }
