@@ -371,16 +371,14 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       if (!WITH_OUT && mt == 1) issue_point(U_MID);
     }
 
-    // ---- O = diag(e^g) Q S + P U ----
+    // ---- O = diag(e^g) Q S + P U, S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
+    // QS and the state update need no P: they run before the LDS-only barrier that makes
+    // every wave's P tiles visible; only the P U products follow it.
+    S8 Ub[2];
+    f32x4 Oacc[4];
     if constexpr (WITH_OUT) {
-      // every wave's tiles of P are in LDS (an LDS-only barrier: the copies of chunk c+1
-      // stay in flight)
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      S8 Ub[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) Ub[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
-      // O^T = S^T Q^T (times e^g per token) + U^T P^T: the same fragments as O = Q S + P U
-      // with the two operands of every product exchanged
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = zero4();
@@ -390,15 +388,9 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
           acc = mfma_bf16(Sb[kb].h, qf, acc);
           acc = mfma_bf16(Sb[kb].l, qf, acc);
         }
-        acc *= sEG[tok(mt, ln)];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
-        Ohold[mt] = acc;
+        Oacc[mt] = acc * sEG[tok(mt, ln)];
       }
     }
-
-    // ---- S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
     const float gC = sEG[CHUNK - 1];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) U[mt] *= *reinterpret_cast<const f32x4*>(sEGC + tok(mt, 4 * gq));
@@ -410,6 +402,17 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       S[mt] *= gC;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], fragKT(sK, mt, kb), Ud[kb]);
+    }
+    if constexpr (WITH_OUT) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc = Oacc[mt];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
+        Ohold[mt] = acc;
+      }
     }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies for chunk c+1 have landed
