@@ -24,8 +24,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["kla_prep.hip", "kla_state.hip", "kla_state_dma.hip", "kla_decode.hip", "kla_api.cpp"]
+# MFMA results go to ordinary VGPRs (-amdgpu-mfma-vgpr-form) rather than accumulation
+# registers: every accumulator here is read back by vector instructions (splits, scalings,
+# stores), and with the accumulation-register form each such read costs a v_accvgpr_read
+# (about 125 of them per chunk in the state kernel, 3% of its time).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall"]
 # The two prefill kernels are latency-bound chains of MFMA, LDS and VALU work run at one wave
 # per SIMD; LLVM's iterative ILP scheduler orders them better than the default occupancy
 # scheduler (measured: state kernel about 7% and prep about 5% faster on gfx950).

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * gq + i;
         float v = 0.f;
-        if (nt <= mt) v = cc <= r ? __expf(fminf(gr[i] - gc, 0.f)) * QK[tix(mt, nt)][i] : 0.f;
+        if (nt <= mt) v = cc <= r ? __expf(gr[i] - gc) * QK[tix(mt, nt)][i] : 0.f;
         stage_put(4 * gq + i, cc, v);
       }
     }
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mt + 4 * gq + i;
         sA[tix(mt, nt) * ABLK + (4 * gq + i) * AP + ln] =
-            cc < r ? br[i] * __expf(fminf(gr[i] - gc, 0.f)) * G[tix(mt, nt)][i] : 0.f;
+            cc < r ? br[i] * __expf(gr[i] - gc) * G[tix(mt, nt)][i] : 0.f;
       }
     }
   }

@@ -295,7 +295,9 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     // right after R tile j, so that the two interleave). A tile is D = K_mi Q_mj^T, so a
     // lane holds four consecutive key tokens of one query token and writes 8 bytes of hi and
     // 8 of lo. The products and the mask are those of the full record's P: fp32 sums of
-    // exact bf16 products, then e^{min(g_r - g_i, 0)} for i <= r.
+    // exact bf16 products times e^{g_r - g_i} for i <= r, and 0 above the diagonal (a select,
+    // so an overflowing exponent there does no harm). Pair j = 1 puts key tokens 0..31
+    // against query tokens 32..63 and needs no mask.
     const float* sG = reinterpret_cast<const float*>(sR + CREC_G_OFF);
     auto ptile = [&](int j) __attribute__((always_inline)) {
       const int mi = (w >> 1) + (j == 2 ? 2 : 0), mj = (w & 1) + (j >= 1 ? 2 : 0);
@@ -307,15 +309,18 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);
       f32x4 pv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pv[e] = i0 + e <= r ? __expf(fminf(gr - gi[e], 0.f)) * acc[e] : 0.f;
-      const bf16x4 ph = __builtin_convertvector(pv, bf16x4);
-      const u32x2 hw = __builtin_bit_cast(u32x2, ph);
+      for (int e = 0; e < 4; ++e) {
+        const float x = __expf(gr - gi[e]) * acc[e];
+        pv[e] = (j == 1 || i0 + e <= r) ? x : 0.f;
+      }
+      const u32x2 hw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv, bf16x4));
       f32x4 hf;
       hf[0] = __uint_as_float(hw[0] << 16);
       hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
       hf[2] = __uint_as_float(hw[1] << 16);
       hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
-      const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv - hf, bf16x4));
+      const f32x4 lv = pv - hf;
+      const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(lv, bf16x4));
       int oh, ol;
       if (j == 0) {  // query tile mj < 2: rows 0..31
         oh = CREC_TOP_OFF + swz_off<128>(r, 2 * i0);
@@ -374,6 +379,13 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     // ---- O = diag(e^g) Q S + P U, S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
     // QS and the state update need no P: they run before the LDS-only barrier that makes
     // every wave's P tiles visible; only the P U products follow it.
+    // U is split twice: scaled by e^{g_C - g} (for the state update) and as it is (for P U)
+    f32x4 Ue[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) Ue[mt] = U[mt] * *reinterpret_cast<const f32x4*>(sEGC + tok(mt, 4 * gq));
+    S8 Ud[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) Ud[kb] = split8(frag_from_acc(Ue[2 * kb], Ue[2 * kb + 1]));
     S8 Ub[2];
     f32x4 Oacc[4];
     if constexpr (WITH_OUT) {
@@ -392,11 +404,6 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       }
     }
     const float gC = sEG[CHUNK - 1];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) U[mt] *= *reinterpret_cast<const f32x4*>(sEGC + tok(mt, 4 * gq));
-    S8 Ud[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) Ud[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
 #pragma unroll
     for (int mt = 0; mt < DK / 16; ++mt) {
       S[mt] *= gC;

@@ -73,6 +73,31 @@ def test_chunk_form_equals_recurrence(name, T, dk, dv, C):
     assert np.max(np.abs(S - S_ref[0, 0])) < 1e-10
 
 
+def test_growth_gates_need_the_unclamped_decay():
+    """log_alpha > 0 is accepted (not clamped), so e^{g_r - g_i} can exceed 1 inside a chunk;
+    the chunk form with the exact factor matches the recurrence, one capped at 1 does not."""
+    q, k, v, la, eta, eps, S0, wl = _head("lm_layer_4k", 5, 200, 32, 16)
+    la = np.random.default_rng(3).uniform(-0.05, 0.04, la.shape)
+    o_ref, S_ref = kla_ref.forward(wl.q, wl.k, wl.v, la[None, :, None].astype(np.float32), wl.eta, eps,
+                                   wl.init_state)
+    la = la.astype(np.float32).astype(np.float64)
+    o, S = chunked_forward(q, k, v, la, eta, eps, S0, 64)
+    scale = np.sqrt(np.mean(o_ref ** 2))
+    assert np.max(np.abs(o - o_ref[0, :, 0])) < 1e-10 * max(scale, 1)
+    assert np.max(np.abs(S - S_ref[0, 0])) < 1e-10
+
+    def clamped_step(S0, Q, K, V, la, eta, eps):
+        g = np.cumsum(la)
+        beta = eta / (np.sum(K * K, 1) + np.float32(eps))
+        D = np.exp(np.minimum(g[:, None] - g[None, :], 0))
+        A = np.tril(beta[:, None] * D * (K @ K.T), -1)
+        U = np.linalg.solve(np.eye(len(la)) + A, np.diag(beta)) @ (V - np.exp(g)[:, None] * (K @ S0))
+        return np.exp(g)[:, None] * (Q @ S0) + np.tril(D * (Q @ K.T)) @ U
+
+    o_c = clamped_step(S0, q[:64], k[:64], v[:64], la[:64], eta[:64], eps)
+    assert np.max(np.abs(o_c - o_ref[0, :64, 0])) > 1e-3 * scale
+
+
 def test_padding_with_identity_steps_changes_nothing():
     """A ragged chunk padded with k = q = v = 0, log_alpha = 0, eta = 0 gives the same result."""
     q, k, v, la, eta, eps, S0, _ = _head("lm_layer_4k", 2, 100, 32, 16)

@@ -5,6 +5,7 @@ inputs, on the outputs and on the end state, element by element. Small cases
 span several chunks and a ragged tail; full-size workloads are compared on
 sampled heads that the C oracle computes over the whole sequence.
 """
+import dataclasses
 import os
 import sys
 
@@ -128,6 +129,21 @@ def test_prefill_small_fp32(dk, dv, T, path):
     o_ref, S_ref = oracle_prefill(wl)
     assert_close(o, o_ref, TOL["f32"], "out")
     assert_close(S, S_ref, TOL["f32"], "final state")
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 256, 64), ("f32", 128, 64)])
+@pytest.mark.parametrize("path", ["sequential", "scan"])
+def test_prefill_growth_gates(dtype, dk, dv, path):
+    """Some log_alpha > 0 (accepted, not clamped): e^{g_r - g_i} exceeds 1 inside a chunk."""
+    log(f"prefill growth gates {dtype} dk={dk} dv={dv} path={path}")
+    name = "lm_layer_4k" if dtype == "bf16" else "tiny_f32"
+    wl = W.make_prefill(name, seed=11 + dk, B=1, T=300, H=2, dk=dk, dv=dv, init_std=0.3)
+    la = np.random.default_rng(7).uniform(-0.05, 0.04, wl.log_alpha.shape).astype(np.float32)
+    wl = dataclasses.replace(wl, log_alpha=la)
+    o, S = run_prefill(wl, path=path, segments=2)
+    o_ref, S_ref = oracle_prefill(wl)
+    assert_close(o, o_ref, TOL[dtype], "out")
+    assert_close(S, S_ref, TOL[dtype], "final state")
 
 
 def test_prefill_psd_recipe_small():
