@@ -11,7 +11,13 @@
 //  * every input of chunk c+1 (rows of K, Q, V and the chunk record) is copied into
 //    the other half of a double-buffered LDS area by buffer_load ... lds while chunk
 //    c is computed, so no registers hold prefetched data and a chunk needs a single
-//    workgroup barrier;
+//    workgroup barrier (plus the one that publishes P, below);
+//  * a fifth wave issues all of those copies. A wave cannot issue past a memory
+//    instruction that the CU has not yet accepted, and in this kernel a 1 KB copy is
+//    accepted only every 50 or so cycles: 53 copies per chunk held each compute wave for
+//    about a thousand cycles when the four shared them. The copy wave takes that wait
+//    instead, and the compute waves issue no memory instructions but their 16-byte output
+//    stores (which they never wait for);
 //  * rows land in the swizzled layout of kla_device.h: the DMA picks, per lane, the
 //    source piece that belongs at its fixed destination;
 //  * K^T operands and the accumulator-layout view of V come from transposed LDS reads
@@ -77,8 +83,10 @@ __device__ __forceinline__ void decode_wg_dma(int L, int ncg, int nunits, int& c
 
 }  // namespace
 
+constexpr int DMA_THREADS = 320;  // four compute waves and the copy wave
+
 template <int DK, bool WITH_OUT, bool AUG>
-__global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
+__global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) {
   using TR = Tr<MODE_BF16>;
   constexpr int NCOLS = 64;
   constexpr int KRB = DK * 2;                 // bytes of a key row
@@ -113,7 +121,6 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   const int col = col0 + 16 * w + ln;
   const bool ident = AUG && col0 < DK;
   const int vcol0 = AUG ? col0 - DK : col0;
-  const int vcol = vcol0 + 16 * w + ln;
   const int c_begin = seg * a.seg_chunks;
   const int c_end = min(a.nc, c_begin + a.seg_chunks);
 
@@ -123,21 +130,47 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
   uint8_t* ob_ = reinterpret_cast<uint8_t*>(a.out) + static_cast<size_t>(b) * T * rowO;
 
-  // per-lane source offsets of this wave's DMA blocks (chunk-relative; blocks w, w + 4, ...);
-  // rows land swizzled
-  constexpr int KPR = KRB / 16, KRPB = 1024 / KRB;  // pieces per key row, key rows per block
+  constexpr int KPR = KRB / 16, KRPB = 1024 / KRB;  // pieces per key row, key rows per 1 KB block
   constexpr int VPR = VRB / 16, VRPB = 1024 / VRB;
-  constexpr int NKB = KBYTES / 4096, NVB = VBYTES / 4096;  // blocks per wave
-  int kS[NKB], vS[NVB];
+
+  if (wu == 4) {
+    // The copy wave. Chunk c's rows of K, Q and V and its record go into buffer B, one
+    // 1 KB block per instruction; each lane fetches the source piece that belongs at its
+    // fixed destination in the swizzled layout. Out-of-range rows of a ragged last chunk
+    // read as zeros. Chunk c + 1 is copied while chunk c is computed; the wave then meets
+    // the compute waves at their barriers (the P barrier and the end of the chunk), having
+    // waited for its copies before the second.
+    auto copy_chunk = [&](int c, uint8_t* B) __attribute__((always_inline)) {
+      const int t0 = c * CHUNK;
+      const rsrc_t rr = make_rsrc_wu(a.rec + (static_cast<size_t>(bh) * a.nc + c) * CREC_BYTES, CREC_BYTES);
 #pragma unroll
-  for (int i = 0; i < NKB; ++i) {
-    const int row = (w + 4 * i) * KRPB + lane / KPR;
-    kS[i] = row * rowK + h * DK * 2 + 16 * ((lane % KPR) ^ swz<KRB>(row));
-  }
+      for (int m = 0; m < RECB / 1024; ++m) dma16(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
+      const rsrc_t rk = make_rsrc_wu(kb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
+      const rsrc_t rq = make_rsrc_wu(qb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
 #pragma unroll
-  for (int i = 0; i < NVB; ++i) {
-    const int row = (w + 4 * i) * VRPB + lane / VPR;
-    vS[i] = row * rowV + (h * DV + vcol0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row));
+      for (int blk = 0; blk < KBYTES / 1024; ++blk) {
+        const int row = blk * KRPB + lane / KPR;
+        const int off = row * rowK + h * DK * 2 + 16 * ((lane % KPR) ^ swz<KRB>(row));
+        dma16(rk, B + K_OFF + 1024 * blk, off);
+        if constexpr (WITH_OUT) dma16(rq, B + Q_OFF + 1024 * blk, off);
+      }
+      if (!ident) {
+        const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV, static_cast<long long>(T - t0) * rowV);
+#pragma unroll
+        for (int blk = 0; blk < VBYTES / 1024; ++blk) {
+          const int row = blk * VRPB + lane / VPR;
+          dma16(rv, B + V_OFF + 1024 * blk, row * rowV + (h * DV + vcol0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row)));
+        }
+      }
+    };
+    if (c_begin < c_end) copy_chunk(c_begin, lds0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int c = c_begin; c < c_end; ++c) {
+      if (c + 1 < c_end) copy_chunk(c + 1, ((c + 1 - c_begin) & 1) ? lds1 : lds0);
+      if constexpr (WITH_OUT) asm volatile("s_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    return;
   }
 
   // Per-lane LDS offsets of the operand reads. Both swizzles ignore row bits 2 and 5, the
@@ -189,43 +222,6 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
     return __builtin_bit_cast(u32x2, v);
   };
 
-  // Copies of chunk c into buffer B, one 1 KB block per slot. A wave cannot issue past a
-  // memory instruction that the memory pipeline has not yet accepted, and the pipeline of a
-  // CU accepts a 1 KB copy only every few dozen cycles; if all four waves issued their
-  // copies (and output stores) at once, each would wait until the pipeline had taken all
-  // of them. So each wave issues its share at its own point of the chunk (wave w at issue
-  // point w), and the pipeline serves one wave while the other three compute.
-  // Slot order: record blocks w, w+4, w+8, w+12 (those below 13), K blocks, Q blocks, V blocks.
-  constexpr int NSLOT = 4 + NKB + (WITH_OUT ? NKB : 0) + NVB;
-  auto copy_slot = [&](int sl, int c, uint8_t* B) __attribute__((always_inline)) {
-    const int t0 = c * CHUNK;
-    if (sl < 4) {
-      const int m = wu + 4 * sl;
-      if (m < RECB / 1024) {
-        const rsrc_t rr = make_rsrc_wu(a.rec + (static_cast<size_t>(bh) * a.nc + c) * CREC_BYTES, CREC_BYTES);
-        dma16(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
-      }
-    } else if (sl < 4 + NKB) {
-      const int i = sl - 4;
-      const rsrc_t rk = make_rsrc_wu(kb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
-      dma16(rk, B + K_OFF + 1024 * (wu + 4 * i), kS[i]);
-    } else if (WITH_OUT && sl < 4 + 2 * NKB) {
-      const int i = sl - 4 - NKB;
-      const rsrc_t rq = make_rsrc_wu(qb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
-      dma16(rq, B + Q_OFF + 1024 * (wu + 4 * i), kS[i]);
-    } else if (sl < NSLOT) {
-      const int i = sl - (NSLOT - NVB);
-      if (!ident) {
-        const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV, static_cast<long long>(T - t0) * rowV);
-        dma16(rv, B + V_OFF + 1024 * (wu + 4 * i), vS[i]);
-      }
-    }
-  };
-  auto issue_dma = [&](int c, uint8_t* B) __attribute__((always_inline)) {
-#pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl) copy_slot(sl, c, B);
-  };
-
   // start state
   f32x4 S[DK / 16];
 #pragma unroll
@@ -244,44 +240,18 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
   }
 
   // The output is computed transposed: tile mt of O^T holds, in lane (gq, ln), token
-  // tok(mt, ln) and this wave's columns 16 w + 4 gq + 0..3, stored as one 16-byte write.
-  // A chunk's output is stored during the next chunk (or after the last): vmcnt counts
-  // stores as well as the copies, so a store issued just before the end-of-chunk wait
-  // would put its write latency on every chunk.
-  f32x4 Ohold[4];
-  auto store_out = [&](int c, int mt) __attribute__((always_inline)) {
+  // tok(mt, ln) and this wave's columns 16 w + 4 gq + 0..3, stored as one 16-byte write
+  // as soon as it is complete. Nothing waits for the stores: the compute waves' barriers
+  // wait only for LDS operations.
+  auto store_out = [&](int c, int mt, const f32x4& o) __attribute__((always_inline)) {
     const int t0 = c * CHUNK;
     const rsrc_t ro = make_rsrc_wu(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
     const int obase = (h * DV + vcol0 + 16 * w + 4 * gq) * 4;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Ohold[mt]), ro, obase + tok(mt, ln) * rowO, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, obase + tok(mt, ln) * rowO, 0, 0);
   };
 
-  // one chunk computed from buffer B while chunk c+1 is copied into buffer D
-  auto chunk = [&](int c, const uint8_t* B, uint8_t* D) __attribute__((always_inline)) {
-    const bool more = c + 1 < c_end;
-    // Issue points: START (chunk start), R_MID (after R tile 1), R_END (after R), U_MID (after
-    // U tile 1). At its point a wave issues its copies of chunk c+1 and stores its output of
-    // chunk c-1. With output: waves 0 and 1 at START, 2 at R_MID, 3 at R_END (no point
-    // separates the P tiles from R, so the two interleave). Without: wave w at point w.
-    enum { START = 0, R_MID = 1, R_END = 2, U_MID = 3 };
-    const int my_point = WITH_OUT ? (wu <= 1 ? START : wu == 2 ? R_MID : R_END) : wu;
-    auto issue_point = [&](int pt) __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (my_point == pt) {
-        if (more) {
-#pragma unroll
-          for (int sl = 0; sl < NSLOT; ++sl) copy_slot(sl, c + 1, D);
-        }
-        if constexpr (WITH_OUT) {
-          if (c > c_begin) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) store_out(c - 1, mt);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    issue_point(START);
+  // one chunk computed from buffer B (while the copy wave fills the other buffer)
+  auto chunk = [&](int c, const uint8_t* B) __attribute__((always_inline)) {
     const uint8_t* sK = B + K_OFF;
     const uint8_t* sQ = B + Q_OFF;
     const uint8_t* sV = B + V_OFF;
@@ -358,9 +328,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
       if constexpr (WITH_OUT) {
         if (mt < 3) ptile(mt);
       }
-      if (mt == 1) issue_point(R_MID);
     }
-    issue_point(R_END);
     S8 Rb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Rb[kb] = split8(frag_from_acc(Rr[2 * kb], Rr[2 * kb + 1]));
@@ -373,7 +341,6 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], fragR(sR, mt, kb), Rb[kb]);
-      if (!WITH_OUT && mt == 1) issue_point(U_MID);
     }
 
     // ---- O = diag(e^g) Q S + P U, S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
@@ -418,26 +385,19 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
-        Ohold[mt] = acc;
+        store_out(c, mt, acc);
       }
     }
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies for chunk c+1 have landed
-    __syncthreads();                     // ... and every wave's; all reads of buffer B are done
+    // end of chunk: this wave's reads of buffer B are done (lgkmcnt) and, past the barrier,
+    // every wave's are, and the copy wave's copies of chunk c + 1 have landed
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
-  if (c_begin < c_end) issue_dma(c_begin, lds0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-  __syncthreads();
+  asm volatile("s_barrier" ::: "memory");  // the first chunk has landed
   for (int c = c_begin; c < c_end; c += 2) {
-    chunk(c, lds0, lds1);
-    if (c + 1 < c_end) chunk(c + 1, lds1, lds0);
-  }
-  if constexpr (WITH_OUT) {
-    if (c_begin < c_end) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) store_out(c_end - 1, mt);
-    }
+    chunk(c, lds0);
+    if (c + 1 < c_end) chunk(c + 1, lds1);
   }
 
   if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
@@ -452,7 +412,7 @@ __global__ __launch_bounds__(256) void state_dma_kernel(StateDmaArgs a) {
 
 template <int DK, bool WITH_OUT, bool AUG>
 static hipError_t launch_dma_t(int nwg, const StateDmaArgs& a, hipStream_t stream) {
-  return launch_kernel(state_dma_kernel<DK, WITH_OUT, AUG>, dim3(nwg), dim3(256), stream, a);
+  return launch_kernel(state_dma_kernel<DK, WITH_OUT, AUG>, dim3(nwg), dim3(DMA_THREADS), stream, a);
 }
 
 bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 64 || dk == 128); }
