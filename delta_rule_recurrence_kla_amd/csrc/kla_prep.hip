@@ -63,7 +63,7 @@ __device__ __forceinline__ F8 a_frag(const float* sA, int I, int C0, int ln, int
 }  // namespace
 
 template <int MODE, int DK, bool COMPACT>
-__global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
+__global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                    const float* __restrict__ log_alpha,
                                                    const float* __restrict__ eta, float eps,
                                                    uint8_t* __restrict__ rec, int T, int H, int nc, int nchunks) {
@@ -73,24 +73,23 @@ __global__ __launch_bounds__(256) void prep_kernel(const void* __restrict__ qv, 
   using DF = typename TR::DF;
   constexpr int SZ = static_cast<int>(sizeof(in_t));
 
-  // per wave: the 10 lower 16x16 blocks of A; a 16-row staging strip (272-byte rows) that
-  // also holds the diagonal-block inverses during the inverse; n (then beta) and g
-  __shared__ __align__(16) float sAbuf[4][10 * ABLK];
-  __shared__ __align__(16) float sStage[4][16 * 68];
-  __shared__ __align__(16) float sVec[4][2][64];
+  // One wave per workgroup (17.3 KB of LDS), so that LDS, not the workgroup shape, sets how
+  // many chunks a CU holds: nine, against eight as four-wave groups (about 6% faster).
+  // The 10 lower 16x16 blocks of A; a 16-row staging strip (272-byte rows) that also holds
+  // the diagonal-block inverses during the inverse; n (then beta) and g.
+  __shared__ __align__(16) float sA[10 * ABLK];
+  __shared__ __align__(16) float st[16 * 68];
+  __shared__ __align__(16) float sVec[2][64];
 
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x;
   const int gq = lane >> 4, ln = lane & 15;
-  const int id = blockIdx.x * 4 + w;
-  if (id >= nchunks) return;  // only wave-level synchronisation below
+  const int id = blockIdx.x;
   const int bh = id / nc, c = id - bh * nc;
   const int b = bh / H, h = bh - b * H;
   const int t0 = c * CHUNK;
-  float* sA = sAbuf[w];
-  float* st = sStage[w];
   float* sDw = st;  // diagonal-block inverses D_I at I * 16 * DP
-  float* sNB = sVec[w][0];
-  float* sGv = sVec[w][1];
+  float* sNB = sVec[0];
+  float* sGv = sVec[1];
 
   // ---- G = K K^T and QK = Q K^T on the lower 10 tiles, operands straight from memory ----
   const int rowK = H * DK * SZ;
@@ -362,9 +361,9 @@ static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, con
                                 float eps, uint8_t* rec, hipStream_t stream) {
   const int nchunks = d.B * d.H * d.nc;
   if (state_dma_supported(MODE, DK))
-    return launch_kernel(prep_kernel<MODE, DK, true>, dim3((nchunks + 3) / 4), dim3(256), stream, q, k, la, eta, eps,
+    return launch_kernel(prep_kernel<MODE, DK, true>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
                          rec, d.T, d.H, d.nc, nchunks);
-  return launch_kernel(prep_kernel<MODE, DK, false>, dim3((nchunks + 3) / 4), dim3(256), stream, q, k, la, eta, eps,
+  return launch_kernel(prep_kernel<MODE, DK, false>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
                        rec, d.T, d.H, d.nc, nchunks);
 }
 
