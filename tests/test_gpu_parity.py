@@ -146,6 +146,20 @@ def test_prefill_growth_gates(dtype, dk, dv, path):
     assert_close(S, S_ref, TOL[dtype], "final state")
 
 
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 256, 128), ("f32", 64, 64)])
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 3, 65), (3, 5, 130)])
+def test_prefill_odd_grids(dtype, dk, dv, B, H, T):
+    """One token, one token past a chunk, and batch x heads that fill no regular grid."""
+    log(f"prefill odd grid {dtype} dk={dk} dv={dv} B={B} H={H} T={T}")
+    name = "lm_layer_4k" if dtype == "bf16" else "tiny_f32"
+    wl = W.make_prefill(name, seed=B * 100 + H * 10 + T % 7, B=B, T=T, H=H, dk=dk, dv=dv, init_std=0.3)
+    for path in ("sequential", "scan"):
+        o, S = run_prefill(wl, path=path, segments=2)
+        o_ref, S_ref = oracle_prefill(wl)
+        assert_close(o, o_ref, TOL[dtype], f"out ({path})")
+        assert_close(S, S_ref, TOL[dtype], f"final state ({path})")
+
+
 def test_prefill_psd_recipe_small():
     log("prefill psd small")
     wl = W.make_prefill("psd_lift_8k", seed=5, B=1, T=700, H=2)
