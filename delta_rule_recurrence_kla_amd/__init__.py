@@ -60,9 +60,10 @@ def load():
     lib.kla_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_f32.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_plan", "kla_decode_step",
-               "kla_decode_step_f32", "kla_timing_enable"):
+               "kla_decode_step_f32", "kla_timing_enable", "kla_timing_select"):
         getattr(lib, fn).restype = I
     lib.kla_timing_enable.argtypes = [I]
+    lib.kla_timing_select.argtypes = [ctypes.c_char_p]
     lib.kla_timing_collect.argtypes = [ctypes.POINTER(KernelTiming), I]
     lib.kla_timing_collect.restype = I
     lib.kla_last_error.restype = ctypes.c_char_p
@@ -189,6 +190,11 @@ def plan(B: int, T: int, H: int, dk: int, dv: int, chunk: int = 64, path: str = 
 
 def timing_enable(enable: bool = True):
     _check(load().kla_timing_enable(1 if enable else 0))
+
+
+def timing_select(kernel: Optional[str] = None):
+    """Stamp only launches of `kernel` (None: every kernel) while the hook is on."""
+    _check(load().kla_timing_select(kernel.encode() if kernel else None))
 
 
 def timing_collect(max_kernels: int = 16):

@@ -44,6 +44,7 @@ struct TimedLaunch {
 };
 struct TimingState {
   bool enabled = false;
+  char only[32] = {0};  // when set, only launches of this kernel are stamped
   std::vector<TimedLaunch> rec;
 };
 thread_local TimingState g_timing;
@@ -60,7 +61,7 @@ namespace {
 template <class F>
 hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
   (void)stream;
-  if (!g_timing.enabled) return launch();
+  if (!g_timing.enabled || (g_timing.only[0] && std::strcmp(g_timing.only, name) != 0)) return launch();
   TimedLaunch t{name, nullptr, nullptr};
   // no system-scope fences around the stamps: they would add a cache flush to every launch
   hipError_t e = hipEventCreateWithFlags(&t.start, hipEventDisableSystemFence);
@@ -338,6 +339,13 @@ const char* kla_version(void) { return "kla-mi355x 0.1.0 (gfx950)"; }
 
 kla_status kla_timing_enable(int enable) {
   g_timing.enabled = enable != 0;
+  return KLA_OK;
+}
+
+kla_status kla_timing_select(const char* kernel) {
+  if (kernel && std::strlen(kernel) >= sizeof g_timing.only)
+    return fail(KLA_ERR_INVALID_ARG, "kernel name too long for the timing hook (%zu characters)", std::strlen(kernel));
+  std::snprintf(g_timing.only, sizeof g_timing.only, "%s", kernel ? kernel : "");
   return KLA_OK;
 }
 

@@ -157,6 +157,15 @@ typedef struct {
 kla_status kla_timing_enable(int enable);
 int kla_timing_collect(kla_kernel_timing* out, int max);
 
+/*
+ * Restricts the hook, on the calling thread, to launches of the kernel named
+ * `kernel` (a name as kla_timing_collect reports it, e.g. "kla_state_seq");
+ * NULL or "" times every kernel again. Each pair of stamps costs the stream a
+ * few microseconds, so a caller that needs one kernel's duration stamps only
+ * that one. Returns KLA_ERR_INVALID_ARG for a name of 32 characters or more.
+ */
+kla_status kla_timing_select(const char* kernel);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_decode_step",
               "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
-              "kla_timing_enable", "kla_timing_collect"):
+              "kla_timing_enable", "kla_timing_collect", "kla_timing_select"):
         assert n in names
 
 
@@ -39,6 +39,13 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", kla.lib_path()], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (kla_\w+)$", out, flags=re.M))
     assert set(_declared_functions()) <= exported
+
+
+def test_timing_select_rejects_long_names():
+    with pytest.raises(kla.KLAError):
+        kla.timing_select("k" * 32)
+    kla.timing_select("kla_state_seq")
+    kla.timing_select(None)
 
 
 def test_version_and_empty_error():

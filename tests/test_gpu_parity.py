@@ -160,6 +160,29 @@ def test_prefill_odd_grids(dtype, dk, dv, B, H, T):
         assert_close(S, S_ref, TOL[dtype], f"final state ({path})")
 
 
+def test_timing_hook_selects_one_kernel():
+    """With a kernel selected, the hook records that kernel's launches and no other."""
+    wl = W.make_prefill("lm_layer_4k", seed=3, B=1, T=256, H=2)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    kla.timing_collect()
+    kla.timing_select("kla_state_seq")
+    kla.timing_enable(True)
+    try:
+        for _ in range(3):
+            kla.chunk_fwd(q, k, v, la, eta, wl.eps, path="sequential")
+        torch.cuda.synchronize()
+    finally:
+        kla.timing_enable(False)
+        kla.timing_select(None)
+    t = kla.timing_collect()
+    assert set(t) == {"kla_state_seq"} and t["kla_state_seq"][0] == 3 and t["kla_state_seq"][1] > 0
+    kla.timing_enable(True)
+    kla.chunk_fwd(q, k, v, la, eta, wl.eps, path="sequential")
+    torch.cuda.synchronize()
+    kla.timing_enable(False)
+    assert {"kla_prep", "kla_state_seq"} <= set(kla.timing_collect())
+
+
 def test_prefill_psd_recipe_small():
     log("prefill psd small")
     wl = W.make_prefill("psd_lift_8k", seed=5, B=1, T=700, H=2)
