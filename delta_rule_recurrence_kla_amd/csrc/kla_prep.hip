@@ -118,10 +118,10 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
     for (int kb = 0; kb < DK / 32; ++kb) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const int off = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 4 * gq) * SZ;
-        const u32x2 k0 = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
-        const u32x2 k1 = __builtin_amdgcn_raw_buffer_load_b64(rk, off + 16 * SZ, 0, 0);
-        kall[kb][x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3));
+        // eight consecutive key columns per lane, one 16-byte load: G = K K^T sums over the
+        // columns in any order in which both operands agree
+        const int off = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 8 * gq) * SZ;
+        kall[kb][x] = __builtin_bit_cast(bf16x8, bload16(rk, off));
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
@@ -136,14 +136,9 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
       if constexpr (PRELOAD) {
         kf[x] = kall[kb][x];
       } else if constexpr (MODE == MODE_BF16) {
-        const u32x2 k0 = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0);
-        const u32x2 k1 = __builtin_amdgcn_raw_buffer_load_b64(rk, off + 16 * SZ, 0, 0);
-        kf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(k0, k1, 0, 1, 2, 3));
-        if constexpr (!COMPACT) {
-          const u32x2 q0 = __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0);
-          const u32x2 q1 = __builtin_amdgcn_raw_buffer_load_b64(rq, off + 16 * SZ, 0, 0);
-          qf[x] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3));
-        }
+        const int off8 = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 8 * gq) * SZ;  // as in the preload
+        kf[x] = __builtin_bit_cast(bf16x8, bload16(rk, off8));
+        if constexpr (!COMPACT) qf[x] = __builtin_bit_cast(bf16x8, bload16(rq, off8));
       } else {
         const f32x4 k0 = __builtin_bit_cast(f32x4, bload16(rk, off));
         const f32x4 k1 = __builtin_bit_cast(f32x4, bload16(rk, off + 16 * SZ));
