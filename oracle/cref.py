@@ -24,10 +24,10 @@ def _load():
             build()
         lib = ctypes.CDLL(LIB)
         lib.kla_ref_forward.argtypes = [_f, _f, _f, _f, _f, ctypes.c_double, _f, _i64, ctypes.c_int,
-                                        _d, _d] + [ctypes.c_int] * 6
+                                        _d, _d] + [ctypes.c_int] * 7
         lib.kla_ref_forward.restype = ctypes.c_int
         lib.kla_ref_decode_step.argtypes = [_f, _f, _f, _f, _f, ctypes.c_double, _d, _i64,
-                                            ctypes.c_int, _d] + [ctypes.c_int] * 5
+                                            ctypes.c_int, _d] + [ctypes.c_int] * 6
         lib.kla_ref_decode_step.restype = ctypes.c_int
         lib.kla_ref_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -46,7 +46,10 @@ def max_threads() -> int:
     return _load().kla_ref_max_threads()
 
 
-def forward(q, k, v, log_alpha, eta, eps, init_state=None, heads=None, nthreads=0):
+_MODES = {"kaczmarz": 0, "direct": 1}
+
+
+def forward(q, k, v, log_alpha, eta, eps, init_state=None, heads=None, nthreads=0, beta_mode="kaczmarz"):
     """Token-by-token float64 forward for a list of (b, h) heads (None = all heads).
 
     Returns (out [n, T, dv], final_state [n, dk, dv]) as float64, n = number of heads.
@@ -66,13 +69,13 @@ def forward(q, k, v, log_alpha, eta, eps, init_state=None, heads=None, nthreads=
     rc = lib.kla_ref_forward(_fp(q), _fp(k), _fp(v), _fp(la), _fp(et), float(np.float32(eps)),
                              _fp(s0), idx.ctypes.data_as(_i64) if idx is not None else None, n,
                              out.ctypes.data_as(_d), fin.ctypes.data_as(_d), B, T, H, dk, dv,
-                             int(nthreads))
+                             int(nthreads), _MODES[beta_mode])
     if rc != 0:
         raise ValueError("kla_ref_forward: bad arguments")
     return out, fin
 
 
-def decode_step(state, q, k, v, log_alpha, eta, eps, heads=None, nthreads=0):
+def decode_step(state, q, k, v, log_alpha, eta, eps, heads=None, nthreads=0, beta_mode="kaczmarz"):
     """One decode step for the listed (n, h) heads. ``state`` is float64 [n_heads, dk, dv]
     for exactly those heads and is updated in place. Returns out [n_heads, dv]."""
     lib = _load()
@@ -91,7 +94,7 @@ def decode_step(state, q, k, v, log_alpha, eta, eps, heads=None, nthreads=0):
     rc = lib.kla_ref_decode_step(_fp(q), _fp(k), _fp(v), _fp(la), _fp(et), float(np.float32(eps)),
                                  state.ctypes.data_as(_d),
                                  idx.ctypes.data_as(_i64) if idx is not None else None, n,
-                                 out.ctypes.data_as(_d), N, H, dk, dv, int(nthreads))
+                                 out.ctypes.data_as(_d), N, H, dk, dv, int(nthreads), _MODES[beta_mode])
     if rc != 0:
         raise ValueError("kla_ref_decode_step: bad arguments")
     return out

@@ -14,6 +14,10 @@
  * silent: S~ = exp(log_alpha_t) * S_{t-1}; o_t = S_t^T q_t after the write, no
  * query scaling; beta_t = 0 when ||k_t||^2 + eps == 0.
  *
+ * beta_mode 1 ("direct") is the Gated DeltaNet baseline the same page sets KLA
+ * against (section "Problem statement"): beta_t = eta_t as given, no division
+ * by ||k_t||^2 + eps. beta_mode 0 is KLA.
+ *
  * Inputs are float32 (bf16 inputs arrive as their exact float32 values); every
  * operation is in double. Layouts: q,k [B,T,H,dk], v [B,T,H,dv], gates [B,T,H],
  * state [B,H,dk,dv] (dv fastest). Outputs are written for a list of heads in
@@ -30,13 +34,13 @@
 /* One token for one head. S is dk x dv (row i = key index), updated in place. */
 static void token(double *S, const float *q, const float *k, const float *v,
                   double log_alpha, double eta, double eps, int dk, int dv,
-                  double *e, double *o)
+                  int beta_mode, double *e, double *o)
 {
     double alpha = exp(log_alpha);
     double nk = 0.0;
     for (int i = 0; i < dk; ++i) nk += (double)k[i] * (double)k[i];
     double denom = nk + eps;
-    double beta = denom != 0.0 ? eta / denom : 0.0;
+    double beta = beta_mode == 1 ? eta : (denom != 0.0 ? eta / denom : 0.0);
 
     /* S~ = alpha S */
     for (int i = 0; i < dk * dv; ++i) S[i] *= alpha;
@@ -81,9 +85,10 @@ int kla_ref_forward(const float *q, const float *k, const float *v,
                     const float *log_alpha, const float *eta, double eps,
                     const float *init_state, const int64_t *heads, int n_heads,
                     double *out, double *final_state,
-                    int B, int T, int H, int dk, int dv, int nthreads)
+                    int B, int T, int H, int dk, int dv, int nthreads, int beta_mode)
 {
     if (B < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_heads < 0) return -1;
+    if (beta_mode != 0 && beta_mode != 1) return -1;
     if (!heads && n_heads != B * H) return -1;
     int err = 0;
     int nt = threads_or_default(nthreads);
@@ -104,7 +109,7 @@ int kla_ref_forward(const float *q, const float *k, const float *v,
         for (int t = 0; t < T; ++t) {
             size_t th = ((size_t)b * T + t) * H + h;
             token(S, q + th * dk, k + th * dk, v + th * dv,
-                  (double)log_alpha[th], (double)eta[th], eps, dk, dv, e,
+                  (double)log_alpha[th], (double)eta[th], eps, dk, dv, beta_mode, e,
                   out + ((size_t)n * T + t) * dv);
         }
         free(e);
@@ -120,9 +125,10 @@ int kla_ref_forward(const float *q, const float *k, const float *v,
 int kla_ref_decode_step(const float *q, const float *k, const float *v,
                         const float *log_alpha, const float *eta, double eps,
                         double *state, const int64_t *heads, int n_heads,
-                        double *out, int N, int H, int dk, int dv, int nthreads)
+                        double *out, int N, int H, int dk, int dv, int nthreads, int beta_mode)
 {
     if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_heads < 0) return -1;
+    if (beta_mode != 0 && beta_mode != 1) return -1;
     if (!heads && n_heads != N * H) return -1;
     int err = 0;
     int nt = threads_or_default(nthreads);
@@ -134,7 +140,7 @@ int kla_ref_decode_step(const float *q, const float *k, const float *v,
         if (!e) { err |= 1; continue; }
         token(state + (size_t)n * dk * dv, q + (size_t)flat * dk, k + (size_t)flat * dk,
               v + (size_t)flat * dv, (double)log_alpha[flat], (double)eta[flat], eps,
-              dk, dv, e, out + (size_t)n * dv);
+              dk, dv, beta_mode, e, out + (size_t)n * dv);
         free(e);
     }
     return err ? -1 : 0;

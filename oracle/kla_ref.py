@@ -21,6 +21,11 @@ Readings where the page is silent (each also listed in the design doc):
   * eps is the float32 value the kernels receive;
   * if ||k_t||^2 + eps == 0 the write is skipped (beta_t = 0).
 
+A second write-strength mode, beta_mode="direct", is the Gated DeltaNet baseline that
+the same page sets KLA against (section "Problem statement"): a learned scalar used as the
+step size as it is, with no division by ||k_t||^2 + eps. The learned scalar arrives in the
+same ``eta`` input. Everything else in the recurrence is unchanged.
+
 Every pin in tests/test_oracle_pins.py exercises this file; none is "parity
 unpinned".
 """
@@ -28,7 +33,9 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["kaczmarz_beta", "step", "forward", "decode_step"]
+__all__ = ["kaczmarz_beta", "write_strength", "step", "forward", "decode_step"]
+
+BETA_MODES = ("kaczmarz", "direct")
 
 
 def kaczmarz_beta(k_t: np.ndarray, eta_t, eps) -> np.ndarray:
@@ -44,7 +51,19 @@ def kaczmarz_beta(k_t: np.ndarray, eta_t, eps) -> np.ndarray:
     return np.where(denom != 0.0, eta_t / safe, 0.0)
 
 
-def step(S, q_t, k_t, v_t, log_alpha_t, eta_t, eps):
+def write_strength(k_t, eta_t, eps, beta_mode="kaczmarz") -> np.ndarray:
+    """beta_t of the write: the Kaczmarz step (KLA page, "KLA update rule") or, in the
+    "direct" mode, the learned scalar eta_t itself (the Gated DeltaNet rule of the
+    page's "Problem statement")."""
+    if beta_mode == "kaczmarz":
+        return kaczmarz_beta(k_t, eta_t, eps)
+    if beta_mode == "direct":
+        k_t = np.asarray(k_t, dtype=np.float64)
+        return np.broadcast_to(np.asarray(eta_t, dtype=np.float64), k_t.shape[:-1]).copy()
+    raise ValueError(f"beta_mode must be one of {BETA_MODES}")
+
+
+def step(S, q_t, k_t, v_t, log_alpha_t, eta_t, eps, beta_mode="kaczmarz"):
     """One token of the recurrence for any number of independent heads.
 
     S: [..., dk, dv] state before the token; q_t, k_t: [..., dk]; v_t: [..., dv];
@@ -55,7 +74,7 @@ def step(S, q_t, k_t, v_t, log_alpha_t, eta_t, eps):
     k_t = np.asarray(k_t, dtype=np.float64)
     v_t = np.asarray(v_t, dtype=np.float64)
     alpha = np.exp(np.asarray(log_alpha_t, dtype=np.float64))
-    beta = kaczmarz_beta(k_t, eta_t, eps)
+    beta = write_strength(k_t, eta_t, eps, beta_mode)
     S_dec = alpha[..., None, None] * S                      # S~ = alpha_t S_{t-1}
     e = v_t - np.einsum("...kv,...k->...v", S_dec, k_t)     # e_t = v_t - S~^T k_t
     S_new = S_dec + beta[..., None, None] * (k_t[..., :, None] * e[..., None, :])  # S~ + beta k e^T
@@ -63,7 +82,7 @@ def step(S, q_t, k_t, v_t, log_alpha_t, eta_t, eps):
     return o, S_new
 
 
-def forward(q, k, v, log_alpha, eta, eps, init_state=None):
+def forward(q, k, v, log_alpha, eta, eps, init_state=None, beta_mode="kaczmarz"):
     """Whole-sequence forward, token by token.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv]; log_alpha, eta: [B, T, H];
@@ -80,14 +99,14 @@ def forward(q, k, v, log_alpha, eta, eps, init_state=None):
         S = np.array(init_state, dtype=np.float64)
     o = np.zeros((B, T, H, dv), np.float64)
     for t in range(T):
-        o[:, t], S = step(S, q[:, t], k[:, t], v[:, t], log_alpha[:, t], eta[:, t], eps)
+        o[:, t], S = step(S, q[:, t], k[:, t], v[:, t], log_alpha[:, t], eta[:, t], eps, beta_mode)
     return o, S
 
 
-def decode_step(state, q, k, v, log_alpha, eta, eps):
+def decode_step(state, q, k, v, log_alpha, eta, eps, beta_mode="kaczmarz"):
     """One decode step: the same single-token update for N x H states.
 
     state: [N, H, dk, dv]; q, k: [N, H, dk]; v: [N, H, dv]; gates [N, H].
     Returns (o [N, H, dv], new_state [N, H, dk, dv]).
     """
-    return step(state, q, k, v, log_alpha, eta, eps)
+    return step(state, q, k, v, log_alpha, eta, eps, beta_mode)

@@ -14,14 +14,21 @@ _real_step = kla_ref.step
 
 
 def _mk(variant):
-    def step(S, q_t, k_t, v_t, log_alpha_t, eta_t, eps):
+    def step(S, q_t, k_t, v_t, log_alpha_t, eta_t, eps, beta_mode="kaczmarz"):
         S = np.asarray(S, dtype=np.float64)
         q_t, k_t, v_t = (np.asarray(x, dtype=np.float64) for x in (q_t, k_t, v_t))
         alpha = np.exp(np.asarray(log_alpha_t, dtype=np.float64))
         nk = np.sum(k_t * k_t, axis=-1)
         eps32 = np.float64(np.float32(eps))
         eta = np.asarray(eta_t, dtype=np.float64)
-        if variant == "beta_norm_not_squared":
+        if beta_mode == "direct":
+            if variant == "direct_still_normalised":
+                beta = eta / np.where(nk + eps32 != 0, nk + eps32, 1.0)
+            elif variant == "direct_ignores_eta":
+                beta = np.ones_like(nk)
+            else:
+                beta = np.broadcast_to(eta, nk.shape).copy()
+        elif variant == "beta_norm_not_squared":
             beta = eta / (np.sqrt(nk) + eps32)
         elif variant == "beta_ignores_eta":
             beta = 1.0 / (nk + eps32)
@@ -61,7 +68,8 @@ def _mk(variant):
 
 MUTANTS = ["beta_norm_not_squared", "beta_ignores_eta", "beta_ignores_eps", "residual_undecayed",
            "residual_sign", "residual_transposed", "write_outer_transposed", "decay_after_write",
-           "no_decay", "readout_before_write", "readout_with_key"]
+           "no_decay", "readout_before_write", "readout_with_key", "direct_still_normalised",
+           "direct_ignores_eta"]
 
 PIN_CALLS = [
     lambda: pins.test_worked_example_exact(kla_ref.forward),
@@ -74,6 +82,8 @@ PIN_CALLS = [
     lambda: pins.test_repeated_key_overwrite(kla_ref.forward),
     lambda: pins.test_pure_decay(kla_ref.forward),
     lambda: pins.test_product_form_brute_force(kla_ref.forward),
+    lambda: pins.test_direct_equals_kaczmarz_on_unit_keys("numpy"),
+    lambda: pins.test_write_residual_law("numpy"),
 ]
 
 

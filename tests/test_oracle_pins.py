@@ -15,6 +15,8 @@ operand, the decay or the readout in the wrong place) fails at least one:
   product form     S_T = A_T..A_1 S_0 + sum_i A_T..A_{i+1} beta_i k_i v_i^T  whole recurrence, other algebra
   linearity        joint linearity in (V, S_0); causality
   NumPy == C       the two builds agree to 1e-12
+  direct mode      the learned-scalar step (KLA "Problem statement") equals KLA on unit keys,
+                   and the residual law (1 - beta ||k||^2) fixes how each mode scales a write
 """
 import os
 
@@ -352,3 +354,82 @@ def test_zero_key_zero_eps_skips_write():
     S = np.arange(6, dtype=np.float64).reshape(3, 2)
     o, S1 = kla_ref.step(S, np.ones(3), np.zeros(3), np.ones(2), 0.0, 1.0, 0.0)
     np.testing.assert_array_equal(S1, S)
+
+
+# ----------------------------------------------------------------------------
+# The direct write-strength mode: Gated DeltaNet's learned scalar used as the step size as
+# given (KLA page, "Problem statement"), beside KLA's beta = eta / (||k||^2 + eps).
+def _fwd_mode(impl, mode):
+    if impl == "numpy":
+        return lambda q, k, v, la, eta, eps, init_state=None: kla_ref.forward(q, k, v, la, eta, eps, init_state,
+                                                                                beta_mode=mode)
+
+    def c(q, k, v, la, eta, eps, init_state=None):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        out, fin = cref.forward(q, k, v, la, eta, eps, init_state, beta_mode=mode)
+        return out.reshape(B, H, T, dv).transpose(0, 2, 1, 3), fin.reshape(B, H, dk, dv)
+    return c
+
+
+@pytest.mark.parametrize("impl", ["numpy", "c"])
+def test_direct_equals_kaczmarz_on_unit_keys(impl):
+    """With ||k||^2 + eps = 1 exactly the Kaczmarz step is eta itself, so the modes agree."""
+    rng = np.random.default_rng(21)
+    B, T, H, dk, dv = 1, 40, 2, 8, 5
+    q, _, v, la, eta = _rand(rng, B, T, H, dk, dv)
+    k = np.zeros((B, T, H, dk), np.float32)
+    for idx in np.ndindex(B, T, H):  # four entries of +-1/2: norm exactly 1 in float32
+        k[idx][rng.choice(dk, 4, replace=False)] = rng.choice([-0.5, 0.5], 4)
+    a = _fwd_mode(impl, "direct")(q, k, v, la, eta, 0.0)
+    b = _fwd_mode(impl, "kaczmarz")(q, k, v, la, eta, 0.0)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-12)
+    # and they differ once the keys are not unit vectors
+    c_ = _fwd_mode(impl, "direct")(q, 2 * k, v, la, eta, 0.0)
+    d_ = _fwd_mode(impl, "kaczmarz")(q, 2 * k, v, la, eta, 0.0)
+    assert not np.allclose(c_[1], d_[1])
+
+
+@pytest.mark.parametrize("impl", ["numpy", "c"])
+def test_write_residual_law(impl):
+    """A write scales the residual on its own key by (1 - beta ||k||^2): the Kaczmarz step
+    leaves 1 - eta whatever the key's norm, while the learned scalar taken as given over-
+    corrects a large-norm key (the factor goes below -1) and under-corrects a small one."""
+    rng = np.random.default_rng(22)
+    dk, dv = 6, 4
+    eta32 = np.float32(0.7)
+    for scale in (3.0, 0.2):
+        S0 = rng.standard_normal((1, 1, dk, dv)).astype(np.float32)
+        k = (rng.standard_normal((1, 1, 1, dk)) * scale).astype(np.float32)
+        q = rng.standard_normal((1, 1, 1, dk)).astype(np.float32)
+        v = rng.standard_normal((1, 1, 1, dv)).astype(np.float32)
+        la = np.full((1, 1, 1), np.log(0.9), np.float32)
+        eta = np.full((1, 1, 1), eta32, np.float32)
+        kk = k[0, 0, 0].astype(np.float64)
+        nk = kk @ kk
+        S_dec = np.exp(np.float64(la[0, 0, 0])) * S0[0, 0].astype(np.float64)
+        e0 = v[0, 0, 0].astype(np.float64) - S_dec.T @ kk
+        for mode, factor in (("direct", 1 - np.float64(eta32) * nk), ("kaczmarz", 1 - np.float64(eta32))):
+            _, S1 = _fwd_mode(impl, mode)(q, k, v, la, eta, 0.0, S0)
+            e1 = v[0, 0, 0].astype(np.float64) - S1[0, 0].T @ kk
+            np.testing.assert_allclose(e1, factor * e0, rtol=1e-10, atol=1e-12)
+            if mode == "direct":
+                assert (factor < -1) if scale > 1 else (factor > 1 - np.float64(eta32))
+
+
+def test_numpy_equals_c_direct_mode():
+    rng = np.random.default_rng(23)
+    B, T, H, dk, dv = 2, 50, 2, 16, 8
+    q, k, v, la, eta = _rand(rng, B, T, H, dk, dv)
+    k *= 0.3  # keep ||k||^2 eta below 2 so the direct write stays stable over the run
+    S0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    o1, F1 = kla_ref.forward(q, k, v, la, eta, 1e-6, S0, beta_mode="direct")
+    o2, F2 = _fwd_mode("c", "direct")(q, k, v, la, eta, 1e-6, S0)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12 * np.sqrt(np.mean(o1 ** 2)))
+    np.testing.assert_allclose(F2, F1, rtol=1e-12, atol=1e-12)
+    st = S0.astype(np.float64)[:, :, :, :].reshape(B * H, dk, dv).copy()
+    out = cref.decode_step(st, q[:, 0], k[:, 0], v[:, 0], la[:, 0], eta[:, 0], 1e-6, beta_mode="direct")
+    o_ref, S_ref = kla_ref.decode_step(S0, q[:, 0], k[:, 0], v[:, 0], la[:, 0], eta[:, 0], 1e-6, beta_mode="direct")
+    np.testing.assert_allclose(out.reshape(B, H, dv), o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st.reshape(B, H, dk, dv), S_ref, rtol=1e-12, atol=1e-12)
