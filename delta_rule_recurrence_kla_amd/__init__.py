@@ -24,6 +24,7 @@ _lib = None
 
 KLA_OK, KLA_ERR_INVALID_ARG, KLA_ERR_UNSUPPORTED, KLA_ERR_HIP, KLA_ERR_OOM = range(5)
 PATHS = {"auto": 0, "sequential": 1, "scan": 2}
+BETA_MODES = {"kaczmarz": 0, "direct": 1}
 DTYPES = {"bf16": 0, "f32": 1}
 _PATH_NAMES = {v: k for k, v in PATHS.items()}
 _STATUS_NAMES = {0: "KLA_OK", 1: "KLA_ERR_INVALID_ARG", 2: "KLA_ERR_UNSUPPORTED", 3: "KLA_ERR_HIP", 4: "KLA_ERR_OOM"}
@@ -55,12 +56,13 @@ def load():
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.kla_chunk_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_f32.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
-    lib.kla_chunk_fwd_ex.argtypes = [I, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.kla_chunk_fwd_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
     lib.kla_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(S)]
     lib.kla_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_f32.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
+    lib.kla_decode_step_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, I, I, I, I, P]
     for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_plan", "kla_decode_step",
-               "kla_decode_step_f32", "kla_timing_enable", "kla_timing_select"):
+               "kla_decode_step_f32", "kla_decode_step_ex", "kla_timing_enable", "kla_timing_select"):
         getattr(lib, fn).restype = I
     lib.kla_timing_enable.argtypes = [I]
     lib.kla_timing_select.argtypes = [ctypes.c_char_p]
@@ -112,9 +114,10 @@ def _need(t, name, shape, dtypes, device):
 
 def chunk_fwd(q, k, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk: int = 64,
               path: str = "auto", segments: int = 0, out=None, final_state=None,
-              want_final: bool = True, stream=None) -> Tuple[object, Optional[object]]:
+              want_final: bool = True, stream=None, beta_mode: str = "kaczmarz") -> Tuple[object, Optional[object]]:
     """Chunkwise KLA prefill. q, k [B,T,H,dk] and v [B,T,H,dv] in bf16 (or all fp32);
-    log_alpha, eta fp32 [B,T,H]; init_state fp32 [B,H,dk,dv] or None.
+    log_alpha, eta fp32 [B,T,H]; init_state fp32 [B,H,dk,dv] or None. beta_mode "kaczmarz"
+    (KLA) or "direct" (beta = eta as given, the Gated DeltaNet rule).
     Returns (out fp32 [B,T,H,dv], final_state fp32 [B,H,dk,dv] or None)."""
     import torch
     lib = load()
@@ -143,27 +146,33 @@ def chunk_fwd(q, k, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk
         _need(final_state, "final_state", (B, H, dk, dv), (torch.float32,), dev)
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
-    st = lib.kla_chunk_fwd_ex(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(eta), float(eps),
+    if beta_mode not in BETA_MODES:
+        raise ValueError(f"beta_mode must be one of {sorted(BETA_MODES)}")
+    st = lib.kla_chunk_fwd_ex(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(eta), float(eps),
                               _ptr(init_state), _ptr(out), _ptr(final_state), B, T, H, dk, dv, chunk,
                               PATHS[path], int(segments), _stream(stream))
     _check(st)
     return out, final_state
 
 
-def decode_step(q, k, v, log_alpha, eta, state, eps: float = 1e-6, out=None, stream=None):
+def decode_step(q, k, v, log_alpha, eta, state, eps: float = 1e-6, out=None, stream=None,
+                beta_mode: str = "kaczmarz"):
     """One decode step for N x H states (updated in place). q, k [N,H,dk], v [N,H,dv] in bf16
-    (or all fp32); log_alpha, eta fp32 [N,H]; state fp32 [N,H,dk,dv]. Returns out fp32 [N,H,dv]."""
+    (or all fp32); log_alpha, eta fp32 [N,H]; state fp32 [N,H,dk,dv]; beta_mode as for
+    chunk_fwd. Returns out fp32 [N,H,dv]."""
     import torch
     lib = load()
     N, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
     if q.dtype == torch.bfloat16:
-        fn = lib.kla_decode_step
+        dtype = 0
     elif q.dtype == torch.float32:
-        fn = lib.kla_decode_step_f32
+        dtype = 1
     else:
         raise TypeError("q, k, v must be bfloat16 or float32")
+    if beta_mode not in BETA_MODES:
+        raise ValueError(f"beta_mode must be one of {sorted(BETA_MODES)}")
     _need(k, "k", (N, H, dk), (q.dtype,), dev)
     _need(v, "v", (N, H, dv), (q.dtype,), dev)
     _need(q, "q", (N, H, dk), (q.dtype,), dev)
@@ -173,8 +182,8 @@ def decode_step(q, k, v, log_alpha, eta, state, eps: float = 1e-6, out=None, str
     if out is None:
         out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     _need(out, "out", (N, H, dv), (torch.float32,), dev)
-    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(eta), float(eps), _ptr(state), _ptr(out),
-              N, H, dk, dv, _stream(stream)))
+    _check(lib.kla_decode_step_ex(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                  _ptr(eta), float(eps), _ptr(state), _ptr(out), N, H, dk, dv, _stream(stream)))
     return out
 
 

@@ -193,12 +193,14 @@ kla_status hip_fail(hipError_t e, const char* what) {
   return fail(KLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-kla_status chunk_fwd_impl(kla_dtype dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                          const float* eta, float eps, const float* init_state, float* out, float* final_state,
-                          int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
-                          hipStream_t stream) {
+kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* eta, float eps, const float* init_state, float* out,
+                          float* final_state, int B, int T, int H, int dk, int dv, int chunk, kla_path path,
+                          int segments, hipStream_t stream) {
   kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
   if (st != KLA_OK) return st;
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
+    return fail(KLA_ERR_INVALID_ARG, "unknown beta_mode %d", (int)beta_mode);
   if (path != KLA_PATH_AUTO && path != KLA_PATH_SEQUENTIAL && path != KLA_PATH_SCAN)
     return fail(KLA_ERR_INVALID_ARG, "unknown path %d", (int)path);
   if (segments < 0) return fail(KLA_ERR_INVALID_ARG, "segments must be >= 0");
@@ -234,7 +236,8 @@ kla_status chunk_fwd_impl(kla_dtype dtype, const void* q, const void* k, const v
   float* maps = reinterpret_cast<float*>(base + p.maps_off);
   float* starts = reinterpret_cast<float*>(base + p.starts_off);
 
-  e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, rec, stream); });
+  const int direct = beta_mode == KLA_BETA_DIRECT;
+  e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
   if (e == hipSuccess) {
     if (p.path == KLA_PATH_SEQUENTIAL) {
       e = timed("kla_state_seq", stream, [&] {
@@ -258,10 +261,12 @@ kla_status chunk_fwd_impl(kla_dtype dtype, const void* q, const void* k, const v
   return KLA_OK;
 }
 
-kla_status decode_impl(kla_dtype dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                       const float* eta, float eps, float* state, float* out, int N, int H, int dk, int dv,
-                       hipStream_t stream) {
+kla_status decode_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* eta, float eps, float* state, float* out, int N, int H,
+                       int dk, int dv, hipStream_t stream) {
   if (dtype != KLA_DTYPE_BF16 && dtype != KLA_DTYPE_F32) return fail(KLA_ERR_INVALID_ARG, "unknown dtype");
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
+    return fail(KLA_ERR_INVALID_ARG, "unknown beta_mode %d", (int)beta_mode);
   if (N < 0 || H < 1) return fail(KLA_ERR_INVALID_ARG, "sizes must satisfy N >= 0, H >= 1 (got N=%d H=%d)", N, H);
   if (dk < 1 || dv < 1) return fail(KLA_ERR_INVALID_ARG, "dk and dv must be positive");
   if (!supported_dk(dk)) return fail(KLA_ERR_UNSUPPORTED, "dk=%d not supported (64, 128, 256)", dk);
@@ -272,7 +277,8 @@ kla_status decode_impl(kla_dtype dtype, const void* q, const void* k, const void
     return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta, state and out must be non-null");
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   hipError_t e = timed("kla_decode", stream, [&] {
-    return kla::launch_decode(mode, N, H, dk, dv, q, k, v, log_alpha, eta, eps, state, out, stream);
+    return kla::launch_decode(mode, N, H, dk, dv, q, k, v, log_alpha, eta, eps, beta_mode == KLA_BETA_DIRECT, state,
+                              out, stream);
   });
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return KLA_OK;
@@ -285,23 +291,23 @@ extern "C" {
 kla_status kla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha, const float* eta,
                          float eps, const float* init_state, float* out, float* final_state, int B, int T, int H,
                          int dk, int dv, int chunk, hipStream_t stream) {
-  return chunk_fwd_impl(KLA_DTYPE_BF16, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv,
-                        chunk, KLA_PATH_AUTO, 0, stream);
+  return chunk_fwd_impl(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, q, k, v, log_alpha, eta, eps, init_state, out, final_state,
+                        B, T, H, dk, dv, chunk, KLA_PATH_AUTO, 0, stream);
 }
 
 kla_status kla_chunk_fwd_f32(const float* q, const float* k, const float* v, const float* log_alpha,
                              const float* eta, float eps, const float* init_state, float* out, float* final_state,
                              int B, int T, int H, int dk, int dv, int chunk, hipStream_t stream) {
-  return chunk_fwd_impl(KLA_DTYPE_F32, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv,
-                        chunk, KLA_PATH_AUTO, 0, stream);
+  return chunk_fwd_impl(KLA_DTYPE_F32, KLA_BETA_KACZMARZ, q, k, v, log_alpha, eta, eps, init_state, out, final_state,
+                        B, T, H, dk, dv, chunk, KLA_PATH_AUTO, 0, stream);
 }
 
-kla_status kla_chunk_fwd_ex(kla_dtype dtype, const void* q, const void* k, const void* v, const float* log_alpha,
-                            const float* eta, float eps, const float* init_state, float* out, float* final_state,
-                            int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
-                            hipStream_t stream) {
-  return chunk_fwd_impl(dtype, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv, chunk,
-                        path, segments, stream);
+kla_status kla_chunk_fwd_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* eta, float eps, const float* init_state, float* out,
+                            float* final_state, int B, int T, int H, int dk, int dv, int chunk, kla_path path,
+                            int segments, hipStream_t stream) {
+  return chunk_fwd_impl(dtype, beta_mode, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv,
+                        chunk, path, segments, stream);
 }
 
 kla_status kla_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,
@@ -324,13 +330,19 @@ kla_status kla_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, int ch
 
 kla_status kla_decode_step(const void* q, const void* k, const void* v, const float* log_alpha, const float* eta,
                            float eps, float* state, float* out, int N, int H, int dk, int dv, hipStream_t stream) {
-  return decode_impl(KLA_DTYPE_BF16, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
+  return decode_impl(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
 }
 
 kla_status kla_decode_step_f32(const float* q, const float* k, const float* v, const float* log_alpha,
                                const float* eta, float eps, float* state, float* out, int N, int H, int dk, int dv,
                                hipStream_t stream) {
-  return decode_impl(KLA_DTYPE_F32, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
+  return decode_impl(KLA_DTYPE_F32, KLA_BETA_KACZMARZ, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
+}
+
+kla_status kla_decode_step_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* eta, float eps, float* state, float* out, int N,
+                              int H, int dk, int dv, hipStream_t stream) {
+  return decode_impl(dtype, beta_mode, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
 }
 
 const char* kla_last_error(void) { return g_err.c_str(); }

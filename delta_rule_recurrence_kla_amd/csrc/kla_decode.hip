@@ -3,6 +3,8 @@
 // Per state (KLA page, "KLA update rule"; the recurrent form keeps a constant-size
 // state per head, KLA page "Key contributions" 4):
 //   alpha = exp(log_alpha), beta = eta / (||k||^2 + eps)   (beta = 0 if the denominator is 0)
+//   (with `direct` set, beta = eta: the learned write strength of the Gated DeltaNet rule the
+//   KLA page sets itself against in its "Problem statement")
 //   a = S^T k, b = S^T q                  (one pass over S)
 //   e = v - alpha a                       residual against the decayed state
 //   o = S_new^T q = alpha b + beta (k . q) e
@@ -21,7 +23,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Tr<MODE>::in
                                                      const typename Tr<MODE>::in_t* __restrict__ k,
                                                      const typename Tr<MODE>::in_t* __restrict__ v,
                                                      const float* __restrict__ log_alpha,
-                                                     const float* __restrict__ eta, float eps,
+                                                     const float* __restrict__ eta, float eps, int direct,
                                                      float* __restrict__ state, float* __restrict__ out) {
   using TR = Tr<MODE>;
   constexpr int TPR = DV / 4;     // threads per state row
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Tr<MODE>::in
   const float dkq = sred[1][0] + sred[1][1] + sred[1][2] + sred[1][3];
   const float alpha = expf(log_alpha[nh]);
   const float denom = nk + eps;
-  const float beta = denom != 0.f ? eta[nh] / denom : 0.f;
+  const float beta = direct ? eta[nh] : denom != 0.f ? eta[nh] / denom : 0.f;
 
   float vv[4];
 #pragma unroll
@@ -112,19 +114,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Tr<MODE>::in
 
 template <int MODE, int DK, int DV>
 static hipError_t launch_decode_t(int N, int H, const void* q, const void* k, const void* v, const float* la,
-                                  const float* eta, float eps, float* state, float* out, hipStream_t stream) {
+                                  const float* eta, float eps, int direct, float* state, float* out,
+                                  hipStream_t stream) {
   using in_t = typename Tr<MODE>::in_t;
   return launch_kernel(decode_kernel<MODE, DK, DV>, dim3(N * H), dim3(256), stream, static_cast<const in_t*>(q),
-                       static_cast<const in_t*>(k), static_cast<const in_t*>(v), la, eta, eps, state, out);
+                       static_cast<const in_t*>(k), static_cast<const in_t*>(v), la, eta, eps, direct, state, out);
 }
 
 template <int MODE>
 static hipError_t dispatch_decode(int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
-                                  const float* la, const float* eta, float eps, float* state, float* out,
-                                  hipStream_t stream) {
+                                  const float* la, const float* eta, float eps, int direct, float* state,
+                                  float* out, hipStream_t stream) {
 #define KLA_DEC_CASE(DKV, DVV)                                                                      \
   if (dk == DKV && dv == DVV)                                                                       \
-    return launch_decode_t<MODE, DKV, DVV>(N, H, q, k, v, la, eta, eps, state, out, stream);
+    return launch_decode_t<MODE, DKV, DVV>(N, H, q, k, v, la, eta, eps, direct, state, out, stream);
   KLA_DEC_CASE(64, 64)
   KLA_DEC_CASE(64, 128)
   KLA_DEC_CASE(128, 64)
@@ -136,10 +139,11 @@ static hipError_t dispatch_decode(int N, int H, int dk, int dv, const void* q, c
 }
 
 hipError_t launch_decode(int mode, int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
-                         const float* log_alpha, const float* eta, float eps, float* state, float* out,
-                         hipStream_t stream) {
-  if (mode == MODE_BF16) return dispatch_decode<MODE_BF16>(N, H, dk, dv, q, k, v, log_alpha, eta, eps, state, out, stream);
-  return dispatch_decode<MODE_F32>(N, H, dk, dv, q, k, v, log_alpha, eta, eps, state, out, stream);
+                         const float* log_alpha, const float* eta, float eps, int direct, float* state,
+                         float* out, hipStream_t stream) {
+  if (mode == MODE_BF16)
+    return dispatch_decode<MODE_BF16>(N, H, dk, dv, q, k, v, log_alpha, eta, eps, direct, state, out, stream);
+  return dispatch_decode<MODE_F32>(N, H, dk, dv, q, k, v, log_alpha, eta, eps, direct, state, out, stream);
 }
 
 }  // namespace kla

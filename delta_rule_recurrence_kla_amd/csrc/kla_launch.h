@@ -32,9 +32,10 @@ struct Dims {
   int nc;  // number of 64-token chunks, ceil(T / 64)
 };
 
-// Chunk prep: one wavefront per (b, h, chunk); writes one record per chunk.
+// Chunk prep: one wavefront per (b, h, chunk); writes one record per chunk. `direct` takes
+// beta = eta as given instead of the Kaczmarz step eta / (||k||^2 + eps).
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
-                       const float* eta, float eps, uint8_t* rec, hipStream_t stream);
+                       const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream);
 
 // Sequential inter-chunk state + output: one workgroup per (b, h, 64-column group of dv).
 // init may be null (zero state); fin may be null (not written).
@@ -67,9 +68,9 @@ hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void
 // Copy (or zero when src is null) n floats; used for T == 0 and as a graph-safe fill.
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);
 
-// Single-token decode for N x H states, in place.
+// Single-token decode for N x H states, in place (`direct` as for launch_prep).
 hipError_t launch_decode(int mode, int N, int H, int dk, int dv, const void* q, const void* k,
-                         const void* v, const float* log_alpha, const float* eta, float eps,
+                         const void* v, const float* log_alpha, const float* eta, float eps, int direct,
                          float* state, float* out, hipStream_t stream);
 
 }  // namespace kla

@@ -65,7 +65,7 @@ __device__ __forceinline__ F8 a_frag(const float* sA, int I, int C0, int ln, int
 template <int MODE, int DK, bool COMPACT>
 __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                    const float* __restrict__ log_alpha,
-                                                   const float* __restrict__ eta, float eps,
+                                                   const float* __restrict__ eta, float eps, int direct,
                                                    uint8_t* __restrict__ rec, int T, int H, int nc, int nchunks) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
   const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 63));
   wave_sync();
   const float denom = sNB[lane] + eps;
-  const float beta = denom != 0.f ? et / denom : 0.f;
+  // the Kaczmarz step, or (direct) the learned write strength as given
+  const float beta = direct ? et : denom != 0.f ? et / denom : 0.f;
   wave_sync();
   sNB[lane] = beta;
   sGv[lane] = g;
@@ -353,29 +354,29 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
 
 template <int MODE, int DK>
 static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, const float* la, const float* eta,
-                                float eps, uint8_t* rec, hipStream_t stream) {
+                                float eps, int direct, uint8_t* rec, hipStream_t stream) {
   const int nchunks = d.B * d.H * d.nc;
   if (state_dma_supported(MODE, DK))
     return launch_kernel(prep_kernel<MODE, DK, true>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
-                         rec, d.T, d.H, d.nc, nchunks);
+                         direct, rec, d.T, d.H, d.nc, nchunks);
   return launch_kernel(prep_kernel<MODE, DK, false>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
-                       rec, d.T, d.H, d.nc, nchunks);
+                       direct, rec, d.T, d.H, d.nc, nchunks);
 }
 
 int record_bytes(int mode, int dk) { return state_dma_supported(mode, dk) ? CREC_BYTES : REC_BYTES; }
 
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
-                       const float* eta, float eps, uint8_t* rec, hipStream_t stream) {
+                       const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream) {
   if (mode == MODE_BF16) {
     switch (d.dk) {
-      case 64: return launch_prep_t<MODE_BF16, 64>(d, q, k, log_alpha, eta, eps, rec, stream);
-      case 128: return launch_prep_t<MODE_BF16, 128>(d, q, k, log_alpha, eta, eps, rec, stream);
-      case 256: return launch_prep_t<MODE_BF16, 256>(d, q, k, log_alpha, eta, eps, rec, stream);
+      case 64: return launch_prep_t<MODE_BF16, 64>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
+      case 128: return launch_prep_t<MODE_BF16, 128>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
+      case 256: return launch_prep_t<MODE_BF16, 256>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
     }
   } else {
     switch (d.dk) {
-      case 64: return launch_prep_t<MODE_F32, 64>(d, q, k, log_alpha, eta, eps, rec, stream);
-      case 128: return launch_prep_t<MODE_F32, 128>(d, q, k, log_alpha, eta, eps, rec, stream);
+      case 64: return launch_prep_t<MODE_F32, 64>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
+      case 128: return launch_prep_t<MODE_F32, 128>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
     }
   }
   return hipErrorInvalidValue;

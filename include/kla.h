@@ -57,6 +57,19 @@ typedef enum {
 
 typedef enum { KLA_DTYPE_BF16 = 0, KLA_DTYPE_F32 = 1 } kla_dtype;
 
+/*
+ * Write strength beta_t of each token's update.
+ *   KLA_BETA_KACZMARZ  beta_t = eta_t / (||k_t||^2 + eps): the KLA rule (KLA page,
+ *                      "KLA update rule"); what kla_chunk_fwd and kla_decode_step use.
+ *   KLA_BETA_DIRECT    beta_t = eta_t as given: the learned-scalar step of Gated
+ *                      DeltaNet that the KLA page sets KLA against (its "Problem
+ *                      statement"). eps is unused. Same kernels, same layouts.
+ */
+typedef enum {
+  KLA_BETA_KACZMARZ = 0,
+  KLA_BETA_DIRECT = 1
+} kla_beta_mode;
+
 typedef enum {
   KLA_PATH_AUTO = 0,       /* let the library choose */
   KLA_PATH_SEQUENTIAL = 1, /* one walk over all chunks per (b, h, 64 dv columns) */
@@ -92,13 +105,14 @@ kla_status kla_chunk_fwd_f32(const float* q, const float* k, const float* v, con
                              hipStream_t stream);
 
 /*
- * kla_chunk_fwd with the input dtype and the inter-chunk path chosen by the
- * caller. `segments` is the number of scan segments for KLA_PATH_SCAN
- * (0 = library choice; clamped to the number of chunks); ignored otherwise.
- * Results of both paths agree to rounding.
+ * kla_chunk_fwd with the input dtype, the write strength and the inter-chunk
+ * path chosen by the caller. `segments` is the number of scan segments for
+ * KLA_PATH_SCAN (0 = library choice; clamped to the number of chunks); ignored
+ * otherwise. Results of both paths agree to rounding. An unknown beta_mode or
+ * path returns KLA_ERR_INVALID_ARG.
  */
-kla_status kla_chunk_fwd_ex(kla_dtype dtype, const void* q, const void* k, const void* v,
-                            const float* log_alpha, const float* eta, float eps,
+kla_status kla_chunk_fwd_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                            const void* v, const float* log_alpha, const float* eta, float eps,
                             const float* init_state, float* out, float* final_state, int B, int T,
                             int H, int dk, int dv, int chunk, kla_path path, int segments,
                             hipStream_t stream);
@@ -131,6 +145,12 @@ kla_status kla_decode_step(const void* q, const void* k, const void* v, const fl
 kla_status kla_decode_step_f32(const float* q, const float* k, const float* v,
                                const float* log_alpha, const float* eta, float eps, float* state,
                                float* out, int N, int H, int dk, int dv, hipStream_t stream);
+
+/* kla_decode_step with the input dtype and the write strength chosen by the caller. */
+kla_status kla_decode_step_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                              const void* v, const float* log_alpha, const float* eta, float eps,
+                              float* state, float* out, int N, int H, int dk, int dv,
+                              hipStream_t stream);
 
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* kla_last_error(void);

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_decode_step",
+    for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_decode_step", "kla_decode_step_ex",
               "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
               "kla_timing_enable", "kla_timing_collect", "kla_timing_select"):
         assert n in names
@@ -53,8 +53,8 @@ def test_version_and_empty_error():
     assert isinstance(kla.last_error(), str)
 
 
-def _chunk(lib, dtype=0, q=FAKE, out=FAKE, B=1, T=64, H=1, dk=64, dv=64, chunk=64, path=0, segs=0):
-    return lib.kla_chunk_fwd_ex(dtype, q, FAKE, FAKE, FAKE, FAKE, 1e-6, None, out, None,
+def _chunk(lib, dtype=0, beta=0, q=FAKE, out=FAKE, B=1, T=64, H=1, dk=64, dv=64, chunk=64, path=0, segs=0):
+    return lib.kla_chunk_fwd_ex(dtype, beta, q, FAKE, FAKE, FAKE, FAKE, 1e-6, None, out, None,
                                 B, T, H, dk, dv, chunk, path, segs, None)
 
 
@@ -62,6 +62,7 @@ def _chunk(lib, dtype=0, q=FAKE, out=FAKE, B=1, T=64, H=1, dk=64, dv=64, chunk=6
     (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1), (dict(q=None), 1), (dict(out=None), 1),
     (dict(dk=96), 2), (dict(dv=256), 2), (dict(chunk=32), 2), (dict(dtype=7), 1),
     (dict(dtype=1, dk=256), 2), (dict(path=5), 1), (dict(segs=-1), 1), (dict(B=70000, H=1), 2),
+    (dict(beta=2), 1), (dict(beta=-1), 1),
 ])
 def test_prefill_validation(kw, status):
     lib = kla.load()
@@ -80,6 +81,14 @@ def test_decode_validation(args, status):
     st = lib.kla_decode_step(a["q"], FAKE, FAKE, FAKE, FAKE, 1e-6, a["state"], FAKE,
                              a["N"], a["H"], a["dk"], a["dv"], None)
     assert st == status
+
+
+@pytest.mark.parametrize("dtype,beta,status", [(0, 2, 1), (7, 0, 1), (1, 1, 0), (0, 1, 0)])
+def test_decode_ex_validation(dtype, beta, status):
+    lib = kla.load()
+    # N = 0: validated, then nothing to do (no device access)
+    assert lib.kla_decode_step_ex(dtype, beta, None, None, None, None, None, 1e-6, None, None, 0, 4, 128, 128,
+                                  None) == status
 
 
 def test_decode_zero_sequences_is_a_no_op():

@@ -160,6 +160,69 @@ def test_prefill_odd_grids(dtype, dk, dv, B, H, T):
         assert_close(S, S_ref, TOL[dtype], f"final state ({path})")
 
 
+def _direct_mode_case(dtype, dk, dv, T, seed):
+    """Keys of norm s in [0.6, 1.6] and eta in [0, 0.7): eta ||k||^2 < 1.8, so the direct write
+    (beta = eta as given) stays non-expansive and the run is well conditioned."""
+    name = "lm_layer_4k" if dtype == "bf16" else "tiny_f32"
+    wl = W.make_prefill(name, seed=seed, B=2, T=T, H=2, dk=dk, dv=dv, init_std=0.3)
+    rng = np.random.default_rng(seed)
+    k = wl.k.astype(np.float64)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    k *= np.clip(np.exp(0.25 * rng.standard_normal(k.shape[:-1] + (1,))), 0.6, 1.6)
+    k = k.astype(np.float32)
+    if dtype == "bf16":
+        k = W.round_to_bf16(k)
+    eta = (0.7 * rng.uniform(0, 1, wl.eta.shape)).astype(np.float32)
+    return dataclasses.replace(wl, k=k, eta=eta)
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 256, 128),
+                                         ("f32", 64, 64), ("f32", 128, 64)])
+@pytest.mark.parametrize("path", ["sequential", "scan"])
+def test_prefill_direct_beta_mode(dtype, dk, dv, path):
+    """beta = eta as given (the Gated DeltaNet rule) through the same kernels, against the oracle's
+    direct mode; and the two modes differ on these keys."""
+    log(f"prefill direct beta {dtype} dk={dk} dv={dv} path={path}")
+    wl = _direct_mode_case(dtype, dk, dv, 300, 31 + dk)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    out, fin = kla.chunk_fwd(q, k, v, la, eta, wl.eps, init_state=s0, path=path, segments=3, beta_mode="direct")
+    torch.cuda.synchronize()
+    o_ref, S_ref = cref.forward(wl.q, wl.k, wl.v, wl.log_alpha, wl.eta, wl.eps, wl.init_state, beta_mode="direct")
+    B, T, H = wl.B, wl.T, wl.H
+    o_ref = o_ref.reshape(B, H, T, dv).transpose(0, 2, 1, 3)
+    S_ref = S_ref.reshape(B, H, dk, dv)
+    assert_close(out.cpu().numpy(), o_ref, TOL[dtype], "out")
+    assert_close(fin.cpu().numpy(), S_ref, TOL[dtype], "final state")
+    o_k, _ = oracle_prefill(wl)
+    assert err_over_rms(o_k, o_ref) > 10 * TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_direct_beta_mode(dtype):
+    log(f"decode direct beta {dtype}")
+    rng = np.random.default_rng(41)
+    N, H, dk, dv = 8, 4, 128, 128
+    S0 = (0.3 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+    q = rng.standard_normal((N, H, dk)).astype(np.float32)
+    k = rng.standard_normal((N, H, dk)).astype(np.float32)
+    k *= (1.3 / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = rng.standard_normal((N, H, dv)).astype(np.float32)
+    la = np.log(rng.uniform(0.8, 1.0, (N, H))).astype(np.float32)
+    eta = rng.uniform(0.1, 1.0, (N, H)).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = (W.round_to_bf16(x) for x in (q, k, v))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    st = torch.from_numpy(S0).to(dev)
+    out = kla.decode_step(*(torch.from_numpy(x).to(dev).to(tdt) for x in (q, k, v)),
+                          torch.from_numpy(la).to(dev), torch.from_numpy(eta).to(dev), st, 1e-6,
+                          beta_mode="direct")
+    torch.cuda.synchronize()
+    o_ref, S_ref = kla_ref.decode_step(S0, q, k, v, la, eta, 1e-6, beta_mode="direct")
+    assert_close(out.cpu().numpy(), o_ref, TOL["f32"], "out")
+    assert_close(st.cpu().numpy(), S_ref, TOL["f32"], "state")
+
+
 def test_timing_hook_selects_one_kernel():
     """With a kernel selected, the hook records that kernel's launches and no other."""
     wl = W.make_prefill("lm_layer_4k", seed=3, B=1, T=256, H=2)
