@@ -7,7 +7,10 @@ it, and the two share no code.
 
   kla_ref.py   plain NumPy token-by-token recurrence (the definition)
   kla_ref.c    the same recurrence in plain C, OpenMP over heads
+  psd_lift.py  the rank-one PSD lift psi(u) = vec(u u^T) of queries and keys
+               (features rounded to bf16) in front of kla_ref.forward
   cref.py      ctypes loader for the C build
   build.py     gcc build of kla_ref.c into oracle/libkla_ref.so
 """
 from . import kla_ref  # noqa: F401
+from . import psd_lift  # noqa: F401
