@@ -7,6 +7,7 @@ Every step of the computation runs in the library's HIP kernels; there is no
 fallback. PyTorch provides device memory and streams.
 
     out, S = chunk_fwd(q, k, v, log_alpha, eta, eps, init_state=None)
+    out, S = chunk_fwd_psd(uq, uk, v, log_alpha, eta, eps)     # q, k = psi(u) formed in the kernels
     out = decode_step(q, k, v, log_alpha, eta, state, eps)     # state updated in place
 """
 from __future__ import annotations
@@ -15,7 +16,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["chunk_fwd", "decode_step", "plan", "version", "last_error", "timing_enable",
+__all__ = ["chunk_fwd", "chunk_fwd_psd", "decode_step", "plan", "version", "last_error", "timing_enable",
            "timing_collect", "lib_path", "load", "KLAError", "PATHS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,11 +58,12 @@ def load():
     lib.kla_chunk_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_f32.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.kla_chunk_fwd_psd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
     lib.kla_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(S)]
     lib.kla_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_f32.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, I, I, I, I, P]
-    for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_plan", "kla_decode_step",
+    for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
                "kla_decode_step_f32", "kla_decode_step_ex", "kla_timing_enable", "kla_timing_select"):
         getattr(lib, fn).restype = I
     lib.kla_timing_enable.argtypes = [I]
@@ -152,6 +154,41 @@ def chunk_fwd(q, k, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk
                               _ptr(init_state), _ptr(out), _ptr(final_state), B, T, H, dk, dv, chunk,
                               PATHS[path], int(segments), _stream(stream))
     _check(st)
+    return out, final_state
+
+
+def chunk_fwd_psd(uq, uk, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk: int = 64,
+                  path: str = "auto", segments: int = 0, out=None, final_state=None,
+                  want_final: bool = True, stream=None) -> Tuple[object, Optional[object]]:
+    """Chunkwise KLA prefill with the rank-one PSD lift done in the kernels: uq, uk bf16
+    [B,T,H,p] (p = 16), v bf16 [B,T,H,dv]; the kernels use q = psi(uq), k = psi(uk) with
+    psi(u) = vec(u u^T) rounded to bf16 (dk = p*p). Other arguments as for chunk_fwd.
+    Returns (out fp32 [B,T,H,dv], final_state fp32 [B,H,p*p,dv] or None)."""
+    import torch
+    lib = load()
+    B, T, H, p = uq.shape
+    dv = v.shape[-1]
+    dk = p * p
+    dev = uq.device
+    _need(uq, "uq", (B, T, H, p), (torch.bfloat16,), dev)
+    _need(uk, "uk", (B, T, H, p), (torch.bfloat16,), dev)
+    _need(v, "v", (B, T, H, dv), (torch.bfloat16,), dev)
+    _need(log_alpha, "log_alpha", (B, T, H), (torch.float32,), dev)
+    _need(eta, "eta", (B, T, H), (torch.float32,), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (B, H, dk, dv), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, T, H, dv), (torch.float32,), dev)
+    if final_state is None and want_final:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (B, H, dk, dv), (torch.float32,), dev)
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    _check(lib.kla_chunk_fwd_psd(_ptr(uq), _ptr(uk), _ptr(v), _ptr(log_alpha), _ptr(eta), float(eps),
+                                 _ptr(init_state), _ptr(out), _ptr(final_state), B, T, H, p, dv, chunk,
+                                 PATHS[path], int(segments), _stream(stream)))
     return out, final_state
 
 

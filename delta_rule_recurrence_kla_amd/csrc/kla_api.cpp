@@ -196,7 +196,7 @@ kla_status hip_fail(hipError_t e, const char* what) {
 kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* eta, float eps, const float* init_state, float* out,
                           float* final_state, int B, int T, int H, int dk, int dv, int chunk, kla_path path,
-                          int segments, hipStream_t stream) {
+                          int segments, hipStream_t stream, int lift = 0) {
   kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
   if (st != KLA_OK) return st;
   if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
@@ -221,7 +221,7 @@ kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* 
   }
 
   const Plan p = make_plan(dtype, B, T, H, dk, dv, path, segments, device_cus());
-  const kla::Dims d{B, T, H, dk, dv, (T + kChunk - 1) / kChunk};
+  const kla::Dims d{B, T, H, dk, dv, (T + kChunk - 1) / kChunk, lift};
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
 
   keep_pool_warm();
@@ -308,6 +308,16 @@ kla_status kla_chunk_fwd_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void
                             int segments, hipStream_t stream) {
   return chunk_fwd_impl(dtype, beta_mode, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk, dv,
                         chunk, path, segments, stream);
+}
+
+kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, const float* log_alpha,
+                             const float* eta, float eps, const float* init_state, float* out, float* final_state,
+                             int B, int T, int H, int p, int dv, int chunk, kla_path path, int segments,
+                             hipStream_t stream) {
+  if (p < 1) return fail(KLA_ERR_INVALID_ARG, "p must be positive");
+  if (p != kla::LIFT_P_HOST) return fail(KLA_ERR_UNSUPPORTED, "psd lift supports p=%d only (got %d)", kla::LIFT_P_HOST, p);
+  return chunk_fwd_impl(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, uq, uk, v, log_alpha, eta, eps, init_state, out,
+                        final_state, B, T, H, p * p, dv, chunk, path, segments, stream, /*lift=*/1);
 }
 
 kla_status kla_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, int chunk, kla_path path, int segments,

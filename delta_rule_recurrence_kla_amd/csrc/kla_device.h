@@ -99,6 +99,9 @@ __device__ __forceinline__ rsrc_t make_rsrc_wu(const void* base, long long bytes
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, int voff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
 __device__ __forceinline__ void bstore_f32(float x, rsrc_t r, int voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, 0, 0);
 }
@@ -182,6 +185,31 @@ __device__ __forceinline__ S8 split8(const F8& x) {
   s.l = __builtin_convertvector(v - hf, bf16x8);
   return s;
 }
+
+// Fused PSD lift (KATA page, section 2.2: psi(u) = vec(u u^T), feature a*16 + b = u_a u_b).
+// The kernels that read queries and keys in lifted form take the 16-wide u rows of bf16 and
+// form the features as they load them. LIFT_P is the width of u, LIFT_DK the feature width.
+constexpr int LIFT_P = 16;
+constexpr int LIFT_DK = LIFT_P * LIFT_P;
+
+// Eight lifted features u_a * u_{b0 + i}, i = 0..7, each rounded to the nearest bf16 (ties to
+// even), as 16 raw bytes. `ua_bits` holds u_a in the high half of a word; `ub` holds
+// u_{b0} .. u_{b0+7} as bf16. The product of two bf16 values has at most 16 significant
+// bits, so the fp32 multiply is exact and the conversion is the only rounding.
+__device__ __forceinline__ u32x4 lift8(uint32_t ua_bits, const u32x4& ub) {
+  const float ua = __uint_as_float(ua_bits & 0xFFFF0000u);
+  f32x8 f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    f[2 * m] = ua * __uint_as_float(ub[m] << 16);
+    f[2 * m + 1] = ua * __uint_as_float(ub[m] & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(u32x4, __builtin_convertvector(f, bf16x8));
+}
+
+// u_a of a lifted row as the high half of a word: `w` is the 32-bit word holding u_{2m} (low
+// half) and u_{2m+1} (high half), `odd` picks u_{2m+1}.
+__device__ __forceinline__ uint32_t lift_pick(uint32_t w, bool odd) { return odd ? w : w << 16; }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

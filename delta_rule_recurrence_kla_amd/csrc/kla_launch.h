@@ -26,10 +26,14 @@ inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t str
   return hipGetLastError();
 }
 
+// Width of the u rows that the fused PSD lift takes (the kernels' LIFT_P).
+constexpr int LIFT_P_HOST = 16;
+
 // Per-launch size bundle shared by the prefill kernels.
 struct Dims {
   int B, T, H, dk, dv;
-  int nc;  // number of 64-token chunks, ceil(T / 64)
+  int nc;        // number of 64-token chunks, ceil(T / 64)
+  int lift = 0;  // q and k hold 16-wide u rows; the kernels form the dk = 256 PSD features
 };
 
 // Chunk prep: one wavefront per (b, h, chunk); writes one record per chunk. `direct` takes

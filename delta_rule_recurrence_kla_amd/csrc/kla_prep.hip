@@ -31,12 +31,19 @@
 // The inverse, by block rows (D_I = (I + A_II)^-1, found by forward substitution):
 //   T_II = D_I,   T_IJ = -D_I X_IJ,   X_IJ = sum_{C=J}^{I-1} A_IC T_CJ   (J < I).
 //
+// With LIFT = true, q and k arrive as the 16-wide vectors u of the KATA page's rank-one PSD
+// feature (section 2.2) and each key/query fragment is formed from them as it is loaded:
+// feature 16a + b is u_a u_b, rounded to bf16, so the products below see exactly the 256
+// features the unfused path would read.
+//
 // Tokens past T in the last chunk enter as identity steps: k = q = 0, log_alpha = 0,
 // eta = 0, so their rows and columns of T' and P are zero.
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
+
+static_assert(LIFT_P_HOST == LIFT_P, "host and kernels must agree on the lift width");
 
 namespace {
 
@@ -62,7 +69,7 @@ __device__ __forceinline__ F8 a_frag(const float* sA, int I, int C0, int ln, int
 
 }  // namespace
 
-template <int MODE, int DK, bool COMPACT>
+template <int MODE, int DK, bool COMPACT, bool LIFT>
 __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                    const float* __restrict__ log_alpha,
                                                    const float* __restrict__ eta, float eps, int direct,
@@ -72,6 +79,8 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
   using XF = typename TR::XF;
   using DF = typename TR::DF;
   constexpr int SZ = static_cast<int>(sizeof(in_t));
+  static_assert(!LIFT || (MODE == MODE_BF16 && DK == LIFT_DK && !COMPACT), "the lift makes 256 bf16 features");
+  constexpr int KIN = LIFT ? LIFT_P : DK;  // elements of a query/key row in memory
 
   // One wave per workgroup (17.3 KB of LDS), so that LDS, not the workgroup shape, sets how
   // many chunks a CU holds: nine, against eight as four-wave groups (about 6% faster).
@@ -92,7 +101,7 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
   float* sGv = sVec[1];
 
   // ---- G = K K^T and QK = Q K^T on the lower 10 tiles, operands straight from memory ----
-  const int rowK = H * DK * SZ;
+  const int rowK = H * KIN * SZ;
   const size_t chunk_off = (static_cast<size_t>(b) * T + t0) * rowK;
   const long long avail = static_cast<long long>(T - t0) * rowK;
   const rsrc_t rk = make_rsrc_wu(static_cast<const uint8_t*>(kv) + chunk_off, avail);
@@ -126,6 +135,20 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
     }
     __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the products
   }
+  // Lifted rows: the chunk's u rows (32 bytes each, keys then queries) go to the staging
+  // strip, which is free until the products are done; lane t loads token t's rows.
+  uint8_t* sU = reinterpret_cast<uint8_t*>(st);
+  if constexpr (LIFT) {
+    static_assert(2 * CHUNK * LIFT_P * 2 <= static_cast<int>(sizeof(st)), "u rows fit the strip");
+    const int off = lane * rowK + h * LIFT_P * 2;
+    const u32x4 k0 = bload16(rk, off), k1 = bload16(rk, off + 16);
+    const u32x4 q0 = bload16(rq, off), q1 = bload16(rq, off + 16);
+    *reinterpret_cast<u32x4*>(sU + 32 * lane) = k0;
+    *reinterpret_cast<u32x4*>(sU + 32 * lane + 16) = k1;
+    *reinterpret_cast<u32x4*>(sU + 2048 + 32 * lane) = q0;
+    *reinterpret_cast<u32x4*>(sU + 2048 + 32 * lane + 16) = q1;
+    wave_sync();
+  }
 
 #pragma unroll
   for (int kb = 0; kb < DK / 32; ++kb) {
@@ -135,6 +158,18 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
       const int off = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 4 * gq) * SZ;
       if constexpr (PRELOAD) {
         kf[x] = kall[kb][x];
+      } else if constexpr (LIFT) {
+        // features 32kb + 8gq + 0..7 = 16a + b0 + 0..7 with a = 2kb + (gq >> 1), b0 = 8 (gq & 1):
+        // u_a is half (gq >> 1) of word kb of the row, u_b0.. the row's half (gq & 1)
+        const bool odd = (gq >> 1) != 0;
+        const uint8_t* ukr = sU + 32 * (16 * x + ln);
+        const uint8_t* uqr = ukr + 2048;
+        const uint32_t kw = *reinterpret_cast<const uint32_t*>(ukr + 4 * kb);
+        const uint32_t qw = *reinterpret_cast<const uint32_t*>(uqr + 4 * kb);
+        const u32x4 kbv = *reinterpret_cast<const u32x4*>(ukr + 16 * (gq & 1));
+        const u32x4 qbv = *reinterpret_cast<const u32x4*>(uqr + 16 * (gq & 1));
+        kf[x] = __builtin_bit_cast(bf16x8, lift8(lift_pick(kw, odd), kbv));
+        qf[x] = __builtin_bit_cast(bf16x8, lift8(lift_pick(qw, odd), qbv));
       } else if constexpr (MODE == MODE_BF16) {
         const int off8 = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 8 * gq) * SZ;  // as in the preload
         kf[x] = __builtin_bit_cast(bf16x8, bload16(rk, off8));
@@ -352,14 +387,14 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
   }
 }
 
-template <int MODE, int DK>
+template <int MODE, int DK, bool LIFT = false>
 static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, const float* la, const float* eta,
                                 float eps, int direct, uint8_t* rec, hipStream_t stream) {
   const int nchunks = d.B * d.H * d.nc;
-  if (state_dma_supported(MODE, DK))
-    return launch_kernel(prep_kernel<MODE, DK, true>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
+  if (!LIFT && state_dma_supported(MODE, DK))
+    return launch_kernel(prep_kernel<MODE, DK, true, false>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
                          direct, rec, d.T, d.H, d.nc, nchunks);
-  return launch_kernel(prep_kernel<MODE, DK, false>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
+  return launch_kernel(prep_kernel<MODE, DK, false, LIFT>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
                        direct, rec, d.T, d.H, d.nc, nchunks);
 }
 
@@ -367,6 +402,11 @@ int record_bytes(int mode, int dk) { return state_dma_supported(mode, dk) ? CREC
 
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
                        const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream) {
+  if (d.lift) {
+    if (mode == MODE_BF16 && d.dk == LIFT_DK)
+      return launch_prep_t<MODE_BF16, LIFT_DK, true>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
+    return hipErrorInvalidValue;
+  }
   if (mode == MODE_BF16) {
     switch (d.dk) {
       case 64: return launch_prep_t<MODE_BF16, 64>(d, q, k, log_alpha, eta, eps, direct, rec, stream);

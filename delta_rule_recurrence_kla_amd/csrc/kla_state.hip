@@ -22,6 +22,11 @@
 // columns zero in the identity part yields [M | N] (AUG = true). A short sequential
 // pass composes the maps of all segments into each segment's true start state, and
 // a final walk per segment produces the outputs.
+//
+// With LIFT = true the queries and keys arrive as the 16-wide vectors u of the KATA page's
+// rank-one PSD feature (section 2.2) and the kernel forms the 256 features u_a u_b (rounded
+// to bf16) as it moves each chunk's rows from the prefetch registers into LDS. Everything
+// after LDS is the dk = 256 kernel unchanged; the rows read from memory shrink 16-fold.
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -65,7 +70,7 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t lo, uint32_t hi, int ha
   return __builtin_amdgcn_perm(hi, lo, half ? 0x07060302u : 0x05040100u);
 }
 
-template <int MODE, int DK, bool WITH_OUT, bool AUG>
+template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT>
 __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
@@ -84,6 +89,8 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   constexpr int VPT = (VBLK + NT - 1) / NT;
   constexpr int TPT = CHUNK * 16 / NT;         // T' (and P) vectors per thread
   static_assert(!AUG || DK % NCOLS == 0, "identity/value columns must not share a workgroup");
+  static_assert(!LIFT || (MODE == MODE_BF16 && DK == LIFT_DK), "the lift makes 256 bf16 features");
+  constexpr int KIN = LIFT ? LIFT_P : DK;      // elements of a query/key row in memory
   static_assert((KCB & (KCB - 1)) == 0 && (VCB & (VCB - 1)) == 0, "shape");
 
   __shared__ __align__(16) in_t sK[CHUNK * LDK];
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   const int c_end = min(a.nc, c_begin + a.seg_chunks);
 
   // byte strides between consecutive tokens, and this batch's first rows
-  const int rowK = H * DK * SZ, rowV = H * DV * SZ, rowO = H * DV * 4;
+  const int rowK = H * KIN * SZ, rowV = H * DV * SZ, rowO = H * DV * 4;
   const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
   const uint8_t* qb_ = static_cast<const uint8_t*>(a.q) + static_cast<size_t>(b) * T * rowK;
   const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
@@ -131,6 +138,10 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   // ---- prefetch registers: the next chunk's inputs, loaded while the current one is computed ----
   u32x4 pk[KPT][4];
   u32x4 pq[WITH_OUT ? KPT : 1][4];
+  // lifted rows: pk/pq hold u_{b0} .. u_{b0+7} and pka/pqa the word holding u_a of the same
+  // row, for the features 16a + b0 .. 16a + b0 + 7 of the thread's 16-byte block
+  uint32_t pka[LIFT ? KPT : 1][4];
+  uint32_t pqa[LIFT && WITH_OUT ? KPT : 1][4];
   u32x4 pv[VPT][4];
   u32x4 pt[TPT];
   u32x4 pp[WITH_OUT ? TPT : 1];
@@ -147,11 +158,27 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
       const int blk = tid + NT * u;
       int rb, cb;
       kblk(blk, rb, cb);
-      const int off = blk < KBLK ? 4 * rb * rowK + h * DK * SZ + 16 * cb : BUF_OOB;
+      if constexpr (LIFT) {
+        // features 8cb .. 8cb + 7 = 16a + b0 + 0..7 with a = cb >> 1, b0 = 8 (cb & 1)
+        const int base = 4 * rb * rowK + h * LIFT_P * 2;
+        const int offb = blk < KBLK ? base + 16 * (cb & 1) : BUF_OOB;
+        const int offa = blk < KBLK ? base + 4 * (cb >> 2) : BUF_OOB;
 #pragma unroll
-      for (int u4 = 0; u4 < 4; ++u4) {
-        pk[u][u4] = bload16(rk, off + u4 * rowK);
-        if constexpr (WITH_OUT) pq[u][u4] = bload16(rq, off + u4 * rowK);
+        for (int u4 = 0; u4 < 4; ++u4) {
+          pk[u][u4] = bload16(rk, offb + u4 * rowK);
+          pka[u][u4] = bload4(rk, offa + u4 * rowK);
+          if constexpr (WITH_OUT) {
+            pq[u][u4] = bload16(rq, offb + u4 * rowK);
+            pqa[u][u4] = bload4(rq, offa + u4 * rowK);
+          }
+        }
+      } else {
+        const int off = blk < KBLK ? 4 * rb * rowK + h * DK * SZ + 16 * cb : BUF_OOB;
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) {
+          pk[u][u4] = bload16(rk, off + u4 * rowK);
+          if constexpr (WITH_OUT) pq[u][u4] = bload16(rq, off + u4 * rowK);
+        }
       }
     }
 #pragma unroll
@@ -195,6 +222,14 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
       if (blk < KBLK) {
         int rb, cb;
         kblk(blk, rb, cb);
+        if constexpr (LIFT) {
+          const bool odd = (cb >> 1) & 1;  // u_a is the high half of its word
+#pragma unroll
+          for (int u4 = 0; u4 < 4; ++u4) {
+            pk[u][u4] = lift8(lift_pick(pka[u][u4], odd), pk[u][u4]);
+            if constexpr (WITH_OUT) pq[u][u4] = lift8(lift_pick(pqa[u][u4], odd), pq[u][u4]);
+          }
+        }
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           *reinterpret_cast<u32x4*>(sK + (4 * rb + u4) * LDK + VEC * cb) = pk[u][u4];
@@ -411,13 +446,17 @@ __global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __rest
 // ---------------------------------------------------------------------------
 constexpr int NCOLS_STATE = 64;  // state columns per workgroup (4 waves x 16)
 
-template <int MODE, int DK, bool WITH_OUT, bool AUG>
+template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT = false>
 static hipError_t launch_state_t(int nwg, const StateArgs& a, hipStream_t stream) {
-  return launch_kernel(state_kernel<MODE, DK, WITH_OUT, AUG>, dim3(nwg), dim3(256), stream, a);
+  return launch_kernel(state_kernel<MODE, DK, WITH_OUT, AUG, LIFT>, dim3(nwg), dim3(256), stream, a);
 }
 
 template <bool WITH_OUT, bool AUG>
-static hipError_t dispatch_state(int mode, int dk, int nwg, const StateArgs& a, hipStream_t stream) {
+static hipError_t dispatch_state(int mode, int dk, bool lift, int nwg, const StateArgs& a, hipStream_t stream) {
+  if (lift) {
+    if (mode == MODE_BF16 && dk == LIFT_DK) return launch_state_t<MODE_BF16, LIFT_DK, WITH_OUT, AUG, true>(nwg, a, stream);
+    return hipErrorInvalidValue;
+  }
   if (mode == MODE_BF16) {
     switch (dk) {
       case 64: return launch_state_t<MODE_BF16, 64, WITH_OUT, AUG>(nwg, a, stream);
@@ -437,22 +476,22 @@ hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* 
                             const uint8_t* rec, const float* init, float* out, float* fin,
                             hipStream_t stream) {
   const int ncg = d.dv / NCOLS_STATE;
-  if (state_dma_supported(mode, d.dk))
+  if (!d.lift && state_dma_supported(mode, d.dk))
     return launch_state_dma(true, false, d.dk, ncg * d.B * d.H, q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out,
                             fin, d.dv, 1, 0, ncg, 1, stream);
   StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out, fin, d.dv, 1, 0, ncg, 1};
-  return dispatch_state<true, false>(mode, d.dk, ncg * d.B * d.H, a, stream);
+  return dispatch_state<true, false>(mode, d.dk, d.lift, ncg * d.B * d.H, a, stream);
 }
 
 hipError_t launch_scan_maps(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
                             int seg_chunks, int segs, float* maps, hipStream_t stream) {
   const int ncg = (d.dk + d.dv) / NCOLS_STATE;
-  if (state_dma_supported(mode, d.dk))
+  if (!d.lift && state_dma_supported(mode, d.dk))
     return launch_state_dma(false, true, d.dk, ncg * (segs - 1) * d.B * d.H, nullptr, k, v, rec, d.T, d.H, d.dv, d.nc,
                             seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv, segs - 1, 0, ncg, segs - 1, stream);
   StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv,
               segs - 1, 0, ncg, segs - 1};
-  return dispatch_state<false, true>(mode, d.dk, ncg * (segs - 1) * d.B * d.H, a, stream);
+  return dispatch_state<false, true>(mode, d.dk, d.lift, ncg * (segs - 1) * d.B * d.H, a, stream);
 }
 
 hipError_t launch_scan_starts(const Dims& d, const float* maps, const float* init, int segs, float* starts,
@@ -470,11 +509,11 @@ hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void*
                              const uint8_t* rec, int seg_chunks, int segs, const float* starts, float* out,
                              float* fin, hipStream_t stream) {
   const int ncg = d.dv / NCOLS_STATE;
-  if (state_dma_supported(mode, d.dk))
+  if (!d.lift && state_dma_supported(mode, d.dk))
     return launch_state_dma(true, false, d.dk, ncg * segs * d.B * d.H, q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks,
                             starts, segs, out, fin, d.dv, 1, 1, ncg, segs, stream);
   StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, starts, segs, out, fin, d.dv, 1, 1, ncg, segs};
-  return dispatch_state<true, false>(mode, d.dk, ncg * segs * d.B * d.H, a, stream);
+  return dispatch_state<true, false>(mode, d.dk, d.lift, ncg * segs * d.B * d.H, a, stream);
 }
 
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream) {

@@ -118,6 +118,28 @@ kla_status kla_chunk_fwd_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void
                             hipStream_t stream);
 
 /*
+ * Prefill with the rank-one PSD lift fused into the kernels (KATA page, section
+ * 2.2, "Capacity theory": the feature psi(u) = vec(u u^T), whose inner products
+ * are squared inner products of u). The caller passes the p-wide vectors u for
+ * the queries and the keys instead of the p*p features; the kernels form
+ *     q_t[a*p + b] = bf16(uq_t[a] * uq_t[b]),   k_t[a*p + b] = bf16(uk_t[a] * uk_t[b])
+ * (the exact product of two bf16 values rounded to the nearest bf16, ties to
+ * even) as they load each chunk, and compute exactly what kla_chunk_fwd_ex does
+ * on those features with dk = p*p. Query and key rows read from memory shrink
+ * from p*p to p elements.
+ *
+ *   uq, uk      bf16 device arrays [B,T,H,p]; only p == 16 (dk = 256) is supported
+ *   v, gates, eps, init_state, out, final_state, B, T, H, dv, chunk, path,
+ *   segments    as for kla_chunk_fwd_ex; states are [B,H,p*p,dv]
+ * The write strength is the Kaczmarz step (KLA_BETA_KACZMARZ). Other p, dv or
+ * chunk give KLA_ERR_UNSUPPORTED.
+ */
+kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, const float* log_alpha,
+                             const float* eta, float eps, const float* init_state, float* out,
+                             float* final_state, int B, int T, int H, int p, int dv, int chunk,
+                             kla_path path, int segments, hipStream_t stream);
+
+/*
  * Host-only planning query: which path and segment count kla_chunk_fwd_ex would
  * use for these sizes and input dtype, and the workspace bytes it would allocate
  * (the per-chunk record is smaller for bf16 with dk <= 128). `num_cus` is the

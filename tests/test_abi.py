@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_decode_step", "kla_decode_step_ex",
+    for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_decode_step", "kla_decode_step_ex",
               "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
               "kla_timing_enable", "kla_timing_collect", "kla_timing_select"):
         assert n in names
@@ -68,6 +68,27 @@ def test_prefill_validation(kw, status):
     lib = kla.load()
     assert _chunk(lib, **kw) == status
     assert kla.last_error() != ""
+
+
+def _psd(lib, uq=FAKE, out=FAKE, B=1, T=64, H=1, p=16, dv=64, chunk=64, path=0, segs=0):
+    return lib.kla_chunk_fwd_psd(uq, FAKE, FAKE, FAKE, FAKE, 1e-6, None, out, None, B, T, H, p, dv, chunk, path,
+                                 segs, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=0), 1), (dict(p=8), 2), (dict(p=12), 2), (dict(p=32), 2), (dict(B=0), 1), (dict(T=-1), 1),
+    (dict(uq=None), 1), (dict(out=None), 1), (dict(dv=96), 2), (dict(chunk=16), 2), (dict(path=3), 1),
+    (dict(segs=-2), 1),
+])
+def test_psd_validation(kw, status):
+    lib = kla.load()
+    assert _psd(lib, **kw) == status
+    assert kla.last_error() != ""
+
+
+def test_psd_zero_tokens_without_final_state_is_a_no_op():
+    lib = kla.load()
+    assert _psd(lib, uq=None, out=None, T=0) == 0
 
 
 @pytest.mark.parametrize("args,status", [

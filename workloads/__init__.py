@@ -184,6 +184,51 @@ def make_prefill(name: str = "tiny_f32", seed: int = 0, *, recipe: Optional[str]
 
 
 # ---------------------------------------------------------------------------
+# PSD workload in unlifted form: the p-wide u vectors themselves (for the fused lift)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class PsdInputs:
+    B: int
+    T: int
+    H: int
+    p: int
+    dv: int
+    uq: np.ndarray         # [B, T, H, p], bf16-exact values
+    uk: np.ndarray         # [B, T, H, p], bf16-exact values
+    v: np.ndarray          # [B, T, H, dv], bf16-exact values
+    log_alpha: np.ndarray  # [B, T, H]
+    eta: np.ndarray        # [B, T, H]
+    eps: float
+    init_state: Optional[np.ndarray]  # [B, H, p*p, dv] or None
+
+
+def make_psd_u(seed: int = 0, *, B: int = 4, T: int = 8192, H: int = 8, p: int = 16, dv: int = 128,
+               gates: str = "psd", init_std: float = 0.0) -> PsdInputs:
+    """The PSD workload's inputs before the lift: u_q, u_k ~ N(0, I_p) unit-normalised, then
+    rounded to bf16; v ~ N(0,1) in bf16. gates "psd": log_alpha = 0, eta = 1 (the workload's
+    exact projection without decay); "gaussian": log_alpha = logsigmoid(N(3,1)),
+    eta = sigmoid(N(0,1)). eps = 1e-6. Defaults are the full PSD workload's shape."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    uq = round_to_bf16(_l2_normalise(rng.standard_normal((B, T, H, p), dtype=f32)))
+    uk = round_to_bf16(_l2_normalise(rng.standard_normal((B, T, H, p), dtype=f32)))
+    v = round_to_bf16(rng.standard_normal((B, T, H, dv), dtype=f32))
+    if gates == "psd":
+        log_alpha = np.zeros((B, T, H), f32)
+        eta = np.ones((B, T, H), f32)
+    elif gates == "gaussian":
+        log_alpha = _logsigmoid(f32(3.0) + rng.standard_normal((B, T, H), dtype=f32))
+        eta = _sigmoid(rng.standard_normal((B, T, H), dtype=f32))
+    else:
+        raise ValueError(f"unknown gates {gates!r}")
+    init = None
+    if init_std > 0:
+        init = (f32(init_std) * rng.standard_normal((B, H, p * p, dv), dtype=f32)).astype(f32)
+    c = lambda a: np.ascontiguousarray(a, f32)
+    return PsdInputs(B, T, H, p, dv, c(uq), c(uk), c(v), c(log_alpha), c(eta), 1e-6, init)
+
+
+# ---------------------------------------------------------------------------
 # Decode workload: N sequences x H heads, fresh single-token inputs every step
 # ---------------------------------------------------------------------------
 DECODE_CONFIG = dict(N=256, H=16, dk=128, dv=128, steps=1024, state_std=0.02, dtype="bf16")
