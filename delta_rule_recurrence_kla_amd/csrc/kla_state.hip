@@ -222,14 +222,6 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
       if (blk < KBLK) {
         int rb, cb;
         kblk(blk, rb, cb);
-        if constexpr (LIFT) {
-          const bool odd = (cb >> 1) & 1;  // u_a is the high half of its word
-#pragma unroll
-          for (int u4 = 0; u4 < 4; ++u4) {
-            pk[u][u4] = lift8(lift_pick(pka[u][u4], odd), pk[u][u4]);
-            if constexpr (WITH_OUT) pq[u][u4] = lift8(lift_pick(pqa[u][u4], odd), pq[u][u4]);
-          }
-        }
 #pragma unroll
         for (int u4 = 0; u4 < 4; ++u4) {
           *reinterpret_cast<u32x4*>(sK + (4 * rb + u4) * LDK + VEC * cb) = pk[u][u4];
@@ -257,6 +249,25 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
     if (tid < 3 * CHUNK / 4) reinterpret_cast<u32x4*>(sTail)[tid] = ptail;
   };
 
+  // Lifted rows: turns the prefetched u pieces into their eight features per block, in place.
+  // Called in the middle of a chunk's products, where its vector work fills the waits on the
+  // MFMA chain instead of sitting between the end-of-chunk barriers.
+  auto lift_regs = [&]() __attribute__((always_inline)) {
+    if constexpr (LIFT) {
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        int rb, cb;
+        kblk(tid + NT * u, rb, cb);
+        const bool odd = (cb >> 1) & 1;  // u_a is the high half of its word
+#pragma unroll
+        for (int u4 = 0; u4 < 4; ++u4) {
+          pk[u][u4] = lift8(lift_pick(pka[u][u4], odd), pk[u][u4]);
+          if constexpr (WITH_OUT) pq[u][u4] = lift8(lift_pick(pqa[u][u4], odd), pq[u][u4]);
+        }
+      }
+    }
+  };
+
   // start state
   f32x4 S[DK / 16];
 #pragma unroll
@@ -276,6 +287,7 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 
   if (c_begin < c_end) {
     issue_loads(c_begin);
+    lift_regs();
     store_lds();
   }
   __syncthreads();
@@ -328,6 +340,8 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
       for (int kb = 0; kb < 2; ++kb)
         if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], TR::ldd(sTP, 16 * mt, 32 * kb, lane), Rb[kb]);
     }
+    // the next chunk's prefetched u pieces (after the last chunk they are stale and never stored)
+    lift_regs();
 
     // ---- O = diag(e^g) Q S + P U ----
     if constexpr (WITH_OUT) {
