@@ -9,8 +9,11 @@ it, and the two share no code.
   kla_ref.c    the same recurrence in plain C, OpenMP over heads
   psd_lift.py  the rank-one PSD lift psi(u) = vec(u u^T) of queries and keys
                (features rounded to bf16) in front of kla_ref.forward
+  loglinear.py log-linear KLA: Fenwick-bucketed states with per-level output weights,
+               as a token-pair definition and as the recurrent (bucket-merge) form
   cref.py      ctypes loader for the C build
   build.py     gcc build of kla_ref.c into oracle/libkla_ref.so
 """
 from . import kla_ref  # noqa: F401
 from . import psd_lift  # noqa: F401
+from . import loglinear  # noqa: F401
