@@ -9,6 +9,7 @@ fallback. PyTorch provides device memory and streams.
     out, S = chunk_fwd(q, k, v, log_alpha, eta, eps, init_state=None)
     out, S = chunk_fwd_psd(uq, uk, v, log_alpha, eta, eps)     # q, k = psi(u) formed in the kernels
     out = decode_step(q, k, v, log_alpha, eta, state, eps)     # state updated in place
+    out = loglinear_decode_step(q, k, v, log_alpha, eta, lam, states, t, eps)  # Fenwick buckets
 """
 from __future__ import annotations
 
@@ -16,7 +17,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["chunk_fwd", "chunk_fwd_psd", "decode_step", "plan", "version", "last_error", "timing_enable",
+__all__ = ["chunk_fwd", "chunk_fwd_psd", "decode_step", "loglinear_decode_step", "plan", "version", "last_error", "timing_enable",
            "timing_collect", "lib_path", "load", "KLAError", "PATHS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,8 +64,10 @@ def load():
     lib.kla_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_f32.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, I, I, I, I, P]
+    lib.kla_loglinear_decode_step.argtypes = [I, I, P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]
     for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
-               "kla_decode_step_f32", "kla_decode_step_ex", "kla_timing_enable", "kla_timing_select"):
+               "kla_decode_step_f32", "kla_decode_step_ex", "kla_loglinear_decode_step", "kla_timing_enable",
+               "kla_timing_select"):
         getattr(lib, fn).restype = I
     lib.kla_timing_enable.argtypes = [I]
     lib.kla_timing_select.argtypes = [ctypes.c_char_p]
@@ -221,6 +224,42 @@ def decode_step(q, k, v, log_alpha, eta, state, eps: float = 1e-6, out=None, str
     _need(out, "out", (N, H, dv), (torch.float32,), dev)
     _check(lib.kla_decode_step_ex(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                   _ptr(eta), float(eps), _ptr(state), _ptr(out), N, H, dk, dv, _stream(stream)))
+    return out
+
+
+def loglinear_decode_step(q, k, v, log_alpha, eta, lam, states, t: int, eps: float = 1e-6, out=None, stream=None,
+                          beta_mode: str = "kaczmarz"):
+    """Log-linear KLA decode of the token at position t for N x H heads. q, k [N,H,dk], v [N,H,dv]
+    in bf16 (or all fp32); log_alpha, eta fp32 [N,H]; lam fp32 [N,H,L] (weight of each level in the
+    output); states fp32 [N,H,L,dk,dv], the Fenwick buckets at position t-1, updated in place to
+    position t. Returns out fp32 [N,H,dv]."""
+    import torch
+    lib = load()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    dev = q.device
+    if q.dtype == torch.bfloat16:
+        dtype = 0
+    elif q.dtype == torch.float32:
+        dtype = 1
+    else:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    if beta_mode not in BETA_MODES:
+        raise ValueError(f"beta_mode must be one of {sorted(BETA_MODES)}")
+    _need(k, "k", (N, H, dk), (q.dtype,), dev)
+    _need(v, "v", (N, H, dv), (q.dtype,), dev)
+    _need(q, "q", (N, H, dk), (q.dtype,), dev)
+    _need(log_alpha, "log_alpha", (N, H), (torch.float32,), dev)
+    _need(eta, "eta", (N, H), (torch.float32,), dev)
+    _need(lam, "lam", (N, H, L), (torch.float32,), dev)
+    _need(states, "states", (N, H, L, dk, dv), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    _need(out, "out", (N, H, dv), (torch.float32,), dev)
+    _check(lib.kla_loglinear_decode_step(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                         _ptr(eta), _ptr(lam), float(eps), _ptr(states), _ptr(out), N, H, dk, dv,
+                                         L, int(t), _stream(stream)))
     return out
 
 

@@ -349,6 +349,33 @@ kla_status kla_decode_step_f32(const float* q, const float* k, const float* v, c
   return decode_impl(KLA_DTYPE_F32, KLA_BETA_KACZMARZ, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
 }
 
+kla_status kla_loglinear_decode_step(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                                     const void* v, const float* log_alpha, const float* eta, const float* lam,
+                                     float eps, float* states, float* out, int N, int H, int dk, int dv, int levels,
+                                     int t, hipStream_t stream) {
+  if (dtype != KLA_DTYPE_BF16 && dtype != KLA_DTYPE_F32) return fail(KLA_ERR_INVALID_ARG, "unknown dtype");
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
+    return fail(KLA_ERR_INVALID_ARG, "unknown beta_mode %d", (int)beta_mode);
+  if (N < 0 || H < 1) return fail(KLA_ERR_INVALID_ARG, "sizes must satisfy N >= 0, H >= 1 (got N=%d H=%d)", N, H);
+  if (dk < 1 || dv < 1) return fail(KLA_ERR_INVALID_ARG, "dk and dv must be positive");
+  if (levels < 1 || levels > 31) return fail(KLA_ERR_INVALID_ARG, "levels must be in 1..31 (got %d)", levels);
+  if (t < 0 || static_cast<long long>(t) >= (1LL << (levels - 1)))
+    return fail(KLA_ERR_INVALID_ARG, "position t=%d needs 0 <= t < 2^(levels-1) with levels=%d", t, levels);
+  if (!supported_dk(dk)) return fail(KLA_ERR_UNSUPPORTED, "dk=%d not supported (64, 128, 256)", dk);
+  if (!supported_dv(dv)) return fail(KLA_ERR_UNSUPPORTED, "dv=%d not supported (64, 128)", dv);
+  if (static_cast<long long>(N) * H > 2147483647LL) return fail(KLA_ERR_UNSUPPORTED, "N*H too large");
+  if (N == 0) return KLA_OK;
+  if (!q || !k || !v || !log_alpha || !eta || !lam || !states || !out)
+    return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta, lam, states and out must be non-null");
+  const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
+  hipError_t e = timed("kla_loglinear_decode", stream, [&] {
+    return kla::launch_loglinear_decode(mode, N, H, dk, dv, q, k, v, log_alpha, eta, lam, eps,
+                                        beta_mode == KLA_BETA_DIRECT, states, out, levels, t, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return KLA_OK;
+}
+
 kla_status kla_decode_step_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
                               const float* log_alpha, const float* eta, float eps, float* state, float* out, int N,
                               int H, int dk, int dv, hipStream_t stream) {

@@ -69,6 +69,13 @@ hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
                             int ncg, int nseg, hipStream_t stream);
 
+// Log-linear decode: one token at position t for N x H heads, each with L bucket states
+// [L, dk, dv] (only the occupied levels are read or written).
+hipError_t launch_loglinear_decode(int mode, int N, int H, int dk, int dv, const void* q, const void* k,
+                                   const void* v, const float* log_alpha, const float* eta, const float* lam,
+                                   float eps, int direct, float* states, float* out, int L, int t,
+                                   hipStream_t stream);
+
 // Copy (or zero when src is null) n floats; used for T == 0 and as a graph-safe fill.
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);
 

@@ -1,0 +1,192 @@
+// Log-linear KLA: the single-token decode step over Fenwick-bucketed states.
+//
+// The Log-Linear page ("Mathematical formalization", recurrent form) keeps one state per
+// Fenwick bucket of the prefix and reads out o_t = sum_l lambda_t^(l) q_t^T S_t^(l); its
+// decoding takes O(log T) time and memory per token. Here the buckets carry the KLA
+// recurrence (KLA page, "KLA update rule"): a bucket's state is the part of the KLA state
+// that its tokens contributed, so every bucket takes the token's transition
+//   A_t S = alpha (S - beta k (k^T S)),   alpha = exp(log_alpha), beta as in kla_decode,
+// and the buckets sum to the KLA state.
+//
+// Buckets at position t (0-based): level 0 holds token t; level l >= 1 holds the 2^(l-1)
+// tokens below bit l-1 of t when that bit is set. Going from t-1 to t (t >= 1, j = number
+// of trailing zeros of t), levels 0..j of t-1 join into level j+1, higher levels keep their
+// tokens, and the new token opens level 0:
+//   S^(j+1) <- A_t (S^(0) + ... + S^(j)),   S^(l) <- A_t S^(l) for the other occupied l,
+//   S^(0)   <- beta k v^T,
+//   o       =  sum over occupied l of lambda^(l) S^(l)^T q
+// with S^T q of a transformed bucket equal to alpha (S^T q - beta (k . q) S^T k), so one
+// pass over a bucket gives both its new value and its output term. Only occupied levels
+// are read or written: 1 + popcount(t-1) buckets in, 1 + popcount(t) out. Slots of levels
+// emptied by a merge keep stale values and are never read again before being overwritten.
+//
+// One workgroup per (sequence, head), 256 threads, each owning 4 adjacent columns of
+// DK / (1024 / DV) rows of a bucket, as in the KLA decode kernel; bound by HBM bandwidth.
+#include "kla_device.h"
+#include "kla_launch.h"
+
+namespace kla {
+
+template <int MODE, int DK, int DV>
+__global__ __launch_bounds__(256) void loglinear_decode_kernel(
+    const typename Tr<MODE>::in_t* __restrict__ q, const typename Tr<MODE>::in_t* __restrict__ k,
+    const typename Tr<MODE>::in_t* __restrict__ v, const float* __restrict__ log_alpha,
+    const float* __restrict__ eta, const float* __restrict__ lam, float eps, int direct,
+    float* __restrict__ states, float* __restrict__ out, int L, int t) {
+  using TR = Tr<MODE>;
+  constexpr int TPR = DV / 4;     // threads per state row
+  constexpr int RPP = 256 / TPR;  // rows per pass
+  constexpr int NP = DK / RPP;    // rows per thread
+  static_assert(DK % RPP == 0 && DK <= 256, "shape");
+
+  __shared__ float sq[DK], sk[DK];
+  __shared__ float4 spa[RPP][TPR], spb[RPP][TPR];
+  __shared__ float sred[2][4];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rg = tid / TPR, c4 = tid - rg * TPR;
+  const size_t nh = blockIdx.x;
+  float* S = states + nh * static_cast<size_t>(L) * DK * DV;
+  const float* lw = lam + nh * L;
+  auto slot = [&](int l) __attribute__((always_inline)) { return S + static_cast<size_t>(l) * DK * DV; };
+
+  float kk = 0.f, kq = 0.f;
+  if (tid < DK) {
+    const float qq = TR::to_f32(q[nh * DK + tid]);
+    const float kv = TR::to_f32(k[nh * DK + tid]);
+    sq[tid] = qq;
+    sk[tid] = kv;
+    kk = kv * kv;
+    kq = kv * qq;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kk += __shfl_xor(kk, o);
+    kq += __shfl_xor(kq, o);
+  }
+  if (lane == 0) {
+    sred[0][w] = kk;
+    sred[1][w] = kq;
+  }
+  __syncthreads();
+  const float nk = sred[0][0] + sred[0][1] + sred[0][2] + sred[0][3];
+  const float dkq = sred[1][0] + sred[1][1] + sred[1][2] + sred[1][3];
+  const float alpha = expf(log_alpha[nh]);
+  const float denom = nk + eps;
+  const float beta = direct ? eta[nh] : denom != 0.f ? eta[nh] / denom : 0.f;
+  const float ab = alpha * beta;
+
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  // One bucket: s holds its state at t-1 (this thread's tile). Applies the transition, writes
+  // the result to slot `dest` and adds the bucket's output term with weight lambda^(dest).
+  auto finish_bucket = [&](float4 (&s)[NP], int dest) __attribute__((always_inline)) {
+    float4 pa = make_float4(0.f, 0.f, 0.f, 0.f), pb = pa;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float kr = sk[rg + p * RPP], qr = sq[rg + p * RPP];
+      pa.x += s[p].x * kr; pa.y += s[p].y * kr; pa.z += s[p].z * kr; pa.w += s[p].w * kr;
+      pb.x += s[p].x * qr; pb.y += s[p].y * qr; pb.z += s[p].z * qr; pb.w += s[p].w * qr;
+    }
+    spa[rg][c4] = pa;
+    spb[rg][c4] = pb;
+    __syncthreads();
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f), Bq = A;
+#pragma unroll
+    for (int g = 0; g < RPP; ++g) {
+      const float4 x = spa[g][c4], y = spb[g][c4];
+      A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
+      Bq.x += y.x; Bq.y += y.y; Bq.z += y.z; Bq.w += y.w;
+    }
+    __syncthreads();  // spa/spb are reused by the next bucket
+    const float lw_d = lw[dest];
+    const float bq = beta * dkq;
+    o.x += lw_d * alpha * (Bq.x - bq * A.x); o.y += lw_d * alpha * (Bq.y - bq * A.y);
+    o.z += lw_d * alpha * (Bq.z - bq * A.z); o.w += lw_d * alpha * (Bq.w - bq * A.w);
+    float* D = slot(dest);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float bk = ab * sk[rg + p * RPP];
+      float4 x = s[p];
+      x.x = alpha * x.x - bk * A.x; x.y = alpha * x.y - bk * A.y;
+      x.z = alpha * x.z - bk * A.z; x.w = alpha * x.w - bk * A.w;
+      *reinterpret_cast<float4*>(D + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4) = x;
+    }
+  };
+  auto load_add = [&](float4 (&s)[NP], int l) __attribute__((always_inline)) {
+    const float* Sl = slot(l);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float4 x = *reinterpret_cast<const float4*>(Sl + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4);
+      s[p].x += x.x; s[p].y += x.y; s[p].z += x.z; s[p].w += x.w;
+    }
+  };
+
+  if (t > 0) {
+    const int j = __builtin_ctz(static_cast<unsigned>(t));
+    float4 s[NP];
+    // levels 0..j of t-1 join into level j+1, then the higher occupied levels are transformed
+    // in place, one bucket per pass: (first, last) is the range of slots summed into `dest`
+    for (int dest = j + 1; dest < 32; ++dest) {
+      if (dest > j + 1 && !((t >> (dest - 1)) & 1)) continue;
+      const int first = dest == j + 1 ? 0 : dest, last = dest == j + 1 ? j : dest;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) s[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int l = first; l <= last; ++l) load_add(s, l);
+      finish_bucket(s, dest);
+    }
+  }
+
+  // the new token opens level 0: S^(0) = beta k v^T, read out as beta (k . q) v
+  float vv[4];
+#pragma unroll
+  for (int jx = 0; jx < 4; ++jx) vv[jx] = TR::to_f32(v[nh * DV + 4 * c4 + jx]);
+  float* D0 = slot(0);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const float bk = beta * sk[rg + p * RPP];
+    const float4 x = make_float4(bk * vv[0], bk * vv[1], bk * vv[2], bk * vv[3]);
+    *reinterpret_cast<float4*>(D0 + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4) = x;
+  }
+  const float w0 = lw[0] * beta * dkq;
+  o.x += w0 * vv[0]; o.y += w0 * vv[1]; o.z += w0 * vv[2]; o.w += w0 * vv[3];
+  if (rg == 0) *reinterpret_cast<float4*>(out + nh * DV + 4 * c4) = o;
+}
+
+template <int MODE, int DK, int DV>
+static hipError_t launch_ll_t(int N, int H, const void* q, const void* k, const void* v, const float* la,
+                              const float* eta, const float* lam, float eps, int direct, float* states, float* out,
+                              int L, int t, hipStream_t stream) {
+  using in_t = typename Tr<MODE>::in_t;
+  return launch_kernel(loglinear_decode_kernel<MODE, DK, DV>, dim3(N * H), dim3(256), stream,
+                       static_cast<const in_t*>(q), static_cast<const in_t*>(k), static_cast<const in_t*>(v), la, eta,
+                       lam, eps, direct, states, out, L, t);
+}
+
+template <int MODE>
+static hipError_t dispatch_ll(int N, int H, int dk, int dv, const void* q, const void* k, const void* v,
+                              const float* la, const float* eta, const float* lam, float eps, int direct,
+                              float* states, float* out, int L, int t, hipStream_t stream) {
+#define KLA_LL_CASE(DKV, DVV)                                                                              \
+  if (dk == DKV && dv == DVV)                                                                              \
+    return launch_ll_t<MODE, DKV, DVV>(N, H, q, k, v, la, eta, lam, eps, direct, states, out, L, t, stream);
+  KLA_LL_CASE(64, 64)
+  KLA_LL_CASE(64, 128)
+  KLA_LL_CASE(128, 64)
+  KLA_LL_CASE(128, 128)
+  KLA_LL_CASE(256, 64)
+  KLA_LL_CASE(256, 128)
+#undef KLA_LL_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_loglinear_decode(int mode, int N, int H, int dk, int dv, const void* q, const void* k,
+                                   const void* v, const float* log_alpha, const float* eta, const float* lam,
+                                   float eps, int direct, float* states, float* out, int L, int t,
+                                   hipStream_t stream) {
+  if (mode == MODE_BF16)
+    return dispatch_ll<MODE_BF16>(N, H, dk, dv, q, k, v, log_alpha, eta, lam, eps, direct, states, out, L, t, stream);
+  return dispatch_ll<MODE_F32>(N, H, dk, dv, q, k, v, log_alpha, eta, lam, eps, direct, states, out, L, t, stream);
+}
+
+}  // namespace kla

@@ -174,6 +174,32 @@ kla_status kla_decode_step_ex(kla_dtype dtype, kla_beta_mode beta_mode, const vo
                               float* state, float* out, int N, int H, int dk, int dv,
                               hipStream_t stream);
 
+/*
+ * Log-linear KLA decode: one token at position t for N x H heads, each with L
+ * Fenwick-bucketed states (Log-Linear page, "Mathematical formalization",
+ * recurrent form: one state per bucket of the prefix, output
+ * o_t = sum_l lambda_t^(l) q_t^T S_t^(l); O(log T) work and memory per token).
+ * The buckets carry the KLA recurrence: every occupied bucket takes the token's
+ * transition S -> exp(log_alpha) (S - beta k (k^T S)), and the buckets sum to the
+ * KLA state, so all-ones weights reproduce kla_decode_step_ex.
+ * Buckets at position t (0-based): level 0 holds token t; level l >= 1 holds the
+ * 2^(l-1) tokens below bit l-1 of t when that bit is set. From t-1 to t, levels
+ * 0..j (j = trailing zeros of t) join into level j+1 and the token opens level 0.
+ *
+ *   q, k, v, log_alpha, eta, eps, dtype, beta_mode   as for kla_decode_step_ex
+ *   lam      fp32 [N,H,L]: lambda_t^(l), the weight of level l in the output
+ *   states   fp32 [N,H,L,dk,dv], updated in place: the buckets at position t-1 on
+ *            entry (zeros, or anything, at t == 0) and at position t on return.
+ *            Only occupied levels are read or written (1 + popcount(t-1) in,
+ *            1 + popcount(t) out); other slots are left as they are.
+ *   out      fp32 [N,H,dv]
+ *   levels   L, 1..31; t must satisfy 0 <= t < 2^(L-1), else KLA_ERR_INVALID_ARG
+ */
+kla_status kla_loglinear_decode_step(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                                     const void* v, const float* log_alpha, const float* eta,
+                                     const float* lam, float eps, float* states, float* out, int N, int H,
+                                     int dk, int dv, int levels, int t, hipStream_t stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* kla_last_error(void);
 

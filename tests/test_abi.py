@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_decode_step", "kla_decode_step_ex",
+    for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_loglinear_decode_step",
+              "kla_decode_step", "kla_decode_step_ex",
               "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
               "kla_timing_enable", "kla_timing_collect", "kla_timing_select"):
         assert n in names
@@ -89,6 +90,28 @@ def test_psd_validation(kw, status):
 def test_psd_zero_tokens_without_final_state_is_a_no_op():
     lib = kla.load()
     assert _psd(lib, uq=None, out=None, T=0) == 0
+
+
+def _ll(lib, dtype=0, beta=0, q=FAKE, lam=FAKE, N=2, H=2, dk=128, dv=128, L=16, t=5):
+    return lib.kla_loglinear_decode_step(dtype, beta, q, FAKE, FAKE, FAKE, FAKE, lam, 1e-6, FAKE, FAKE, N, H, dk, dv,
+                                         L, t, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), 1), (dict(L=32), 1), (dict(t=-1), 1), (dict(L=4, t=8), 1), (dict(L=1, t=1), 1),
+    (dict(dk=100), 2), (dict(dv=32), 2), (dict(q=None), 1), (dict(lam=None), 1), (dict(dtype=5), 1),
+    (dict(beta=3), 1), (dict(N=-1), 1), (dict(H=0), 1),
+])
+def test_loglinear_validation(kw, status):
+    lib = kla.load()
+    assert _ll(lib, **kw) == status
+    assert kla.last_error() != ""
+
+
+def test_loglinear_zero_sequences_is_a_no_op():
+    lib = kla.load()
+    assert _ll(lib, q=None, lam=None, N=0, L=31, t=(1 << 30) - 1) == 0
+    assert _ll(lib, q=None, lam=None, N=0, L=1, t=0) == 0
 
 
 @pytest.mark.parametrize("args,status", [

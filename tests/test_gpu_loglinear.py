@@ -1,0 +1,115 @@
+"""GPU parity of the log-linear KLA decode step (kla_loglinear_decode_step) against the
+CPU oracle's recurrent form (oracle/loglinear.py).
+
+Each case runs successive positions from a start position, comparing every step's output
+and the occupied bucket states with the oracle. Bar: fp32 arithmetic on exact inputs, so
+max|err| <= 1e-4 * RMS(ref) per step (the fp32 bar; the kernels' order of sums differs from
+the oracle's); at full size, sampled heads at the bf16 bar.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import loglinear
+from tests.gpu_common import TOL, assert_close, err_over_rms, upload
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import delta_rule_recurrence_kla_amd as kla  # noqa: E402
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(N, H, dk, dv, L, t0, steps, dtype, beta_mode="kaczmarz", seed=0, std=0.3, heads=None, tol=1e-4,
+         unit_weights=False):
+    S0 = W.make_loglinear_states(N, H, L, dk, dv, std=std, seed=seed)
+    S_dev = upload(S0, "f32")
+    if heads is None:
+        heads = [(n, h) for n in range(N) for h in range(H)]
+    S_ref = np.stack([S0[n, h] for n, h in heads])[:, None].astype(np.float64)   # [n, 1, L, dk, dv]
+    pick = lambda a: np.stack([a[n, h] for n, h in heads])[:, None]
+    worst = 0.0
+    for i in range(steps):
+        t = t0 + i
+        st = W.make_decode_step(i, N, H, dk, dv, dtype=dtype, seed=seed)
+        lam = np.ones((N, H, L), np.float32) if unit_weights else W.make_loglinear_lambda(i, N, H, L, seed=seed)
+        o = kla.loglinear_decode_step(upload(st.q, dtype), upload(st.k, dtype), upload(st.v, dtype),
+                                      upload(st.log_alpha, "f32"), upload(st.eta, "f32"), upload(lam, "f32"),
+                                      S_dev, t, st.eps, beta_mode=beta_mode)
+        o_ref, S_ref = loglinear.decode_step_loglinear(S_ref, t, pick(st.q), pick(st.k), pick(st.v),
+                                                       pick(st.log_alpha), pick(st.eta), pick(lam), st.eps,
+                                                       beta_mode)
+        og = o.cpu().numpy()
+        got = np.stack([og[n, h] for n, h in heads])
+        e = err_over_rms(got, o_ref[:, 0])
+        worst = max(worst, e)
+        assert np.all(np.isfinite(got)) and e <= tol, f"step t={t}: out max|err|/RMS = {e:.3e}"
+    occ = loglinear.occupied_levels(t0 + steps - 1)
+    Sg = S_dev.cpu().numpy()
+    got_S = np.stack([Sg[n, h][occ] for n, h in heads])
+    assert_close(got_S, S_ref[:, 0][:, occ], tol, "occupied bucket states")
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (256, 128), (128, 64), (64, 128), (256, 64)])
+def test_loglinear_from_empty(dtype, dk, dv):
+    """Positions 0..69 from empty buckets (every merge pattern up to level 7)."""
+    log(f"loglinear from empty dtype={dtype} dk={dk} dv={dv}")
+    _run(N=2, H=3, dk=dk, dv=dv, L=8, t0=0, steps=70, dtype=dtype, std=0.0)
+
+
+@pytest.mark.parametrize("t0", [1, 255, 1023, 32768 - 3])
+def test_loglinear_from_positions(t0):
+    """Start from filled buckets at positions whose next steps merge many levels at once
+    (e.g. 1023 -> 1024 joins ten buckets), and at the top of a 16-level range."""
+    log(f"loglinear from t0={t0}")
+    _run(N=2, H=2, dk=128, dv=128, L=16, t0=t0, steps=3, dtype="bf16", seed=t0)
+
+
+@pytest.mark.parametrize("beta_mode", ["kaczmarz", "direct"])
+def test_loglinear_beta_modes(beta_mode):
+    log(f"loglinear beta_mode={beta_mode}")
+    _run(N=2, H=2, dk=64, dv=64, L=7, t0=5, steps=20, dtype="f32", beta_mode=beta_mode, std=0.1)
+
+
+def test_unit_weights_match_kla_decode():
+    """All-ones weights: the buckets sum to the KLA state, so outputs equal kla_decode_step's
+    from the summed start state."""
+    N, H, dk, dv, L, t0, steps = 3, 2, 128, 128, 10, 37, 12
+    log("loglinear unit weights == KLA decode")
+    S0 = W.make_loglinear_states(N, H, L, dk, dv, std=0.2, seed=4)
+    occ = loglinear.occupied_levels(t0 - 1)
+    S_dev = upload(S0, "f32")
+    K_dev = upload(S0[:, :, occ].sum(axis=2), "f32")
+    ones = upload(np.ones((N, H, L), np.float32), "f32")
+    for i in range(steps):
+        st = W.make_decode_step(i, N, H, dk, dv, dtype="bf16", seed=4)
+        args = [upload(st.q, "bf16"), upload(st.k, "bf16"), upload(st.v, "bf16"), upload(st.log_alpha, "f32"),
+                upload(st.eta, "f32")]
+        o_ll = kla.loglinear_decode_step(*args, ones, S_dev, t0 + i, st.eps)
+        o_k = kla.decode_step(*args, K_dev, st.eps)
+        assert_close(o_ll.cpu().numpy(), o_k.cpu().numpy(), 1e-5, f"step {i}")
+    occ = loglinear.occupied_levels(t0 + steps - 1)
+    assert_close(S_dev.cpu().numpy()[:, :, occ].sum(axis=2), K_dev.cpu().numpy(), 1e-5, "summed buckets")
+
+
+def test_loglinear_full_size_sampled():
+    """256 sequences x 16 heads, dk=dv=128, 16 levels, 32 successive positions ending at
+    32767 (up to 16 occupied buckets per head), sampled heads against the oracle."""
+    cfg = W.LOGLINEAR_DECODE_CONFIG
+    N, H, dk, dv, L = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"], cfg["levels"]
+    rng = np.random.default_rng(7)
+    heads = sorted({(int(a), int(b)) for a, b in zip(rng.integers(0, N, 10), rng.integers(0, H, 10))})
+    log(f"loglinear full size N={N} H={H} L={L} heads={len(heads)}")
+    worst = _run(N=N, H=H, dk=dk, dv=dv, L=L, t0=32768 - 32, steps=32, dtype="bf16", std=cfg["state_std"],
+                 heads=heads, tol=TOL["bf16"])
+    log(f"loglinear full size worst max|err|/RMS = {worst:.2e}")

@@ -272,3 +272,29 @@ def make_decode_steps(steps: int, **kw) -> DecodeInputs:
     per = [make_decode_step(s, **kw) for s in range(steps)]
     return DecodeInputs(*(np.stack([getattr(p, f) for p in per]) for f in ("q", "k", "v", "log_alpha", "eta")),
                         per[0].eps)
+
+
+# ---------------------------------------------------------------------------
+# Log-linear decode: per-level output weights and bucket states
+# ---------------------------------------------------------------------------
+# 256 sequences x 16 heads at 32K context (the KLA page measures decode at a 32K-token
+# context): 16 levels cover positions below 2^15; the timed steps are the last 1024
+# positions before 32768.
+LOGLINEAR_DECODE_CONFIG = dict(N=256, H=16, dk=128, dv=128, levels=16, t0=32768 - 1024, steps=1024,
+                               state_std=0.02, dtype="bf16")
+
+
+def make_loglinear_lambda(step: int, N: int = 256, H: int = 16, levels: int = 16, seed: int = 0) -> np.ndarray:
+    """Weights lambda^(l) of decode step ``step``: sigmoid(N(0,1)) per sequence, head and level,
+    float32 [N, H, levels]; drawn from their own stream, so the step's q, k, v and gates are the
+    same as make_decode_step's."""
+    rng = np.random.default_rng([seed, step, 1])
+    return _sigmoid(rng.standard_normal((N, H, levels), dtype=np.float32))
+
+
+def make_loglinear_states(N: int = 256, H: int = 16, levels: int = 16, dk: int = 128, dv: int = 128,
+                          std: float = 0.02, seed: int = 0) -> np.ndarray:
+    """Bucket states to start a log-linear decode from, N(0, std) in every slot, float32
+    [N, H, levels, dk, dv] (slots of levels that are empty at the start position are never read)."""
+    rng = np.random.default_rng([seed, 2])
+    return (np.float32(std) * rng.standard_normal((N, H, levels, dk, dv), dtype=np.float32)).astype(np.float32)
