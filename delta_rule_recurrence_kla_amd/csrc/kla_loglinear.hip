@@ -20,28 +20,39 @@
 // are read or written: 1 + popcount(t-1) buckets in, 1 + popcount(t) out. Slots of levels
 // emptied by a merge keep stale values and are never read again before being overwritten.
 //
-// One workgroup per (sequence, head), 256 threads, each owning 4 adjacent columns of
-// DK / (1024 / DV) rows of a bucket, as in the KLA decode kernel; bound by HBM bandwidth.
+// One workgroup per (sequence, head), each thread owning 4 adjacent columns of a stripe of
+// rows of a bucket, as in the KLA decode kernel; bound by HBM bandwidth.
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
 
+// Workgroup barrier that waits for the wave's LDS operations only: global loads issued before
+// it stay in flight (a plain __syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Threads per workgroup: 512 for the larger buckets, so that a thread's two tiles (the bucket
+// being finished and the one being loaded) stay small enough for four waves per SIMD.
+template <int DK, int DV>
+constexpr int ll_threads() { return DK * DV >= 128 * 128 ? 512 : 256; }
+
 template <int MODE, int DK, int DV>
-__global__ __launch_bounds__(256) void loglinear_decode_kernel(
+__global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kernel(
     const typename Tr<MODE>::in_t* __restrict__ q, const typename Tr<MODE>::in_t* __restrict__ k,
     const typename Tr<MODE>::in_t* __restrict__ v, const float* __restrict__ log_alpha,
     const float* __restrict__ eta, const float* __restrict__ lam, float eps, int direct,
     float* __restrict__ states, float* __restrict__ out, int L, int t) {
   using TR = Tr<MODE>;
+  constexpr int NT = ll_threads<DK, DV>();
+  constexpr int NW = NT / 64;     // waves
   constexpr int TPR = DV / 4;     // threads per state row
-  constexpr int RPP = 256 / TPR;  // rows per pass
+  constexpr int RPP = NT / TPR;   // rows per pass
   constexpr int NP = DK / RPP;    // rows per thread
-  static_assert(DK % RPP == 0 && DK <= 256, "shape");
+  static_assert(DK % RPP == 0 && DK <= NT, "shape");
 
   __shared__ float sq[DK], sk[DK];
   __shared__ float4 spa[RPP][TPR], spb[RPP][TPR];
-  __shared__ float sred[2][4];
+  __shared__ float sred[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rg = tid / TPR, c4 = tid - rg * TPR;
@@ -69,8 +80,12 @@ __global__ __launch_bounds__(256) void loglinear_decode_kernel(
     sred[1][w] = kq;
   }
   __syncthreads();
-  const float nk = sred[0][0] + sred[0][1] + sred[0][2] + sred[0][3];
-  const float dkq = sred[1][0] + sred[1][1] + sred[1][2] + sred[1][3];
+  float nk = 0.f, dkq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    nk += sred[0][i];
+    dkq += sred[1][i];
+  }
   const float alpha = expf(log_alpha[nh]);
   const float denom = nk + eps;
   const float beta = direct ? eta[nh] : denom != 0.f ? eta[nh] / denom : 0.f;
@@ -90,7 +105,7 @@ __global__ __launch_bounds__(256) void loglinear_decode_kernel(
     }
     spa[rg][c4] = pa;
     spb[rg][c4] = pb;
-    __syncthreads();
+    lds_barrier();
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f), Bq = A;
 #pragma unroll
     for (int g = 0; g < RPP; ++g) {
@@ -98,7 +113,7 @@ __global__ __launch_bounds__(256) void loglinear_decode_kernel(
       A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
       Bq.x += y.x; Bq.y += y.y; Bq.z += y.z; Bq.w += y.w;
     }
-    __syncthreads();  // spa/spb are reused by the next bucket
+    lds_barrier();  // spa/spb are reused by the next bucket
     const float lw_d = lw[dest];
     const float bq = beta * dkq;
     o.x += lw_d * alpha * (Bq.x - bq * A.x); o.y += lw_d * alpha * (Bq.y - bq * A.y);
@@ -113,6 +128,12 @@ __global__ __launch_bounds__(256) void loglinear_decode_kernel(
       *reinterpret_cast<float4*>(D + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4) = x;
     }
   };
+  auto load_set = [&](float4 (&s)[NP], int l) __attribute__((always_inline)) {
+    const float* Sl = slot(l);
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      s[p] = *reinterpret_cast<const float4*>(Sl + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4);
+  };
   auto load_add = [&](float4 (&s)[NP], int l) __attribute__((always_inline)) {
     const float* Sl = slot(l);
 #pragma unroll
@@ -123,17 +144,25 @@ __global__ __launch_bounds__(256) void loglinear_decode_kernel(
   };
 
   if (t > 0) {
+    // Levels 0..j of t-1 join into level j+1; then the higher occupied levels (the set bits of t
+    // above bit j) are transformed in place, one bucket per pass. The next bucket's loads are
+    // issued before the current one's reductions, whose barriers wait for LDS only, so a
+    // workgroup keeps a bucket of reads in flight while it finishes the previous one.
     const int j = __builtin_ctz(static_cast<unsigned>(t));
-    float4 s[NP];
-    // levels 0..j of t-1 join into level j+1, then the higher occupied levels are transformed
-    // in place, one bucket per pass: (first, last) is the range of slots summed into `dest`
-    for (int dest = j + 1; dest < 32; ++dest) {
-      if (dest > j + 1 && !((t >> (dest - 1)) & 1)) continue;
-      const int first = dest == j + 1 ? 0 : dest, last = dest == j + 1 ? j : dest;
+    float4 cur[NP], nxt[NP];
 #pragma unroll
-      for (int p = 0; p < NP; ++p) s[p] = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int l = first; l <= last; ++l) load_add(s, l);
-      finish_bucket(s, dest);
+    for (int p = 0; p < NP; ++p) cur[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int l = 0; l <= j; ++l) load_add(cur, l);
+    int dest = j + 1;
+    while (true) {
+      const unsigned rest = static_cast<unsigned>(t) >> dest;             // bits of t above bit dest - 1
+      const int next = rest ? dest + __builtin_ctz(rest) + 1 : -1;          // level of the lowest of them
+      if (next > 0) load_set(nxt, next);  // consumed only after this bucket's barriers
+      finish_bucket(cur, dest);
+      if (next < 0) break;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) cur[p] = nxt[p];
+      dest = next;
     }
   }
 
@@ -158,7 +187,7 @@ static hipError_t launch_ll_t(int N, int H, const void* q, const void* k, const 
                               const float* eta, const float* lam, float eps, int direct, float* states, float* out,
                               int L, int t, hipStream_t stream) {
   using in_t = typename Tr<MODE>::in_t;
-  return launch_kernel(loglinear_decode_kernel<MODE, DK, DV>, dim3(N * H), dim3(256), stream,
+  return launch_kernel(loglinear_decode_kernel<MODE, DK, DV>, dim3(N * H), dim3(ll_threads<DK, DV>()), stream,
                        static_cast<const in_t*>(q), static_cast<const in_t*>(k), static_cast<const in_t*>(v), la, eta,
                        lam, eps, direct, states, out, L, t);
 }
