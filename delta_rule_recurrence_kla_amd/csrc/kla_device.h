@@ -99,6 +99,10 @@ __device__ __forceinline__ rsrc_t make_rsrc_wu(const void* base, long long bytes
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
+// Workgroup barrier that waits for the wave's LDS operations only: global loads and stores
+// issued before it stay in flight (__syncthreads also waits for every one of them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
 }

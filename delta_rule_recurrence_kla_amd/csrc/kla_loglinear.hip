@@ -27,10 +27,6 @@
 
 namespace kla {
 
-// Workgroup barrier that waits for the wave's LDS operations only: global loads issued before
-// it stay in flight (a plain __syncthreads also waits for them).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Threads per workgroup: 512 for the larger buckets, so that a thread's two tiles (the bucket
 // being finished and the one being loaded) stay small enough for four waves per SIMD.
 template <int DK, int DV>

@@ -382,9 +382,11 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], TR::ldx(sKt, LDT, 16 * mt, 32 * kb, lane), Ud[kb]);
     }
-    __syncthreads();  // every read of this chunk's LDS is done
+    // Both barriers guard LDS only: the output stores and the next chunk's prefetch loads stay
+    // in flight (store_lds waits for the loads it consumes, not for the stores issued after them).
+    lds_barrier();  // every read of this chunk's LDS is done
     if (more) store_lds();
-    __syncthreads();
+    lds_barrier();
   }
 
   // end state
