@@ -17,7 +17,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["chunk_fwd", "chunk_fwd_psd", "decode_step", "loglinear_decode_step", "plan", "version", "last_error", "timing_enable",
+__all__ = ["chunk_fwd", "chunk_fwd_psd", "decode_step", "loglinear_decode_step", "loglinear_fwd", "plan", "version", "last_error", "timing_enable",
            "timing_collect", "lib_path", "load", "KLAError", "PATHS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,8 +65,10 @@ def load():
     lib.kla_decode_step_f32.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_decode_step_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_loglinear_decode_step.argtypes = [I, I, P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]
+    lib.kla_loglinear_fwd.argtypes = [I, I, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, P]
     for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
-               "kla_decode_step_f32", "kla_decode_step_ex", "kla_loglinear_decode_step", "kla_timing_enable",
+               "kla_decode_step_f32", "kla_decode_step_ex", "kla_loglinear_decode_step", "kla_loglinear_fwd",
+               "kla_timing_enable",
                "kla_timing_select"):
         getattr(lib, fn).restype = I
     lib.kla_timing_enable.argtypes = [I]
@@ -260,6 +262,40 @@ def loglinear_decode_step(q, k, v, log_alpha, eta, lam, states, t: int, eps: flo
     _check(lib.kla_loglinear_decode_step(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                          _ptr(eta), _ptr(lam), float(eps), _ptr(states), _ptr(out), N, H, dk, dv,
                                          L, int(t), _stream(stream)))
+    return out
+
+
+def loglinear_fwd(q, k, v, log_alpha, eta, lam, eps: float = 1e-6, chunk: int = 64, out=None, stream=None,
+                  beta_mode: str = "kaczmarz"):
+    """Log-linear KLA prefill from empty buckets. q, k [B,T,H,dk], v [B,T,H,dv] in bf16 (or all
+    fp32); log_alpha, eta fp32 [B,T,H]; lam fp32 [B,T,H,L] with T <= 2^(L-1).
+    Returns out fp32 [B,T,H,dv]."""
+    import torch
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    dev = q.device
+    if q.dtype == torch.bfloat16:
+        dtype = 0
+    elif q.dtype == torch.float32:
+        dtype = 1
+    else:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    if beta_mode not in BETA_MODES:
+        raise ValueError(f"beta_mode must be one of {sorted(BETA_MODES)}")
+    _need(q, "q", (B, T, H, dk), (q.dtype,), dev)
+    _need(k, "k", (B, T, H, dk), (q.dtype,), dev)
+    _need(v, "v", (B, T, H, dv), (q.dtype,), dev)
+    _need(log_alpha, "log_alpha", (B, T, H), (torch.float32,), dev)
+    _need(eta, "eta", (B, T, H), (torch.float32,), dev)
+    _need(lam, "lam", (B, T, H, L), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, T, H, dv), (torch.float32,), dev)
+    _check(lib.kla_loglinear_fwd(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                 _ptr(eta), _ptr(lam), float(eps), _ptr(out), B, T, H, dk, dv, L, chunk,
+                                 _stream(stream)))
     return out
 
 

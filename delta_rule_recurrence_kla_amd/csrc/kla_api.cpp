@@ -376,6 +376,58 @@ kla_status kla_loglinear_decode_step(kla_dtype dtype, kla_beta_mode beta_mode, c
   return KLA_OK;
 }
 
+kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* eta, const float* lam, float eps, float* out, int B,
+                             int T, int H, int dk, int dv, int levels, int chunk, hipStream_t stream) {
+  if (dtype != KLA_DTYPE_BF16 && dtype != KLA_DTYPE_F32) return fail(KLA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
+  if (st != KLA_OK) return st;
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
+    return fail(KLA_ERR_INVALID_ARG, "unknown beta_mode %d", (int)beta_mode);
+  if (levels < 1 || levels > 31) return fail(KLA_ERR_INVALID_ARG, "levels must be in 1..31 (got %d)", levels);
+  if (static_cast<long long>(T) > (1LL << (levels - 1)))
+    return fail(KLA_ERR_INVALID_ARG, "T=%d needs T <= 2^(levels-1) with levels=%d", T, levels);
+  if (T == 0) return KLA_OK;
+  if (!q || !k || !v || !log_alpha || !eta || !lam || !out)
+    return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta, lam and out must be non-null when T > 0");
+  const int nc = (T + kChunk - 1) / kChunk;
+  kla::Dims d{B, T, H, dk, dv, nc};
+  d.full_rec = 1;
+  const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
+  const size_t bh = static_cast<size_t>(B) * H;
+  const size_t rec_bytes = align256(bh * nc * kla::full_record_bytes());
+  const size_t ends_bytes = align256(bh * ((nc + 1) / 2) * dk * dv * 4);  // the most left half-blocks: scale 7
+  if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
+    if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
+  }
+  keep_pool_warm();
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, rec_bytes + ends_bytes, stream);
+  if (e != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return fail(KLA_ERR_OOM, "hipMallocAsync(%zu bytes) failed: %s", rec_bytes + ends_bytes, hipGetErrorString(e));
+  }
+  uint8_t* rec = static_cast<uint8_t*>(ws);
+  float* ends = reinterpret_cast<float*>(rec + rec_bytes);
+  const int direct = beta_mode == KLA_BETA_DIRECT;
+  e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
+  if (e == hipSuccess)
+    e = timed("kla_loglinear_intra", stream, [&] { return kla::launch_loglinear_intra(mode, d, rec, v, lam, levels, out, stream); });
+  // scale l >= 7: half-blocks of 2^(l-7) chunks; the right ones read the left siblings' end states
+  for (int level = 7, half = 1; e == hipSuccess && half < nc; ++level, half *= 2) {
+    const int nblk = (nc + half - 1) / half, nleft = (nblk + 1) / 2, nright = nblk / 2;
+    e = timed("kla_loglinear_left", stream, [&] { return kla::launch_loglinear_left(mode, d, k, v, rec, half, nleft, ends, stream); });
+    if (e == hipSuccess)
+      e = timed("kla_loglinear_right", stream, [&] {
+        return kla::launch_loglinear_right(mode, d, q, k, rec, half, nright, ends, nleft, lam, levels, level, out, stream);
+      });
+  }
+  hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
+  return KLA_OK;
+}
+
 kla_status kla_decode_step_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
                               const float* log_alpha, const float* eta, float eps, float* state, float* out, int N,
                               int H, int dk, int dv, hipStream_t stream) {

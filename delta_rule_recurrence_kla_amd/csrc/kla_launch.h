@@ -34,6 +34,7 @@ struct Dims {
   int B, T, H, dk, dv;
   int nc;        // number of 64-token chunks, ceil(T / 64)
   int lift = 0;  // q and k hold 16-wide u rows; the kernels form the dk = 256 PSD features
+  int full_rec = 0;  // prep writes the full record (T' and P) whatever the dtype and dk
 };
 
 // Chunk prep: one wavefront per (b, h, chunk); writes one record per chunk. `direct` takes
@@ -64,6 +65,7 @@ bool state_dma_supported(int mode, int dk);
 // Bytes of one chunk record: compact (no P, T' without its zero quadrant) when the DMA-fed
 // state kernel consumes it, else the full record.
 int record_bytes(int mode, int dk);
+int full_record_bytes();  // T' and P in full, for the kernels that read both
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
@@ -75,6 +77,18 @@ hipError_t launch_loglinear_decode(int mode, int N, int H, int dk, int dv, const
                                    const void* v, const float* log_alpha, const float* eta, const float* lam,
                                    float eps, int direct, float* states, float* out, int L, int t,
                                    hipStream_t stream);
+
+// Log-linear prefill (full records). Intra-chunk levels 0..6 written to out; then per scale
+// l >= 7 with half-blocks of `half` chunks: the zero-start end state of every left half-block
+// into ends [B*H][nleft][dk][dv], and the walk over every right half-block from its left
+// sibling's end state with no values, lambda^(l)-weighted outputs added to out.
+hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, const void* v, const float* lam,
+                                  int L, float* out, hipStream_t stream);
+hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int half,
+                                 int nleft, float* ends, hipStream_t stream);
+hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec, int half,
+                                  int nright, const float* ends, int nleft, const float* lam, int L, int level,
+                                  float* out, hipStream_t stream);
 
 // Copy (or zero when src is null) n floats; used for T == 0 and as a graph-safe fill.
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);

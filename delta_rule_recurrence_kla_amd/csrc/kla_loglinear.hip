@@ -178,6 +178,113 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
   if (rg == 0) *reinterpret_cast<float4*>(out + nh * DV + 4 * c4) = o;
 }
 
+// ---------------------------------------------------------------------------
+// Log-linear prefill, levels 0..6: the pairs of tokens inside one 64-token chunk.
+//
+// From a zero start, the chunk algebra of the KLA prefill gives the chunk's outputs as
+// O = P T' V (P and T' from the chunk record), so W = P T' holds the token-pair weights
+// W_ts = beta_s q_t^T A_t ... A_{s+1} k_s of the token-pair definition. Two tokens of one
+// chunk differ only in their low six bits, so their bucket is level 0 (s = t) or the index of
+// their highest differing bit plus one, at most 6:
+//   out_t = sum_{s <= t in the chunk} lambda_t^(level(t,s)) W_ts v_s          (written, not added)
+// One workgroup per (batch, head, chunk), fp32 on the vector ALU: W = P T' (16 pairs per
+// thread), then the weighted W times the chunk's values.
+template <int MODE>
+__device__ __forceinline__ float rec_elem(const uint8_t* row_base, int r, int s) {
+  if constexpr (MODE == MODE_BF16) {
+    const uint16_t hi = *reinterpret_cast<const uint16_t*>(row_base + swz_off<256>(r, 2 * s));
+    const uint16_t lo = *reinterpret_cast<const uint16_t*>(row_base + swz_off<256>(r, 128 + 2 * s));
+    return bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
+  } else {
+    return *reinterpret_cast<const float*>(row_base + swz_off<256>(r, 4 * s));
+  }
+}
+
+template <int MODE, int DV>
+__global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __restrict__ rec,
+                                                              const typename Tr<MODE>::in_t* __restrict__ v,
+                                                              const float* __restrict__ lam, float* __restrict__ out,
+                                                              int T, int H, int nc, int L) {
+  using TR = Tr<MODE>;
+  constexpr int G = 256 / DV;        // row groups
+  constexpr int NR = CHUNK / G;      // rows per thread in the product with V
+  __shared__ float sT[CHUNK][CHUNK + 1];
+  __shared__ float sW[CHUNK][CHUNK + 1];  // P, then the weighted W
+  __shared__ float sV[CHUNK][DV + 1];
+
+  const int tid = threadIdx.x;
+  const int id = blockIdx.x;
+  const int bh = id / nc, c = id - bh * nc;
+  const int b = bh / H, h = bh - b * H;
+  const int t0 = c * CHUNK;
+  const uint8_t* R = rec + static_cast<size_t>(id) * REC_BYTES;
+  for (int e = tid; e < CHUNK * CHUNK; e += 256) {
+    const int r = e >> 6, s = e & 63;
+    sT[r][s] = rec_elem<MODE>(R + REC_T_OFF, r, s);
+    sW[r][s] = rec_elem<MODE>(R + REC_P_OFF, r, s);
+  }
+  for (int e = tid; e < CHUNK * DV; e += 256) {
+    const int s = e / DV, cc = e - s * DV;
+    const int t = t0 + s;
+    sV[s][cc] = t < T ? TR::to_f32(v[(static_cast<size_t>(b) * T + t) * H * DV + h * DV + cc]) : 0.f;
+  }
+  __syncthreads();
+
+  // W_ts = sum_r P_tr T'_rs for row t and columns s0 .. s0 + 15 (both factors are lower triangular)
+  const int t = tid >> 2, s0 = (tid & 3) * 16;
+  float w[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) w[j] = 0.f;
+  for (int r = 0; r < CHUNK; ++r) {
+    const float p = sW[t][r];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] += p * sT[r][s0 + j];
+  }
+  const bool live = t0 + t < T;
+  const float* lw = lam + ((static_cast<size_t>(b) * T + t0 + t) * H + h) * L;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int s = s0 + j;
+    const int lev = s == t ? 0 : 32 - __clz(static_cast<unsigned>(t ^ s));
+    w[j] = (live && s <= t) ? w[j] * lw[lev] : 0.f;
+  }
+  __syncthreads();  // every read of P is done
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sW[t][s0 + j] = w[j];
+  __syncthreads();
+
+  // out_t = sum_s W_ts v_s for this thread's column cc and rows g, g + G, ...
+  const int g = tid / DV, cc = tid - g * DV;
+  float acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) acc[i] = 0.f;
+  for (int s = 0; s < CHUNK; ++s) {
+    const float vv = sV[s][cc];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) acc[i] += sW[g + G * i][s] * vv;
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int tt = t0 + g + G * i;
+    if (tt < T) out[(static_cast<size_t>(b) * T + tt) * H * DV + h * DV + cc] = acc[i];
+  }
+}
+
+hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, const void* v, const float* lam,
+                                  int L, float* out, hipStream_t stream) {
+  const dim3 grid(d.B * d.H * d.nc);
+  if (mode == MODE_BF16) {
+    const auto* vb = static_cast<const Tr<MODE_BF16>::in_t*>(v);
+    if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 64>, grid, dim3(256), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
+    if (d.dv == 128) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 128>, grid, dim3(256), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
+  } else {
+    const auto* vf = static_cast<const Tr<MODE_F32>::in_t*>(v);
+    if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_F32, 64>, grid, dim3(256), stream, rec, vf, lam, out, d.T, d.H, d.nc, L);
+    if (d.dv == 128) return launch_kernel(loglinear_intra_kernel<MODE_F32, 128>, grid, dim3(256), stream, rec, vf, lam, out, d.T, d.H, d.nc, L);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int MODE, int DK, int DV>
 static hipError_t launch_ll_t(int N, int H, const void* q, const void* k, const void* v, const float* la,
                               const float* eta, const float* lam, float eps, int direct, float* states, float* out,

@@ -391,7 +391,7 @@ template <int MODE, int DK, bool LIFT = false>
 static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, const float* la, const float* eta,
                                 float eps, int direct, uint8_t* rec, hipStream_t stream) {
   const int nchunks = d.B * d.H * d.nc;
-  if (!LIFT && state_dma_supported(MODE, DK))
+  if (!LIFT && !d.full_rec && state_dma_supported(MODE, DK))
     return launch_kernel(prep_kernel<MODE, DK, true, false>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
                          direct, rec, d.T, d.H, d.nc, nchunks);
   return launch_kernel(prep_kernel<MODE, DK, false, LIFT>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
@@ -399,6 +399,7 @@ static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, con
 }
 
 int record_bytes(int mode, int dk) { return state_dma_supported(mode, dk) ? CREC_BYTES : REC_BYTES; }
+int full_record_bytes() { return REC_BYTES; }
 
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
                        const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream) {

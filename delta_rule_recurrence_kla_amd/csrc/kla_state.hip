@@ -48,6 +48,14 @@ struct StateArgs {
   int fin_last_only;     // write only from the last segment, into slot 0
   int ncg;               // column groups per (segment, head)
   int nseg;              // segments in the grid
+  // Segment s of the grid walks chunks [(s * seg_mul + seg_add) * seg_chunks, + seg_chunks):
+  // every segment (1, 0), or every other one (2, 0 / 2, 1) for the log-linear scales.
+  int seg_mul = 1;
+  int seg_add = 0;
+  // ACC kernels: out[b, t, h, :] += lam[((b * T + t) * H + h) * lam_L + lam_level] * o_t
+  const float* lam = nullptr;
+  int lam_L = 0;
+  int lam_level = 0;
 };
 
 // Workgroup id -> (column group, unit), unit = bh * nseg + seg. The column groups of one
@@ -70,7 +78,7 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t lo, uint32_t hi, int ha
   return __builtin_amdgcn_perm(hi, lo, half ? 0x07060302u : 0x05040100u);
 }
 
-template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT>
+template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT, bool ACC>
 __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   const bool ident = AUG && col0 < DK;    // identity part of [M | N]
   const int vcol0 = AUG ? col0 - DK : col0;
   const int vcol = vcol0 + 16 * w + ln;
-  const int c_begin = seg * a.seg_chunks;
+  const int c_begin = (seg * a.seg_mul + a.seg_add) * a.seg_chunks;
   const int c_end = min(a.nc, c_begin + a.seg_chunks);
 
   // byte strides between consecutive tokens, and this batch's first rows
@@ -152,7 +160,8 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
     const long long rem = static_cast<long long>(T - t0);
     const rsrc_t rk = make_rsrc(kb_ + static_cast<size_t>(t0) * rowK, rem * rowK);
     const rsrc_t rq = make_rsrc(qb_ + static_cast<size_t>(t0) * rowK, WITH_OUT ? rem * rowK : 0);
-    const rsrc_t rv = make_rsrc(vb_ + static_cast<size_t>(t0) * rowV, ident ? 0 : rem * rowV);
+    // no values (a.v null: the log-linear propagation walks) read as zeros, like the identity part
+    const rsrc_t rv = make_rsrc(vb_ + static_cast<size_t>(t0) * rowV, ident || !a.v ? 0 : rem * rowV);
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int blk = tid + NT * u;
@@ -364,8 +373,21 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           if (kb == 0 || mt >= 2) O[mt] = TR::mma_dd(O[mt], TR::ldd(sPP, 16 * mt, 32 * kb, lane), Ub[kb]);
+        if constexpr (ACC) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bstore_f32(O[mt][i], ro, obase + (16 * mt + i) * rowO);
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * mt + 4 * gq + i;
+            if (t < T) {
+              const float w = a.lam[((static_cast<size_t>(b) * T + t) * H + h) * a.lam_L + a.lam_level];
+              const int off = obase + (16 * mt + i) * rowO;
+              const float old = __uint_as_float(bload4(ro, off));
+              bstore_f32(old + w * O[mt][i], ro, off);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bstore_f32(O[mt][i], ro, obase + (16 * mt + i) * rowO);
+        }
       }
     }
 
@@ -462,9 +484,9 @@ __global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __rest
 // ---------------------------------------------------------------------------
 constexpr int NCOLS_STATE = 64;  // state columns per workgroup (4 waves x 16)
 
-template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT = false>
+template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT = false, bool ACC = false>
 static hipError_t launch_state_t(int nwg, const StateArgs& a, hipStream_t stream) {
-  return launch_kernel(state_kernel<MODE, DK, WITH_OUT, AUG, LIFT>, dim3(nwg), dim3(256), stream, a);
+  return launch_kernel(state_kernel<MODE, DK, WITH_OUT, AUG, LIFT, ACC>, dim3(nwg), dim3(256), stream, a);
 }
 
 template <bool WITH_OUT, bool AUG>
@@ -530,6 +552,46 @@ hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void*
                             starts, segs, out, fin, d.dv, 1, 1, ncg, segs, stream);
   StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, starts, segs, out, fin, d.dv, 1, 1, ncg, segs};
   return dispatch_state<true, false>(mode, d.dk, d.lift, ncg * segs * d.B * d.H, a, stream);
+}
+
+// Log-linear prefill, one scale: half-blocks of `half` chunks, left ones (even) and right ones (odd).
+template <bool WITH_OUT, bool ACC>
+static hipError_t dispatch_scale(int mode, int dk, int nwg, const StateArgs& a, hipStream_t stream) {
+  if (mode == MODE_BF16) {
+    switch (dk) {
+      case 64: return launch_state_t<MODE_BF16, 64, WITH_OUT, false, false, ACC>(nwg, a, stream);
+      case 128: return launch_state_t<MODE_BF16, 128, WITH_OUT, false, false, ACC>(nwg, a, stream);
+      case 256: return launch_state_t<MODE_BF16, 256, WITH_OUT, false, false, ACC>(nwg, a, stream);
+    }
+  } else {
+    switch (dk) {
+      case 64: return launch_state_t<MODE_F32, 64, WITH_OUT, false, false, ACC>(nwg, a, stream);
+      case 128: return launch_state_t<MODE_F32, 128, WITH_OUT, false, false, ACC>(nwg, a, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int half,
+                                 int nleft, float* ends, hipStream_t stream) {
+  const int ncg = d.dv / NCOLS_STATE;
+  StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, half, nullptr, 1, nullptr, ends, d.dv, nleft, 0, ncg, nleft};
+  a.seg_mul = 2;
+  a.seg_add = 0;
+  return dispatch_scale<false, false>(mode, d.dk, ncg * nleft * d.B * d.H, a, stream);
+}
+
+hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec, int half,
+                                  int nright, const float* ends, int nleft, const float* lam, int L, int level,
+                                  float* out, hipStream_t stream) {
+  const int ncg = d.dv / NCOLS_STATE;
+  StateArgs a{q, k, nullptr, rec, d.T, d.H, d.dv, d.nc, half, ends, nleft, out, nullptr, d.dv, 1, 0, ncg, nright};
+  a.seg_mul = 2;
+  a.seg_add = 1;
+  a.lam = lam;
+  a.lam_L = L;
+  a.lam_level = level;
+  return dispatch_scale<true, true>(mode, d.dk, ncg * nright * d.B * d.H, a, stream);
 }
 
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream) {

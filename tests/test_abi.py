@@ -27,6 +27,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_loglinear_decode_step",
+              "kla_loglinear_fwd",
               "kla_decode_step", "kla_decode_step_ex",
               "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
               "kla_timing_enable", "kla_timing_collect", "kla_timing_select"):
@@ -106,6 +107,26 @@ def test_loglinear_validation(kw, status):
     lib = kla.load()
     assert _ll(lib, **kw) == status
     assert kla.last_error() != ""
+
+
+def _llf(lib, dtype=0, q=FAKE, lam=FAKE, B=1, T=64, H=1, dk=64, dv=64, L=8, chunk=64):
+    return lib.kla_loglinear_fwd(dtype, 0, q, FAKE, FAKE, FAKE, FAKE, lam, 1e-6, FAKE, B, T, H, dk, dv, L, chunk, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), 1), (dict(L=32), 1), (dict(T=65, L=7), 1), (dict(T=129, L=8), 1), (dict(q=None), 1),
+    (dict(lam=None), 1), (dict(dk=96), 2), (dict(dv=256), 2), (dict(chunk=32), 2), (dict(dtype=1, dk=256), 2),
+    (dict(B=0), 1), (dict(T=-1), 1),
+])
+def test_loglinear_prefill_validation(kw, status):
+    lib = kla.load()
+    assert _llf(lib, **kw) == status
+    assert kla.last_error() != ""
+
+
+def test_loglinear_prefill_zero_tokens_is_a_no_op():
+    lib = kla.load()
+    assert _llf(lib, q=None, lam=None, T=0, L=1) == 0
 
 
 def test_loglinear_zero_sequences_is_a_no_op():

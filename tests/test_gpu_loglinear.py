@@ -113,3 +113,83 @@ def test_loglinear_full_size_sampled():
     worst = _run(N=N, H=H, dk=dk, dv=dv, L=L, t0=32768 - 32, steps=32, dtype="bf16", std=cfg["state_std"],
                  heads=heads, tol=TOL["bf16"])
     log(f"loglinear full size worst max|err|/RMS = {worst:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# prefill (kla_loglinear_fwd)
+def _prefill_case(B, T, H, dk, dv, L, dtype, seed, beta_mode="kaczmarz"):
+    recipe = "gaussian" if dtype == "f32" else "l2norm"
+    wl = W.make_prefill("lm_layer_4k", seed=seed, recipe=recipe, B=B, T=T, H=H, dk=dk, dv=dv,
+                        dtype=dtype)
+    rng = np.random.default_rng(seed + 1)
+    lam = rng.uniform(0.2, 1.5, (B, T, H, L)).astype(np.float32)
+    return wl, lam
+
+
+def _run_prefill(wl, lam, beta_mode="kaczmarz"):
+    q, k, v = (upload(x, wl.dtype) for x in (wl.q, wl.k, wl.v))
+    out = kla.loglinear_fwd(q, k, v, upload(wl.log_alpha, "f32"), upload(wl.eta, "f32"), upload(lam, "f32"), wl.eps,
+                            beta_mode=beta_mode)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 128, 64), ("bf16", 256, 64),
+                                         ("f32", 64, 128), ("f32", 128, 128)])
+@pytest.mark.parametrize("T", [1, 70, 300])
+def test_loglinear_prefill_small(dtype, dk, dv, T):
+    """Against the token-pair definition: T = 300 covers the intra-chunk levels and the scales
+    of 1, 2 and 4 chunks, with a ragged last chunk."""
+    log(f"loglinear prefill dtype={dtype} dk={dk} dv={dv} T={T}")
+    wl, lam = _prefill_case(2, T, 2, dk, dv, 10, dtype, seed=T + dk + dv)
+    o = _run_prefill(wl, lam)
+    o_ref = loglinear.forward_loglinear(wl.q, wl.k, wl.v, wl.log_alpha, wl.eta, lam, wl.eps)
+    assert_close(o, o_ref, 1e-4 if dtype == "f32" else TOL["bf16"] / 10, "out")
+
+
+def test_loglinear_prefill_direct_mode():
+    log("loglinear prefill direct mode")
+    # keys of norm ~1 (the l2norm recipe) keep eta ||k||^2 below 2, so the direct writes stay bounded
+    wl = W.make_prefill("lm_layer_4k", seed=3, recipe="l2norm", B=1, T=200, H=2, dk=64, dv=64, dtype="f32")
+    lam = np.random.default_rng(4).uniform(0.2, 1.5, (1, 200, 2, 9)).astype(np.float32)
+    wl.eta = (wl.eta * 0.3).astype(np.float32)
+    o = _run_prefill(wl, lam, beta_mode="direct")
+    o_ref = loglinear.forward_loglinear(wl.q, wl.k, wl.v, wl.log_alpha, wl.eta, lam, wl.eps, beta_mode="direct")
+    assert_close(o, o_ref, 1e-4, "out")
+
+
+def test_loglinear_prefill_unit_weights_equal_kla():
+    """All-ones weights: the buckets sum to the KLA state, so the outputs are kla_chunk_fwd's."""
+    log("loglinear prefill unit weights == KLA prefill")
+    wl, _ = _prefill_case(2, 64 * 21 + 9, 3, 128, 128, 12, "bf16", seed=8)
+    lam = np.ones((wl.B, wl.T, wl.H, 12), np.float32)
+    o = _run_prefill(wl, lam)
+    q, k, v = (upload(x, "bf16") for x in (wl.q, wl.k, wl.v))
+    o_k, _ = kla.chunk_fwd(q, k, v, upload(wl.log_alpha, "f32"), upload(wl.eta, "f32"), wl.eps)
+    torch.cuda.synchronize()
+    # two GPU paths with their own split-bf16 rounding (each about 5e-4 of RMS from the oracle on
+    # such inputs): the bf16 small-case bar
+    assert_close(o, o_k.cpu().numpy(), TOL["bf16"] / 10, "out")
+
+
+def test_loglinear_prefill_full_size_sampled():
+    """The LM-layer shape (B=8, T=4096, H=16, dk=dv=128) with 13 levels, sampled heads against
+    the oracle's recurrent form over all 4096 tokens."""
+    B, T, H, L = 8, 4096, 16, 13
+    log(f"loglinear prefill full size B={B} T={T} H={H} L={L}")
+    wl = W.make_prefill("lm_layer_4k", seed=0)
+    rng = np.random.default_rng(11)
+    lam = rng.uniform(0.2, 1.5, (B, T, H, L)).astype(np.float32)
+    o = _run_prefill(wl, lam)
+    heads = [(3, 5), (7, 14)]
+    for b, h in heads:
+        S = np.zeros((1, 1, L, 128, 128))
+        ref = np.zeros((T, 128))
+        for t in range(T):
+            pick = lambda a: a[b, t, h][None, None]
+            o_t, S = loglinear.decode_step_loglinear(S, t, pick(wl.q), pick(wl.k), pick(wl.v),
+                                                     wl.log_alpha[b, t, h][None, None], wl.eta[b, t, h][None, None],
+                                                     lam[b, t, h][None, None], wl.eps)
+            ref[t] = o_t[0, 0]
+        e = assert_close(o[b, :, h], ref, TOL["bf16"], f"head {(b, h)}")
+        log(f"loglinear prefill full size head {(b, h)}: {e:.2e}")
