@@ -189,17 +189,6 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
 //   out_t = sum_{s <= t in the chunk} lambda_t^(level(t,s)) W_ts v_s          (written, not added)
 // One workgroup per (batch, head, chunk), fp32 on the vector ALU: W = P T' (16 pairs per
 // thread), then the weighted W times the chunk's values.
-template <int MODE>
-__device__ __forceinline__ float rec_elem(const uint8_t* row_base, int r, int s) {
-  if constexpr (MODE == MODE_BF16) {
-    const uint16_t hi = *reinterpret_cast<const uint16_t*>(row_base + swz_off<256>(r, 2 * s));
-    const uint16_t lo = *reinterpret_cast<const uint16_t*>(row_base + swz_off<256>(r, 128 + 2 * s));
-    return bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
-  } else {
-    return *reinterpret_cast<const float*>(row_base + swz_off<256>(r, 4 * s));
-  }
-}
-
 template <int MODE, int DV>
 __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __restrict__ rec,
                                                               const typename Tr<MODE>::in_t* __restrict__ v,
@@ -208,9 +197,10 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   using TR = Tr<MODE>;
   constexpr int G = 256 / DV;        // row groups
   constexpr int NR = CHUNK / G;      // rows per thread in the product with V
-  __shared__ float sT[CHUNK][CHUNK + 1];
-  __shared__ float sW[CHUNK][CHUNK + 1];  // P, then the weighted W
-  __shared__ float sV[CHUNK][DV + 1];
+  constexpr int PT = CHUNK + 4;      // row pitch: 16-byte aligned rows, read four values at a time
+  __shared__ __align__(16) float sT[CHUNK][PT];
+  __shared__ __align__(16) float sW[CHUNK][PT];  // P, then the weighted W
+  __shared__ __align__(16) float sV[CHUNK][DV + 4];
 
   const int tid = threadIdx.x;
   const int id = blockIdx.x;
@@ -218,15 +208,53 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   const int b = bh / H, h = bh - b * H;
   const int t0 = c * CHUNK;
   const uint8_t* R = rec + static_cast<size_t>(id) * REC_BYTES;
-  for (int e = tid; e < CHUNK * CHUNK; e += 256) {
-    const int r = e >> 6, s = e & 63;
-    sT[r][s] = rec_elem<MODE>(R + REC_T_OFF, r, s);
-    sW[r][s] = rec_elem<MODE>(R + REC_P_OFF, r, s);
+  // T' and P rows in 16-byte pieces: a thread takes (row, block of 8 columns) and, in bf16 mode,
+  // the hi and the lo piece of that block (pieces are swizzled within their row)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;  // 512 (row, block) pairs
+    const int r = e >> 3, cb = e & 7;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t* base = R + (m == 0 ? REC_T_OFF : REC_P_OFF);
+      float* dst = m == 0 ? &sT[r][8 * cb] : &sW[r][8 * cb];
+      if constexpr (MODE == MODE_BF16) {
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz_off<256>(r, 16 * cb));
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz_off<256>(r, 16 * (cb + 8)));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dst[2 * j] = __uint_as_float(hi[j] << 16) + __uint_as_float(lo[j] << 16);
+          dst[2 * j + 1] = __uint_as_float(hi[j] & 0xFFFF0000u) + __uint_as_float(lo[j] & 0xFFFF0000u);
+        }
+      } else {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(base + swz_off<256>(r, 32 * cb));
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(base + swz_off<256>(r, 32 * cb + 16));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dst[j] = x0[j];
+          dst[4 + j] = x1[j];
+        }
+      }
+    }
   }
-  for (int e = tid; e < CHUNK * DV; e += 256) {
-    const int s = e / DV, cc = e - s * DV;
-    const int t = t0 + s;
-    sV[s][cc] = t < T ? TR::to_f32(v[(static_cast<size_t>(b) * T + t) * H * DV + h * DV + cc]) : 0.f;
+  // the chunk's value rows in 16-byte pieces
+  constexpr int VE = 16 / static_cast<int>(sizeof(typename TR::in_t));  // values per piece
+  constexpr int VP = DV / VE;                                            // pieces per row
+  for (int e = tid; e < CHUNK * VP; e += 256) {
+    const int sr = e / VP, pc = e - sr * VP;
+    const int t = t0 + sr;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (t < T) x = *reinterpret_cast<const u32x4*>(v + (static_cast<size_t>(b) * T + t) * H * DV + h * DV + VE * pc);
+    if constexpr (MODE == MODE_BF16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sV[sr][8 * pc + 2 * j] = __uint_as_float(x[j] << 16);
+        sV[sr][8 * pc + 2 * j + 1] = __uint_as_float(x[j] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sV[sr][4 * pc + j] = __uint_as_float(x[j]);
+    }
   }
   __syncthreads();
 
@@ -238,7 +266,13 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   for (int r = 0; r < CHUNK; ++r) {
     const float p = sW[t][r];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) w[j] += p * sT[r][s0 + j];
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const float4 tr = *reinterpret_cast<const float4*>(&sT[r][s0 + 4 * j4]);
+      w[4 * j4] += p * tr.x;
+      w[4 * j4 + 1] += p * tr.y;
+      w[4 * j4 + 2] += p * tr.z;
+      w[4 * j4 + 3] += p * tr.w;
+    }
   }
   const bool live = t0 + t < T;
   const float* lw = lam + ((static_cast<size_t>(b) * T + t0 + t) * H + h) * L;
@@ -258,10 +292,13 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   float acc[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i] = 0.f;
-  for (int s = 0; s < CHUNK; ++s) {
-    const float vv = sV[s][cc];
+  for (int s = 0; s < CHUNK; s += 4) {
+    const float v0 = sV[s][cc], v1 = sV[s + 1][cc], v2 = sV[s + 2][cc], v3 = sV[s + 3][cc];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) acc[i] += sW[g + G * i][s] * vv;
+    for (int i = 0; i < NR; ++i) {
+      const float4 wr = *reinterpret_cast<const float4*>(&sW[g + G * i][s]);
+      acc[i] += wr.x * v0 + wr.y * v1 + wr.z * v2 + wr.w * v3;
+    }
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {

@@ -305,6 +305,23 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
     const int t0 = c * CHUNK;
     const bool more = c + 1 < c_end;
     if (more) issue_loads(c + 1);
+    // ACC: the outputs already there and the weights of this chunk's rows, loaded now so that the
+    // adds at the end of the chunk never wait on a memory round trip (a load issued after the
+    // output stores would also wait for them: loads and stores share one in-order counter)
+    float acc_old[ACC ? 16 : 1], acc_w[ACC ? 16 : 1];
+    if constexpr (ACC) {
+      const rsrc_t ra = make_rsrc(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
+      const int abase = 4 * gq * rowO + (h * DV + vcol) * 4;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * mt + 4 * gq + i;
+          acc_old[4 * mt + i] = __uint_as_float(bload4(ra, abase + (16 * mt + i) * rowO));
+          acc_w[4 * mt + i] = t < T ? a.lam[((static_cast<size_t>(b) * T + t) * H + h) * a.lam_L + a.lam_level] : 0.f;
+        }
+      }
+    }
 
     // ---- S as B operand (contraction over keys) ----
     DF Sb[DK / 32];
@@ -375,15 +392,8 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
           if (kb == 0 || mt >= 2) O[mt] = TR::mma_dd(O[mt], TR::ldd(sPP, 16 * mt, 32 * kb, lane), Ub[kb]);
         if constexpr (ACC) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 16 * mt + 4 * gq + i;
-            if (t < T) {
-              const float w = a.lam[((static_cast<size_t>(b) * T + t) * H + h) * a.lam_L + a.lam_level];
-              const int off = obase + (16 * mt + i) * rowO;
-              const float old = __uint_as_float(bload4(ro, off));
-              bstore_f32(old + w * O[mt][i], ro, off);
-            }
-          }
+          for (int i = 0; i < 4; ++i)  // rows past T: weight 0, and the store falls outside the buffer
+            bstore_f32(acc_old[4 * mt + i] + acc_w[4 * mt + i] * O[mt][i], ro, obase + (16 * mt + i) * rowO);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) bstore_f32(O[mt][i], ro, obase + (16 * mt + i) * rowO);
