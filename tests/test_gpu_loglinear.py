@@ -193,3 +193,14 @@ def test_loglinear_prefill_full_size_sampled():
             ref[t] = o_t[0, 0]
         e = assert_close(o[b, :, h], ref, TOL["bf16"], f"head {(b, h)}")
         log(f"loglinear prefill full size head {(b, h)}: {e:.2e}")
+
+
+@pytest.mark.parametrize("B,H,T,L", [(1, 1, 256, 9), (3, 5, 130, 9), (1, 2, 128, 8), (2, 1, 64 * 5, 10)])
+def test_loglinear_prefill_edges(B, H, T, L):
+    """T = 2^(L-1) exactly (the top level in use), a grid of 15 heads, one and two full scales, and a
+    sequence of whole chunks with an odd number of half-blocks at the lowest scale."""
+    log(f"loglinear prefill edges B={B} H={H} T={T} L={L}")
+    wl, lam = _prefill_case(B, T, H, 64, 64, L, "bf16", seed=B * 1000 + H * 100 + T)
+    o = _run_prefill(wl, lam)
+    o_ref = loglinear.forward_loglinear(wl.q, wl.k, wl.v, wl.log_alpha, wl.eta, lam, wl.eps)
+    assert_close(o, o_ref, TOL["bf16"] / 10, "out")
