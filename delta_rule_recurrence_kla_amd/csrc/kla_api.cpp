@@ -396,7 +396,20 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   const size_t bh = static_cast<size_t>(B) * H;
   const size_t rec_bytes = align256(bh * nc * kla::full_record_bytes());
-  const size_t ends_bytes = align256(bh * ((nc + 1) / 2) * dk * dv * 4);  // the most left half-blocks: scale 7
+  // scales l >= 7: half-blocks of 2^(l-7) chunks while a right half-block exists; every scale's
+  // left end states are kept at once (at most nc states per head over all scales)
+  int nscale = 0, half[32], nleft[32], nright[32];
+  long long ends_off[32];
+  long long ends_floats = 0;
+  for (int hb = 1; hb < nc && nscale < 32; hb *= 2, ++nscale) {
+    const int nblk = (nc + hb - 1) / hb;
+    half[nscale] = hb;
+    nleft[nscale] = (nblk + 1) / 2;
+    nright[nscale] = nblk / 2;
+    ends_off[nscale] = ends_floats;
+    ends_floats += static_cast<long long>(bh) * nleft[nscale] * dk * dv;
+  }
+  const size_t ends_bytes = align256(static_cast<size_t>(ends_floats) * 4);
   if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
     if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
   }
@@ -413,14 +426,17 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
   e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
   if (e == hipSuccess)
     e = timed("kla_loglinear_intra", stream, [&] { return kla::launch_loglinear_intra(mode, d, rec, v, lam, levels, out, stream); });
-  // scale l >= 7: half-blocks of 2^(l-7) chunks; the right ones read the left siblings' end states
-  for (int level = 7, half = 1; e == hipSuccess && half < nc; ++level, half *= 2) {
-    const int nblk = (nc + half - 1) / half, nleft = (nblk + 1) / 2, nright = nblk / 2;
-    e = timed("kla_loglinear_left", stream, [&] { return kla::launch_loglinear_left(mode, d, k, v, rec, half, nleft, ends, stream); });
-    if (e == hipSuccess)
-      e = timed("kla_loglinear_right", stream, [&] {
-        return kla::launch_loglinear_right(mode, d, q, k, rec, half, nright, ends, nleft, lam, levels, level, out, stream);
-      });
+  // every scale's left walks in one grid (they are independent), then the right walks scale by
+  // scale (the scales add to the same outputs)
+  if (e == hipSuccess && nscale > 0)
+    e = timed("kla_loglinear_left", stream, [&] {
+      return kla::launch_loglinear_left(mode, d, k, v, rec, nscale, half, nleft, ends_off, ends, stream);
+    });
+  for (int i = 0; e == hipSuccess && i < nscale; ++i) {
+    e = timed("kla_loglinear_right", stream, [&] {
+      return kla::launch_loglinear_right(mode, d, q, k, rec, half[i], nright[i], ends + ends_off[i], nleft[i], lam, levels,
+                                         7 + i, out, stream);
+    });
   }
   hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

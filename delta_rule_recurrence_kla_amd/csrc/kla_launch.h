@@ -78,14 +78,17 @@ hipError_t launch_loglinear_decode(int mode, int N, int H, int dk, int dv, const
                                    float eps, int direct, float* states, float* out, int L, int t,
                                    hipStream_t stream);
 
-// Log-linear prefill (full records). Intra-chunk levels 0..6 written to out; then per scale
-// l >= 7 with half-blocks of `half` chunks: the zero-start end state of every left half-block
-// into ends [B*H][nleft][dk][dv], and the walk over every right half-block from its left
-// sibling's end state with no values, lambda^(l)-weighted outputs added to out.
+// Log-linear prefill (full records). Intra-chunk levels 0..6 written to out; the zero-start end
+// state of every left half-block of every scale l >= 7 (half-blocks of 2^(l-7) chunks) into
+// ends, per scale [B*H][nleft][dk][dv]; then per scale the walk over every right half-block from
+// its left sibling's end state with no values, lambda^(l)-weighted outputs added to out.
 hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, const void* v, const float* lam,
                                   int L, float* out, hipStream_t stream);
-hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int half,
-                                 int nleft, float* ends, hipStream_t stream);
+// All scales' left walks in one grid: scale i has half-blocks of half[i] chunks, nleft[i] left
+// ones per head, and writes their end states at ends + ends_off[i] (floats).
+hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int nscale,
+                                 const int* half, const int* nleft, const long long* ends_off, float* ends,
+                                 hipStream_t stream);
 hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec, int half,
                                   int nright, const float* ends, int nleft, const float* lam, int L, int level,
                                   float* out, hipStream_t stream);

@@ -25,12 +25,20 @@
 //
 // With LIFT = true the queries and keys arrive as the 16-wide vectors u of the KATA page's
 // rank-one PSD feature (section 2.2) and the kernel forms the 256 features u_a u_b (rounded
-// to bf16) as it moves each chunk's rows from the prefetch registers into LDS. Everything
-// after LDS is the dk = 256 kernel unchanged; the rows read from memory shrink 16-fold.
+// to bf16) in the prefetch registers, in the middle of the previous chunk's products, before
+// they move into LDS. Everything after LDS is the dk = 256 kernel unchanged; the rows read
+// from memory shrink 16-fold.
+//
+// The log-linear prefill (Log-Linear page, "Mathematical formalization") uses three more
+// options: a segment stride (seg_mul, seg_add: every other half-block of a scale), walks
+// with no values (v null: value loads go through a zero-size buffer range and read as
+// zeros), and ACC = true, which adds lambda-weighted outputs to the ones already in `out`.
 #include "kla_device.h"
 #include "kla_launch.h"
 
 namespace kla {
+
+constexpr int kMaxScales = 24;  // scales of 1, 2, 4, ... chunks: enough for any int T
 
 struct StateArgs {
   const void* q;
@@ -56,6 +64,14 @@ struct StateArgs {
   const float* lam = nullptr;
   int lam_L = 0;
   int lam_level = 0;
+  // Several scales in one grid (walks without outputs on the plain state only): scale i owns
+  // workgroups [scale_wg[i], scale_wg[i + 1]), walks segments of scale_half[i] chunks with
+  // stride 2, and writes its scale_nseg[i] end states per head at fin + scale_fin_off[i].
+  int nscale = 0;
+  int scale_wg[kMaxScales + 1] = {};
+  int scale_half[kMaxScales] = {};
+  int scale_nseg[kMaxScales] = {};
+  long long scale_fin_off[kMaxScales] = {};
 };
 
 // Workgroup id -> (column group, unit), unit = bh * nseg + seg. The column groups of one
@@ -114,8 +130,23 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int gq = lane >> 4, ln = lane & 15;
   int cg, unit;
-  decode_wg(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
-  const int bh = unit / a.nseg, seg = unit - bh * a.nseg;
+  // this workgroup's segment geometry (per scale when several scales share the grid)
+  int wg = blockIdx.x, nwg_here = static_cast<int>(gridDim.x);
+  int seg_chunks = a.seg_chunks, nseg = a.nseg, fin_segs = a.fin_segs;
+  float* fin_base = a.fin;
+  if constexpr (!WITH_OUT && !AUG) {
+    if (a.nscale > 0) {
+      int sc = 0;
+      while (sc + 1 < a.nscale && wg >= a.scale_wg[sc + 1]) ++sc;
+      wg -= a.scale_wg[sc];
+      nwg_here = a.scale_wg[sc + 1] - a.scale_wg[sc];
+      seg_chunks = a.scale_half[sc];
+      nseg = fin_segs = a.scale_nseg[sc];
+      fin_base = a.fin + a.scale_fin_off[sc];
+    }
+  }
+  decode_wg(wg, a.ncg, nwg_here / a.ncg, cg, unit);
+  const int bh = unit / nseg, seg = unit - bh * nseg;
   const int H = a.H, T = a.T, DV = a.DV;
   const int b = bh / H, h = bh - b * H;
   const int col0 = cg * NCOLS;            // first (augmented) column of the workgroup
@@ -123,8 +154,8 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   const bool ident = AUG && col0 < DK;    // identity part of [M | N]
   const int vcol0 = AUG ? col0 - DK : col0;
   const int vcol = vcol0 + 16 * w + ln;
-  const int c_begin = (seg * a.seg_mul + a.seg_add) * a.seg_chunks;
-  const int c_end = min(a.nc, c_begin + a.seg_chunks);
+  const int c_begin = (seg * a.seg_mul + a.seg_add) * seg_chunks;
+  const int c_end = min(a.nc, c_begin + seg_chunks);
 
   // byte strides between consecutive tokens, and this batch's first rows
   const int rowK = H * KIN * SZ, rowV = H * DV * SZ, rowO = H * DV * 4;
@@ -422,8 +453,8 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   }
 
   // end state
-  if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
-    float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
+  if (fin_base && (!a.fin_last_only || seg == nseg - 1)) {
+    float* F = fin_base + (static_cast<size_t>(bh) * fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
 #pragma unroll
     for (int mt = 0; mt < DK / 16; ++mt) {
 #pragma unroll
@@ -582,13 +613,26 @@ static hipError_t dispatch_scale(int mode, int dk, int nwg, const StateArgs& a, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int half,
-                                 int nleft, float* ends, hipStream_t stream) {
+hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int nscale,
+                                 const int* half, const int* nleft, const long long* ends_off, float* ends,
+                                 hipStream_t stream) {
+  if (nscale < 1 || nscale > kMaxScales) return hipErrorInvalidValue;
   const int ncg = d.dv / NCOLS_STATE;
-  StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, half, nullptr, 1, nullptr, ends, d.dv, nleft, 0, ncg, nleft};
+  StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, half[0], nullptr, 1, nullptr, ends, d.dv, nleft[0], 0, ncg,
+              nleft[0]};
   a.seg_mul = 2;
   a.seg_add = 0;
-  return dispatch_scale<false, false>(mode, d.dk, ncg * nleft * d.B * d.H, a, stream);
+  a.nscale = nscale;
+  int nwg = 0;
+  for (int i = 0; i < nscale; ++i) {
+    a.scale_wg[i] = nwg;
+    a.scale_half[i] = half[i];
+    a.scale_nseg[i] = nleft[i];
+    a.scale_fin_off[i] = ends_off[i];
+    nwg += ncg * nleft[i] * d.B * d.H;
+  }
+  a.scale_wg[nscale] = nwg;
+  return dispatch_scale<false, false>(mode, d.dk, nwg, a, stream);
 }
 
 hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec, int half,
