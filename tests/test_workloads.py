@@ -81,3 +81,36 @@ def test_head_slice():
     s = a.head_slice([(1, 2), (0, 1)])
     np.testing.assert_array_equal(s.q[0, :, 0], a.q[1, :, 2])
     np.testing.assert_array_equal(s.init_state[1, 0], a.init_state[0, 1])
+
+
+def test_psd_u_workload():
+    """The PSD workload before the lift: the same unit vectors as the lifted recipe, in bf16."""
+    a = W.make_psd_u(seed=0, B=2, T=50, H=3)
+    b = W.make_psd_u(seed=0, B=2, T=50, H=3)
+    np.testing.assert_array_equal(a.uq, b.uq)
+    assert a.uq.shape == (2, 50, 3, 16) and a.v.shape == (2, 50, 3, 128)
+    for x in (a.uq, a.uk, a.v):
+        np.testing.assert_array_equal(x, W.round_to_bf16(x))          # bf16-exact values
+    np.testing.assert_allclose(np.linalg.norm(a.uq, axis=-1), 1.0, atol=4e-3)
+    assert np.all(a.log_alpha == 0) and np.all(a.eta == 1) and a.init_state is None
+    lifted = W.make_prefill("psd_lift_8k", seed=0, B=2, T=50, H=3)
+    # same draws in the same order: the lifted recipe's features are psi of the unrounded u
+    np.testing.assert_allclose(W.psd_lift(a.uq), lifted.q, atol=2e-2)
+    g = W.make_psd_u(seed=1, B=1, T=20, H=2, dv=64, gates="gaussian", init_std=0.5)
+    assert np.all(g.log_alpha < 0) and np.all((g.eta > 0) & (g.eta < 1)) and g.init_state.shape == (1, 2, 256, 64)
+    with pytest.raises(ValueError):
+        W.make_psd_u(gates="other", B=1, T=1, H=1)
+
+
+def test_loglinear_inputs():
+    lam = W.make_loglinear_lambda(3, N=4, H=2, levels=5, seed=0)
+    assert lam.shape == (4, 2, 5) and lam.dtype == np.float32 and np.all((lam > 0) & (lam < 1))
+    np.testing.assert_array_equal(lam, W.make_loglinear_lambda(3, N=4, H=2, levels=5, seed=0))
+    assert not np.array_equal(lam, W.make_loglinear_lambda(4, N=4, H=2, levels=5, seed=0))
+    # the weights come from their own stream: the step's q, k, v are unchanged by drawing them
+    st = W.make_decode_step(3, N=4, H=2, dk=8, dv=8, seed=0)
+    np.testing.assert_array_equal(st.q, W.make_decode_step(3, N=4, H=2, dk=8, dv=8, seed=0).q)
+    S = W.make_loglinear_states(N=2, H=2, levels=3, dk=4, dv=4, std=0.5, seed=1)
+    assert S.shape == (2, 2, 3, 4, 4) and abs(float(S.std()) - 0.5) < 0.2
+    cfg = W.LOGLINEAR_DECODE_CONFIG
+    assert cfg["t0"] + cfg["steps"] <= 1 << (cfg["levels"] - 1)
