@@ -187,15 +187,19 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
 // chunk differ only in their low six bits, so their bucket is level 0 (s = t) or the index of
 // their highest differing bit plus one, at most 6:
 //   out_t = sum_{s <= t in the chunk} lambda_t^(level(t,s)) W_ts v_s          (written, not added)
-// One workgroup per (batch, head, chunk), fp32 on the vector ALU: W = P T' (16 pairs per
+// One workgroup per (batch, head, chunk), fp32 on the vector ALU: W = P T' (8 pairs per
 // thread), then the weighted W times the chunk's values.
+constexpr int INTRA_THREADS = 512;
+
 template <int MODE, int DV>
-__global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __restrict__ rec,
+__global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_kernel(const uint8_t* __restrict__ rec,
                                                               const typename Tr<MODE>::in_t* __restrict__ v,
                                                               const float* __restrict__ lam, float* __restrict__ out,
                                                               int T, int H, int nc, int L) {
   using TR = Tr<MODE>;
-  constexpr int G = 256 / DV;        // row groups
+  constexpr int NT = INTRA_THREADS;
+  constexpr int SPT = CHUNK * CHUNK / NT;  // pairs of W per thread (8)
+  constexpr int G = NT / DV;         // row groups
   constexpr int NR = CHUNK / G;      // rows per thread in the product with V
   constexpr int PT = CHUNK + 4;      // row pitch: 16-byte aligned rows, read four values at a time
   __shared__ __align__(16) float sT[CHUNK][PT];
@@ -211,8 +215,8 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   // T' and P rows in 16-byte pieces: a thread takes (row, block of 8 columns) and, in bf16 mode,
   // the hi and the lo piece of that block (pieces are swizzled within their row)
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + 256 * u;  // 512 (row, block) pairs
+  for (int u = 0; u < 512 / NT; ++u) {
+    const int e = tid + NT * u;  // 512 (row, block) pairs
     const int r = e >> 3, cb = e & 7;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   // the chunk's value rows in 16-byte pieces
   constexpr int VE = 16 / static_cast<int>(sizeof(typename TR::in_t));  // values per piece
   constexpr int VP = DV / VE;                                            // pieces per row
-  for (int e = tid; e < CHUNK * VP; e += 256) {
+  for (int e = tid; e < CHUNK * VP; e += NT) {
     const int sr = e / VP, pc = e - sr * VP;
     const int t = t0 + sr;
     u32x4 x = {0u, 0u, 0u, 0u};
@@ -258,15 +262,15 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   }
   __syncthreads();
 
-  // W_ts = sum_r P_tr T'_rs for row t and columns s0 .. s0 + 15 (both factors are lower triangular)
-  const int t = tid >> 2, s0 = (tid & 3) * 16;
-  float w[16];
+  // W_ts = sum_r P_tr T'_rs for row t and columns s0 .. s0 + SPT - 1 (both factors are lower triangular)
+  const int t = tid / (CHUNK / SPT), s0 = (tid % (CHUNK / SPT)) * SPT;
+  float w[SPT];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) w[j] = 0.f;
+  for (int j = 0; j < SPT; ++j) w[j] = 0.f;
   for (int r = 0; r < CHUNK; ++r) {
     const float p = sW[t][r];
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
+    for (int j4 = 0; j4 < SPT / 4; ++j4) {
       const float4 tr = *reinterpret_cast<const float4*>(&sT[r][s0 + 4 * j4]);
       w[4 * j4] += p * tr.x;
       w[4 * j4 + 1] += p * tr.y;
@@ -277,14 +281,14 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   const bool live = t0 + t < T;
   const float* lw = lam + ((static_cast<size_t>(b) * T + t0 + t) * H + h) * L;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < SPT; ++j) {
     const int s = s0 + j;
     const int lev = s == t ? 0 : 32 - __clz(static_cast<unsigned>(t ^ s));
     w[j] = (live && s <= t) ? w[j] * lw[lev] : 0.f;
   }
   __syncthreads();  // every read of P is done
 #pragma unroll
-  for (int j = 0; j < 16; ++j) sW[t][s0 + j] = w[j];
+  for (int j = 0; j < SPT; ++j) sW[t][s0 + j] = w[j];
   __syncthreads();
 
   // out_t = sum_s W_ts v_s for this thread's column cc and rows g, g + G, ...
@@ -292,6 +296,10 @@ __global__ __launch_bounds__(256) void loglinear_intra_kernel(const uint8_t* __r
   float acc[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) acc[i] = 0.f;
+  // full unrolling of this loop hoists every row's LDS reads at DV = 64 (and spills), so unroll it
+  // only where that keeps the registers low
+  constexpr int UNR = DV >= 128 ? 4 : 2;
+#pragma unroll UNR
   for (int s = 0; s < CHUNK; s += 4) {
     const float v0 = sV[s][cc], v1 = sV[s + 1][cc], v2 = sV[s + 2][cc], v3 = sV[s + 3][cc];
 #pragma unroll
@@ -312,12 +320,12 @@ hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, c
   const dim3 grid(d.B * d.H * d.nc);
   if (mode == MODE_BF16) {
     const auto* vb = static_cast<const Tr<MODE_BF16>::in_t*>(v);
-    if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 64>, grid, dim3(256), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
-    if (d.dv == 128) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 128>, grid, dim3(256), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
+    if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 64>, grid, dim3(INTRA_THREADS), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
+    if (d.dv == 128) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 128>, grid, dim3(INTRA_THREADS), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
   } else {
     const auto* vf = static_cast<const Tr<MODE_F32>::in_t*>(v);
-    if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_F32, 64>, grid, dim3(256), stream, rec, vf, lam, out, d.T, d.H, d.nc, L);
-    if (d.dv == 128) return launch_kernel(loglinear_intra_kernel<MODE_F32, 128>, grid, dim3(256), stream, rec, vf, lam, out, d.T, d.H, d.nc, L);
+    if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_F32, 64>, grid, dim3(INTRA_THREADS), stream, rec, vf, lam, out, d.T, d.H, d.nc, L);
+    if (d.dv == 128) return launch_kernel(loglinear_intra_kernel<MODE_F32, 128>, grid, dim3(INTRA_THREADS), stream, rec, vf, lam, out, d.T, d.H, d.nc, L);
   }
   return hipErrorInvalidValue;
 }
