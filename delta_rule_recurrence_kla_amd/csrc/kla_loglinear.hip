@@ -156,8 +156,7 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
       if (next > 0) load_set(nxt, next);  // consumed only after this bucket's barriers
       finish_bucket(cur, dest);
       if (next < 0) break;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) cur[p] = nxt[p];
+      for (int p = 0; p < NP; ++p) cur[p] = nxt[p];  // register renaming once unrolled
       dest = next;
     }
   }
