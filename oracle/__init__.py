@@ -11,9 +11,12 @@ it, and the two share no code.
                (features rounded to bf16) in front of kla_ref.forward
   loglinear.py log-linear KLA: Fenwick-bucketed states with per-level output weights,
                as a token-pair definition and as the recurrent (bucket-merge) form
+  kla_bwd.py   reverse-mode gradients of the token loop (dq, dk, dv, dlog_alpha, deta, dS0)
+               for a loss with given dO and dS_T
   cref.py      ctypes loader for the C build
   build.py     gcc build of kla_ref.c into oracle/libkla_ref.so
 """
 from . import kla_ref  # noqa: F401
 from . import psd_lift  # noqa: F401
 from . import loglinear  # noqa: F401
+from . import kla_bwd  # noqa: F401
