@@ -66,6 +66,7 @@ def load():
     lib.kla_decode_step_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, I, I, I, I, P]
     lib.kla_loglinear_decode_step.argtypes = [I, I, P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]
     lib.kla_loglinear_fwd.argtypes = [I, I, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, P]
+    lib.kla_chunk_bwd.argtypes = [I, I, P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
                "kla_decode_step_f32", "kla_decode_step_ex", "kla_loglinear_decode_step", "kla_loglinear_fwd",
                "kla_timing_enable",
@@ -297,6 +298,47 @@ def loglinear_fwd(q, k, v, log_alpha, eta, lam, eps: float = 1e-6, chunk: int = 
                                  _ptr(eta), _ptr(lam), float(eps), _ptr(out), B, T, H, dk, dv, L, chunk,
                                  _stream(stream)))
     return out
+
+
+def chunk_bwd(q, k, v, log_alpha, eta, grad_out, eps: float = 1e-6, init_state=None, grad_final_state=None,
+              chunk: int = 64, stream=None, beta_mode: str = "kaczmarz", want_grad_init: bool = True):
+    """Gradients of the prefill for given d loss / d out (grad_out fp32 [B,T,H,dv]) and
+    d loss / d final state (grad_final_state fp32 [B,H,dk,dv] or None: zero). Inputs as for
+    chunk_fwd (dk in {64, 128}). Returns a dict of fp32 tensors: dq, dk [B,T,H,dk], dv [B,T,H,dv],
+    dlog_alpha, deta [B,T,H] and dinit_state [B,H,dk,dv] (None unless want_grad_init)."""
+    import torch
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype == torch.bfloat16:
+        dtype = 0
+    elif q.dtype == torch.float32:
+        dtype = 1
+    else:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    if beta_mode not in BETA_MODES:
+        raise ValueError(f"beta_mode must be one of {sorted(BETA_MODES)}")
+    _need(q, "q", (B, T, H, dk), (q.dtype,), dev)
+    _need(k, "k", (B, T, H, dk), (q.dtype,), dev)
+    _need(v, "v", (B, T, H, dv), (q.dtype,), dev)
+    _need(log_alpha, "log_alpha", (B, T, H), (torch.float32,), dev)
+    _need(eta, "eta", (B, T, H), (torch.float32,), dev)
+    _need(grad_out, "grad_out", (B, T, H, dv), (torch.float32,), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (B, H, dk, dv), (torch.float32,), dev)
+    if grad_final_state is not None:
+        _need(grad_final_state, "grad_final_state", (B, H, dk, dv), (torch.float32,), dev)
+    f = dict(dtype=torch.float32, device=dev)
+    g = dict(dq=torch.empty((B, T, H, dk), **f), dk=torch.empty((B, T, H, dk), **f),
+             dv=torch.empty((B, T, H, dv), **f), dlog_alpha=torch.empty((B, T, H), **f),
+             deta=torch.empty((B, T, H), **f),
+             dinit_state=torch.empty((B, H, dk, dv), **f) if want_grad_init else None)
+    _check(lib.kla_chunk_bwd(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(eta),
+                             float(eps), _ptr(init_state), _ptr(grad_out), _ptr(grad_final_state), _ptr(g["dq"]),
+                             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["deta"]),
+                             _ptr(g["dinit_state"]), B, T, H, dk, dv, chunk, _stream(stream)))
+    return g
 
 
 def plan(B: int, T: int, H: int, dk: int, dv: int, chunk: int = 64, path: str = "auto",

@@ -444,6 +444,63 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
   return KLA_OK;
 }
 
+kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* eta, float eps, const float* init_state,
+                         const float* grad_out, const float* grad_final_state, float* grad_q, float* grad_k,
+                         float* grad_v, float* grad_log_alpha, float* grad_eta, float* grad_init_state, int B, int T,
+                         int H, int dk, int dv, int chunk, hipStream_t stream) {
+  kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
+  if (st != KLA_OK) return st;
+  if (dk > 128) return fail(KLA_ERR_UNSUPPORTED, "the backward supports dk in {64, 128} (got %d)", dk);
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
+    return fail(KLA_ERR_INVALID_ARG, "unknown beta_mode %d", (int)beta_mode);
+  if (T > 0 && (!q || !k || !v || !log_alpha || !eta || !grad_out || !grad_q || !grad_k || !grad_v ||
+                !grad_log_alpha || !grad_eta))
+    return fail(KLA_ERR_INVALID_ARG,
+                "q, k, v, log_alpha, eta, grad_out and grad_q .. grad_eta must be non-null when T > 0");
+  const size_t state_n = static_cast<size_t>(B) * H * dk * dv;
+  if (T == 0) {  // the start state's gradient is the end state's
+    if (grad_init_state && grad_init_state != grad_final_state) {
+      hipError_t e = timed("kla_copy_or_zero", stream, [&] {
+        return kla::launch_copy_or_zero(grad_final_state, grad_init_state, state_n, stream);
+      });
+      if (e != hipSuccess) return hip_fail(e, "launch");
+    }
+    return KLA_OK;
+  }
+  if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
+    if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
+  }
+  const int nc = (T + kChunk - 1) / kChunk;
+  const size_t nch = static_cast<size_t>(B) * H * nc;
+  const size_t bytes = kla::bwd_workspace_bytes(B, T, H, dk, dv);
+  keep_pool_warm();
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  if (e != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return fail(KLA_ERR_OOM, "hipMallocAsync(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  }
+  kla::BwdArgs a{};
+  a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.nc = nc;
+  a.direct = beta_mode == KLA_BETA_DIRECT;
+  a.eps = eps;
+  a.q = q; a.k = k; a.v = v;
+  a.log_alpha = log_alpha; a.eta = eta; a.init = init_state; a.dout = grad_out; a.dfin = grad_final_state;
+  a.rec = static_cast<float*>(ws);
+  a.states = a.rec + nch * kla::bwd_record_floats();
+  a.dstates = a.states + nch * dk * dv;
+  a.gq = grad_q; a.gk = grad_k; a.gv = grad_v; a.gla = grad_log_alpha; a.geta = grad_eta; a.ginit = grad_init_state;
+  const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
+  static const char* const names[4] = {"kla_bwd_prep", "kla_bwd_states", "kla_bwd_dstates", "kla_bwd_grads"};
+  for (int stage = 0; e == hipSuccess && stage < 4; ++stage)
+    e = timed(names[stage], stream, [&] { return kla::launch_bwd(mode, a, stage, stream); });
+  hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
+  return KLA_OK;
+}
+
 kla_status kla_decode_step_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
                               const float* log_alpha, const float* eta, float eps, float* state, float* out, int N,
                               int H, int dk, int dv, hipStream_t stream) {

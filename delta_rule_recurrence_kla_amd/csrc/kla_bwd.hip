@@ -1,0 +1,519 @@
+// Chunkwise backward of the KLA prefill (gradients for training), fp32 arithmetic.
+//
+// The forward of one 64-token chunk with start state S0 (UT form of the delta rule, the
+// chunkwise parallel algorithm that the KLA page trains with; KLA page, "Implementation"):
+//   g  = cumsum(log_alpha) inside the chunk,  Dl[r][i] = e^{g_r - g_i},  w = e^{g_C - g}
+//   A  = strict_lower(beta_r Dl[r][i] (k_r . k_i)),  Minv = (I + A)^-1,  T' = Minv diag(beta)
+//   X  = V - e^g . (K S0),   U = T' X,   P = tril_incl(Dl . Q K^T)
+//   O  = e^g . (Q S0) + P U,   S1 = e^{g_C} S0 + K^T (w . U)
+// Reverse mode through these products runs in four kernels:
+//   prep     per chunk: g, beta, ||k||^2 + eps, Minv, and P with K K^T in one matrix
+//   states   forward walk over chunks per 16-column block of the state: every chunk-start S0
+//   dstates  reverse walk per 16-column block: every chunk-end gradient dS1, from
+//              dS0 = e^{g_C} dS1 + Q^T (e^g . dO) - K^T (e^g . dX),
+//              dX  = diag(beta) Minv^T dU,  dU = w . (K dS1) + P^T dO
+//   grads    per chunk, from S0 and dS1: dq, dk, dv, dlog_alpha, deta (the chunk-local
+//            products of the reverse pass, then a reverse cumulative sum of dg inside the chunk)
+// The columns of the state (the dv index) are independent in both walks, so a walk
+// workgroup owns 16 columns. A ragged last chunk is padded with identity steps
+// (k = q = v = 0, log_alpha = 0, eta = 0), which changes neither outputs nor gradients.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_launch.h"
+
+namespace kla {
+namespace {
+
+constexpr int BC = 64;    // chunk length
+constexpr int BT = 256;   // threads per workgroup
+constexpr int MP = 65;    // LDS pitch of 64 x 64 matrices
+constexpr int NJ = 16;    // state columns per walk workgroup / per grads column block
+constexpr int NJP = NJ + 1;
+// chunk record: Minv [64][64], PG [64][64] (lower incl: P; strict upper: K K^T), g, beta, den
+constexpr int REC_M = 0, REC_PG = BC * BC, REC_G = 2 * BC * BC, REC_B = REC_G + BC, REC_D = REC_B + BC;
+constexpr int RECF = REC_D + 2 * BC;
+
+template <int MODE>
+__device__ __forceinline__ float ldin(const void* p, size_t i) {
+  if constexpr (MODE == 0) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  else return static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ size_t tok(int b, int t, int T, int H, int h) {
+  return (static_cast<size_t>(b) * T + t) * H + h;
+}
+
+// Loads rows of a [B,T,H,D] input for the 64 tokens of chunk c into s[64][D + 1] (zeros past T).
+template <int MODE, int D>
+__device__ __forceinline__ void load_rows(float (*s)[D + 1], const void* x, int b, int h, int c, int T, int H) {
+  for (int e = threadIdx.x; e < BC * D; e += BT) {
+    const int r = e / D, d = e % D, t = c * BC + r;
+    s[r][d] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * D + d) : 0.f;
+  }
+}
+
+// Columns jb .. jb+15 of a [B,T,H,DV] fp32 or input array for chunk c into s[64][NJP].
+template <int MODE>
+__device__ __forceinline__ void load_cols(float* s, const void* x, int b, int h, int c, int T, int H, int DV, int jb) {
+  for (int e = threadIdx.x; e < BC * NJ; e += BT) {
+    const int r = e / NJ, j = e % NJ, t = c * BC + r;
+    s[r * NJP + j] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * DV + jb + j) : 0.f;
+  }
+}
+
+template <int MODE, int DK>
+__global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void* k, const float* log_alpha,
+                                                      const float* eta, float eps, int direct, int T, int H, int nc,
+                                                      float* rec) {
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1];
+  __shared__ float sA[BC][MP], sM[BC][MP];
+  __shared__ float sla[BC], sg[BC], sb[BC];
+  load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
+  load_rows<MODE, DK>(sK, k, b, h, c, T, H);
+  float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
+  const int t = c * BC + tid;
+  if (tid < BC) sla[tid] = t < T ? log_alpha[tok(b, t, T, H, h)] : 0.f;
+  __syncthreads();
+  if (tid < BC) {
+    float gs = 0.f;
+    for (int i = 0; i <= tid; ++i) gs += sla[i];
+    float n = 0.f;
+    for (int d = 0; d < DK; ++d) n = fmaf(sK[tid][d], sK[tid][d], n);
+    const float et = t < T ? eta[tok(b, t, T, H, h)] : 0.f;
+    const float den = n + eps;
+    const float beta = direct ? et : (den != 0.f ? et / den : 0.f);
+    sg[tid] = gs;
+    sb[tid] = beta;
+    R[REC_G + tid] = gs;
+    R[REC_B + tid] = beta;
+    R[REC_D + tid] = den;
+  }
+  __syncthreads();
+  // lower triangle incl. the diagonal: P = Dl . Q K^T; strict upper: K K^T (symmetric, so
+  // entry [r][i], i > r, is also G[i][r]); A = strict lower beta_r Dl G
+  for (int e = tid; e < BC * BC; e += BT) {
+    const int r = e / BC, i = e % BC;
+    float qk = 0.f, kk = 0.f;
+    for (int d = 0; d < DK; ++d) {
+      qk = fmaf(sQ[r][d], sK[i][d], qk);
+      kk = fmaf(sK[r][d], sK[i][d], kk);
+    }
+    const float dl = i <= r ? expf(sg[r] - sg[i]) : 0.f;
+    R[REC_PG + e] = i <= r ? dl * qk : kk;
+    sA[r][i] = i < r ? sb[r] * dl * kk : 0.f;
+  }
+  __syncthreads();
+  // (I + A)^-1 is unit lower triangular; forward substitution, one column per thread
+  if (tid < BC) {
+    const int col = tid;
+    for (int r = 0; r < BC; ++r) {
+      float m = r == col ? 1.f : 0.f;
+      if (r > col) {
+        float s = 0.f;
+        for (int i = col; i < r; ++i) s = fmaf(sA[r][i], sM[i][col], s);
+        m = -s;
+      }
+      sM[r][col] = m;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < BC * BC; e += BT) R[REC_M + e] = sM[e / BC][e % BC];
+}
+
+// Forward walk over the chunks of one (b, h) for state columns jb .. jb+15; stores every
+// chunk-start state S0 into states[bh][c][DK][DV].
+template <int MODE, int DK>
+__global__ __launch_bounds__(BT) void bwd_states_kernel(const void* k, const void* v, const float* rec,
+                                                        const float* init, int T, int H, int DV, int nc,
+                                                        float* states) {
+  constexpr int EPT = DK * NJ / BT, TPR = NJ / EPT;
+  const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  __shared__ float sK[BC][DK + 1], sM[BC][MP];
+  __shared__ float sS[DK][NJP], sX[BC * NJP], sU[BC][NJP];
+  __shared__ float sg[BC], sb[BC];
+  const int sd = tid / TPR, sj = (tid % TPR) * EPT;  // state elements owned
+  const int r = tid >> 2, j0 = (tid & 3) * 4;         // 64 x 16 chunk elements owned
+  float s[EPT];
+  for (int e = 0; e < EPT; ++e)
+    s[e] = init ? init[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
+    float* S0 = states + (static_cast<size_t>(bh) * nc + c) * DK * DV;
+    for (int e = 0; e < EPT; ++e) {
+      S0[sd * DV + jb + sj + e] = s[e];
+      sS[sd][sj + e] = s[e];
+    }
+    load_rows<MODE, DK>(sK, k, b, h, c, T, H);
+    load_cols<MODE>(sX, v, b, h, c, T, H, DV, jb);
+    for (int e = tid; e < BC * BC; e += BT) sM[e / BC][e % BC] = R[REC_M + e];
+    if (tid < BC) {
+      sg[tid] = R[REC_G + tid];
+      sb[tid] = R[REC_B + tid];
+    }
+    __syncthreads();
+    // beta . X with X = V - e^g . (K S0)
+    const float egr = expf(sg[r]);
+    float x[4];
+    for (int jj = 0; jj < 4; ++jj) {
+      float a = 0.f;
+      for (int d = 0; d < DK; ++d) a = fmaf(sK[r][d], sS[d][j0 + jj], a);
+      x[jj] = sb[r] * (sX[r * NJP + j0 + jj] - egr * a);
+    }
+    for (int jj = 0; jj < 4; ++jj) sX[r * NJP + j0 + jj] = x[jj];
+    __syncthreads();
+    // w . U with U = Minv (beta . X)
+    const float gC = sg[BC - 1];
+    const float wr = expf(gC - sg[r]);
+    for (int jj = 0; jj < 4; ++jj) {
+      float a = 0.f;
+      for (int i = 0; i <= r; ++i) a = fmaf(sM[r][i], sX[i * NJP + j0 + jj], a);
+      sU[r][j0 + jj] = wr * a;
+    }
+    __syncthreads();
+    const float gam = expf(gC);
+    for (int e = 0; e < EPT; ++e) {
+      float a = 0.f;
+      for (int i = 0; i < BC; ++i) a = fmaf(sK[i][sd], sU[i][sj + e], a);
+      s[e] = fmaf(gam, s[e], a);
+    }
+    __syncthreads();
+  }
+}
+
+// Reverse walk: every chunk-end state gradient dS1 into dstates[bh][c]; the start state's
+// gradient into dinit (if not null).
+template <int MODE, int DK>
+__global__ __launch_bounds__(BT) void bwd_dstates_kernel(const void* q, const void* k, const float* dout,
+                                                         const float* rec, const float* dfin, int T, int H, int DV,
+                                                         int nc, float* dstates, float* dinit) {
+  constexpr int EPT = DK * NJ / BT, TPR = NJ / EPT;
+  const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1], sM[BC][MP], sPG[BC][MP];
+  __shared__ float sS[DK][NJP], sO[BC * NJP], sU[BC][NJP], sX[BC][NJP];
+  __shared__ float sg[BC], sb[BC];
+  const int sd = tid / TPR, sj = (tid % TPR) * EPT;
+  const int r = tid >> 2, j0 = (tid & 3) * 4;
+  float s[EPT];
+  for (int e = 0; e < EPT; ++e)
+    s[e] = dfin ? dfin[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
+  for (int c = nc - 1; c >= 0; --c) {
+    const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
+    float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
+    for (int e = 0; e < EPT; ++e) {
+      D1[sd * DV + jb + sj + e] = s[e];
+      sS[sd][sj + e] = s[e];
+    }
+    load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
+    load_rows<MODE, DK>(sK, k, b, h, c, T, H);
+    load_cols<1>(sO, dout, b, h, c, T, H, DV, jb);
+    for (int e = tid; e < BC * BC; e += BT) {
+      sM[e / BC][e % BC] = R[REC_M + e];
+      sPG[e / BC][e % BC] = R[REC_PG + e];
+    }
+    if (tid < BC) {
+      sg[tid] = R[REC_G + tid];
+      sb[tid] = R[REC_B + tid];
+    }
+    __syncthreads();
+    const float gC = sg[BC - 1];
+    const float wr = expf(gC - sg[r]), egr = expf(sg[r]);
+    // dU = w . (K dS1) + P^T dO
+    for (int jj = 0; jj < 4; ++jj) {
+      float a = 0.f;
+      for (int d = 0; d < DK; ++d) a = fmaf(sK[r][d], sS[d][j0 + jj], a);
+      float p = 0.f;
+      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], sO[i * NJP + j0 + jj], p);
+      sU[r][j0 + jj] = fmaf(wr, a, p);
+    }
+    __syncthreads();
+    // e^g . dX with dX = diag(beta) Minv^T dU; e^g . dO in place
+    for (int jj = 0; jj < 4; ++jj) {
+      float a = 0.f;
+      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[i][j0 + jj], a);
+      sX[r][j0 + jj] = egr * sb[r] * a;
+      sO[r * NJP + j0 + jj] *= egr;
+    }
+    __syncthreads();
+    const float gam = expf(gC);
+    for (int e = 0; e < EPT; ++e) {
+      float a = 0.f;
+      for (int i = 0; i < BC; ++i) a = fmaf(sQ[i][sd], sO[i * NJP + sj + e], fmaf(-sK[i][sd], sX[i][sj + e], a));
+      s[e] = fmaf(gam, s[e], a);
+    }
+    __syncthreads();
+  }
+  if (dinit)
+    for (int e = 0; e < EPT; ++e) dinit[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] = s[e];
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
+// Per-chunk gradients from the chunk-start state S0 and the chunk-end gradient dS1.
+template <int MODE, int DK>
+__global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void* k, const void* v, const float* eta,
+                                                       const float* dout, const float* rec, const float* states,
+                                                       const float* dstates, int direct, int T, int H, int DV, int nc,
+                                                       float* dq, float* dk, float* dv, float* dla, float* deta) {
+  constexpr int EPT = DK * NJ / BT, TPR = NJ / EPT, DQ = DK / 4;
+  constexpr int WCOL = 2 * DK * NJP + 5 * BC * NJP, WMAT = 2 * BC * MP;
+  constexpr int WN = WCOL > WMAT ? WCOL : WMAT;
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1], sM[BC][MP], sPG[BC][MP];
+  __shared__ float sW[WN];
+  __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], sdg[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
+  __shared__ float sgam;
+  // column-block phase
+  float* cS = sW;             // S0 [DK][NJP]
+  float* cD = cS + DK * NJP;  // dS1 [DK][NJP]
+  float* cX = cD + DK * NJP;  // V, then X [BC][NJP]
+  float* cO = cX + BC * NJP;  // dO
+  float* cU = cO + BC * NJP;  // U
+  float* cDU = cU + BC * NJP;
+  float* cDX = cDU + BC * NJP;
+  // matrix phase
+  float* m1 = sW;
+  float* m2 = sW + BC * MP;
+
+  const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
+  const float* S0 = states + (static_cast<size_t>(bh) * nc + c) * DK * DV;
+  const float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
+  load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
+  load_rows<MODE, DK>(sK, k, b, h, c, T, H);
+  for (int e = tid; e < BC * BC; e += BT) {
+    sM[e / BC][e % BC] = R[REC_M + e];
+    sPG[e / BC][e % BC] = R[REC_PG + e];
+  }
+  if (tid < BC) {
+    sg[tid] = R[REC_G + tid];
+    sb[tid] = R[REC_B + tid];
+    sden[tid] = R[REC_D + tid];
+  }
+  if (tid == 0) sgam = 0.f;
+  const int r = tid >> 2, qd = tid & 3, j0 = qd * 4, i0 = qd * 16, d0 = qd * DQ;
+  const int sd = tid / TPR, sj = (tid % TPR) * EPT;
+  float accP[16], accT[16], accQ[DQ], accK[DQ];
+  for (int i = 0; i < 16; ++i) accP[i] = accT[i] = 0.f;
+  for (int i = 0; i < DQ; ++i) accQ[i] = accK[i] = 0.f;
+  float dwp = 0.f, degp = 0.f, gamp = 0.f;
+  __syncthreads();
+  const float gC = sg[BC - 1];
+  const float egr = expf(sg[r]), wr = expf(gC - sg[r]);
+
+  for (int jb = 0; jb < DV; jb += NJ) {
+    for (int e = 0; e < EPT; ++e) {
+      cS[sd * NJP + sj + e] = S0[sd * DV + jb + sj + e];
+      cD[sd * NJP + sj + e] = D1[sd * DV + jb + sj + e];
+    }
+    load_cols<MODE>(cX, v, b, h, c, T, H, DV, jb);
+    load_cols<1>(cO, dout, b, h, c, T, H, DV, jb);
+    __syncthreads();
+    float ks[4], kd[4];
+    for (int jj = 0; jj < 4; ++jj) {
+      float a = 0.f, qs = 0.f, e2 = 0.f;
+      for (int d = 0; d < DK; ++d) {
+        a = fmaf(sK[r][d], cS[d * NJP + j0 + jj], a);
+        qs = fmaf(sQ[r][d], cS[d * NJP + j0 + jj], qs);
+        e2 = fmaf(sK[r][d], cD[d * NJP + j0 + jj], e2);
+      }
+      ks[jj] = a;
+      kd[jj] = e2;
+      degp = fmaf(cO[r * NJP + j0 + jj], qs, degp);
+    }
+    for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[sd * NJP + sj + e], cD[sd * NJP + sj + e], gamp);
+    for (int jj = 0; jj < 4; ++jj) cX[r * NJP + j0 + jj] -= egr * ks[jj];  // X
+    __syncthreads();
+    // U = Minv (beta . X); dU = w . (K dS1) + P^T dO
+    for (int jj = 0; jj < 4; ++jj) {
+      float u = 0.f, p = 0.f;
+      for (int i = 0; i <= r; ++i) u = fmaf(sM[r][i], sb[i] * cX[i * NJP + j0 + jj], u);
+      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], cO[i * NJP + j0 + jj], p);
+      cU[r * NJP + j0 + jj] = u;
+      cDU[r * NJP + j0 + jj] = fmaf(wr, kd[jj], p);
+      dwp = fmaf(u, kd[jj], dwp);
+    }
+    __syncthreads();
+    // dX = diag(beta) Minv^T dU, which is also dV
+    for (int jj = 0; jj < 4; ++jj) {
+      float a = 0.f;
+      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], cDU[i * NJP + j0 + jj], a);
+      const float dx = sb[r] * a;
+      cDX[r * NJP + j0 + jj] = dx;
+      degp = fmaf(-dx, ks[jj], degp);
+      const int t = c * BC + r;
+      if (t < T) dv[tok(b, t, T, H, h) * DV + jb + j0 + jj] = dx;
+    }
+    __syncthreads();
+    // dP += dO U^T and dT' += dU X^T over these columns (16 entries of row r each)
+    for (int j = 0; j < NJ; ++j) {
+      const float o = cO[r * NJP + j], du = cDU[r * NJP + j];
+      for (int ii = 0; ii < 16; ++ii) {
+        accP[ii] = fmaf(o, cU[(i0 + ii) * NJP + j], accP[ii]);
+        accT[ii] = fmaf(du, cX[(i0 + ii) * NJP + j], accT[ii]);
+      }
+    }
+    // dQ += e^g . (dO S0^T);  dK += w . (U dS1^T) - e^g . (dX S0^T)
+    for (int j = 0; j < NJ; ++j) {
+      const float o = egr * cO[r * NJP + j], u = wr * cU[r * NJP + j], x = egr * cDX[r * NJP + j];
+      for (int dd = 0; dd < DQ; ++dd) {
+        const float s0 = cS[(d0 + dd) * NJP + j];
+        accQ[dd] = fmaf(o, s0, accQ[dd]);
+        accK[dd] = fmaf(u, cD[(d0 + dd) * NJP + j], fmaf(-x, s0, accK[dd]));
+      }
+    }
+    __syncthreads();
+  }
+
+  const float dw = quad_sum(dwp), deg = quad_sum(degp);
+  gamp = quad_sum(gamp);
+  if (qd == 0) {
+    sdw[r] = dw;
+    sdeg[r] = deg;
+    atomicAdd(&sgam, gamp);
+  }
+  // dQK = tril_incl(dP) . Dl;  dDl . Dl collects dP . P (and below dA . A)
+  float dd16[16];
+  for (int ii = 0; ii < 16; ++ii) {
+    const int i = i0 + ii;
+    const bool low = i <= r;
+    m1[r * MP + i] = low ? accP[ii] * expf(sg[r] - sg[i]) : 0.f;
+    m2[r * MP + i] = accT[ii];
+    dd16[ii] = low ? accP[ii] * sPG[r][i] : 0.f;
+  }
+  __syncthreads();
+  for (int i = 0; i < BC; ++i) {
+    const float a = m1[r * MP + i], at = m1[i * MP + r];
+    for (int dd = 0; dd < DQ; ++dd) {
+      accQ[dd] = fmaf(a, sK[i][d0 + dd], accQ[dd]);
+      accK[dd] = fmaf(at, sQ[i][d0 + dd], accK[dd]);
+    }
+  }
+  if (tid < BC) {  // dbeta from T' = Minv diag(beta): column sums of Minv . dT'
+    float a = 0.f;
+    for (int i = tid; i < BC; ++i) a = fmaf(sM[i][tid], m2[i * MP + tid], a);
+    sdb[tid] = a;
+  }
+  // W1 = Minv^T dT' diag(beta)
+  float w1[16];
+  for (int ii = 0; ii < 16; ++ii) {
+    const int i = i0 + ii;
+    float a = 0.f;
+    for (int j = r; j < BC; ++j) a = fmaf(sM[j][r], m2[j * MP + i], a);
+    w1[ii] = a * sb[i];
+  }
+  __syncthreads();
+  for (int ii = 0; ii < 16; ++ii) m1[r * MP + i0 + ii] = w1[ii];
+  __syncthreads();
+  // dA = strict_lower(-W1 Minv^T); A = beta_r Dl G gives dbeta, dDl and dG
+  float dbp = 0.f;
+  float dG[16];
+  for (int ii = 0; ii < 16; ++ii) {
+    const int i = i0 + ii;
+    dG[ii] = 0.f;
+    if (i < r) {
+      float a = 0.f;
+      for (int j = 0; j <= i; ++j) a = fmaf(m1[r * MP + j], sM[i][j], a);
+      const float da = -a, dl = expf(sg[r] - sg[i]), G = sPG[i][r];
+      dbp = fmaf(da * dl, G, dbp);
+      dd16[ii] = fmaf(da * sb[r] * dl, G, dd16[ii]);
+      dG[ii] = da * sb[r] * dl;
+    }
+  }
+  dbp = quad_sum(dbp);
+  __syncthreads();  // m1 (W1) and m2 (dT') fully read
+  for (int ii = 0; ii < 16; ++ii) {
+    m2[r * MP + i0 + ii] = dG[ii];
+    m1[r * MP + i0 + ii] = dd16[ii];
+  }
+  float rs = 0.f;
+  for (int ii = 0; ii < 16; ++ii) rs += dd16[ii];
+  rs = quad_sum(rs);
+  if (qd == 0) {
+    srow[r] = rs;
+    sdb[r] += dbp;
+  }
+  __syncthreads();
+  // dK += (dG + dG^T) K
+  for (int i = 0; i < BC; ++i) {
+    const float a = m2[r * MP + i] + m2[i * MP + r];
+    for (int dd = 0; dd < DQ; ++dd) accK[dd] = fmaf(a, sK[i][d0 + dd], accK[dd]);
+  }
+  if (tid < BC) {
+    const int i = tid, t = c * BC + i;
+    float cs = 0.f;
+    for (int j = 0; j < BC; ++j) cs += m1[j * MP + i];
+    float dg = srow[i] - cs + sdeg[i] * expf(sg[i]) - sdw[i] * expf(gC - sg[i]);
+    if (i == BC - 1) {
+      float a = 0.f;
+      for (int j = 0; j < BC; ++j) a = fmaf(sdw[j], expf(gC - sg[j]), a);
+      dg += a + sgam * expf(gC);
+    }
+    sdg[i] = dg;
+    const float db = sdb[i], den = sden[i];
+    const float et = t < T ? eta[tok(b, t, T, H, h)] : 0.f;
+    float de = db, kc = 0.f;
+    if (!direct) {
+      de = den != 0.f ? db / den : 0.f;
+      kc = den != 0.f ? -2.f * db * et / (den * den) : 0.f;
+    }
+    skc[i] = kc;
+    if (t < T) deta[tok(b, t, T, H, h)] = de;
+  }
+  __syncthreads();
+  if (tid < BC) {
+    const int i = tid, t = c * BC + i;
+    float a = 0.f;
+    for (int j = BC - 1; j >= i; --j) a += sdg[j];
+    if (t < T) dla[tok(b, t, T, H, h)] = a;
+  }
+  const int t = c * BC + r;
+  if (t < T) {
+    const size_t o = tok(b, t, T, H, h) * DK + d0;
+    for (int dd = 0; dd < DQ; ++dd) {
+      dq[o + dd] = accQ[dd];
+      dk[o + dd] = fmaf(skc[r], sK[r][d0 + dd], accK[dd]);
+    }
+  }
+}
+
+template <int MODE, int DK>
+hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
+  const dim3 blk(BT);
+  const int bh = a.B * a.H;
+  switch (stage) {
+    case 0:
+      return launch_kernel(bwd_prep_kernel<MODE, DK>, dim3(a.nc, bh), blk, stream, a.q, a.k, a.log_alpha, a.eta, a.eps,
+                           a.direct, a.T, a.H, a.nc, a.rec);
+    case 1:
+      return launch_kernel(bwd_states_kernel<MODE, DK>, dim3(a.dv / NJ, bh), blk, stream, a.k, a.v, a.rec, a.init, a.T,
+                           a.H, a.dv, a.nc, a.states);
+    case 2:
+      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJ, bh), blk, stream, a.q, a.k, a.dout, a.rec,
+                           a.dfin, a.T, a.H, a.dv, a.nc, a.dstates, a.ginit);
+    default:
+      return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), blk, stream, a.q, a.k, a.v, a.eta, a.dout,
+                           a.rec, a.states, a.dstates, a.direct, a.T, a.H, a.dv, a.nc, a.gq, a.gk, a.gv, a.gla,
+                           a.geta);
+  }
+}
+
+}  // namespace
+
+size_t bwd_record_floats() { return RECF; }
+
+size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
+  const size_t nch = static_cast<size_t>(B) * H * ((T + BC - 1) / BC);
+  return nch * (RECF + 2 * static_cast<size_t>(dk) * dv) * sizeof(float);
+}
+
+hipError_t launch_bwd(int mode, const BwdArgs& a, int stage, hipStream_t stream) {
+  if (mode == 0) return a.dk == 64 ? launch_bwd_t<0, 64>(a, stage, stream) : launch_bwd_t<0, 128>(a, stage, stream);
+  return a.dk == 64 ? launch_bwd_t<1, 64>(a, stage, stream) : launch_bwd_t<1, 128>(a, stage, stream);
+}
+
+}  // namespace kla

@@ -140,6 +140,35 @@ kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, cons
                              kla_path path, int segments, hipStream_t stream);
 
 /*
+ * Chunkwise backward of the prefill, for training (KLA page, "Implementation": the
+ * model keeps Gated DeltaNet's chunkwise parallel training algorithm; the HLA page,
+ * section 4, trains chunked recurrences exactly rather than by truncated
+ * backpropagation through time). The gradients are those of the exact recurrence,
+ * taken in reverse through each chunk's UT form. Given the inputs of a kla_chunk_fwd_ex
+ * call and the gradients of a loss with respect to its outputs, it writes the
+ * gradients with respect to every input:
+ *   grad_out          fp32 [B,T,H,dv]   d loss / d out
+ *   grad_final_state  fp32 [B,H,dk,dv]  d loss / d final_state, or NULL (zero)
+ *   grad_q, grad_k    fp32 [B,T,H,dk];  grad_v fp32 [B,T,H,dv]
+ *   grad_log_alpha, grad_eta            fp32 [B,T,H]
+ *   grad_init_state   fp32 [B,H,dk,dv], or NULL (not written)
+ * Every output is overwritten (not accumulated). q, k, v, gates, eps, init_state
+ * (NULL: zero), beta_mode and sizes are as for kla_chunk_fwd_ex; dk must be 64
+ * or 128. In Kaczmarz mode a token with ||k||^2 + eps == 0 has beta = 0 and
+ * passes no gradient to eta or through beta to k. The arithmetic is fp32; the
+ * call takes a stream-ordered workspace of about B*H*ceil(T/64) * (34 KB +
+ * 8*dk*dv bytes) (chunk records, every chunk-start state and every chunk-end
+ * state gradient) and frees it on the stream. T == 0 copies grad_final_state
+ * (or zeros) into grad_init_state.
+ */
+kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                         const void* v, const float* log_alpha, const float* eta, float eps,
+                         const float* init_state, const float* grad_out, const float* grad_final_state,
+                         float* grad_q, float* grad_k, float* grad_v, float* grad_log_alpha,
+                         float* grad_eta, float* grad_init_state, int B, int T, int H, int dk, int dv,
+                         int chunk, hipStream_t stream);
+
+/*
  * Host-only planning query: which path and segment count kla_chunk_fwd_ex would
  * use for these sizes and input dtype, and the workspace bytes it would allocate
  * (the per-chunk record is smaller for bf16 with dk <= 128). `num_cus` is the

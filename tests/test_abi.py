@@ -27,7 +27,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_loglinear_decode_step",
-              "kla_loglinear_fwd",
+              "kla_loglinear_fwd", "kla_chunk_bwd",
               "kla_decode_step", "kla_decode_step_ex",
               "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
               "kla_timing_enable", "kla_timing_collect", "kla_timing_select"):
@@ -199,3 +199,23 @@ def test_plan_workspace_bytes(dtype, dk, rec_bytes):
     starts = 2 * 5 * dk * 64 * 4
     up = lambda x: (x + 255) // 256 * 256
     assert w == up(rec) + up(maps) + up(starts)
+
+
+def _bwd(lib, dtype=0, beta=0, q=FAKE, dout=FAKE, gq=FAKE, ginit=None, B=1, T=64, H=1, dk=64, dv=64, chunk=64):
+    return lib.kla_chunk_bwd(dtype, beta, q, FAKE, FAKE, FAKE, FAKE, 1e-6, None, dout, None, gq, FAKE, FAKE, FAKE,
+                             FAKE, ginit, B, T, H, dk, dv, chunk, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(dout=None), 1), (dict(gq=None), 1), (dict(dtype=7), 1), (dict(beta=4), 1),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(dk=256), 2), (dict(dk=96), 2), (dict(dv=32), 2), (dict(chunk=128), 2),
+])
+def test_bwd_validation(kw, status):
+    lib = kla.load()
+    assert _bwd(lib, **kw) == status
+    assert kla.last_error() != ""
+
+
+def test_bwd_zero_tokens_without_start_gradient_is_a_no_op():
+    lib = kla.load()
+    assert _bwd(lib, q=None, dout=None, gq=None, T=0) == 0

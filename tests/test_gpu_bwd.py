@@ -1,0 +1,115 @@
+"""GPU parity of the chunkwise backward (kla_chunk_bwd) against the gradient oracle
+(oracle/kla_bwd.py: reverse mode through the token loop, pinned by finite differences).
+
+Every gradient (dq, dk, dv, dlog_alpha, deta and the start state's) is compared element by
+element with the oracle run in float64 on the same (bf16-exact or fp32) inputs. Bar: the
+kernels compute in fp32 on exact inputs, so the forward's fp32 bar holds for every gradient:
+max|err| <= 1e-4 * RMS(ref) per gradient and head.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import kla_bwd
+from tests.gpu_common import err_over_rms, upload, upload_prefill
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import delta_rule_recurrence_kla_amd as kla  # noqa: E402
+
+BAR = 1e-4
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "deta")
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(wl, heads=None, beta_mode="kaczmarz", with_init=True, with_dfin=True, bar=BAR, seed=0):
+    B, T, H = wl.q.shape[:3]
+    dk, dv = wl.q.shape[-1], wl.v.shape[-1]
+    d_out, d_fin = W.make_bwd_grads(B, T, H, dk, dv, seed=seed)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    if not with_init:
+        s0 = None
+    g = kla.chunk_bwd(q, k, v, la, eta, upload(d_out, "f32"), eps=wl.eps, init_state=s0,
+                      grad_final_state=upload(d_fin, "f32") if with_dfin else None, beta_mode=beta_mode)
+    torch.cuda.synchronize()
+    got = {n: t.cpu().numpy() for n, t in g.items() if t is not None}
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    worst = {}
+    for b, h in heads:
+        f = lambda a: np.asarray(a[b, :, h], np.float64)
+        S0 = None if (not with_init or wl.init_state is None) else wl.init_state[b, h]
+        ref = kla_bwd.backward(f(wl.q), f(wl.k), f(wl.v), f(wl.log_alpha), f(wl.eta), wl.eps, f(d_out),
+                               d_fin[b, h] if with_dfin else None, S0, beta_mode)
+        for n in NAMES:
+            e = err_over_rms(got[n][b, :, h], ref[n])
+            worst[n] = max(worst.get(n, 0.0), e)
+            assert np.all(np.isfinite(got[n][b, :, h])), f"{n} head {(b, h)}: non-finite"
+            assert e <= bar, f"{n} head {(b, h)}: max|err|/RMS = {e:.3e} > {bar:.1e}"
+        e = err_over_rms(got["dinit_state"][b, h], ref["dS0"])
+        worst["dS0"] = max(worst.get("dS0", 0.0), e)
+        assert e <= bar, f"dS0 head {(b, h)}: max|err|/RMS = {e:.3e} > {bar:.1e}"
+    log("worst max|err|/RMS: " + ", ".join(f"{n} {e:.2e}" for n, e in worst.items()))
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_bwd_several_chunks_ragged_tail(dtype, dk, dv):
+    log(f"case: bwd dtype={dtype} dk={dk} dv={dv} T=200")
+    wl = W.make_prefill("tiny_f32", seed=1, B=1, T=200, H=2, dk=dk, dv=dv, dtype=dtype, init_std=0.3)
+    _run(wl)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 128])
+def test_bwd_chunk_edges(T):
+    log(f"case: bwd edges T={T}")
+    wl = W.make_prefill("tiny_f32", seed=2, B=2, T=T, H=1, init_std=0.3)
+    _run(wl)
+
+
+def test_bwd_without_start_state_or_end_gradient():
+    log("case: bwd no init, no dS_T")
+    wl = W.make_prefill("tiny_f32", seed=3, T=150)
+    _run(wl, with_init=False, with_dfin=False)
+
+
+def test_bwd_direct_write_strength():
+    log("case: bwd direct mode")
+    wl = W.make_prefill("tiny_f32", seed=4, T=190, recipe="l2norm", init_std=0.3)
+    _run(wl, beta_mode="direct")
+
+
+def test_bwd_growth_gates():
+    """log_alpha > 0 in places (e^{g_r - g_i} > 1 inside a chunk)."""
+    log("case: bwd growth gates")
+    wl = W.make_prefill("tiny_f32", seed=5, T=160, init_std=0.3)
+    wl.log_alpha[:] = np.random.default_rng(5).uniform(-0.05, 0.04, wl.log_alpha.shape).astype(np.float32)
+    _run(wl)
+
+
+def test_bwd_zero_tokens_passes_the_end_gradient_through():
+    log("case: bwd T=0")
+    B, H, dk, dv = 2, 3, 64, 64
+    _, d_fin = W.make_bwd_grads(B, 0, H, dk, dv, seed=6)
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+    q = torch.empty((B, 0, H, dk), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((B, 0, H, dv), dtype=torch.bfloat16, device="cuda")
+    g = kla.chunk_bwd(q, q, v, e(B, 0, H), e(B, 0, H), e(B, 0, H, dv), grad_final_state=upload(d_fin, "f32"))
+    np.testing.assert_array_equal(g["dinit_state"].cpu().numpy(), d_fin)
+
+
+def test_bwd_lm_layer_full_size_sampled_heads():
+    """B=8, T=4096, H=16, dk=dv=128 in bf16: the whole call, two heads checked in full."""
+    log("case: bwd lm_layer_4k full size, heads (0,0) and (7,15)")
+    wl = W.make_prefill("lm_layer_4k", seed=0, init_std=0.3)
+    _run(wl, heads=[(0, 0), (7, 15)])

@@ -298,3 +298,14 @@ def make_loglinear_states(N: int = 256, H: int = 16, levels: int = 16, dk: int =
     [N, H, levels, dk, dv] (slots of levels that are empty at the start position are never read)."""
     rng = np.random.default_rng([seed, 2])
     return (np.float32(std) * rng.standard_normal((N, H, levels, dk, dv), dtype=np.float32)).astype(np.float32)
+
+
+def make_bwd_grads(B: int, T: int, H: int, dk: int, dv: int, seed: int = 0, std: float = 1.0):
+    """Upstream gradients for the prefill backward: d loss / d out ~ N(0, std) float32
+    [B, T, H, dv] and d loss / d final state ~ N(0, std) float32 [B, H, dk, dv], from their own
+    stream (the forward inputs of the same seed are unchanged)."""
+    rng = np.random.default_rng([seed, 3])
+    f = np.float32
+    d_out = (f(std) * rng.standard_normal((B, T, H, dv), dtype=f)).astype(f)
+    d_fin = (f(std) * rng.standard_normal((B, H, dk, dv), dtype=f)).astype(f)
+    return d_out, d_fin
