@@ -15,7 +15,7 @@
 //   grads    per chunk, from S0 and dS1: dq, dk, dv, dlog_alpha, deta (the chunk-local
 //            products of the reverse pass, then a reverse cumulative sum of dg inside the chunk)
 // The columns of the state (the dv index) are independent in both walks, so a walk
-// workgroup owns 16 columns. A ragged last chunk is padded with identity steps
+// workgroup owns 16 columns. Walk and grads workgroups have 512 threads, 8 per chunk row. A ragged last chunk is padded with identity steps
 // (k = q = v = 0, log_alpha = 0, eta = 0), which changes neither outputs nor gradients.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,7 +26,9 @@ namespace kla {
 namespace {
 
 constexpr int BC = 64;    // chunk length
-constexpr int BT = 256;   // threads per workgroup
+constexpr int BT = 256;   // threads of a prep workgroup
+constexpr int NT = 512;   // threads of a walk or grads workgroup: 8 per chunk row
+constexpr int TPRW = NT / 64, CPT = 16 / TPRW, IPT = 64 / TPRW;  // per row: threads, columns, row entries
 constexpr int MP = 65;    // LDS pitch of 64 x 64 matrices
 constexpr int NJ = 16;    // state columns per walk workgroup / per grads column block
 constexpr int NJP = NJ + 1;
@@ -47,7 +49,7 @@ __device__ __forceinline__ size_t tok(int b, int t, int T, int H, int h) {
 // Loads rows of a [B,T,H,D] input for the 64 tokens of chunk c into s[64][D + 1] (zeros past T).
 template <int MODE, int D>
 __device__ __forceinline__ void load_rows(float (*s)[D + 1], const void* x, int b, int h, int c, int T, int H) {
-  for (int e = threadIdx.x; e < BC * D; e += BT) {
+  for (int e = threadIdx.x; e < BC * D; e += blockDim.x) {
     const int r = e / D, d = e % D, t = c * BC + r;
     s[r][d] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * D + d) : 0.f;
   }
@@ -56,7 +58,7 @@ __device__ __forceinline__ void load_rows(float (*s)[D + 1], const void* x, int 
 // Columns jb .. jb+15 of a [B,T,H,DV] fp32 or input array for chunk c into s[64][NJP].
 template <int MODE>
 __device__ __forceinline__ void load_cols(float* s, const void* x, int b, int h, int c, int T, int H, int DV, int jb) {
-  for (int e = threadIdx.x; e < BC * NJ; e += BT) {
+  for (int e = threadIdx.x; e < BC * NJ; e += blockDim.x) {
     const int r = e / NJ, j = e % NJ, t = c * BC + r;
     s[r * NJP + j] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * DV + jb + j) : 0.f;
   }
@@ -66,9 +68,10 @@ template <int MODE, int DK>
 __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void* k, const float* log_alpha,
                                                       const float* eta, float eps, int direct, int T, int H, int nc,
                                                       float* rec) {
+  constexpr int AP = 68;  // pitch of A: 16-byte rows for vector reads
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1];
-  __shared__ float sA[BC][MP], sM[BC][MP];
+  __shared__ __align__(16) float sA[BC * AP];
   __shared__ float sla[BC], sg[BC], sb[BC];
   load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
   load_rows<MODE, DK>(sK, k, b, h, c, T, H);
@@ -91,50 +94,74 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
     R[REC_D + tid] = den;
   }
   __syncthreads();
-  // lower triangle incl. the diagonal: P = Dl . Q K^T; strict upper: K K^T (symmetric, so
-  // entry [r][i], i > r, is also G[i][r]); A = strict lower beta_r Dl G
-  for (int e = tid; e < BC * BC; e += BT) {
-    const int r = e / BC, i = e % BC;
-    float qk = 0.f, kk = 0.f;
+  // Q K^T and K K^T in 4 x 4 tiles (rows r0 + 4a, columns i0 + 4b... strided by 16 so that a
+  // wave's reads of K rows spread over banks). Lower triangle incl. the diagonal: P = Dl . Q K^T;
+  // strict upper: K K^T (symmetric, so entry [r][i], i > r, is also G[i][r]);
+  // A = strict lower beta_r Dl G.
+  {
+    const int r0 = tid >> 4, i0 = tid & 15;
+    float qk[4][4] = {}, kk[4][4] = {};
     for (int d = 0; d < DK; ++d) {
-      qk = fmaf(sQ[r][d], sK[i][d], qk);
-      kk = fmaf(sK[r][d], sK[i][d], kk);
+      float qa[4], ka[4], kb[4];
+      for (int a = 0; a < 4; ++a) {
+        qa[a] = sQ[r0 + 16 * a][d];
+        ka[a] = sK[r0 + 16 * a][d];
+        kb[a] = sK[i0 + 16 * a][d];
+      }
+      for (int a = 0; a < 4; ++a)
+        for (int e = 0; e < 4; ++e) {
+          qk[a][e] = fmaf(qa[a], kb[e], qk[a][e]);
+          kk[a][e] = fmaf(ka[a], kb[e], kk[a][e]);
+        }
     }
-    const float dl = i <= r ? expf(sg[r] - sg[i]) : 0.f;
-    R[REC_PG + e] = i <= r ? dl * qk : kk;
-    sA[r][i] = i < r ? sb[r] * dl * kk : 0.f;
+    for (int a = 0; a < 4; ++a)
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + 16 * a, i = i0 + 16 * e;
+        const float dl = i <= r ? expf(sg[r] - sg[i]) : 0.f;
+        R[REC_PG + r * BC + i] = i <= r ? dl * qk[a][e] : kk[a][e];
+        sA[r * AP + i] = i < r ? sb[r] * dl * kk[a][e] : 0.f;
+      }
   }
   __syncthreads();
-  // (I + A)^-1 is unit lower triangular; forward substitution, one column per thread
+  // (I + A)^-1 is unit lower triangular. Forward substitution with one column per lane held in
+  // registers: row r of the inverse is e_r - A[r][:] m over the rows already found (m[i] = 0
+  // for i above the column), and every lane reads the same A row (an LDS broadcast).
   if (tid < BC) {
     const int col = tid;
+    float m[BC];
+#pragma unroll
     for (int r = 0; r < BC; ++r) {
-      float m = r == col ? 1.f : 0.f;
-      if (r > col) {
-        float s = 0.f;
-        for (int i = col; i < r; ++i) s = fmaf(sA[r][i], sM[i][col], s);
-        m = -s;
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i + 4 <= r; i += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&sA[r * AP + i]);
+        s0 = fmaf(a4.x, m[i], s0);
+        s1 = fmaf(a4.y, m[i + 1], s1);
+        s0 = fmaf(a4.z, m[i + 2], s0);
+        s1 = fmaf(a4.w, m[i + 3], s1);
       }
-      sM[r][col] = m;
+#pragma unroll
+      for (int i = r & ~3; i < r; ++i) s0 = fmaf(sA[r * AP + i], m[i], s0);
+      m[r] = r == col ? 1.f : -(s0 + s1);
     }
+#pragma unroll
+    for (int r = 0; r < BC; ++r) R[REC_M + r * BC + col] = m[r];
   }
-  __syncthreads();
-  for (int e = tid; e < BC * BC; e += BT) R[REC_M + e] = sM[e / BC][e % BC];
 }
 
 // Forward walk over the chunks of one (b, h) for state columns jb .. jb+15; stores every
 // chunk-start state S0 into states[bh][c][DK][DV].
 template <int MODE, int DK>
-__global__ __launch_bounds__(BT) void bwd_states_kernel(const void* k, const void* v, const float* rec,
+__global__ __launch_bounds__(NT) void bwd_states_kernel(const void* k, const void* v, const float* rec,
                                                         const float* init, int T, int H, int DV, int nc,
                                                         float* states) {
-  constexpr int EPT = DK * NJ / BT, TPR = NJ / EPT;
+  constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT;
   const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   __shared__ float sK[BC][DK + 1], sM[BC][MP];
   __shared__ float sS[DK][NJP], sX[BC * NJP], sU[BC][NJP];
   __shared__ float sg[BC], sb[BC];
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;  // state elements owned
-  const int r = tid >> 2, j0 = (tid & 3) * 4;         // 64 x 16 chunk elements owned
+  const int r = tid / TPRW, j0 = (tid % TPRW) * CPT;         // 64 x 16 chunk elements owned
   float s[EPT];
   for (int e = 0; e < EPT; ++e)
     s[e] = init ? init[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
@@ -147,7 +174,7 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(const void* k, const voi
     }
     load_rows<MODE, DK>(sK, k, b, h, c, T, H);
     load_cols<MODE>(sX, v, b, h, c, T, H, DV, jb);
-    for (int e = tid; e < BC * BC; e += BT) sM[e / BC][e % BC] = R[REC_M + e];
+    for (int e = tid; e < BC * BC; e += NT) sM[e / BC][e % BC] = R[REC_M + e];
     if (tid < BC) {
       sg[tid] = R[REC_G + tid];
       sb[tid] = R[REC_B + tid];
@@ -155,18 +182,18 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(const void* k, const voi
     __syncthreads();
     // beta . X with X = V - e^g . (K S0)
     const float egr = expf(sg[r]);
-    float x[4];
-    for (int jj = 0; jj < 4; ++jj) {
+    float x[CPT];
+    for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
       for (int d = 0; d < DK; ++d) a = fmaf(sK[r][d], sS[d][j0 + jj], a);
       x[jj] = sb[r] * (sX[r * NJP + j0 + jj] - egr * a);
     }
-    for (int jj = 0; jj < 4; ++jj) sX[r * NJP + j0 + jj] = x[jj];
+    for (int jj = 0; jj < CPT; ++jj) sX[r * NJP + j0 + jj] = x[jj];
     __syncthreads();
     // w . U with U = Minv (beta . X)
     const float gC = sg[BC - 1];
     const float wr = expf(gC - sg[r]);
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
       for (int i = 0; i <= r; ++i) a = fmaf(sM[r][i], sX[i * NJP + j0 + jj], a);
       sU[r][j0 + jj] = wr * a;
@@ -185,16 +212,16 @@ __global__ __launch_bounds__(BT) void bwd_states_kernel(const void* k, const voi
 // Reverse walk: every chunk-end state gradient dS1 into dstates[bh][c]; the start state's
 // gradient into dinit (if not null).
 template <int MODE, int DK>
-__global__ __launch_bounds__(BT) void bwd_dstates_kernel(const void* q, const void* k, const float* dout,
+__global__ __launch_bounds__(NT) void bwd_dstates_kernel(const void* q, const void* k, const float* dout,
                                                          const float* rec, const float* dfin, int T, int H, int DV,
                                                          int nc, float* dstates, float* dinit) {
-  constexpr int EPT = DK * NJ / BT, TPR = NJ / EPT;
+  constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT;
   const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1], sM[BC][MP], sPG[BC][MP];
   __shared__ float sS[DK][NJP], sO[BC * NJP], sU[BC][NJP], sX[BC][NJP];
   __shared__ float sg[BC], sb[BC];
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
-  const int r = tid >> 2, j0 = (tid & 3) * 4;
+  const int r = tid / TPRW, j0 = (tid % TPRW) * CPT;
   float s[EPT];
   for (int e = 0; e < EPT; ++e)
     s[e] = dfin ? dfin[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
@@ -208,7 +235,7 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(const void* q, const vo
     load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
     load_rows<MODE, DK>(sK, k, b, h, c, T, H);
     load_cols<1>(sO, dout, b, h, c, T, H, DV, jb);
-    for (int e = tid; e < BC * BC; e += BT) {
+    for (int e = tid; e < BC * BC; e += NT) {
       sM[e / BC][e % BC] = R[REC_M + e];
       sPG[e / BC][e % BC] = R[REC_PG + e];
     }
@@ -220,17 +247,20 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(const void* q, const vo
     const float gC = sg[BC - 1];
     const float wr = expf(gC - sg[r]), egr = expf(sg[r]);
     // dU = w . (K dS1) + P^T dO
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
+      #pragma unroll 8
       for (int d = 0; d < DK; ++d) a = fmaf(sK[r][d], sS[d][j0 + jj], a);
       float p = 0.f;
+      #pragma unroll 8
       for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], sO[i * NJP + j0 + jj], p);
       sU[r][j0 + jj] = fmaf(wr, a, p);
     }
     __syncthreads();
     // e^g . dX with dX = diag(beta) Minv^T dU; e^g . dO in place
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
+      #pragma unroll 8
       for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[i][j0 + jj], a);
       sX[r][j0 + jj] = egr * sb[r] * a;
       sO[r * NJP + j0 + jj] *= egr;
@@ -239,6 +269,7 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(const void* q, const vo
     const float gam = expf(gC);
     for (int e = 0; e < EPT; ++e) {
       float a = 0.f;
+      #pragma unroll 8
       for (int i = 0; i < BC; ++i) a = fmaf(sQ[i][sd], sO[i * NJP + sj + e], fmaf(-sK[i][sd], sX[i][sj + e], a));
       s[e] = fmaf(gam, s[e], a);
     }
@@ -248,19 +279,19 @@ __global__ __launch_bounds__(BT) void bwd_dstates_kernel(const void* q, const vo
     for (int e = 0; e < EPT; ++e) dinit[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] = s[e];
 }
 
+// Sum over the TPRW adjacent lanes that share a chunk row.
 __device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
+  for (int m = 1; m < TPRW; m <<= 1) x += __shfl_xor(x, m);
   return x;
 }
 
 // Per-chunk gradients from the chunk-start state S0 and the chunk-end gradient dS1.
 template <int MODE, int DK>
-__global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void* k, const void* v, const float* eta,
+__global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void* k, const void* v, const float* eta,
                                                        const float* dout, const float* rec, const float* states,
                                                        const float* dstates, int direct, int T, int H, int DV, int nc,
                                                        float* dq, float* dk, float* dv, float* dla, float* deta) {
-  constexpr int EPT = DK * NJ / BT, TPR = NJ / EPT, DQ = DK / 4;
+  constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT, DQ = DK / TPRW;
   constexpr int WCOL = 2 * DK * NJP + 5 * BC * NJP, WMAT = 2 * BC * MP;
   constexpr int WN = WCOL > WMAT ? WCOL : WMAT;
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
@@ -285,7 +316,7 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
   const float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
   load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
   load_rows<MODE, DK>(sK, k, b, h, c, T, H);
-  for (int e = tid; e < BC * BC; e += BT) {
+  for (int e = tid; e < BC * BC; e += NT) {
     sM[e / BC][e % BC] = R[REC_M + e];
     sPG[e / BC][e % BC] = R[REC_PG + e];
   }
@@ -295,10 +326,10 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
     sden[tid] = R[REC_D + tid];
   }
   if (tid == 0) sgam = 0.f;
-  const int r = tid >> 2, qd = tid & 3, j0 = qd * 4, i0 = qd * 16, d0 = qd * DQ;
+  const int r = tid / TPRW, qd = tid % TPRW, j0 = qd * CPT, i0 = qd * IPT, d0 = qd * DQ;
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
-  float accP[16], accT[16], accQ[DQ], accK[DQ];
-  for (int i = 0; i < 16; ++i) accP[i] = accT[i] = 0.f;
+  float accP[IPT], accT[IPT], accQ[DQ], accK[DQ];
+  for (int i = 0; i < IPT; ++i) accP[i] = accT[i] = 0.f;
   for (int i = 0; i < DQ; ++i) accQ[i] = accK[i] = 0.f;
   float dwp = 0.f, degp = 0.f, gamp = 0.f;
   __syncthreads();
@@ -313,8 +344,8 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
     load_cols<MODE>(cX, v, b, h, c, T, H, DV, jb);
     load_cols<1>(cO, dout, b, h, c, T, H, DV, jb);
     __syncthreads();
-    float ks[4], kd[4];
-    for (int jj = 0; jj < 4; ++jj) {
+    float ks[CPT], kd[CPT];
+    for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f, qs = 0.f, e2 = 0.f;
       for (int d = 0; d < DK; ++d) {
         a = fmaf(sK[r][d], cS[d * NJP + j0 + jj], a);
@@ -326,10 +357,10 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
       degp = fmaf(cO[r * NJP + j0 + jj], qs, degp);
     }
     for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[sd * NJP + sj + e], cD[sd * NJP + sj + e], gamp);
-    for (int jj = 0; jj < 4; ++jj) cX[r * NJP + j0 + jj] -= egr * ks[jj];  // X
+    for (int jj = 0; jj < CPT; ++jj) cX[r * NJP + j0 + jj] -= egr * ks[jj];  // X
     __syncthreads();
     // U = Minv (beta . X); dU = w . (K dS1) + P^T dO
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < CPT; ++jj) {
       float u = 0.f, p = 0.f;
       for (int i = 0; i <= r; ++i) u = fmaf(sM[r][i], sb[i] * cX[i * NJP + j0 + jj], u);
       for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], cO[i * NJP + j0 + jj], p);
@@ -339,7 +370,7 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
     }
     __syncthreads();
     // dX = diag(beta) Minv^T dU, which is also dV
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
       for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], cDU[i * NJP + j0 + jj], a);
       const float dx = sb[r] * a;
@@ -349,10 +380,10 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
       if (t < T) dv[tok(b, t, T, H, h) * DV + jb + j0 + jj] = dx;
     }
     __syncthreads();
-    // dP += dO U^T and dT' += dU X^T over these columns (16 entries of row r each)
+    // dP += dO U^T and dT' += dU X^T over these columns (IPT entries of row r each)
     for (int j = 0; j < NJ; ++j) {
       const float o = cO[r * NJP + j], du = cDU[r * NJP + j];
-      for (int ii = 0; ii < 16; ++ii) {
+      for (int ii = 0; ii < IPT; ++ii) {
         accP[ii] = fmaf(o, cU[(i0 + ii) * NJP + j], accP[ii]);
         accT[ii] = fmaf(du, cX[(i0 + ii) * NJP + j], accT[ii]);
       }
@@ -377,13 +408,13 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
     atomicAdd(&sgam, gamp);
   }
   // dQK = tril_incl(dP) . Dl;  dDl . Dl collects dP . P (and below dA . A)
-  float dd16[16];
-  for (int ii = 0; ii < 16; ++ii) {
+  float ddl[IPT];
+  for (int ii = 0; ii < IPT; ++ii) {
     const int i = i0 + ii;
     const bool low = i <= r;
     m1[r * MP + i] = low ? accP[ii] * expf(sg[r] - sg[i]) : 0.f;
     m2[r * MP + i] = accT[ii];
-    dd16[ii] = low ? accP[ii] * sPG[r][i] : 0.f;
+    ddl[ii] = low ? accP[ii] * sPG[r][i] : 0.f;
   }
   __syncthreads();
   for (int i = 0; i < BC; ++i) {
@@ -399,20 +430,20 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
     sdb[tid] = a;
   }
   // W1 = Minv^T dT' diag(beta)
-  float w1[16];
-  for (int ii = 0; ii < 16; ++ii) {
+  float w1[IPT];
+  for (int ii = 0; ii < IPT; ++ii) {
     const int i = i0 + ii;
     float a = 0.f;
     for (int j = r; j < BC; ++j) a = fmaf(sM[j][r], m2[j * MP + i], a);
     w1[ii] = a * sb[i];
   }
   __syncthreads();
-  for (int ii = 0; ii < 16; ++ii) m1[r * MP + i0 + ii] = w1[ii];
+  for (int ii = 0; ii < IPT; ++ii) m1[r * MP + i0 + ii] = w1[ii];
   __syncthreads();
   // dA = strict_lower(-W1 Minv^T); A = beta_r Dl G gives dbeta, dDl and dG
   float dbp = 0.f;
-  float dG[16];
-  for (int ii = 0; ii < 16; ++ii) {
+  float dG[IPT];
+  for (int ii = 0; ii < IPT; ++ii) {
     const int i = i0 + ii;
     dG[ii] = 0.f;
     if (i < r) {
@@ -420,18 +451,18 @@ __global__ __launch_bounds__(BT) void bwd_grads_kernel(const void* q, const void
       for (int j = 0; j <= i; ++j) a = fmaf(m1[r * MP + j], sM[i][j], a);
       const float da = -a, dl = expf(sg[r] - sg[i]), G = sPG[i][r];
       dbp = fmaf(da * dl, G, dbp);
-      dd16[ii] = fmaf(da * sb[r] * dl, G, dd16[ii]);
+      ddl[ii] = fmaf(da * sb[r] * dl, G, ddl[ii]);
       dG[ii] = da * sb[r] * dl;
     }
   }
   dbp = quad_sum(dbp);
   __syncthreads();  // m1 (W1) and m2 (dT') fully read
-  for (int ii = 0; ii < 16; ++ii) {
+  for (int ii = 0; ii < IPT; ++ii) {
     m2[r * MP + i0 + ii] = dG[ii];
-    m1[r * MP + i0 + ii] = dd16[ii];
+    m1[r * MP + i0 + ii] = ddl[ii];
   }
   float rs = 0.f;
-  for (int ii = 0; ii < 16; ++ii) rs += dd16[ii];
+  for (int ii = 0; ii < IPT; ++ii) rs += ddl[ii];
   rs = quad_sum(rs);
   if (qd == 0) {
     srow[r] = rs;
@@ -490,13 +521,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
       return launch_kernel(bwd_prep_kernel<MODE, DK>, dim3(a.nc, bh), blk, stream, a.q, a.k, a.log_alpha, a.eta, a.eps,
                            a.direct, a.T, a.H, a.nc, a.rec);
     case 1:
-      return launch_kernel(bwd_states_kernel<MODE, DK>, dim3(a.dv / NJ, bh), blk, stream, a.k, a.v, a.rec, a.init, a.T,
+      return launch_kernel(bwd_states_kernel<MODE, DK>, dim3(a.dv / NJ, bh), dim3(NT), stream, a.k, a.v, a.rec, a.init, a.T,
                            a.H, a.dv, a.nc, a.states);
     case 2:
-      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJ, bh), blk, stream, a.q, a.k, a.dout, a.rec,
+      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJ, bh), dim3(NT), stream, a.q, a.k, a.dout, a.rec,
                            a.dfin, a.T, a.H, a.dv, a.nc, a.dstates, a.ginit);
     default:
-      return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), blk, stream, a.q, a.k, a.v, a.eta, a.dout,
+      return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.k, a.v, a.eta, a.dout,
                            a.rec, a.states, a.dstates, a.direct, a.T, a.H, a.dv, a.nc, a.gq, a.gk, a.gv, a.gla,
                            a.geta);
   }
