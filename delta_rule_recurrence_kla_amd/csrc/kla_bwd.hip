@@ -55,12 +55,27 @@ __device__ __forceinline__ void load_rows(float (*s)[D + 1], const void* x, int 
   }
 }
 
-// Columns jb .. jb+15 of a [B,T,H,DV] fp32 or input array for chunk c into s[64][NJP].
-template <int MODE>
+// Columns jb .. jb+W-1 of a [B,T,H,DV] fp32 or input array for chunk c into s[64][W + 1].
+template <int MODE, int W = NJ>
 __device__ __forceinline__ void load_cols(float* s, const void* x, int b, int h, int c, int T, int H, int DV, int jb) {
-  for (int e = threadIdx.x; e < BC * NJ; e += blockDim.x) {
-    const int r = e / NJ, j = e % NJ, t = c * BC + r;
-    s[r * NJP + j] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * DV + jb + j) : 0.f;
+  for (int e = threadIdx.x; e < BC * W; e += blockDim.x) {
+    const int r = e / W, j = e % W, t = c * BC + r;
+    s[r * (W + 1) + j] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * DV + jb + j) : 0.f;
+  }
+}
+
+// Query and key rows in LDS keep the input's type: bf16 inputs stay bf16 (exact), which halves
+// their footprint.
+template <int MODE> struct LdsIn { using type = float; };
+template <> struct LdsIn<0> { using type = uint16_t; };
+__device__ __forceinline__ float lds_f(float x) { return x; }
+__device__ __forceinline__ float lds_f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+
+template <int MODE, int D, class E>
+__device__ __forceinline__ void load_rows_in(E (*s)[D + 2], const void* x, int b, int h, int c, int T, int H) {
+  for (int e = threadIdx.x; e < BC * D; e += blockDim.x) {
+    const int r = e / D, d = e % D, t = c * BC + r;
+    s[r][d] = t < T ? static_cast<const E*>(x)[tok(b, t, T, H, h) * D + d] : E(0);
   }
 }
 
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
 // Forward walk over the chunks of one (b, h) for state columns jb .. jb+15; stores every
 // chunk-start state S0 into states[bh][c][DK][DV].
 template <int MODE, int DK>
-__global__ __launch_bounds__(NT) void bwd_states_kernel(const void* k, const void* v, const float* rec,
+__global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const void* v, const float* rec,
                                                         const float* init, int T, int H, int DV, int nc,
                                                         float* states) {
   constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT;
@@ -185,6 +200,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const void* k, const voi
     float x[CPT];
     for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
+#pragma unroll 8
       for (int d = 0; d < DK; ++d) a = fmaf(sK[r][d], sS[d][j0 + jj], a);
       x[jj] = sb[r] * (sX[r * NJP + j0 + jj] - egr * a);
     }
@@ -195,6 +211,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const void* k, const voi
     const float wr = expf(gC - sg[r]);
     for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
+#pragma unroll 8
       for (int i = 0; i <= r; ++i) a = fmaf(sM[r][i], sX[i * NJP + j0 + jj], a);
       sU[r][j0 + jj] = wr * a;
     }
@@ -202,6 +219,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const void* k, const voi
     const float gam = expf(gC);
     for (int e = 0; e < EPT; ++e) {
       float a = 0.f;
+#pragma unroll 8
       for (int i = 0; i < BC; ++i) a = fmaf(sK[i][sd], sU[i][sj + e], a);
       s[e] = fmaf(gam, s[e], a);
     }
@@ -210,18 +228,22 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(const void* k, const voi
 }
 
 // Reverse walk: every chunk-end state gradient dS1 into dstates[bh][c]; the start state's
-// gradient into dinit (if not null).
+// gradient into dinit (if not null). A workgroup owns 8 state columns, and its LDS (bf16 query
+// and key rows for bf16 inputs) stays under half of the CU's, so two workgroups share a CU.
+constexpr int NJW = 8, NJWP = NJW + 1, CPW = NJW / TPRW;
 template <int MODE, int DK>
-__global__ __launch_bounds__(NT) void bwd_dstates_kernel(const void* q, const void* k, const float* dout,
-                                                         const float* rec, const float* dfin, int T, int H, int DV,
-                                                         int nc, float* dstates, float* dinit) {
-  constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT;
-  const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1], sM[BC][MP], sPG[BC][MP];
-  __shared__ float sS[DK][NJP], sO[BC * NJP], sU[BC][NJP], sX[BC][NJP];
+__global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(const void* q, const void* k, const float* dout,
+                                                            const float* rec, const float* dfin, int T, int H, int DV,
+                                                            int nc, float* dstates, float* dinit) {
+  using E = typename LdsIn<MODE>::type;
+  constexpr int EPT = DK * NJW / NT, TPR = NJW / EPT;
+  const int jb = blockIdx.x * NJW, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  __shared__ E sQ[BC][DK + 2], sK[BC][DK + 2];
+  __shared__ float sM[BC][BC], sPG[BC][BC];  // read down columns only: no padding needed
+  __shared__ float sS[DK][NJWP], sO[BC * NJWP], sU[BC][NJWP], sX[BC][NJWP];
   __shared__ float sg[BC], sb[BC];
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
-  const int r = tid / TPRW, j0 = (tid % TPRW) * CPT;
+  const int r = tid / TPRW, j0 = (tid % TPRW) * CPW;
   float s[EPT];
   for (int e = 0; e < EPT; ++e)
     s[e] = dfin ? dfin[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
@@ -232,9 +254,9 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(const void* q, const vo
       D1[sd * DV + jb + sj + e] = s[e];
       sS[sd][sj + e] = s[e];
     }
-    load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
-    load_rows<MODE, DK>(sK, k, b, h, c, T, H);
-    load_cols<1>(sO, dout, b, h, c, T, H, DV, jb);
+    load_rows_in<MODE, DK, E>(sQ, q, b, h, c, T, H);
+    load_rows_in<MODE, DK, E>(sK, k, b, h, c, T, H);
+    load_cols<1, NJW>(sO, dout, b, h, c, T, H, DV, jb);
     for (int e = tid; e < BC * BC; e += NT) {
       sM[e / BC][e % BC] = R[REC_M + e];
       sPG[e / BC][e % BC] = R[REC_PG + e];
@@ -247,30 +269,31 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(const void* q, const vo
     const float gC = sg[BC - 1];
     const float wr = expf(gC - sg[r]), egr = expf(sg[r]);
     // dU = w . (K dS1) + P^T dO
-    for (int jj = 0; jj < CPT; ++jj) {
+    for (int jj = 0; jj < CPW; ++jj) {
       float a = 0.f;
-      #pragma unroll 8
-      for (int d = 0; d < DK; ++d) a = fmaf(sK[r][d], sS[d][j0 + jj], a);
+#pragma unroll 8
+      for (int d = 0; d < DK; ++d) a = fmaf(lds_f(sK[r][d]), sS[d][j0 + jj], a);
       float p = 0.f;
-      #pragma unroll 8
-      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], sO[i * NJP + j0 + jj], p);
+#pragma unroll 8
+      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], sO[i * NJWP + j0 + jj], p);
       sU[r][j0 + jj] = fmaf(wr, a, p);
     }
     __syncthreads();
     // e^g . dX with dX = diag(beta) Minv^T dU; e^g . dO in place
-    for (int jj = 0; jj < CPT; ++jj) {
+    for (int jj = 0; jj < CPW; ++jj) {
       float a = 0.f;
-      #pragma unroll 8
+#pragma unroll 8
       for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[i][j0 + jj], a);
       sX[r][j0 + jj] = egr * sb[r] * a;
-      sO[r * NJP + j0 + jj] *= egr;
+      sO[r * NJWP + j0 + jj] *= egr;
     }
     __syncthreads();
     const float gam = expf(gC);
     for (int e = 0; e < EPT; ++e) {
       float a = 0.f;
-      #pragma unroll 8
-      for (int i = 0; i < BC; ++i) a = fmaf(sQ[i][sd], sO[i * NJP + sj + e], fmaf(-sK[i][sd], sX[i][sj + e], a));
+#pragma unroll 8
+      for (int i = 0; i < BC; ++i)
+        a = fmaf(lds_f(sQ[i][sd]), sO[i * NJWP + sj + e], fmaf(-lds_f(sK[i][sd]), sX[i][sj + e], a));
       s[e] = fmaf(gam, s[e], a);
     }
     __syncthreads();
@@ -524,7 +547,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
       return launch_kernel(bwd_states_kernel<MODE, DK>, dim3(a.dv / NJ, bh), dim3(NT), stream, a.k, a.v, a.rec, a.init, a.T,
                            a.H, a.dv, a.nc, a.states);
     case 2:
-      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJ, bh), dim3(NT), stream, a.q, a.k, a.dout, a.rec,
+      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJW, bh), dim3(NT), stream, a.q, a.k, a.dout, a.rec,
                            a.dfin, a.T, a.H, a.dv, a.nc, a.dstates, a.ginit);
     default:
       return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.k, a.v, a.eta, a.dout,
