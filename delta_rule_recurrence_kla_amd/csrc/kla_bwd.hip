@@ -315,21 +315,23 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
                                                        const float* dstates, int direct, int T, int H, int DV, int nc,
                                                        float* dq, float* dk, float* dv, float* dla, float* deta) {
   constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT, DQ = DK / TPRW;
-  constexpr int WCOL = 2 * DK * NJP + 5 * BC * NJP, WMAT = 2 * BC * MP;
+  constexpr int SP = DK + 4, RP = BC + 4;  // pitches of the column-major blocks (16-byte rows)
+  constexpr int WCOL = 2 * NJ * SP + 5 * NJ * RP, WMAT = 2 * BC * MP;
   constexpr int WN = WCOL > WMAT ? WCOL : WMAT;
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1], sM[BC][MP], sPG[BC][MP];
-  __shared__ float sW[WN];
+  __shared__ __align__(16) float sW[WN];
   __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], sdg[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
   __shared__ float sgam;
-  // column-block phase
-  float* cS = sW;             // S0 [DK][NJP]
-  float* cD = cS + DK * NJP;  // dS1 [DK][NJP]
-  float* cX = cD + DK * NJP;  // V, then X [BC][NJP]
-  float* cO = cX + BC * NJP;  // dO
-  float* cU = cO + BC * NJP;  // U
-  float* cDU = cU + BC * NJP;
-  float* cDX = cDU + BC * NJP;
+  // column-block phase: 16 columns of each operand, stored column by column so that a
+  // thread's run of rows (or of state rows) is one 16-byte read
+  float* cS = sW;             // S0 [NJ][SP]
+  float* cD = cS + NJ * SP;   // dS1 [NJ][SP]
+  float* cX = cD + NJ * SP;   // V, then X [NJ][RP]
+  float* cO = cX + NJ * RP;   // dO
+  float* cU = cO + NJ * RP;   // U
+  float* cDU = cU + NJ * RP;
+  float* cDX = cDU + NJ * RP;
   // matrix phase
   float* m1 = sW;
   float* m2 = sW + BC * MP;
@@ -361,63 +363,95 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
 
   for (int jb = 0; jb < DV; jb += NJ) {
     for (int e = 0; e < EPT; ++e) {
-      cS[sd * NJP + sj + e] = S0[sd * DV + jb + sj + e];
-      cD[sd * NJP + sj + e] = D1[sd * DV + jb + sj + e];
+      cS[(sj + e) * SP + sd] = S0[sd * DV + jb + sj + e];
+      cD[(sj + e) * SP + sd] = D1[sd * DV + jb + sj + e];
     }
-    load_cols<MODE>(cX, v, b, h, c, T, H, DV, jb);
-    load_cols<1>(cO, dout, b, h, c, T, H, DV, jb);
+    for (int e = tid; e < BC * NJ; e += NT) {
+      const int rr = e / NJ, j = e % NJ, t = c * BC + rr;
+      const size_t o = tok(b, t, T, H, h) * DV + jb + j;
+      cX[j * RP + rr] = t < T ? ldin<MODE>(v, o) : 0.f;
+      cO[j * RP + rr] = t < T ? dout[o] : 0.f;
+    }
     __syncthreads();
     float ks[CPT], kd[CPT];
     for (int jj = 0; jj < CPT; ++jj) {
+      const float* s0 = cS + (j0 + jj) * SP;
+      const float* s1 = cD + (j0 + jj) * SP;
       float a = 0.f, qs = 0.f, e2 = 0.f;
+#pragma unroll 4
       for (int d = 0; d < DK; ++d) {
-        a = fmaf(sK[r][d], cS[d * NJP + j0 + jj], a);
-        qs = fmaf(sQ[r][d], cS[d * NJP + j0 + jj], qs);
-        e2 = fmaf(sK[r][d], cD[d * NJP + j0 + jj], e2);
+        a = fmaf(sK[r][d], s0[d], a);
+        qs = fmaf(sQ[r][d], s0[d], qs);
+        e2 = fmaf(sK[r][d], s1[d], e2);
       }
       ks[jj] = a;
       kd[jj] = e2;
-      degp = fmaf(cO[r * NJP + j0 + jj], qs, degp);
+      degp = fmaf(cO[(j0 + jj) * RP + r], qs, degp);
     }
-    for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[sd * NJP + sj + e], cD[sd * NJP + sj + e], gamp);
-    for (int jj = 0; jj < CPT; ++jj) cX[r * NJP + j0 + jj] -= egr * ks[jj];  // X
+    for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[(sj + e) * SP + sd], cD[(sj + e) * SP + sd], gamp);
+    for (int jj = 0; jj < CPT; ++jj) cX[(j0 + jj) * RP + r] -= egr * ks[jj];  // X
     __syncthreads();
     // U = Minv (beta . X); dU = w . (K dS1) + P^T dO
     for (int jj = 0; jj < CPT; ++jj) {
+      const float* xc = cX + (j0 + jj) * RP;
+      const float* oc = cO + (j0 + jj) * RP;
       float u = 0.f, p = 0.f;
-      for (int i = 0; i <= r; ++i) u = fmaf(sM[r][i], sb[i] * cX[i * NJP + j0 + jj], u);
-      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], cO[i * NJP + j0 + jj], p);
-      cU[r * NJP + j0 + jj] = u;
-      cDU[r * NJP + j0 + jj] = fmaf(wr, kd[jj], p);
+#pragma unroll 4
+      for (int i = 0; i <= r; ++i) u = fmaf(sM[r][i], sb[i] * xc[i], u);
+#pragma unroll 4
+      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], oc[i], p);
+      cU[(j0 + jj) * RP + r] = u;
+      cDU[(j0 + jj) * RP + r] = fmaf(wr, kd[jj], p);
       dwp = fmaf(u, kd[jj], dwp);
     }
     __syncthreads();
     // dX = diag(beta) Minv^T dU, which is also dV
     for (int jj = 0; jj < CPT; ++jj) {
+      const float* uc = cDU + (j0 + jj) * RP;
       float a = 0.f;
-      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], cDU[i * NJP + j0 + jj], a);
+#pragma unroll 4
+      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], uc[i], a);
       const float dx = sb[r] * a;
-      cDX[r * NJP + j0 + jj] = dx;
+      cDX[(j0 + jj) * RP + r] = dx;
       degp = fmaf(-dx, ks[jj], degp);
       const int t = c * BC + r;
       if (t < T) dv[tok(b, t, T, H, h) * DV + jb + j0 + jj] = dx;
     }
     __syncthreads();
     // dP += dO U^T and dT' += dU X^T over these columns (IPT entries of row r each)
+#pragma unroll 2
     for (int j = 0; j < NJ; ++j) {
-      const float o = cO[r * NJP + j], du = cDU[r * NJP + j];
-      for (int ii = 0; ii < IPT; ++ii) {
-        accP[ii] = fmaf(o, cU[(i0 + ii) * NJP + j], accP[ii]);
-        accT[ii] = fmaf(du, cX[(i0 + ii) * NJP + j], accT[ii]);
+      const float o = cO[j * RP + r], du = cDU[j * RP + r];
+      const float4* u4 = reinterpret_cast<const float4*>(cU + j * RP + i0);
+      const float4* x4 = reinterpret_cast<const float4*>(cX + j * RP + i0);
+      for (int q4 = 0; q4 < IPT / 4; ++q4) {
+        const float4 uu = u4[q4], xx = x4[q4];
+        accP[4 * q4 + 0] = fmaf(o, uu.x, accP[4 * q4 + 0]);
+        accP[4 * q4 + 1] = fmaf(o, uu.y, accP[4 * q4 + 1]);
+        accP[4 * q4 + 2] = fmaf(o, uu.z, accP[4 * q4 + 2]);
+        accP[4 * q4 + 3] = fmaf(o, uu.w, accP[4 * q4 + 3]);
+        accT[4 * q4 + 0] = fmaf(du, xx.x, accT[4 * q4 + 0]);
+        accT[4 * q4 + 1] = fmaf(du, xx.y, accT[4 * q4 + 1]);
+        accT[4 * q4 + 2] = fmaf(du, xx.z, accT[4 * q4 + 2]);
+        accT[4 * q4 + 3] = fmaf(du, xx.w, accT[4 * q4 + 3]);
       }
     }
     // dQ += e^g . (dO S0^T);  dK += w . (U dS1^T) - e^g . (dX S0^T)
+#pragma unroll 2
     for (int j = 0; j < NJ; ++j) {
-      const float o = egr * cO[r * NJP + j], u = wr * cU[r * NJP + j], x = egr * cDX[r * NJP + j];
-      for (int dd = 0; dd < DQ; ++dd) {
-        const float s0 = cS[(d0 + dd) * NJP + j];
-        accQ[dd] = fmaf(o, s0, accQ[dd]);
-        accK[dd] = fmaf(u, cD[(d0 + dd) * NJP + j], fmaf(-x, s0, accK[dd]));
+      const float o = egr * cO[j * RP + r], u = wr * cU[j * RP + r], x = egr * cDX[j * RP + r];
+      const float4* s4 = reinterpret_cast<const float4*>(cS + j * SP + d0);
+      const float4* t4 = reinterpret_cast<const float4*>(cD + j * SP + d0);
+      for (int q4 = 0; q4 < DQ / 4; ++q4) {
+        const float4 a = s4[q4], e = t4[q4];
+        accQ[4 * q4 + 0] = fmaf(o, a.x, accQ[4 * q4 + 0]);
+        accQ[4 * q4 + 1] = fmaf(o, a.y, accQ[4 * q4 + 1]);
+        accQ[4 * q4 + 2] = fmaf(o, a.z, accQ[4 * q4 + 2]);
+        accQ[4 * q4 + 3] = fmaf(o, a.w, accQ[4 * q4 + 3]);
+        accK[4 * q4 + 0] = fmaf(u, e.x, fmaf(-x, a.x, accK[4 * q4 + 0]));
+        accK[4 * q4 + 1] = fmaf(u, e.y, fmaf(-x, a.y, accK[4 * q4 + 1]));
+        accK[4 * q4 + 2] = fmaf(u, e.z, fmaf(-x, a.z, accK[4 * q4 + 2]));
+        accK[4 * q4 + 3] = fmaf(u, e.w, fmaf(-x, a.w, accK[4 * q4 + 3]));
       }
     }
     __syncthreads();
