@@ -47,8 +47,8 @@ __device__ __forceinline__ size_t tok(int b, int t, int T, int H, int h) {
 }
 
 // Loads rows of a [B,T,H,D] input for the 64 tokens of chunk c into s[64][D + 1] (zeros past T).
-template <int MODE, int D>
-__device__ __forceinline__ void load_rows(float (*s)[D + 1], const void* x, int b, int h, int c, int T, int H) {
+template <int MODE, int D, int P = D + 1>
+__device__ __forceinline__ void load_rows(float (*s)[P], const void* x, int b, int h, int c, int T, int H) {
   for (int e = threadIdx.x; e < BC * D; e += blockDim.x) {
     const int r = e / D, d = e % D, t = c * BC + r;
     s[r][d] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * D + d) : 0.f;
@@ -319,7 +319,9 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   constexpr int WCOL = 2 * NJ * SP + 5 * NJ * RP, WMAT = 2 * BC * MP;
   constexpr int WN = WCOL > WMAT ? WCOL : WMAT;
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1], sM[BC][MP], sPG[BC][MP];
+  constexpr int QP = DK + 4;  // 16-byte rows of queries and keys
+  __shared__ __align__(16) float sQ[BC][QP], sK[BC][QP];
+  __shared__ float sM[BC][MP], sPG[BC][MP];
   __shared__ __align__(16) float sW[WN];
   __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], sdg[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
   __shared__ float sgam;
@@ -339,8 +341,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
   const float* S0 = states + (static_cast<size_t>(bh) * nc + c) * DK * DV;
   const float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
-  load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
-  load_rows<MODE, DK>(sK, k, b, h, c, T, H);
+  load_rows<MODE, DK, QP>(sQ, q, b, h, c, T, H);
+  load_rows<MODE, DK, QP>(sK, k, b, h, c, T, H);
   for (int e = tid; e < BC * BC; e += NT) {
     sM[e / BC][e % BC] = R[REC_M + e];
     sPG[e / BC][e % BC] = R[REC_PG + e];
@@ -375,14 +377,17 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     __syncthreads();
     float ks[CPT], kd[CPT];
     for (int jj = 0; jj < CPT; ++jj) {
-      const float* s0 = cS + (j0 + jj) * SP;
-      const float* s1 = cD + (j0 + jj) * SP;
+      const float4* s0 = reinterpret_cast<const float4*>(cS + (j0 + jj) * SP);
+      const float4* s1 = reinterpret_cast<const float4*>(cD + (j0 + jj) * SP);
+      const float4* kr = reinterpret_cast<const float4*>(&sK[r][0]);
+      const float4* qr = reinterpret_cast<const float4*>(&sQ[r][0]);
       float a = 0.f, qs = 0.f, e2 = 0.f;
-#pragma unroll 4
-      for (int d = 0; d < DK; ++d) {
-        a = fmaf(sK[r][d], s0[d], a);
-        qs = fmaf(sQ[r][d], s0[d], qs);
-        e2 = fmaf(sK[r][d], s1[d], e2);
+#pragma unroll 2
+      for (int d4 = 0; d4 < DK / 4; ++d4) {
+        const float4 kk = kr[d4], qq = qr[d4], x0 = s0[d4], x1 = s1[d4];
+        a = fmaf(kk.x, x0.x, fmaf(kk.y, x0.y, fmaf(kk.z, x0.z, fmaf(kk.w, x0.w, a))));
+        qs = fmaf(qq.x, x0.x, fmaf(qq.y, x0.y, fmaf(qq.z, x0.z, fmaf(qq.w, x0.w, qs))));
+        e2 = fmaf(kk.x, x1.x, fmaf(kk.y, x1.y, fmaf(kk.z, x1.z, fmaf(kk.w, x1.w, e2))));
       }
       ks[jj] = a;
       kd[jj] = e2;
@@ -476,9 +481,18 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __syncthreads();
   for (int i = 0; i < BC; ++i) {
     const float a = m1[r * MP + i], at = m1[i * MP + r];
-    for (int dd = 0; dd < DQ; ++dd) {
-      accQ[dd] = fmaf(a, sK[i][d0 + dd], accQ[dd]);
-      accK[dd] = fmaf(at, sQ[i][d0 + dd], accK[dd]);
+    const float4* ki = reinterpret_cast<const float4*>(&sK[i][d0]);
+    const float4* qi = reinterpret_cast<const float4*>(&sQ[i][d0]);
+    for (int q4 = 0; q4 < DQ / 4; ++q4) {
+      const float4 kk = ki[q4], qq = qi[q4];
+      accQ[4 * q4 + 0] = fmaf(a, kk.x, accQ[4 * q4 + 0]);
+      accQ[4 * q4 + 1] = fmaf(a, kk.y, accQ[4 * q4 + 1]);
+      accQ[4 * q4 + 2] = fmaf(a, kk.z, accQ[4 * q4 + 2]);
+      accQ[4 * q4 + 3] = fmaf(a, kk.w, accQ[4 * q4 + 3]);
+      accK[4 * q4 + 0] = fmaf(at, qq.x, accK[4 * q4 + 0]);
+      accK[4 * q4 + 1] = fmaf(at, qq.y, accK[4 * q4 + 1]);
+      accK[4 * q4 + 2] = fmaf(at, qq.z, accK[4 * q4 + 2]);
+      accK[4 * q4 + 3] = fmaf(at, qq.w, accK[4 * q4 + 3]);
     }
   }
   if (tid < BC) {  // dbeta from T' = Minv diag(beta): column sums of Minv . dT'
@@ -529,7 +543,14 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   // dK += (dG + dG^T) K
   for (int i = 0; i < BC; ++i) {
     const float a = m2[r * MP + i] + m2[i * MP + r];
-    for (int dd = 0; dd < DQ; ++dd) accK[dd] = fmaf(a, sK[i][d0 + dd], accK[dd]);
+    const float4* ki = reinterpret_cast<const float4*>(&sK[i][d0]);
+    for (int q4 = 0; q4 < DQ / 4; ++q4) {
+      const float4 kk = ki[q4];
+      accK[4 * q4 + 0] = fmaf(a, kk.x, accK[4 * q4 + 0]);
+      accK[4 * q4 + 1] = fmaf(a, kk.y, accK[4 * q4 + 1]);
+      accK[4 * q4 + 2] = fmaf(a, kk.z, accK[4 * q4 + 2]);
+      accK[4 * q4 + 3] = fmaf(a, kk.w, accK[4 * q4 + 3]);
+    }
   }
   if (tid < BC) {
     const int i = tid, t = c * BC + i;
