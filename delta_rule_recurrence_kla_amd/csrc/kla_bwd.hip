@@ -71,8 +71,23 @@ template <> struct LdsIn<0> { using type = uint16_t; };
 __device__ __forceinline__ float lds_f(float x) { return x; }
 __device__ __forceinline__ float lds_f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
 
-template <int MODE, int D, class E>
-__device__ __forceinline__ void load_rows_in(E (*s)[D + 2], const void* x, int b, int h, int c, int T, int H) {
+// Eight consecutive row elements from a 16-byte aligned LDS address, as fp32.
+__device__ __forceinline__ void row8(const uint16_t* p, float f[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void row8(const float* p, float f[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+template <int MODE, int D, int P, class E>
+__device__ __forceinline__ void load_rows_in(E (*s)[P], const void* x, int b, int h, int c, int T, int H) {
   for (int e = threadIdx.x; e < BC * D; e += blockDim.x) {
     const int r = e / D, d = e % D, t = c * BC + r;
     s[r][d] = t < T ? static_cast<const E*>(x)[tok(b, t, T, H, h) * D + d] : E(0);
@@ -230,20 +245,26 @@ __global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const 
 // Reverse walk: every chunk-end state gradient dS1 into dstates[bh][c]; the start state's
 // gradient into dinit (if not null). A workgroup owns 8 state columns, and its LDS (bf16 query
 // and key rows for bf16 inputs) stays under half of the CU's, so two workgroups share a CU.
-constexpr int NJW = 8, NJWP = NJW + 1, CPW = NJW / TPRW;
+constexpr int NJW = 8, CPW = NJW / TPRW;
 template <int MODE, int DK>
 __global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(const void* q, const void* k, const float* dout,
                                                             const float* rec, const float* dfin, int T, int H, int DV,
                                                             int nc, float* dstates, float* dinit) {
   using E = typename LdsIn<MODE>::type;
+  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows of queries and keys
+  constexpr int SP = DK + 4, RP = BC + 4;         // column-major blocks: state columns, chunk columns
   constexpr int EPT = DK * NJW / NT, TPR = NJW / EPT;
   const int jb = blockIdx.x * NJW, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ E sQ[BC][DK + 2], sK[BC][DK + 2];
+  __shared__ __align__(16) E sQ[BC][EP];
+  __shared__ __align__(16) E sK[BC][EP];
   __shared__ float sM[BC][BC], sPG[BC][BC];  // read down columns only: no padding needed
-  __shared__ float sS[DK][NJWP], sO[BC * NJWP], sU[BC][NJWP], sX[BC][NJWP];
+  __shared__ __align__(16) float sS[NJW][SP];
+  __shared__ __align__(16) float sO[NJW][RP];
+  __shared__ __align__(16) float sU[NJW][RP];
+  __shared__ __align__(16) float sX[NJW][RP];
   __shared__ float sg[BC], sb[BC];
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
-  const int r = tid / TPRW, j0 = (tid % TPRW) * CPW;
+  const int r = tid / TPRW, j = (tid % TPRW) * CPW;  // CPW == 1: one chunk column per thread
   float s[EPT];
   for (int e = 0; e < EPT; ++e)
     s[e] = dfin ? dfin[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
@@ -252,11 +273,14 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(cons
     float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
     for (int e = 0; e < EPT; ++e) {
       D1[sd * DV + jb + sj + e] = s[e];
-      sS[sd][sj + e] = s[e];
+      sS[sj + e][sd] = s[e];
     }
-    load_rows_in<MODE, DK, E>(sQ, q, b, h, c, T, H);
-    load_rows_in<MODE, DK, E>(sK, k, b, h, c, T, H);
-    load_cols<1, NJW>(sO, dout, b, h, c, T, H, DV, jb);
+    load_rows_in<MODE, DK, EP, E>(sQ, q, b, h, c, T, H);
+    load_rows_in<MODE, DK, EP, E>(sK, k, b, h, c, T, H);
+    for (int e = tid; e < BC * NJW; e += NT) {
+      const int rr = e / NJW, jj = e % NJW, t = c * BC + rr;
+      sO[jj][rr] = t < T ? dout[tok(b, t, T, H, h) * DV + jb + jj] : 0.f;
+    }
     for (int e = tid; e < BC * BC; e += NT) {
       sM[e / BC][e % BC] = R[REC_M + e];
       sPG[e / BC][e % BC] = R[REC_PG + e];
@@ -269,31 +293,44 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(cons
     const float gC = sg[BC - 1];
     const float wr = expf(gC - sg[r]), egr = expf(sg[r]);
     // dU = w . (K dS1) + P^T dO
-    for (int jj = 0; jj < CPW; ++jj) {
+    {
       float a = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < DK; ++d) a = fmaf(lds_f(sK[r][d]), sS[d][j0 + jj], a);
+#pragma unroll 2
+      for (int d = 0; d < DK; d += 8) {
+        float kf[8], sf[8];
+        row8(&sK[r][d], kf);
+        row8(&sS[j][d], sf);
+        for (int x = 0; x < 8; ++x) a = fmaf(kf[x], sf[x], a);
+      }
       float p = 0.f;
 #pragma unroll 8
-      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], sO[i * NJWP + j0 + jj], p);
-      sU[r][j0 + jj] = fmaf(wr, a, p);
+      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], sO[j][i], p);
+      sU[j][r] = fmaf(wr, a, p);
     }
     __syncthreads();
     // e^g . dX with dX = diag(beta) Minv^T dU; e^g . dO in place
-    for (int jj = 0; jj < CPW; ++jj) {
+    {
       float a = 0.f;
 #pragma unroll 8
-      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[i][j0 + jj], a);
-      sX[r][j0 + jj] = egr * sb[r] * a;
-      sO[r * NJWP + j0 + jj] *= egr;
+      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[j][i], a);
+      sX[j][r] = egr * sb[r] * a;
+      sO[j][r] *= egr;
     }
     __syncthreads();
     const float gam = expf(gC);
     for (int e = 0; e < EPT; ++e) {
+      const float4* o4 = reinterpret_cast<const float4*>(&sO[sj + e][0]);
+      const float4* x4 = reinterpret_cast<const float4*>(&sX[sj + e][0]);
       float a = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < BC; ++i)
-        a = fmaf(lds_f(sQ[i][sd]), sO[i * NJWP + sj + e], fmaf(-lds_f(sK[i][sd]), sX[i][sj + e], a));
+#pragma unroll 4
+      for (int i4 = 0; i4 < BC / 4; ++i4) {
+        const float4 oo = o4[i4], xx = x4[i4];
+        const int i = 4 * i4;
+        a = fmaf(lds_f(sQ[i][sd]), oo.x, fmaf(-lds_f(sK[i][sd]), xx.x, a));
+        a = fmaf(lds_f(sQ[i + 1][sd]), oo.y, fmaf(-lds_f(sK[i + 1][sd]), xx.y, a));
+        a = fmaf(lds_f(sQ[i + 2][sd]), oo.z, fmaf(-lds_f(sK[i + 2][sd]), xx.z, a));
+        a = fmaf(lds_f(sQ[i + 3][sd]), oo.w, fmaf(-lds_f(sK[i + 3][sd]), xx.w, a));
+      }
       s[e] = fmaf(gam, s[e], a);
     }
     __syncthreads();
