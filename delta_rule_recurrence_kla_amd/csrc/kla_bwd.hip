@@ -339,6 +339,14 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(cons
     for (int e = 0; e < EPT; ++e) dinit[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] = s[e];
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// One fp32 MFMA step (16 x 16 tile, K = 4, full fp32 products): lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16]; the tile's rows 4 (l / 16) + i, column l % 16, sit in lane l's acc[i].
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
 // Sum over the TPRW adjacent lanes that share a chunk row.
 __device__ __forceinline__ float quad_sum(float x) {
   for (int m = 1; m < TPRW; m <<= 1) x += __shfl_xor(x, m);
@@ -361,6 +369,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __shared__ float sM[BC][MP], sPG[BC][MP];
   __shared__ __align__(16) float sW[WN];
   __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], sdg[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
+  __shared__ float seg[BC], sww[BC];  // e^{g}, e^{g_C - g}
   __shared__ float sgam;
   // column-block phase: 16 columns of each operand, stored column by column so that a
   // thread's run of rows (or of state rows) is one 16-byte read
@@ -392,43 +401,87 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   if (tid == 0) sgam = 0.f;
   const int r = tid / TPRW, qd = tid % TPRW, j0 = qd * CPT, i0 = qd * IPT, d0 = qd * DQ;
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
-  float accP[IPT], accT[IPT], accQ[DQ], accK[DQ];
-  for (int i = 0; i < IPT; ++i) accP[i] = accT[i] = 0.f;
+  // Rank-16 updates on the fp32 MFMA: wave w owns row tile mt of the chunk and column tiles
+  // nt = w / 4 + 2u of dP, dT' (64 x 64) and of dQ, dK (64 x DK).
+  constexpr int NTW = DK / 32;
+  const int lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15, mt = wv & 3, nt0 = wv >> 2;
+  v4f mP[2], mT[2], mQ[NTW], mK[NTW];
+  for (int u = 0; u < 2; ++u) mP[u] = mT[u] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NTW; ++u) mQ[u] = mK[u] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the products after the column blocks accumulate in the row layout
+  float accQ[DQ], accK[DQ];
   for (int i = 0; i < DQ; ++i) accQ[i] = accK[i] = 0.f;
   float dwp = 0.f, degp = 0.f, gamp = 0.f;
   __syncthreads();
   const float gC = sg[BC - 1];
   const float egr = expf(sg[r]), wr = expf(gC - sg[r]);
+  if (tid < BC) {
+    seg[tid] = expf(sg[tid]);
+    sww[tid] = expf(gC - sg[tid]);
+  }
 
+  // the next column block's S0, dS1, V and dO are loaded into registers while this one is
+  // computed
+  constexpr int VPT = BC * NJ / NT;
+  float pS[EPT], pD[EPT], pV[VPT], pO[VPT];
+  auto fetch = [&](int jb) {
+    for (int e = 0; e < EPT; ++e) {
+      pS[e] = S0[sd * DV + jb + sj + e];
+      pD[e] = D1[sd * DV + jb + sj + e];
+    }
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * NT, rr = e / NJ, j = e % NJ, t = c * BC + rr;
+      const size_t o = tok(b, t, T, H, h) * DV + jb + j;
+      pV[x] = t < T ? ldin<MODE>(v, o) : 0.f;
+      pO[x] = t < T ? dout[o] : 0.f;
+    }
+  };
+  fetch(0);
   for (int jb = 0; jb < DV; jb += NJ) {
     for (int e = 0; e < EPT; ++e) {
-      cS[(sj + e) * SP + sd] = S0[sd * DV + jb + sj + e];
-      cD[(sj + e) * SP + sd] = D1[sd * DV + jb + sj + e];
+      cS[(sj + e) * SP + sd] = pS[e];
+      cD[(sj + e) * SP + sd] = pD[e];
     }
-    for (int e = tid; e < BC * NJ; e += NT) {
-      const int rr = e / NJ, j = e % NJ, t = c * BC + rr;
-      const size_t o = tok(b, t, T, H, h) * DV + jb + j;
-      cX[j * RP + rr] = t < T ? ldin<MODE>(v, o) : 0.f;
-      cO[j * RP + rr] = t < T ? dout[o] : 0.f;
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * NT, rr = e / NJ, j = e % NJ;
+      cX[j * RP + rr] = pV[x];
+      cO[j * RP + rr] = pO[x];
+    }
+    if (jb + NJ < DV) fetch(jb + NJ);
+    __syncthreads();
+    // K S0, K dS1 (waves 0-3) and Q S0 (waves 4-7) for row tile mt on the fp32 MFMA, parked in
+    // the U, dU and dX blocks, which this column block has not written yet
+    {
+      const int row = 16 * mt + ln;
+      if (wv < 4) {
+        v4f aks = {0.f, 0.f, 0.f, 0.f}, akd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int kk = 0; kk < DK / 4; ++kk) {
+          const int d = 4 * kk + gq;
+          const float a = sK[row][d];
+          aks = mfma4(a, cS[ln * SP + d], aks);
+          akd = mfma4(a, cD[ln * SP + d], akd);
+        }
+        for (int e = 0; e < 4; ++e) {
+          cU[ln * RP + 16 * mt + 4 * gq + e] = aks[e];
+          cDU[ln * RP + 16 * mt + 4 * gq + e] = akd[e];
+        }
+      } else {
+        v4f aqs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int kk = 0; kk < DK / 4; ++kk) {
+          const int d = 4 * kk + gq;
+          aqs = mfma4(sQ[row][d], cS[ln * SP + d], aqs);
+        }
+        for (int e = 0; e < 4; ++e) cDX[ln * RP + 16 * mt + 4 * gq + e] = aqs[e];
+      }
     }
     __syncthreads();
     float ks[CPT], kd[CPT];
     for (int jj = 0; jj < CPT; ++jj) {
-      const float4* s0 = reinterpret_cast<const float4*>(cS + (j0 + jj) * SP);
-      const float4* s1 = reinterpret_cast<const float4*>(cD + (j0 + jj) * SP);
-      const float4* kr = reinterpret_cast<const float4*>(&sK[r][0]);
-      const float4* qr = reinterpret_cast<const float4*>(&sQ[r][0]);
-      float a = 0.f, qs = 0.f, e2 = 0.f;
-#pragma unroll 2
-      for (int d4 = 0; d4 < DK / 4; ++d4) {
-        const float4 kk = kr[d4], qq = qr[d4], x0 = s0[d4], x1 = s1[d4];
-        a = fmaf(kk.x, x0.x, fmaf(kk.y, x0.y, fmaf(kk.z, x0.z, fmaf(kk.w, x0.w, a))));
-        qs = fmaf(qq.x, x0.x, fmaf(qq.y, x0.y, fmaf(qq.z, x0.z, fmaf(qq.w, x0.w, qs))));
-        e2 = fmaf(kk.x, x1.x, fmaf(kk.y, x1.y, fmaf(kk.z, x1.z, fmaf(kk.w, x1.w, e2))));
-      }
-      ks[jj] = a;
-      kd[jj] = e2;
-      degp = fmaf(cO[(j0 + jj) * RP + r], qs, degp);
+      ks[jj] = cU[(j0 + jj) * RP + r];
+      kd[jj] = cDU[(j0 + jj) * RP + r];
+      degp = fmaf(cO[(j0 + jj) * RP + r], cDX[(j0 + jj) * RP + r], degp);
     }
     for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[(sj + e) * SP + sd], cD[(sj + e) * SP + sd], gamp);
     for (int jj = 0; jj < CPT; ++jj) cX[(j0 + jj) * RP + r] -= egr * ks[jj];  // X
@@ -460,40 +513,28 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
       if (t < T) dv[tok(b, t, T, H, h) * DV + jb + j0 + jj] = dx;
     }
     __syncthreads();
-    // dP += dO U^T and dT' += dU X^T over these columns (IPT entries of row r each)
-#pragma unroll 2
-    for (int j = 0; j < NJ; ++j) {
-      const float o = cO[j * RP + r], du = cDU[j * RP + r];
-      const float4* u4 = reinterpret_cast<const float4*>(cU + j * RP + i0);
-      const float4* x4 = reinterpret_cast<const float4*>(cX + j * RP + i0);
-      for (int q4 = 0; q4 < IPT / 4; ++q4) {
-        const float4 uu = u4[q4], xx = x4[q4];
-        accP[4 * q4 + 0] = fmaf(o, uu.x, accP[4 * q4 + 0]);
-        accP[4 * q4 + 1] = fmaf(o, uu.y, accP[4 * q4 + 1]);
-        accP[4 * q4 + 2] = fmaf(o, uu.z, accP[4 * q4 + 2]);
-        accP[4 * q4 + 3] = fmaf(o, uu.w, accP[4 * q4 + 3]);
-        accT[4 * q4 + 0] = fmaf(du, xx.x, accT[4 * q4 + 0]);
-        accT[4 * q4 + 1] = fmaf(du, xx.y, accT[4 * q4 + 1]);
-        accT[4 * q4 + 2] = fmaf(du, xx.z, accT[4 * q4 + 2]);
-        accT[4 * q4 + 3] = fmaf(du, xx.w, accT[4 * q4 + 3]);
-      }
-    }
-    // dQ += e^g . (dO S0^T);  dK += w . (U dS1^T) - e^g . (dX S0^T)
-#pragma unroll 2
-    for (int j = 0; j < NJ; ++j) {
-      const float o = egr * cO[j * RP + r], u = wr * cU[j * RP + r], x = egr * cDX[j * RP + r];
-      const float4* s4 = reinterpret_cast<const float4*>(cS + j * SP + d0);
-      const float4* t4 = reinterpret_cast<const float4*>(cD + j * SP + d0);
-      for (int q4 = 0; q4 < DQ / 4; ++q4) {
-        const float4 a = s4[q4], e = t4[q4];
-        accQ[4 * q4 + 0] = fmaf(o, a.x, accQ[4 * q4 + 0]);
-        accQ[4 * q4 + 1] = fmaf(o, a.y, accQ[4 * q4 + 1]);
-        accQ[4 * q4 + 2] = fmaf(o, a.z, accQ[4 * q4 + 2]);
-        accQ[4 * q4 + 3] = fmaf(o, a.w, accQ[4 * q4 + 3]);
-        accK[4 * q4 + 0] = fmaf(u, e.x, fmaf(-x, a.x, accK[4 * q4 + 0]));
-        accK[4 * q4 + 1] = fmaf(u, e.y, fmaf(-x, a.y, accK[4 * q4 + 1]));
-        accK[4 * q4 + 2] = fmaf(u, e.z, fmaf(-x, a.z, accK[4 * q4 + 2]));
-        accK[4 * q4 + 3] = fmaf(u, e.w, fmaf(-x, a.w, accK[4 * q4 + 3]));
+    // dP += dO U^T, dT' += dU X^T, dQ += e^g . (dO S0^T), dK += w . (U dS1^T) - e^g . (dX S0^T)
+    {
+      const int row = 16 * mt + ln;
+      const float eg_row = seg[row], w_row = sww[row];
+#pragma unroll
+      for (int kk = 0; kk < NJ / 4; ++kk) {
+        const int jk = 4 * kk + gq;
+        const float o = cO[jk * RP + row], du = cDU[jk * RP + row];
+        const float ao = eg_row * o, au = w_row * cU[jk * RP + row], ax = -eg_row * cDX[jk * RP + row];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int col = 16 * (nt0 + 2 * u) + ln;
+          mP[u] = mfma4(o, cU[jk * RP + col], mP[u]);
+          mT[u] = mfma4(du, cX[jk * RP + col], mT[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+          const int col = 16 * (nt0 + 2 * u) + ln;
+          const float s0 = cS[jk * SP + col];
+          mQ[u] = mfma4(ao, s0, mQ[u]);
+          mK[u] = mfma4(ax, s0, mfma4(au, cD[jk * SP + col], mK[u]));
+        }
       }
     }
     __syncthreads();
@@ -506,15 +547,25 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     sdeg[r] = deg;
     atomicAdd(&sgam, gamp);
   }
+  // dP into m1 and dT' into m2 from the MFMA tiles
+  for (int u = 0; u < 2; ++u)
+    for (int e = 0; e < 4; ++e) {
+      const int rr = 16 * mt + 4 * gq + e, col = 16 * (nt0 + 2 * u) + ln;
+      m1[rr * MP + col] = mP[u][e];
+      m2[rr * MP + col] = mT[u][e];
+    }
+  __syncthreads();
   // dQK = tril_incl(dP) . Dl;  dDl . Dl collects dP . P (and below dA . A)
-  float ddl[IPT];
+  float ddl[IPT], dqk[IPT];
   for (int ii = 0; ii < IPT; ++ii) {
     const int i = i0 + ii;
     const bool low = i <= r;
-    m1[r * MP + i] = low ? accP[ii] * expf(sg[r] - sg[i]) : 0.f;
-    m2[r * MP + i] = accT[ii];
-    ddl[ii] = low ? accP[ii] * sPG[r][i] : 0.f;
+    const float dp = m1[r * MP + i];
+    dqk[ii] = low ? dp * expf(sg[r] - sg[i]) : 0.f;
+    ddl[ii] = low ? dp * sPG[r][i] : 0.f;
   }
+  __syncthreads();
+  for (int ii = 0; ii < IPT; ++ii) m1[r * MP + i0 + ii] = dqk[ii];
   __syncthreads();
   for (int i = 0; i < BC; ++i) {
     const float a = m1[r * MP + i], at = m1[i * MP + r];
@@ -616,6 +667,19 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     float a = 0.f;
     for (int j = BC - 1; j >= i; --j) a += sdg[j];
     if (t < T) dla[tok(b, t, T, H, h)] = a;
+  }
+  // add the MFMA parts of dQ and dK (through LDS, in the row layout); m1 and m2 are free
+  constexpr int CP = DK + 4;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int u = 0; u < NTW; ++u)
+      for (int e = 0; e < 4; ++e)
+        sW[(16 * mt + 4 * gq + e) * CP + 16 * (nt0 + 2 * u) + ln] = pass == 0 ? mQ[u][e] : mK[u][e];
+    __syncthreads();
+    for (int dd = 0; dd < DQ; ++dd) {
+      if (pass == 0) accQ[dd] += sW[r * CP + d0 + dd];
+      else accK[dd] += sW[r * CP + d0 + dd];
+    }
+    __syncthreads();
   }
   const int t = c * BC + r;
   if (t < T) {
