@@ -490,10 +490,12 @@ kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q
   a.rec = static_cast<float*>(ws);
   a.states = a.rec + nch * kla::bwd_record_floats();
   a.dstates = a.states + nch * dk * dv;
+  a.vt = a.dstates + nch * dk * dv;
   a.gq = grad_q; a.gk = grad_k; a.gv = grad_v; a.gla = grad_log_alpha; a.geta = grad_eta; a.ginit = grad_init_state;
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
-  static const char* const names[4] = {"kla_bwd_prep", "kla_bwd_states", "kla_bwd_dstates", "kla_bwd_grads"};
-  for (int stage = 0; e == hipSuccess && stage < 4; ++stage)
+  static const char* const names[5] = {"kla_bwd_prep", "kla_bwd_states", "kla_bwd_dprep", "kla_bwd_dstates",
+                                       "kla_bwd_grads"};
+  for (int stage = 0; e == hipSuccess && stage < 5; ++stage)
     e = timed(names[stage], stream, [&] { return kla::launch_bwd(mode, a, stage, stream); });
   hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

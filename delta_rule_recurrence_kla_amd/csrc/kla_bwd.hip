@@ -6,10 +6,12 @@
 //   A  = strict_lower(beta_r Dl[r][i] (k_r . k_i)),  Minv = (I + A)^-1,  T' = Minv diag(beta)
 //   X  = V - e^g . (K S0),   U = T' X,   P = tril_incl(Dl . Q K^T)
 //   O  = e^g . (Q S0) + P U,   S1 = e^{g_C} S0 + K^T (w . U)
-// Reverse mode through these products runs in four kernels:
+// Reverse mode through these products runs in five kernels:
 //   prep     per chunk: g, beta, ||k||^2 + eps, Minv, and P with K K^T in one matrix
 //   states   forward walk over chunks per 16-column block of the state: every chunk-start S0
-//   dstates  reverse walk per 16-column block: every chunk-end gradient dS1, from
+//   dprep    per chunk: the terms of the reverse walk that do not depend on the carried
+//            gradient, P^T dO and Q^T (e^g . dO)
+//   dstates  reverse walk per 8-column block: every chunk-end gradient dS1, from
 //              dS0 = e^{g_C} dS1 + Q^T (e^g . dO) - K^T (e^g . dX),
 //              dX  = diag(beta) Minv^T dU,  dU = w . (K dS1) + P^T dO
 //   grads    per chunk, from S0 and dS1: dq, dk, dv, dlog_alpha, deta (the chunk-local
@@ -242,24 +244,80 @@ __global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const 
   }
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// One fp32 MFMA step (16 x 16 tile, K = 4, full fp32 products): lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16]; the tile's rows 4 (l / 16) + i, column l % 16, sit in lane l's acc[i].
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// Chunk-local terms of the reverse walk, all chunks in parallel on the fp32 MFMA:
+//   V~ = P^T dO (64 x dv) into vt, and Q^T (e^g . dO) (dk x dv) into the chunk's slot of dstates,
+// which the reverse walk reads and then overwrites with the chunk-end state gradient.
+template <int MODE, int DK>
+__global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const float* dout, const float* rec, int T, int H,
+                                                       int DV, int nc, float* vt, float* cq) {
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  __shared__ float sQ[BC][DK + 1];
+  __shared__ float sO[BC][128 + 1];  // dv <= 128
+  __shared__ float sP[BC][MP];
+  __shared__ float seg[BC];
+  const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
+  load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
+  for (int e = tid; e < BC * DV; e += NT) {
+    const int rr = e / DV, j = e % DV, t = c * BC + rr;
+    sO[rr][j] = t < T ? dout[tok(b, t, T, H, h) * DV + j] : 0.f;
+  }
+  for (int e = tid; e < BC * BC; e += NT) sP[e / BC][e % BC] = R[REC_PG + e];
+  if (tid < BC) seg[tid] = expf(R[REC_G + tid]);
+  __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
+  const int ntj = DV / 16, ntiles = (BC / 16 + DK / 16) * ntj;
+  const size_t cidx = static_cast<size_t>(bh) * nc + c;
+  for (int tile = wv; tile < ntiles; tile += NT / 64) {
+    const int mt = tile / ntj, col = 16 * (tile % ntj) + ln;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    if (mt < BC / 16) {  // V~[r][j] = sum over i >= r of P[i][r] dO[i][j]
+      const int row = 16 * mt + ln;
+#pragma unroll 4
+      for (int kk = 0; kk < BC / 4; ++kk) {
+        const int i = 4 * kk + gq;
+        acc = mfma4(i >= row ? sP[i][row] : 0.f, sO[i][col], acc);
+      }
+      float* o = vt + (cidx * BC + 16 * mt + 4 * gq) * DV + col;
+      for (int e = 0; e < 4; ++e) o[e * DV] = acc[e];
+    } else {  // C[d][j] = sum over i of Q[i][d] e^{g_i} dO[i][j]
+      const int m2 = mt - BC / 16, d = 16 * m2 + ln;
+#pragma unroll 4
+      for (int kk = 0; kk < BC / 4; ++kk) {
+        const int i = 4 * kk + gq;
+        acc = mfma4(sQ[i][d], seg[i] * sO[i][col], acc);
+      }
+      float* o = cq + (cidx * DK + 16 * m2 + 4 * gq) * DV + col;
+      for (int e = 0; e < 4; ++e) o[e * DV] = acc[e];
+    }
+  }
+}
+
 // Reverse walk: every chunk-end state gradient dS1 into dstates[bh][c]; the start state's
-// gradient into dinit (if not null). A workgroup owns 8 state columns, and its LDS (bf16 query
-// and key rows for bf16 inputs) stays under half of the CU's, so two workgroups share a CU.
+// gradient into dinit (if not null). With the chunk-local terms from bwd_dprep, a step is
+//   dU = w . (K dS1) + V~,  dX = diag(beta) Minv^T dU,  dS0 = e^{g_C} dS1 + C - K^T (e^g . dX).
+// A workgroup owns 8 state columns; for bf16 inputs the key rows stay bf16 in LDS (exact).
 constexpr int NJW = 8, CPW = NJW / TPRW;
 template <int MODE, int DK>
-__global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(const void* q, const void* k, const float* dout,
+__global__ __launch_bounds__(NT, MODE == 0 ? 6 : 4) void bwd_dstates_kernel(const void* k, const float* vt,
                                                             const float* rec, const float* dfin, int T, int H, int DV,
                                                             int nc, float* dstates, float* dinit) {
   using E = typename LdsIn<MODE>::type;
-  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows of queries and keys
+  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows of keys
   constexpr int SP = DK + 4, RP = BC + 4;         // column-major blocks: state columns, chunk columns
   constexpr int EPT = DK * NJW / NT, TPR = NJW / EPT;
   const int jb = blockIdx.x * NJW, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ __align__(16) E sQ[BC][EP];
   __shared__ __align__(16) E sK[BC][EP];
-  __shared__ float sM[BC][BC], sPG[BC][BC];  // read down columns only: no padding needed
+  __shared__ float sM[BC][BC];  // read down columns only: no padding needed
   __shared__ __align__(16) float sS[NJW][SP];
-  __shared__ __align__(16) float sO[NJW][RP];
+  __shared__ __align__(16) float sV[NJW][RP];
   __shared__ __align__(16) float sU[NJW][RP];
   __shared__ __align__(16) float sX[NJW][RP];
   __shared__ float sg[BC], sb[BC];
@@ -269,22 +327,21 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(cons
   for (int e = 0; e < EPT; ++e)
     s[e] = dfin ? dfin[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
   for (int c = nc - 1; c >= 0; --c) {
-    const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
-    float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
+    const size_t cidx = static_cast<size_t>(bh) * nc + c;
+    const float* R = rec + cidx * RECF;
+    float* D1 = dstates + cidx * DK * DV;
+    float cterm[EPT];
     for (int e = 0; e < EPT; ++e) {
+      cterm[e] = D1[sd * DV + jb + sj + e];  // Q^T (e^g . dO), this thread's elements only
       D1[sd * DV + jb + sj + e] = s[e];
       sS[sj + e][sd] = s[e];
     }
-    load_rows_in<MODE, DK, EP, E>(sQ, q, b, h, c, T, H);
     load_rows_in<MODE, DK, EP, E>(sK, k, b, h, c, T, H);
     for (int e = tid; e < BC * NJW; e += NT) {
-      const int rr = e / NJW, jj = e % NJW, t = c * BC + rr;
-      sO[jj][rr] = t < T ? dout[tok(b, t, T, H, h) * DV + jb + jj] : 0.f;
+      const int rr = e / NJW, jj = e % NJW;
+      sV[jj][rr] = vt[(cidx * BC + rr) * DV + jb + jj];
     }
-    for (int e = tid; e < BC * BC; e += NT) {
-      sM[e / BC][e % BC] = R[REC_M + e];
-      sPG[e / BC][e % BC] = R[REC_PG + e];
-    }
+    for (int e = tid; e < BC * BC; e += NT) sM[e / BC][e % BC] = R[REC_M + e];
     if (tid < BC) {
       sg[tid] = R[REC_G + tid];
       sb[tid] = R[REC_B + tid];
@@ -292,7 +349,7 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(cons
     __syncthreads();
     const float gC = sg[BC - 1];
     const float wr = expf(gC - sg[r]), egr = expf(sg[r]);
-    // dU = w . (K dS1) + P^T dO
+    // dU = w . (K dS1) + V~
     {
       float a = 0.f;
 #pragma unroll 2
@@ -302,49 +359,36 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 4 : 2) void bwd_dstates_kernel(cons
         row8(&sS[j][d], sf);
         for (int x = 0; x < 8; ++x) a = fmaf(kf[x], sf[x], a);
       }
-      float p = 0.f;
-#pragma unroll 8
-      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], sO[j][i], p);
-      sU[j][r] = fmaf(wr, a, p);
+      sU[j][r] = fmaf(wr, a, sV[j][r]);
     }
     __syncthreads();
-    // e^g . dX with dX = diag(beta) Minv^T dU; e^g . dO in place
+    // e^g . dX with dX = diag(beta) Minv^T dU
     {
       float a = 0.f;
 #pragma unroll 8
       for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[j][i], a);
       sX[j][r] = egr * sb[r] * a;
-      sO[j][r] *= egr;
     }
     __syncthreads();
     const float gam = expf(gC);
     for (int e = 0; e < EPT; ++e) {
-      const float4* o4 = reinterpret_cast<const float4*>(&sO[sj + e][0]);
       const float4* x4 = reinterpret_cast<const float4*>(&sX[sj + e][0]);
       float a = 0.f;
 #pragma unroll 4
       for (int i4 = 0; i4 < BC / 4; ++i4) {
-        const float4 oo = o4[i4], xx = x4[i4];
+        const float4 xx = x4[i4];
         const int i = 4 * i4;
-        a = fmaf(lds_f(sQ[i][sd]), oo.x, fmaf(-lds_f(sK[i][sd]), xx.x, a));
-        a = fmaf(lds_f(sQ[i + 1][sd]), oo.y, fmaf(-lds_f(sK[i + 1][sd]), xx.y, a));
-        a = fmaf(lds_f(sQ[i + 2][sd]), oo.z, fmaf(-lds_f(sK[i + 2][sd]), xx.z, a));
-        a = fmaf(lds_f(sQ[i + 3][sd]), oo.w, fmaf(-lds_f(sK[i + 3][sd]), xx.w, a));
+        a = fmaf(lds_f(sK[i][sd]), xx.x, a);
+        a = fmaf(lds_f(sK[i + 1][sd]), xx.y, a);
+        a = fmaf(lds_f(sK[i + 2][sd]), xx.z, a);
+        a = fmaf(lds_f(sK[i + 3][sd]), xx.w, a);
       }
-      s[e] = fmaf(gam, s[e], a);
+      s[e] = fmaf(gam, s[e], cterm[e] - a);
     }
     __syncthreads();
   }
   if (dinit)
     for (int e = 0; e < EPT; ++e) dinit[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] = s[e];
-}
-
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-// One fp32 MFMA step (16 x 16 tile, K = 4, full fp32 products): lane l supplies A[l % 16][l / 16]
-// and B[l / 16][l % 16]; the tile's rows 4 (l / 16) + i, column l % 16, sit in lane l's acc[i].
-__device__ __forceinline__ v4f mfma4(float a, float b, v4f acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
 // Sum over the TPRW adjacent lanes that share a chunk row.
@@ -703,7 +747,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
       return launch_kernel(bwd_states_kernel<MODE, DK>, dim3(a.dv / NJ, bh), dim3(NT), stream, a.k, a.v, a.rec, a.init, a.T,
                            a.H, a.dv, a.nc, a.states);
     case 2:
-      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJW, bh), dim3(NT), stream, a.q, a.k, a.dout, a.rec,
+      return launch_kernel(bwd_dprep_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.dout, a.rec, a.T, a.H,
+                           a.dv, a.nc, a.vt, a.dstates);
+    case 3:
+      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJW, bh), dim3(NT), stream, a.k, a.vt, a.rec,
                            a.dfin, a.T, a.H, a.dv, a.nc, a.dstates, a.ginit);
     default:
       return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.k, a.v, a.eta, a.dout,
@@ -718,7 +765,7 @@ size_t bwd_record_floats() { return RECF; }
 
 size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
   const size_t nch = static_cast<size_t>(B) * H * ((T + BC - 1) / BC);
-  return nch * (RECF + 2 * static_cast<size_t>(dk) * dv) * sizeof(float);
+  return nch * (RECF + 2 * static_cast<size_t>(dk) * dv + static_cast<size_t>(BC) * dv) * sizeof(float);
 }
 
 hipError_t launch_bwd(int mode, const BwdArgs& a, int stage, hipStream_t stream) {

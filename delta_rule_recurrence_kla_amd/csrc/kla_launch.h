@@ -101,19 +101,21 @@ hipError_t launch_decode(int mode, int N, int H, int dk, int dv, const void* q, 
                          const void* v, const float* log_alpha, const float* eta, float eps, int direct,
                          float* state, float* out, hipStream_t stream);
 
-// Chunkwise backward (kla_bwd.hip). Workspace: per chunk one record and two dk x dv states.
+// Chunkwise backward (kla_bwd.hip). Workspace: per chunk one record, two dk x dv states and a
+// 64 x dv block.
 struct BwdArgs {
   int B, T, H, dk, dv, nc, direct;
   float eps;
   const void *q, *k, *v;
   const float *log_alpha, *eta, *init, *dout, *dfin;
-  float *rec, *states, *dstates;                    // workspace parts
+  float *rec, *states, *dstates, *vt;               // workspace parts
   float *gq, *gk, *gv, *gla, *geta, *ginit;         // gradients (ginit may be null)
 };
 size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
 size_t bwd_record_floats();
-// stage 0: chunk records; 1: forward walk (chunk-start states); 2: reverse walk (chunk-end
-// state gradients, and the start state's); 3: per-chunk gradients.
+// stage 0: chunk records; 1: forward walk (chunk-start states); 2: chunk-local terms of the
+// reverse walk; 3: reverse walk (chunk-end state gradients, and the start state's); 4: per-chunk
+// gradients.
 hipError_t launch_bwd(int mode, const BwdArgs& a, int stage, hipStream_t stream);
 
 }  // namespace kla
