@@ -33,7 +33,6 @@ constexpr int NT = 512;   // threads of a walk or grads workgroup: 8 per chunk r
 constexpr int TPRW = NT / 64, CPT = 16 / TPRW, IPT = 64 / TPRW;  // per row: threads, columns, row entries
 constexpr int MP = 65;    // LDS pitch of 64 x 64 matrices
 constexpr int NJ = 16;    // state columns per walk workgroup / per grads column block
-constexpr int NJP = NJ + 1;
 // chunk record: Minv [64][64], PG [64][64] (lower incl: P; strict upper: K K^T), g, beta, den
 constexpr int REC_M = 0, REC_PG = BC * BC, REC_G = 2 * BC * BC, REC_B = REC_G + BC, REC_D = REC_B + BC;
 constexpr int RECF = REC_D + 2 * BC;
@@ -54,15 +53,6 @@ __device__ __forceinline__ void load_rows(float (*s)[P], const void* x, int b, i
   for (int e = threadIdx.x; e < BC * D; e += blockDim.x) {
     const int r = e / D, d = e % D, t = c * BC + r;
     s[r][d] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * D + d) : 0.f;
-  }
-}
-
-// Columns jb .. jb+W-1 of a [B,T,H,DV] fp32 or input array for chunk c into s[64][W + 1].
-template <int MODE, int W = NJ>
-__device__ __forceinline__ void load_cols(float* s, const void* x, int b, int h, int c, int T, int H, int DV, int jb) {
-  for (int e = threadIdx.x; e < BC * W; e += blockDim.x) {
-    const int r = e / W, j = e % W, t = c * BC + r;
-    s[r * (W + 1) + j] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * DV + jb + j) : 0.f;
   }
 }
 
@@ -182,18 +172,25 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
 }
 
 // Forward walk over the chunks of one (b, h) for state columns jb .. jb+15; stores every
-// chunk-start state S0 into states[bh][c][DK][DV].
+// chunk-start state S0 into states[bh][c][DK][DV]. Key rows stay bf16 in LDS for bf16 inputs
+// (exact) and the column blocks are stored column-major, for 16-byte reads.
 template <int MODE, int DK>
-__global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const void* v, const float* rec,
-                                                        const float* init, int T, int H, int DV, int nc,
-                                                        float* states) {
+__global__ __launch_bounds__(NT, MODE == 0 ? 6 : 4) void bwd_states_kernel(const void* k, const void* v,
+                                                            const float* rec, const float* init, int T, int H,
+                                                            int DV, int nc, float* states) {
+  using E = typename LdsIn<MODE>::type;
+  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;
+  constexpr int SP = DK + 4, RP = BC + 4;
   constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT;
   const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ float sK[BC][DK + 1], sM[BC][MP];
-  __shared__ float sS[DK][NJP], sX[BC * NJP], sU[BC][NJP];
+  __shared__ __align__(16) E sK[BC][EP];
+  __shared__ float sM[BC][MP];
+  __shared__ __align__(16) float sS[NJ][SP];
+  __shared__ __align__(16) float sX[NJ][RP];
+  __shared__ __align__(16) float sU[NJ][RP];
   __shared__ float sg[BC], sb[BC];
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;  // state elements owned
-  const int r = tid / TPRW, j0 = (tid % TPRW) * CPT;         // 64 x 16 chunk elements owned
+  const int r = tid / TPRW, j0 = (tid % TPRW) * CPT;  // 64 x 16 chunk elements owned
   float s[EPT];
   for (int e = 0; e < EPT; ++e)
     s[e] = init ? init[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
@@ -202,10 +199,13 @@ __global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const 
     float* S0 = states + (static_cast<size_t>(bh) * nc + c) * DK * DV;
     for (int e = 0; e < EPT; ++e) {
       S0[sd * DV + jb + sj + e] = s[e];
-      sS[sd][sj + e] = s[e];
+      sS[sj + e][sd] = s[e];
     }
-    load_rows<MODE, DK>(sK, k, b, h, c, T, H);
-    load_cols<MODE>(sX, v, b, h, c, T, H, DV, jb);
+    load_rows_in<MODE, DK, EP, E>(sK, k, b, h, c, T, H);
+    for (int e = tid; e < BC * NJ; e += NT) {
+      const int rr = e / NJ, jj = e % NJ, t = c * BC + rr;
+      sX[jj][rr] = t < T ? ldin<MODE>(v, tok(b, t, T, H, h) * DV + jb + jj) : 0.f;
+    }
     for (int e = tid; e < BC * BC; e += NT) sM[e / BC][e % BC] = R[REC_M + e];
     if (tid < BC) {
       sg[tid] = R[REC_G + tid];
@@ -217,11 +217,16 @@ __global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const 
     float x[CPT];
     for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < DK; ++d) a = fmaf(sK[r][d], sS[d][j0 + jj], a);
-      x[jj] = sb[r] * (sX[r * NJP + j0 + jj] - egr * a);
+#pragma unroll 2
+      for (int d = 0; d < DK; d += 8) {
+        float kf[8], sf[8];
+        row8(&sK[r][d], kf);
+        row8(&sS[j0 + jj][d], sf);
+        for (int q = 0; q < 8; ++q) a = fmaf(kf[q], sf[q], a);
+      }
+      x[jj] = sb[r] * (sX[j0 + jj][r] - egr * a);
     }
-    for (int jj = 0; jj < CPT; ++jj) sX[r * NJP + j0 + jj] = x[jj];
+    for (int jj = 0; jj < CPT; ++jj) sX[j0 + jj][r] = x[jj];
     __syncthreads();
     // w . U with U = Minv (beta . X)
     const float gC = sg[BC - 1];
@@ -229,15 +234,23 @@ __global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const 
     for (int jj = 0; jj < CPT; ++jj) {
       float a = 0.f;
 #pragma unroll 8
-      for (int i = 0; i <= r; ++i) a = fmaf(sM[r][i], sX[i * NJP + j0 + jj], a);
-      sU[r][j0 + jj] = wr * a;
+      for (int i = 0; i <= r; ++i) a = fmaf(sM[r][i], sX[j0 + jj][i], a);
+      sU[j0 + jj][r] = wr * a;
     }
     __syncthreads();
     const float gam = expf(gC);
     for (int e = 0; e < EPT; ++e) {
+      const float4* u4 = reinterpret_cast<const float4*>(&sU[sj + e][0]);
       float a = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < BC; ++i) a = fmaf(sK[i][sd], sU[i][sj + e], a);
+#pragma unroll 4
+      for (int i4 = 0; i4 < BC / 4; ++i4) {
+        const float4 uu = u4[i4];
+        const int i = 4 * i4;
+        a = fmaf(lds_f(sK[i][sd]), uu.x, a);
+        a = fmaf(lds_f(sK[i + 1][sd]), uu.y, a);
+        a = fmaf(lds_f(sK[i + 2][sd]), uu.z, a);
+        a = fmaf(lds_f(sK[i + 3][sd]), uu.w, a);
+      }
       s[e] = fmaf(gam, s[e], a);
     }
     __syncthreads();
