@@ -92,11 +92,12 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
                                                       float* rec) {
   constexpr int AP = 68;  // pitch of A: 16-byte rows for vector reads
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ float sQ[BC][DK + 1], sK[BC][DK + 1];
+  using E = typename LdsIn<MODE>::type;  // bf16 inputs stay bf16 in LDS (exact): three workgroups per CU
+  __shared__ E sQ[BC][DK + 2], sK[BC][DK + 2];
   __shared__ __align__(16) float sA[BC * AP];
   __shared__ float sla[BC], sg[BC], sb[BC];
-  load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
-  load_rows<MODE, DK>(sK, k, b, h, c, T, H);
+  load_rows_in<MODE, DK, DK + 2, E>(sQ, q, b, h, c, T, H);
+  load_rows_in<MODE, DK, DK + 2, E>(sK, k, b, h, c, T, H);
   float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
   const int t = c * BC + tid;
   if (tid < BC) sla[tid] = t < T ? log_alpha[tok(b, t, T, H, h)] : 0.f;
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
     float gs = 0.f;
     for (int i = 0; i <= tid; ++i) gs += sla[i];
     float n = 0.f;
-    for (int d = 0; d < DK; ++d) n = fmaf(sK[tid][d], sK[tid][d], n);
+    for (int d = 0; d < DK; ++d) n = fmaf(lds_f(sK[tid][d]), lds_f(sK[tid][d]), n);
     const float et = t < T ? eta[tok(b, t, T, H, h)] : 0.f;
     const float den = n + eps;
     const float beta = direct ? et : (den != 0.f ? et / den : 0.f);
@@ -126,9 +127,9 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
     for (int d = 0; d < DK; ++d) {
       float qa[4], ka[4], kb[4];
       for (int a = 0; a < 4; ++a) {
-        qa[a] = sQ[r0 + 16 * a][d];
-        ka[a] = sK[r0 + 16 * a][d];
-        kb[a] = sK[i0 + 16 * a][d];
+        qa[a] = lds_f(sQ[r0 + 16 * a][d]);
+        ka[a] = lds_f(sK[r0 + 16 * a][d]);
+        kb[a] = lds_f(sK[i0 + 16 * a][d]);
       }
       for (int a = 0; a < 4; ++a)
         for (int e = 0; e < 4; ++e) {
@@ -272,12 +273,13 @@ template <int MODE, int DK>
 __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const float* dout, const float* rec, int T, int H,
                                                        int DV, int nc, float* vt, float* cq) {
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ float sQ[BC][DK + 1];
+  using E = typename LdsIn<MODE>::type;
+  __shared__ E sQ[BC][DK + 2];
   __shared__ float sO[BC][128 + 1];  // dv <= 128
   __shared__ float sP[BC][MP];
   __shared__ float seg[BC];
   const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
-  load_rows<MODE, DK>(sQ, q, b, h, c, T, H);
+  load_rows_in<MODE, DK, DK + 2, E>(sQ, q, b, h, c, T, H);
   for (int e = tid; e < BC * DV; e += NT) {
     const int rr = e / DV, j = e % DV, t = c * BC + rr;
     sO[rr][j] = t < T ? dout[tok(b, t, T, H, h) * DV + j] : 0.f;
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const floa
 #pragma unroll 4
       for (int kk = 0; kk < BC / 4; ++kk) {
         const int i = 4 * kk + gq;
-        acc = mfma4(sQ[i][d], seg[i] * sO[i][col], acc);
+        acc = mfma4(lds_f(sQ[i][d]), seg[i] * sO[i][col], acc);
       }
       float* o = cq + (cidx * DK + 16 * m2 + 4 * gq) * DV + col;
       for (int e = 0; e < 4; ++e) o[e * DV] = acc[e];
