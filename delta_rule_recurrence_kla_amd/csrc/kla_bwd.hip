@@ -467,7 +467,9 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   v4f mP[2], mT[2], mQ[NTW], mK[NTW];
   for (int u = 0; u < 2; ++u) mP[u] = mT[u] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int u = 0; u < NTW; ++u) mQ[u] = mK[u] = v4f{0.f, 0.f, 0.f, 0.f};
-  float accQ[DQ], accK[DQ];  // dQ, dK in the row layout, from the MFMA tiles at the end
+  // the products after the column blocks accumulate in the row layout
+  float accQ[DQ], accK[DQ];
+  for (int i = 0; i < DQ; ++i) accQ[i] = accK[i] = 0.f;
   float dwp = 0.f, degp = 0.f, gamp = 0.f;
   __syncthreads();
   const float gC = sg[BC - 1];
@@ -624,19 +626,20 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __syncthreads();
   for (int ii = 0; ii < IPT; ++ii) m1[r * MP + i0 + ii] = dqk[ii];
   __syncthreads();
-  // dQ += dQK K, dK += dQK^T Q on the MFMA tiles
-  {
-    const int row = 16 * mt + ln;
-#pragma unroll 4
-    for (int kk = 0; kk < BC / 4; ++kk) {
-      const int i = 4 * kk + gq;
-      const float a = m1[row * MP + i], at = m1[i * MP + row];
-#pragma unroll
-      for (int u = 0; u < NTW; ++u) {
-        const int col = 16 * (nt0 + 2 * u) + ln;
-        mQ[u] = mfma4(a, sK[i][col], mQ[u]);
-        mK[u] = mfma4(at, sQ[i][col], mK[u]);
-      }
+  for (int i = 0; i < BC; ++i) {
+    const float a = m1[r * MP + i], at = m1[i * MP + r];
+    const float4* ki = reinterpret_cast<const float4*>(&sK[i][d0]);
+    const float4* qi = reinterpret_cast<const float4*>(&sQ[i][d0]);
+    for (int q4 = 0; q4 < DQ / 4; ++q4) {
+      const float4 kk = ki[q4], qq = qi[q4];
+      accQ[4 * q4 + 0] = fmaf(a, kk.x, accQ[4 * q4 + 0]);
+      accQ[4 * q4 + 1] = fmaf(a, kk.y, accQ[4 * q4 + 1]);
+      accQ[4 * q4 + 2] = fmaf(a, kk.z, accQ[4 * q4 + 2]);
+      accQ[4 * q4 + 3] = fmaf(a, kk.w, accQ[4 * q4 + 3]);
+      accK[4 * q4 + 0] = fmaf(at, qq.x, accK[4 * q4 + 0]);
+      accK[4 * q4 + 1] = fmaf(at, qq.y, accK[4 * q4 + 1]);
+      accK[4 * q4 + 2] = fmaf(at, qq.z, accK[4 * q4 + 2]);
+      accK[4 * q4 + 3] = fmaf(at, qq.w, accK[4 * q4 + 3]);
     }
   }
   if (tid < BC) {  // dbeta from T' = Minv diag(beta): column sums of Minv . dT'
@@ -685,15 +688,15 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   }
   __syncthreads();
   // dK += (dG + dG^T) K
-  // dK += (dG + dG^T) K on the MFMA tiles
-  {
-    const int row = 16 * mt + ln;
-#pragma unroll 4
-    for (int kk = 0; kk < BC / 4; ++kk) {
-      const int i = 4 * kk + gq;
-      const float a = m2[row * MP + i] + m2[i * MP + row];
-#pragma unroll
-      for (int u = 0; u < NTW; ++u) mK[u] = mfma4(a, sK[i][16 * (nt0 + 2 * u) + ln], mK[u]);
+  for (int i = 0; i < BC; ++i) {
+    const float a = m2[r * MP + i] + m2[i * MP + r];
+    const float4* ki = reinterpret_cast<const float4*>(&sK[i][d0]);
+    for (int q4 = 0; q4 < DQ / 4; ++q4) {
+      const float4 kk = ki[q4];
+      accK[4 * q4 + 0] = fmaf(a, kk.x, accK[4 * q4 + 0]);
+      accK[4 * q4 + 1] = fmaf(a, kk.y, accK[4 * q4 + 1]);
+      accK[4 * q4 + 2] = fmaf(a, kk.z, accK[4 * q4 + 2]);
+      accK[4 * q4 + 3] = fmaf(a, kk.w, accK[4 * q4 + 3]);
     }
   }
   if (tid < BC) {
@@ -724,7 +727,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     for (int j = BC - 1; j >= i; --j) a += sdg[j];
     if (t < T) dla[tok(b, t, T, H, h)] = a;
   }
-  // dQ and dK from the MFMA tiles into the row layout (through LDS); m1 and m2 are free
+  // add the MFMA parts of dQ and dK (through LDS, in the row layout); m1 and m2 are free
   constexpr int CP = DK + 4;
   for (int pass = 0; pass < 2; ++pass) {
     for (int u = 0; u < NTW; ++u)
@@ -732,8 +735,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
         sW[(16 * mt + 4 * gq + e) * CP + 16 * (nt0 + 2 * u) + ln] = pass == 0 ? mQ[u][e] : mK[u][e];
     __syncthreads();
     for (int dd = 0; dd < DQ; ++dd) {
-      if (pass == 0) accQ[dd] = sW[r * CP + d0 + dd];
-      else accK[dd] = sW[r * CP + d0 + dd];
+      if (pass == 0) accQ[dd] += sW[r * CP + d0 + dd];
+      else accK[dd] += sW[r * CP + d0 + dd];
     }
     __syncthreads();
   }
