@@ -545,33 +545,55 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[(sj + e) * SP + sd], cD[(sj + e) * SP + sd], gamp);
     for (int jj = 0; jj < CPT; ++jj) cX[(j0 + jj) * RP + r] -= egr * ks[jj];  // X
     __syncthreads();
-    // U = Minv (beta . X); dU = w . (K dS1) + P^T dO
+    // U = Minv (beta . X) (waves 0-3) and P^T dO (waves 4-7) for row tile mt on the fp32 MFMA
+    {
+      const int row = 16 * mt + ln;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      if (wv < 4) {
+#pragma unroll 4
+        for (int kk = 0; kk < BC / 4; ++kk) {
+          const int i = 4 * kk + gq;
+          acc = mfma4(sM[row][i] * sb[i], cX[ln * RP + i], acc);
+        }
+        for (int e = 0; e < 4; ++e) cU[ln * RP + 16 * mt + 4 * gq + e] = acc[e];
+      } else {
+#pragma unroll 4
+        for (int kk = 0; kk < BC / 4; ++kk) {
+          const int i = 4 * kk + gq;
+          acc = mfma4(i >= row ? sPG[i][row] : 0.f, cO[ln * RP + i], acc);
+        }
+        for (int e = 0; e < 4; ++e) cDU[ln * RP + 16 * mt + 4 * gq + e] = acc[e];
+      }
+    }
+    __syncthreads();
+    // dU = w . (K dS1) + P^T dO, each element by its owner
     for (int jj = 0; jj < CPT; ++jj) {
-      const float* xc = cX + (j0 + jj) * RP;
-      const float* oc = cO + (j0 + jj) * RP;
-      float u = 0.f, p = 0.f;
-#pragma unroll 4
-      for (int i = 0; i <= r; ++i) u = fmaf(sM[r][i], sb[i] * xc[i], u);
-#pragma unroll 4
-      for (int i = r; i < BC; ++i) p = fmaf(sPG[i][r], oc[i], p);
-      cU[(j0 + jj) * RP + r] = u;
-      cDU[(j0 + jj) * RP + r] = fmaf(wr, kd[jj], p);
+      const float u = cU[(j0 + jj) * RP + r];
+      cDU[(j0 + jj) * RP + r] = fmaf(wr, kd[jj], cDU[(j0 + jj) * RP + r]);
       dwp = fmaf(u, kd[jj], dwp);
     }
     __syncthreads();
-    // dX = diag(beta) Minv^T dU, which is also dV
-    for (int jj = 0; jj < CPT; ++jj) {
-      const float* uc = cDU + (j0 + jj) * RP;
-      float a = 0.f;
+    // dX = diag(beta) Minv^T dU (waves 0-3), which is also dV
+    if (wv < 4) {
+      const int row = 16 * mt + ln;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], uc[i], a);
-      const float dx = sb[r] * a;
-      cDX[(j0 + jj) * RP + r] = dx;
+      for (int kk = 0; kk < BC / 4; ++kk) {
+        const int i = 4 * kk + gq;
+        acc = mfma4(sM[i][row], cDU[ln * RP + i], acc);
+      }
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * mt + 4 * gq + e;
+        cDX[ln * RP + rr] = sb[rr] * acc[e];
+      }
+    }
+    __syncthreads();
+    for (int jj = 0; jj < CPT; ++jj) {
+      const float dx = cDX[(j0 + jj) * RP + r];
       degp = fmaf(-dx, ks[jj], degp);
       const int t = c * BC + r;
       if (t < T) dv[tok(b, t, T, H, h) * DV + jb + j0 + jj] = dx;
     }
-    __syncthreads();
     // dP += dO U^T, dT' += dU X^T, dQ += e^g . (dO S0^T), dK += w . (U dS1^T) - e^g . (dX S0^T)
     {
       const int row = 16 * mt + ln;
