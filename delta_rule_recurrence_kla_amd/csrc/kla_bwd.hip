@@ -176,13 +176,18 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
 // chunk-start state S0 into states[bh][c][DK][DV]. Key rows stay bf16 in LDS for bf16 inputs
 // (exact) and the column blocks are stored column-major, for 16-byte reads.
 template <int MODE, int DK>
-__global__ __launch_bounds__(NT, MODE == 0 ? 6 : 4) void bwd_states_kernel(const void* k, const void* v,
-                                                            const float* rec, const float* init, int T, int H,
-                                                            int DV, int nc, float* states) {
+__global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const void* v, const float* rec,
+                                                            const float* init, int T, int H, int DV, int nc,
+                                                            float* states) {
   using E = typename LdsIn<MODE>::type;
   constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;
   constexpr int SP = DK + 4, RP = BC + 4;
   constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT;
+  constexpr int KV = DK * sizeof(E) / 16;  // 16-byte pieces per key row
+  constexpr int KPT = BC * KV / NT;        // key pieces per thread
+  constexpr int MPT = BC * BC / 4 / NT;    // float4s of the inverse per thread
+  constexpr int VPT = BC * NJ / NT;        // value elements per thread
+  static_assert(KPT * NT == BC * KV && MPT * NT * 4 == BC * BC && VPT * NT == BC * NJ, "walk tiling");
   const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   __shared__ __align__(16) E sK[BC][EP];
   __shared__ float sM[BC][MP];
@@ -192,26 +197,57 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 6 : 4) void bwd_states_kernel(const
   __shared__ float sg[BC], sb[BC];
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;  // state elements owned
   const int r = tid / TPRW, j0 = (tid % TPRW) * CPT;  // 64 x 16 chunk elements owned
+  // the next chunk's keys, inverse, values and gates, loaded into registers during this chunk
+  uint4 pk[KPT];
+  float4 pm[MPT];
+  float pv[VPT], pg = 0.f, pb = 0.f;
+  auto fetch = [&](int c) {
+    const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
+    for (int x = 0; x < KPT; ++x) {
+      const int e = tid + x * NT, rr = e / KV, pc = e % KV, t = c * BC + rr;
+      pk[x] = t < T ? *(reinterpret_cast<const uint4*>(static_cast<const E*>(k) + tok(b, t, T, H, h) * DK) + pc)
+                    : uint4{0u, 0u, 0u, 0u};
+    }
+    for (int x = 0; x < MPT; ++x) pm[x] = reinterpret_cast<const float4*>(R + REC_M)[tid + x * NT];
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * NT, rr = e / NJ, jj = e % NJ, t = c * BC + rr;
+      pv[x] = t < T ? ldin<MODE>(v, tok(b, t, T, H, h) * DV + jb + jj) : 0.f;
+    }
+    if (tid < BC) {
+      pg = R[REC_G + tid];
+      pb = R[REC_B + tid];
+    }
+  };
   float s[EPT];
   for (int e = 0; e < EPT; ++e)
     s[e] = init ? init[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
+  fetch(0);
   for (int c = 0; c < nc; ++c) {
-    const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
     float* S0 = states + (static_cast<size_t>(bh) * nc + c) * DK * DV;
     for (int e = 0; e < EPT; ++e) {
       S0[sd * DV + jb + sj + e] = s[e];
       sS[sj + e][sd] = s[e];
     }
-    load_rows_in<MODE, DK, EP, E>(sK, k, b, h, c, T, H);
-    for (int e = tid; e < BC * NJ; e += NT) {
-      const int rr = e / NJ, jj = e % NJ, t = c * BC + rr;
-      sX[jj][rr] = t < T ? ldin<MODE>(v, tok(b, t, T, H, h) * DV + jb + jj) : 0.f;
+    for (int x = 0; x < KPT; ++x) {
+      const int e = tid + x * NT;
+      *reinterpret_cast<uint4*>(&sK[e / KV][(e % KV) * (16 / sizeof(E))]) = pk[x];
     }
-    for (int e = tid; e < BC * BC; e += NT) sM[e / BC][e % BC] = R[REC_M + e];
+    for (int x = 0; x < MPT; ++x) {
+      const int e = 4 * (tid + x * NT), rr = e / BC, cc = e % BC;
+      sM[rr][cc] = pm[x].x;
+      sM[rr][cc + 1] = pm[x].y;
+      sM[rr][cc + 2] = pm[x].z;
+      sM[rr][cc + 3] = pm[x].w;
+    }
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * NT;
+      sX[e % NJ][e / NJ] = pv[x];
+    }
     if (tid < BC) {
-      sg[tid] = R[REC_G + tid];
-      sb[tid] = R[REC_B + tid];
+      sg[tid] = pg;
+      sb[tid] = pb;
     }
+    if (c + 1 < nc) fetch(c + 1);
     __syncthreads();
     // beta . X with X = V - e^g . (K S0)
     const float egr = expf(sg[r]);
@@ -318,16 +354,20 @@ __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const floa
 // Reverse walk: every chunk-end state gradient dS1 into dstates[bh][c]; the start state's
 // gradient into dinit (if not null). With the chunk-local terms from bwd_dprep, a step is
 //   dU = w . (K dS1) + V~,  dX = diag(beta) Minv^T dU,  dS0 = e^{g_C} dS1 + C - K^T (e^g . dX).
-// A workgroup owns 8 state columns; for bf16 inputs the key rows stay bf16 in LDS (exact).
-constexpr int NJW = 8, CPW = NJW / TPRW;
+// A workgroup owns 16 state columns; for bf16 inputs the key rows stay bf16 in LDS (exact). The
+// next chunk's keys, inverse, V~ columns, C elements and gates are loaded into registers while
+// the current chunk is computed.
+constexpr int NJW = 16;
 template <int MODE, int DK>
-__global__ __launch_bounds__(NT, MODE == 0 ? 6 : 4) void bwd_dstates_kernel(const void* k, const float* vt,
-                                                            const float* rec, const float* dfin, int T, int H, int DV,
-                                                            int nc, float* dstates, float* dinit) {
+__global__ __launch_bounds__(NT, 4) void bwd_dstates_kernel(const void* k, const float* vt, const float* rec,
+                                                            const float* dfin, int T, int H, int DV, int nc,
+                                                            float* dstates, float* dinit) {
   using E = typename LdsIn<MODE>::type;
   constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows of keys
   constexpr int SP = DK + 4, RP = BC + 4;         // column-major blocks: state columns, chunk columns
-  constexpr int EPT = DK * NJW / NT, TPR = NJW / EPT;
+  constexpr int EPT = DK * NJW / NT, TPR = NJW / EPT, CPW = NJW / TPRW;
+  constexpr int KV = DK * sizeof(E) / 16, KPT = BC * KV / NT, MPT = BC * BC / 4 / NT, VPT = BC * NJW / NT;
+  static_assert(KPT * NT == BC * KV && MPT * NT * 4 == BC * BC && VPT * NT == BC * NJW, "walk tiling");
   const int jb = blockIdx.x * NJW, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   __shared__ __align__(16) E sK[BC][EP];
   __shared__ float sM[BC][BC];  // read down columns only: no padding needed
@@ -337,55 +377,94 @@ __global__ __launch_bounds__(NT, MODE == 0 ? 6 : 4) void bwd_dstates_kernel(cons
   __shared__ __align__(16) float sX[NJW][RP];
   __shared__ float sg[BC], sb[BC];
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
-  const int r = tid / TPRW, j = (tid % TPRW) * CPW;  // CPW == 1: one chunk column per thread
+  const int r = tid / TPRW, j0 = (tid % TPRW) * CPW;
+  uint4 pk[KPT];
+  float4 pm[MPT];
+  float pv[VPT], pc[EPT], pg = 0.f, pb = 0.f;
+  auto fetch = [&](int c) {
+    const size_t cidx = static_cast<size_t>(bh) * nc + c;
+    const float* R = rec + cidx * RECF;
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const int e = tid + x * NT, rr = e / KV, pe = e % KV, t = c * BC + rr;
+      pk[x] = t < T ? *(reinterpret_cast<const uint4*>(static_cast<const E*>(k) + tok(b, t, T, H, h) * DK) + pe)
+                    : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int x = 0; x < MPT; ++x) pm[x] = reinterpret_cast<const float4*>(R + REC_M)[tid + x * NT];
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * NT, rr = e / NJW, jj = e % NJW;
+      pv[x] = vt[(cidx * BC + rr) * DV + jb + jj];
+    }
+    // Q^T (e^g . dO) of this chunk, this thread's elements only (its slot is overwritten with dS1)
+    const float* D = dstates + cidx * DK * DV;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) pc[e] = D[sd * DV + jb + sj + e];
+    if (tid < BC) {
+      pg = R[REC_G + tid];
+      pb = R[REC_B + tid];
+    }
+  };
   float s[EPT];
   for (int e = 0; e < EPT; ++e)
     s[e] = dfin ? dfin[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
+  fetch(nc - 1);
   for (int c = nc - 1; c >= 0; --c) {
-    const size_t cidx = static_cast<size_t>(bh) * nc + c;
-    const float* R = rec + cidx * RECF;
-    float* D1 = dstates + cidx * DK * DV;
+    float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
     float cterm[EPT];
+#pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      cterm[e] = D1[sd * DV + jb + sj + e];  // Q^T (e^g . dO), this thread's elements only
+      cterm[e] = pc[e];
       D1[sd * DV + jb + sj + e] = s[e];
       sS[sj + e][sd] = s[e];
     }
-    load_rows_in<MODE, DK, EP, E>(sK, k, b, h, c, T, H);
-    for (int e = tid; e < BC * NJW; e += NT) {
-      const int rr = e / NJW, jj = e % NJW;
-      sV[jj][rr] = vt[(cidx * BC + rr) * DV + jb + jj];
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const int e = tid + x * NT;
+      *reinterpret_cast<uint4*>(&sK[e / KV][(e % KV) * (16 / sizeof(E))]) = pk[x];
     }
-    for (int e = tid; e < BC * BC; e += NT) sM[e / BC][e % BC] = R[REC_M + e];
+#pragma unroll
+    for (int x = 0; x < MPT; ++x) {
+      const int e = 4 * (tid + x * NT), rr = e / BC, cc = e % BC;
+      *reinterpret_cast<float4*>(&sM[rr][cc]) = pm[x];
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+      const int e = tid + x * NT;
+      sV[e % NJW][e / NJW] = pv[x];
+    }
     if (tid < BC) {
-      sg[tid] = R[REC_G + tid];
-      sb[tid] = R[REC_B + tid];
+      sg[tid] = pg;
+      sb[tid] = pb;
     }
+    if (c > 0) fetch(c - 1);
     __syncthreads();
     const float gC = sg[BC - 1];
     const float wr = expf(gC - sg[r]), egr = expf(sg[r]);
     // dU = w . (K dS1) + V~
-    {
+    for (int jj = 0; jj < CPW; ++jj) {
       float a = 0.f;
 #pragma unroll 2
       for (int d = 0; d < DK; d += 8) {
         float kf[8], sf[8];
         row8(&sK[r][d], kf);
-        row8(&sS[j][d], sf);
+        row8(&sS[j0 + jj][d], sf);
         for (int x = 0; x < 8; ++x) a = fmaf(kf[x], sf[x], a);
       }
-      sU[j][r] = fmaf(wr, a, sV[j][r]);
+      sU[j0 + jj][r] = fmaf(wr, a, sV[j0 + jj][r]);
     }
     __syncthreads();
     // e^g . dX with dX = diag(beta) Minv^T dU
-    {
+    for (int jj = 0; jj < CPW; ++jj) {
       float a = 0.f;
 #pragma unroll 8
-      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[j][i], a);
-      sX[j][r] = egr * sb[r] * a;
+      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[j0 + jj][i], a);
+      sX[j0 + jj][r] = egr * sb[r] * a;
     }
     __syncthreads();
     const float gam = expf(gC);
+#pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const float4* x4 = reinterpret_cast<const float4*>(&sX[sj + e][0]);
       float a = 0.f;
