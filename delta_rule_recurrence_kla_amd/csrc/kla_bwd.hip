@@ -525,11 +525,40 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
   const float* S0 = states + (static_cast<size_t>(bh) * nc + c) * DK * DV;
   const float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
-  load_rows<MODE, DK, QP>(sQ, q, b, h, c, T, H);
-  load_rows<MODE, DK, QP>(sK, k, b, h, c, T, H);
-  for (int e = tid; e < BC * BC; e += NT) {
-    sM[e / BC][e % BC] = R[REC_M + e];
-    sPG[e / BC][e % BC] = R[REC_PG + e];
+  // query and key rows and the record's two matrices, in 16-byte loads
+  {
+    using E = typename LdsIn<MODE>::type;
+    constexpr int EV = 16 / sizeof(E), KV = DK / EV;  // elements per piece, pieces per row
+#pragma unroll
+    for (int x = 0; x < BC * KV / NT; ++x) {
+      const int e = tid + x * NT, rr = e / KV, pe = e % KV, t = c * BC + rr;
+      uint4 uq = {0u, 0u, 0u, 0u}, uk = {0u, 0u, 0u, 0u};
+      if (t < T) {
+        const size_t o = tok(b, t, T, H, h) * DK;
+        uq = reinterpret_cast<const uint4*>(static_cast<const E*>(q) + o)[pe];
+        uk = reinterpret_cast<const uint4*>(static_cast<const E*>(k) + o)[pe];
+      }
+      float fq[EV], fk[EV];
+      if constexpr (MODE == 0) {
+        row8(reinterpret_cast<const uint16_t*>(&uq), fq);
+        row8(reinterpret_cast<const uint16_t*>(&uk), fk);
+      } else {
+        fq[0] = __uint_as_float(uq.x); fq[1] = __uint_as_float(uq.y); fq[2] = __uint_as_float(uq.z); fq[3] = __uint_as_float(uq.w);
+        fk[0] = __uint_as_float(uk.x); fk[1] = __uint_as_float(uk.y); fk[2] = __uint_as_float(uk.z); fk[3] = __uint_as_float(uk.w);
+      }
+      for (int z = 0; z < EV; z += 4) {
+        *reinterpret_cast<float4*>(&sQ[rr][pe * EV + z]) = float4{fq[z], fq[z + 1], fq[z + 2], fq[z + 3]};
+        *reinterpret_cast<float4*>(&sK[rr][pe * EV + z]) = float4{fk[z], fk[z + 1], fk[z + 2], fk[z + 3]};
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < BC * BC / 4 / NT; ++x) {
+      const int e = tid + x * NT, rr = (4 * e) / BC, cc = (4 * e) % BC;
+      const float4 m = reinterpret_cast<const float4*>(R + REC_M)[e];
+      const float4 pg = reinterpret_cast<const float4*>(R + REC_PG)[e];
+      sM[rr][cc] = m.x; sM[rr][cc + 1] = m.y; sM[rr][cc + 2] = m.z; sM[rr][cc + 3] = m.w;
+      sPG[rr][cc] = pg.x; sPG[rr][cc + 1] = pg.y; sPG[rr][cc + 2] = pg.z; sPG[rr][cc + 3] = pg.w;
+    }
   }
   if (tid < BC) {
     sg[tid] = R[REC_G + tid];
