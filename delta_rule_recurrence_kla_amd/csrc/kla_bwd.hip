@@ -47,14 +47,6 @@ __device__ __forceinline__ size_t tok(int b, int t, int T, int H, int h) {
   return (static_cast<size_t>(b) * T + t) * H + h;
 }
 
-// Loads rows of a [B,T,H,D] input for the 64 tokens of chunk c into s[64][D + 1] (zeros past T).
-template <int MODE, int D, int P = D + 1>
-__device__ __forceinline__ void load_rows(float (*s)[P], const void* x, int b, int h, int c, int T, int H) {
-  for (int e = threadIdx.x; e < BC * D; e += blockDim.x) {
-    const int r = e / D, d = e % D, t = c * BC + r;
-    s[r][d] = t < T ? ldin<MODE>(x, tok(b, t, T, H, h) * D + d) : 0.f;
-  }
-}
 
 // Query and key rows in LDS keep the input's type: bf16 inputs stay bf16 (exact), which halves
 // their footprint.
@@ -78,13 +70,20 @@ __device__ __forceinline__ void row8(const float* p, float f[8]) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
+// Rows of a [B,T,H,D] input (in its own element type) for the 64 tokens of chunk c into s[64][P],
+// in 16-byte pieces, zeros past T; rows of s must start on 16-byte boundaries.
 template <int MODE, int D, int P, class E>
-__device__ __forceinline__ void load_rows_in(E (*s)[P], const void* x, int b, int h, int c, int T, int H) {
-  for (int e = threadIdx.x; e < BC * D; e += blockDim.x) {
-    const int r = e / D, d = e % D, t = c * BC + r;
-    s[r][d] = t < T ? static_cast<const E*>(x)[tok(b, t, T, H, h) * D + d] : E(0);
+__device__ __forceinline__ void load_rows_vec(E (*s)[P], const void* x, int b, int h, int c, int T, int H) {
+  constexpr int EV = 16 / sizeof(E), KV = D / EV;
+  static_assert((P * sizeof(E)) % 16 == 0, "16-byte rows");
+  for (int e = threadIdx.x; e < BC * KV; e += blockDim.x) {
+    const int rr = e / KV, pe = e % KV, t = c * BC + rr;
+    uint4 u = {0u, 0u, 0u, 0u};
+    if (t < T) u = reinterpret_cast<const uint4*>(static_cast<const E*>(x) + tok(b, t, T, H, h) * D)[pe];
+    *reinterpret_cast<uint4*>(&s[rr][pe * EV]) = u;
   }
 }
+
 
 template <int MODE, int DK>
 __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void* k, const float* log_alpha,
@@ -93,11 +92,13 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
   constexpr int AP = 68;  // pitch of A: 16-byte rows for vector reads
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   using E = typename LdsIn<MODE>::type;  // bf16 inputs stay bf16 in LDS (exact): three workgroups per CU
-  __shared__ E sQ[BC][DK + 2], sK[BC][DK + 2];
+  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows
+  __shared__ __align__(16) E sQ[BC][EP];
+  __shared__ __align__(16) E sK[BC][EP];
   __shared__ __align__(16) float sA[BC * AP];
   __shared__ float sla[BC], sg[BC], sb[BC];
-  load_rows_in<MODE, DK, DK + 2, E>(sQ, q, b, h, c, T, H);
-  load_rows_in<MODE, DK, DK + 2, E>(sK, k, b, h, c, T, H);
+  load_rows_vec<MODE, DK, EP, E>(sQ, q, b, h, c, T, H);
+  load_rows_vec<MODE, DK, EP, E>(sK, k, b, h, c, T, H);
   float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
   const int t = c * BC + tid;
   if (tid < BC) sla[tid] = t < T ? log_alpha[tok(b, t, T, H, h)] : 0.f;
@@ -310,12 +311,13 @@ __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const floa
                                                        int DV, int nc, float* vt, float* cq) {
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   using E = typename LdsIn<MODE>::type;
-  __shared__ E sQ[BC][DK + 2];
+  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows
+  __shared__ __align__(16) E sQ[BC][EP];
   __shared__ float sO[BC][128 + 1];  // dv <= 128
   __shared__ float sP[BC][MP];
   __shared__ float seg[BC];
   const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
-  load_rows_in<MODE, DK, DK + 2, E>(sQ, q, b, h, c, T, H);
+  load_rows_vec<MODE, DK, EP, E>(sQ, q, b, h, c, T, H);
   for (int e = tid; e < BC * DV; e += NT) {
     const int rr = e / DV, j = e % DV, t = c * BC + rr;
     sO[rr][j] = t < T ? dout[tok(b, t, T, H, h) * DV + j] : 0.f;
