@@ -508,7 +508,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __shared__ __align__(16) float sQ[BC][QP], sK[BC][QP];
   __shared__ float sM[BC][MP], sPG[BC][MP];
   __shared__ __align__(16) float sW[WN];
-  __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], sdg[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
+  __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
   __shared__ float seg[BC], sww[BC];  // e^{g}, e^{g_C - g}
   __shared__ float sgam;
   // column-block phase: 16 columns of each operand, stored column by column so that a
@@ -831,17 +831,22 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
       accK[4 * q4 + 3] = fmaf(a, kk.w, accK[4 * q4 + 3]);
     }
   }
-  if (tid < BC) {
+  if (tid < BC) {  // one wave: lane i is token i of the chunk
     const int i = tid, t = c * BC + i;
     float cs = 0.f;
     for (int j = 0; j < BC; ++j) cs += m1[j * MP + i];
-    float dg = srow[i] - cs + sdeg[i] * expf(sg[i]) - sdw[i] * expf(gC - sg[i]);
-    if (i == BC - 1) {
-      float a = 0.f;
-      for (int j = 0; j < BC; ++j) a = fmaf(sdw[j], expf(gC - sg[j]), a);
-      dg += a + sgam * expf(gC);
+    const float dww = sdw[i] * sww[i];
+    float tot = dww;  // sum over the chunk of dw . w, across the wave
+    for (int m = 1; m < BC; m <<= 1) tot += __shfl_xor(tot, m);
+    float dg = srow[i] - cs + sdeg[i] * seg[i] - dww;
+    if (i == BC - 1) dg += tot + sgam * expf(gC);
+    // dlog_alpha: the sum of dg over this token and the later ones in the chunk (a suffix scan)
+    float sfx = dg;
+    for (int m = 1; m < BC; m <<= 1) {
+      const float o = __shfl_down(sfx, m);
+      if (i + m < BC) sfx += o;
     }
-    sdg[i] = dg;
+    if (t < T) dla[tok(b, t, T, H, h)] = sfx;
     const float db = sdb[i], den = sden[i];
     const float et = t < T ? eta[tok(b, t, T, H, h)] : 0.f;
     float de = db, kc = 0.f;
@@ -853,12 +858,6 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     if (t < T) deta[tok(b, t, T, H, h)] = de;
   }
   __syncthreads();
-  if (tid < BC) {
-    const int i = tid, t = c * BC + i;
-    float a = 0.f;
-    for (int j = BC - 1; j >= i; --j) a += sdg[j];
-    if (t < T) dla[tok(b, t, T, H, h)] = a;
-  }
   // add the MFMA parts of dQ and dK (through LDS, in the row layout); m1 and m2 are free
   constexpr int CP = DK + 4;
   for (int pass = 0; pass < 2; ++pass) {
