@@ -1,4 +1,5 @@
-// Chunkwise backward of the KLA prefill (gradients for training), fp32 arithmetic.
+// Chunkwise backward of the KLA prefill (gradients for training), fp32 arithmetic: the vector
+// ALU and the fp32 MFMA (v_mfma_f32_16x16x4_f32, full fp32 products and accumulation).
 //
 // The forward of one 64-token chunk with start state S0 (UT form of the delta rule, the
 // chunkwise parallel algorithm that the KLA page trains with; KLA page, "Implementation"):
@@ -11,14 +12,15 @@
 //   states   forward walk over chunks per 16-column block of the state: every chunk-start S0
 //   dprep    per chunk: the terms of the reverse walk that do not depend on the carried
 //            gradient, P^T dO and Q^T (e^g . dO)
-//   dstates  reverse walk per 8-column block: every chunk-end gradient dS1, from
+//   dstates  reverse walk per 16-column block: every chunk-end gradient dS1, from
 //              dS0 = e^{g_C} dS1 + Q^T (e^g . dO) - K^T (e^g . dX),
 //              dX  = diag(beta) Minv^T dU,  dU = w . (K dS1) + P^T dO
 //   grads    per chunk, from S0 and dS1: dq, dk, dv, dlog_alpha, deta (the chunk-local
 //            products of the reverse pass, then a reverse cumulative sum of dg inside the chunk)
 // The columns of the state (the dv index) are independent in both walks, so a walk
-// workgroup owns 16 columns. Walk and grads workgroups have 512 threads, 8 per chunk row. A ragged last chunk is padded with identity steps
-// (k = q = v = 0, log_alpha = 0, eta = 0), which changes neither outputs nor gradients.
+// workgroup owns 16 columns. Walk and grads workgroups have 512 threads, 8 per chunk row. A
+// ragged last chunk is padded with identity steps (k = q = v = 0, log_alpha = 0, eta = 0),
+// which changes neither outputs nor gradients.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

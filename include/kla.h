@@ -158,8 +158,8 @@ kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, cons
  * passes no gradient to eta or through beta to k. The arithmetic is fp32; the
  * call takes a stream-ordered workspace of about B*H*ceil(T/64) * (34 KB +
  * 8*dk*dv + 256*dv bytes) (chunk records, every chunk-start state, every
- * chunk-end state gradient and a 64 x dv block) and frees it on the stream. T == 0 copies grad_final_state
- * (or zeros) into grad_init_state.
+ * chunk-end state gradient and a 64 x dv block) and frees it on the stream.
+ * T == 0 copies grad_final_state (or zeros) into grad_init_state.
  */
 kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
                          const void* v, const float* log_alpha, const float* eta, float eps,
