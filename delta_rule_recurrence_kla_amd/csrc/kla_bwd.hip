@@ -512,7 +512,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __shared__ __align__(16) float sW[WN];
   __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
   __shared__ float seg[BC], sww[BC];  // e^{g}, e^{g_C - g}
-  __shared__ float sgam;
+  __shared__ float sgp[BC];  // per-row parts of <dS1, S0>
   // column-block phase: 16 columns of each operand, stored column by column so that a
   // thread's run of rows (or of state rows) is one 16-byte read
   float* cS = sW;             // S0 [NJ][SP]
@@ -569,7 +569,6 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     sb[tid] = R[REC_B + tid];
     sden[tid] = R[REC_D + tid];
   }
-  if (tid == 0) sgam = 0.f;
   const int r = tid / TPRW, qd = tid % TPRW, j0 = qd * CPT, i0 = qd * IPT, d0 = qd * DQ;
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
   // Rank-16 updates on the fp32 MFMA: wave w owns row tile mt of the chunk and column tiles
@@ -738,7 +737,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   if (qd == 0) {
     sdw[r] = dw;
     sdeg[r] = deg;
-    atomicAdd(&sgam, gamp);
+    sgp[r] = gamp;
   }
   // dP into m1 and dT' into m2 from the MFMA tiles
   for (int u = 0; u < 2; ++u)
@@ -841,7 +840,9 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     float tot = dww;  // sum over the chunk of dw . w, across the wave
     for (int m = 1; m < BC; m <<= 1) tot += __shfl_xor(tot, m);
     float dg = srow[i] - cs + sdeg[i] * seg[i] - dww;
-    if (i == BC - 1) dg += tot + sgam * expf(gC);
+    float gam = sgp[i];  // <dS1, S0>, summed across the wave in a fixed order
+    for (int m = 1; m < BC; m <<= 1) gam += __shfl_xor(gam, m);
+    if (i == BC - 1) dg += tot + gam * expf(gC);
     // dlog_alpha: the sum of dg over this token and the later ones in the chunk (a suffix scan)
     float sfx = dg;
     for (int m = 1; m < BC; m <<= 1) {

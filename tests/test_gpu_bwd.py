@@ -113,3 +113,24 @@ def test_bwd_lm_layer_full_size_sampled_heads():
     log("case: bwd lm_layer_4k full size, heads (0,0) and (7,15)")
     wl = W.make_prefill("lm_layer_4k", seed=0, init_std=0.3)
     _run(wl, heads=[(0, 0), (7, 15)])
+
+
+def test_bwd_odd_batch_and_heads():
+    """B=3, H=5 (B*H not a multiple of the XCD count or of the column groups), bf16, dk=64, dv=128."""
+    log("case: bwd B=3 H=5 T=130 dk=64 dv=128 bf16")
+    wl = W.make_prefill("tiny_f32", seed=7, B=3, T=130, H=5, dk=64, dv=128, dtype="bf16", init_std=0.3)
+    _run(wl, heads=[(0, 0), (1, 3), (2, 4)])
+
+
+def test_bwd_repeat_calls_are_bit_identical():
+    """No atomics or order-dependent reductions: two calls on the same inputs agree bit for bit."""
+    log("case: bwd determinism, lm_layer shape with B=2")
+    wl = W.make_prefill("lm_layer_4k", seed=8, B=2, T=1000, init_std=0.3)
+    d_out, d_fin = W.make_bwd_grads(2, 1000, wl.H, wl.dk, wl.dv, seed=8)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    args = (q, k, v, la, eta, upload(d_out, "f32"))
+    g1 = kla.chunk_bwd(*args, eps=wl.eps, init_state=s0, grad_final_state=upload(d_fin, "f32"))
+    g2 = kla.chunk_bwd(*args, eps=wl.eps, init_state=s0, grad_final_state=upload(d_fin, "f32"))
+    torch.cuda.synchronize()
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
