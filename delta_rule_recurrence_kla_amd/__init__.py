@@ -17,8 +17,9 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["chunk_fwd", "chunk_fwd_psd", "decode_step", "loglinear_decode_step", "loglinear_fwd", "plan", "version", "last_error", "timing_enable",
-           "timing_collect", "lib_path", "load", "KLAError", "PATHS"]
+__all__ = ["chunk_fwd", "chunk_fwd_psd", "chunk_bwd", "decode_step", "loglinear_decode_step", "loglinear_fwd", "plan",
+           "version", "last_error", "timing_enable", "timing_select", "timing_collect", "workspace_trim", "lib_path",
+           "load", "KLAError", "PATHS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "lib", "libkla.so")
@@ -67,7 +68,8 @@ def load():
     lib.kla_loglinear_decode_step.argtypes = [I, I, P, P, P, P, P, P, F, P, P, I, I, I, I, I, I, P]
     lib.kla_loglinear_fwd.argtypes = [I, I, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, P]
     lib.kla_chunk_bwd.argtypes = [I, I, P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
-    for fn in ("kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
+    lib.kla_workspace_trim.argtypes = []
+    for fn in ("kla_workspace_trim", "kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
                "kla_decode_step_f32", "kla_decode_step_ex", "kla_loglinear_decode_step", "kla_loglinear_fwd",
                "kla_timing_enable",
                "kla_timing_select"):
@@ -118,6 +120,8 @@ def _need(t, name, shape, dtypes, device):
         raise ValueError(f"{name} must be contiguous")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.numel() and t.data_ptr() % 16:
+        raise ValueError(f"{name} must start on a 16-byte boundary (a view with a storage offset is not)")
 
 
 def chunk_fwd(q, k, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk: int = 64,
@@ -349,6 +353,11 @@ def plan(B: int, T: int, H: int, dk: int, dv: int, chunk: int = 64, path: str = 
     _check(lib.kla_plan(DTYPES[dtype], B, T, H, dk, dv, chunk, PATHS[path], segments, num_cus,
                         ctypes.byref(p), ctypes.byref(s), ctypes.byref(w)))
     return _PATH_NAMES[p.value], s.value, w.value
+
+
+def workspace_trim():
+    """Release the workspace the library's pool keeps reserved on the current device."""
+    _check(load().kla_workspace_trim())
 
 
 def timing_enable(enable: bool = True):

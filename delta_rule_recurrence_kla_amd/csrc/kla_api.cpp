@@ -66,28 +66,87 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
   // no system-scope fences around the stamps: they would add a cache flush to every launch
   hipError_t e = hipEventCreateWithFlags(&t.start, hipEventDisableSystemFence);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&t.stop, hipEventDisableSystemFence);
-  if (e != hipSuccess) return e;
-  g_launch_events = {t.start, t.stop};
-  e = launch();
-  g_launch_events = {};
-  if (e == hipSuccess) g_timing.rec.push_back(t);
+  if (e == hipSuccess) {
+    g_launch_events = {t.start, t.stop};
+    e = launch();
+    g_launch_events = {};
+  }
+  if (e == hipSuccess) {
+    g_timing.rec.push_back(t);
+  } else {  // the stamps of a launch that did not happen are never read: release them now
+    if (t.start) (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+  }
   return e;
 }
 
 // ---------------------------------------------------------------------------
-// device bookkeeping: keep freed workspace in the stream-ordered pool between calls
-std::once_flag g_pool_once[64];
+// workspace: the library's own stream-ordered pool, one per device
+//
+// Prefill and backward workspaces come from a memory pool the library creates on a
+// device's first call. Its release threshold is raised so that freed blocks stay
+// reserved for the next call instead of going back to the driver at each
+// synchronisation. The device's default pool, which other code in the process may
+// use, is never touched. kla_workspace_trim() hands the reserved blocks back.
+constexpr int kMaxDevices = 64;
+std::once_flag g_pool_once[kMaxDevices];
+hipMemPool_t g_pool[kMaxDevices] = {};
+hipError_t g_pool_err[kMaxDevices] = {};
 
-void keep_pool_warm() {
+hipError_t library_pool(hipMemPool_t* pool) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::call_once(g_pool_once[dev], [dev] {
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    hipError_t err = hipMemPoolCreate(&p, &props);
+    if (err == hipSuccess) {
       uint64_t thr = UINT64_MAX;
-      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+      err = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &thr);
+      if (err != hipSuccess) (void)hipMemPoolDestroy(p);
     }
+    if (err == hipSuccess) g_pool[dev] = p;
+    g_pool_err[dev] = err;
   });
+  if (!g_pool[dev]) return g_pool_err[dev] != hipSuccess ? g_pool_err[dev] : hipErrorNotInitialized;
+  *pool = g_pool[dev];
+  return hipSuccess;
+}
+
+// Stream-ordered workspace of `bytes` from the library pool; KLA_ERR_OOM (with the
+// message set) if it cannot be had. Nothing has been enqueued on failure.
+kla_status workspace_alloc(void** ws, size_t bytes, hipStream_t stream) {
+  *ws = nullptr;
+  if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
+    if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
+  }
+  hipMemPool_t pool = nullptr;
+  hipError_t e = library_pool(&pool);
+  if (e == hipSuccess) e = hipMallocFromPoolAsync(ws, bytes, pool, stream);
+  if (e != hipSuccess || !*ws) {
+    (void)hipGetLastError();
+    *ws = nullptr;
+    return fail(KLA_ERR_OOM, "workspace of %zu bytes from the library pool failed: %s", bytes, hipGetErrorString(e));
+  }
+  return KLA_OK;
+}
+
+// Every array argument must be 16-byte aligned: the kernels move rows, states and
+// gates with 16-byte vector and buffer accesses.
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+template <class... P>
+kla_status check_aligned(const char* names, P... ptrs) {
+  const void* list[] = {static_cast<const void*>(ptrs)...};
+  for (const void* p : list)
+    if (p && misaligned(p)) return fail(KLA_ERR_INVALID_ARG, "every array must be 16-byte aligned (%s)", names);
+  return KLA_OK;
 }
 
 int device_cus() {
@@ -193,10 +252,12 @@ kla_status hip_fail(hipError_t e, const char* what) {
   return fail(KLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
-                          const float* log_alpha, const float* eta, float eps, const float* init_state, float* out,
-                          float* final_state, int B, int T, int H, int dk, int dv, int chunk, kla_path path,
-                          int segments, hipStream_t stream, int lift = 0) {
+// Everything a prefill call checks before it touches HIP; on KLA_OK the call has work
+// to enqueue (T > 0) or has already handled T == 0 (`done` set).
+kla_status chunk_fwd_check(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* eta, const float* init_state, float* out,
+                           float* final_state, int B, int T, int H, int dk, int dv, int chunk, kla_path path,
+                           int segments) {
   kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
   if (st != KLA_OK) return st;
   if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
@@ -206,38 +267,32 @@ kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* 
   if (segments < 0) return fail(KLA_ERR_INVALID_ARG, "segments must be >= 0");
   if (T > 0 && (!q || !k || !v || !log_alpha || !eta || !out))
     return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta and out must be non-null when T > 0");
-  const size_t state_n = static_cast<size_t>(B) * H * dk * dv;
+  return check_aligned("q, k, v, log_alpha, eta, init_state, out, final_state", q, k, v, log_alpha, eta, init_state,
+                       out, final_state);
+}
 
-  if (T == 0) {
-    if (final_state && final_state != init_state) {
-      hipError_t e = timed("kla_copy_or_zero", stream, [&] { return kla::launch_copy_or_zero(init_state, final_state, state_n, stream); });
-      if (e != hipSuccess) return hip_fail(e, "launch");
-    }
-    return KLA_OK;
+// T == 0: final_state receives init_state (or zeros).
+kla_status chunk_fwd_empty(const float* init_state, float* final_state, size_t state_n, hipStream_t stream) {
+  if (final_state && final_state != init_state) {
+    hipError_t e = timed("kla_copy_or_zero", stream, [&] { return kla::launch_copy_or_zero(init_state, final_state, state_n, stream); });
+    if (e != hipSuccess) return hip_fail(e, "launch");
   }
+  return KLA_OK;
+}
 
-  if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
-    if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
-  }
-
-  const Plan p = make_plan(dtype, B, T, H, dk, dv, path, segments, device_cus());
+// Enqueues prep and the state walk(s) of plan `p` with the workspace at `base`
+// (p.total bytes, 256-byte aligned, owned by the caller of this function).
+hipError_t chunk_fwd_enqueue(const Plan& p, kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                             const void* v, const float* log_alpha, const float* eta, float eps,
+                             const float* init_state, float* out, float* final_state, int B, int T, int H, int dk,
+                             int dv, int lift, uint8_t* base, hipStream_t stream) {
   const kla::Dims d{B, T, H, dk, dv, (T + kChunk - 1) / kChunk, lift};
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
-
-  keep_pool_warm();
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, p.total, stream);
-  if (e != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return fail(KLA_ERR_OOM, "hipMallocAsync(%zu bytes) failed: %s", p.total, hipGetErrorString(e));
-  }
-  uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* rec = base + p.rec_off;
   float* maps = reinterpret_cast<float*>(base + p.maps_off);
   float* starts = reinterpret_cast<float*>(base + p.starts_off);
-
   const int direct = beta_mode == KLA_BETA_DIRECT;
-  e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
+  hipError_t e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
   if (e == hipSuccess) {
     if (p.path == KLA_PATH_SEQUENTIAL) {
       e = timed("kla_state_seq", stream, [&] {
@@ -255,6 +310,24 @@ kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* 
         });
     }
   }
+  return e;
+}
+
+kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* eta, float eps, const float* init_state, float* out,
+                          float* final_state, int B, int T, int H, int dk, int dv, int chunk, kla_path path,
+                          int segments, hipStream_t stream, int lift = 0) {
+  kla_status st = chunk_fwd_check(dtype, beta_mode, q, k, v, log_alpha, eta, init_state, out, final_state, B, T, H,
+                                  dk, dv, chunk, path, segments);
+  if (st != KLA_OK) return st;
+  if (T == 0) return chunk_fwd_empty(init_state, final_state, static_cast<size_t>(B) * H * dk * dv, stream);
+
+  const Plan p = make_plan(dtype, B, T, H, dk, dv, path, segments, device_cus());
+  void* ws = nullptr;
+  st = workspace_alloc(&ws, p.total, stream);
+  if (st != KLA_OK) return st;
+  hipError_t e = chunk_fwd_enqueue(p, dtype, beta_mode, q, k, v, log_alpha, eta, eps, init_state, out, final_state,
+                                   B, T, H, dk, dv, lift, static_cast<uint8_t*>(ws), stream);
   hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
@@ -275,6 +348,8 @@ kla_status decode_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, 
   if (N == 0) return KLA_OK;
   if (!q || !k || !v || !log_alpha || !eta || !state || !out)
     return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta, state and out must be non-null");
+  kla_status st = check_aligned("q, k, v, log_alpha, eta, state, out", q, k, v, log_alpha, eta, state, out);
+  if (st != KLA_OK) return st;
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   hipError_t e = timed("kla_decode", stream, [&] {
     return kla::launch_decode(mode, N, H, dk, dv, q, k, v, log_alpha, eta, eps, beta_mode == KLA_BETA_DIRECT, state,
@@ -367,6 +442,8 @@ kla_status kla_loglinear_decode_step(kla_dtype dtype, kla_beta_mode beta_mode, c
   if (N == 0) return KLA_OK;
   if (!q || !k || !v || !log_alpha || !eta || !lam || !states || !out)
     return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta, lam, states and out must be non-null");
+  kla_status st = check_aligned("q, k, v, log_alpha, eta, lam, states, out", q, k, v, log_alpha, eta, lam, states, out);
+  if (st != KLA_OK) return st;
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   hipError_t e = timed("kla_loglinear_decode", stream, [&] {
     return kla::launch_loglinear_decode(mode, N, H, dk, dv, q, k, v, log_alpha, eta, lam, eps,
@@ -390,6 +467,8 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
   if (T == 0) return KLA_OK;
   if (!q || !k || !v || !log_alpha || !eta || !lam || !out)
     return fail(KLA_ERR_INVALID_ARG, "q, k, v, log_alpha, eta, lam and out must be non-null when T > 0");
+  st = check_aligned("q, k, v, log_alpha, eta, lam, out", q, k, v, log_alpha, eta, lam, out);
+  if (st != KLA_OK) return st;
   const int nc = (T + kChunk - 1) / kChunk;
   kla::Dims d{B, T, H, dk, dv, nc};
   d.full_rec = 1;
@@ -410,16 +489,10 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
     ends_floats += static_cast<long long>(bh) * nleft[nscale] * dk * dv;
   }
   const size_t ends_bytes = align256(static_cast<size_t>(ends_floats) * 4);
-  if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
-    if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
-  }
-  keep_pool_warm();
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, rec_bytes + ends_bytes, stream);
-  if (e != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return fail(KLA_ERR_OOM, "hipMallocAsync(%zu bytes) failed: %s", rec_bytes + ends_bytes, hipGetErrorString(e));
-  }
+  st = workspace_alloc(&ws, rec_bytes + ends_bytes, stream);
+  if (st != KLA_OK) return st;
+  hipError_t e = hipSuccess;
   uint8_t* rec = static_cast<uint8_t*>(ws);
   float* ends = reinterpret_cast<float*>(rec + rec_bytes);
   const int direct = beta_mode == KLA_BETA_DIRECT;
@@ -458,6 +531,10 @@ kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q
                 !grad_log_alpha || !grad_eta))
     return fail(KLA_ERR_INVALID_ARG,
                 "q, k, v, log_alpha, eta, grad_out and grad_q .. grad_eta must be non-null when T > 0");
+  st = check_aligned("q, k, v, log_alpha, eta, init_state, grad_out, grad_final_state, grad_q .. grad_init_state", q,
+                     k, v, log_alpha, eta, init_state, grad_out, grad_final_state, grad_q, grad_k, grad_v,
+                     grad_log_alpha, grad_eta, grad_init_state);
+  if (st != KLA_OK) return st;
   const size_t state_n = static_cast<size_t>(B) * H * dk * dv;
   if (T == 0) {  // the start state's gradient is the end state's
     if (grad_init_state && grad_init_state != grad_final_state) {
@@ -468,19 +545,13 @@ kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q
     }
     return KLA_OK;
   }
-  if (const char* f = std::getenv("KLA_TEST_FAIL_ALLOC")) {
-    if (f[0] == '1') return fail(KLA_ERR_OOM, "workspace allocation failed (forced by KLA_TEST_FAIL_ALLOC)");
-  }
   const int nc = (T + kChunk - 1) / kChunk;
   const size_t nch = static_cast<size_t>(B) * H * nc;
   const size_t bytes = kla::bwd_workspace_bytes(B, T, H, dk, dv);
-  keep_pool_warm();
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, stream);
-  if (e != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return fail(KLA_ERR_OOM, "hipMallocAsync(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
-  }
+  st = workspace_alloc(&ws, bytes, stream);
+  if (st != KLA_OK) return st;
+  hipError_t e = hipSuccess;
   kla::BwdArgs a{};
   a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.nc = nc;
   a.direct = beta_mode == KLA_BETA_DIRECT;
@@ -507,6 +578,14 @@ kla_status kla_decode_step_ex(kla_dtype dtype, kla_beta_mode beta_mode, const vo
                               const float* log_alpha, const float* eta, float eps, float* state, float* out, int N,
                               int H, int dk, int dv, hipStream_t stream) {
   return decode_impl(dtype, beta_mode, q, k, v, log_alpha, eta, eps, state, out, N, H, dk, dv, stream);
+}
+
+kla_status kla_workspace_trim(void) {
+  hipMemPool_t pool = nullptr;
+  hipError_t e = library_pool(&pool);
+  if (e == hipSuccess) e = hipMemPoolTrimTo(pool, 0);
+  if (e != hipSuccess) return hip_fail(e, "trimming the workspace pool");
+  return KLA_OK;
 }
 
 const char* kla_last_error(void) { return g_err.c_str(); }

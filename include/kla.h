@@ -33,9 +33,14 @@
  *  - Supported sizes: dk in {64, 128, 256}, dv in {64, 128}, chunk == 64.
  *    The fp32 prefill entry points support dk in {64, 128}. Other sizes give
  *    KLA_ERR_UNSUPPORTED. T need not be a multiple of the chunk.
- *  - Calls on different streams may run concurrently; the library holds no
- *    mutable global state apart from the per-thread error text and the
- *    per-thread timing record.
+ *  - Every array pointer must be 16-byte aligned (the kernels move rows,
+ *    states and gates with 16-byte accesses); a misaligned one gives
+ *    KLA_ERR_INVALID_ARG before anything is enqueued.
+ *  - Calls on different streams may run concurrently. The library's mutable
+ *    global state is the per-thread error text, the per-thread timing record,
+ *    and one workspace memory pool per device (see kla_workspace_trim); it
+ *    never changes the device's default memory pool or any other setting of
+ *    the process.
  */
 #ifndef KLA_H_
 #define KLA_H_
@@ -55,7 +60,18 @@ typedef enum {
   KLA_ERR_OOM = 4          /* the stream-ordered workspace allocation failed */
 } kla_status;
 
-typedef enum { KLA_DTYPE_BF16 = 0, KLA_DTYPE_F32 = 1 } kla_dtype;
+/*
+ * The *_RANGE_MIN / *_RANGE_MAX members of the enums below are not valid arguments.
+ * They make every int a value of the enum type, so that whatever int a caller passes
+ * is read by the library as it is (in C++ an out-of-range value of an enum without
+ * them cannot be read safely) and rejected by validation as KLA_ERR_INVALID_ARG.
+ */
+typedef enum {
+  KLA_DTYPE_BF16 = 0,
+  KLA_DTYPE_F32 = 1,
+  KLA_DTYPE_RANGE_MIN = -2147483647 - 1,
+  KLA_DTYPE_RANGE_MAX = 2147483647
+} kla_dtype;
 
 /*
  * Write strength beta_t of each token's update.
@@ -67,13 +83,17 @@ typedef enum { KLA_DTYPE_BF16 = 0, KLA_DTYPE_F32 = 1 } kla_dtype;
  */
 typedef enum {
   KLA_BETA_KACZMARZ = 0,
-  KLA_BETA_DIRECT = 1
+  KLA_BETA_DIRECT = 1,
+  KLA_BETA_RANGE_MIN = -2147483647 - 1,
+  KLA_BETA_RANGE_MAX = 2147483647
 } kla_beta_mode;
 
 typedef enum {
   KLA_PATH_AUTO = 0,       /* let the library choose */
   KLA_PATH_SEQUENTIAL = 1, /* one walk over all chunks per (b, h, 64 dv columns) */
-  KLA_PATH_SCAN = 2        /* segments composed by an associative scan over affine chunk maps */
+  KLA_PATH_SCAN = 2,       /* segments composed by an associative scan over affine chunk maps */
+  KLA_PATH_RANGE_MIN = -2147483647 - 1,
+  KLA_PATH_RANGE_MAX = 2147483647
 } kla_path;
 
 /*
@@ -89,8 +109,9 @@ typedef enum {
  *   out            fp32 [B,T,H,dv] (required unless T == 0)
  *   final_state    fp32 [B,H,dk,dv], or NULL to skip; may alias init_state
  *   B, T, H        sizes (B, H >= 1; T >= 0); dk, dv, chunk as supported
- * The workspace (about 33 KB per chunk per head) is taken from the device's
- * stream-ordered pool on `stream` and released on it before return.
+ * The workspace (13 KB per chunk per head for bf16 with dk <= 128, 33 KB
+ * otherwise, plus the scan's segment maps) is taken from the library's
+ * workspace pool, stream-ordered on `stream`, and released on it before return.
  * With T == 0, final_state receives init_state (or zeros) and out is untouched.
  */
 kla_status kla_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -156,7 +177,7 @@ kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, cons
  * (NULL: zero), beta_mode and sizes are as for kla_chunk_fwd_ex; dk must be 64
  * or 128. In Kaczmarz mode a token with ||k||^2 + eps == 0 has beta = 0 and
  * passes no gradient to eta or through beta to k. The arithmetic is fp32; the
- * call takes a stream-ordered workspace of about B*H*ceil(T/64) * (34 KB +
+ * call takes a stream-ordered workspace from the library's pool of about B*H*ceil(T/64) * (34 KB +
  * 8*dk*dv + 256*dv bytes) (chunk records, every chunk-start state, every
  * chunk-end state gradient and a 64 x dv block) and frees it on the stream.
  * T == 0 copies grad_final_state (or zeros) into grad_init_state.
@@ -244,12 +265,25 @@ kla_status kla_loglinear_decode_step(kla_dtype dtype, kla_beta_mode beta_mode, c
  *   out      fp32 [B,T,H,dv]
  *   levels   L, 1..31, with T <= 2^(L-1), else KLA_ERR_INVALID_ARG
  * The workspace (the chunk records and the left half-blocks' end states) comes from the
- * device's stream-ordered pool on `stream`, as for kla_chunk_fwd.
+ * library's workspace pool on `stream`, as for kla_chunk_fwd.
  */
 kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
                              const void* v, const float* log_alpha, const float* eta, const float* lam,
                              float eps, float* out, int B, int T, int H, int dk, int dv, int levels,
                              int chunk, hipStream_t stream);
+
+/*
+ * Workspace pool. The prefill, log-linear prefill and backward calls take their
+ * workspace from a stream-ordered memory pool that the library creates for a
+ * device on its first such call there (hipMemPoolCreate, never the device's
+ * default pool). Freed workspace stays reserved in that pool for later calls, so
+ * a call does not map fresh memory each time; the pool therefore holds as much
+ * device memory as the largest concurrent set of calls has needed.
+ * kla_workspace_trim() releases every reserved block of the current device's
+ * pool that no enqueued call still uses (hipMemPoolTrimTo). Returns KLA_ERR_HIP
+ * if the pool cannot be created or trimmed.
+ */
+kla_status kla_workspace_trim(void);
 
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 const char* kla_last_error(void);

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
               "kla_loglinear_fwd", "kla_chunk_bwd",
               "kla_decode_step", "kla_decode_step_ex",
               "kla_decode_step_f32", "kla_plan", "kla_last_error", "kla_version",
-              "kla_timing_enable", "kla_timing_collect", "kla_timing_select"):
+              "kla_timing_enable", "kla_timing_collect", "kla_timing_select", "kla_workspace_trim"):
         assert n in names
 
 
@@ -219,3 +219,40 @@ def test_bwd_validation(kw, status):
 def test_bwd_zero_tokens_without_start_gradient_is_a_no_op():
     lib = kla.load()
     assert _bwd(lib, q=None, dout=None, gq=None, T=0) == 0
+
+
+MIS = ctypes.c_void_p(0x1008)  # 8-byte aligned only: rejected before any HIP call
+
+
+@pytest.mark.parametrize("call", [
+    lambda lib: lib.kla_chunk_fwd_ex(0, 0, MIS, FAKE, FAKE, FAKE, FAKE, 1e-6, None, FAKE, None, 1, 64, 1, 64, 64, 64,
+                                     0, 0, None),
+    lambda lib: lib.kla_chunk_fwd_ex(0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, MIS, FAKE, None, 1, 64, 1, 64, 64, 64,
+                                     0, 0, None),
+    lambda lib: lib.kla_chunk_fwd_ex(1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, None, FAKE, MIS, 1, 64, 1, 64, 64, 64,
+                                     0, 0, None),
+    lambda lib: lib.kla_chunk_fwd_psd(FAKE, MIS, FAKE, FAKE, FAKE, 1e-6, None, FAKE, None, 1, 64, 1, 16, 64, 64, 0, 0,
+                                      None),
+    lambda lib: lib.kla_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, MIS, FAKE, 4, 2, 128, 128, None),
+    lambda lib: lib.kla_decode_step_f32(FAKE, FAKE, FAKE, MIS, FAKE, 1e-6, FAKE, FAKE, 4, 2, 128, 128, None),
+    lambda lib: lib.kla_loglinear_decode_step(0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, MIS, 1e-6, FAKE, FAKE, 2, 2, 128,
+                                              128, 16, 5, None),
+    lambda lib: lib.kla_loglinear_fwd(0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, MIS, 1, 64, 1, 64, 64, 8, 64,
+                                      None),
+    lambda lib: lib.kla_chunk_bwd(0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, None, FAKE, None, FAKE, FAKE, FAKE, MIS,
+                                  FAKE, None, 1, 64, 1, 64, 64, 64, None),
+])
+def test_misaligned_arrays_are_rejected(call):
+    """kla.h: every array pointer is 16-byte aligned; a view with a storage offset is refused
+    on the host with KLA_ERR_INVALID_ARG, before anything is enqueued."""
+    lib = kla.load()
+    assert call(lib) == 1
+    assert "16-byte" in kla.last_error()
+
+
+def test_binding_refuses_offset_views():
+    torch = pytest.importorskip("torch")
+    base = torch.zeros(16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="16-byte"):
+        kla._need(base[1:9], "x", (8,), (torch.float32,), base.device)
+    kla._need(base[4:12], "x", (8,), (torch.float32,), base.device)  # 16 bytes in: accepted
