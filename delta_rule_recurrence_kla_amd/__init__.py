@@ -17,7 +17,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["chunk_fwd", "chunk_fwd_psd", "chunk_bwd", "decode_step", "loglinear_decode_step", "loglinear_fwd", "plan",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_psd", "chunk_bwd", "decode_step", "loglinear_decode_step", "loglinear_fwd", "plan",
            "version", "last_error", "timing_enable", "timing_select", "timing_collect", "workspace_trim", "lib_path",
            "load", "KLAError", "PATHS"]
 
@@ -60,6 +60,7 @@ def load():
     lib.kla_chunk_fwd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_f32.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_ex.argtypes = [I, I, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.kla_chunk_fwd_noalloc.argtypes = [I, I, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
     lib.kla_chunk_fwd_psd.argtypes = [P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, I, P]
     lib.kla_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(S)]
     lib.kla_decode_step.argtypes = [P, P, P, P, P, F, P, P, I, I, I, I, P]
@@ -69,7 +70,7 @@ def load():
     lib.kla_loglinear_fwd.argtypes = [I, I, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, P]
     lib.kla_chunk_bwd.argtypes = [I, I, P, P, P, P, P, F, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
     lib.kla_workspace_trim.argtypes = []
-    for fn in ("kla_workspace_trim", "kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
+    for fn in ("kla_workspace_trim", "kla_chunk_fwd_noalloc", "kla_chunk_fwd", "kla_chunk_fwd_f32", "kla_chunk_fwd_ex", "kla_chunk_fwd_psd", "kla_plan", "kla_decode_step",
                "kla_decode_step_f32", "kla_decode_step_ex", "kla_loglinear_decode_step", "kla_loglinear_fwd",
                "kla_timing_enable",
                "kla_timing_select"):
@@ -164,6 +165,39 @@ def chunk_fwd(q, k, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk
                               _ptr(init_state), _ptr(out), _ptr(final_state), B, T, H, dk, dv, chunk,
                               PATHS[path], int(segments), _stream(stream))
     _check(st)
+    return out, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, eta, eps: float = 1e-6, init_state=None, chunk: int = 64,
+                      path: str = "auto", segments: int = 0, out=None, final_state=None, stream=None,
+                      beta_mode: str = "kaczmarz"):
+    """chunk_fwd through kla_chunk_fwd_noalloc: the workspace is the library's static device
+    scratch buffer, so the call allocates no device memory (out and final_state must be given
+    to avoid the binding's own allocations). Same results as chunk_fwd."""
+    import torch
+    lib = load()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dtype = {torch.bfloat16: 0, torch.float32: 1}.get(q.dtype)
+    if dtype is None:
+        raise TypeError("q, k, v must be bfloat16 or float32")
+    for t, n, shp in ((q, "q", (B, T, H, dk)), (k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv))):
+        _need(t, n, shp, (q.dtype,), dev)
+    _need(log_alpha, "log_alpha", (B, T, H), (torch.float32,), dev)
+    _need(eta, "eta", (B, T, H), (torch.float32,), dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (B, H, dk, dv), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, T, H, dv), (torch.float32,), dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (B, H, dk, dv), (torch.float32,), dev)
+    if path not in PATHS or beta_mode not in BETA_MODES:
+        raise ValueError("unknown path or beta_mode")
+    _check(lib.kla_chunk_fwd_noalloc(dtype, BETA_MODES[beta_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                     _ptr(eta), float(eps), _ptr(init_state), _ptr(out), _ptr(final_state), B, T, H,
+                                     dk, dv, chunk, PATHS[path], int(segments), _stream(stream)))
     return out, final_state
 
 

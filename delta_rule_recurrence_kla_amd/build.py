@@ -24,7 +24,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["kla_prep.hip", "kla_state.hip", "kla_state_dma.hip", "kla_decode.hip", "kla_loglinear.hip", "kla_bwd.hip",
-           "kla_api.cpp"]
+           "kla_scratch.hip", "kla_api.cpp"]
 # MFMA results go to ordinary VGPRs (-amdgpu-mfma-vgpr-form) rather than accumulation
 # registers: every accumulator here is read back by vector instructions (splits, scalings,
 # stores), and with the accumulation-register form each such read costs a v_accvgpr_read

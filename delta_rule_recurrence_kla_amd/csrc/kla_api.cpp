@@ -385,6 +385,31 @@ kla_status kla_chunk_fwd_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void
                         chunk, path, segments, stream);
 }
 
+kla_status kla_chunk_fwd_noalloc(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                                 const void* v, const float* log_alpha, const float* eta, float eps,
+                                 const float* init_state, float* out, float* final_state, int B, int T, int H, int dk,
+                                 int dv, int chunk, kla_path path, int segments, hipStream_t stream) {
+  kla_status st = chunk_fwd_check(dtype, beta_mode, q, k, v, log_alpha, eta, init_state, out, final_state, B, T, H,
+                                  dk, dv, chunk, path, segments);
+  if (st != KLA_OK) return st;
+  if (T == 0) return chunk_fwd_empty(init_state, final_state, static_cast<size_t>(B) * H * dk * dv, stream);
+  const Plan p = make_plan(dtype, B, T, H, dk, dv, path, segments, device_cus());
+  if (p.total > static_cast<size_t>(KLA_NOALLOC_SCRATCH_BYTES))
+    return fail(KLA_ERR_UNSUPPORTED,
+                "the workspace of this call (%zu bytes) exceeds the static scratch buffer of kla_chunk_fwd_noalloc "
+                "(%zu bytes); use kla_chunk_fwd_ex, or fewer tokens or heads per call",
+                p.total, static_cast<size_t>(KLA_NOALLOC_SCRATCH_BYTES));
+  void* base = nullptr;
+  size_t cap = 0;
+  hipError_t e = kla::scratch_buffer(&base, &cap);
+  if (e != hipSuccess) return hip_fail(e, "device address of the scratch buffer");
+  if (cap < p.total) return fail(KLA_ERR_UNSUPPORTED, "scratch buffer of %zu bytes too small for %zu", cap, p.total);
+  e = chunk_fwd_enqueue(p, dtype, beta_mode, q, k, v, log_alpha, eta, eps, init_state, out, final_state, B, T, H, dk,
+                        dv, 0, static_cast<uint8_t*>(base), stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return KLA_OK;
+}
+
 kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, const float* log_alpha,
                              const float* eta, float eps, const float* init_state, float* out, float* final_state,
                              int B, int T, int H, int p, int dv, int chunk, kla_path path, int segments,

@@ -93,6 +93,10 @@ hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const 
                                   int nright, const float* ends, int nleft, const float* lam, int L, int level,
                                   float* out, hipStream_t stream);
 
+// Device address and size of the static scratch buffer of kla_chunk_fwd_noalloc on the
+// current device (kla_scratch.hip); the address is looked up once per device.
+hipError_t scratch_buffer(void** addr, size_t* bytes);
+
 // Copy (or zero when src is null) n floats; used for T == 0 and as a graph-safe fill.
 hipError_t launch_copy_or_zero(const float* src, float* dst, size_t n, hipStream_t stream);
 

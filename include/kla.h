@@ -139,6 +139,30 @@ kla_status kla_chunk_fwd_ex(kla_dtype dtype, kla_beta_mode beta_mode, const void
                             hipStream_t stream);
 
 /*
+ * kla_chunk_fwd_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, kernels and results (bit for bit) as kla_chunk_fwd_ex; the workspace is
+ * a static device buffer of KLA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends, instead of memory from the workspace pool.
+ *  - A call whose workspace (kla_plan's workspace_bytes) exceeds the buffer returns
+ *    KLA_ERR_UNSUPPORTED before anything is enqueued. 128 MiB holds, e.g., the chunk
+ *    records of B*H = 128 heads x 4096 tokens at dk = dv = 128 in bf16 (102 MiB).
+ *  - The call makes no allocation (no hipMalloc, hipMallocAsync or hipFree) while the
+ *    timing hook is off (its default); with the hook on, it creates HIP events.
+ *  - Every call on one GPU uses that GPU's one buffer, which keeps the last call's
+ *    contents. Calls that may overlap on one GPU (different streams without ordering
+ *    between them) race on it; calls ordered on one stream do not. No part of the
+ *    buffer needs clearing: each call writes every byte it reads before reading it.
+ */
+#define KLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+kla_status kla_chunk_fwd_noalloc(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
+                                 const void* v, const float* log_alpha, const float* eta, float eps,
+                                 const float* init_state, float* out, float* final_state, int B, int T,
+                                 int H, int dk, int dv, int chunk, kla_path path, int segments,
+                                 hipStream_t stream);
+
+/*
  * Prefill with the rank-one PSD lift fused into the kernels (KATA page, section
  * 2.2, "Capacity theory": the feature psi(u) = vec(u u^T), whose inner products
  * are squared inner products of u). The caller passes the p-wide vectors u for

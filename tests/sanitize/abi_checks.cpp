@@ -55,6 +55,12 @@ int main() {
         KLA_ERR_UNSUPPORTED);
   CHECK(kla_chunk_fwd_psd(P, P, P, F, F, 1e-6f, nullptr, F, nullptr, 1, 64, 1, 0, 64, 64, KLA_PATH_AUTO, 0, nullptr) ==
         KLA_ERR_INVALID_ARG);
+  CHECK(kla_chunk_fwd_noalloc(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, P, P, P, F, F, 1e-6f, nullptr, F, nullptr, 1, 64, 1, 96,
+                              64, 64, KLA_PATH_AUTO, 0, nullptr) == KLA_ERR_UNSUPPORTED);
+  // a workspace beyond the static scratch buffer is refused before anything is enqueued
+  CHECK(kla_chunk_fwd_noalloc(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, P, P, P, F, F, 1e-6f, nullptr, F, nullptr, 64, 8192, 16,
+                              128, 128, 64, KLA_PATH_SEQUENTIAL, 0, nullptr) == KLA_ERR_UNSUPPORTED);
+  CHECK(std::strstr(kla_last_error(), "scratch") != nullptr);
 
   // backward
   CHECK(kla_chunk_bwd(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, P, P, P, F, F, 1e-6f, nullptr, F, nullptr, F, F, F, F, F, nullptr,
