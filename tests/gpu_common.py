@@ -37,3 +37,16 @@ def assert_close(got, ref, tol, what):
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     assert e <= tol, f"{what}: max|err|/RMS = {e:.3e} > {tol:.1e}"
     return e
+
+
+def hip_runtime():
+    """ctypes handle of the HIP runtime loaded in this process (the one torch and libkla use).
+    A plain CDLL("libamdhip64.so") may load a second, separate copy of the runtime."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    for line in open("/proc/self/maps"):
+        path = line.split()[-1] if len(line.split()) >= 6 else ""
+        if "libamdhip64.so" in path:
+            return ctypes.CDLL(path)
+    raise RuntimeError("no HIP runtime loaded")

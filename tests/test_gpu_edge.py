@@ -22,7 +22,7 @@ import pytest
 
 import workloads as W
 from oracle import cref, kla_bwd, kla_ref, loglinear
-from tests.gpu_common import TOL, assert_close, err_over_rms, upload, upload_prefill
+from tests.gpu_common import TOL, assert_close, err_over_rms, hip_runtime, upload, upload_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -195,7 +195,7 @@ def test_full_long_131k_lm_layer_distributions():
 # ---------------------------------------------------------------------------
 # the boundary leaves the process's memory settings alone
 def _default_pool_threshold():
-    hip = ctypes.CDLL("libamdhip64.so")
+    hip = hip_runtime()
     pool = ctypes.c_void_p()
     assert hip.hipDeviceGetDefaultMemPool(ctypes.byref(pool), torch.cuda.current_device()) == 0
     val = ctypes.c_uint64()
