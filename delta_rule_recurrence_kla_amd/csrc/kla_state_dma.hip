@@ -1,31 +1,35 @@
-// Inter-chunk state and output kernel, bf16 inputs, dk in {64, 128}: the DMA-fed variant.
+// Inter-chunk state kernels, bf16 inputs, dk in {64, 128}: the DMA-fed variants.
 //
 // Same mathematics as state_kernel in kla_state.hip (see there; KLA page, "KLA update
 // rule" and "Implementation"):
 //   R  = V - diag(e^g) K S,   U = T' R,   O = diag(e^g) Q S + P U,
-//   S <- e^{g_C} S + K^T diag(e^{g_C - g}) U,
-// with one workgroup per (b, h, 64 state columns), one wave per 16 columns, and the
-// state held in MFMA accumulator registers for the whole walk over the chunks.
+// with one workgroup per (b, h, 64 state columns), 16 columns per wave, and the state held in
+// MFMA accumulator registers for the whole walk over the chunks. Two kernels:
+//  * state_map_kernel walks a segment without outputs on the augmented state [I | 0] and
+//    leaves the segment's affine map [M | N] (the scan's first phase): one compute wave per
+//    16 columns and a copy wave;
+//  * state_walk_kernel walks with outputs (the sequential path, and the scan's walk from
+//    every segment's start): per 16 columns one wave runs the recurrence and another the
+//    output products, with a copy wave (see the comment above it).
 //
-// What differs is how a chunk's operands reach LDS and registers:
-//  * every input of chunk c+1 (rows of K, Q, V and the chunk record) is copied into
-//    the other half of a double-buffered LDS area by buffer_load ... lds while chunk
-//    c is computed, so no registers hold prefetched data and a chunk needs a single
-//    workgroup barrier (plus the one that publishes P, below);
-//  * a fifth wave issues all of those copies. A wave cannot issue past a memory
-//    instruction that the CU has not yet accepted, and in this kernel a 1 KB copy is
-//    accepted only every 50 or so cycles: 53 copies per chunk held each compute wave for
-//    about a thousand cycles when the four shared them. The copy wave takes that wait
-//    instead, and the compute waves issue no memory instructions but their 16-byte output
-//    stores (which they never wait for);
+// What both share is how a chunk's operands reach LDS and registers:
+//  * every input of chunk c+1 (rows of K, Q, V and the chunk record) is copied into LDS by
+//    buffer_load ... lds while chunk c is computed (double-buffered), so no registers hold
+//    prefetched data;
+//  * a copy wave issues those copies. A wave cannot issue past a memory instruction that the
+//    CU has not yet accepted, and in these kernels a 1 KB copy is accepted only every 50 or
+//    so cycles: 53 copies per chunk held each compute wave for about a thousand cycles when
+//    the compute waves shared them. The copy wave takes that wait instead, and the compute
+//    waves issue no memory instructions but their 16-byte output stores (which they never
+//    wait for);
 //  * rows land in the swizzled layout of kla_device.h: the DMA picks, per lane, the
 //    source piece that belongs at its fixed destination;
 //  * K^T operands and the accumulator-layout view of V come from transposed LDS reads
 //    (ds_read_b64_tr_b16) of the row-major rows, so no transposed copies are built;
-//  * P = tril(e^{g_r - g_i} Q K^T) is formed here from the Q and K rows already in LDS
-//    (twelve 16 x 16 tiles, three per wave, shared through LDS), so the chunk record
-//    carries only T' (without its zero quadrant) and the gates: 12.75 KB instead of
-//    33.5 KB per chunk, the larger part of what the kernel streams in;
+//  * P = tril(e^{g_r - g_i} Q K^T) is formed from the Q and K rows already in LDS (twelve
+//    16 x 16 tiles, three per slice, shared through LDS), so the chunk record carries only T'
+//    (without its zero quadrant) and the gates: 12.75 KB instead of 33.5 KB per chunk, the
+//    larger part of what the kernel streams in;
 //  * rows of every 64-row tile (tokens, and state rows) are taken in the permuted order
 //    tok(m, r) = 32(m >> 1) + 8(r >> 2) + 4(m & 1) + (r & 3) for MFMA tile m, tile row r.
 //    An accumulator pair (tiles 2a, 2a + 1) then gives each lane eight consecutive
@@ -83,10 +87,10 @@ __device__ __forceinline__ void decode_wg_dma(int L, int ncg, int nunits, int& c
 
 }  // namespace
 
-constexpr int DMA_THREADS = 320;  // four compute waves and the copy wave
+constexpr int MAP_THREADS = 320;  // four compute waves and the copy wave
 
-template <int DK, bool WITH_OUT, bool AUG>
-__global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) {
+template <int DK>
+__global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) {
   using TR = Tr<MODE_BF16>;
   constexpr int NCOLS = 64;
   constexpr int KRB = DK * 2;                 // bytes of a key row
@@ -95,19 +99,17 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
   constexpr int VBYTES = CHUNK * VRB;
   constexpr int RECB = 13 * 1024;             // compact record (13056 bytes) rounded up to whole DMA blocks
   constexpr int K_OFF = 0;
-  constexpr int Q_OFF = K_OFF + KBYTES;
-  constexpr int V_OFF = Q_OFF + (WITH_OUT ? KBYTES : 0);
+  constexpr int V_OFF = K_OFF + KBYTES;
   constexpr int R_OFF = V_OFF + VBYTES;
   constexpr int BUF = R_OFF + RECB;           // one buffer
   static_assert(KRB == 128 || KRB == 256, "dk must be 64 or 128");
-  static_assert(!AUG || DK % NCOLS == 0, "identity/value columns must not share a workgroup");
+  static_assert(DK % NCOLS == 0, "identity/value columns must not share a workgroup");
 
   // Two separate buffers (not one array indexed by parity): the compiler must see that the
   // copies into one buffer cannot alias the reads of the other, or it waits for the copies
   // before the first read and the overlap is lost.
   __shared__ __align__(1024) uint8_t lds0[BUF];
   __shared__ __align__(1024) uint8_t lds1[BUF];
-  __shared__ __align__(1024) uint8_t ldsP[WITH_OUT ? CREC_EG_OFF : 16];  // P of the chunk, compact T' layout
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a scalar
@@ -119,16 +121,14 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
   const int b = bh / H, h = bh - b * H;
   const int col0 = cg * NCOLS;
   const int col = col0 + 16 * w + ln;
-  const bool ident = AUG && col0 < DK;
-  const int vcol0 = AUG ? col0 - DK : col0;
+  const bool ident = col0 < DK;  // identity columns (they carry M), else value columns (N)
+  const int vcol0 = col0 - DK;
   const int c_begin = seg * a.seg_chunks;
   const int c_end = min(a.nc, c_begin + a.seg_chunks);
 
-  const int rowK = H * DK * 2, rowV = H * DV * 2, rowO = H * DV * 4;
+  const int rowK = H * DK * 2, rowV = H * DV * 2;
   const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
-  const uint8_t* qb_ = static_cast<const uint8_t*>(a.q) + static_cast<size_t>(b) * T * rowK;
   const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
-  uint8_t* ob_ = reinterpret_cast<uint8_t*>(a.out) + static_cast<size_t>(b) * T * rowO;
 
   constexpr int KPR = KRB / 16, KRPB = 1024 / KRB;  // pieces per key row, key rows per 1 KB block
   constexpr int VPR = VRB / 16, VRPB = 1024 / VRB;
@@ -146,13 +146,11 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
 #pragma unroll
       for (int m = 0; m < RECB / 1024; ++m) dma16(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
       const rsrc_t rk = make_rsrc_wu(kb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
-      const rsrc_t rq = make_rsrc_wu(qb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
 #pragma unroll
       for (int blk = 0; blk < KBYTES / 1024; ++blk) {
         const int row = blk * KRPB + lane / KPR;
         const int off = row * rowK + h * DK * 2 + 16 * ((lane % KPR) ^ swz<KRB>(row));
         dma16(rk, B + K_OFF + 1024 * blk, off);
-        if constexpr (WITH_OUT) dma16(rq, B + Q_OFF + 1024 * blk, off);
       }
       if (!ident) {
         const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV, static_cast<long long>(T - t0) * rowV);
@@ -167,7 +165,6 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     for (int c = c_begin; c < c_end; ++c) {
       if (c + 1 < c_end) copy_chunk(c + 1, ((c + 1 - c_begin) & 1) ? lds1 : lds0);
-      if constexpr (WITH_OUT) asm volatile("s_barrier" ::: "memory");
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
     return;
@@ -229,79 +226,17 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = tok(mt, 4 * gq + i);
-      float s0 = 0.f;
-      if constexpr (AUG) {
-        s0 = (ident && r == col) ? 1.f : 0.f;
-      } else {
-        if (a.init) s0 = a.init[(static_cast<size_t>(bh) * a.init_segs + seg) * DK * DV + r * DV + col];
-      }
-      S[mt][i] = s0;
+      S[mt][i] = (ident && r == col) ? 1.f : 0.f;
     }
   }
 
-  // The output is computed transposed: tile mt of O^T holds, in lane (gq, ln), token
-  // tok(mt, ln) and this wave's columns 16 w + 4 gq + 0..3, stored as one 16-byte write
-  // as soon as it is complete. Nothing waits for the stores: the compute waves' barriers
-  // wait only for LDS operations.
-  auto store_out = [&](int c, int mt, const f32x4& o) __attribute__((always_inline)) {
-    const int t0 = c * CHUNK;
-    const rsrc_t ro = make_rsrc_wu(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
-    const int obase = (h * DV + vcol0 + 16 * w + 4 * gq) * 4;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, obase + tok(mt, ln) * rowO, 0, 0);
-  };
-
   // one chunk computed from buffer B (while the copy wave fills the other buffer)
-  auto chunk = [&](int c, const uint8_t* B) __attribute__((always_inline)) {
+  auto chunk = [&](const uint8_t* B) __attribute__((always_inline)) {
     const uint8_t* sK = B + K_OFF;
-    const uint8_t* sQ = B + Q_OFF;
     const uint8_t* sV = B + V_OFF;
     const uint8_t* sR = B + R_OFF;
     const float* sEG = reinterpret_cast<const float*>(sR + CREC_EG_OFF);
     const float* sEGC = reinterpret_cast<const float*>(sR + CREC_EGC_OFF);
-
-    // ---- P = tril(e^{g_r - g_i} Q K^T) into ldsP (rows r = query tokens, columns i = key tokens) ----
-    // Twelve 16 x 16 tiles pair key tile mi with query tile mj (permuted token order) where
-    // the half of mi does not exceed the half of mj; wave w computes three of them (tile j
-    // right after R tile j, so that the two interleave). A tile is D = K_mi Q_mj^T, so a
-    // lane holds four consecutive key tokens of one query token and writes 8 bytes of hi and
-    // 8 of lo. The products and the mask are those of the full record's P: fp32 sums of
-    // exact bf16 products times e^{g_r - g_i} for i <= r, and 0 above the diagonal (a select,
-    // so an overflowing exponent there does no harm). Pair j = 1 puts key tokens 0..31
-    // against query tokens 32..63 and needs no mask.
-    const float* sG = reinterpret_cast<const float*>(sR + CREC_G_OFF);
-    auto ptile = [&](int j) __attribute__((always_inline)) {
-      const int mi = (w >> 1) + (j == 2 ? 2 : 0), mj = (w & 1) + (j >= 1 ? 2 : 0);
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) acc = mfma_bf16(fragK(sK, mi, kb), fragK(sQ, mj, kb), acc);
-      const int r = tok(mj, ln), i0 = tok(mi, 4 * gq);
-      const float gr = sG[r];
-      const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);
-      f32x4 pv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = __expf(gr - gi[e]) * acc[e];
-        pv[e] = (j == 1 || i0 + e <= r) ? x : 0.f;
-      }
-      const u32x2 hw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv, bf16x4));
-      f32x4 hf;
-      hf[0] = __uint_as_float(hw[0] << 16);
-      hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
-      hf[2] = __uint_as_float(hw[1] << 16);
-      hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
-      const f32x4 lv = pv - hf;
-      const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(lv, bf16x4));
-      int oh, ol;
-      if (j == 0) {  // query tile mj < 2: rows 0..31
-        oh = CREC_TOP_OFF + swz_off<128>(r, 2 * i0);
-        ol = CREC_TOP_OFF + swz_off<128>(r, 64 + 2 * i0);
-      } else {
-        oh = CREC_BOT_OFF + swz_off<256>(r - 32, 2 * i0);
-        ol = CREC_BOT_OFF + swz_off<256>(r - 32, 128 + 2 * i0);
-      }
-      *reinterpret_cast<u32x2*>(ldsP + oh) = hw;
-      *reinterpret_cast<u32x2*>(ldsP + ol) = lw;
-    };
 
     // ---- S as B operand ----
     S8 Sb[DK / 32];
@@ -325,9 +260,6 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
         vv[3] = __uint_as_float(x[1] & 0xFFFF0000u);
       }
       Rr[mt] = vv - eg * acc;
-      if constexpr (WITH_OUT) {
-        if (mt < 3) ptile(mt);
-      }
     }
     S8 Rb[2];
 #pragma unroll
@@ -343,33 +275,13 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
         if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], fragR(sR, mt, kb), Rb[kb]);
     }
 
-    // ---- O = diag(e^g) Q S + P U, S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
-    // QS and the state update need no P: they run before the LDS-only barrier that makes
-    // every wave's P tiles visible; only the P U products follow it.
-    // U is split twice: scaled by e^{g_C - g} (for the state update) and as it is (for P U)
+    // ---- S <- e^{g_C} S + K^T diag(e^{g_C - g}) U ----
     f32x4 Ue[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) Ue[mt] = U[mt] * *reinterpret_cast<const f32x4*>(sEGC + tok(mt, 4 * gq));
     S8 Ud[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Ud[kb] = split8(frag_from_acc(Ue[2 * kb], Ue[2 * kb + 1]));
-    S8 Ub[2];
-    f32x4 Oacc[4];
-    if constexpr (WITH_OUT) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) Ub[kb] = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-          const bf16x8 qf = fragK(sQ, mt, kb);
-          acc = mfma_bf16(Sb[kb].h, qf, acc);
-          acc = mfma_bf16(Sb[kb].l, qf, acc);
-        }
-        Oacc[mt] = acc * sEG[tok(mt, ln)];
-      }
-    }
     const float gC = sEG[CHUNK - 1];
 #pragma unroll
     for (int mt = 0; mt < DK / 16; ++mt) {
@@ -377,18 +289,6 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], fragKT(sK, mt, kb), Ud[kb]);
     }
-    if constexpr (WITH_OUT) {
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4 acc = Oacc[mt];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
-        store_out(c, mt, acc);
-      }
-    }
-
     // end of chunk: this wave's reads of buffer B are done (lgkmcnt) and, past the barrier,
     // every wave's are, and the copy wave's copies of chunk c + 1 have landed
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -396,8 +296,8 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
 
   asm volatile("s_barrier" ::: "memory");  // the first chunk has landed
   for (int c = c_begin; c < c_end; c += 2) {
-    chunk(c, lds0);
-    if (c + 1 < c_end) chunk(c + 1, lds1);
+    chunk(lds0);
+    if (c + 1 < c_end) chunk(lds1);
   }
 
   if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
@@ -410,9 +310,335 @@ __global__ __launch_bounds__(DMA_THREADS) void state_dma_kernel(StateDmaArgs a) 
   }
 }
 
-template <int DK, bool WITH_OUT, bool AUG>
-static hipError_t launch_dma_t(int nwg, const StateDmaArgs& a, hipStream_t stream) {
-  return launch_kernel(state_dma_kernel<DK, WITH_OUT, AUG>, dim3(nwg), dim3(DMA_THREADS), stream, a);
+// ---------------------------------------------------------------------------
+// The walk with outputs (sequential path, and the scan's walk from each segment's start).
+//
+// Per 16-column slice of the workgroup's 64 state columns the chunk's work splits into the
+// recurrence chain, which carries the state from chunk to chunk,
+//   R = V - diag(e^g) K S,  U = T' R,  S <- e^{g_C} S + K^T diag(e^{g_C - g}) U,
+// and work off that chain, which only produces outputs: P = tril(e^{g_r - g_i} Q K^T), Q S and
+// O = diag(e^g) Q S + P U. Each slice gets two waves on one SIMD, plus one copy wave for the
+// workgroup:
+//  * the recurrence wave (waves 0..3) runs the chain. It hands U, split hi/lo, to the output
+//    wave through LDS, and at the end of each chunk the hi/lo split of the new S, which it
+//    keeps in registers for its own next chunk;
+//  * the output wave (waves 4..7) computes its three P tiles and Q S from that split of S while
+//    the recurrence wave computes U, then P U, and stores its output tiles;
+//  * the copy wave (wave 8) copies chunk c+1's rows of K and Q and its record into the other
+//    half of a double-buffered LDS area while chunk c is computed. V rows are read only by the
+//    recurrence wave, before the mid-chunk barrier, so they have one buffer, which the copy
+//    wave refills after that barrier.
+// Two barriers per chunk: the mid-chunk one publishes U and every output wave's P tiles (and
+// tells the recurrence wave the output wave is done with the S split it may now overwrite);
+// the end-of-chunk one follows the state update and the copies. The products are those of the
+// single-wave walk, in the same order, so the results are the same bit for bit; split this way
+// the walk takes about 3% less time on the LM-layer shape (the chain's latency dominates).
+// LDS: 2 x 45,824 B (K, Q, record) + 8 KB (V) + 12 KB (P) + 16 KB (U split) + 32 KB (S split)
+// = 161,280 B, so the record's last copy is cut to its 768 remaining bytes.
+constexpr int WALK_THREADS = 576;  // four recurrence waves, four output waves, one copy wave
+
+template <int DK>
+__global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a) {
+  using TR = Tr<MODE_BF16>;
+  constexpr int NCOLS = 64;
+  constexpr int KRB = DK * 2;
+  constexpr int VRB = NCOLS * 2;
+  constexpr int KBYTES = CHUNK * KRB;
+  constexpr int VBYTES = CHUNK * VRB;
+  constexpr int RECB = CREC_BYTES;  // the last 1 KB copy is cut to the record's 768 remaining bytes
+  constexpr int K_OFF = 0;
+  constexpr int Q_OFF = K_OFF + KBYTES;
+  constexpr int R_OFF = Q_OFF + KBYTES;
+  constexpr int BUF = R_OFF + RECB;
+  constexpr int KPR = KRB / 16, KRPB = 1024 / KRB;
+  constexpr int VPR = VRB / 16, VRPB = 1024 / VRB;
+
+  static_assert(BUF % 256 == 0, "buffers start on the 256-byte bank period");
+  __shared__ __align__(256) uint8_t lds0[BUF];
+  __shared__ __align__(256) uint8_t lds1[BUF];
+  __shared__ __align__(256) uint8_t ldsV[VBYTES];  // V rows: read before the mid-chunk barrier only
+  __shared__ __align__(256) uint8_t ldsP[CREC_EG_OFF];
+  __shared__ __align__(16) u32x4 ldsUb[4][2][2][64];         // [slice][kb][hi, lo][lane]: U split, 8 KB
+  __shared__ __align__(16) u32x4 ldsSb[4][DK / 32][2][64];   // [slice][kb][hi, lo][lane]: S split, 32 KB
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int sl = wu & 3;
+  const int gq = lane >> 4, ln = lane & 15;
+  int cg, unit;
+  decode_wg_dma(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
+  const int bh = unit / a.nseg, seg = unit - bh * a.nseg;
+  const int H = a.H, T = a.T, DV = a.DV;
+  const int b = bh / H, h = bh - b * H;
+  const int col0 = cg * NCOLS;
+  const int col = col0 + 16 * sl + ln;
+  const int c_begin = seg * a.seg_chunks;
+  const int c_end = min(a.nc, c_begin + a.seg_chunks);
+  const int rowK = H * DK * 2, rowV = H * DV * 2, rowO = H * DV * 4;
+  const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
+  const uint8_t* qb_ = static_cast<const uint8_t*>(a.q) + static_cast<size_t>(b) * T * rowK;
+  const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
+  uint8_t* ob_ = reinterpret_cast<uint8_t*>(a.out) + static_cast<size_t>(b) * T * rowO;
+
+  if (wu == 8) {  // the copy wave, as in state_dma_kernel
+    // chunk c's rows of K and Q and its record into buffer B; its V rows into the one V buffer
+    auto copy_kqr = [&](int c, uint8_t* B) __attribute__((always_inline)) {
+      const int t0 = c * CHUNK;
+      const rsrc_t rr = make_rsrc_wu(a.rec + (static_cast<size_t>(bh) * a.nc + c) * CREC_BYTES, CREC_BYTES);
+#pragma unroll
+      for (int m = 0; m < CREC_BYTES / 1024; ++m) dma16(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
+      if (lane < (CREC_BYTES % 1024) / 16)
+        dma16(rr, B + R_OFF + (CREC_BYTES / 1024) * 1024, (CREC_BYTES / 1024) * 1024 + 16 * lane);
+      const rsrc_t rk = make_rsrc_wu(kb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
+      const rsrc_t rq = make_rsrc_wu(qb_ + static_cast<size_t>(t0) * rowK, static_cast<long long>(T - t0) * rowK);
+#pragma unroll
+      for (int blk = 0; blk < KBYTES / 1024; ++blk) {
+        const int row = blk * KRPB + lane / KPR;
+        const int off = row * rowK + h * DK * 2 + 16 * ((lane % KPR) ^ swz<KRB>(row));
+        dma16(rk, B + K_OFF + 1024 * blk, off);
+        dma16(rq, B + Q_OFF + 1024 * blk, off);
+      }
+    };
+    auto copy_v = [&](int c) __attribute__((always_inline)) {
+      const int t0 = c * CHUNK;
+      const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV, static_cast<long long>(T - t0) * rowV);
+#pragma unroll
+      for (int blk = 0; blk < VBYTES / 1024; ++blk) {
+        const int row = blk * VRPB + lane / VPR;
+        dma16(rv, ldsV + 1024 * blk, row * rowV + (h * DV + col0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row)));
+      }
+    };
+    if (c_begin < c_end) {
+      copy_kqr(c_begin, lds0);
+      copy_v(c_begin);
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int c = c_begin; c < c_end; ++c) {
+      if (c + 1 < c_end) copy_kqr(c + 1, ((c + 1 - c_begin) & 1) ? lds1 : lds0);
+      asm volatile("s_barrier" ::: "memory");  // past it, this chunk's V rows have been read
+      if (c + 1 < c_end) copy_v(c + 1);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    return;
+  }
+
+  int oK[DK / 32], oT[DK / 32], oRt[2], oRb[2][2];
+#pragma unroll
+  for (int kb = 0; kb < DK / 32; ++kb) {
+    oK[kb] = swz_off<KRB>(tok(0, ln), 64 * kb + 16 * gq);
+    oT[kb] = swz_off<KRB>(8 * gq + (ln >> 2), 2 * (32 * kb + 8 * (ln & 3)));
+  }
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl) {
+    oRt[hl] = CREC_TOP_OFF + swz_off<128>(tok(0, ln), 64 * hl + 16 * gq);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) oRb[kb][hl] = CREC_BOT_OFF + swz_off<256>(tok(0, ln), 128 * hl + 64 * kb + 16 * gq);
+  }
+  const int oV = swz_off<VRB>(8 * gq + (ln >> 2), 2 * (16 * sl + 4 * (ln & 3)));
+  auto mrow = [](int m) { return 32 * (m >> 1) + 4 * (m & 1); };
+  auto fragK = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oK[kb] + mrow(m) * KRB));
+  };
+  auto fragKT = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    const uint8_t* p = X + oT[m >> 1] + 32 * kb * KRB + 8 * (m & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * KRB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto fragR = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    const uint8_t* p = m < 2 ? X + oRt[0] + 4 * (m & 1) * 128 : X + oRb[kb][0] + 4 * (m & 1) * 256;
+    const int lo = m < 2 ? oRt[1] - oRt[0] : oRb[kb][1] - oRb[kb][0];
+    S8 r;
+    r.h = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+    r.l = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + lo));
+    return r;
+  };
+  auto trV = [&](const uint8_t* X, int m) __attribute__((always_inline)) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + oV + mrow(m) * VRB));
+    return __builtin_bit_cast(u32x2, v);
+  };
+
+  if (wu < 4) {  // recurrence wave
+    f32x4 S[DK / 16];
+#pragma unroll
+    for (int mt = 0; mt < DK / 16; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = tok(mt, 4 * gq + i);
+        S[mt][i] = a.init ? a.init[(static_cast<size_t>(bh) * a.init_segs + seg) * DK * DV + r * DV + col] : 0.f;
+      }
+    }
+    // S split hi/lo: kept in registers for this wave's next chunk and handed to the output wave
+    S8 Sb[DK / 32];
+    auto split_and_publish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        Sb[kb] = split8(frag_from_acc(S[2 * kb], S[2 * kb + 1]));
+        ldsSb[sl][kb][0][lane] = __builtin_bit_cast(u32x4, Sb[kb].h);
+        ldsSb[sl][kb][1][lane] = __builtin_bit_cast(u32x4, Sb[kb].l);
+      }
+    };
+    auto rec_chunk = [&](const uint8_t* B) __attribute__((always_inline)) {
+      const uint8_t* sK = B + K_OFF;
+      const uint8_t* sV = ldsV;
+      const uint8_t* sR = B + R_OFF;
+      const float* sEG = reinterpret_cast<const float*>(sR + CREC_EG_OFF);
+      const float* sEGC = reinterpret_cast<const float*>(sR + CREC_EGC_OFF);
+      f32x4 Rr[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, fragK(sK, mt, kb), Sb[kb]);
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tok(mt, 4 * gq));
+        const u32x2 x = trV(sV, mt);
+        f32x4 vv;
+        vv[0] = __uint_as_float(x[0] << 16);
+        vv[1] = __uint_as_float(x[0] & 0xFFFF0000u);
+        vv[2] = __uint_as_float(x[1] << 16);
+        vv[3] = __uint_as_float(x[1] & 0xFFFF0000u);
+        Rr[mt] = vv - eg * acc;
+      }
+      S8 Rb[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) Rb[kb] = split8(frag_from_acc(Rr[2 * kb], Rr[2 * kb + 1]));
+      f32x4 U[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        U[mt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], fragR(sR, mt, kb), Rb[kb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const S8 ub = split8(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
+        ldsUb[sl][kb][0][lane] = __builtin_bit_cast(u32x4, ub.h);
+        ldsUb[sl][kb][1][lane] = __builtin_bit_cast(u32x4, ub.l);
+      }
+      // U published; the output wave has read this chunk's S split (its reads precede its
+      // arrival here), so the next one may be written after this barrier
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      f32x4 Ue[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) Ue[mt] = U[mt] * *reinterpret_cast<const f32x4*>(sEGC + tok(mt, 4 * gq));
+      S8 Ud[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) Ud[kb] = split8(frag_from_acc(Ue[2 * kb], Ue[2 * kb + 1]));
+      const float gC = sEG[CHUNK - 1];
+#pragma unroll
+      for (int mt = 0; mt < DK / 16; ++mt) {
+        S[mt] *= gC;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], fragKT(sK, mt, kb), Ud[kb]);
+      }
+      split_and_publish();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    split_and_publish();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int c = c_begin; c < c_end; c += 2) {
+      rec_chunk(lds0);
+      if (c + 1 < c_end) rec_chunk(lds1);
+    }
+    if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
+      float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
+#pragma unroll
+      for (int mt = 0; mt < DK / 16; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) F[(tok(mt, 4 * gq) + i) * a.fin_ld + col] = S[mt][i];
+      }
+    }
+  } else {  // output wave
+    auto store_out = [&](int c, int mt, const f32x4& o) __attribute__((always_inline)) {
+      const int t0 = c * CHUNK;
+      const rsrc_t ro = make_rsrc_wu(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
+      const int obase = (h * DV + col0 + 16 * sl + 4 * gq) * 4;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, obase + tok(mt, ln) * rowO, 0, 0);
+    };
+    auto out_chunk = [&](int c, const uint8_t* B) __attribute__((always_inline)) {
+      const uint8_t* sK = B + K_OFF;
+      const uint8_t* sQ = B + Q_OFF;
+      const uint8_t* sR = B + R_OFF;
+      const float* sG = reinterpret_cast<const float*>(sR + CREC_G_OFF);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int mi = (sl >> 1) + (j == 2 ? 2 : 0), mj = (sl & 1) + (j >= 1 ? 2 : 0);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) acc = mfma_bf16(fragK(sK, mi, kb), fragK(sQ, mj, kb), acc);
+        const int r = tok(mj, ln), i0 = tok(mi, 4 * gq);
+        const float gr = sG[r];
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = __expf(gr - gi[e]) * acc[e];
+          pv[e] = (j == 1 || i0 + e <= r) ? x : 0.f;
+        }
+        const u32x2 hw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv, bf16x4));
+        f32x4 hf;
+        hf[0] = __uint_as_float(hw[0] << 16);
+        hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
+        hf[2] = __uint_as_float(hw[1] << 16);
+        hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
+        const f32x4 lv = pv - hf;
+        const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(lv, bf16x4));
+        int oh, ol;
+        if (j == 0) {
+          oh = CREC_TOP_OFF + swz_off<128>(r, 2 * i0);
+          ol = CREC_TOP_OFF + swz_off<128>(r, 64 + 2 * i0);
+        } else {
+          oh = CREC_BOT_OFF + swz_off<256>(r - 32, 2 * i0);
+          ol = CREC_BOT_OFF + swz_off<256>(r - 32, 128 + 2 * i0);
+        }
+        *reinterpret_cast<u32x2*>(ldsP + oh) = hw;
+        *reinterpret_cast<u32x2*>(ldsP + ol) = lw;
+      }
+      f32x4 Oacc[4];
+      {
+        S8 Sb[DK / 32];
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          Sb[kb].h = __builtin_bit_cast(bf16x8, ldsSb[sl][kb][0][lane]);
+          Sb[kb].l = __builtin_bit_cast(bf16x8, ldsSb[sl][kb][1][lane]);
+        }
+        const float* sEG = reinterpret_cast<const float*>(sR + CREC_EG_OFF);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < DK / 32; ++kb) {
+            const bf16x8 qf = fragK(sQ, mt, kb);
+            acc = mfma_bf16(Sb[kb].h, qf, acc);
+            acc = mfma_bf16(Sb[kb].l, qf, acc);
+          }
+          Oacc[mt] = acc * sEG[tok(mt, ln)];
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      S8 Ub[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Ub[kb].h = __builtin_bit_cast(bf16x8, ldsUb[sl][kb][0][lane]);
+        Ub[kb].l = __builtin_bit_cast(bf16x8, ldsUb[sl][kb][1][lane]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc = Oacc[mt];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
+        store_out(c, mt, acc);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    asm volatile("s_barrier" ::: "memory");
+    for (int c = c_begin; c < c_end; c += 2) {
+      out_chunk(c, lds0);
+      if (c + 1 < c_end) out_chunk(c + 1, lds1);
+    }
+  }
 }
 
 bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 64 || dk == 128); }
@@ -423,12 +649,14 @@ hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void
                             int ncg, int nseg, hipStream_t stream) {
   const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, seg_chunks, init, init_segs, out, fin, fin_ld, fin_segs,
                        fin_last_only, ncg, nseg};
+  if (with_out == aug) return hipErrorInvalidValue;  // a walk either has outputs or carries [M | N]
   if (dk == 64) {
-    if (with_out) return launch_dma_t<64, true, false>(nwg, a, stream);
-    if (aug) return launch_dma_t<64, false, true>(nwg, a, stream);
-  } else if (dk == 128) {
-    if (with_out) return launch_dma_t<128, true, false>(nwg, a, stream);
-    if (aug) return launch_dma_t<128, false, true>(nwg, a, stream);
+    if (with_out) return launch_kernel(state_walk_kernel<64>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    return launch_kernel(state_map_kernel<64>, dim3(nwg), dim3(MAP_THREADS), stream, a);
+  }
+  if (dk == 128) {
+    if (with_out) return launch_kernel(state_walk_kernel<128>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    return launch_kernel(state_map_kernel<128>, dim3(nwg), dim3(MAP_THREADS), stream, a);
   }
   return hipErrorInvalidValue;
 }
