@@ -514,14 +514,24 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
     ends_floats += static_cast<long long>(bh) * nleft[nscale] * dk * dv;
   }
   const size_t ends_bytes = align256(static_cast<size_t>(ends_floats) * 4);
+  // bf16 with dk <= 128: the right walks run on the DMA-fed walk kernel, which reads compact
+  // records (T' and the gates; it forms P itself), from a second prep pass
+  const bool compact = kla::state_dma_supported(mode, dk);
+  const size_t crec_bytes = compact ? align256(bh * nc * static_cast<size_t>(kla::record_bytes(mode, dk))) : 0;
   void* ws = nullptr;
-  st = workspace_alloc(&ws, rec_bytes + ends_bytes, stream);
+  st = workspace_alloc(&ws, rec_bytes + ends_bytes + crec_bytes, stream);
   if (st != KLA_OK) return st;
   hipError_t e = hipSuccess;
   uint8_t* rec = static_cast<uint8_t*>(ws);
   float* ends = reinterpret_cast<float*>(rec + rec_bytes);
+  uint8_t* crec = compact ? rec + rec_bytes + ends_bytes : nullptr;
   const int direct = beta_mode == KLA_BETA_DIRECT;
   e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
+  if (e == hipSuccess && compact) {
+    kla::Dims dc = d;
+    dc.full_rec = 0;
+    e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, dc, q, k, log_alpha, eta, eps, direct, crec, stream); });
+  }
   if (e == hipSuccess)
     e = timed("kla_loglinear_intra", stream, [&] { return kla::launch_loglinear_intra(mode, d, rec, v, lam, levels, out, stream); });
   // every scale's left walks in one grid (they are independent), then the right walks scale by
@@ -532,8 +542,8 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
     });
   for (int i = 0; e == hipSuccess && i < nscale; ++i) {
     e = timed("kla_loglinear_right", stream, [&] {
-      return kla::launch_loglinear_right(mode, d, q, k, rec, half[i], nright[i], ends + ends_off[i], nleft[i], lam, levels,
-                                         7 + i, out, stream);
+      return kla::launch_loglinear_right(mode, d, q, k, rec, crec, half[i], nright[i], ends + ends_off[i], nleft[i], lam,
+                                         levels, 7 + i, out, stream);
     });
   }
   hipError_t ef = hipFreeAsync(ws, stream);

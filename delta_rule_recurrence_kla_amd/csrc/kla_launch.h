@@ -66,10 +66,13 @@ bool state_dma_supported(int mode, int dk);
 // state kernel consumes it, else the full record.
 int record_bytes(int mode, int dk);
 int full_record_bytes();  // T' and P in full, for the kernels that read both
+// With lam non-null the walk adds lam-weighted outputs to out (values read as zeros when v is
+// null); segment s walks chunks [(s * seg_mul + seg_add) * seg_chunks, + seg_chunks).
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
-                            int ncg, int nseg, hipStream_t stream);
+                            int ncg, int nseg, hipStream_t stream, int seg_mul = 1, int seg_add = 0,
+                            const float* lam = nullptr, int lam_L = 0, int lam_level = 0);
 
 // Log-linear decode: one token at position t for N x H heads, each with L bucket states
 // [L, dk, dv] (only the occupied levels are read or written).
@@ -89,9 +92,11 @@ hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, c
 hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int nscale,
                                  const int* half, const int* nleft, const long long* ends_off, float* ends,
                                  hipStream_t stream);
-hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec, int half,
-                                  int nright, const float* ends, int nleft, const float* lam, int L, int level,
-                                  float* out, hipStream_t stream);
+// rec_compact: compact records of the same chunks (bf16, dk <= 128), for the DMA-fed walk; null
+// takes the register-prefetch walk on the full records.
+hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec,
+                                  const uint8_t* rec_compact, int half, int nright, const float* ends, int nleft,
+                                  const float* lam, int L, int level, float* out, hipStream_t stream);
 
 // Device address and size of the static scratch buffer of kla_chunk_fwd_noalloc on the
 // current device (kla_scratch.hip); the address is looked up once per device.

@@ -61,6 +61,15 @@ struct StateDmaArgs {
   int fin_last_only;
   int ncg;
   int nseg;
+  // Segment s walks chunks [(s * seg_mul + seg_add) * seg_chunks, + seg_chunks): every segment
+  // (1, 0), or every other one (2, 1) for the right half-blocks of a log-linear scale.
+  int seg_mul;
+  int seg_add;
+  // ACC walks (values read as zeros when v is null): out[b, t, h, :] += lam[((b * T + t) * H + h)
+  // * lam_L + lam_level] * o_t instead of out = o_t.
+  const float* lam;
+  int lam_L;
+  int lam_level;
 };
 
 namespace {
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
 // = 161,280 B, so the record's last copy is cut to its 768 remaining bytes.
 constexpr int WALK_THREADS = 576;  // four recurrence waves, four output waves, one copy wave
 
-template <int DK>
+template <int DK, bool ACC>
 __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a) {
   using TR = Tr<MODE_BF16>;
   constexpr int NCOLS = 64;
@@ -372,7 +381,7 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
   const int b = bh / H, h = bh - b * H;
   const int col0 = cg * NCOLS;
   const int col = col0 + 16 * sl + ln;
-  const int c_begin = seg * a.seg_chunks;
+  const int c_begin = (seg * a.seg_mul + a.seg_add) * a.seg_chunks;
   const int c_end = min(a.nc, c_begin + a.seg_chunks);
   const int rowK = H * DK * 2, rowV = H * DV * 2, rowO = H * DV * 4;
   const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
@@ -401,7 +410,9 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
     };
     auto copy_v = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CHUNK;
-      const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV, static_cast<long long>(T - t0) * rowV);
+      // without values (v null) the copies read through an empty range and land as zeros
+      const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV,
+                                     a.v ? static_cast<long long>(T - t0) * rowV : 0);
 #pragma unroll
       for (int blk = 0; blk < VBYTES / 1024; ++blk) {
         const int row = blk * VRPB + lane / VPR;
@@ -557,6 +568,22 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, obase + tok(mt, ln) * rowO, 0, 0);
     };
     auto out_chunk = [&](int c, const uint8_t* B) __attribute__((always_inline)) {
+      // ACC: the outputs already there and the weights of this wave's output rows, loaded first so
+      // that the adds never wait on a memory round trip (a load issued after the stores would also
+      // wait for them: loads and stores retire in order on one counter)
+      u32x4 acc_old[ACC ? 4 : 1];
+      float acc_w[ACC ? 4 : 1];
+      if constexpr (ACC) {
+        const int t0 = c * CHUNK;
+        const rsrc_t ra = make_rsrc_wu(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
+        const int obase = (h * DV + col0 + 16 * sl + 4 * gq) * 4;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int t = t0 + tok(mt, ln);
+          acc_old[mt] = bload16(ra, obase + tok(mt, ln) * rowO);
+          acc_w[mt] = t < T ? a.lam[((static_cast<size_t>(b) * T + t) * H + h) * a.lam_L + a.lam_level] : 0.f;
+        }
+      }
       const uint8_t* sK = B + K_OFF;
       const uint8_t* sQ = B + Q_OFF;
       const uint8_t* sR = B + R_OFF;
@@ -629,6 +656,7 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
+        if constexpr (ACC) acc = __builtin_bit_cast(f32x4, acc_old[mt]) + acc_w[mt] * acc;  // rows past T: weight 0
         store_out(c, mt, acc);
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -646,16 +674,21 @@ bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
-                            int ncg, int nseg, hipStream_t stream) {
+                            int ncg, int nseg, hipStream_t stream, int seg_mul, int seg_add, const float* lam,
+                            int lam_L, int lam_level) {
   const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, seg_chunks, init, init_segs, out, fin, fin_ld, fin_segs,
-                       fin_last_only, ncg, nseg};
+                       fin_last_only, ncg, nseg, seg_mul, seg_add, lam, lam_L, lam_level};
   if (with_out == aug) return hipErrorInvalidValue;  // a walk either has outputs or carries [M | N]
+  const bool acc = lam != nullptr;
+  if (acc && !with_out) return hipErrorInvalidValue;
   if (dk == 64) {
-    if (with_out) return launch_kernel(state_walk_kernel<64>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    if (acc) return launch_kernel(state_walk_kernel<64, true>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    if (with_out) return launch_kernel(state_walk_kernel<64, false>, dim3(nwg), dim3(WALK_THREADS), stream, a);
     return launch_kernel(state_map_kernel<64>, dim3(nwg), dim3(MAP_THREADS), stream, a);
   }
   if (dk == 128) {
-    if (with_out) return launch_kernel(state_walk_kernel<128>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    if (acc) return launch_kernel(state_walk_kernel<128, true>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    if (with_out) return launch_kernel(state_walk_kernel<128, false>, dim3(nwg), dim3(WALK_THREADS), stream, a);
     return launch_kernel(state_map_kernel<128>, dim3(nwg), dim3(MAP_THREADS), stream, a);
   }
   return hipErrorInvalidValue;
