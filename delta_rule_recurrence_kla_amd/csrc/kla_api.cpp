@@ -56,8 +56,9 @@ kla::LaunchEvents& kla::launch_events() { return g_launch_events; }
 
 namespace {
 
-// Each launcher enqueues one kernel. With timing on, that launch stamps a pair of events
-// from its own dispatch (kla::launch_kernel), so the recorded interval is the kernel alone.
+// With timing on, the kernels a launcher enqueues stamp a pair of events from their own
+// dispatches (kla::launch_kernel): the interval runs from the first kernel's start to the
+// last one's end, with no host-side gap in it.
 template <class F>
 hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
   (void)stream;

@@ -18,11 +18,16 @@ struct LaunchEvents {
 LaunchEvents& launch_events();
 
 // Every kernel of the library is launched through this (arguments are converted to the
-// kernel's parameter types); returns the launch status.
+// kernel's parameter types); returns the launch status. With timing on, the first launch of a
+// timed call stamps the start event from its dispatch and every launch restamps the stop
+// event, so a call that enqueues several kernels is timed from the first one's start to the
+// last one's end.
 template <class F, class... A>
 inline hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
-  const LaunchEvents& ev = launch_events();
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  LaunchEvents& ev = launch_events();
+  hipEvent_t start = ev.start;
+  ev.start = nullptr;
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, ev.stop, 0, args...);
   return hipGetLastError();
 }
 

@@ -21,7 +21,10 @@
 // emptied by a merge keep stale values and are never read again before being overwritten.
 //
 // One workgroup per (sequence, head), each thread owning 4 adjacent columns of a stripe of
-// rows of a bucket, as in the KLA decode kernel; bound by HBM bandwidth.
+// rows of a bucket, as in the KLA decode kernel; bound by HBM bandwidth. A step moves several
+// GB of buckets, far more than the last-level cache holds, and a bucket is not touched again
+// until a later step, so bucket reads and writes are non-temporal (the `nt` bit): streaming
+// past the caches this way moved the same bytes about 7% faster on MI355X.
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -121,21 +124,24 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
       float4 x = s[p];
       x.x = alpha * x.x - bk * A.x; x.y = alpha * x.y - bk * A.y;
       x.z = alpha * x.z - bk * A.z; x.w = alpha * x.w - bk * A.w;
-      *reinterpret_cast<float4*>(D + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4) = x;
+      __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4*>(D + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4));
     }
   };
   auto load_set = [&](float4 (&s)[NP], int l) __attribute__((always_inline)) {
     const float* Sl = slot(l);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      s[p] = *reinterpret_cast<const float4*>(Sl + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4);
+    {
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sl + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4));
+      s[p] = make_float4(x[0], x[1], x[2], x[3]);
+    }
   };
   auto load_add = [&](float4 (&s)[NP], int l) __attribute__((always_inline)) {
     const float* Sl = slot(l);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const float4 x = *reinterpret_cast<const float4*>(Sl + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4);
-      s[p].x += x.x; s[p].y += x.y; s[p].z += x.z; s[p].w += x.w;
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sl + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4));
+      s[p].x += x[0]; s[p].y += x[1]; s[p].z += x[2]; s[p].w += x[3];
     }
   };
 
@@ -169,8 +175,8 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const float bk = beta * sk[rg + p * RPP];
-    const float4 x = make_float4(bk * vv[0], bk * vv[1], bk * vv[2], bk * vv[3]);
-    *reinterpret_cast<float4*>(D0 + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4) = x;
+    __builtin_nontemporal_store(f32x4{bk * vv[0], bk * vv[1], bk * vv[2], bk * vv[3]},
+                                reinterpret_cast<f32x4*>(D0 + static_cast<size_t>(rg + p * RPP) * DV + 4 * c4));
   }
   const float w0 = lw[0] * beta * dkq;
   o.x += w0 * vv[0]; o.y += w0 * vv[1]; o.z += w0 * vv[2]; o.w += w0 * vv[3];
