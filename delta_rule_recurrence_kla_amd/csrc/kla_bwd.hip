@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kla_launch.h"
 
 namespace kla {
@@ -175,128 +177,6 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
   }
 }
 
-// Forward walk over the chunks of one (b, h) for state columns jb .. jb+15; stores every
-// chunk-start state S0 into states[bh][c][DK][DV]. Key rows stay bf16 in LDS for bf16 inputs
-// (exact) and the column blocks are stored column-major, for 16-byte reads.
-template <int MODE, int DK>
-__global__ __launch_bounds__(NT, 4) void bwd_states_kernel(const void* k, const void* v, const float* rec,
-                                                            const float* init, int T, int H, int DV, int nc,
-                                                            float* states) {
-  using E = typename LdsIn<MODE>::type;
-  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;
-  constexpr int SP = DK + 4, RP = BC + 4;
-  constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT;
-  constexpr int KV = DK * sizeof(E) / 16;  // 16-byte pieces per key row
-  constexpr int KPT = BC * KV / NT;        // key pieces per thread
-  constexpr int MPT = BC * BC / 4 / NT;    // float4s of the inverse per thread
-  constexpr int VPT = BC * NJ / NT;        // value elements per thread
-  static_assert(KPT * NT == BC * KV && MPT * NT * 4 == BC * BC && VPT * NT == BC * NJ, "walk tiling");
-  const int jb = blockIdx.x * NJ, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ __align__(16) E sK[BC][EP];
-  __shared__ float sM[BC][MP];
-  __shared__ __align__(16) float sS[NJ][SP];
-  __shared__ __align__(16) float sX[NJ][RP];
-  __shared__ __align__(16) float sU[NJ][RP];
-  __shared__ float sg[BC], sb[BC];
-  const int sd = tid / TPR, sj = (tid % TPR) * EPT;  // state elements owned
-  const int r = tid / TPRW, j0 = (tid % TPRW) * CPT;  // 64 x 16 chunk elements owned
-  // the next chunk's keys, inverse, values and gates, loaded into registers during this chunk
-  uint4 pk[KPT];
-  float4 pm[MPT];
-  float pv[VPT], pg = 0.f, pb = 0.f;
-  auto fetch = [&](int c) {
-    const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
-    for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * NT, rr = e / KV, pc = e % KV, t = c * BC + rr;
-      pk[x] = t < T ? *(reinterpret_cast<const uint4*>(static_cast<const E*>(k) + tok(b, t, T, H, h) * DK) + pc)
-                    : uint4{0u, 0u, 0u, 0u};
-    }
-    for (int x = 0; x < MPT; ++x) pm[x] = reinterpret_cast<const float4*>(R + REC_M)[tid + x * NT];
-    for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * NT, rr = e / NJ, jj = e % NJ, t = c * BC + rr;
-      pv[x] = t < T ? ldin<MODE>(v, tok(b, t, T, H, h) * DV + jb + jj) : 0.f;
-    }
-    if (tid < BC) {
-      pg = R[REC_G + tid];
-      pb = R[REC_B + tid];
-    }
-  };
-  float s[EPT];
-  for (int e = 0; e < EPT; ++e)
-    s[e] = init ? init[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
-  fetch(0);
-  for (int c = 0; c < nc; ++c) {
-    float* S0 = states + (static_cast<size_t>(bh) * nc + c) * DK * DV;
-    for (int e = 0; e < EPT; ++e) {
-      S0[sd * DV + jb + sj + e] = s[e];
-      sS[sj + e][sd] = s[e];
-    }
-    for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * NT;
-      *reinterpret_cast<uint4*>(&sK[e / KV][(e % KV) * (16 / sizeof(E))]) = pk[x];
-    }
-    for (int x = 0; x < MPT; ++x) {
-      const int e = 4 * (tid + x * NT), rr = e / BC, cc = e % BC;
-      sM[rr][cc] = pm[x].x;
-      sM[rr][cc + 1] = pm[x].y;
-      sM[rr][cc + 2] = pm[x].z;
-      sM[rr][cc + 3] = pm[x].w;
-    }
-    for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * NT;
-      sX[e % NJ][e / NJ] = pv[x];
-    }
-    if (tid < BC) {
-      sg[tid] = pg;
-      sb[tid] = pb;
-    }
-    if (c + 1 < nc) fetch(c + 1);
-    __syncthreads();
-    // beta . X with X = V - e^g . (K S0)
-    const float egr = expf(sg[r]);
-    float x[CPT];
-    for (int jj = 0; jj < CPT; ++jj) {
-      float a = 0.f;
-#pragma unroll 2
-      for (int d = 0; d < DK; d += 8) {
-        float kf[8], sf[8];
-        row8(&sK[r][d], kf);
-        row8(&sS[j0 + jj][d], sf);
-        for (int q = 0; q < 8; ++q) a = fmaf(kf[q], sf[q], a);
-      }
-      x[jj] = sb[r] * (sX[j0 + jj][r] - egr * a);
-    }
-    for (int jj = 0; jj < CPT; ++jj) sX[j0 + jj][r] = x[jj];
-    __syncthreads();
-    // w . U with U = Minv (beta . X)
-    const float gC = sg[BC - 1];
-    const float wr = expf(gC - sg[r]);
-    for (int jj = 0; jj < CPT; ++jj) {
-      float a = 0.f;
-#pragma unroll 8
-      for (int i = 0; i <= r; ++i) a = fmaf(sM[r][i], sX[j0 + jj][i], a);
-      sU[j0 + jj][r] = wr * a;
-    }
-    __syncthreads();
-    const float gam = expf(gC);
-    for (int e = 0; e < EPT; ++e) {
-      const float4* u4 = reinterpret_cast<const float4*>(&sU[sj + e][0]);
-      float a = 0.f;
-#pragma unroll 4
-      for (int i4 = 0; i4 < BC / 4; ++i4) {
-        const float4 uu = u4[i4];
-        const int i = 4 * i4;
-        a = fmaf(lds_f(sK[i][sd]), uu.x, a);
-        a = fmaf(lds_f(sK[i + 1][sd]), uu.y, a);
-        a = fmaf(lds_f(sK[i + 2][sd]), uu.z, a);
-        a = fmaf(lds_f(sK[i + 3][sd]), uu.w, a);
-      }
-      s[e] = fmaf(gam, s[e], a);
-    }
-    __syncthreads();
-  }
-}
-
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // One fp32 MFMA step (16 x 16 tile, K = 4, full fp32 products): lane l supplies A[l % 16][l / 16]
@@ -355,138 +235,274 @@ __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const floa
   }
 }
 
-// Reverse walk: every chunk-end state gradient dS1 into dstates[bh][c]; the start state's
-// gradient into dinit (if not null). With the chunk-local terms from bwd_dprep, a step is
-//   dU = w . (K dS1) + V~,  dX = diag(beta) Minv^T dU,  dS0 = e^{g_C} dS1 + C - K^T (e^g . dX).
-// A workgroup owns 16 state columns; for bf16 inputs the key rows stay bf16 in LDS (exact). The
-// next chunk's keys, inverse, V~ columns, C elements and gates are loaded into registers while
-// the current chunk is computed.
-constexpr int NJW = 16;
-template <int MODE, int DK>
-__global__ __launch_bounds__(NT, 4) void bwd_dstates_kernel(const void* k, const float* vt, const float* rec,
-                                                            const float* dfin, int T, int H, int DV, int nc,
-                                                            float* dstates, float* dinit) {
+// The two walks on the fp32 MFMA, one kernel: one workgroup per (b, h, 64 state columns), four
+// waves of 16 columns, each wave's 16 columns of the carried matrix in MFMA accumulators for the
+// whole walk. Every product has a chunk's 64 tokens or the state's dk rows as its contraction;
+// the carried matrix enters as the B operand straight from the accumulators (a 16 x 16 tile's
+// lane l holds rows 4 (l / 16) + i, i = 0..3, of column l % 16, which is the B operand of four
+// K = 4 steps whose contraction slots are those rows), so only the A operands come from LDS:
+//   forward (REV = false), S = chunk-start state, stored for every chunk:
+//     R = K S,  X = beta . (V - e^g . R),  U = Minv X,  S <- e^{g_C} S + K^T (w . U)
+//   reverse (REV = true), dS = chunk-end gradient dS1, stored for every chunk over the chunk's
+//   slot of Q^T (e^g . dO) after reading it, the start state's gradient at the end:
+//     dU = w . (K dS1) + V~,  dX = diag(beta) Minv^T dU,
+//     dS0 = e^{g_C} dS1 + Q^T (e^g . dO) - K^T (e^g . dX)
+// Key rows are staged in LDS twice (row-major for K, transposed for K^T) in the input's type
+// (bf16 stays exact), the inverse row-major (forward) or transposed (reverse), the values (or
+// V~) transposed in fp32, so that every A operand of a K = 4 step is one 8- or 16-byte read.
+// The next chunk's rows are loaded into registers while the current chunk is computed.
+constexpr int WT = 256;     // threads of a walk workgroup: four waves
+
+// Element j of a 16-byte piece of E values, taken from the piece's words (no address of the
+// register piece is taken, so it stays in registers).
+template <class E>
+__device__ __forceinline__ E piece_elem(const uint4& u, int j) {
+  const uint32_t wd = j / (4 / sizeof(E)) == 0 ? u.x : j / (4 / sizeof(E)) == 1 ? u.y : j / (4 / sizeof(E)) == 2 ? u.z : u.w;
+  if constexpr (sizeof(E) == 2) return static_cast<E>((j & 1) ? wd >> 16 : wd & 0xFFFFu);
+  else return __uint_as_float(wd);
+}
+constexpr int WCOL = 64;    // state columns per walk workgroup
+
+template <int MODE, int DK, bool REV>
+__global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void* vin, const float* rec,
+                                                      const float* sin, int T, int H, int DV, int nc, float* sdump,
+                                                      float* slast) {
   using E = typename LdsIn<MODE>::type;
-  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows of keys
-  constexpr int SP = DK + 4, RP = BC + 4;         // column-major blocks: state columns, chunk columns
-  constexpr int EPT = DK * NJW / NT, TPR = NJW / EPT, CPW = NJW / TPRW;
-  constexpr int KV = DK * sizeof(E) / 16, KPT = BC * KV / NT, MPT = BC * BC / 4 / NT, VPT = BC * NJW / NT;
-  static_assert(KPT * NT == BC * KV && MPT * NT * 4 == BC * BC && VPT * NT == BC * NJW, "walk tiling");
-  const int jb = blockIdx.x * NJW, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  __shared__ __align__(16) E sK[BC][EP];
-  __shared__ float sM[BC][BC];  // read down columns only: no padding needed
-  __shared__ __align__(16) float sS[NJW][SP];
-  __shared__ __align__(16) float sV[NJW][RP];
-  __shared__ __align__(16) float sU[NJW][RP];
-  __shared__ __align__(16) float sX[NJW][RP];
-  __shared__ float sg[BC], sb[BC];
-  const int sd = tid / TPR, sj = (tid % TPR) * EPT;
-  const int r = tid / TPRW, j0 = (tid % TPRW) * CPW;
+  constexpr int EV = 16 / sizeof(E);          // elements per 16-byte piece
+  constexpr int KP = DK + EV, TP = BC + EV;   // pitches of K [BC][KP] and K^T [DK][TP] (16-byte rows)
+  constexpr int MPP = BC + 4, VP = BC + 4;    // pitches of the inverse and of the transposed values
+  constexpr int KV = DK / EV, KPT = BC * KV / WT;   // key pieces per row, per thread
+  constexpr int MPT = BC * BC / 4 / WT;             // float4s of the inverse per thread
+  using VE = typename std::conditional<REV, float, E>::type;  // element type of the value rows
+  constexpr int VEV = 16 / sizeof(VE), VV = WCOL / VEV, VPT = BC * VV / WT;  // value pieces
+  constexpr int NDT = DK / 16;                      // 16-row tiles of the carried matrix
+  static_assert(KPT * WT == BC * KV && MPT * WT * 4 == BC * BC && VPT * WT == BC * VV, "walk tiling");
+  __shared__ __align__(16) E sK[BC][KP];
+  __shared__ __align__(16) E sKt[DK][TP];
+  __shared__ __align__(16) float sM[BC][MPP];
+  __shared__ __align__(16) float sV[WCOL][VP];
+  // per-token factors of the chunk: e^g, beta, w = e^{g_C - g}, e^g beta; and e^{g_C}
+  __shared__ __align__(16) float sEG[BC], sB[BC], sW[BC], sEB[BC];
+  __shared__ float sGam;
+  // per-wave 16 x 16 transpose tile: the accumulator layout to and from rows of 16-byte pieces
+  __shared__ __align__(16) float sTr[4][16][20];
+  const int jb = blockIdx.x * WCOL, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, ln = lane & 15;
+  const int col = jb + 16 * w + ln;  // this lane's column of the carried matrix
+
+  // ---- next chunk's rows in registers ----
   uint4 pk[KPT];
-  float4 pm[MPT];
-  float pv[VPT], pc[EPT], pg = 0.f, pb = 0.f;
-  auto fetch = [&](int c) {
+  v4f pm[MPT];
+  uint4 pv[VPT];
+  float pg = 0.f, pb = 0.f;
+  v4f pc[REV ? NDT : 1];
+  // a lane's 16-byte piece of a 16 x 16 tile of the carried matrix: row lane / 4, columns 4 (lane % 4) + 0..3
+  const int prow = lane >> 2, pcol = jb + 16 * w + 4 * (lane & 3);
+  auto fetch = [&](int c) __attribute__((always_inline)) {
     const size_t cidx = static_cast<size_t>(bh) * nc + c;
     const float* R = rec + cidx * RECF;
 #pragma unroll
     for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * NT, rr = e / KV, pe = e % KV, t = c * BC + rr;
+      const int e = tid + x * WT, rr = e / KV, pe = e % KV, t = c * BC + rr;
       pk[x] = t < T ? *(reinterpret_cast<const uint4*>(static_cast<const E*>(k) + tok(b, t, T, H, h) * DK) + pe)
                     : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int x = 0; x < MPT; ++x) pm[x] = reinterpret_cast<const float4*>(R + REC_M)[tid + x * NT];
+    for (int x = 0; x < MPT; ++x) pm[x] = reinterpret_cast<const v4f*>(R + REC_M)[tid + x * WT];
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * NT, rr = e / NJW, jj = e % NJW;
-      pv[x] = vt[(cidx * BC + rr) * DV + jb + jj];
+      const int e = tid + x * WT, rr = e / VV, pe = e % VV, t = c * BC + rr;
+      if constexpr (REV) {  // V~ = P^T dO of the chunk, fp32 [BC][DV] (zero rows past T already)
+        pv[x] = *reinterpret_cast<const uint4*>(static_cast<const float*>(vin) + (cidx * BC + rr) * DV + jb + VEV * pe);
+      } else {
+        pv[x] = t < T ? *reinterpret_cast<const uint4*>(static_cast<const E*>(vin) + tok(b, t, T, H, h) * DV + jb + VEV * pe)
+                      : uint4{0u, 0u, 0u, 0u};
+      }
     }
-    // Q^T (e^g . dO) of this chunk, this thread's elements only (its slot is overwritten with dS1)
-    const float* D = dstates + cidx * DK * DV;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) pc[e] = D[sd * DV + jb + sj + e];
     if (tid < BC) {
       pg = R[REC_G + tid];
       pb = R[REC_B + tid];
     }
-  };
-  float s[EPT];
-  for (int e = 0; e < EPT; ++e)
-    s[e] = dfin ? dfin[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] : 0.f;
-  fetch(nc - 1);
-  for (int c = nc - 1; c >= 0; --c) {
-    float* D1 = dstates + (static_cast<size_t>(bh) * nc + c) * DK * DV;
-    float cterm[EPT];
+    if constexpr (REV) {  // this wave's columns of Q^T (e^g . dO), the chunk's slot of dstates
+      const float* C = sdump + cidx * DK * DV;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      cterm[e] = pc[e];
-      D1[sd * DV + jb + sj + e] = s[e];
-      sS[sj + e][sd] = s[e];
+      for (int dt = 0; dt < NDT; ++dt) pc[dt] = *reinterpret_cast<const v4f*>(C + (16 * dt + prow) * DV + pcol);
     }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * NT;
-      *reinterpret_cast<uint4*>(&sK[e / KV][(e % KV) * (16 / sizeof(E))]) = pk[x];
+      const int e = tid + x * WT, rr = e / KV, pe = e % KV;
+      *reinterpret_cast<uint4*>(&sK[rr][pe * EV]) = pk[x];
+#pragma unroll
+      for (int j = 0; j < EV; ++j) sKt[pe * EV + j][rr] = piece_elem<E>(pk[x], j);
     }
 #pragma unroll
     for (int x = 0; x < MPT; ++x) {
-      const int e = 4 * (tid + x * NT), rr = e / BC, cc = e % BC;
-      *reinterpret_cast<float4*>(&sM[rr][cc]) = pm[x];
+      const int e = 4 * (tid + x * WT), rr = e / BC, cc = e % BC;
+      if constexpr (REV) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sM[cc + j][rr] = pm[x][j];
+      } else {
+        *reinterpret_cast<v4f*>(&sM[rr][cc]) = pm[x];
+      }
     }
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * NT;
-      sV[e % NJW][e / NJW] = pv[x];
-    }
-    if (tid < BC) {
-      sg[tid] = pg;
-      sb[tid] = pb;
-    }
-    if (c > 0) fetch(c - 1);
-    __syncthreads();
-    const float gC = sg[BC - 1];
-    const float wr = expf(gC - sg[r]), egr = expf(sg[r]);
-    // dU = w . (K dS1) + V~
-    for (int jj = 0; jj < CPW; ++jj) {
-      float a = 0.f;
-#pragma unroll 2
-      for (int d = 0; d < DK; d += 8) {
-        float kf[8], sf[8];
-        row8(&sK[r][d], kf);
-        row8(&sS[j0 + jj][d], sf);
-        for (int x = 0; x < 8; ++x) a = fmaf(kf[x], sf[x], a);
-      }
-      sU[j0 + jj][r] = fmaf(wr, a, sV[j0 + jj][r]);
-    }
-    __syncthreads();
-    // e^g . dX with dX = diag(beta) Minv^T dU
-    for (int jj = 0; jj < CPW; ++jj) {
-      float a = 0.f;
-#pragma unroll 8
-      for (int i = r; i < BC; ++i) a = fmaf(sM[i][r], sU[j0 + jj][i], a);
-      sX[j0 + jj][r] = egr * sb[r] * a;
-    }
-    __syncthreads();
-    const float gam = expf(gC);
+      const int e = tid + x * WT, rr = e / VV, pe = e % VV;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const float4* x4 = reinterpret_cast<const float4*>(&sX[sj + e][0]);
-      float a = 0.f;
-#pragma unroll 4
-      for (int i4 = 0; i4 < BC / 4; ++i4) {
-        const float4 xx = x4[i4];
-        const int i = 4 * i4;
-        a = fmaf(lds_f(sK[i][sd]), xx.x, a);
-        a = fmaf(lds_f(sK[i + 1][sd]), xx.y, a);
-        a = fmaf(lds_f(sK[i + 2][sd]), xx.z, a);
-        a = fmaf(lds_f(sK[i + 3][sd]), xx.w, a);
-      }
-      s[e] = fmaf(gam, s[e], cterm[e] - a);
+      for (int j = 0; j < VEV; ++j) sV[VEV * pe + j][rr] = lds_f(piece_elem<VE>(pv[x], j));
     }
+    if (tid < BC) {  // wave 0: one token per lane
+      const float gC = __shfl(pg, BC - 1);
+      const float eg = expf(pg);
+      sEG[tid] = eg;
+      sB[tid] = pb;
+      sW[tid] = expf(gC - pg);
+      sEB[tid] = eg * pb;
+      if (tid == 0) sGam = expf(gC);
+    }
+  };
+  // four consecutive elements of an LDS row as fp32 (an A operand of four K = 4 steps)
+  auto rd4 = [](const E* p) __attribute__((always_inline)) {
+    float f[4];
+    if constexpr (MODE == 0) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      f[0] = __uint_as_float(u.x << 16);
+      f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+      f[2] = __uint_as_float(u.y << 16);
+      f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else {
+      const float4 u = *reinterpret_cast<const float4*>(p);
+      f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+    }
+    return float4{f[0], f[1], f[2], f[3]};
+  };
+  auto el4 = [](const float4& x, int i) __attribute__((always_inline)) {
+    return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+  };
+
+  // ---- the carried matrix ----
+  v4f S[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[dt][i] = sin ? sin[(static_cast<size_t>(bh) * DK + 16 * dt + 4 * gq + i) * DV + col] : 0.f;
+
+  const int c_first = REV ? nc - 1 : 0, c_step = REV ? -1 : 1;
+  fetch(c_first);
+  for (int n = 0; n < nc; ++n) {
+    const int c = c_first + n * c_step;
+    __syncthreads();  // every wave's reads of the previous chunk's rows are done
+    stage();
+    // the prefetched registers are consumed (and, for the reverse walk, this lane's elements of
+    // Q^T (e^g . dO) have arrived) before this chunk's slot is overwritten below
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // per 16-row tile, through the wave's transpose tile (LDS operations of a wave run in order):
+    // the reverse walk's Q^T (e^g . dO) into the accumulator layout, then the carried matrix out
+    // to this chunk's slot in 16-byte pieces
+    float cterm[REV ? NDT * 4 : 1];
+    {
+      float* D = sdump + (static_cast<size_t>(bh) * nc + c) * DK * DV;
+      float (*tr)[20] = sTr[w];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        if constexpr (REV) {
+          *reinterpret_cast<v4f*>(&tr[prow][4 * (lane & 3)]) = pc[dt];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cterm[4 * dt + i] = tr[4 * gq + i][ln];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tr[4 * gq + i][ln] = S[dt][i];
+        *reinterpret_cast<v4f*>(D + (16 * dt + prow) * DV + pcol) = *reinterpret_cast<const v4f*>(&tr[prow][4 * (lane & 3)]);
+      }
+    }
+    if (n + 1 < nc) fetch(c + c_step);
     __syncthreads();
+
+    // R = K S (token tiles mt)
+    v4f R[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) R[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      float4 a[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = rd4(&sK[16 * mt + ln][16 * dt + 4 * gq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) R[mt] = mfma4(el4(a[mt], i), S[dt][i], R[mt]);
+    }
+    // forward: X = beta . (V - e^g . R); reverse: dU = w . R + V~
+    v4f X[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 vv = *reinterpret_cast<const float4*>(&sV[16 * w + ln][16 * mt + 4 * gq]);
+      const float4 eg = *reinterpret_cast<const float4*>(&sEG[16 * mt + 4 * gq]);
+      const float4 bb = *reinterpret_cast<const float4*>(&sB[16 * mt + 4 * gq]);
+      const float4 ww = *reinterpret_cast<const float4*>(&sW[16 * mt + 4 * gq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (REV) X[mt][i] = fmaf(el4(ww, i), R[mt][i], el4(vv, i));
+        else X[mt][i] = el4(bb, i) * (el4(vv, i) - el4(eg, i) * R[mt][i]);
+      }
+    }
+    // forward: U = Minv X (lower triangular blocks kt <= mt); reverse: Minv^T dU (kt >= mt)
+    v4f U[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) U[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      float4 a[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        if (REV ? kt >= mt : kt <= mt) a[mt] = *reinterpret_cast<const float4*>(&sM[16 * mt + ln][16 * kt + 4 * gq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          if (REV ? kt >= mt : kt <= mt) U[mt] = mfma4(el4(a[mt], i), X[kt][i], U[mt]);
+    }
+    // forward: Y = w . U, S <- e^{g_C} S + K^T Y;  reverse: Y = -e^g . beta . (Minv^T dU),
+    // dS <- e^{g_C} dS + Q^T (e^g . dO) + K^T Y
+    v4f Y[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 eb = *reinterpret_cast<const float4*>(&sEB[16 * mt + 4 * gq]);
+      const float4 ww = *reinterpret_cast<const float4*>(&sW[16 * mt + 4 * gq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (REV) Y[mt][i] = -el4(eb, i) * U[mt][i];
+        else Y[mt][i] = el4(ww, i) * U[mt][i];
+      }
+    }
+    const float gam = sGam;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (REV) S[dt][i] = fmaf(gam, S[dt][i], cterm[4 * dt + i]);
+        else S[dt][i] = gam * S[dt][i];
+      }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      float4 a[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) a[dt] = rd4(&sKt[16 * dt + ln][16 * kt + 4 * gq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) S[dt] = mfma4(el4(a[dt], i), Y[kt][i], S[dt]);
+    }
   }
-  if (dinit)
-    for (int e = 0; e < EPT; ++e) dinit[(static_cast<size_t>(bh) * DK + sd) * DV + jb + sj + e] = s[e];
+  if (slast) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) slast[(static_cast<size_t>(bh) * DK + 16 * dt + 4 * gq + i) * DV + col] = S[dt][i];
+  }
 }
 
 // Sum over the TPRW adjacent lanes that share a chunk row.
@@ -893,13 +909,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
       return launch_kernel(bwd_prep_kernel<MODE, DK>, dim3(a.nc, bh), blk, stream, a.q, a.k, a.log_alpha, a.eta, a.eps,
                            a.direct, a.T, a.H, a.nc, a.rec);
     case 1:
-      return launch_kernel(bwd_states_kernel<MODE, DK>, dim3(a.dv / NJ, bh), dim3(NT), stream, a.k, a.v, a.rec, a.init, a.T,
-                           a.H, a.dv, a.nc, a.states);
+      return launch_kernel(bwd_walk_kernel<MODE, DK, false>, dim3(a.dv / WCOL, bh), dim3(WT), stream, a.k, a.v, a.rec,
+                           a.init, a.T, a.H, a.dv, a.nc, a.states, static_cast<float*>(nullptr));
     case 2:
       return launch_kernel(bwd_dprep_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.dout, a.rec, a.T, a.H,
                            a.dv, a.nc, a.vt, a.dstates);
     case 3:
-      return launch_kernel(bwd_dstates_kernel<MODE, DK>, dim3(a.dv / NJW, bh), dim3(NT), stream, a.k, a.vt, a.rec,
+      return launch_kernel(bwd_walk_kernel<MODE, DK, true>, dim3(a.dv / WCOL, bh), dim3(WT), stream, a.k, a.vt, a.rec,
                            a.dfin, a.T, a.H, a.dv, a.nc, a.dstates, a.ginit);
     default:
       return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.k, a.v, a.eta, a.dout,
