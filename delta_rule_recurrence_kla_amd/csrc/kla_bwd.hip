@@ -303,15 +303,19 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
     const float* R = rec + cidx * RECF;
 #pragma unroll
     for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * WT, rr = e / KV, pe = e % KV, t = c * BC + rr;
+      const int e = tid + x * WT, rr = e % BC, pe = e / BC, t = c * BC + rr;
       pk[x] = t < T ? *(reinterpret_cast<const uint4*>(static_cast<const E*>(k) + tok(b, t, T, H, h) * DK) + pe)
                     : uint4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int x = 0; x < MPT; ++x) pm[x] = reinterpret_cast<const v4f*>(R + REC_M)[tid + x * WT];
+    for (int x = 0; x < MPT; ++x) {
+      // forward: row-major pieces (coalesced); reverse: consecutive lanes take consecutive rows
+      const int e = tid + x * WT;
+      pm[x] = reinterpret_cast<const v4f*>(R + REC_M)[REV ? (e % BC) * (BC / 4) + e / BC : e];
+    }
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * WT, rr = e / VV, pe = e % VV, t = c * BC + rr;
+      const int e = tid + x * WT, rr = e % BC, pe = e / BC, t = c * BC + rr;
       if constexpr (REV) {  // V~ = P^T dO of the chunk, fp32 [BC][DV] (zero rows past T already)
         pv[x] = *reinterpret_cast<const uint4*>(static_cast<const float*>(vin) + (cidx * BC + rr) * DV + jb + VEV * pe);
       } else {
@@ -332,24 +336,26 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < KPT; ++x) {
-      const int e = tid + x * WT, rr = e / KV, pe = e % KV;
+      const int e = tid + x * WT, rr = e % BC, pe = e / BC;
       *reinterpret_cast<uint4*>(&sK[rr][pe * EV]) = pk[x];
 #pragma unroll
       for (int j = 0; j < EV; ++j) sKt[pe * EV + j][rr] = piece_elem<E>(pk[x], j);
     }
 #pragma unroll
     for (int x = 0; x < MPT; ++x) {
-      const int e = 4 * (tid + x * WT), rr = e / BC, cc = e % BC;
+      const int e = tid + x * WT;
       if constexpr (REV) {
+        const int rr = e % BC, cc = 4 * (e / BC);
 #pragma unroll
         for (int j = 0; j < 4; ++j) sM[cc + j][rr] = pm[x][j];
       } else {
+        const int rr = (4 * e) / BC, cc = (4 * e) % BC;
         *reinterpret_cast<v4f*>(&sM[rr][cc]) = pm[x];
       }
     }
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * WT, rr = e / VV, pe = e % VV;
+      const int e = tid + x * WT, rr = e % BC, pe = e / BC;
 #pragma unroll
       for (int j = 0; j < VEV; ++j) sV[VEV * pe + j][rr] = lds_f(piece_elem<VE>(pv[x], j));
     }
@@ -594,7 +600,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   v4f mP[2], mT[2], mQ[NTW], mK[NTW];
   for (int u = 0; u < 2; ++u) mP[u] = mT[u] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int u = 0; u < NTW; ++u) mQ[u] = mK[u] = v4f{0.f, 0.f, 0.f, 0.f};
-  // the products after the column blocks accumulate in the row layout
+  // row-layout copies of dQ and dK, filled from the MFMA tiles at the end
   float accQ[DQ], accK[DQ];
   for (int i = 0; i < DQ; ++i) accQ[i] = accK[i] = 0.f;
   float dwp = 0.f, degp = 0.f, gamp = 0.f;
@@ -775,55 +781,82 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __syncthreads();
   for (int ii = 0; ii < IPT; ++ii) m1[r * MP + i0 + ii] = dqk[ii];
   __syncthreads();
-  for (int i = 0; i < BC; ++i) {
-    const float a = m1[r * MP + i], at = m1[i * MP + r];
-    const float4* ki = reinterpret_cast<const float4*>(&sK[i][d0]);
-    const float4* qi = reinterpret_cast<const float4*>(&sQ[i][d0]);
-    for (int q4 = 0; q4 < DQ / 4; ++q4) {
-      const float4 kk = ki[q4], qq = qi[q4];
-      accQ[4 * q4 + 0] = fmaf(a, kk.x, accQ[4 * q4 + 0]);
-      accQ[4 * q4 + 1] = fmaf(a, kk.y, accQ[4 * q4 + 1]);
-      accQ[4 * q4 + 2] = fmaf(a, kk.z, accQ[4 * q4 + 2]);
-      accQ[4 * q4 + 3] = fmaf(a, kk.w, accQ[4 * q4 + 3]);
-      accK[4 * q4 + 0] = fmaf(at, qq.x, accK[4 * q4 + 0]);
-      accK[4 * q4 + 1] = fmaf(at, qq.y, accK[4 * q4 + 1]);
-      accK[4 * q4 + 2] = fmaf(at, qq.z, accK[4 * q4 + 2]);
-      accK[4 * q4 + 3] = fmaf(at, qq.w, accK[4 * q4 + 3]);
+  // The 64 x 64 products below run on the fp32 MFMA, wave wv on row tile mt and column tiles
+  // nt0 + 2u (a K = 4 step: lane l supplies A[row 16 mt + l % 16][k = 4 s + l / 16] and
+  // B[k][col]; the result's rows 16 mt + 4 (l / 16) + e, column col sit in lane l's acc[e]).
+  const int arow = 16 * mt + ln;
+  // dQ += dQK K and dK += dQK^T Q, into the dQ and dK tiles
+#pragma unroll 4
+  for (int s4 = 0; s4 < BC / 4; ++s4) {
+    const int kk = 4 * s4 + gq;
+    const float a = m1[arow * MP + kk], at = m1[kk * MP + arow];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      const int col = 16 * (nt0 + 2 * u) + ln;
+      mQ[u] = mfma4(a, sK[kk][col], mQ[u]);
+      mK[u] = mfma4(at, sQ[kk][col], mK[u]);
     }
   }
-  if (tid < BC) {  // dbeta from T' = Minv diag(beta): column sums of Minv . dT'
-    float a = 0.f;
-    for (int i = tid; i < BC; ++i) a = fmaf(sM[i][tid], m2[i * MP + tid], a);
-    sdb[tid] = a;
+  // W1 = Minv^T dT' diag(beta): Minv^T[row][k] = Minv[k][row] is zero for k < row, so the
+  // contraction starts at this row tile. dbeta_i (T' = Minv diag(beta)) is the diagonal of
+  // Minv^T dT' before the scaling.
+  v4f w1t[2];
+  for (int u = 0; u < 2; ++u) w1t[u] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s4 = 4 * mt; s4 < BC / 4; ++s4) {
+    const int kk = 4 * s4 + gq;
+    const float a = sM[kk][arow];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) w1t[u] = mfma4(a, m2[kk * MP + 16 * (nt0 + 2 * u) + ln], w1t[u]);
   }
-  // W1 = Minv^T dT' diag(beta)
-  float w1[IPT];
-  for (int ii = 0; ii < IPT; ++ii) {
-    const int i = i0 + ii;
-    float a = 0.f;
-    for (int j = r; j < BC; ++j) a = fmaf(sM[j][r], m2[j * MP + i], a);
-    w1[ii] = a * sb[i];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (nt0 + 2 * u == mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * gq + e == ln) sdb[arow] = w1t[u][e];
+  __syncthreads();  // every read of dQK (m1) and dT' (m2) is done
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int col = 16 * (nt0 + 2 * u) + ln;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m1[(16 * mt + 4 * gq + e) * MP + col] = w1t[u][e] * sb[col];
   }
   __syncthreads();
-  for (int ii = 0; ii < IPT; ++ii) m1[r * MP + i0 + ii] = w1[ii];
+  // dA = -W1 Minv^T (used below on the strict lower triangle) into m2
+  {
+    v4f dat[2];
+    for (int u = 0; u < 2; ++u) dat[u] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s4 = 0; s4 < BC / 4; ++s4) {
+      const int kk = 4 * s4 + gq;
+      const float a = m1[arow * MP + kk];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dat[u] = mfma4(a, sM[16 * (nt0 + 2 * u) + ln][kk], dat[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int col = 16 * (nt0 + 2 * u) + ln;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m2[(16 * mt + 4 * gq + e) * MP + col] = -dat[u][e];
+    }
+  }
   __syncthreads();
-  // dA = strict_lower(-W1 Minv^T); A = beta_r Dl G gives dbeta, dDl and dG
+  // A = beta_r Dl G gives dbeta, dDl and dG
   float dbp = 0.f;
   float dG[IPT];
   for (int ii = 0; ii < IPT; ++ii) {
     const int i = i0 + ii;
     dG[ii] = 0.f;
     if (i < r) {
-      float a = 0.f;
-      for (int j = 0; j <= i; ++j) a = fmaf(m1[r * MP + j], sM[i][j], a);
-      const float da = -a, dl = expf(sg[r] - sg[i]), G = sPG[i][r];
+      const float da = m2[r * MP + i], dl = expf(sg[r] - sg[i]), G = sPG[i][r];
       dbp = fmaf(da * dl, G, dbp);
       ddl[ii] = fmaf(da * sb[r] * dl, G, ddl[ii]);
       dG[ii] = da * sb[r] * dl;
     }
   }
   dbp = quad_sum(dbp);
-  __syncthreads();  // m1 (W1) and m2 (dT') fully read
+  __syncthreads();  // every thread's reads of dA (m2) are done
   for (int ii = 0; ii < IPT; ++ii) {
     m2[r * MP + i0 + ii] = dG[ii];
     m1[r * MP + i0 + ii] = ddl[ii];
@@ -836,17 +869,13 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     sdb[r] += dbp;
   }
   __syncthreads();
-  // dK += (dG + dG^T) K
-  for (int i = 0; i < BC; ++i) {
-    const float a = m2[r * MP + i] + m2[i * MP + r];
-    const float4* ki = reinterpret_cast<const float4*>(&sK[i][d0]);
-    for (int q4 = 0; q4 < DQ / 4; ++q4) {
-      const float4 kk = ki[q4];
-      accK[4 * q4 + 0] = fmaf(a, kk.x, accK[4 * q4 + 0]);
-      accK[4 * q4 + 1] = fmaf(a, kk.y, accK[4 * q4 + 1]);
-      accK[4 * q4 + 2] = fmaf(a, kk.z, accK[4 * q4 + 2]);
-      accK[4 * q4 + 3] = fmaf(a, kk.w, accK[4 * q4 + 3]);
-    }
+  // dK += (dG + dG^T) K, into the dK tiles
+#pragma unroll 4
+  for (int s4 = 0; s4 < BC / 4; ++s4) {
+    const int kk = 4 * s4 + gq;
+    const float a = m2[arow * MP + kk] + m2[kk * MP + arow];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) mK[u] = mfma4(a, sK[kk][16 * (nt0 + 2 * u) + ln], mK[u]);
   }
   if (tid < BC) {  // one wave: lane i is token i of the chunk
     const int i = tid, t = c * BC + i;
