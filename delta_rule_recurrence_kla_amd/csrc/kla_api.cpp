@@ -515,8 +515,8 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
     ends_floats += static_cast<long long>(bh) * nleft[nscale] * dk * dv;
   }
   const size_t ends_bytes = align256(static_cast<size_t>(ends_floats) * 4);
-  // bf16 with dk <= 128: the right walks run on the DMA-fed walk kernel, which reads compact
-  // records (T' and the gates; it forms P itself), from a second prep pass
+  // bf16 with dk <= 128: the left and right walks run on the DMA-fed walk kernels, which read
+  // compact records (T' and the gates; the right walks form P themselves), from a second prep pass
   const bool compact = kla::state_dma_supported(mode, dk);
   const size_t crec_bytes = compact ? align256(bh * nc * static_cast<size_t>(kla::record_bytes(mode, dk))) : 0;
   void* ws = nullptr;
@@ -539,7 +539,7 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
   // scale (the scales add to the same outputs)
   if (e == hipSuccess && nscale > 0)
     e = timed("kla_loglinear_left", stream, [&] {
-      return kla::launch_loglinear_left(mode, d, k, v, rec, nscale, half, nleft, ends_off, ends, stream);
+      return kla::launch_loglinear_left(mode, d, k, v, rec, crec, nscale, half, nleft, ends_off, ends, stream);
     });
   for (int i = 0; e == hipSuccess && i < nscale; ++i) {
     e = timed("kla_loglinear_right", stream, [&] {

@@ -94,9 +94,17 @@ hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, c
                                   int L, float* out, hipStream_t stream);
 // All scales' left walks in one grid: scale i has half-blocks of half[i] chunks, nleft[i] left
 // ones per head, and writes their end states at ends + ends_off[i] (floats).
-hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int nscale,
-                                 const int* half, const int* nleft, const long long* ends_off, float* ends,
-                                 hipStream_t stream);
+// rec_compact: compact records of the same chunks (bf16, dk <= 128): the left walks of every
+// scale then run in one grid of the DMA-fed map walk; null takes one grid of register-prefetch
+// walks on the full records.
+// The DMA-fed map walk over the left half-blocks of every scale (plain state from zero, end
+// states into ends + ends_off[i]), one grid; bf16, dk in {64, 128}, DV a multiple of 64.
+hipError_t launch_left_walks_dma(int dk, const void* k, const void* v, const uint8_t* rec, int T, int H, int DV,
+                                 int nc, int BH, int nscale, const int* half, const int* nleft,
+                                 const long long* ends_off, float* ends, hipStream_t stream);
+hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
+                                 const uint8_t* rec_compact, int nscale, const int* half, const int* nleft,
+                                 const long long* ends_off, float* ends, hipStream_t stream);
 // rec_compact: compact records of the same chunks (bf16, dk <= 128), for the DMA-fed walk; null
 // takes the register-prefetch walk on the full records.
 hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec,

@@ -613,11 +613,14 @@ static hipError_t dispatch_scale(int mode, int dk, int nwg, const StateArgs& a, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec, int nscale,
-                                 const int* half, const int* nleft, const long long* ends_off, float* ends,
-                                 hipStream_t stream) {
+hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
+                                 const uint8_t* rec_compact, int nscale, const int* half, const int* nleft,
+                                 const long long* ends_off, float* ends, hipStream_t stream) {
   if (nscale < 1 || nscale > kMaxScales) return hipErrorInvalidValue;
   const int ncg = d.dv / NCOLS_STATE;
+  if (rec_compact && !d.lift && state_dma_supported(mode, d.dk))
+    return launch_left_walks_dma(d.dk, k, v, rec_compact, d.T, d.H, d.dv, d.nc, d.B * d.H, nscale, half, nleft,
+                                 ends_off, ends, stream);
   StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, half[0], nullptr, 1, nullptr, ends, d.dv, nleft[0], 0, ncg,
               nleft[0]};
   a.seg_mul = 2;

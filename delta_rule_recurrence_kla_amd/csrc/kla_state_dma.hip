@@ -5,9 +5,10 @@
 //   R  = V - diag(e^g) K S,   U = T' R,   O = diag(e^g) Q S + P U,
 // with one workgroup per (b, h, 64 state columns), 16 columns per wave, and the state held in
 // MFMA accumulator registers for the whole walk over the chunks. Two kernels:
-//  * state_map_kernel walks a segment without outputs on the augmented state [I | 0] and
-//    leaves the segment's affine map [M | N] (the scan's first phase): one compute wave per
-//    16 columns and a copy wave;
+//  * state_map_kernel walks a segment without outputs and leaves its end state: on the
+//    augmented state [I | 0] that is the segment's affine map [M | N] (the scan's first phase);
+//    on the plain state from zero, the state of the segment's own tokens (the left half-blocks
+//    of log-linear KLA). One compute wave per 16 columns and a copy wave;
 //  * state_walk_kernel walks with outputs (the sequential path, and the scan's walk from
 //    every segment's start): per 16 columns one wave runs the recurrence and another the
 //    output products, with a copy wave (see the comment above it).
@@ -45,6 +46,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
+constexpr int kDmaMaxScales = 24;  // scales of 1, 2, 4, ... chunks: enough for any int T
+
 struct StateDmaArgs {
   const void* q;
   const void* k;
@@ -70,6 +73,14 @@ struct StateDmaArgs {
   const float* lam;
   int lam_L;
   int lam_level;
+  // Several scales in one grid (map walks only, nscale > 0): workgroups [scale_wg[i],
+  // scale_wg[i + 1]) walk segments of scale_half[i] chunks, scale_nseg[i] per (b, h), and leave
+  // their end states at fin + scale_fin_off[i] (scale_nseg[i] per (b, h)).
+  int nscale;
+  int scale_wg[kDmaMaxScales + 1];
+  int scale_half[kDmaMaxScales];
+  int scale_nseg[kDmaMaxScales];
+  long long scale_fin_off[kDmaMaxScales];
 };
 
 namespace {
@@ -98,7 +109,7 @@ __device__ __forceinline__ void decode_wg_dma(int L, int ncg, int nunits, int& c
 
 constexpr int MAP_THREADS = 320;  // four compute waves and the copy wave
 
-template <int DK>
+template <int DK, bool AUG>
 __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) {
   using TR = Tr<MODE_BF16>;
   constexpr int NCOLS = 64;
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
   constexpr int R_OFF = V_OFF + VBYTES;
   constexpr int BUF = R_OFF + RECB;           // one buffer
   static_assert(KRB == 128 || KRB == 256, "dk must be 64 or 128");
-  static_assert(DK % NCOLS == 0, "identity/value columns must not share a workgroup");
+  static_assert(!AUG || DK % NCOLS == 0, "identity/value columns must not share a workgroup");
 
   // Two separate buffers (not one array indexed by parity): the compiler must see that the
   // copies into one buffer cannot alias the reads of the other, or it waits for the copies
@@ -123,17 +134,28 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a scalar
   const int gq = lane >> 4, ln = lane & 15;
+  int wg = blockIdx.x, nwg = gridDim.x, seg_chunks = a.seg_chunks, nseg = a.nseg, fin_segs = a.fin_segs;
+  float* fin = a.fin;
+  if (a.nscale > 0) {
+    int sc = 0;
+    while (sc + 1 < a.nscale && wg >= a.scale_wg[sc + 1]) ++sc;
+    wg -= a.scale_wg[sc];
+    nwg = a.scale_wg[sc + 1] - a.scale_wg[sc];
+    seg_chunks = a.scale_half[sc];
+    nseg = fin_segs = a.scale_nseg[sc];
+    fin = a.fin + a.scale_fin_off[sc];
+  }
   int cg, unit;
-  decode_wg_dma(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
-  const int bh = unit / a.nseg, seg = unit - bh * a.nseg;
+  decode_wg_dma(wg, a.ncg, nwg / a.ncg, cg, unit);
+  const int bh = unit / nseg, seg = unit - bh * nseg;
   const int H = a.H, T = a.T, DV = a.DV;
   const int b = bh / H, h = bh - b * H;
   const int col0 = cg * NCOLS;
   const int col = col0 + 16 * w + ln;
-  const bool ident = col0 < DK;  // identity columns (they carry M), else value columns (N)
-  const int vcol0 = col0 - DK;
-  const int c_begin = seg * a.seg_chunks;
-  const int c_end = min(a.nc, c_begin + a.seg_chunks);
+  const bool ident = AUG && col0 < DK;  // identity columns (they carry M), else value columns (N)
+  const int vcol0 = AUG ? col0 - DK : col0;
+  const int c_begin = (seg * a.seg_mul + a.seg_add) * seg_chunks;
+  const int c_end = min(a.nc, c_begin + seg_chunks);
 
   const int rowK = H * DK * 2, rowV = H * DV * 2;
   const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
@@ -309,8 +331,8 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
     if (c + 1 < c_end) chunk(lds1);
   }
 
-  if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
-    float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
+  if (fin && (!a.fin_last_only || seg == nseg - 1)) {
+    float* F = fin + (static_cast<size_t>(bh) * fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
 #pragma unroll
     for (int mt = 0; mt < DK / 16; ++mt) {
 #pragma unroll
@@ -671,6 +693,31 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
 
 bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 64 || dk == 128); }
 
+hipError_t launch_left_walks_dma(int dk, const void* k, const void* v, const uint8_t* rec, int T, int H, int DV,
+                                 int nc, int BH, int nscale, const int* half, const int* nleft,
+                                 const long long* ends_off, float* ends, hipStream_t stream) {
+  if (nscale < 1 || nscale > kDmaMaxScales) return hipErrorInvalidValue;
+  const int ncg = DV / 64;
+  StateDmaArgs a{nullptr, k, v, rec, T, H, DV, nc, 0, nullptr, 0, nullptr, ends, DV, 0, 0, ncg, 0, 2, 0,
+                 nullptr, 0, 0};
+  // coarsest scale first: its long walks start at once, and the short walks of the fine
+  // scales fill the chip behind them
+  a.nscale = nscale;
+  int nwg = 0;
+  for (int j = 0; j < nscale; ++j) {
+    const int i = nscale - 1 - j;
+    a.scale_wg[j] = nwg;
+    a.scale_half[j] = half[i];
+    a.scale_nseg[j] = nleft[i];
+    a.scale_fin_off[j] = ends_off[i];
+    nwg += ncg * nleft[i] * BH;
+  }
+  a.scale_wg[nscale] = nwg;
+  if (dk == 64) return launch_kernel(state_map_kernel<64, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
+  if (dk == 128) return launch_kernel(state_map_kernel<128, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
@@ -678,18 +725,20 @@ hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void
                             int lam_L, int lam_level) {
   const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, seg_chunks, init, init_segs, out, fin, fin_ld, fin_segs,
                        fin_last_only, ncg, nseg, seg_mul, seg_add, lam, lam_L, lam_level};
-  if (with_out == aug) return hipErrorInvalidValue;  // a walk either has outputs or carries [M | N]
+  if (with_out && aug) return hipErrorInvalidValue;  // a walk with outputs carries the plain state
   const bool acc = lam != nullptr;
   if (acc && !with_out) return hipErrorInvalidValue;
   if (dk == 64) {
     if (acc) return launch_kernel(state_walk_kernel<64, true>, dim3(nwg), dim3(WALK_THREADS), stream, a);
     if (with_out) return launch_kernel(state_walk_kernel<64, false>, dim3(nwg), dim3(WALK_THREADS), stream, a);
-    return launch_kernel(state_map_kernel<64>, dim3(nwg), dim3(MAP_THREADS), stream, a);
+    if (aug) return launch_kernel(state_map_kernel<64, true>, dim3(nwg), dim3(MAP_THREADS), stream, a);
+    return launch_kernel(state_map_kernel<64, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
   }
   if (dk == 128) {
     if (acc) return launch_kernel(state_walk_kernel<128, true>, dim3(nwg), dim3(WALK_THREADS), stream, a);
     if (with_out) return launch_kernel(state_walk_kernel<128, false>, dim3(nwg), dim3(WALK_THREADS), stream, a);
-    return launch_kernel(state_map_kernel<128>, dim3(nwg), dim3(MAP_THREADS), stream, a);
+    if (aug) return launch_kernel(state_map_kernel<128, true>, dim3(nwg), dim3(MAP_THREADS), stream, a);
+    return launch_kernel(state_map_kernel<128, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
   }
   return hipErrorInvalidValue;
 }
