@@ -41,6 +41,8 @@ constexpr int NJ = 16;    // state columns per walk workgroup / per grads column
 constexpr int REC_M = 0, REC_PG = BC * BC, REC_G = 2 * BC * BC, REC_B = REC_G + BC, REC_D = REC_B + BC;
 constexpr int RECF = REC_D + 2 * BC;
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 template <int MODE>
 __device__ __forceinline__ float ldin(const void* p, size_t i) {
   if constexpr (MODE == 0) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
@@ -107,48 +109,103 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
   const int t = c * BC + tid;
   if (tid < BC) sla[tid] = t < T ? log_alpha[tok(b, t, T, H, h)] : 0.f;
   __syncthreads();
-  if (tid < BC) {
-    float gs = 0.f;
-    for (int i = 0; i <= tid; ++i) gs += sla[i];
-    float n = 0.f;
-    for (int d = 0; d < DK; ++d) n = fmaf(lds_f(sK[tid][d]), lds_f(sK[tid][d]), n);
-    const float et = t < T ? eta[tok(b, t, T, H, h)] : 0.f;
-    const float den = n + eps;
-    const float beta = direct ? et : (den != 0.f ? et / den : 0.f);
-    sg[tid] = gs;
-    sb[tid] = beta;
-    R[REC_G + tid] = gs;
-    R[REC_B + tid] = beta;
-    R[REC_D + tid] = den;
-  }
-  __syncthreads();
-  // Q K^T and K K^T in 4 x 4 tiles (rows r0 + 4a, columns i0 + 4b... strided by 16 so that a
-  // wave's reads of K rows spread over banks). Lower triangle incl. the diagonal: P = Dl . Q K^T;
-  // strict upper: K K^T (symmetric, so entry [r][i], i > r, is also G[i][r]);
-  // A = strict lower beta_r Dl G.
-  {
-    const int r0 = tid >> 4, i0 = tid & 15;
-    float qk[4][4] = {}, kk[4][4] = {};
-    for (int d = 0; d < DK; ++d) {
-      float qa[4], ka[4], kb[4];
-      for (int a = 0; a < 4; ++a) {
-        qa[a] = lds_f(sQ[r0 + 16 * a][d]);
-        ka[a] = lds_f(sK[r0 + 16 * a][d]);
-        kb[a] = lds_f(sK[i0 + 16 * a][d]);
+  if constexpr (MODE == 0) {
+    // bf16 inputs: Q K^T and K K^T on the bf16 MFMA (exact products, fp32 accumulation), wave w
+    // on row tile w and all four column tiles (lane l supplies row l % 16, columns
+    // 32 kb + 8 (l / 16) + 0..7 of both operands; the result's rows 4 (l / 16) + e, column l % 16
+    // sit in lane l's acc[e]); ||k||^2 is the diagonal of K K^T.
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    const int lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
+    v4f qk[4], kk[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) qk[nt] = kk[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      const bf16x8_t aq = *reinterpret_cast<const bf16x8_t*>(&sQ[16 * wv + ln][32 * kb + 8 * gq]);
+      const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(&sK[16 * wv + ln][32 * kb + 8 * gq]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(&sK[16 * nt + ln][32 * kb + 8 * gq]);
+        qk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bk, qk[nt], 0, 0, 0);
+        kk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bk, kk[nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * gq + e == ln) sb[16 * wv + ln] = kk[wv][e];  // ||k_r||^2, until beta replaces it
+    __syncthreads();
+    if (tid < BC) {  // wave 0, lane r = token r: g by an inclusive scan over the wave
+      float gs = sla[tid];
+#pragma unroll
+      for (int o = 1; o < BC; o <<= 1) {
+        const float y = __shfl_up(gs, o);
+        if (lane >= o) gs += y;
+      }
+      const float et = t < T ? eta[tok(b, t, T, H, h)] : 0.f;
+      const float den = sb[tid] + eps;
+      const float beta = direct ? et : (den != 0.f ? et / den : 0.f);
+      sg[tid] = gs;
+      sb[tid] = beta;
+      R[REC_G + tid] = gs;
+      R[REC_B + tid] = beta;
+      R[REC_D + tid] = den;
+    }
+    __syncthreads();
+    // lower triangle incl. the diagonal: P = Dl . Q K^T; strict upper: K K^T; A = strict lower
+    // beta_r Dl G
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wv + 4 * gq + e, i = 16 * nt + ln;
+        const float dl = i <= r ? expf(sg[r] - sg[i]) : 0.f;
+        R[REC_PG + r * BC + i] = i <= r ? dl * qk[nt][e] : kk[nt][e];
+        sA[r * AP + i] = i < r ? sb[r] * dl * kk[nt][e] : 0.f;
+      }
+  } else {  // fp32 inputs: the vector ALU in 4 x 4 register tiles
+    if (tid < BC) {
+      float gs = 0.f;
+      for (int i = 0; i <= tid; ++i) gs += sla[i];
+      float n = 0.f;
+      for (int d = 0; d < DK; ++d) n = fmaf(lds_f(sK[tid][d]), lds_f(sK[tid][d]), n);
+      const float et = t < T ? eta[tok(b, t, T, H, h)] : 0.f;
+      const float den = n + eps;
+      const float beta = direct ? et : (den != 0.f ? et / den : 0.f);
+      sg[tid] = gs;
+      sb[tid] = beta;
+      R[REC_G + tid] = gs;
+      R[REC_B + tid] = beta;
+      R[REC_D + tid] = den;
+    }
+    __syncthreads();
+    // Q K^T and K K^T in 4 x 4 tiles (rows r0 + 4a, columns i0 + 4b... strided by 16 so that a
+    // wave's reads of K rows spread over banks). Lower triangle incl. the diagonal: P = Dl . Q K^T;
+    // strict upper: K K^T (symmetric, so entry [r][i], i > r, is also G[i][r]);
+    // A = strict lower beta_r Dl G.
+    {
+      const int r0 = tid >> 4, i0 = tid & 15;
+      float qk[4][4] = {}, kk[4][4] = {};
+      for (int d = 0; d < DK; ++d) {
+        float qa[4], ka[4], kb[4];
+        for (int a = 0; a < 4; ++a) {
+          qa[a] = lds_f(sQ[r0 + 16 * a][d]);
+          ka[a] = lds_f(sK[r0 + 16 * a][d]);
+          kb[a] = lds_f(sK[i0 + 16 * a][d]);
+        }
+        for (int a = 0; a < 4; ++a)
+          for (int e = 0; e < 4; ++e) {
+            qk[a][e] = fmaf(qa[a], kb[e], qk[a][e]);
+            kk[a][e] = fmaf(ka[a], kb[e], kk[a][e]);
+          }
       }
       for (int a = 0; a < 4; ++a)
         for (int e = 0; e < 4; ++e) {
-          qk[a][e] = fmaf(qa[a], kb[e], qk[a][e]);
-          kk[a][e] = fmaf(ka[a], kb[e], kk[a][e]);
+          const int r = r0 + 16 * a, i = i0 + 16 * e;
+          const float dl = i <= r ? expf(sg[r] - sg[i]) : 0.f;
+          R[REC_PG + r * BC + i] = i <= r ? dl * qk[a][e] : kk[a][e];
+          sA[r * AP + i] = i < r ? sb[r] * dl * kk[a][e] : 0.f;
         }
     }
-    for (int a = 0; a < 4; ++a)
-      for (int e = 0; e < 4; ++e) {
-        const int r = r0 + 16 * a, i = i0 + 16 * e;
-        const float dl = i <= r ? expf(sg[r] - sg[i]) : 0.f;
-        R[REC_PG + r * BC + i] = i <= r ? dl * qk[a][e] : kk[a][e];
-        sA[r * AP + i] = i < r ? sb[r] * dl * kk[a][e] : 0.f;
-      }
   }
   __syncthreads();
   // (I + A)^-1 is unit lower triangular. Forward substitution with one column per lane held in
@@ -177,7 +234,6 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
   }
 }
 
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 // One fp32 MFMA step (16 x 16 tile, K = 4, full fp32 products): lane l supplies A[l % 16][l / 16]
 // and B[l / 16][l % 16]; the tile's rows 4 (l / 16) + i, column l % 16, sit in lane l's acc[i].
