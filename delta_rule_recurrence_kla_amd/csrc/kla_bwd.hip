@@ -241,54 +241,105 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+// Element j of a 16-byte piece of E values, taken from the piece's words (no address of the
+// register piece is taken, so it stays in registers).
+template <class E>
+__device__ __forceinline__ E piece_elem(const uint4& u, int j) {
+  const uint32_t wd = j / (4 / sizeof(E)) == 0 ? u.x : j / (4 / sizeof(E)) == 1 ? u.y : j / (4 / sizeof(E)) == 2 ? u.z : u.w;
+  if constexpr (sizeof(E) == 2) return static_cast<E>((j & 1) ? wd >> 16 : wd & 0xFFFFu);
+  else return __uint_as_float(wd);
+}
+
 // Chunk-local terms of the reverse walk, all chunks in parallel on the fp32 MFMA:
 //   V~ = P^T dO (64 x dv) into vt, and Q^T (e^g . dO) (dk x dv) into the chunk's slot of dstates,
 // which the reverse walk reads and then overwrites with the chunk-end state gradient.
+// One workgroup per (b, h, chunk), one wave per 16 columns of dO. A wave loads its columns of
+// dO straight into the accumulator layout of a 64 x 16 tile set (lane l: tokens 16 t + 4 (l/16)
+// + e, column l % 16), which is the B operand of the K = 4 steps over the chunk's tokens; the A
+// operands (P^T and Q^T, staged transposed in LDS) are one 16- or 8-byte read per four steps.
 template <int MODE, int DK>
 __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const float* dout, const float* rec, int T, int H,
                                                        int DV, int nc, float* vt, float* cq) {
-  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   using E = typename LdsIn<MODE>::type;
-  constexpr int EP = MODE == 0 ? DK + 8 : DK + 4;  // 16-byte rows
-  __shared__ __align__(16) E sQ[BC][EP];
-  __shared__ float sO[BC][128 + 1];  // dv <= 128
-  __shared__ float sP[BC][MP];
-  __shared__ float seg[BC];
+  constexpr int EV = 16 / sizeof(E), KV = DK / EV;  // elements per 16-byte piece, pieces per query row
+  constexpr int QTP = BC + EV;                     // pitch of Q^T [DK][QTP] (16-byte rows)
+  constexpr int PTP = BC + 4;                      // pitch of P^T [BC][PTP]
+  __shared__ __align__(16) E sQt[DK][QTP];
+  __shared__ __align__(16) float sPt[BC][PTP];
+  __shared__ __align__(16) float seg[BC];
+  const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int nthr = static_cast<int>(blockDim.x);
+  const int lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
   const float* R = rec + (static_cast<size_t>(bh) * nc + c) * RECF;
-  load_rows_vec<MODE, DK, EP, E>(sQ, q, b, h, c, T, H);
-  for (int e = tid; e < BC * DV; e += NT) {
-    const int rr = e / DV, j = e % DV, t = c * BC + rr;
-    sO[rr][j] = t < T ? dout[tok(b, t, T, H, h) * DV + j] : 0.f;
+  const size_t cidx = static_cast<size_t>(bh) * nc + c;
+  const int col = 16 * wv + ln;
+  // this wave's columns of dO in the accumulator layout (zero past T)
+  float o[4][4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = c * BC + 16 * tt + 4 * gq + e;
+      o[tt][e] = t < T ? dout[tok(b, t, T, H, h) * DV + col] : 0.f;
+    }
+  // Q^T and P^T (P's lower triangle incl. the diagonal) into LDS; consecutive lanes take
+  // consecutive tokens, so the transposed writes hit consecutive words
+  for (int e = tid; e < BC * KV; e += nthr) {
+    const int rr = e % BC, pe = e / BC, t = c * BC + rr;
+    uint4 u = {0u, 0u, 0u, 0u};
+    if (t < T) u = *(reinterpret_cast<const uint4*>(static_cast<const E*>(q) + tok(b, t, T, H, h) * DK) + pe);
+#pragma unroll
+    for (int j = 0; j < EV; ++j) sQt[pe * EV + j][rr] = piece_elem<E>(u, j);
   }
-  for (int e = tid; e < BC * BC; e += NT) sP[e / BC][e % BC] = R[REC_PG + e];
+  for (int e = tid; e < BC * BC / 4; e += nthr) {
+    const int rr = e % BC, pc = e / BC;  // token rr, columns 4 pc .. 4 pc + 3 of its row of P
+    const v4f x = reinterpret_cast<const v4f*>(R + REC_PG)[rr * (BC / 4) + pc];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sPt[4 * pc + j][rr] = 4 * pc + j <= rr ? x[j] : 0.f;
+  }
   if (tid < BC) seg[tid] = expf(R[REC_G + tid]);
   __syncthreads();
-  const int lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
-  const int ntj = DV / 16, ntiles = (BC / 16 + DK / 16) * ntj;
-  const size_t cidx = static_cast<size_t>(bh) * nc + c;
-  for (int tile = wv; tile < ntiles; tile += NT / 64) {
-    const int mt = tile / ntj, col = 16 * (tile % ntj) + ln;
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    if (mt < BC / 16) {  // V~[r][j] = sum over i >= r of P[i][r] dO[i][j]
-      const int row = 16 * mt + ln;
-#pragma unroll 4
-      for (int kk = 0; kk < BC / 4; ++kk) {
-        const int i = 4 * kk + gq;
-        acc = mfma4(i >= row ? sP[i][row] : 0.f, sO[i][col], acc);
+  v4f P4[4], C4[DK / 16];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) P4[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dt = 0; dt < DK / 16; ++dt) C4[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const v4f eg = *reinterpret_cast<const v4f*>(&seg[16 * tt + 4 * gq]);
+    v4f ap[4];
+#pragma unroll
+    for (int mt = 0; mt <= tt; ++mt) ap[mt] = *reinterpret_cast<const v4f*>(&sPt[16 * mt + ln][16 * tt + 4 * gq]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int mt = 0; mt <= tt; ++mt) P4[mt] = mfma4(ap[mt][e], o[tt][e], P4[mt]);  // P^T[row][token] = 0 below
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      const E* pq = &sQt[16 * dt + ln][16 * tt + 4 * gq];
+      float aq[4];
+      if constexpr (MODE == 0) {
+        const uint2 w2 = *reinterpret_cast<const uint2*>(pq);
+        aq[0] = __uint_as_float(w2.x << 16);
+        aq[1] = __uint_as_float(w2.x & 0xFFFF0000u);
+        aq[2] = __uint_as_float(w2.y << 16);
+        aq[3] = __uint_as_float(w2.y & 0xFFFF0000u);
+      } else {
+        const v4f w4 = *reinterpret_cast<const v4f*>(pq);
+        aq[0] = w4[0]; aq[1] = w4[1]; aq[2] = w4[2]; aq[3] = w4[3];
       }
-      float* o = vt + (cidx * BC + 16 * mt + 4 * gq) * DV + col;
-      for (int e = 0; e < 4; ++e) o[e * DV] = acc[e];
-    } else {  // C[d][j] = sum over i of Q[i][d] e^{g_i} dO[i][j]
-      const int m2 = mt - BC / 16, d = 16 * m2 + ln;
-#pragma unroll 4
-      for (int kk = 0; kk < BC / 4; ++kk) {
-        const int i = 4 * kk + gq;
-        acc = mfma4(lds_f(sQ[i][d]), seg[i] * sO[i][col], acc);
-      }
-      float* o = cq + (cidx * DK + 16 * m2 + 4 * gq) * DV + col;
-      for (int e = 0; e < 4; ++e) o[e * DV] = acc[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) C4[dt] = mfma4(aq[e], eg[e] * o[tt][e], C4[dt]);
     }
   }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vt[(cidx * BC + 16 * mt + 4 * gq + e) * DV + col] = P4[mt][e];
+#pragma unroll
+  for (int dt = 0; dt < DK / 16; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cq[(cidx * DK + 16 * dt + 4 * gq + e) * DV + col] = C4[dt][e];
 }
 
 // The two walks on the fp32 MFMA, one kernel: one workgroup per (b, h, 64 state columns), four
@@ -309,14 +360,6 @@ __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const floa
 // The next chunk's rows are loaded into registers while the current chunk is computed.
 constexpr int WT = 256;     // threads of a walk workgroup: four waves
 
-// Element j of a 16-byte piece of E values, taken from the piece's words (no address of the
-// register piece is taken, so it stays in registers).
-template <class E>
-__device__ __forceinline__ E piece_elem(const uint4& u, int j) {
-  const uint32_t wd = j / (4 / sizeof(E)) == 0 ? u.x : j / (4 / sizeof(E)) == 1 ? u.y : j / (4 / sizeof(E)) == 2 ? u.z : u.w;
-  if constexpr (sizeof(E) == 2) return static_cast<E>((j & 1) ? wd >> 16 : wd & 0xFFFFu);
-  else return __uint_as_float(wd);
-}
 constexpr int WCOL = 64;    // state columns per walk workgroup
 
 template <int MODE, int DK, bool REV>
@@ -997,7 +1040,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
       return launch_kernel(bwd_walk_kernel<MODE, DK, false>, dim3(a.dv / WCOL, bh), dim3(WT), stream, a.k, a.v, a.rec,
                            a.init, a.T, a.H, a.dv, a.nc, a.states, static_cast<float*>(nullptr));
     case 2:
-      return launch_kernel(bwd_dprep_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.dout, a.rec, a.T, a.H,
+      return launch_kernel(bwd_dprep_kernel<MODE, DK>, dim3(a.nc, bh), dim3(64 * (a.dv / 16)), stream, a.q, a.dout, a.rec, a.T, a.H,
                            a.dv, a.nc, a.vt, a.dstates);
     case 3:
       return launch_kernel(bwd_walk_kernel<MODE, DK, true>, dim3(a.dv / WCOL, bh), dim3(WT), stream, a.k, a.vt, a.rec,
