@@ -1,5 +1,8 @@
-// Chunkwise backward of the KLA prefill (gradients for training), fp32 arithmetic: the vector
-// ALU and the fp32 MFMA (v_mfma_f32_16x16x4_f32, full fp32 products and accumulation).
+// Chunkwise backward of the KLA prefill (gradients for training) in fp32 arithmetic: the fp32
+// MFMA (v_mfma_f32_16x16x4_f32, full fp32 products and accumulation) and the vector ALU. For
+// bf16 inputs, products whose one operand is a bf16 input run on the bf16 MFMA: exactly when
+// both operands are inputs (Q K^T, K K^T), and with the fp32 operand as a hi + lo bf16 pair
+// (about 2^-17 of its size kept) in the gradients kernel's K S0, K dS1 and Q S0.
 //
 // The forward of one 64-token chunk with start state S0 (UT form of the delta rule, the
 // chunkwise parallel algorithm that the KLA page trains with; KLA page, "Implementation"):
@@ -42,6 +45,41 @@ constexpr int REC_M = 0, REC_PG = BC * BC, REC_G = 2 * BC * BC, REC_B = REC_G + 
 constexpr int RECF = REC_D + 2 * BC;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Eight fp32 values that are bf16 numbers (bf16 inputs widened in LDS) as a bf16 MFMA operand:
+// the upper halves, exactly.
+__device__ __forceinline__ bf16x8_t bf16_exact8(const float* p) {
+  const v4f a = *reinterpret_cast<const v4f*>(p), b = *reinterpret_cast<const v4f*>(p + 4);
+  u32x4_t w;
+  w[0] = (__float_as_uint(a[1]) & 0xFFFF0000u) | (__float_as_uint(a[0]) >> 16);
+  w[1] = (__float_as_uint(a[3]) & 0xFFFF0000u) | (__float_as_uint(a[2]) >> 16);
+  w[2] = (__float_as_uint(b[1]) & 0xFFFF0000u) | (__float_as_uint(b[0]) >> 16);
+  w[3] = (__float_as_uint(b[3]) & 0xFFFF0000u) | (__float_as_uint(b[2]) >> 16);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// Eight fp32 values as hi + lo bf16 operands: hi rounded to nearest even, lo the same rounding of
+// the exact residual x - hi, so hi + lo carries x to about 2^-17 of its size.
+__device__ __forceinline__ void bf16_split8(const float* p, bf16x8_t& hi, bf16x8_t& lo) {
+  const v4f a = *reinterpret_cast<const v4f*>(p), b = *reinterpret_cast<const v4f*>(p + 4);
+  const f32x8_t x = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  hi = __builtin_convertvector(x, bf16x8_t);
+  const u32x4_t hw = __builtin_bit_cast(u32x4_t, hi);
+  f32x8_t hf;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    hf[2 * m] = __uint_as_float(hw[m] << 16);
+    hf[2 * m + 1] = __uint_as_float(hw[m] & 0xFFFF0000u);
+  }
+  lo = __builtin_convertvector(x - hf, bf16x8_t);
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 template <int MODE>
 __device__ __forceinline__ float ldin(const void* p, size_t i) {
@@ -114,7 +152,6 @@ __global__ __launch_bounds__(BT) void bwd_prep_kernel(const void* q, const void*
     // on row tile w and all four column tiles (lane l supplies row l % 16, columns
     // 32 kb + 8 (l / 16) + 0..7 of both operands; the result's rows 4 (l / 16) + e, column l % 16
     // sit in lane l's acc[e]); ||k||^2 is the diagonal of K K^T.
-    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     const int lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
     v4f qk[4], kk[4];
 #pragma unroll
@@ -740,9 +777,35 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     }
     if (jb + NJ < DV) fetch(jb + NJ);
     __syncthreads();
-    // K S0, K dS1 (waves 0-3) and Q S0 (waves 4-7) for row tile mt on the fp32 MFMA, parked in
-    // the U, dU and dX blocks, which this column block has not written yet
-    {
+    // K S0, K dS1 (waves 0-3) and Q S0 (waves 4-7) for row tile mt, parked in the U, dU and dX
+    // blocks, which this column block has not written yet. bf16 inputs: k and q are exact in bf16
+    // and the fp32 state columns enter as hi + lo bf16 pairs, two bf16 MFMA passes per product;
+    // fp32 inputs: the fp32 MFMA.
+    if constexpr (MODE == 0) {
+      const int row = 16 * mt + ln;
+      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        const int dd = 32 * kb + 8 * gq;
+        const bf16x8_t a = bf16_exact8(wv < 4 ? &sK[row][dd] : &sQ[row][dd]);
+        bf16x8_t h8, l8;
+        bf16_split8(&cS[ln * SP + dd], h8, l8);
+        acc0 = mfma_bf16(a, l8, mfma_bf16(a, h8, acc0));
+        if (wv < 4) {
+          bf16_split8(&cD[ln * SP + dd], h8, l8);
+          acc1 = mfma_bf16(a, l8, mfma_bf16(a, h8, acc1));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (wv < 4) {
+          cU[ln * RP + 16 * mt + 4 * gq + e] = acc0[e];
+          cDU[ln * RP + 16 * mt + 4 * gq + e] = acc1[e];
+        } else {
+          cDX[ln * RP + 16 * mt + 4 * gq + e] = acc0[e];
+        }
+      }
+    } else {
       const int row = 16 * mt + ln;
       if (wv < 4) {
         v4f aks = {0.f, 0.f, 0.f, 0.f}, akd = {0.f, 0.f, 0.f, 0.f};
