@@ -399,34 +399,48 @@ constexpr int WT = 256;     // threads of a walk workgroup: four waves
 
 constexpr int WCOL = 64;    // state columns per walk workgroup
 
+// The LDS of one chunk of a walk: key rows, transposed key rows, the inverse (or its
+// transpose), the transposed values (or V~), and the chunk's per-token factors e^g, beta,
+// w = e^{g_C - g}, e^g beta and e^{g_C}.
+template <class E, int DK>
+struct WalkChunkLds {
+  static constexpr int EV = 16 / sizeof(E);
+  static constexpr int KP = DK + EV, TP = BC + EV;  // pitches of K [BC][KP] and K^T [DK][TP] (16-byte rows)
+  static constexpr int MPP = BC + 4, VP = BC + 4;   // pitches of the inverse and of the transposed values
+  E sK[BC][KP];
+  E sKt[DK][TP];
+  float sM[BC][MPP];
+  float sV[WCOL][VP];
+  float sEG[BC], sB[BC], sW[BC], sEB[BC];
+  float sGam;
+};
+
 template <int MODE, int DK, bool REV>
 __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void* vin, const float* rec,
                                                       const float* sin, int T, int H, int DV, int nc, float* sdump,
                                                       float* slast) {
   using E = typename LdsIn<MODE>::type;
-  constexpr int EV = 16 / sizeof(E);          // elements per 16-byte piece
-  constexpr int KP = DK + EV, TP = BC + EV;   // pitches of K [BC][KP] and K^T [DK][TP] (16-byte rows)
-  constexpr int MPP = BC + 4, VP = BC + 4;    // pitches of the inverse and of the transposed values
+  using L = WalkChunkLds<E, DK>;
+  constexpr int EV = L::EV;
   constexpr int KV = DK / EV, KPT = BC * KV / WT;   // key pieces per row, per thread
   constexpr int MPT = BC * BC / 4 / WT;             // float4s of the inverse per thread
   using VE = typename std::conditional<REV, float, E>::type;  // element type of the value rows
   constexpr int VEV = 16 / sizeof(VE), VV = WCOL / VEV, VPT = BC * VV / WT;  // value pieces
   constexpr int NDT = DK / 16;                      // 16-row tiles of the carried matrix
+  // bf16 rows leave room for two chunks' LDS: the next chunk is staged while this one is
+  // computed, with one workgroup barrier per chunk. fp32 rows stage between two barriers.
+  constexpr bool DB = MODE == 0;
   static_assert(KPT * WT == BC * KV && MPT * WT * 4 == BC * BC && VPT * WT == BC * VV, "walk tiling");
-  __shared__ __align__(16) E sK[BC][KP];
-  __shared__ __align__(16) E sKt[DK][TP];
-  __shared__ __align__(16) float sM[BC][MPP];
-  __shared__ __align__(16) float sV[WCOL][VP];
-  // per-token factors of the chunk: e^g, beta, w = e^{g_C - g}, e^g beta; and e^{g_C}
-  __shared__ __align__(16) float sEG[BC], sB[BC], sW[BC], sEB[BC];
-  __shared__ float sGam;
+  __shared__ __align__(16) L lds0;
+  __shared__ __align__(16) L lds1_[1];  // referenced (and allocated) only when DB
+  L& lds1 = DB ? lds1_[0] : lds0;
   // per-wave 16 x 16 transpose tile: the accumulator layout to and from rows of 16-byte pieces
   __shared__ __align__(16) float sTr[4][16][20];
   const int jb = blockIdx.x * WCOL, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, ln = lane & 15;
   const int col = jb + 16 * w + ln;  // this lane's column of the carried matrix
 
-  // ---- next chunk's rows in registers ----
+  // ---- a later chunk's rows in registers ----
   uint4 pk[KPT];
   v4f pm[MPT];
   uint4 pv[VPT];
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
   v4f pc[REV ? NDT : 1];
   // a lane's 16-byte piece of a 16 x 16 tile of the carried matrix: row lane / 4, columns 4 (lane % 4) + 0..3
   const int prow = lane >> 2, pcol = jb + 16 * w + 4 * (lane & 3);
-  auto fetch = [&](int c) __attribute__((always_inline)) {
+  auto fetch_rows = [&](int c) __attribute__((always_inline)) {
     const size_t cidx = static_cast<size_t>(bh) * nc + c;
     const float* R = rec + cidx * RECF;
 #pragma unroll
@@ -463,19 +477,22 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
       pg = R[REC_G + tid];
       pb = R[REC_B + tid];
     }
-    if constexpr (REV) {  // this wave's columns of Q^T (e^g . dO), the chunk's slot of dstates
-      const float* C = sdump + cidx * DK * DV;
+  };
+  // reverse walk: this wave's columns of Q^T (e^g . dO), the chunk's slot of dstates
+  auto fetch_c = [&](int c) __attribute__((always_inline)) {
+    if constexpr (REV) {
+      const float* C = sdump + (static_cast<size_t>(bh) * nc + c) * DK * DV;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) pc[dt] = *reinterpret_cast<const v4f*>(C + (16 * dt + prow) * DV + pcol);
     }
   };
-  auto stage = [&]() __attribute__((always_inline)) {
+  auto stage = [&](L& Q) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < KPT; ++x) {
       const int e = tid + x * WT, rr = e % BC, pe = e / BC;
-      *reinterpret_cast<uint4*>(&sK[rr][pe * EV]) = pk[x];
+      *reinterpret_cast<uint4*>(&Q.sK[rr][pe * EV]) = pk[x];
 #pragma unroll
-      for (int j = 0; j < EV; ++j) sKt[pe * EV + j][rr] = piece_elem<E>(pk[x], j);
+      for (int j = 0; j < EV; ++j) Q.sKt[pe * EV + j][rr] = piece_elem<E>(pk[x], j);
     }
 #pragma unroll
     for (int x = 0; x < MPT; ++x) {
@@ -483,26 +500,26 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
       if constexpr (REV) {
         const int rr = e % BC, cc = 4 * (e / BC);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sM[cc + j][rr] = pm[x][j];
+        for (int j = 0; j < 4; ++j) Q.sM[cc + j][rr] = pm[x][j];
       } else {
         const int rr = (4 * e) / BC, cc = (4 * e) % BC;
-        *reinterpret_cast<v4f*>(&sM[rr][cc]) = pm[x];
+        *reinterpret_cast<v4f*>(&Q.sM[rr][cc]) = pm[x];
       }
     }
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
       const int e = tid + x * WT, rr = e % BC, pe = e / BC;
 #pragma unroll
-      for (int j = 0; j < VEV; ++j) sV[VEV * pe + j][rr] = lds_f(piece_elem<VE>(pv[x], j));
+      for (int j = 0; j < VEV; ++j) Q.sV[VEV * pe + j][rr] = lds_f(piece_elem<VE>(pv[x], j));
     }
     if (tid < BC) {  // wave 0: one token per lane
       const float gC = __shfl(pg, BC - 1);
       const float eg = expf(pg);
-      sEG[tid] = eg;
-      sB[tid] = pb;
-      sW[tid] = expf(gC - pg);
-      sEB[tid] = eg * pb;
-      if (tid == 0) sGam = expf(gC);
+      Q.sEG[tid] = eg;
+      Q.sB[tid] = pb;
+      Q.sW[tid] = expf(gC - pg);
+      Q.sEB[tid] = eg * pb;
+      if (tid == 0) Q.sGam = expf(gC);
     }
   };
   // four consecutive elements of an LDS row as fp32 (an A operand of four K = 4 steps)
@@ -532,37 +549,29 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
     for (int i = 0; i < 4; ++i)
       S[dt][i] = sin ? sin[(static_cast<size_t>(bh) * DK + 16 * dt + 4 * gq + i) * DV + col] : 0.f;
 
-  const int c_first = REV ? nc - 1 : 0, c_step = REV ? -1 : 1;
-  fetch(c_first);
-  for (int n = 0; n < nc; ++n) {
-    const int c = c_first + n * c_step;
-    __syncthreads();  // every wave's reads of the previous chunk's rows are done
-    stage();
-    // the prefetched registers are consumed (and, for the reverse walk, this lane's elements of
-    // Q^T (e^g . dO) have arrived) before this chunk's slot is overwritten below
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // per 16-row tile, through the wave's transpose tile (LDS operations of a wave run in order):
-    // the reverse walk's Q^T (e^g . dO) into the accumulator layout, then the carried matrix out
-    // to this chunk's slot in 16-byte pieces
-    float cterm[REV ? NDT * 4 : 1];
-    {
-      float* D = sdump + (static_cast<size_t>(bh) * nc + c) * DK * DV;
-      float (*tr)[20] = sTr[w];
+  // The start of chunk c: the reverse walk's Q^T (e^g . dO) of the chunk into the accumulator
+  // layout, then the carried matrix out to the chunk's slot in 16-byte pieces, per 16-row tile
+  // through the wave's transpose tile (LDS operations of a wave run in order). Every load of the
+  // slot has returned before it is overwritten (the caller waits for vmcnt(0)).
+  float cterm[REV ? NDT * 4 : 1];
+  auto chunk_start = [&](int c) __attribute__((always_inline)) {
+    float* D = sdump + (static_cast<size_t>(bh) * nc + c) * DK * DV;
+    float (*tr)[20] = sTr[w];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        if constexpr (REV) {
-          *reinterpret_cast<v4f*>(&tr[prow][4 * (lane & 3)]) = pc[dt];
+    for (int dt = 0; dt < NDT; ++dt) {
+      if constexpr (REV) {
+        *reinterpret_cast<v4f*>(&tr[prow][4 * (lane & 3)]) = pc[dt];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cterm[4 * dt + i] = tr[4 * gq + i][ln];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tr[4 * gq + i][ln] = S[dt][i];
-        *reinterpret_cast<v4f*>(D + (16 * dt + prow) * DV + pcol) = *reinterpret_cast<const v4f*>(&tr[prow][4 * (lane & 3)]);
+        for (int i = 0; i < 4; ++i) cterm[4 * dt + i] = tr[4 * gq + i][ln];
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tr[4 * gq + i][ln] = S[dt][i];
+      *reinterpret_cast<v4f*>(D + (16 * dt + prow) * DV + pcol) = *reinterpret_cast<const v4f*>(&tr[prow][4 * (lane & 3)]);
     }
-    if (n + 1 < nc) fetch(c + c_step);
-    __syncthreads();
-
+  };
+  // One chunk's products from the staged chunk Q. `mid` runs after the first product has been
+  // issued (the next chunk's staging, in the double-buffered walk).
+  auto compute = [&](const L& Q, auto&& mid) __attribute__((always_inline)) {
     // R = K S (token tiles mt)
     v4f R[4];
 #pragma unroll
@@ -571,20 +580,21 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
     for (int dt = 0; dt < NDT; ++dt) {
       float4 a[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = rd4(&sK[16 * mt + ln][16 * dt + 4 * gq]);
+      for (int mt = 0; mt < 4; ++mt) a[mt] = rd4(&Q.sK[16 * mt + ln][16 * dt + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) R[mt] = mfma4(el4(a[mt], i), S[dt][i], R[mt]);
     }
+    mid();
     // forward: X = beta . (V - e^g . R); reverse: dU = w . R + V~
     v4f X[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const float4 vv = *reinterpret_cast<const float4*>(&sV[16 * w + ln][16 * mt + 4 * gq]);
-      const float4 eg = *reinterpret_cast<const float4*>(&sEG[16 * mt + 4 * gq]);
-      const float4 bb = *reinterpret_cast<const float4*>(&sB[16 * mt + 4 * gq]);
-      const float4 ww = *reinterpret_cast<const float4*>(&sW[16 * mt + 4 * gq]);
+      const float4 vv = *reinterpret_cast<const float4*>(&Q.sV[16 * w + ln][16 * mt + 4 * gq]);
+      const float4 eg = *reinterpret_cast<const float4*>(&Q.sEG[16 * mt + 4 * gq]);
+      const float4 bb = *reinterpret_cast<const float4*>(&Q.sB[16 * mt + 4 * gq]);
+      const float4 ww = *reinterpret_cast<const float4*>(&Q.sW[16 * mt + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (REV) X[mt][i] = fmaf(el4(ww, i), R[mt][i], el4(vv, i));
@@ -600,7 +610,7 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
       float4 a[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        if (REV ? kt >= mt : kt <= mt) a[mt] = *reinterpret_cast<const float4*>(&sM[16 * mt + ln][16 * kt + 4 * gq]);
+        if (REV ? kt >= mt : kt <= mt) a[mt] = *reinterpret_cast<const float4*>(&Q.sM[16 * mt + ln][16 * kt + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -612,15 +622,15 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
     v4f Y[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const float4 eb = *reinterpret_cast<const float4*>(&sEB[16 * mt + 4 * gq]);
-      const float4 ww = *reinterpret_cast<const float4*>(&sW[16 * mt + 4 * gq]);
+      const float4 eb = *reinterpret_cast<const float4*>(&Q.sEB[16 * mt + 4 * gq]);
+      const float4 ww = *reinterpret_cast<const float4*>(&Q.sW[16 * mt + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (REV) Y[mt][i] = -el4(eb, i) * U[mt][i];
         else Y[mt][i] = el4(ww, i) * U[mt][i];
       }
     }
-    const float gam = sGam;
+    const float gam = Q.sGam;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -632,11 +642,56 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
     for (int kt = 0; kt < 4; ++kt) {
       float4 a[NDT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) a[dt] = rd4(&sKt[16 * dt + ln][16 * kt + 4 * gq]);
+      for (int dt = 0; dt < NDT; ++dt) a[dt] = rd4(&Q.sKt[16 * dt + ln][16 * kt + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) S[dt] = mfma4(el4(a[dt], i), Y[kt][i], S[dt]);
+    }
+  };
+
+  const int c_first = REV ? nc - 1 : 0, c_step = REV ? -1 : 1;
+  if constexpr (DB) {
+    // chunk n is computed from lds[n % 2] while chunk n + 1 is staged into the other; the rows of
+    // chunk n + 2 are loaded into registers meanwhile, the reverse walk's Q^T (e^g . dO) of chunk
+    // n + 1 after chunk n's slot is written
+    fetch_rows(c_first);
+    fetch_c(c_first);
+    stage(lds0);
+    if (nc > 1) fetch_rows(c_first + c_step);
+    __syncthreads();
+    auto step = [&](int n, L& cur, L& nxt) __attribute__((always_inline)) {
+      const int c = c_first + n * c_step;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      chunk_start(c);
+      if (n + 1 < nc) fetch_c(c + c_step);
+      compute(cur, [&]() __attribute__((always_inline)) {
+        if (n + 1 < nc) {
+          stage(nxt);
+          if (n + 2 < nc) fetch_rows(c + 2 * c_step);
+        }
+      });
+      __syncthreads();  // the next chunk is staged; every read of this one is done
+    };
+    for (int n = 0; n < nc; n += 2) {
+      step(n, lds0, lds1);
+      if (n + 1 < nc) step(n + 1, lds1, lds0);
+    }
+  } else {
+    fetch_rows(c_first);
+    fetch_c(c_first);
+    for (int n = 0; n < nc; ++n) {
+      const int c = c_first + n * c_step;
+      __syncthreads();  // every wave's reads of the previous chunk's rows are done
+      stage(lds0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      chunk_start(c);
+      if (n + 1 < nc) {
+        fetch_rows(c + c_step);
+        fetch_c(c + c_step);
+      }
+      __syncthreads();
+      compute(lds0, []() __attribute__((always_inline)) {});
     }
   }
   if (slast) {
