@@ -320,13 +320,137 @@ __global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_kernel(const ui
   }
 }
 
+// The same for bf16 inputs on the bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation), one
+// workgroup per (batch, head, chunk), eight waves:
+//   W = P T' from the record's hi and lo halves, three passes (hi hi, hi lo, lo hi), wave w on row
+//   tile w % 4 and column tiles w / 4 + {0, 2}; W is lower triangular, so tiles above the
+//   diagonal are zero and the contraction runs only over the tokens between the two tiles;
+//   the weighted W (row t, column s scaled by lambda_t^(level(t,s)), zero above the diagonal and
+//   past T) into LDS in fp32;
+//   out = W V with W as hi + lo bf16 pairs and V exact, two passes.
+// P's rows enter straight from the record as A operands (eight consecutive columns per lane);
+// T'^T and V^T are staged transposed in LDS, so each B operand is one 16-byte read.
+template <int DV>
+__global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_mfma_kernel(const uint8_t* __restrict__ rec,
+                                                                   const uint16_t* __restrict__ v,
+                                                                   const float* __restrict__ lam,
+                                                                   float* __restrict__ out, int T, int H, int nc,
+                                                                   int L) {
+  constexpr int BP = CHUNK + 8;  // bf16 pitch of the transposed rows (16-byte aligned)
+  constexpr int WP = CHUNK + 4;  // fp32 pitch of W
+  __shared__ __align__(16) uint16_t sTh[CHUNK][BP];  // T'^T, hi and lo
+  __shared__ __align__(16) uint16_t sTl[CHUNK][BP];
+  __shared__ __align__(16) uint16_t sVt[DV][BP];     // V^T
+  __shared__ __align__(16) float sW[CHUNK][WP];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
+  const int id = blockIdx.x;
+  const int bh = id / nc, c = id - bh * nc;
+  const int b = bh / H, h = bh - b * H;
+  const int t0 = c * CHUNK;
+  const uint8_t* R = rec + static_cast<size_t>(id) * REC_BYTES;
+  const int mt = wv & 3;
+
+  // P's rows for this wave's row tile (A operands), loaded first: row 16 mt + ln, columns
+  // 32 kb + 8 gq + 0..7, hi and lo
+  u32x4 ph[2], pl[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    ph[kb] = *reinterpret_cast<const u32x4*>(R + REC_P_OFF + swz_off<256>(16 * mt + ln, 16 * (4 * kb + gq)));
+    pl[kb] = *reinterpret_cast<const u32x4*>(R + REC_P_OFF + swz_off<256>(16 * mt + ln, 16 * (4 * kb + gq + 8)));
+  }
+  // T' transposed: consecutive lanes take consecutive rows r, so the transposed writes hit
+  // consecutive halves of LDS words
+  {
+    const int r = tid & 63, cb = tid >> 6;  // 64 rows x 8 blocks of 8 columns
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(R + REC_T_OFF + swz_off<256>(r, 16 * cb));
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(R + REC_T_OFF + swz_off<256>(r, 16 * (cb + 8)));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sTh[8 * cb + j][r] = static_cast<uint16_t>((j & 1) ? hi[j >> 1] >> 16 : hi[j >> 1] & 0xFFFFu);
+      sTl[8 * cb + j][r] = static_cast<uint16_t>((j & 1) ? lo[j >> 1] >> 16 : lo[j >> 1] & 0xFFFFu);
+    }
+  }
+  // V transposed, zero past T
+#pragma unroll
+  for (int u = 0; u < CHUNK * DV / 8 / INTRA_THREADS; ++u) {
+    const int e = tid + INTRA_THREADS * u, tt = e & 63, pc = e >> 6;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (t0 + tt < T) x = *reinterpret_cast<const u32x4*>(v + (static_cast<size_t>(b) * T + t0 + tt) * H * DV + h * DV + 8 * pc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sVt[8 * pc + j][tt] = static_cast<uint16_t>((j & 1) ? x[j >> 1] >> 16 : x[j >> 1] & 0xFFFFu);
+  }
+  __syncthreads();
+
+  // W = P T' on tiles (mt, nt), nt = wv / 4 + 2 u; the contraction over r needs only
+  // 16 nt <= r <= 16 mt + 15
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int nt = (wv >> 2) + 2 * u;
+    f32x4 acc = zero4();
+    if (nt <= mt) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (32 * kb > 16 * mt + 15 || 32 * kb + 31 < 16 * nt) continue;
+        const bf16x8 th = *reinterpret_cast<const bf16x8*>(&sTh[16 * nt + ln][32 * kb + 8 * gq]);
+        const bf16x8 tl = *reinterpret_cast<const bf16x8*>(&sTl[16 * nt + ln][32 * kb + 8 * gq]);
+        const bf16x8 a_h = __builtin_bit_cast(bf16x8, ph[kb]), a_l = __builtin_bit_cast(bf16x8, pl[kb]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_h, th, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_h, tl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_l, th, acc, 0, 0, 0);
+      }
+    }
+    // weights: row t = 16 mt + 4 gq + e, column s = 16 nt + ln
+    const int s = 16 * nt + ln;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * mt + 4 * gq + e;
+      float wgt = 0.f;
+      if (s <= t && t0 + t < T) {
+        const int lev = s == t ? 0 : 32 - __clz(static_cast<unsigned>(t ^ s));
+        wgt = acc[e] * lam[((static_cast<size_t>(b) * T + t0 + t) * H + h) * L + lev];
+      }
+      sW[t][s] = wgt;
+    }
+  }
+  __syncthreads();
+
+  // out = W V on tiles (mt, nt), nt = wv / 4 + 2 u; W is zero for s > t, so row tiles 0 and 1
+  // need only the first 32 tokens
+#pragma unroll
+  for (int u = 0; u < DV / 32; ++u) {
+    const int nt = (wv >> 2) + 2 * u;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1 && mt < 2) continue;
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sW[16 * mt + ln][32 * kb + 8 * gq]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sW[16 * mt + ln][32 * kb + 8 * gq + 4]);
+      F8 wf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wf.v[j] = w0[j];
+        wf.v[4 + j] = w1[j];
+      }
+      const S8 ws = split8(wf);
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + ln][32 * kb + 8 * gq]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws.h, vb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws.l, vb, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tt = t0 + 16 * mt + 4 * gq + e;
+      if (tt < T) out[(static_cast<size_t>(b) * T + tt) * H * DV + h * DV + 16 * nt + ln] = acc[e];
+    }
+  }
+}
+
 hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, const void* v, const float* lam,
                                   int L, float* out, hipStream_t stream) {
   const dim3 grid(d.B * d.H * d.nc);
   if (mode == MODE_BF16) {
-    const auto* vb = static_cast<const Tr<MODE_BF16>::in_t*>(v);
-    if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 64>, grid, dim3(INTRA_THREADS), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
-    if (d.dv == 128) return launch_kernel(loglinear_intra_kernel<MODE_BF16, 128>, grid, dim3(INTRA_THREADS), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
+    const auto* vb = static_cast<const uint16_t*>(v);
+    if (d.dv == 64) return launch_kernel(loglinear_intra_mfma_kernel<64>, grid, dim3(INTRA_THREADS), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
+    if (d.dv == 128) return launch_kernel(loglinear_intra_mfma_kernel<128>, grid, dim3(INTRA_THREADS), stream, rec, vb, lam, out, d.T, d.H, d.nc, L);
   } else {
     const auto* vf = static_cast<const Tr<MODE_F32>::in_t*>(v);
     if (d.dv == 64) return launch_kernel(loglinear_intra_kernel<MODE_F32, 64>, grid, dim3(INTRA_THREADS), stream, rec, vf, lam, out, d.T, d.H, d.nc, L);
