@@ -500,7 +500,10 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
   d.full_rec = 1;
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   const size_t bh = static_cast<size_t>(B) * H;
-  const size_t rec_bytes = align256(bh * nc * kla::full_record_bytes());
+  // bf16 with dk <= 128: every kernel reads compact records (T' and the gates; the intra-chunk
+  // kernel and the right walks form P themselves), from one prep pass; otherwise full records
+  const bool compact = kla::state_dma_supported(mode, dk);
+  const size_t rec_bytes = compact ? 0 : align256(bh * nc * kla::full_record_bytes());
   // scales l >= 7: half-blocks of 2^(l-7) chunks while a right half-block exists; every scale's
   // left end states are kept at once (at most nc states per head over all scales)
   int nscale = 0, half[32], nleft[32], nright[32];
@@ -515,26 +518,28 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
     ends_floats += static_cast<long long>(bh) * nleft[nscale] * dk * dv;
   }
   const size_t ends_bytes = align256(static_cast<size_t>(ends_floats) * 4);
-  // bf16 with dk <= 128: the left and right walks run on the DMA-fed walk kernels, which read
-  // compact records (T' and the gates; the right walks form P themselves), from a second prep pass
-  const bool compact = kla::state_dma_supported(mode, dk);
   const size_t crec_bytes = compact ? align256(bh * nc * static_cast<size_t>(kla::record_bytes(mode, dk))) : 0;
   void* ws = nullptr;
   st = workspace_alloc(&ws, rec_bytes + ends_bytes + crec_bytes, stream);
   if (st != KLA_OK) return st;
   hipError_t e = hipSuccess;
-  uint8_t* rec = static_cast<uint8_t*>(ws);
-  float* ends = reinterpret_cast<float*>(rec + rec_bytes);
-  uint8_t* crec = compact ? rec + rec_bytes + ends_bytes : nullptr;
+  uint8_t* rec = compact ? nullptr : static_cast<uint8_t*>(ws);
+  float* ends = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + rec_bytes);
+  uint8_t* crec = compact ? static_cast<uint8_t*>(ws) + rec_bytes + ends_bytes : nullptr;
   const int direct = beta_mode == KLA_BETA_DIRECT;
-  e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
-  if (e == hipSuccess && compact) {
+  if (compact) {
     kla::Dims dc = d;
     dc.full_rec = 0;
     e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, dc, q, k, log_alpha, eta, eps, direct, crec, stream); });
+    if (e == hipSuccess)
+      e = timed("kla_loglinear_intra", stream, [&] {
+        return kla::launch_loglinear_intra_compact(d, q, k, crec, v, lam, levels, out, stream);
+      });
+  } else {
+    e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
+    if (e == hipSuccess)
+      e = timed("kla_loglinear_intra", stream, [&] { return kla::launch_loglinear_intra(mode, d, rec, v, lam, levels, out, stream); });
   }
-  if (e == hipSuccess)
-    e = timed("kla_loglinear_intra", stream, [&] { return kla::launch_loglinear_intra(mode, d, rec, v, lam, levels, out, stream); });
   // every scale's left walks in one grid (they are independent), then the right walks scale by
   // scale (the scales add to the same outputs)
   if (e == hipSuccess && nscale > 0)

@@ -92,6 +92,9 @@ hipError_t launch_loglinear_decode(int mode, int N, int H, int dk, int dv, const
 // its left sibling's end state with no values, lambda^(l)-weighted outputs added to out.
 hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, const void* v, const float* lam,
                                   int L, float* out, hipStream_t stream);
+// The same from compact records (bf16, dk <= 128), forming P from q and k.
+hipError_t launch_loglinear_intra_compact(const Dims& d, const void* q, const void* k, const uint8_t* crec,
+                                          const void* v, const float* lam, int L, float* out, hipStream_t stream);
 // All scales' left walks in one grid: scale i has half-blocks of half[i] chunks, nleft[i] left
 // ones per head, and writes their end states at ends + ends_off[i] (floats).
 // rec_compact: compact records of the same chunks (bf16, dk <= 128): the left walks of every

@@ -444,6 +444,190 @@ __global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_mfma_kernel(con
   }
 }
 
+// The same on the compact record (T' without its zero quadrant, and the gates), which the walks
+// read anyway, so that no full record is prepared: P = tril(e^{g_t - g_r} Q K^T) is formed here
+// from the chunk's query and key rows on the bf16 MFMA (exact products), on its lower 16 x 16
+// tiles, and staged in LDS in fp32 for the P T' product.
+template <int DK, int DV>
+__global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_compact_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint8_t* __restrict__ crec,
+    const uint16_t* __restrict__ v, const float* __restrict__ lam, float* __restrict__ out, int T, int H, int nc,
+    int L) {
+  constexpr int BP = CHUNK + 8;  // bf16 pitch of the transposed rows (16-byte aligned)
+  constexpr int WP = CHUNK + 4;  // fp32 pitch of P and W
+  __shared__ __align__(16) uint16_t sTh[CHUNK][BP];  // T'^T, hi and lo
+  __shared__ __align__(16) uint16_t sTl[CHUNK][BP];
+  __shared__ __align__(16) uint16_t sVt[DV][BP];     // V^T
+  __shared__ __align__(16) float sP[CHUNK][WP];
+  __shared__ __align__(16) float sW[CHUNK][WP];
+  __shared__ float sg[CHUNK];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
+  const int id = blockIdx.x;
+  const int bh = id / nc, c = id - bh * nc;
+  const int b = bh / H, h = bh - b * H;
+  const int t0 = c * CHUNK;
+  const uint8_t* R = crec + static_cast<size_t>(id) * CREC_BYTES;
+  const int mt = wv & 3;
+  const size_t row0 = (static_cast<size_t>(b) * T + t0) * H + h;  // (b, t0, h) in token-head units
+
+  // Every global load first, so that they are all in flight together: the query row 16 mt + ln
+  // and the key rows 16 nt + ln of this wave's tiles (mt, nt), nt = wv / 4 + 2 u, columns
+  // 32 kb + 8 gq + 0..7 (zero past T); T' (transposed below) and V
+  u32x4 qa[DK / 32], ka[2][DK / 32];
+  {
+    const int tq = 16 * mt + ln;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+      qa[kb] = u32x4{0u, 0u, 0u, 0u};
+      if (t0 + tq < T) qa[kb] = *reinterpret_cast<const u32x4*>(q + (row0 + static_cast<size_t>(tq) * H) * DK + 32 * kb + 8 * gq);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int nt = (wv >> 2) + 2 * u;
+      const int tk = 16 * nt + ln;
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) {
+        ka[u][kb] = u32x4{0u, 0u, 0u, 0u};
+        if (nt <= mt && t0 + tk < T)
+          ka[u][kb] = *reinterpret_cast<const u32x4*>(k + (row0 + static_cast<size_t>(tk) * H) * DK + 32 * kb + 8 * gq);
+      }
+    }
+  }
+  // T' from the compact record: rows 0..31 hold columns 0..31 (128-byte rows), rows 32..63 all
+  // 64 (256-byte rows); consecutive lanes take consecutive rows
+  const bool top = tid < 32 * 4;
+  const int tr = top ? (tid & 31) : 32 + ((tid - 128) & 31);
+  const int tcb = top ? (tid >> 5) : ((tid - 128) >> 5);
+  u32x4 thi = {0u, 0u, 0u, 0u}, tlo = {0u, 0u, 0u, 0u};
+  if (tid < 32 * 4 + 32 * 8) {
+    thi = *reinterpret_cast<const u32x4*>(top ? R + CREC_TOP_OFF + swz_off<128>(tr, 16 * tcb)
+                                              : R + CREC_BOT_OFF + swz_off<256>(tr - 32, 16 * tcb));
+    tlo = *reinterpret_cast<const u32x4*>(top ? R + CREC_TOP_OFF + swz_off<128>(tr, 16 * (tcb + 4))
+                                              : R + CREC_BOT_OFF + swz_off<256>(tr - 32, 16 * (tcb + 8)));
+  }
+  constexpr int NVL = CHUNK * DV / 8 / INTRA_THREADS;
+  u32x4 vx[NVL];
+#pragma unroll
+  for (int u = 0; u < NVL; ++u) {
+    const int e = tid + INTRA_THREADS * u, tt = e & 63, pc = e >> 6;
+    vx[u] = u32x4{0u, 0u, 0u, 0u};
+    if (t0 + tt < T) vx[u] = *reinterpret_cast<const u32x4*>(v + (row0 + static_cast<size_t>(tt) * H) * DV + 8 * pc);
+  }
+  // Q K^T on the bf16 MFMA (exact products, fp32 sums)
+  f32x4 qk[2] = {zero4(), zero4()};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if ((wv >> 2) + 2 * u > mt) continue;
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb)
+      qk[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kb]),
+                                                      __builtin_bit_cast(bf16x8, ka[u][kb]), qk[u], 0, 0, 0);
+  }
+  // T' and V transposed into LDS
+  if (tid < 32 * 4 + 32 * 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sTh[8 * tcb + j][tr] = static_cast<uint16_t>((j & 1) ? thi[j >> 1] >> 16 : thi[j >> 1] & 0xFFFFu);
+      sTl[8 * tcb + j][tr] = static_cast<uint16_t>((j & 1) ? tlo[j >> 1] >> 16 : tlo[j >> 1] & 0xFFFFu);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NVL; ++u) {
+    const int e = tid + INTRA_THREADS * u, tt = e & 63, pc = e >> 6;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sVt[8 * pc + j][tt] = static_cast<uint16_t>((j & 1) ? vx[u][j >> 1] >> 16 : vx[u][j >> 1] & 0xFFFFu);
+  }
+  if (tid < CHUNK) sg[tid] = reinterpret_cast<const float*>(R + CREC_G_OFF)[tid];
+  __syncthreads();
+  // P = e^{g_t - g_r} Q K^T on and below the diagonal, zero above
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int nt = (wv >> 2) + 2 * u;
+    const int r = 16 * nt + ln;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * mt + 4 * gq + e;
+      sP[t][r] = r <= t ? __expf(sg[t] - sg[r]) * qk[u][e] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // W = P T' on tiles (mt, nt) with P split hi + lo (three passes); the contraction needs only
+  // 16 nt <= r <= 16 mt + 15
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int nt = (wv >> 2) + 2 * u;
+    f32x4 acc = zero4();
+    if (nt <= mt) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (32 * kb > 16 * mt + 15 || 32 * kb + 31 < 16 * nt) continue;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&sP[16 * mt + ln][32 * kb + 8 * gq]);
+        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&sP[16 * mt + ln][32 * kb + 8 * gq + 4]);
+        const S8 ps = split8(frag_from_acc(p0, p1));
+        const bf16x8 th = *reinterpret_cast<const bf16x8*>(&sTh[16 * nt + ln][32 * kb + 8 * gq]);
+        const bf16x8 tl = *reinterpret_cast<const bf16x8*>(&sTl[16 * nt + ln][32 * kb + 8 * gq]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps.h, th, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps.h, tl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps.l, th, acc, 0, 0, 0);
+      }
+    }
+    const int s = 16 * nt + ln;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * mt + 4 * gq + e;
+      float wgt = 0.f;
+      if (s <= t && t0 + t < T) {
+        const int lev = s == t ? 0 : 32 - __clz(static_cast<unsigned>(t ^ s));
+        wgt = acc[e] * lam[(row0 + static_cast<size_t>(t) * H) * L + lev];
+      }
+      sW[t][s] = wgt;
+    }
+  }
+  __syncthreads();
+
+  // out = W V, W split hi + lo, V exact (two passes); row tiles 0 and 1 need only 32 tokens
+#pragma unroll
+  for (int u = 0; u < DV / 32; ++u) {
+    const int nt = (wv >> 2) + 2 * u;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1 && mt < 2) continue;
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sW[16 * mt + ln][32 * kb + 8 * gq]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sW[16 * mt + ln][32 * kb + 8 * gq + 4]);
+      const S8 ws = split8(frag_from_acc(w0, w1));
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + ln][32 * kb + 8 * gq]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws.h, vb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws.l, vb, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tt = 16 * mt + 4 * gq + e;
+      if (t0 + tt < T) out[(row0 + static_cast<size_t>(tt) * H) * DV + 16 * nt + ln] = acc[e];
+    }
+  }
+}
+
+hipError_t launch_loglinear_intra_compact(const Dims& d, const void* q, const void* k, const uint8_t* crec,
+                                          const void* v, const float* lam, int L, float* out, hipStream_t stream) {
+  const dim3 grid(d.B * d.H * d.nc), block(INTRA_THREADS);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  const auto* vb = static_cast<const uint16_t*>(v);
+#define KLA_LLI_CASE(DKV, DVV)                                                                                   \
+  if (d.dk == DKV && d.dv == DVV)                                                                                \
+    return launch_kernel(loglinear_intra_compact_kernel<DKV, DVV>, grid, block, stream, qb, kb, crec, vb, lam, out, \
+                         d.T, d.H, d.nc, L);
+  KLA_LLI_CASE(64, 64)
+  KLA_LLI_CASE(64, 128)
+  KLA_LLI_CASE(128, 64)
+  KLA_LLI_CASE(128, 128)
+#undef KLA_LLI_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, const void* v, const float* lam,
                                   int L, float* out, hipStream_t stream) {
   const dim3 grid(d.B * d.H * d.nc);
