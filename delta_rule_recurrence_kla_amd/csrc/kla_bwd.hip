@@ -708,19 +708,25 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-// Per-chunk gradients from the chunk-start state S0 and the chunk-end gradient dS1.
+// Per-chunk gradients from the chunk-start state S0 and the chunk-end gradient dS1. The state
+// columns are taken in blocks of NJG: 32 for bf16 inputs, whose query and key rows stay bf16 in
+// LDS (exact), 16 for fp32 inputs, whose rows take twice the room.
 template <int MODE, int DK>
 __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void* k, const void* v, const float* eta,
                                                        const float* dout, const float* rec, const float* states,
                                                        const float* dstates, int direct, int T, int H, int DV, int nc,
                                                        float* dq, float* dk, float* dv, float* dla, float* deta) {
-  constexpr int EPT = DK * NJ / NT, TPR = NJ / EPT, DQ = DK / TPRW;
+  constexpr int NJG = MODE == 0 ? 32 : 16, NCT = NJG / 16, CPTG = NJG / TPRW;
+  constexpr int EPT = DK * NJG / NT, TPR = NJG / EPT, DQ = DK / TPRW;
   constexpr int SP = DK + 4, RP = BC + 4;  // pitches of the column-major blocks (16-byte rows)
-  constexpr int WCOL = 2 * NJ * SP + 5 * NJ * RP, WMAT = 2 * BC * MP;
+  constexpr int WCOL = 2 * NJG * SP + 5 * NJG * RP, WMAT = 2 * BC * MP;
   constexpr int WN = WCOL > WMAT ? WCOL : WMAT;
   const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
-  constexpr int QP = DK + 4;  // 16-byte rows of queries and keys
-  __shared__ __align__(16) float sQ[BC][QP], sK[BC][QP];
+  // Query and key rows in their input type, 16-byte rows; the bf16 pitch (DK + 16 halves) puts
+  // the four rows of an MFMA K step on disjoint banks
+  using QE = typename LdsIn<MODE>::type;
+  constexpr int QP = MODE == 0 ? DK + 16 : DK + 4;
+  __shared__ __align__(16) QE sQ[BC][QP], sK[BC][QP];
   __shared__ float sM[BC][MP], sPG[BC][MP];
   __shared__ __align__(16) float sW[WN];
   __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
@@ -728,13 +734,13 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __shared__ float sgp[BC];  // per-row parts of <dS1, S0>
   // column-block phase: 16 columns of each operand, stored column by column so that a
   // thread's run of rows (or of state rows) is one 16-byte read
-  float* cS = sW;             // S0 [NJ][SP]
-  float* cD = cS + NJ * SP;   // dS1 [NJ][SP]
-  float* cX = cD + NJ * SP;   // V, then X [NJ][RP]
-  float* cO = cX + NJ * RP;   // dO
-  float* cU = cO + NJ * RP;   // U
-  float* cDU = cU + NJ * RP;
-  float* cDX = cDU + NJ * RP;
+  float* cS = sW;              // S0 [NJG][SP]
+  float* cD = cS + NJG * SP;   // dS1 [NJG][SP]
+  float* cX = cD + NJG * SP;   // V, then X [NJG][RP]
+  float* cO = cX + NJG * RP;   // dO
+  float* cU = cO + NJG * RP;   // U
+  float* cDU = cU + NJG * RP;
+  float* cDX = cDU + NJG * RP;
   // matrix phase
   float* m1 = sW;
   float* m2 = sW + BC * MP;
@@ -755,18 +761,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
         uq = reinterpret_cast<const uint4*>(static_cast<const E*>(q) + o)[pe];
         uk = reinterpret_cast<const uint4*>(static_cast<const E*>(k) + o)[pe];
       }
-      float fq[EV], fk[EV];
-      if constexpr (MODE == 0) {
-        row8(reinterpret_cast<const uint16_t*>(&uq), fq);
-        row8(reinterpret_cast<const uint16_t*>(&uk), fk);
-      } else {
-        fq[0] = __uint_as_float(uq.x); fq[1] = __uint_as_float(uq.y); fq[2] = __uint_as_float(uq.z); fq[3] = __uint_as_float(uq.w);
-        fk[0] = __uint_as_float(uk.x); fk[1] = __uint_as_float(uk.y); fk[2] = __uint_as_float(uk.z); fk[3] = __uint_as_float(uk.w);
-      }
-      for (int z = 0; z < EV; z += 4) {
-        *reinterpret_cast<float4*>(&sQ[rr][pe * EV + z]) = float4{fq[z], fq[z + 1], fq[z + 2], fq[z + 3]};
-        *reinterpret_cast<float4*>(&sK[rr][pe * EV + z]) = float4{fk[z], fk[z + 1], fk[z + 2], fk[z + 3]};
-      }
+      *reinterpret_cast<uint4*>(&sQ[rr][pe * EV]) = uq;
+      *reinterpret_cast<uint4*>(&sK[rr][pe * EV]) = uk;
     }
 #pragma unroll
     for (int x = 0; x < BC * BC / 4 / NT; ++x) {
@@ -782,7 +778,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     sb[tid] = R[REC_B + tid];
     sden[tid] = R[REC_D + tid];
   }
-  const int r = tid / TPRW, qd = tid % TPRW, j0 = qd * CPT, i0 = qd * IPT, d0 = qd * DQ;
+  const int r = tid / TPRW, qd = tid % TPRW, j0 = qd * CPTG, i0 = qd * IPT, d0 = qd * DQ;
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
   // Rank-16 updates on the fp32 MFMA: wave w owns row tile mt of the chunk and column tiles
   // nt = w / 4 + 2u of dP, dT' (64 x 64) and of dQ, dK (64 x DK).
@@ -805,60 +801,85 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
 
   // the next column block's S0, dS1, V and dO are loaded into registers while this one is
   // computed
-  constexpr int VPT = BC * NJ / NT;
-  float pS[EPT], pD[EPT], pV[VPT], pO[VPT];
+  constexpr int VPT = BC * NJG / NT;
+  // V and dO are fetched without a branch (a clamped token past T, zeroed when staged): a load
+  // inside a conditional is waited for inside it, which would serialize the prefetch
+  using VE = typename LdsIn<MODE>::type;
+  float pS[EPT], pD[EPT], pO[VPT];
+  VE pV[VPT];
   auto fetch = [&](int jb) {
-    for (int e = 0; e < EPT; ++e) {
-      pS[e] = S0[sd * DV + jb + sj + e];
-      pD[e] = D1[sd * DV + jb + sj + e];
+    if constexpr (EPT % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < EPT; e += 4) {
+        const v4f xs = *reinterpret_cast<const v4f*>(S0 + sd * DV + jb + sj + e);
+        const v4f xd = *reinterpret_cast<const v4f*>(D1 + sd * DV + jb + sj + e);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          pS[e + z] = xs[z];
+          pD[e + z] = xd[z];
+        }
+      }
+    } else {
+      for (int e = 0; e < EPT; ++e) {
+        pS[e] = S0[sd * DV + jb + sj + e];
+        pD[e] = D1[sd * DV + jb + sj + e];
+      }
     }
     for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * NT, rr = e / NJ, j = e % NJ, t = c * BC + rr;
-      const size_t o = tok(b, t, T, H, h) * DV + jb + j;
-      pV[x] = t < T ? ldin<MODE>(v, o) : 0.f;
-      pO[x] = t < T ? dout[o] : 0.f;
+      const int e = tid + x * NT, rr = e / NJG, j = e % NJG, t = c * BC + rr;
+      const size_t o = tok(b, t < T ? t : T - 1, T, H, h) * DV + jb + j;
+      pV[x] = static_cast<const VE*>(v)[o];
+      pO[x] = dout[o];
     }
   };
   fetch(0);
-  for (int jb = 0; jb < DV; jb += NJ) {
+  for (int jb = 0; jb < DV; jb += NJG) {
+#pragma unroll
     for (int e = 0; e < EPT; ++e) {
       cS[(sj + e) * SP + sd] = pS[e];
       cD[(sj + e) * SP + sd] = pD[e];
     }
     for (int x = 0; x < VPT; ++x) {
-      const int e = tid + x * NT, rr = e / NJ, j = e % NJ;
-      cX[j * RP + rr] = pV[x];
-      cO[j * RP + rr] = pO[x];
+      const int e = tid + x * NT, rr = e / NJG, j = e % NJG;
+      const bool in = c * BC + rr < T;
+      cX[j * RP + rr] = in ? lds_f(pV[x]) : 0.f;
+      cO[j * RP + rr] = in ? pO[x] : 0.f;
     }
-    if (jb + NJ < DV) fetch(jb + NJ);
+    if (jb + NJG < DV) fetch(jb + NJG);
     __syncthreads();
-    // K S0, K dS1 (waves 0-3) and Q S0 (waves 4-7) for row tile mt, parked in the U, dU and dX
-    // blocks, which this column block has not written yet. bf16 inputs: k and q are exact in bf16
-    // and the fp32 state columns enter as hi + lo bf16 pairs, two bf16 MFMA passes per product;
-    // fp32 inputs: the fp32 MFMA.
+    // K S0, K dS1 and Q S0 for row tile mt, parked in the U, dU and dX blocks, which this column
+    // block has not written yet. bf16 inputs: k and q are exact in bf16 and the fp32 state columns
+    // enter as hi + lo bf16 pairs, two bf16 MFMA passes per product; the six 16 x 16 tiles of a
+    // row tile (three products, two column tiles) go three to a wave: waves 0-3 K S0 on both
+    // column tiles and K dS1 on the first, waves 4-7 Q S0 on both and K dS1 on the second.
+    // fp32 inputs: the fp32 MFMA, one column tile.
     if constexpr (MODE == 0) {
       const int row = 16 * mt + ln;
-      v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      const bool kw = wv < 4;
+      v4f acc[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) {
         const int dd = 32 * kb + 8 * gq;
-        const bf16x8_t a = bf16_exact8(wv < 4 ? &sK[row][dd] : &sQ[row][dd]);
+        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(&sK[row][dd]);
+        const bf16x8_t a0 = kw ? ak : *reinterpret_cast<const bf16x8_t*>(&sQ[row][dd]);
         bf16x8_t h8, l8;
-        bf16_split8(&cS[ln * SP + dd], h8, l8);
-        acc0 = mfma_bf16(a, l8, mfma_bf16(a, h8, acc0));
-        if (wv < 4) {
-          bf16_split8(&cD[ln * SP + dd], h8, l8);
-          acc1 = mfma_bf16(a, l8, mfma_bf16(a, h8, acc1));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          bf16_split8(&cS[(16 * ct + ln) * SP + dd], h8, l8);
+          acc[ct] = mfma_bf16(a0, l8, mfma_bf16(a0, h8, acc[ct]));
         }
+        bf16_split8(&cD[(16 * nt0 + ln) * SP + dd], h8, l8);
+        acc[2] = mfma_bf16(ak, l8, mfma_bf16(ak, h8, acc[2]));
       }
+      float* const dst = kw ? cU : cDX;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (wv < 4) {
-          cU[ln * RP + 16 * mt + 4 * gq + e] = acc0[e];
-          cDU[ln * RP + 16 * mt + 4 * gq + e] = acc1[e];
-        } else {
-          cDX[ln * RP + 16 * mt + 4 * gq + e] = acc0[e];
-        }
+        const int rr = 16 * mt + 4 * gq + e;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) dst[(16 * ct + ln) * RP + rr] = acc[ct][e];
+        cDU[(16 * nt0 + ln) * RP + rr] = acc[2][e];
       }
     } else {
       const int row = 16 * mt + ln;
@@ -886,59 +907,71 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
       }
     }
     __syncthreads();
-    float ks[CPT], kd[CPT];
-    for (int jj = 0; jj < CPT; ++jj) {
+    float ks[CPTG], kd[CPTG];
+    for (int jj = 0; jj < CPTG; ++jj) {
       ks[jj] = cU[(j0 + jj) * RP + r];
       kd[jj] = cDU[(j0 + jj) * RP + r];
       degp = fmaf(cO[(j0 + jj) * RP + r], cDX[(j0 + jj) * RP + r], degp);
     }
     for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[(sj + e) * SP + sd], cD[(sj + e) * SP + sd], gamp);
-    for (int jj = 0; jj < CPT; ++jj) cX[(j0 + jj) * RP + r] -= egr * ks[jj];  // X
+    for (int jj = 0; jj < CPTG; ++jj) cX[(j0 + jj) * RP + r] -= egr * ks[jj];  // X
     __syncthreads();
-    // U = Minv (beta . X) (waves 0-3) and P^T dO (waves 4-7) for row tile mt on the fp32 MFMA
+    // U = Minv (beta . X) (waves 0-3) and P^T dO (waves 4-7) for row tile mt and every column
+    // tile of the block, on the fp32 MFMA
     {
       const int row = 16 * mt + ln;
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      v4f acc[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
       if (wv < 4) {
 #pragma unroll 4
         for (int kk = 0; kk < BC / 4; ++kk) {
           const int i = 4 * kk + gq;
-          acc = mfma4(sM[row][i] * sb[i], cX[ln * RP + i], acc);
+          const float a = sM[row][i] * sb[i];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(a, cX[(16 * ct + ln) * RP + i], acc[ct]);
         }
-        for (int e = 0; e < 4; ++e) cU[ln * RP + 16 * mt + 4 * gq + e] = acc[e];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          for (int e = 0; e < 4; ++e) cU[(16 * ct + ln) * RP + 16 * mt + 4 * gq + e] = acc[ct][e];
       } else {
 #pragma unroll 4
         for (int kk = 0; kk < BC / 4; ++kk) {
           const int i = 4 * kk + gq;
-          acc = mfma4(i >= row ? sPG[i][row] : 0.f, cO[ln * RP + i], acc);
+          const float a = i >= row ? sPG[i][row] : 0.f;
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(a, cO[(16 * ct + ln) * RP + i], acc[ct]);
         }
-        for (int e = 0; e < 4; ++e) cDU[ln * RP + 16 * mt + 4 * gq + e] = acc[e];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          for (int e = 0; e < 4; ++e) cDU[(16 * ct + ln) * RP + 16 * mt + 4 * gq + e] = acc[ct][e];
       }
     }
     __syncthreads();
     // dU = w . (K dS1) + P^T dO, each element by its owner
-    for (int jj = 0; jj < CPT; ++jj) {
+    for (int jj = 0; jj < CPTG; ++jj) {
       const float u = cU[(j0 + jj) * RP + r];
       cDU[(j0 + jj) * RP + r] = fmaf(wr, kd[jj], cDU[(j0 + jj) * RP + r]);
       dwp = fmaf(u, kd[jj], dwp);
     }
     __syncthreads();
-    // dX = diag(beta) Minv^T dU (waves 0-3), which is also dV
-    if (wv < 4) {
-      const int row = 16 * mt + ln;
+    // dX = diag(beta) Minv^T dU, which is also dV: wave wv on row tile mt and column tile
+    // wv / 4 (waves 4-7 idle with one column tile)
+    if (nt0 < NCT) {
+      const int row = 16 * mt + ln, jc = 16 * nt0 + ln;
       v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
       for (int kk = 0; kk < BC / 4; ++kk) {
         const int i = 4 * kk + gq;
-        acc = mfma4(sM[i][row], cDU[ln * RP + i], acc);
+        acc = mfma4(sM[i][row], cDU[jc * RP + i], acc);
       }
       for (int e = 0; e < 4; ++e) {
         const int rr = 16 * mt + 4 * gq + e;
-        cDX[ln * RP + rr] = sb[rr] * acc[e];
+        cDX[jc * RP + rr] = sb[rr] * acc[e];
       }
     }
     __syncthreads();
-    for (int jj = 0; jj < CPT; ++jj) {
+    for (int jj = 0; jj < CPTG; ++jj) {
       const float dx = cDX[(j0 + jj) * RP + r];
       degp = fmaf(-dx, ks[jj], degp);
       const int t = c * BC + r;
@@ -949,7 +982,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
       const int row = 16 * mt + ln;
       const float eg_row = seg[row], w_row = sww[row];
 #pragma unroll
-      for (int kk = 0; kk < NJ / 4; ++kk) {
+      for (int kk = 0; kk < NJG / 4; ++kk) {
         const int jk = 4 * kk + gq;
         const float o = cO[jk * RP + row], du = cDU[jk * RP + row];
         const float ao = eg_row * o, au = w_row * cU[jk * RP + row], ax = -eg_row * cDX[jk * RP + row];
@@ -1010,8 +1043,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
       const int col = 16 * (nt0 + 2 * u) + ln;
-      mQ[u] = mfma4(a, sK[kk][col], mQ[u]);
-      mK[u] = mfma4(at, sQ[kk][col], mK[u]);
+      mQ[u] = mfma4(a, lds_f(sK[kk][col]), mQ[u]);
+      mK[u] = mfma4(at, lds_f(sQ[kk][col]), mK[u]);
     }
   }
   // W1 = Minv^T dT' diag(beta): Minv^T[row][k] = Minv[k][row] is zero for k < row, so the
@@ -1092,7 +1125,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     const int kk = 4 * s4 + gq;
     const float a = m2[arow * MP + kk] + m2[kk * MP + arow];
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) mK[u] = mfma4(a, sK[kk][16 * (nt0 + 2 * u) + ln], mK[u]);
+    for (int u = 0; u < NTW; ++u) mK[u] = mfma4(a, lds_f(sK[kk][16 * (nt0 + 2 * u) + ln]), mK[u]);
   }
   if (tid < BC) {  // one wave: lane i is token i of the chunk
     const int i = tid, t = c * BC + i;
@@ -1141,7 +1174,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     const size_t o = tok(b, t, T, H, h) * DK + d0;
     for (int dd = 0; dd < DQ; ++dd) {
       dq[o + dd] = accQ[dd];
-      dk[o + dd] = fmaf(skc[r], sK[r][d0 + dd], accK[dd]);
+      dk[o + dd] = fmaf(skc[r], lds_f(sK[r][d0 + dd]), accK[dd]);
     }
   }
 }
