@@ -716,8 +716,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
                                                        const float* dout, const float* rec, const float* states,
                                                        const float* dstates, int direct, int T, int H, int DV, int nc,
                                                        float* dq, float* dk, float* dv, float* dla, float* deta) {
-  constexpr int NJG = MODE == 0 ? 32 : 16, NCT = NJG / 16, CPTG = NJG / TPRW;
-  constexpr int EPT = DK * NJG / NT, TPR = NJG / EPT, DQ = DK / TPRW;
+  constexpr int NJG = MODE == 0 ? 32 : 16, CPTG = NJG / TPRW;
+  constexpr int EPT = DK * NJG / NT, TPR = NJG / EPT;
   constexpr int SP = DK + 4, RP = BC + 4;  // pitches of the column-major blocks (16-byte rows)
   constexpr int WCOL = 2 * NJG * SP + 5 * NJG * RP, WMAT = 2 * BC * MP;
   constexpr int WN = WCOL > WMAT ? WCOL : WMAT;
@@ -732,6 +732,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
   __shared__ float seg[BC], sww[BC];  // e^{g}, e^{g_C - g}
   __shared__ float sgp[BC];  // per-row parts of <dS1, S0>
+  __shared__ float sdw2[MODE == 0 ? BC : 1], sdeg2[MODE == 0 ? BC : 1];  // second column-tile halves
   // column-block phase: 16 columns of each operand, stored column by column so that a
   // thread's run of rows (or of state rows) is one 16-byte read
   float* cS = sW;              // S0 [NJG][SP]
@@ -778,7 +779,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     sb[tid] = R[REC_B + tid];
     sden[tid] = R[REC_D + tid];
   }
-  const int r = tid / TPRW, qd = tid % TPRW, j0 = qd * CPTG, i0 = qd * IPT, d0 = qd * DQ;
+  const int r = tid / TPRW, qd = tid % TPRW, j0 = qd * CPTG, i0 = qd * IPT;
   const int sd = tid / TPR, sj = (tid % TPR) * EPT;
   // Rank-16 updates on the fp32 MFMA: wave w owns row tile mt of the chunk and column tiles
   // nt = w / 4 + 2u of dP, dT' (64 x 64) and of dQ, dK (64 x DK).
@@ -787,10 +788,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   v4f mP[2], mT[2], mQ[NTW], mK[NTW];
   for (int u = 0; u < 2; ++u) mP[u] = mT[u] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int u = 0; u < NTW; ++u) mQ[u] = mK[u] = v4f{0.f, 0.f, 0.f, 0.f};
-  // row-layout copies of dQ and dK, filled from the MFMA tiles at the end
-  float accQ[DQ], accK[DQ];
-  for (int i = 0; i < DQ; ++i) accQ[i] = accK[i] = 0.f;
   float dwp = 0.f, degp = 0.f, gamp = 0.f;
+  float dwp4[4] = {0.f, 0.f, 0.f, 0.f}, degp4[4] = {0.f, 0.f, 0.f, 0.f};  // bf16 inputs: rows 4 gq + e
   __syncthreads();
   const float gC = sg[BC - 1];
   const float egr = expf(sg[r]), wr = expf(gC - sg[r]);
@@ -845,46 +844,77 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
       cX[j * RP + rr] = in ? lds_f(pV[x]) : 0.f;
       cO[j * RP + rr] = in ? pO[x] : 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) gamp = fmaf(pS[e], pD[e], gamp);
     if (jb + NJG < DV) fetch(jb + NJG);
     __syncthreads();
-    // K S0, K dS1 and Q S0 for row tile mt, parked in the U, dU and dX blocks, which this column
-    // block has not written yet. bf16 inputs: k and q are exact in bf16 and the fp32 state columns
-    // enter as hi + lo bf16 pairs, two bf16 MFMA passes per product; the six 16 x 16 tiles of a
-    // row tile (three products, two column tiles) go three to a wave: waves 0-3 K S0 on both
-    // column tiles and K dS1 on the first, waves 4-7 Q S0 on both and K dS1 on the second.
-    // fp32 inputs: the fp32 MFMA, one column tile.
     if constexpr (MODE == 0) {
-      const int row = 16 * mt + ln;
-      const bool kw = wv < 4;
-      v4f acc[3];
-#pragma unroll
-      for (int u = 0; u < 3; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+      // Wave wv owns tile (row tile mt, column tile nt0) of the block in every product below:
+      // lane l holds rows 16 mt + 4 (l / 16) + e of block column jc = 16 nt0 + l % 16, so the
+      // elementwise steps and the per-row sums run in the MFMA epilogues.
+      const int row = 16 * mt + ln, jc = 16 * nt0 + ln;
+      // K S0, K dS1, Q S0 on the bf16 MFMA: k and q are exact in bf16, the fp32 state columns
+      // enter as hi + lo bf16 pairs (two passes per product)
+      v4f aks = {0.f, 0.f, 0.f, 0.f}, akd = aks, aqs = aks;
 #pragma unroll
       for (int kb = 0; kb < DK / 32; ++kb) {
         const int dd = 32 * kb + 8 * gq;
         const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(&sK[row][dd]);
-        const bf16x8_t a0 = kw ? ak : *reinterpret_cast<const bf16x8_t*>(&sQ[row][dd]);
+        const bf16x8_t aq = *reinterpret_cast<const bf16x8_t*>(&sQ[row][dd]);
         bf16x8_t h8, l8;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          bf16_split8(&cS[(16 * ct + ln) * SP + dd], h8, l8);
-          acc[ct] = mfma_bf16(a0, l8, mfma_bf16(a0, h8, acc[ct]));
-        }
-        bf16_split8(&cD[(16 * nt0 + ln) * SP + dd], h8, l8);
-        acc[2] = mfma_bf16(ak, l8, mfma_bf16(ak, h8, acc[2]));
+        bf16_split8(&cS[jc * SP + dd], h8, l8);
+        aks = mfma_bf16(ak, l8, mfma_bf16(ak, h8, aks));
+        aqs = mfma_bf16(aq, l8, mfma_bf16(aq, h8, aqs));
+        bf16_split8(&cD[jc * SP + dd], h8, l8);
+        akd = mfma_bf16(ak, l8, mfma_bf16(ak, h8, akd));
       }
-      float* const dst = kw ? cU : cDX;
+      // X = V - e^g . (K S0) in place; dO . (Q S0) into the row sums of dg
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = jc * RP + 16 * mt + 4 * gq + e;
+        cX[x] = fmaf(-seg[16 * mt + 4 * gq + e], aks[e], cX[x]);
+        degp4[e] = fmaf(cO[x], aqs[e], degp4[e]);
+      }
+      __syncthreads();
+      // U = Minv (beta . X) and P^T dO on the fp32 MFMA; dU = w . (K dS1) + P^T dO
+      v4f au = {0.f, 0.f, 0.f, 0.f}, ap = au;
+#pragma unroll 4
+      for (int kk = 0; kk < BC / 4; ++kk) {
+        const int i = 4 * kk + gq;
+        au = mfma4(sM[row][i] * sb[i], cX[jc * RP + i], au);
+        ap = mfma4(i >= row ? sPG[i][row] : 0.f, cO[jc * RP + i], ap);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rr = 16 * mt + 4 * gq + e;
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) dst[(16 * ct + ln) * RP + rr] = acc[ct][e];
-        cDU[(16 * nt0 + ln) * RP + rr] = acc[2][e];
+        cU[jc * RP + rr] = au[e];
+        cDU[jc * RP + rr] = fmaf(sww[rr], akd[e], ap[e]);
+        dwp4[e] = fmaf(au[e], akd[e], dwp4[e]);
       }
+      __syncthreads();
+      // dX = diag(beta) Minv^T dU, which is also dV
+      v4f ax = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int kk = 0; kk < BC / 4; ++kk) {
+        const int i = 4 * kk + gq;
+        ax = mfma4(sM[i][row], cDU[jc * RP + i], ax);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * mt + 4 * gq + e, t = c * BC + rr;
+        const float dx = sb[rr] * ax[e];
+        cDX[jc * RP + rr] = dx;
+        degp4[e] = fmaf(-dx, aks[e], degp4[e]);
+        if (t < T) dv[tok(b, t, T, H, h) * DV + jb + jc] = dx;
+      }
+      __syncthreads();
     } else {
+      // fp32 inputs (one column tile): K S0, K dS1 (waves 0-3) and Q S0 (waves 4-7) for row tile
+      // mt on the fp32 MFMA, parked in the U, dU and dX blocks, which this column block has not
+      // written yet; the elementwise steps by each element's owner thread
       const int row = 16 * mt + ln;
       if (wv < 4) {
-        v4f aks = {0.f, 0.f, 0.f, 0.f}, akd = {0.f, 0.f, 0.f, 0.f};
+        v4f aks = {0.f, 0.f, 0.f, 0.f}, akd = aks;
 #pragma unroll 8
         for (int kk = 0; kk < DK / 4; ++kk) {
           const int d = 4 * kk + gq;
@@ -905,77 +935,62 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
         }
         for (int e = 0; e < 4; ++e) cDX[ln * RP + 16 * mt + 4 * gq + e] = aqs[e];
       }
-    }
-    __syncthreads();
-    float ks[CPTG], kd[CPTG];
-    for (int jj = 0; jj < CPTG; ++jj) {
-      ks[jj] = cU[(j0 + jj) * RP + r];
-      kd[jj] = cDU[(j0 + jj) * RP + r];
-      degp = fmaf(cO[(j0 + jj) * RP + r], cDX[(j0 + jj) * RP + r], degp);
-    }
-    for (int e = 0; e < EPT; ++e) gamp = fmaf(cS[(sj + e) * SP + sd], cD[(sj + e) * SP + sd], gamp);
-    for (int jj = 0; jj < CPTG; ++jj) cX[(j0 + jj) * RP + r] -= egr * ks[jj];  // X
-    __syncthreads();
-    // U = Minv (beta . X) (waves 0-3) and P^T dO (waves 4-7) for row tile mt and every column
-    // tile of the block, on the fp32 MFMA
-    {
-      const int row = 16 * mt + ln;
-      v4f acc[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) acc[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      float ks[CPTG], kd[CPTG];
+      for (int jj = 0; jj < CPTG; ++jj) {
+        ks[jj] = cU[(j0 + jj) * RP + r];
+        kd[jj] = cDU[(j0 + jj) * RP + r];
+        degp = fmaf(cO[(j0 + jj) * RP + r], cDX[(j0 + jj) * RP + r], degp);
+      }
+      for (int jj = 0; jj < CPTG; ++jj) cX[(j0 + jj) * RP + r] -= egr * ks[jj];  // X
+      __syncthreads();
+      // U = Minv (beta . X) (waves 0-3) and P^T dO (waves 4-7) for row tile mt
+      {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        if (wv < 4) {
+#pragma unroll 4
+          for (int kk = 0; kk < BC / 4; ++kk) {
+            const int i = 4 * kk + gq;
+            acc = mfma4(sM[row][i] * sb[i], cX[ln * RP + i], acc);
+          }
+          for (int e = 0; e < 4; ++e) cU[ln * RP + 16 * mt + 4 * gq + e] = acc[e];
+        } else {
+#pragma unroll 4
+          for (int kk = 0; kk < BC / 4; ++kk) {
+            const int i = 4 * kk + gq;
+            acc = mfma4(i >= row ? sPG[i][row] : 0.f, cO[ln * RP + i], acc);
+          }
+          for (int e = 0; e < 4; ++e) cDU[ln * RP + 16 * mt + 4 * gq + e] = acc[e];
+        }
+      }
+      __syncthreads();
+      // dU = w . (K dS1) + P^T dO
+      for (int jj = 0; jj < CPTG; ++jj) {
+        const float u = cU[(j0 + jj) * RP + r];
+        cDU[(j0 + jj) * RP + r] = fmaf(wr, kd[jj], cDU[(j0 + jj) * RP + r]);
+        dwp = fmaf(u, kd[jj], dwp);
+      }
+      __syncthreads();
+      // dX = diag(beta) Minv^T dU (waves 0-3), which is also dV
       if (wv < 4) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
         for (int kk = 0; kk < BC / 4; ++kk) {
           const int i = 4 * kk + gq;
-          const float a = sM[row][i] * sb[i];
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(a, cX[(16 * ct + ln) * RP + i], acc[ct]);
+          acc = mfma4(sM[i][row], cDU[ln * RP + i], acc);
         }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          for (int e = 0; e < 4; ++e) cU[(16 * ct + ln) * RP + 16 * mt + 4 * gq + e] = acc[ct][e];
-      } else {
-#pragma unroll 4
-        for (int kk = 0; kk < BC / 4; ++kk) {
-          const int i = 4 * kk + gq;
-          const float a = i >= row ? sPG[i][row] : 0.f;
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma4(a, cO[(16 * ct + ln) * RP + i], acc[ct]);
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * mt + 4 * gq + e;
+          cDX[ln * RP + rr] = sb[rr] * acc[e];
         }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          for (int e = 0; e < 4; ++e) cDU[(16 * ct + ln) * RP + 16 * mt + 4 * gq + e] = acc[ct][e];
       }
-    }
-    __syncthreads();
-    // dU = w . (K dS1) + P^T dO, each element by its owner
-    for (int jj = 0; jj < CPTG; ++jj) {
-      const float u = cU[(j0 + jj) * RP + r];
-      cDU[(j0 + jj) * RP + r] = fmaf(wr, kd[jj], cDU[(j0 + jj) * RP + r]);
-      dwp = fmaf(u, kd[jj], dwp);
-    }
-    __syncthreads();
-    // dX = diag(beta) Minv^T dU, which is also dV: wave wv on row tile mt and column tile
-    // wv / 4 (waves 4-7 idle with one column tile)
-    if (nt0 < NCT) {
-      const int row = 16 * mt + ln, jc = 16 * nt0 + ln;
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int kk = 0; kk < BC / 4; ++kk) {
-        const int i = 4 * kk + gq;
-        acc = mfma4(sM[i][row], cDU[jc * RP + i], acc);
+      __syncthreads();
+      for (int jj = 0; jj < CPTG; ++jj) {
+        const float dx = cDX[(j0 + jj) * RP + r];
+        degp = fmaf(-dx, ks[jj], degp);
+        const int t = c * BC + r;
+        if (t < T) dv[tok(b, t, T, H, h) * DV + jb + j0 + jj] = dx;
       }
-      for (int e = 0; e < 4; ++e) {
-        const int rr = 16 * mt + 4 * gq + e;
-        cDX[jc * RP + rr] = sb[rr] * acc[e];
-      }
-    }
-    __syncthreads();
-    for (int jj = 0; jj < CPTG; ++jj) {
-      const float dx = cDX[(j0 + jj) * RP + r];
-      degp = fmaf(-dx, ks[jj], degp);
-      const int t = c * BC + r;
-      if (t < T) dv[tok(b, t, T, H, h) * DV + jb + j0 + jj] = dx;
     }
     // dP += dO U^T, dT' += dU X^T, dQ += e^g . (dO S0^T), dK += w . (U dS1^T) - e^g . (dX S0^T)
     {
@@ -1004,13 +1019,32 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     __syncthreads();
   }
 
-  const float dw = quad_sum(dwp), deg = quad_sum(degp);
-  gamp = quad_sum(gamp);
-  if (qd == 0) {
-    sdw[r] = dw;
-    sdeg[r] = deg;
-    sgp[r] = gamp;
+  if constexpr (MODE == 0) {
+    // row sums: over the 16 lanes of a row group, then (in the per-token step) over the two
+    // column-tile waves of the row tile
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = dwp4[e], y = degp4[e];
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        x += __shfl_xor(x, m);
+        y += __shfl_xor(y, m);
+      }
+      if (ln == 0) {
+        const int rr = 16 * mt + 4 * gq + e;
+        (nt0 == 0 ? sdw : sdw2)[rr] = x;
+        (nt0 == 0 ? sdeg : sdeg2)[rr] = y;
+      }
+    }
+  } else {
+    const float dw = quad_sum(dwp), deg = quad_sum(degp);
+    if (qd == 0) {
+      sdw[r] = dw;
+      sdeg[r] = deg;
+    }
   }
+  gamp = quad_sum(gamp);
+  if (qd == 0) sgp[r] = gamp;
   // dP into m1 and dT' into m2 from the MFMA tiles
   for (int u = 0; u < 2; ++u)
     for (int e = 0; e < 4; ++e) {
@@ -1131,10 +1165,12 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     const int i = tid, t = c * BC + i;
     float cs = 0.f;
     for (int j = 0; j < BC; ++j) cs += m1[j * MP + i];
-    const float dww = sdw[i] * sww[i];
+    const float sdwi = MODE == 0 ? sdw[i] + sdw2[i] : sdw[i];
+    const float sdegi = MODE == 0 ? sdeg[i] + sdeg2[i] : sdeg[i];
+    const float dww = sdwi * sww[i];
     float tot = dww;  // sum over the chunk of dw . w, across the wave
     for (int m = 1; m < BC; m <<= 1) tot += __shfl_xor(tot, m);
-    float dg = srow[i] - cs + sdeg[i] * seg[i] - dww;
+    float dg = srow[i] - cs + sdegi * seg[i] - dww;
     float gam = sgp[i];  // <dS1, S0>, summed across the wave in a fixed order
     for (int m = 1; m < BC; m <<= 1) gam += __shfl_xor(gam, m);
     if (i == BC - 1) dg += tot + gam * expf(gC);
@@ -1156,25 +1192,20 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     if (t < T) deta[tok(b, t, T, H, h)] = de;
   }
   __syncthreads();
-  // add the MFMA parts of dQ and dK (through LDS, in the row layout); m1 and m2 are free
-  constexpr int CP = DK + 4;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int u = 0; u < NTW; ++u)
-      for (int e = 0; e < 4; ++e)
-        sW[(16 * mt + 4 * gq + e) * CP + 16 * (nt0 + 2 * u) + ln] = pass == 0 ? mQ[u][e] : mK[u][e];
-    __syncthreads();
-    for (int dd = 0; dd < DQ; ++dd) {
-      if (pass == 0) accQ[dd] += sW[r * CP + d0 + dd];
-      else accK[dd] += sW[r * CP + d0 + dd];
-    }
-    __syncthreads();
-  }
-  const int t = c * BC + r;
-  if (t < T) {
-    const size_t o = tok(b, t, T, H, h) * DK + d0;
-    for (int dd = 0; dd < DQ; ++dd) {
-      dq[o + dd] = accQ[dd];
-      dk[o + dd] = fmaf(skc[r], lds_f(sK[r][d0 + dd]), accK[dd]);
+  // dQ and dK straight from the MFMA tiles: lane l holds rows 16 mt + 4 (l / 16) + e of column
+  // 16 nt + l % 16, so each store covers 64 contiguous bytes of four rows
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int rr = 16 * mt + 4 * gq + e, t = c * BC + rr;
+    if (t < T) {
+      const size_t o = tok(b, t, T, H, h) * DK;
+      const float kc = skc[rr];
+#pragma unroll
+      for (int u = 0; u < NTW; ++u) {
+        const int col = 16 * (nt0 + 2 * u) + ln;
+        dq[o + col] = mQ[u][e];
+        dk[o + col] = fmaf(kc, lds_f(sK[rr][col]), mK[u][e]);
+      }
     }
   }
 }
