@@ -63,8 +63,7 @@ __device__ __forceinline__ bf16x8_t bf16_exact8(const float* p) {
 
 // Eight fp32 values as hi + lo bf16 operands: hi rounded to nearest even, lo the same rounding of
 // the exact residual x - hi, so hi + lo carries x to about 2^-17 of its size.
-__device__ __forceinline__ void bf16_split8(const float* p, bf16x8_t& hi, bf16x8_t& lo) {
-  const v4f a = *reinterpret_cast<const v4f*>(p), b = *reinterpret_cast<const v4f*>(p + 4);
+__device__ __forceinline__ void bf16_split8(const v4f& a, const v4f& b, bf16x8_t& hi, bf16x8_t& lo) {
   const f32x8_t x = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   hi = __builtin_convertvector(x, bf16x8_t);
   const u32x4_t hw = __builtin_bit_cast(u32x4_t, hi);
@@ -75,6 +74,15 @@ __device__ __forceinline__ void bf16_split8(const float* p, bf16x8_t& hi, bf16x8
     hf[2 * m + 1] = __uint_as_float(hw[m] & 0xFFFF0000u);
   }
   lo = __builtin_convertvector(x - hf, bf16x8_t);
+}
+__device__ __forceinline__ void bf16_split8(const float* p, bf16x8_t& hi, bf16x8_t& lo) {
+  bf16_split8(*reinterpret_cast<const v4f*>(p), *reinterpret_cast<const v4f*>(p + 4), hi, lo);
+}
+
+// A bf16 MFMA operand from two runs of four bf16 values 16 elements apart (k = 0..3 and 4..7).
+__device__ __forceinline__ bf16x8_t bf16_pair4(const uint16_t* p) {
+  const uint2 u0 = *reinterpret_cast<const uint2*>(p), u1 = *reinterpret_cast<const uint2*>(p + 16);
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{u0.x, u0.y, u1.x, u1.y});
 }
 
 __device__ __forceinline__ v4f mfma_bf16(const bf16x8_t& a, const bf16x8_t& b, v4f c) {
@@ -569,9 +577,100 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
       *reinterpret_cast<v4f*>(D + (16 * dt + prow) * DV + pcol) = *reinterpret_cast<const v4f*>(&tr[prow][4 * (lane & 3)]);
     }
   };
+  // bf16 inputs: the same products on the bf16 MFMA (16 x 16 x 32). Keys are exact in bf16; the
+  // fp32 operands (the carried matrix, X or dU, Y and the inverse) enter as hi + lo pairs: two
+  // passes where the other operand is a key, three (hi hi, hi lo, lo hi) for the inverse. The
+  // contraction index of a 32-wide step is ordered so that a lane's B operand is its accumulator
+  // values of two adjacent 16-row tiles: k = 8 (l / 16) + j is row 4 (l / 16) + j of the first
+  // tile for j < 4 and of the second for j >= 4; the A operands follow the same order.
+  auto compute_bf16 = [&](const L& Q, auto&& mid) __attribute__((always_inline)) {
+    if constexpr (MODE == 0) {
+      // R = K S (token tiles mt), over 32-row slabs of S
+      v4f R[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) R[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < NDT / 2; ++sl) {
+        bf16x8_t bh, bl;
+        bf16_split8(S[2 * sl], S[2 * sl + 1], bh, bl);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8_t a = bf16_pair4(&Q.sK[16 * mt + ln][32 * sl + 4 * gq]);
+          R[mt] = mfma_bf16(a, bl, mfma_bf16(a, bh, R[mt]));
+        }
+      }
+      mid();
+      // forward: X = beta . (V - e^g . R); reverse: dU = w . R + V~
+      v4f X[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const v4f vv = *reinterpret_cast<const v4f*>(&Q.sV[16 * w + ln][16 * mt + 4 * gq]);
+        const v4f eg = *reinterpret_cast<const v4f*>(&Q.sEG[16 * mt + 4 * gq]);
+        const v4f bb = *reinterpret_cast<const v4f*>(&Q.sB[16 * mt + 4 * gq]);
+        const v4f ww = *reinterpret_cast<const v4f*>(&Q.sW[16 * mt + 4 * gq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (REV) X[mt][i] = fmaf(ww[i], R[mt][i], vv[i]);
+          else X[mt][i] = bb[i] * (vv[i] - eg[i] * R[mt][i]);
+        }
+      }
+      // forward: U = Minv X (token slabs at or below the row tile); reverse: Minv^T dU (at or above)
+      v4f U[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) U[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        bf16x8_t xh, xl;
+        bf16_split8(X[2 * sl], X[2 * sl + 1], xh, xl);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          if (REV ? 2 * sl + 1 < mt : 2 * sl > mt) continue;
+          const float* m = &Q.sM[16 * mt + ln][32 * sl + 4 * gq];
+          bf16x8_t ah, al;
+          bf16_split8(*reinterpret_cast<const v4f*>(m), *reinterpret_cast<const v4f*>(m + 16), ah, al);
+          U[mt] = mfma_bf16(al, xh, mfma_bf16(ah, xl, mfma_bf16(ah, xh, U[mt])));
+        }
+      }
+      // forward: Y = w . U, S <- e^{g_C} S + K^T Y;  reverse: Y = -e^g . beta . (Minv^T dU),
+      // dS <- e^{g_C} dS + Q^T (e^g . dO) + K^T Y
+      v4f Y[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const v4f eb = *reinterpret_cast<const v4f*>(&Q.sEB[16 * mt + 4 * gq]);
+        const v4f ww = *reinterpret_cast<const v4f*>(&Q.sW[16 * mt + 4 * gq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (REV) Y[mt][i] = -eb[i] * U[mt][i];
+          else Y[mt][i] = ww[i] * U[mt][i];
+        }
+      }
+      const float gam = Q.sGam;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (REV) S[dt][i] = fmaf(gam, S[dt][i], cterm[4 * dt + i]);
+          else S[dt][i] = gam * S[dt][i];
+        }
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        bf16x8_t yh, yl;
+        bf16_split8(Y[2 * sl], Y[2 * sl + 1], yh, yl);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8_t a = bf16_pair4(&Q.sKt[16 * dt + ln][32 * sl + 4 * gq]);
+          S[dt] = mfma_bf16(a, yl, mfma_bf16(a, yh, S[dt]));
+        }
+      }
+    }
+  };
   // One chunk's products from the staged chunk Q. `mid` runs after the first product has been
   // issued (the next chunk's staging, in the double-buffered walk).
   auto compute = [&](const L& Q, auto&& mid) __attribute__((always_inline)) {
+    if constexpr (MODE == 0) {
+      compute_bf16(Q, mid);
+      return;
+    }
     // R = K S (token tiles mt)
     v4f R[4];
 #pragma unroll
