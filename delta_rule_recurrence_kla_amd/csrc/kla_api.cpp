@@ -565,7 +565,8 @@ kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q
                          int H, int dk, int dv, int chunk, hipStream_t stream) {
   kla_status st = check_prefill_sizes(dtype, B, T, H, dk, dv, chunk);
   if (st != KLA_OK) return st;
-  if (dk > 128) return fail(KLA_ERR_UNSUPPORTED, "the backward supports dk in {64, 128} (got %d)", dk);
+  if (dk > 128 && dtype != KLA_DTYPE_BF16)
+    return fail(KLA_ERR_UNSUPPORTED, "the fp32 backward supports dk in {64, 128} (got %d)", dk);
   if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT)
     return fail(KLA_ERR_INVALID_ARG, "unknown beta_mode %d", (int)beta_mode);
   if (T > 0 && (!q || !k || !v || !log_alpha || !eta || !grad_out || !grad_q || !grad_k || !grad_v ||

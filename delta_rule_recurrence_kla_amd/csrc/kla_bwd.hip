@@ -435,9 +435,10 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
   using VE = typename std::conditional<REV, float, E>::type;  // element type of the value rows
   constexpr int VEV = 16 / sizeof(VE), VV = WCOL / VEV, VPT = BC * VV / WT;  // value pieces
   constexpr int NDT = DK / 16;                      // 16-row tiles of the carried matrix
-  // bf16 rows leave room for two chunks' LDS: the next chunk is staged while this one is
-  // computed, with one workgroup barrier per chunk. fp32 rows stage between two barriers.
-  constexpr bool DB = MODE == 0;
+  // bf16 rows at dk <= 128 leave room for two chunks' LDS: the next chunk is staged while this
+  // one is computed, with one workgroup barrier per chunk. fp32 rows and dk = 256 stage between
+  // two barriers.
+  constexpr bool DB = MODE == 0 && DK <= 128;
   static_assert(KPT * WT == BC * KV && MPT * WT * 4 == BC * BC && VPT * WT == BC * VV, "walk tiling");
   __shared__ __align__(16) L lds0;
   __shared__ __align__(16) L lds1_[1];  // referenced (and allocated) only when DB
@@ -815,7 +816,11 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
                                                        const float* dout, const float* rec, const float* states,
                                                        const float* dstates, int direct, int T, int H, int DV, int nc,
                                                        float* dq, float* dk, float* dv, float* dla, float* deta) {
-  constexpr int NJG = MODE == 0 ? 32 : 16, CPTG = NJG / TPRW;
+  // bf16 inputs with dk <= 128: 32-column blocks, one 16 x 16 tile of every product per wave
+  // (FUSED); otherwise (fp32 rows, or dk = 256, where the LDS holds only 16-column blocks)
+  // 16-column blocks, split over the waves by product
+  constexpr bool FUSED = MODE == 0 && DK <= 128;
+  constexpr int NJG = FUSED ? 32 : 16, CPTG = NJG / TPRW;
   constexpr int EPT = DK * NJG / NT, TPR = NJG / EPT;
   constexpr int SP = DK + 4, RP = BC + 4;  // pitches of the column-major blocks (16-byte rows)
   constexpr int WCOL = 2 * NJG * SP + 5 * NJG * RP, WMAT = 2 * BC * MP;
@@ -831,7 +836,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   __shared__ float sg[BC], sb[BC], sden[BC], sdb[BC], srow[BC], sdeg[BC], sdw[BC], skc[BC];
   __shared__ float seg[BC], sww[BC];  // e^{g}, e^{g_C - g}
   __shared__ float sgp[BC];  // per-row parts of <dS1, S0>
-  __shared__ float sdw2[MODE == 0 ? BC : 1], sdeg2[MODE == 0 ? BC : 1];  // second column-tile halves
+  __shared__ float sdw2[FUSED ? BC : 1], sdeg2[FUSED ? BC : 1];  // second column-tile halves
   // column-block phase: 16 columns of each operand, stored column by column so that a
   // thread's run of rows (or of state rows) is one 16-byte read
   float* cS = sW;              // S0 [NJG][SP]
@@ -947,7 +952,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     for (int e = 0; e < EPT; ++e) gamp = fmaf(pS[e], pD[e], gamp);
     if (jb + NJG < DV) fetch(jb + NJG);
     __syncthreads();
-    if constexpr (MODE == 0) {
+    if constexpr (FUSED) {
       // Wave wv owns tile (row tile mt, column tile nt0) of the block in every product below:
       // lane l holds rows 16 mt + 4 (l / 16) + e of block column jc = 16 nt0 + l % 16, so the
       // elementwise steps and the per-row sums run in the MFMA epilogues.
@@ -1008,16 +1013,16 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
       }
       __syncthreads();
     } else {
-      // fp32 inputs (one column tile): K S0, K dS1 (waves 0-3) and Q S0 (waves 4-7) for row tile
-      // mt on the fp32 MFMA, parked in the U, dU and dX blocks, which this column block has not
-      // written yet; the elementwise steps by each element's owner thread
+      // one column tile: K S0, K dS1 (waves 0-3) and Q S0 (waves 4-7) for row tile mt on the fp32
+      // MFMA, parked in the U, dU and dX blocks, which this column block has not written yet; the
+      // elementwise steps by each element's owner thread
       const int row = 16 * mt + ln;
       if (wv < 4) {
         v4f aks = {0.f, 0.f, 0.f, 0.f}, akd = aks;
 #pragma unroll 8
         for (int kk = 0; kk < DK / 4; ++kk) {
           const int d = 4 * kk + gq;
-          const float a = sK[row][d];
+          const float a = lds_f(sK[row][d]);
           aks = mfma4(a, cS[ln * SP + d], aks);
           akd = mfma4(a, cD[ln * SP + d], akd);
         }
@@ -1030,7 +1035,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
 #pragma unroll 8
         for (int kk = 0; kk < DK / 4; ++kk) {
           const int d = 4 * kk + gq;
-          aqs = mfma4(sQ[row][d], cS[ln * SP + d], aqs);
+          aqs = mfma4(lds_f(sQ[row][d]), cS[ln * SP + d], aqs);
         }
         for (int e = 0; e < 4; ++e) cDX[ln * RP + 16 * mt + 4 * gq + e] = aqs[e];
       }
@@ -1118,7 +1123,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     __syncthreads();
   }
 
-  if constexpr (MODE == 0) {
+  if constexpr (FUSED) {
     // row sums: over the 16 lanes of a row group, then (in the per-token step) over the two
     // column-tile waves of the row tile
 #pragma unroll
@@ -1264,8 +1269,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
     const int i = tid, t = c * BC + i;
     float cs = 0.f;
     for (int j = 0; j < BC; ++j) cs += m1[j * MP + i];
-    const float sdwi = MODE == 0 ? sdw[i] + sdw2[i] : sdw[i];
-    const float sdegi = MODE == 0 ? sdeg[i] + sdeg2[i] : sdeg[i];
+    const float sdwi = FUSED ? sdw[i] + sdw2[i] : sdw[i];
+    const float sdegi = FUSED ? sdeg[i] + sdeg2[i] : sdeg[i];
     const float dww = sdwi * sww[i];
     float tot = dww;  // sum over the chunk of dw . w, across the wave
     for (int m = 1; m < BC; m <<= 1) tot += __shfl_xor(tot, m);
@@ -1343,7 +1348,10 @@ size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
 }
 
 hipError_t launch_bwd(int mode, const BwdArgs& a, int stage, hipStream_t stream) {
-  if (mode == 0) return a.dk == 64 ? launch_bwd_t<0, 64>(a, stage, stream) : launch_bwd_t<0, 128>(a, stage, stream);
+  if (mode == 0) {
+    if (a.dk == 256) return launch_bwd_t<0, 256>(a, stage, stream);
+    return a.dk == 64 ? launch_bwd_t<0, 64>(a, stage, stream) : launch_bwd_t<0, 128>(a, stage, stream);
+  }
   return a.dk == 64 ? launch_bwd_t<1, 64>(a, stage, stream) : launch_bwd_t<1, 128>(a, stage, stream);
 }
 

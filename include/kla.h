@@ -199,9 +199,11 @@ kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, cons
  *   grad_init_state   fp32 [B,H,dk,dv], or NULL (not written)
  * Every output is overwritten (not accumulated). q, k, v, gates, eps, init_state
  * (NULL: zero), beta_mode and sizes are as for kla_chunk_fwd_ex; dk must be 64
- * or 128. In Kaczmarz mode a token with ||k||^2 + eps == 0 has beta = 0 and
- * passes no gradient to eta or through beta to k. The arithmetic is fp32; the
- * call takes a stream-ordered workspace from the library's pool of about B*H*ceil(T/64) * (34 KB +
+ * or 128 for fp32 inputs, 64, 128 or 256 for bf16 inputs. In Kaczmarz mode a token
+ * with ||k||^2 + eps == 0 has beta = 0 and passes no gradient to eta or through beta
+ * to k. Products are fp32-accurate: fp32 MFMA, or for bf16 inputs the bf16 MFMA with
+ * the exact bf16 keys and queries against hi + lo bf16 pairs of the fp32 operands;
+ * sums are fp32. The call takes a stream-ordered workspace from the library's pool of about B*H*ceil(T/64) * (34 KB +
  * 8*dk*dv + 256*dv bytes) (chunk records, every chunk-start state, every
  * chunk-end state gradient and a 64 x dv block) and frees it on the stream.
  * T == 0 copies grad_final_state (or zeros) into grad_init_state.

@@ -63,7 +63,7 @@ int main() {
   CHECK(std::strstr(kla_last_error(), "scratch") != nullptr);
 
   // backward
-  CHECK(kla_chunk_bwd(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, P, P, P, F, F, 1e-6f, nullptr, F, nullptr, F, F, F, F, F, nullptr,
+  CHECK(kla_chunk_bwd(KLA_DTYPE_F32, KLA_BETA_KACZMARZ, F, F, F, F, F, 1e-6f, nullptr, F, nullptr, F, F, F, F, F, nullptr,
                       1, 64, 1, 256, 64, 64, nullptr) == KLA_ERR_UNSUPPORTED);
   CHECK(kla_chunk_bwd(KLA_DTYPE_BF16, KLA_BETA_KACZMARZ, P, P, P, F, F, 1e-6f, nullptr, nullptr, nullptr, F, F, F, F, F,
                       nullptr, 1, 64, 1, 64, 64, 64, nullptr) == KLA_ERR_INVALID_ARG);

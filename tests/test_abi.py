@@ -208,7 +208,7 @@ def _bwd(lib, dtype=0, beta=0, q=FAKE, dout=FAKE, gq=FAKE, ginit=None, B=1, T=64
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(dout=None), 1), (dict(gq=None), 1), (dict(dtype=7), 1), (dict(beta=4), 1),
-    (dict(B=0), 1), (dict(T=-1), 1), (dict(dk=256), 2), (dict(dk=96), 2), (dict(dv=32), 2), (dict(chunk=128), 2),
+    (dict(B=0), 1), (dict(T=-1), 1), (dict(dk=256, dtype=1), 2), (dict(dk=96), 2), (dict(dv=32), 2), (dict(chunk=128), 2),
 ])
 def test_bwd_validation(kw, status):
     lib = kla.load()

@@ -70,6 +70,44 @@ def test_bwd_several_chunks_ragged_tail(dtype, dk, dv):
     _run(wl)
 
 
+def test_bwd_dk256_bf16():
+    """dk = 256 (the PSD lift's feature width) in bf16, several chunks and a ragged tail."""
+    log("case: bwd dtype=bf16 dk=256 dv=128 T=200")
+    wl = W.make_prefill("tiny_f32", seed=9, B=1, T=200, H=2, dk=256, dv=128, dtype="bf16", init_std=0.3)
+    _run(wl)
+
+
+def test_bwd_psd_shape_full_size_prefix_gradient():
+    """The PSD workload's shape (B=4, T=8192, H=8, dk=256 lifted features, dv=128, bf16), the
+    whole call. The output gradient is zero past token 1024 and there is no end-state gradient,
+    so every gradient past token 1024 is exactly zero and the first 1024 tokens' gradients (and
+    the start state's) are those of the 1024-token prefix, which the oracle computes for one
+    sampled head."""
+    log("case: bwd psd_lift_8k full size, prefix 1024 of head (3,7)")
+    wl = W.make_prefill("psd_lift_8k", seed=0, init_std=0.3)
+    B, T, H, dk, dv, TP = wl.B, wl.T, wl.H, wl.dk, wl.dv, 1024
+    d_out, _ = W.make_bwd_grads(B, T, H, dk, dv, seed=0)
+    d_out[:, TP:] = 0.0
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    g = kla.chunk_bwd(q, k, v, la, eta, upload(d_out, "f32"), eps=wl.eps, init_state=s0)
+    torch.cuda.synchronize()
+    b, h = 3, 7
+    f = lambda a: np.asarray(a[b, :TP, h], np.float64)
+    ref = kla_bwd.backward(f(wl.q), f(wl.k), f(wl.v), f(wl.log_alpha), f(wl.eta), wl.eps, f(d_out), None,
+                           wl.init_state[b, h], "kaczmarz")
+    worst = {}
+    for n in NAMES:
+        got = g[n][b, :, h].cpu().numpy()
+        assert not np.any(got[TP:]), f"{n}: nonzero past the gradient's support"
+        e = err_over_rms(got[:TP], ref[n])
+        worst[n] = e
+        assert e <= BAR, f"{n}: max|err|/RMS = {e:.3e} > {BAR:.1e}"
+    e = err_over_rms(g["dinit_state"][b, h].cpu().numpy(), ref["dS0"])
+    worst["dS0"] = e
+    assert e <= BAR, f"dS0: max|err|/RMS = {e:.3e} > {BAR:.1e}"
+    log("worst max|err|/RMS: " + ", ".join(f"{n} {e:.2e}" for n, e in worst.items()))
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 128])
 def test_bwd_chunk_edges(T):
     log(f"case: bwd edges T={T}")
