@@ -403,14 +403,14 @@ __global__ __launch_bounds__(NT) void bwd_dprep_kernel(const void* q, const floa
 // (bf16 stays exact), the inverse row-major (forward) or transposed (reverse), the values (or
 // V~) transposed in fp32, so that every A operand of a K = 4 step is one 8- or 16-byte read.
 // The next chunk's rows are loaded into registers while the current chunk is computed.
-constexpr int WT = 256;     // threads of a walk workgroup: four waves
-
-constexpr int WCOL = 64;    // state columns per walk workgroup
+// A walk workgroup has NW waves of 16 state columns: four (64 columns) when that gives every CU
+// a workgroup, fewer otherwise (few heads: dk = 256 workloads, long single sequences), at least
+// two at dk = 256, where one wave's registers cannot hold a chunk's prefetched rows.
 
 // The LDS of one chunk of a walk: key rows, transposed key rows, the inverse (or its
 // transpose), the transposed values (or V~), and the chunk's per-token factors e^g, beta,
 // w = e^{g_C - g}, e^g beta and e^{g_C}.
-template <class E, int DK>
+template <class E, int DK, int WC>
 struct WalkChunkLds {
   static constexpr int EV = 16 / sizeof(E);
   static constexpr int KP = DK + EV, TP = BC + EV;  // pitches of K [BC][KP] and K^T [DK][TP] (16-byte rows)
@@ -418,17 +418,18 @@ struct WalkChunkLds {
   E sK[BC][KP];
   E sKt[DK][TP];
   float sM[BC][MPP];
-  float sV[WCOL][VP];
+  float sV[WC][VP];
   float sEG[BC], sB[BC], sW[BC], sEB[BC];
   float sGam;
 };
 
-template <int MODE, int DK, bool REV>
-__global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void* vin, const float* rec,
+template <int MODE, int DK, bool REV, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const void* vin, const float* rec,
                                                       const float* sin, int T, int H, int DV, int nc, float* sdump,
                                                       float* slast) {
   using E = typename LdsIn<MODE>::type;
-  using L = WalkChunkLds<E, DK>;
+  constexpr int WT = 64 * NW, WCOL = 16 * NW;     // threads, state columns
+  using L = WalkChunkLds<E, DK, WCOL>;
   constexpr int EV = L::EV;
   constexpr int KV = DK / EV, KPT = BC * KV / WT;   // key pieces per row, per thread
   constexpr int MPT = BC * BC / 4 / WT;             // float4s of the inverse per thread
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(WT) void bwd_walk_kernel(const void* k, const void*
   __shared__ __align__(16) L lds1_[1];  // referenced (and allocated) only when DB
   L& lds1 = DB ? lds1_[0] : lds0;
   // per-wave 16 x 16 transpose tile: the accumulator layout to and from rows of 16-byte pieces
-  __shared__ __align__(16) float sTr[4][16][20];
+  __shared__ __align__(16) float sTr[NW][16][20];
   const int jb = blockIdx.x * WCOL, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, ln = lane & 15;
   const int col = jb + 16 * w + ln;  // this lane's column of the carried matrix
@@ -1314,6 +1315,42 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   }
 }
 
+// Waves per walk workgroup: four when the workgroups (one per head and 64 state columns) fill
+// the device's CUs, else two or one (two or four times as many workgroups); two at least for
+// dk = 256.
+int walk_waves(const BwdArgs& a) {
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
+  const long long bh = static_cast<long long>(a.B) * a.H;
+  if ((a.dv / 64) * bh >= ncu) return 4;
+  if (a.dk == 256 || (a.dv / 32) * bh >= ncu) return 2;
+  return 1;
+}
+
+template <int MODE, int DK, bool REV>
+hipError_t launch_walk_any(const BwdArgs& a, hipStream_t stream);
+
+template <int MODE, int DK, bool REV, int NW>
+hipError_t launch_walk(const BwdArgs& a, hipStream_t stream) {
+  const dim3 grid(a.dv / (16 * NW), a.B * a.H), blk(64 * NW);
+  if constexpr (REV)
+    return launch_kernel(bwd_walk_kernel<MODE, DK, true, NW>, grid, blk, stream, a.k, a.vt, a.rec, a.dfin, a.T, a.H,
+                         a.dv, a.nc, a.dstates, a.ginit);
+  else
+    return launch_kernel(bwd_walk_kernel<MODE, DK, false, NW>, grid, blk, stream, a.k, a.v, a.rec, a.init, a.T, a.H,
+                         a.dv, a.nc, a.states, static_cast<float*>(nullptr));
+}
+
+template <int MODE, int DK, bool REV>
+hipError_t launch_walk_any(const BwdArgs& a, hipStream_t stream) {
+  const int nw = walk_waves(a);
+  if (nw == 4) return launch_walk<MODE, DK, REV, 4>(a, stream);
+  if (nw == 2) return launch_walk<MODE, DK, REV, 2>(a, stream);
+  if constexpr (DK == 256) return hipErrorInvalidValue;
+  else return launch_walk<MODE, DK, REV, 1>(a, stream);
+}
+
 template <int MODE, int DK>
 hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
   const dim3 blk(BT);
@@ -1323,14 +1360,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
       return launch_kernel(bwd_prep_kernel<MODE, DK>, dim3(a.nc, bh), blk, stream, a.q, a.k, a.log_alpha, a.eta, a.eps,
                            a.direct, a.T, a.H, a.nc, a.rec);
     case 1:
-      return launch_kernel(bwd_walk_kernel<MODE, DK, false>, dim3(a.dv / WCOL, bh), dim3(WT), stream, a.k, a.v, a.rec,
-                           a.init, a.T, a.H, a.dv, a.nc, a.states, static_cast<float*>(nullptr));
+      return launch_walk_any<MODE, DK, false>(a, stream);
     case 2:
       return launch_kernel(bwd_dprep_kernel<MODE, DK>, dim3(a.nc, bh), dim3(64 * (a.dv / 16)), stream, a.q, a.dout, a.rec, a.T, a.H,
                            a.dv, a.nc, a.vt, a.dstates);
     case 3:
-      return launch_kernel(bwd_walk_kernel<MODE, DK, true>, dim3(a.dv / WCOL, bh), dim3(WT), stream, a.k, a.vt, a.rec,
-                           a.dfin, a.T, a.H, a.dv, a.nc, a.dstates, a.ginit);
+      return launch_walk_any<MODE, DK, true>(a, stream);
     default:
       return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.k, a.v, a.eta, a.dout,
                            a.rec, a.states, a.dstates, a.direct, a.T, a.H, a.dv, a.nc, a.gq, a.gk, a.gv, a.gla,

@@ -160,6 +160,15 @@ def test_bwd_odd_batch_and_heads():
     _run(wl, heads=[(0, 0), (1, 3), (2, 4)])
 
 
+@pytest.mark.parametrize("B", [2, 4])
+def test_bwd_walk_workgroup_sizes(B):
+    """The walks take one-wave (B=2: 32 heads) or two-wave (B=4: 64 heads) workgroups when
+    four-wave ones would not give every CU one; the LM-layer test covers four waves."""
+    log(f"case: bwd lm_layer heads, B={B} T=300")
+    wl = W.make_prefill("lm_layer_4k", seed=10, B=B, T=300, init_std=0.3)
+    _run(wl, heads=[(0, 0), (B - 1, 15)])
+
+
 def test_bwd_repeat_calls_are_bit_identical():
     """No atomics or order-dependent reductions: two calls on the same inputs agree bit for bit."""
     log("case: bwd determinism, lm_layer shape with B=2")
