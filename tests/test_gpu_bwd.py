@@ -108,6 +108,35 @@ def test_bwd_psd_shape_full_size_prefix_gradient():
     log("worst max|err|/RMS: " + ", ".join(f"{n} {e:.2e}" for n, e in worst.items()))
 
 
+def test_bwd_long_context_prefix_gradient():
+    """The long-context shape (B=1, T=131072, H=16, dk=dv=128, bf16): 2048 chunks per walk on few
+    heads. As in the PSD-shape test, the output gradient is zero past token 1024, so every later
+    gradient must be exactly zero and the first 1024 tokens' gradients are those of the prefix."""
+    log("case: bwd long_131k full size, prefix 1024 of head (0,9)")
+    wl = W.make_prefill("long_131k", seed=0, init_std=0.3)
+    B, T, H, dk, dv, TP = wl.B, wl.T, wl.H, wl.dk, wl.dv, 1024
+    d_out = np.zeros((B, T, H, dv), np.float32)
+    d_out[:, :TP] = W.make_bwd_grads(B, TP, H, dk, dv, seed=0)[0]
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    g = kla.chunk_bwd(q, k, v, la, eta, upload(d_out, "f32"), eps=wl.eps, init_state=s0)
+    torch.cuda.synchronize()
+    b, h = 0, 9
+    f = lambda a: np.asarray(a[b, :TP, h], np.float64)
+    ref = kla_bwd.backward(f(wl.q), f(wl.k), f(wl.v), f(wl.log_alpha), f(wl.eta), wl.eps, f(d_out), None,
+                           wl.init_state[b, h], "kaczmarz")
+    worst = {}
+    for n in NAMES:
+        got = g[n][b, :, h].cpu().numpy()
+        assert not np.any(got[TP:]), f"{n}: nonzero past the gradient's support"
+        e = err_over_rms(got[:TP], ref[n])
+        worst[n] = e
+        assert e <= BAR, f"{n}: max|err|/RMS = {e:.3e} > {BAR:.1e}"
+    e = err_over_rms(g["dinit_state"][b, h].cpu().numpy(), ref["dS0"])
+    worst["dS0"] = e
+    assert e <= BAR, f"dS0: max|err|/RMS = {e:.3e} > {BAR:.1e}"
+    log("worst max|err|/RMS: " + ", ".join(f"{n} {e:.2e}" for n, e in worst.items()))
+
+
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 128])
 def test_bwd_chunk_edges(T):
     log(f"case: bwd edges T={T}")
