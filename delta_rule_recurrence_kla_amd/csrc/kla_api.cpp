@@ -589,7 +589,20 @@ kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q
   }
   const int nc = (T + kChunk - 1) / kChunk;
   const size_t nch = static_cast<size_t>(B) * H * nc;
-  const size_t bytes = kla::bwd_workspace_bytes(B, T, H, dk, dv);
+  const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
+  // Few heads over a long sequence (where the forward takes the scan path): both walks run in
+  // segments, in parallel. The forward walk starts each segment from the state the forward
+  // scan's maps and fold give; the reverse walk folds the transposed segment maps over the
+  // segments' zero-end walks, then walks every segment from its end gradient. Needs the DMA
+  // map kernel (bf16, dk <= 128).
+  const Plan fp = make_plan(dtype, B, T, H, dk, dv, KLA_PATH_AUTO, 0, device_cus());
+  const bool segmented = fp.path == KLA_PATH_SCAN && fp.segs >= 2 && kla::state_dma_supported(mode, dk);
+  const int segs = segmented ? fp.segs : 1, segc = segmented ? fp.seg_chunks : nc;
+  const size_t bh = static_cast<size_t>(B) * H;
+  const size_t map_bytes = segmented ? align256(bh * (segs - 1) * dk * (dk + dv) * 4) : 0;
+  const size_t seg_state_bytes = segmented ? align256(bh * segs * dk * dv * 4) : 0;
+  const size_t base_bytes = align256(kla::bwd_workspace_bytes(B, T, H, dk, dv));
+  const size_t bytes = base_bytes + (segmented ? fp.rec_bytes + 2 * map_bytes + 3 * seg_state_bytes : 0);
   void* ws = nullptr;
   st = workspace_alloc(&ws, bytes, stream);
   if (st != KLA_OK) return st;
@@ -605,11 +618,55 @@ kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q
   a.dstates = a.states + nch * dk * dv;
   a.vt = a.dstates + nch * dk * dv;
   a.gq = grad_q; a.gk = grad_k; a.gv = grad_v; a.gla = grad_log_alpha; a.geta = grad_eta; a.ginit = grad_init_state;
-  const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   static const char* const names[5] = {"kla_bwd_prep", "kla_bwd_states", "kla_bwd_dprep", "kla_bwd_dstates",
                                        "kla_bwd_grads"};
-  for (int stage = 0; e == hipSuccess && stage < 5; ++stage)
-    e = timed(names[stage], stream, [&] { return kla::launch_bwd(mode, a, stage, stream); });
+  if (!segmented) {
+    for (int stage = 0; e == hipSuccess && stage < 5; ++stage)
+      e = timed(names[stage], stream, [&] { return kla::launch_bwd(mode, a, stage, stream); });
+  } else {
+    uint8_t* x = static_cast<uint8_t*>(ws) + base_bytes;
+    uint8_t* crec = x;
+    float* maps_f = reinterpret_cast<float*>(crec + fp.rec_bytes);
+    float* maps_r = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(maps_f) + map_bytes);
+    float* starts = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(maps_r) + map_bytes);
+    float* zero_ends = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(starts) + seg_state_bytes);
+    float* gends = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(zero_ends) + seg_state_bytes);
+    const kla::Dims d{B, T, H, dk, dv, nc};
+    const int direct = beta_mode == KLA_BETA_DIRECT;
+    const int ncg = (dk + dv) / 64;
+    e = timed(names[0], stream, [&] { return kla::launch_bwd(mode, a, 0, stream); });
+    // the forward walk: segment start states from the forward scan's maps and fold
+    if (e == hipSuccess)
+      e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, crec, stream); });
+    if (e == hipSuccess)
+      e = timed("kla_scan_maps", stream, [&] { return kla::launch_scan_maps(mode, d, k, v, crec, segc, segs, maps_f, stream); });
+    if (e == hipSuccess)
+      e = timed("kla_scan_starts", stream, [&] { return kla::launch_scan_starts(d, maps_f, init_state, segs, starts, stream); });
+    if (e == hipSuccess)
+      e = timed(names[1], stream, [&] {
+        return kla::launch_bwd_walk_segs(mode, a, false, kla::WalkSegs{segc, segs, 0, starts, segs, nullptr, 1, 1}, stream);
+      });
+    if (e == hipSuccess) e = timed(names[2], stream, [&] { return kla::launch_bwd(mode, a, 2, stream); });
+    // the reverse walk: maps of segments 1 .. segs - 1, their walks from a zero end gradient,
+    // the fold, then every segment from its end gradient
+    if (e == hipSuccess)
+      e = timed("kla_bwd_rev_maps", stream, [&] {
+        return kla::launch_state_dma(false, true, dk, ncg * (segs - 1) * B * H, nullptr, k, v, crec, T, H, dv, nc, segc,
+                                     nullptr, 1, nullptr, maps_r, dk + dv, segs - 1, 0, ncg, segs - 1, stream, 1, 1);
+      });
+    if (e == hipSuccess)
+      e = timed("kla_bwd_rev_zero", stream, [&] {
+        return kla::launch_bwd_walk_segs(mode, a, true, kla::WalkSegs{segc, segs - 1, 1, nullptr, 1, zero_ends, segs, 0},
+                                         stream);
+      });
+    if (e == hipSuccess)
+      e = timed("kla_bwd_rev_fold", stream, [&] { return kla::launch_bwd_rev_fold(a, maps_r, zero_ends, gends, segs, stream); });
+    if (e == hipSuccess)
+      e = timed(names[3], stream, [&] {
+        return kla::launch_bwd_walk_segs(mode, a, true, kla::WalkSegs{segc, segs, 0, gends, segs, a.ginit, 1, 1}, stream);
+      });
+    if (e == hipSuccess) e = timed(names[4], stream, [&] { return kla::launch_bwd(mode, a, 4, stream); });
+  }
   hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");

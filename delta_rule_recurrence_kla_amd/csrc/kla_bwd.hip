@@ -423,10 +423,16 @@ struct WalkChunkLds {
   float sGam;
 };
 
+// A launch walks segments seg0 .. seg0 + nseg - 1 of seg_chunks chunks each (one segment of nc
+// chunks for the whole sequence), workgroup row blockIdx.y = bh * nseg + (segment - seg0). A
+// segment starts from sin's slot (bh, segment) of sin_segs per head (zero if sin is null),
+// stores every chunk's carried matrix if dump is set, and leaves its final carried matrix in
+// slast's slot (bh, segment) when segment < slast_segs.
 template <int MODE, int DK, bool REV, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const void* vin, const float* rec,
                                                       const float* sin, int T, int H, int DV, int nc, float* sdump,
-                                                      float* slast) {
+                                                      float* slast, int seg_chunks, int nseg, int seg0, int sin_segs,
+                                                      int slast_segs, int dump) {
   using E = typename LdsIn<MODE>::type;
   constexpr int WT = 64 * NW, WCOL = 16 * NW;     // threads, state columns
   using L = WalkChunkLds<E, DK, WCOL>;
@@ -446,7 +452,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const 
   L& lds1 = DB ? lds1_[0] : lds0;
   // per-wave 16 x 16 transpose tile: the accumulator layout to and from rows of 16-byte pieces
   __shared__ __align__(16) float sTr[NW][16][20];
-  const int jb = blockIdx.x * WCOL, bh = blockIdx.y, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int bh = blockIdx.y / nseg, seg = seg0 + blockIdx.y % nseg;
+  const int jb = blockIdx.x * WCOL, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int cb = seg * seg_chunks, ncount = min(nc, cb + seg_chunks) - cb;  // this segment's chunks
   const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, ln = lane & 15;
   const int col = jb + 16 * w + ln;  // this lane's column of the carried matrix
 
@@ -557,7 +565,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const 
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      S[dt][i] = sin ? sin[(static_cast<size_t>(bh) * DK + 16 * dt + 4 * gq + i) * DV + col] : 0.f;
+      S[dt][i] = sin ? sin[((static_cast<size_t>(bh) * sin_segs + seg) * DK + 16 * dt + 4 * gq + i) * DV + col] : 0.f;
 
   // The start of chunk c: the reverse walk's Q^T (e^g . dO) of the chunk into the accumulator
   // layout, then the carried matrix out to the chunk's slot in 16-byte pieces, per 16-row tile
@@ -574,9 +582,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const 
 #pragma unroll
         for (int i = 0; i < 4; ++i) cterm[4 * dt + i] = tr[4 * gq + i][ln];
       }
+      if (dump) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tr[4 * gq + i][ln] = S[dt][i];
-      *reinterpret_cast<v4f*>(D + (16 * dt + prow) * DV + pcol) = *reinterpret_cast<const v4f*>(&tr[prow][4 * (lane & 3)]);
+        for (int i = 0; i < 4; ++i) tr[4 * gq + i][ln] = S[dt][i];
+        *reinterpret_cast<v4f*>(D + (16 * dt + prow) * DV + pcol) = *reinterpret_cast<const v4f*>(&tr[prow][4 * (lane & 3)]);
+      }
     }
   };
   // bf16 inputs: the same products on the bf16 MFMA (16 x 16 x 32). Keys are exact in bf16; the
@@ -751,7 +761,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const 
     }
   };
 
-  const int c_first = REV ? nc - 1 : 0, c_step = REV ? -1 : 1;
+  const int c_first = REV ? cb + ncount - 1 : cb, c_step = REV ? -1 : 1;
   if constexpr (DB) {
     // chunk n is computed from lds[n % 2] while chunk n + 1 is staged into the other; the rows of
     // chunk n + 2 are loaded into registers meanwhile, the reverse walk's Q^T (e^g . dO) of chunk
@@ -759,35 +769,35 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const 
     fetch_rows(c_first);
     fetch_c(c_first);
     stage(lds0);
-    if (nc > 1) fetch_rows(c_first + c_step);
+    if (ncount > 1) fetch_rows(c_first + c_step);
     __syncthreads();
     auto step = [&](int n, L& cur, L& nxt) __attribute__((always_inline)) {
       const int c = c_first + n * c_step;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       chunk_start(c);
-      if (n + 1 < nc) fetch_c(c + c_step);
+      if (n + 1 < ncount) fetch_c(c + c_step);
       compute(cur, [&]() __attribute__((always_inline)) {
-        if (n + 1 < nc) {
+        if (n + 1 < ncount) {
           stage(nxt);
-          if (n + 2 < nc) fetch_rows(c + 2 * c_step);
+          if (n + 2 < ncount) fetch_rows(c + 2 * c_step);
         }
       });
       __syncthreads();  // the next chunk is staged; every read of this one is done
     };
-    for (int n = 0; n < nc; n += 2) {
+    for (int n = 0; n < ncount; n += 2) {
       step(n, lds0, lds1);
-      if (n + 1 < nc) step(n + 1, lds1, lds0);
+      if (n + 1 < ncount) step(n + 1, lds1, lds0);
     }
   } else {
     fetch_rows(c_first);
     fetch_c(c_first);
-    for (int n = 0; n < nc; ++n) {
+    for (int n = 0; n < ncount; ++n) {
       const int c = c_first + n * c_step;
       __syncthreads();  // every wave's reads of the previous chunk's rows are done
       stage(lds0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       chunk_start(c);
-      if (n + 1 < nc) {
+      if (n + 1 < ncount) {
         fetch_rows(c + c_step);
         fetch_c(c + c_step);
       }
@@ -795,11 +805,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_walk_kernel(const void* k, const 
       compute(lds0, []() __attribute__((always_inline)) {});
     }
   }
-  if (slast) {
+  if (slast && seg < slast_segs) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) slast[(static_cast<size_t>(bh) * DK + 16 * dt + 4 * gq + i) * DV + col] = S[dt][i];
+      for (int i = 0; i < 4; ++i)
+        slast[((static_cast<size_t>(bh) * slast_segs + seg) * DK + 16 * dt + 4 * gq + i) * DV + col] = S[dt][i];
   }
 }
 
@@ -1315,40 +1326,97 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(const void* q, const void
   }
 }
 
-// Waves per walk workgroup: four when the workgroups (one per head and 64 state columns) fill
-// the device's CUs, else two or one (two or four times as many workgroups); two at least for
-// dk = 256.
-int walk_waves(const BwdArgs& a) {
+// The reverse walk's fold over segments (the segmented backward of long sequences). The forward
+// walk over segment s takes S to M_s S + N_s, so the gradient at its start is M_s^T G_s + D_s,
+// with G_s the gradient at its end and D_s what the reverse walk over the segment gives from a
+// zero end gradient. G of the last segment is the end state's gradient (zero if null); the fold
+// writes G_s for every segment, last to first. maps holds [M_s | N_s] (dk x (dk + dv)) for
+// segments 1 .. segs - 1, D holds D_s at slot (bh, s). One workgroup per (16 columns, head), the
+// carried columns transposed in LDS, the products on the fp32 MFMA.
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_rev_fold_kernel(const float* __restrict__ maps, const float* __restrict__ D,
+                                                           const float* __restrict__ dfin, float* __restrict__ gend,
+                                                           int DV, int segs) {
+  constexpr int XP = DK + 4;  // padded pitch of X^T rows (floats)
+  __shared__ __align__(16) float XT[2][16 * XP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, gq = lane >> 4, ln = lane & 15;
+  const int c0 = blockIdx.x * 16, bh = blockIdx.y;
+  const int LDM = DK + DV;
+  for (int o = tid; o < DK * 16; o += 256) {
+    const int r = o >> 4, j = o & 15;
+    const float x = dfin ? dfin[static_cast<size_t>(bh) * DK * DV + r * DV + c0 + j] : 0.f;
+    XT[(segs - 1) & 1][j * XP + r] = x;
+    gend[(static_cast<size_t>(bh) * segs + segs - 1) * DK * DV + r * DV + c0 + j] = x;
+  }
+  __syncthreads();
+  for (int s = segs - 1; s >= 1; --s) {
+    const float* M = maps + (static_cast<size_t>(bh) * (segs - 1) + (s - 1)) * DK * LDM;
+    const float* Ds = D + (static_cast<size_t>(bh) * segs + s) * DK * DV;
+    const float* X = XT[s & 1];
+    float* Xn = XT[(s - 1) & 1];
+    float* out = gend + (static_cast<size_t>(bh) * segs + s - 1) * DK * DV;
+#pragma unroll
+    for (int u = 0; u < DK / 64; ++u) {
+      const int mt = w + 4 * u;
+      v4f acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = Ds[static_cast<size_t>(16 * mt + 4 * gq + i) * DV + c0 + ln];
+#pragma unroll 4
+      for (int kk = 0; kk < DK / 16; ++kk) {
+        const v4f b4 = *reinterpret_cast<const v4f*>(X + ln * XP + 16 * kk + 4 * gq);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)  // M^T[16 mt + ln][k] = M[k][16 mt + ln]
+          acc = mfma4(M[static_cast<size_t>(16 * kk + 4 * gq + q) * LDM + 16 * mt + ln], b4[q], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[static_cast<size_t>(16 * mt + 4 * gq + i) * DV + c0 + ln] = acc[i];
+      *reinterpret_cast<v4f*>(Xn + ln * XP + 16 * mt + 4 * gq) = acc;
+    }
+    __syncthreads();
+  }
+}
+
+// Waves per walk workgroup (one workgroup per head, segment and 16 x waves state columns): the
+// count whose workgroups take the fewest rounds of one per CU, the smallest count on a tie (the
+// chains are latency-bound, so more CUs with fewer waves each go faster); two at least for
+// dk = 256, where one wave's registers cannot hold a chunk's prefetched rows.
+int walk_waves(const BwdArgs& a, int nseg) {
   int dev = 0, ncu = 256;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     ncu = 256;
-  const long long bh = static_cast<long long>(a.B) * a.H;
-  if ((a.dv / 64) * bh >= ncu) return 4;
-  if (a.dk == 256 || (a.dv / 32) * bh >= ncu) return 2;
-  return 1;
+  const long long units = static_cast<long long>(a.B) * a.H * nseg;
+  int best = 4;
+  long long best_rounds = -1;
+  for (int nw = a.dk == 256 ? 2 : 1; nw <= 4; nw *= 2) {
+    const long long rounds = ((a.dv / (16 * nw)) * units + ncu - 1) / ncu;
+    if (best_rounds < 0 || rounds < best_rounds) {
+      best = nw;
+      best_rounds = rounds;
+    }
+  }
+  return best;
 }
-
-template <int MODE, int DK, bool REV>
-hipError_t launch_walk_any(const BwdArgs& a, hipStream_t stream);
 
 template <int MODE, int DK, bool REV, int NW>
-hipError_t launch_walk(const BwdArgs& a, hipStream_t stream) {
-  const dim3 grid(a.dv / (16 * NW), a.B * a.H), blk(64 * NW);
+hipError_t launch_walk(const BwdArgs& a, const WalkSegs& g, hipStream_t stream) {
+  const dim3 grid(a.dv / (16 * NW), a.B * a.H * g.nseg), blk(64 * NW);
   if constexpr (REV)
-    return launch_kernel(bwd_walk_kernel<MODE, DK, true, NW>, grid, blk, stream, a.k, a.vt, a.rec, a.dfin, a.T, a.H,
-                         a.dv, a.nc, a.dstates, a.ginit);
+    return launch_kernel(bwd_walk_kernel<MODE, DK, true, NW>, grid, blk, stream, a.k, a.vt, a.rec, g.sin, a.T, a.H,
+                         a.dv, a.nc, a.dstates, g.slast, g.seg_chunks, g.nseg, g.seg0, g.sin_segs, g.slast_segs,
+                         g.dump);
   else
-    return launch_kernel(bwd_walk_kernel<MODE, DK, false, NW>, grid, blk, stream, a.k, a.v, a.rec, a.init, a.T, a.H,
-                         a.dv, a.nc, a.states, static_cast<float*>(nullptr));
+    return launch_kernel(bwd_walk_kernel<MODE, DK, false, NW>, grid, blk, stream, a.k, a.v, a.rec, g.sin, a.T, a.H,
+                         a.dv, a.nc, a.states, g.slast, g.seg_chunks, g.nseg, g.seg0, g.sin_segs, g.slast_segs,
+                         g.dump);
 }
 
 template <int MODE, int DK, bool REV>
-hipError_t launch_walk_any(const BwdArgs& a, hipStream_t stream) {
-  const int nw = walk_waves(a);
-  if (nw == 4) return launch_walk<MODE, DK, REV, 4>(a, stream);
-  if (nw == 2) return launch_walk<MODE, DK, REV, 2>(a, stream);
+hipError_t launch_walk_any(const BwdArgs& a, const WalkSegs& g, hipStream_t stream) {
+  const int nw = walk_waves(a, g.nseg);
+  if (nw == 4) return launch_walk<MODE, DK, REV, 4>(a, g, stream);
+  if (nw == 2) return launch_walk<MODE, DK, REV, 2>(a, g, stream);
   if constexpr (DK == 256) return hipErrorInvalidValue;
-  else return launch_walk<MODE, DK, REV, 1>(a, stream);
+  else return launch_walk<MODE, DK, REV, 1>(a, g, stream);
 }
 
 template <int MODE, int DK>
@@ -1360,12 +1428,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage, hipStream_t stream) {
       return launch_kernel(bwd_prep_kernel<MODE, DK>, dim3(a.nc, bh), blk, stream, a.q, a.k, a.log_alpha, a.eta, a.eps,
                            a.direct, a.T, a.H, a.nc, a.rec);
     case 1:
-      return launch_walk_any<MODE, DK, false>(a, stream);
+      return launch_walk_any<MODE, DK, false>(a, WalkSegs{a.nc, 1, 0, a.init, 1, nullptr, 1, 1}, stream);
     case 2:
       return launch_kernel(bwd_dprep_kernel<MODE, DK>, dim3(a.nc, bh), dim3(64 * (a.dv / 16)), stream, a.q, a.dout, a.rec, a.T, a.H,
                            a.dv, a.nc, a.vt, a.dstates);
     case 3:
-      return launch_walk_any<MODE, DK, true>(a, stream);
+      return launch_walk_any<MODE, DK, true>(a, WalkSegs{a.nc, 1, 0, a.dfin, 1, a.ginit, 1, 1}, stream);
     default:
       return launch_kernel(bwd_grads_kernel<MODE, DK>, dim3(a.nc, bh), dim3(NT), stream, a.q, a.k, a.v, a.eta, a.dout,
                            a.rec, a.states, a.dstates, a.direct, a.T, a.H, a.dv, a.nc, a.gq, a.gk, a.gv, a.gla,
@@ -1380,6 +1448,29 @@ size_t bwd_record_floats() { return RECF; }
 size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv) {
   const size_t nch = static_cast<size_t>(B) * H * ((T + BC - 1) / BC);
   return nch * (RECF + 2 * static_cast<size_t>(dk) * dv + static_cast<size_t>(BC) * dv) * sizeof(float);
+}
+
+hipError_t launch_bwd_walk_segs(int mode, const BwdArgs& a, bool rev, const WalkSegs& g, hipStream_t stream) {
+  if (mode == 0) {
+    if (a.dk == 64) return rev ? launch_walk_any<0, 64, true>(a, g, stream) : launch_walk_any<0, 64, false>(a, g, stream);
+    if (a.dk == 128) return rev ? launch_walk_any<0, 128, true>(a, g, stream) : launch_walk_any<0, 128, false>(a, g, stream);
+    if (a.dk == 256) return rev ? launch_walk_any<0, 256, true>(a, g, stream) : launch_walk_any<0, 256, false>(a, g, stream);
+    return hipErrorInvalidValue;
+  }
+  if (a.dk == 64) return rev ? launch_walk_any<1, 64, true>(a, g, stream) : launch_walk_any<1, 64, false>(a, g, stream);
+  if (a.dk == 128) return rev ? launch_walk_any<1, 128, true>(a, g, stream) : launch_walk_any<1, 128, false>(a, g, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_rev_fold(const BwdArgs& a, const float* maps, const float* D, float* gend, int segs,
+                               hipStream_t stream) {
+  const dim3 grid(a.dv / 16, a.B * a.H), blk(256);
+  switch (a.dk) {
+    case 64: return launch_kernel(bwd_rev_fold_kernel<64>, grid, blk, stream, maps, D, a.dfin, gend, a.dv, segs);
+    case 128: return launch_kernel(bwd_rev_fold_kernel<128>, grid, blk, stream, maps, D, a.dfin, gend, a.dv, segs);
+    case 256: return launch_kernel(bwd_rev_fold_kernel<256>, grid, blk, stream, maps, D, a.dfin, gend, a.dv, segs);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bwd(int mode, const BwdArgs& a, int stage, hipStream_t stream) {

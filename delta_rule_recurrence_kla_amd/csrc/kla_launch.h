@@ -136,7 +136,24 @@ struct BwdArgs {
   float *rec, *states, *dstates, *vt;               // workspace parts
   float *gq, *gk, *gv, *gla, *geta, *ginit;         // gradients (ginit may be null)
 };
+// Segments of a backward walk launch: segments seg0 .. seg0 + nseg - 1 of seg_chunks chunks;
+// each starts from sin's slot (bh, segment) of sin_segs per head (null: zero), stores every
+// chunk's carried matrix when dump is set, and leaves its final one in slast's slot
+// (bh, segment) when segment < slast_segs.
+struct WalkSegs {
+  int seg_chunks, nseg, seg0;
+  const float* sin;
+  int sin_segs;
+  float* slast;
+  int slast_segs, dump;
+};
 size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
+// One backward walk (rev: the reverse one) over the segments of g.
+hipError_t launch_bwd_walk_segs(int mode, const BwdArgs& a, bool rev, const WalkSegs& g, hipStream_t stream);
+// The reverse walk's fold over segs segments (see bwd_rev_fold_kernel): maps [M | N] of segments
+// 1 .. segs - 1, D the zero-end reverse walks' results, gend the end gradients of every segment.
+hipError_t launch_bwd_rev_fold(const BwdArgs& a, const float* maps, const float* D, float* gend, int segs,
+                               hipStream_t stream);
 size_t bwd_record_floats();
 // stage 0: chunk records; 1: forward walk (chunk-start states); 2: chunk-local terms of the
 // reverse walk; 3: reverse walk (chunk-end state gradients, and the start state's); 4: per-chunk

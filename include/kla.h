@@ -203,9 +203,15 @@ kla_status kla_chunk_fwd_psd(const void* uq, const void* uk, const void* v, cons
  * with ||k||^2 + eps == 0 has beta = 0 and passes no gradient to eta or through beta
  * to k. Products are fp32-accurate: fp32 MFMA, or for bf16 inputs the bf16 MFMA with
  * the exact bf16 keys and queries against hi + lo bf16 pairs of the fp32 operands;
- * sums are fp32. The call takes a stream-ordered workspace from the library's pool of about B*H*ceil(T/64) * (34 KB +
- * 8*dk*dv + 256*dv bytes) (chunk records, every chunk-start state, every
- * chunk-end state gradient and a 64 x dv block) and frees it on the stream.
+ * sums are fp32. Where the forward would take the scan path (few heads over a long
+ * sequence; bf16, dk <= 128), both walks run in segments: the forward walk from the
+ * forward scan's segment start states, the reverse walk from end gradients folded
+ * over the transposed segment maps (HLA page, section 4: the scan form of the
+ * chunked recurrence). The call takes a stream-ordered workspace from the library's
+ * pool of about B*H*ceil(T/64) * (34 KB + 8*dk*dv + 256*dv bytes) (chunk records,
+ * every chunk-start state, every chunk-end state gradient and a 64 x dv block), plus
+ * for segmented walks the forward's chunk records (13 KB per chunk) and per head two
+ * sets of segment maps and three of segment states, and frees it on the stream.
  * T == 0 copies grad_final_state (or zeros) into grad_init_state.
  */
 kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
