@@ -50,7 +50,7 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
   static_assert(DK % RPP == 0 && DK <= NT, "shape");
 
   __shared__ float sq[DK], sk[DK];
-  __shared__ float4 spa[RPP][TPR], spb[RPP][TPR];
+  __shared__ float4 spa[2][RPP][TPR], spb[2][RPP][TPR];  // alternate buckets use alternate halves
   __shared__ float sred[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -91,6 +91,7 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
   const float ab = alpha * beta;
 
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  int half = 0;  // the partial-sum buffers of the next bucket
 
   // One bucket: s holds its state at t-1 (this thread's tile). Applies the transition, writes
   // the result to slot `dest` and adds the bucket's output term with weight lambda^(dest).
@@ -102,17 +103,19 @@ __global__ __launch_bounds__((ll_threads<DK, DV>())) void loglinear_decode_kerne
       pa.x += s[p].x * kr; pa.y += s[p].y * kr; pa.z += s[p].z * kr; pa.w += s[p].w * kr;
       pb.x += s[p].x * qr; pb.y += s[p].y * qr; pb.z += s[p].z * qr; pb.w += s[p].w * qr;
     }
-    spa[rg][c4] = pa;
-    spb[rg][c4] = pb;
+    spa[half][rg][c4] = pa;
+    spb[half][rg][c4] = pb;
     lds_barrier();
     float4 A = make_float4(0.f, 0.f, 0.f, 0.f), Bq = A;
 #pragma unroll
     for (int g = 0; g < RPP; ++g) {
-      const float4 x = spa[g][c4], y = spb[g][c4];
+      const float4 x = spa[half][g][c4], y = spb[half][g][c4];
       A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
       Bq.x += y.x; Bq.y += y.y; Bq.z += y.z; Bq.w += y.w;
     }
-    lds_barrier();  // spa/spb are reused by the next bucket
+    // the next bucket writes the other half; the one after it writes this half again only
+    // after the next bucket's barrier, which every thread reaches after these reads
+    half ^= 1;
     const float lw_d = lw[dest];
     const float bq = beta * dkq;
     o.x += lw_d * alpha * (Bq.x - bq * A.x); o.y += lw_d * alpha * (Bq.y - bq * A.y);
