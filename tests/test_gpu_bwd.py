@@ -108,16 +108,16 @@ def test_bwd_psd_shape_full_size_prefix_gradient():
     log("worst max|err|/RMS: " + ", ".join(f"{n} {e:.2e}" for n, e in worst.items()))
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
-def test_bwd_segmented_walks(dk, dv):
+@pytest.mark.parametrize("dk,dv,ends", [(128, 128, True), (64, 128, True), (128, 64, False)])
+def test_bwd_segmented_walks(dk, dv, ends):
     """Two heads over 25 chunks (ragged tail): the planner segments this shape (few heads, long
     enough), so both walks run in segments from the forward scan's start states and the folded
-    end gradients; every token and head against the oracle, with a start state and an end-state
-    gradient."""
-    log(f"case: bwd segmented walks dk={dk} dv={dv} B=1 H=2 T=1553")
+    end gradients; every token and head against the oracle, with or without a start state and
+    an end-state gradient."""
+    log(f"case: bwd segmented walks dk={dk} dv={dv} B=1 H=2 T=1553 ends={ends}")
     wl = W.make_prefill("tiny_f32", seed=11, B=1, T=64 * 24 + 17, H=2, dk=dk, dv=dv, dtype="bf16", init_std=0.3)
     assert kla.plan(1, wl.T, 2, dk, dv)[0] == "scan"
-    _run(wl)
+    _run(wl, with_init=ends, with_dfin=ends)
 
 
 def test_bwd_long_context_prefix_gradient():
