@@ -1,8 +1,9 @@
-"""Decode steps captured in a HIP graph (through torch.cuda.graph) replay exactly what the
-eager calls compute. Decode allocates nothing, so a serving loop can capture a run of steps
-and replay it without per-launch host overhead. Each replay starts from a state reset by an
-eager copy, and every replay is checked against the eager results, bit for bit (same kernel,
-same inputs)."""
+"""Decode steps, and the allocation-free prefill, captured in a HIP graph (through
+torch.cuda.graph) replay exactly what the eager calls compute. Decode and
+kla_chunk_fwd_noalloc allocate nothing, so a serving loop can capture a run of calls and
+replay it without per-launch host overhead. Each replay starts from a state reset by an
+eager copy (or outputs overwritten eagerly), and every replay is checked against the eager
+results, bit for bit (same kernels, same inputs)."""
 import numpy as np
 import pytest
 
@@ -85,3 +86,40 @@ def test_loglinear_decode_graph_replays_match_eager():
         for s in range(n):
             assert torch.equal(outs[s], eager[s]), f"replay {rep}, step {s}"
         assert torch.equal(S_g, S_e), f"replay {rep}: buckets"
+
+
+@pytest.mark.parametrize("path,segments", [("sequential", 0), ("scan", 3)])
+def test_noalloc_prefill_graph_replays_match_eager(path, segments):
+    """The allocation-free prefill (kla_chunk_fwd_noalloc: its workspace is the library's static
+    device scratch) captured in a HIP graph on both inter-chunk paths: every replay, with eager
+    work on the outputs between replays, matches the eager call bit for bit."""
+    from tests.gpu_common import upload_prefill
+    wl = W.make_prefill("tiny_f32", seed=12, B=2, T=64 * 6 + 9, H=3, dk=128, dv=128, dtype="bf16", init_std=0.2)
+    q, k, v, la, eta, s0 = upload_prefill(wl)
+    shp_o, shp_s = (wl.B, wl.T, wl.H, wl.dv), (wl.B, wl.H, wl.dk, wl.dv)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out_e, fin_e = torch.empty(shp_o, **f32), torch.empty(shp_s, **f32)
+    kla.chunk_fwd_noalloc(q, k, v, la, eta, wl.eps, init_state=s0, path=path, segments=segments, out=out_e,
+                          final_state=fin_e)
+    torch.cuda.synchronize()
+
+    out_g, fin_g = torch.empty(shp_o, **f32), torch.empty(shp_s, **f32)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture
+        kla.chunk_fwd_noalloc(q, k, v, la, eta, wl.eps, init_state=s0, path=path, segments=segments, out=out_g,
+                              final_state=fin_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kla.chunk_fwd_noalloc(q, k, v, la, eta, wl.eps, init_state=s0, path=path, segments=segments, out=out_g,
+                              final_state=fin_g)
+    for rep in range(3):
+        out_g.fill_(float("nan"))
+        fin_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {rep}: outputs"
+        assert torch.equal(fin_g, fin_e), f"replay {rep}: end state"
