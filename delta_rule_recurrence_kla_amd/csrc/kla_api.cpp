@@ -500,34 +500,31 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
   d.full_rec = 1;
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   const size_t bh = static_cast<size_t>(B) * H;
-  // bf16 with dk <= 128: every kernel reads compact records (T' and the gates; the intra-chunk
-  // kernel and the right walks form P themselves), from one prep pass; otherwise full records
-  const bool compact = kla::state_dma_supported(mode, dk);
-  const size_t rec_bytes = compact ? 0 : align256(bh * nc * kla::full_record_bytes());
-  // scales l >= 7: half-blocks of 2^(l-7) chunks while a right half-block exists; every scale's
-  // left end states are kept at once (at most nc states per head over all scales)
+  // scales s >= 0 (level 7 + s): half-blocks of 2^s chunks while a right half-block exists
   int nscale = 0, half[32], nleft[32], nright[32];
-  long long ends_off[32];
-  long long ends_floats = 0;
   for (int hb = 1; hb < nc && nscale < 32; hb *= 2, ++nscale) {
     const int nblk = (nc + hb - 1) / hb;
     half[nscale] = hb;
     nleft[nscale] = (nblk + 1) / 2;
     nright[nscale] = nblk / 2;
-    ends_off[nscale] = ends_floats;
-    ends_floats += static_cast<long long>(bh) * nleft[nscale] * dk * dv;
   }
-  const size_t ends_bytes = align256(static_cast<size_t>(ends_floats) * 4);
-  const size_t crec_bytes = compact ? align256(bh * nc * static_cast<size_t>(kla::record_bytes(mode, dk))) : 0;
-  void* ws = nullptr;
-  st = workspace_alloc(&ws, rec_bytes + ends_bytes + crec_bytes, stream);
-  if (st != KLA_OK) return st;
-  hipError_t e = hipSuccess;
-  uint8_t* rec = compact ? nullptr : static_cast<uint8_t*>(ws);
-  float* ends = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + rec_bytes);
-  uint8_t* crec = compact ? static_cast<uint8_t*>(ws) + rec_bytes + ends_bytes : nullptr;
   const int direct = beta_mode == KLA_BETA_DIRECT;
-  if (compact) {
+  void* ws = nullptr;
+  hipError_t e = hipSuccess;
+  if (kla::state_dma_supported(mode, dk)) {
+    // bf16 with dk <= 128: one prep pass of compact records (T' and the gates; the intra-chunk
+    // kernel and the walks form P themselves); then per scale one walk over its right
+    // half-blocks that starts from the end states of the scale below, held in two buffers
+    // used in turn
+    const size_t crec_bytes = align256(bh * nc * static_cast<size_t>(kla::record_bytes(mode, dk)));
+    size_t carry = 0;
+    for (int i = 1; i < nscale; ++i) carry = std::max(carry, bh * nright[i] * static_cast<size_t>(dk) * dv);
+    const size_t carry_bytes = align256(carry * 4);
+    st = workspace_alloc(&ws, crec_bytes + 2 * carry_bytes, stream);
+    if (st != KLA_OK) return st;
+    uint8_t* crec = static_cast<uint8_t*>(ws);
+    float* carried[2] = {reinterpret_cast<float*>(crec + crec_bytes),
+                         reinterpret_cast<float*>(crec + crec_bytes + carry_bytes)};
     kla::Dims dc = d;
     dc.full_rec = 0;
     e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, dc, q, k, log_alpha, eta, eps, direct, crec, stream); });
@@ -535,22 +532,42 @@ kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const voi
       e = timed("kla_loglinear_intra", stream, [&] {
         return kla::launch_loglinear_intra_compact(d, q, k, crec, v, lam, levels, out, stream);
       });
+    for (int i = 0; e == hipSuccess && i < nscale; ++i) {
+      e = timed("kla_loglinear_scale", stream, [&] {
+        return kla::launch_loglinear_scale_dma(dk, q, k, v, crec, T, H, dv, nc, static_cast<int>(bh), i, nright[i],
+                                               i > 0 ? carried[(i - 1) & 1] : nullptr,
+                                               i + 1 < nscale ? carried[i & 1] : nullptr,
+                                               i + 1 < nscale ? nright[i + 1] : 0, lam, levels, out, stream);
+      });
+    }
   } else {
+    // full records; every scale's left end states kept at once (at most nc states per head)
+    const size_t rec_bytes = align256(bh * nc * kla::full_record_bytes());
+    long long ends_off[32];
+    long long ends_floats = 0;
+    for (int i = 0; i < nscale; ++i) {
+      ends_off[i] = ends_floats;
+      ends_floats += static_cast<long long>(bh) * nleft[i] * dk * dv;
+    }
+    st = workspace_alloc(&ws, rec_bytes + align256(static_cast<size_t>(ends_floats) * 4), stream);
+    if (st != KLA_OK) return st;
+    uint8_t* rec = static_cast<uint8_t*>(ws);
+    float* ends = reinterpret_cast<float*>(rec + rec_bytes);
     e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
     if (e == hipSuccess)
       e = timed("kla_loglinear_intra", stream, [&] { return kla::launch_loglinear_intra(mode, d, rec, v, lam, levels, out, stream); });
-  }
-  // every scale's left walks in one grid (they are independent), then the right walks scale by
-  // scale (the scales add to the same outputs)
-  if (e == hipSuccess && nscale > 0)
-    e = timed("kla_loglinear_left", stream, [&] {
-      return kla::launch_loglinear_left(mode, d, k, v, rec, crec, nscale, half, nleft, ends_off, ends, stream);
-    });
-  for (int i = 0; e == hipSuccess && i < nscale; ++i) {
-    e = timed("kla_loglinear_right", stream, [&] {
-      return kla::launch_loglinear_right(mode, d, q, k, rec, crec, half[i], nright[i], ends + ends_off[i], nleft[i], lam,
-                                         levels, 7 + i, out, stream);
-    });
+    // every scale's left walks in one grid (they are independent), then the right walks scale by
+    // scale (the scales add to the same outputs)
+    if (e == hipSuccess && nscale > 0)
+      e = timed("kla_loglinear_left", stream, [&] {
+        return kla::launch_loglinear_left(mode, d, k, v, rec, nscale, half, nleft, ends_off, ends, stream);
+      });
+    for (int i = 0; e == hipSuccess && i < nscale; ++i) {
+      e = timed("kla_loglinear_right", stream, [&] {
+        return kla::launch_loglinear_right(mode, d, q, k, rec, half[i], nright[i], ends + ends_off[i], nleft[i], lam,
+                                           levels, 7 + i, out, stream);
+      });
+    }
   }
   hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

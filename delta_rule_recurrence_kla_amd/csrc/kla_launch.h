@@ -71,13 +71,20 @@ bool state_dma_supported(int mode, int dk);
 // state kernel consumes it, else the full record.
 int record_bytes(int mode, int dk);
 int full_record_bytes();  // T' and P in full, for the kernels that read both
-// With lam non-null the walk adds lam-weighted outputs to out (values read as zeros when v is
-// null); segment s walks chunks [(s * seg_mul + seg_add) * seg_chunks, + seg_chunks).
+// Segment s walks chunks [(s * seg_mul + seg_add) * seg_chunks, + seg_chunks).
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
-                            int ncg, int nseg, hipStream_t stream, int seg_mul = 1, int seg_add = 0,
-                            const float* lam = nullptr, int lam_L = 0, int lam_level = 0);
+                            int ncg, int nseg, hipStream_t stream, int seg_mul = 1, int seg_add = 0);
+// Log-linear prefill on compact records (bf16, dk in {64, 128}, DV a multiple of 64): the walk of
+// chunk scale s (level 7 + s of L) over its nright right half-blocks of 2^s chunks per head, each
+// from the state [B*H][nright][dk][DV] in init (written by scale s - 1; scale 0 starts every
+// pair of chunks from zero and takes null), adding its weighted outputs to out, and leaving the
+// end states of its even half-blocks in fin ([B*H][fin_segs][dk][DV], fin_segs = the next
+// scale's nright; null for the last scale). See state_walk_kernel.
+hipError_t launch_loglinear_scale_dma(int dk, const void* q, const void* k, const void* v, const uint8_t* rec, int T,
+                                      int H, int DV, int nc, int BH, int s, int nright, const float* init, float* fin,
+                                      int fin_segs, const float* lam, int L, float* out, hipStream_t stream);
 
 // Log-linear decode: one token at position t for N x H heads, each with L bucket states
 // [L, dk, dv] (only the occupied levels are read or written).
@@ -86,33 +93,26 @@ hipError_t launch_loglinear_decode(int mode, int N, int H, int dk, int dv, const
                                    float eps, int direct, float* states, float* out, int L, int t,
                                    hipStream_t stream);
 
-// Log-linear prefill (full records). Intra-chunk levels 0..6 written to out; the zero-start end
-// state of every left half-block of every scale l >= 7 (half-blocks of 2^(l-7) chunks) into
-// ends, per scale [B*H][nleft][dk][dv]; then per scale the walk over every right half-block from
-// its left sibling's end state with no values, lambda^(l)-weighted outputs added to out.
+// Log-linear prefill (full records; fp32, or dk = 256). Intra-chunk levels 0..6 written to out;
+// the zero-start end state of every left half-block of every scale l >= 7 (half-blocks of
+// 2^(l-7) chunks) into ends, per scale [B*H][nleft][dk][dv]; then per scale the walk over every
+// right half-block from its left sibling's end state with no values, lambda^(l)-weighted outputs
+// added to out.
 hipError_t launch_loglinear_intra(int mode, const Dims& d, const uint8_t* rec, const void* v, const float* lam,
                                   int L, float* out, hipStream_t stream);
-// The same from compact records (bf16, dk <= 128), forming P from q and k.
+// The intra-chunk levels from compact records (bf16, dk <= 128), forming P from q and k, for the
+// scale walks of launch_loglinear_scale_dma: on chunk c >= 1 every pair's weight lambda^(l) is
+// taken less lambda^(7 + lowest set bit of c).
 hipError_t launch_loglinear_intra_compact(const Dims& d, const void* q, const void* k, const uint8_t* crec,
                                           const void* v, const float* lam, int L, float* out, hipStream_t stream);
 // All scales' left walks in one grid: scale i has half-blocks of half[i] chunks, nleft[i] left
 // ones per head, and writes their end states at ends + ends_off[i] (floats).
-// rec_compact: compact records of the same chunks (bf16, dk <= 128): the left walks of every
-// scale then run in one grid of the DMA-fed map walk; null takes one grid of register-prefetch
-// walks on the full records.
-// The DMA-fed map walk over the left half-blocks of every scale (plain state from zero, end
-// states into ends + ends_off[i]), one grid; bf16, dk in {64, 128}, DV a multiple of 64.
-hipError_t launch_left_walks_dma(int dk, const void* k, const void* v, const uint8_t* rec, int T, int H, int DV,
-                                 int nc, int BH, int nscale, const int* half, const int* nleft,
-                                 const long long* ends_off, float* ends, hipStream_t stream);
 hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
-                                 const uint8_t* rec_compact, int nscale, const int* half, const int* nleft,
-                                 const long long* ends_off, float* ends, hipStream_t stream);
-// rec_compact: compact records of the same chunks (bf16, dk <= 128), for the DMA-fed walk; null
-// takes the register-prefetch walk on the full records.
-hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec,
-                                  const uint8_t* rec_compact, int half, int nright, const float* ends, int nleft,
-                                  const float* lam, int L, int level, float* out, hipStream_t stream);
+                                 int nscale, const int* half, const int* nleft, const long long* ends_off,
+                                 float* ends, hipStream_t stream);
+hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec, int half,
+                                  int nright, const float* ends, int nleft, const float* lam, int L, int level,
+                                  float* out, hipStream_t stream);
 
 // Device address and size of the static scratch buffer of kla_chunk_fwd_noalloc on the
 // current device (kla_scratch.hip); the address is looked up once per device.

@@ -450,7 +450,10 @@ __global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_mfma_kernel(con
 // The same on the compact record (T' without its zero quadrant, and the gates), which the walks
 // read anyway, so that no full record is prepared: P = tril(e^{g_t - g_r} Q K^T) is formed here
 // from the chunk's query and key rows on the bf16 MFMA (exact products), on its lower 16 x 16
-// tiles, and staged in LDS in fp32 for the P T' product.
+// tiles, and staged in LDS in fp32 for the P T' product. It serves the scale walks of
+// state_walk_kernel (kla_state_dma.hip), whose outputs on chunk c >= 1 carry the chunk-local term
+// P T' V with the total weight lambda^(7 + lowest set bit of c): that weight is taken off every
+// pair here.
 template <int DK, int DV>
 __global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_compact_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint8_t* __restrict__ crec,
@@ -583,7 +586,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_compact_kernel(
       float wgt = 0.f;
       if (s <= t && t0 + t < T) {
         const int lev = s == t ? 0 : 32 - __clz(static_cast<unsigned>(t ^ s));
-        wgt = acc[e] * lam[(row0 + static_cast<size_t>(t) * H) * L + lev];
+        const float* lp = lam + (row0 + static_cast<size_t>(t) * H) * L;
+        wgt = acc[e] * (c > 0 ? lp[lev] - lp[7 + __builtin_ctz(static_cast<unsigned>(c))] : lp[lev]);
       }
       sW[t][s] = wgt;
     }

@@ -614,13 +614,10 @@ static hipError_t dispatch_scale(int mode, int dk, int nwg, const StateArgs& a, 
 }
 
 hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
-                                 const uint8_t* rec_compact, int nscale, const int* half, const int* nleft,
-                                 const long long* ends_off, float* ends, hipStream_t stream) {
+                                 int nscale, const int* half, const int* nleft, const long long* ends_off,
+                                 float* ends, hipStream_t stream) {
   if (nscale < 1 || nscale > kMaxScales) return hipErrorInvalidValue;
   const int ncg = d.dv / NCOLS_STATE;
-  if (rec_compact && !d.lift && state_dma_supported(mode, d.dk))
-    return launch_left_walks_dma(d.dk, k, v, rec_compact, d.T, d.H, d.dv, d.nc, d.B * d.H, nscale, half, nleft,
-                                 ends_off, ends, stream);
   StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, half[0], nullptr, 1, nullptr, ends, d.dv, nleft[0], 0, ncg,
               nleft[0]};
   a.seg_mul = 2;
@@ -638,14 +635,10 @@ hipError_t launch_loglinear_left(int mode, const Dims& d, const void* k, const v
   return dispatch_scale<false, false>(mode, d.dk, nwg, a, stream);
 }
 
-hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec,
-                                  const uint8_t* rec_compact, int half, int nright, const float* ends, int nleft,
-                                  const float* lam, int L, int level, float* out, hipStream_t stream) {
+hipError_t launch_loglinear_right(int mode, const Dims& d, const void* q, const void* k, const uint8_t* rec, int half,
+                                  int nright, const float* ends, int nleft, const float* lam, int L, int level,
+                                  float* out, hipStream_t stream) {
   const int ncg = d.dv / NCOLS_STATE;
-  if (rec_compact && !d.lift && state_dma_supported(mode, d.dk))
-    return launch_state_dma(true, false, d.dk, ncg * nright * d.B * d.H, q, k, nullptr, rec_compact, d.T, d.H, d.dv,
-                            d.nc, half, ends, nleft, out, nullptr, d.dv, 1, 0, ncg, nright, stream, 2, 1, lam, L,
-                            level);
   StateArgs a{q, k, nullptr, rec, d.T, d.H, d.dv, d.nc, half, ends, nleft, out, nullptr, d.dv, 1, 0, ncg, nright};
   a.seg_mul = 2;
   a.seg_add = 1;

@@ -6,12 +6,11 @@
 // with one workgroup per (b, h, 64 state columns), 16 columns per wave, and the state held in
 // MFMA accumulator registers for the whole walk over the chunks. Two kernels:
 //  * state_map_kernel walks a segment without outputs and leaves its end state: on the
-//    augmented state [I | 0] that is the segment's affine map [M | N] (the scan's first phase);
-//    on the plain state from zero, the state of the segment's own tokens (the left half-blocks
-//    of log-linear KLA). One compute wave per 16 columns and a copy wave;
-//  * state_walk_kernel walks with outputs (the sequential path, and the scan's walk from
-//    every segment's start): per 16 columns one wave runs the recurrence and another the
-//    output products, with a copy wave (see the comment above it).
+//    augmented state [I | 0] that is the segment's affine map [M | N] (the scan's first phase).
+//    One compute wave per 16 columns and a copy wave;
+//  * state_walk_kernel walks with outputs (the sequential path, the scan's walk from every
+//    segment's start, and the scales of log-linear KLA): per 16 columns one wave runs the
+//    recurrence and another the output products, with a copy wave (see the comment above it).
 //
 // What both share is how a chunk's operands reach LDS and registers:
 //  * every input of chunk c+1 (rows of K, Q, V and the chunk record) is copied into LDS by
@@ -36,6 +35,8 @@
 //    An accumulator pair (tiles 2a, 2a + 1) then gives each lane eight consecutive
 //    indices 32a + 8(lane >> 4) + 0..7 as the contraction slots of the next product, so
 //    every row-major operand fragment is one contiguous 16-byte LDS read.
+#include <algorithm>
+
 #include "kla_device.h"
 #include "kla_launch.h"
 
@@ -45,8 +46,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-
-constexpr int kDmaMaxScales = 24;  // scales of 1, 2, 4, ... chunks: enough for any int T
 
 struct StateDmaArgs {
   const void* q;
@@ -68,19 +67,12 @@ struct StateDmaArgs {
   // (1, 0), or every other one (2, 1) for the right half-blocks of a log-linear scale.
   int seg_mul;
   int seg_add;
-  // ACC walks (values read as zeros when v is null): out[b, t, h, :] += lam[((b * T + t) * H + h)
-  // * lam_L + lam_level] * o_t instead of out = o_t.
+  // Log-linear scale walks only (see state_walk_kernel): weights lam [B, T, H, lam_L] of level
+  // lam_level, and wg_segs consecutive segments per workgroup.
   const float* lam;
   int lam_L;
   int lam_level;
-  // Several scales in one grid (map walks only, nscale > 0): workgroups [scale_wg[i],
-  // scale_wg[i + 1]) walk segments of scale_half[i] chunks, scale_nseg[i] per (b, h), and leave
-  // their end states at fin + scale_fin_off[i] (scale_nseg[i] per (b, h)).
-  int nscale;
-  int scale_wg[kDmaMaxScales + 1];
-  int scale_half[kDmaMaxScales];
-  int scale_nseg[kDmaMaxScales];
-  long long scale_fin_off[kDmaMaxScales];
+  int wg_segs;
 };
 
 namespace {
@@ -92,6 +84,11 @@ __device__ __forceinline__ int tok(int m, int r) {
 
 __device__ __forceinline__ void dma16(rsrc_t r, uint8_t* lds_dst, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+}
+
+// 4 bytes per lane; lane i's dword lands at lds_dst + 4 i
+__device__ __forceinline__ void dma4(rsrc_t r, void* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 4, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ void decode_wg_dma(int L, int ncg, int nunits, int& cg, int& unit) {
@@ -134,19 +131,10 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index as a scalar
   const int gq = lane >> 4, ln = lane & 15;
-  int wg = blockIdx.x, nwg = gridDim.x, seg_chunks = a.seg_chunks, nseg = a.nseg, fin_segs = a.fin_segs;
+  const int seg_chunks = a.seg_chunks, nseg = a.nseg, fin_segs = a.fin_segs;
   float* fin = a.fin;
-  if (a.nscale > 0) {
-    int sc = 0;
-    while (sc + 1 < a.nscale && wg >= a.scale_wg[sc + 1]) ++sc;
-    wg -= a.scale_wg[sc];
-    nwg = a.scale_wg[sc + 1] - a.scale_wg[sc];
-    seg_chunks = a.scale_half[sc];
-    nseg = fin_segs = a.scale_nseg[sc];
-    fin = a.fin + a.scale_fin_off[sc];
-  }
   int cg, unit;
-  decode_wg_dma(wg, a.ncg, nwg / a.ncg, cg, unit);
+  decode_wg_dma(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
   const int bh = unit / nseg, seg = unit - bh * nseg;
   const int H = a.H, T = a.T, DV = a.DV;
   const int b = bh / H, h = bh - b * H;
@@ -342,7 +330,8 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// The walk with outputs (sequential path, and the scan's walk from each segment's start).
+// The walk with outputs (sequential path, the scan's walk from each segment's start, and the
+// scales of log-linear KLA).
 //
 // Per 16-column slice of the workgroup's 64 state columns the chunk's work splits into the
 // recurrence chain, which carries the state from chunk to chunk,
@@ -365,11 +354,34 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
 // single-wave walk, in the same order, so the results are the same bit for bit; split this way
 // the walk takes about 3% less time on the LM-layer shape (the chain's latency dominates).
 // LDS: 2 x 45,824 B (K, Q, record) + 8 KB (V) + 12 KB (P) + 16 KB (U split) + 32 KB (S split)
-// = 161,280 B, so the record's last copy is cut to its 768 remaining bytes.
+// = 161,280 B, so the record's last copy is cut to its 768 remaining bytes (the log-linear walks
+// add 1 KB of output weights).
+//
+// LL: one chunk scale s of log-linear KLA (Log-Linear page, "Mathematical formalization": the
+// Fenwick buckets; level l = 7 + s holds, seen from a token of chunk c whose bit s is set, the
+// 2^s chunks below c's bit s). Let C_l(t) be the KLA output of token t from the tokens whose
+// level seen from t is at most l. For l = 7 + s these are the tokens from the start of the
+// aligned block of 2^(s+1) chunks that holds t, so C_l is the output of a KLA walk restarted
+// from zero at every multiple of 2^(s+1) chunks. Then
+//   o_t = sum_l lambda^(l) (C_l - C_{l-1}) = sum_l (lambda^(l) - lambda^(l+1)) C_l,
+// and on a chunk whose bit s is clear C_{7+s} = C_{6+s}. So the scale's walk covers only its
+// right half-blocks (bit s set), one segment each; a segment starts from the state that the
+// walk of scale s - 1 leaves at the end of the left sibling (its own right half-block of even
+// index), and its outputs are added to out with the weight lambda^(7+s) - lambda^(7+s'), s' the
+// next set bit of the chunk index above s (lambda^(7+s) alone if there is none). Each segment
+// of even index leaves its end state for scale s + 1. Scale 0 walks each pair of chunks from
+// zero, the left chunk without outputs (lead = 1). The chunk-local term P T' V that every C_l
+// carries sums over a chunk's scales to lambda^(7 + lowest set bit of c) P T' V, which the
+// intra-chunk kernel takes off its pairs. A workgroup walks wg_segs consecutive segments one
+// after another, so the copies run on across segment boundaries.
 constexpr int WALK_THREADS = 576;  // four recurrence waves, four output waves, one copy wave
+// the walk's kinds: with outputs, a log-linear scale s >= 1, log-linear scale 0 (lead chunks)
+constexpr int WALK_PLAIN = 0, WALK_LL = 1, WALK_LL_PAIRS = 2;
 
-template <int DK, bool ACC>
+template <int DK, int WK>
 __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a) {
+  constexpr bool LL = WK != WALK_PLAIN;
+  constexpr bool PAIRS = WK == WALK_LL_PAIRS;
   using TR = Tr<MODE_BF16>;
   constexpr int NCOLS = 64;
   constexpr int KRB = DK * 2;
@@ -391,6 +403,8 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
   __shared__ __align__(256) uint8_t ldsP[CREC_EG_OFF];
   __shared__ __align__(16) u32x4 ldsUb[4][2][2][64];         // [slice][kb][hi, lo][lane]: U split, 8 KB
   __shared__ __align__(16) u32x4 ldsSb[4][DK / 32][2][64];   // [slice][kb][hi, lo][lane]: S split, 32 KB
+  // LL: the chunk's two output weights per token, [buffer][lambda^(7+s), lambda^(7+s')][token], 1 KB
+  __shared__ __align__(256) float ldsL[LL ? 2 : 1][2][LL ? CHUNK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -398,13 +412,26 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
   const int gq = lane >> 4, ln = lane & 15;
   int cg, unit;
   decode_wg_dma(blockIdx.x, a.ncg, static_cast<int>(gridDim.x) / a.ncg, cg, unit);
-  const int bh = unit / a.nseg, seg = unit - bh * a.nseg;
+  // segments [i0, i1) of this workgroup: one, except for the log-linear scales
+  const int ngrp = LL ? (a.nseg + a.wg_segs - 1) / a.wg_segs : a.nseg;
+  const int bh = unit / ngrp, grp = unit - bh * ngrp;
+  const int i0 = LL ? grp * a.wg_segs : grp;
+  const int i1 = LL ? min(a.nseg, i0 + a.wg_segs) : grp + 1;
+  const int seg = i0;
   const int H = a.H, T = a.T, DV = a.DV;
   const int b = bh / H, h = bh - b * H;
   const int col0 = cg * NCOLS;
   const int col = col0 + 16 * sl + ln;
   const int c_begin = (seg * a.seg_mul + a.seg_add) * a.seg_chunks;
   const int c_end = min(a.nc, c_begin + a.seg_chunks);
+  // LL: segment i covers chunks [seg_start(i), seg_end(i)), its first `lead` chunks without outputs
+  const int lead = PAIRS ? 1 : 0;
+  auto seg_begin = [&](int i) { return (i * a.seg_mul + a.seg_add) * a.seg_chunks; };
+  auto seg_start = [&](int i) { return seg_begin(i) - lead; };
+  auto seg_end = [&](int i) { return min(a.nc, seg_begin(i) + a.seg_chunks); };
+  int nchunks = 0;
+  if constexpr (LL)
+    for (int i = i0; i < i1; ++i) nchunks += seg_end(i) - seg_start(i);
   const int rowK = H * DK * 2, rowV = H * DV * 2, rowO = H * DV * 4;
   const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
   const uint8_t* qb_ = static_cast<const uint8_t*>(a.q) + static_cast<size_t>(b) * T * rowK;
@@ -432,25 +459,55 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
     };
     auto copy_v = [&](int c) __attribute__((always_inline)) {
       const int t0 = c * CHUNK;
-      // without values (v null) the copies read through an empty range and land as zeros
-      const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV,
-                                     a.v ? static_cast<long long>(T - t0) * rowV : 0);
+      const rsrc_t rv = make_rsrc_wu(vb_ + static_cast<size_t>(t0) * rowV, static_cast<long long>(T - t0) * rowV);
 #pragma unroll
       for (int blk = 0; blk < VBYTES / 1024; ++blk) {
         const int row = blk * VRPB + lane / VPR;
         dma16(rv, ldsV + 1024 * blk, row * rowV + (h * DV + col0) * 2 + 16 * ((lane % VPR) ^ swz<VRB>(row)));
       }
     };
-    if (c_begin < c_end) {
-      copy_kqr(c_begin, lds0);
-      copy_v(c_begin);
-    }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int c = c_begin; c < c_end; ++c) {
-      if (c + 1 < c_end) copy_kqr(c + 1, ((c + 1 - c_begin) & 1) ? lds1 : lds0);
-      asm volatile("s_barrier" ::: "memory");  // past it, this chunk's V rows have been read
-      if (c + 1 < c_end) copy_v(c + 1);
+    if constexpr (LL) {
+      // chunk c's weights lambda^(7+s) and lambda^(7+s') (see out_chunk) of its 64 tokens into
+      // weight buffer `par`, one dword per lane (zero past T)
+      auto copy_lam = [&](int c, int par) __attribute__((always_inline)) {
+        const int t0 = c * CHUNK, HL = H * a.lam_L;
+        const int s = __builtin_ctz(static_cast<unsigned>(a.seg_chunks));
+        const unsigned above = static_cast<unsigned>(c) >> (s + 1);
+        const int lev2 = above ? a.lam_level + 1 + __builtin_ctz(above) : a.lam_level;
+        const rsrc_t rl = make_rsrc_wu(a.lam + ((static_cast<size_t>(b) * T + t0) * H + h) * a.lam_L,
+                                       (static_cast<long long>(T - t0 - 1) * HL + a.lam_L) * 4);
+        dma4(rl, &ldsL[par][0][0], (lane * HL + a.lam_level) * 4);
+        dma4(rl, &ldsL[par][1][0], (lane * HL + lev2) * 4);
+      };
+      int i = i0, c = seg_start(i0);  // the next chunk to copy
+      if (nchunks > 0) {
+        copy_kqr(c, lds0);
+        copy_lam(c, 0);
+        copy_v(c);
+      }
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      for (int j = 0; j < nchunks; ++j) {
+        if (++c >= seg_end(i)) c = seg_start(++i);
+        if (j + 1 < nchunks) {
+          copy_kqr(c, ((j + 1) & 1) ? lds1 : lds0);
+          copy_lam(c, (j + 1) & 1);
+        }
+        asm volatile("s_barrier" ::: "memory");  // past it, this chunk's V rows have been read
+        if (j + 1 < nchunks) copy_v(c);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    } else {
+      if (c_begin < c_end) {
+        copy_kqr(c_begin, lds0);
+        copy_v(c_begin);
+      }
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      for (int c = c_begin; c < c_end; ++c) {
+        if (c + 1 < c_end) copy_kqr(c + 1, ((c + 1 - c_begin) & 1) ? lds1 : lds0);
+        asm volatile("s_barrier" ::: "memory");  // past it, this chunk's V rows have been read
+        if (c + 1 < c_end) copy_v(c + 1);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
     }
     return;
   }
@@ -493,14 +550,22 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
 
   if (wu < 4) {  // recurrence wave
     f32x4 S[DK / 16];
+    // the start state of segment i (zero without init)
+    // (row tok(mt, 4 gq + e) = 8 gq + 32 (mt >> 1) + 4 (mt & 1) + e: a lane base plus a uniform offset)
+    auto load_init = [&](int i) __attribute__((always_inline)) {
+      if (a.init) {
+        const float* ip = a.init + (static_cast<size_t>(bh) * a.init_segs + i) * DK * DV + 8 * gq * DV + col;
 #pragma unroll
-    for (int mt = 0; mt < DK / 16; ++mt) {
+        for (int mt = 0; mt < DK / 16; ++mt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = tok(mt, 4 * gq + i);
-        S[mt][i] = a.init ? a.init[(static_cast<size_t>(bh) * a.init_segs + seg) * DK * DV + r * DV + col] : 0.f;
+          for (int e = 0; e < 4; ++e) S[mt][e] = ip[(32 * (mt >> 1) + 4 * (mt & 1) + e) * DV];
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < DK / 16; ++mt) S[mt] = zero4();
       }
-    }
+    };
+    load_init(seg);
     // S split hi/lo: kept in registers for this wave's next chunk and handed to the output wave
     S8 Sb[DK / 32];
     auto split_and_publish = [&]() __attribute__((always_inline)) {
@@ -511,7 +576,9 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
         ldsSb[sl][kb][1][lane] = __builtin_bit_cast(u32x4, Sb[kb].l);
       }
     };
-    auto rec_chunk = [&](const uint8_t* B) __attribute__((always_inline)) {
+    // one chunk from buffer B; `zero`: S is zero (a lead chunk), `last`: the end of segment i,
+    // `lead_next`: the next chunk is a lead chunk (S restarts from zero, and its split is not read)
+    auto rec_chunk = [&](const uint8_t* B, bool zero, bool last, int i, bool lead_next) __attribute__((always_inline)) {
       const uint8_t* sK = B + K_OFF;
       const uint8_t* sV = ldsV;
       const uint8_t* sR = B + R_OFF;
@@ -521,8 +588,10 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         f32x4 acc = zero4();
+        if (!zero) {
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, fragK(sK, mt, kb), Sb[kb]);
+          for (int kb = 0; kb < DK / 32; ++kb) acc = TR::mma_xd(acc, fragK(sK, mt, kb), Sb[kb]);
+        }
         const f32x4 eg = *reinterpret_cast<const f32x4*>(sEG + tok(mt, 4 * gq));
         const u32x2 x = trV(sV, mt);
         f32x4 vv;
@@ -565,21 +634,60 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], fragKT(sK, mt, kb), Ud[kb]);
       }
-      split_and_publish();
+      if constexpr (LL) {
+        if (last) {  // the segment's end state for the next scale (even segments), then the next start
+          if (a.fin && !(i & 1) && (i >> 1) < a.fin_segs) {
+            float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (i >> 1)) * DK * DV + 8 * gq * DV + col;
+#pragma unroll
+            for (int mt = 0; mt < DK / 16; ++mt) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) F[(32 * (mt >> 1) + 4 * (mt & 1) + e) * DV] = S[mt][e];
+            }
+          }
+          if (lead_next) {
+#pragma unroll
+            for (int mt = 0; mt < DK / 16; ++mt) S[mt] = zero4();
+          } else if (i + 1 < i1) {
+            load_init(i + 1);
+          }
+        }
+      }
+      if (!lead_next) split_and_publish();
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
     split_and_publish();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int c = c_begin; c < c_end; c += 2) {
-      rec_chunk(lds0);
-      if (c + 1 < c_end) rec_chunk(lds1);
-    }
-    if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
-      float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
+    if constexpr (PAIRS) {  // scale 0: every segment is a lead chunk (buffer 0) and an output chunk (buffer 1)
+      for (int i = i0; i < i1; ++i) {
+        rec_chunk(lds0, true, false, i, false);
+        rec_chunk(lds1, false, true, i, true);
+      }
+    } else if constexpr (LL) {
+      {
+        // Segments of 2^s >= 2 chunks: a segment ends on buffer 1, except the last one of the
+        // sequence when it is cut short by its end, whose end state no scale reads
+        int i = i0, c = seg_start(i0);
+        for (int j = 0; j < nchunks; j += 2) {
+          rec_chunk(lds0, false, false, i, false);
+          if (++c >= seg_end(i)) c = seg_start(++i);
+          if (j + 1 < nchunks) {
+            rec_chunk(lds1, false, c + 1 >= seg_end(i), i, false);
+            if (++c >= seg_end(i)) c = seg_start(++i);
+          }
+        }
+      }
+    } else {
+      for (int c = c_begin; c < c_end; c += 2) {
+        rec_chunk(lds0, false, false, seg, false);
+        if (c + 1 < c_end) rec_chunk(lds1, false, false, seg, false);
+      }
+      if (a.fin && (!a.fin_last_only || seg == a.nseg - 1)) {
+        float* F = a.fin + (static_cast<size_t>(bh) * a.fin_segs + (a.fin_last_only ? 0 : seg)) * DK * a.fin_ld;
 #pragma unroll
-      for (int mt = 0; mt < DK / 16; ++mt) {
+        for (int mt = 0; mt < DK / 16; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) F[(tok(mt, 4 * gq) + i) * a.fin_ld + col] = S[mt][i];
+          for (int e = 0; e < 4; ++e) F[(tok(mt, 4 * gq) + e) * a.fin_ld + col] = S[mt][e];
+        }
       }
     }
   } else {  // output wave
@@ -589,22 +697,21 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
       const int obase = (h * DV + col0 + 16 * sl + 4 * gq) * 4;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro, obase + tok(mt, ln) * rowO, 0, 0);
     };
-    auto out_chunk = [&](int c, const uint8_t* B) __attribute__((always_inline)) {
-      // ACC: the outputs already there and the weights of this wave's output rows, loaded first so
-      // that the adds never wait on a memory round trip (a load issued after the stores would also
-      // wait for them: loads and stores retire in order on one counter)
-      u32x4 acc_old[ACC ? 4 : 1];
-      float acc_w[ACC ? 4 : 1];
-      if constexpr (ACC) {
+    auto out_chunk = [&](int c, const uint8_t* B, int par) __attribute__((always_inline)) {
+      // LL: the outputs already there, loaded first so that the adds never wait on a memory round
+      // trip (a load issued after the stores would also wait for them: loads and stores retire in
+      // order on one counter); the weights come from LDS (buffer `par`), combined as
+      // lambda^(7+s) - lambda^(7+s'), s' the next set bit of c above s (none: lambda^(7+s))
+      u32x4 acc_old[LL ? 4 : 1];
+      float keep_b = 0.f;
+      if constexpr (LL) {
         const int t0 = c * CHUNK;
         const rsrc_t ra = make_rsrc_wu(ob_ + static_cast<size_t>(t0) * rowO, static_cast<long long>(T - t0) * rowO);
         const int obase = (h * DV + col0 + 16 * sl + 4 * gq) * 4;
+        const int s = __builtin_ctz(static_cast<unsigned>(a.seg_chunks));
+        keep_b = (static_cast<unsigned>(c) >> (s + 1)) ? 1.f : 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int t = t0 + tok(mt, ln);
-          acc_old[mt] = bload16(ra, obase + tok(mt, ln) * rowO);
-          acc_w[mt] = t < T ? a.lam[((static_cast<size_t>(b) * T + t) * H + h) * a.lam_L + a.lam_level] : 0.f;
-        }
+        for (int mt = 0; mt < 4; ++mt) acc_old[mt] = bload16(ra, obase + tok(mt, ln) * rowO);
       }
       const uint8_t* sK = B + K_OFF;
       const uint8_t* sQ = B + Q_OFF;
@@ -666,6 +773,9 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // LL: nothing below may be hoisted above the barrier; the scheduler would otherwise move
+      // the weights' arithmetic up and with it a wait for the loads of this chunk's weights
+      if constexpr (LL) __builtin_amdgcn_sched_barrier(0);
       S8 Ub[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -678,68 +788,85 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           if (kb == 0 || mt >= 2) acc = TR::mma_dd(acc, Ub[kb], fragR(ldsP, mt, kb));
-        if constexpr (ACC) acc = __builtin_bit_cast(f32x4, acc_old[mt]) + acc_w[mt] * acc;  // rows past T: weight 0
+        if constexpr (LL) {  // rows past T are not stored
+          const int r = tok(mt, ln);
+          const float wt = ldsL[par][0][r] - keep_b * ldsL[par][1][r];
+          acc = __builtin_bit_cast(f32x4, acc_old[mt]) + wt * acc;
+        }
         store_out(c, mt, acc);
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
     asm volatile("s_barrier" ::: "memory");
-    for (int c = c_begin; c < c_end; c += 2) {
-      out_chunk(c, lds0);
-      if (c + 1 < c_end) out_chunk(c + 1, lds1);
+    if constexpr (PAIRS) {  // a lead chunk has no outputs: its two barriers only
+      for (int i = i0; i < i1; ++i) {
+        asm volatile("s_barrier\n\ts_barrier" ::: "memory");
+        out_chunk(seg_begin(i), lds1, 1);
+      }
+    } else if constexpr (LL) {
+      {
+        int i = i0, c = seg_start(i0);
+        for (int j = 0; j < nchunks; j += 2) {
+          out_chunk(c, lds0, 0);
+          if (++c >= seg_end(i)) c = seg_start(++i);
+          if (j + 1 < nchunks) {
+            out_chunk(c, lds1, 1);
+            if (++c >= seg_end(i)) c = seg_start(++i);
+          }
+        }
+      }
+    } else {
+      for (int c = c_begin; c < c_end; c += 2) {
+        out_chunk(c, lds0, 0);
+        if (c + 1 < c_end) out_chunk(c + 1, lds1, 1);
+      }
     }
   }
 }
 
 bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 64 || dk == 128); }
 
-hipError_t launch_left_walks_dma(int dk, const void* k, const void* v, const uint8_t* rec, int T, int H, int DV,
-                                 int nc, int BH, int nscale, const int* half, const int* nleft,
-                                 const long long* ends_off, float* ends, hipStream_t stream) {
-  if (nscale < 1 || nscale > kDmaMaxScales) return hipErrorInvalidValue;
-  const int ncg = DV / 64;
-  StateDmaArgs a{nullptr, k, v, rec, T, H, DV, nc, 0, nullptr, 0, nullptr, ends, DV, 0, 0, ncg, 0, 2, 0,
-                 nullptr, 0, 0};
-  // coarsest scale first: its long walks start at once, and the short walks of the fine
-  // scales fill the chip behind them
-  a.nscale = nscale;
-  int nwg = 0;
-  for (int j = 0; j < nscale; ++j) {
-    const int i = nscale - 1 - j;
-    a.scale_wg[j] = nwg;
-    a.scale_half[j] = half[i];
-    a.scale_nseg[j] = nleft[i];
-    a.scale_fin_off[j] = ends_off[i];
-    nwg += ncg * nleft[i] * BH;
-  }
-  a.scale_wg[nscale] = nwg;
-  if (dk == 64) return launch_kernel(state_map_kernel<64, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
-  if (dk == 128) return launch_kernel(state_map_kernel<128, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
-                            int ncg, int nseg, hipStream_t stream, int seg_mul, int seg_add, const float* lam,
-                            int lam_L, int lam_level) {
+                            int ncg, int nseg, hipStream_t stream, int seg_mul, int seg_add) {
   const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, seg_chunks, init, init_segs, out, fin, fin_ld, fin_segs,
-                       fin_last_only, ncg, nseg, seg_mul, seg_add, lam, lam_L, lam_level};
+                       fin_last_only, ncg, nseg, seg_mul, seg_add, nullptr, 0, 0, 1};
   if (with_out && aug) return hipErrorInvalidValue;  // a walk with outputs carries the plain state
-  const bool acc = lam != nullptr;
-  if (acc && !with_out) return hipErrorInvalidValue;
   if (dk == 64) {
-    if (acc) return launch_kernel(state_walk_kernel<64, true>, dim3(nwg), dim3(WALK_THREADS), stream, a);
-    if (with_out) return launch_kernel(state_walk_kernel<64, false>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    if (with_out) return launch_kernel(state_walk_kernel<64, WALK_PLAIN>, dim3(nwg), dim3(WALK_THREADS), stream, a);
     if (aug) return launch_kernel(state_map_kernel<64, true>, dim3(nwg), dim3(MAP_THREADS), stream, a);
     return launch_kernel(state_map_kernel<64, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
   }
   if (dk == 128) {
-    if (acc) return launch_kernel(state_walk_kernel<128, true>, dim3(nwg), dim3(WALK_THREADS), stream, a);
-    if (with_out) return launch_kernel(state_walk_kernel<128, false>, dim3(nwg), dim3(WALK_THREADS), stream, a);
+    if (with_out) return launch_kernel(state_walk_kernel<128, WALK_PLAIN>, dim3(nwg), dim3(WALK_THREADS), stream, a);
     if (aug) return launch_kernel(state_map_kernel<128, true>, dim3(nwg), dim3(MAP_THREADS), stream, a);
     return launch_kernel(state_map_kernel<128, false>, dim3(nwg), dim3(MAP_THREADS), stream, a);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_loglinear_scale_dma(int dk, const void* q, const void* k, const void* v, const uint8_t* rec, int T,
+                                      int H, int DV, int nc, int BH, int s, int nright, const float* init, float* fin,
+                                      int fin_segs, const float* lam, int L, float* out, hipStream_t stream) {
+  if (nright <= 0) return hipSuccess;
+  if (s < 0 || s > 24 || 7 + s >= L || DV % 64 != 0) return hipErrorInvalidValue;
+  const int ncg = DV / 64;
+  // about one workgroup per compute unit: a (b, h, column group) walks all of its segments when
+  // there are enough of them, else they are shared out in consecutive runs
+  const int units = ncg * BH;
+  const int groups = std::max(1, std::min(nright, (256 + units - 1) / units));
+  const int wg_segs = (nright + groups - 1) / groups;
+  const int ngrp = (nright + wg_segs - 1) / wg_segs;
+  const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, 1 << s, init, nright, out, fin, DV, fin_segs, 0, ncg, nright,
+                       2, 1, lam, L, 7 + s, wg_segs};
+  const dim3 grid(units * ngrp), block(WALK_THREADS);
+  if (dk == 64)
+    return s == 0 ? launch_kernel(state_walk_kernel<64, WALK_LL_PAIRS>, grid, block, stream, a)
+                  : launch_kernel(state_walk_kernel<64, WALK_LL>, grid, block, stream, a);
+  if (dk == 128)
+    return s == 0 ? launch_kernel(state_walk_kernel<128, WALK_LL_PAIRS>, grid, block, stream, a)
+                  : launch_kernel(state_walk_kernel<128, WALK_LL>, grid, block, stream, a);
   return hipErrorInvalidValue;
 }
 

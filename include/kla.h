@@ -287,16 +287,19 @@ kla_status kla_loglinear_decode_step(kla_dtype dtype, kla_beta_mode beta_mode, c
  * Log-Linear page's "Mathematical formalization"): for every token,
  *     o_t = sum over s <= t of lambda_t^(level(t,s)) beta_s (q_t^T A_t ... A_{s+1} k_s) v_s
  * with the buckets and transitions of kla_loglinear_decode_step. Work is O(T log T):
- * the pairs inside a 64-token chunk (levels 0..6) from the chunk's pair matrix P T'; each
- * coarser level l from a walk over every left half-block of 2^(l-7) chunks from a zero
- * state, then a walk over its right sibling from that end state with no values.
+ * the pairs inside a 64-token chunk (levels 0..6) from the chunk's pair matrix P T'; the
+ * coarser levels l = 7 + s from walks over chunk blocks of 2^s: for bf16 with dk <= 128 one
+ * walk per scale over its right half-blocks that carries the KLA state of the enclosing
+ * 2^(s+1)-chunk block (weights lambda^(l) - lambda^(next level present) telescope to the
+ * definition), otherwise a zero-start walk over every left half-block and a walk over its
+ * right sibling from that end state with no values.
  *
  *   q, k, v, log_alpha, eta, eps, dtype, beta_mode, B, T, H, dk, dv, chunk
  *            as for kla_chunk_fwd_ex (the fp32 dtype supports dk in {64, 128})
  *   lam      fp32 [B,T,H,L]: lambda_t^(l)
  *   out      fp32 [B,T,H,dv]
  *   levels   L, 1..31, with T <= 2^(L-1), else KLA_ERR_INVALID_ARG
- * The workspace (the chunk records and the left half-blocks' end states) comes from the
+ * The workspace (the chunk records and the scales' carried end states) comes from the
  * library's workspace pool on `stream`, as for kla_chunk_fwd.
  */
 kla_status kla_loglinear_fwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q, const void* k,
