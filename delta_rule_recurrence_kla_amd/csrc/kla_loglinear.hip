@@ -448,185 +448,284 @@ __global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_mfma_kernel(con
 }
 
 // The same on the compact record (T' without its zero quadrant, and the gates), which the walks
-// read anyway, so that no full record is prepared: P = tril(e^{g_t - g_r} Q K^T) is formed here
-// from the chunk's query and key rows on the bf16 MFMA (exact products), on its lower 16 x 16
-// tiles, and staged in LDS in fp32 for the P T' product. It serves the scale walks of
-// state_walk_kernel (kla_state_dma.hip), whose outputs on chunk c >= 1 carry the chunk-local term
-// P T' V with the total weight lambda^(7 + lowest set bit of c): that weight is taken off every
-// pair here.
+// read anyway, so that no full record is prepared. A persistent, DMA-fed kernel: each workgroup
+// takes chunks blockIdx.x, blockIdx.x + gridDim.x, ... of all heads; a copy wave brings chunk
+// n + 1's rows of Q, K and V, its record and its weights into the other half of a
+// double-buffered LDS area (buffer_load ... lds, rows in the swizzled layout of kla_device.h)
+// while four compute waves work on chunk n, in three steps between workgroup barriers:
+//  1. P = tril(e^{g_t - g_r} Q K^T) on the bf16 MFMA (exact products), three 16 x 16 tiles per
+//     wave, split hi + lo into LDS in the record's layout (as the walk's output waves do);
+//  2. W = P T' on the 12 tiles on or below the diagonal (four tile-contractions per wave), computed
+//     transposed, W^T = T'^T P^T: T'^T from the record by transposed LDS reads
+//     (ds_read_b64_tr_b16), P^T as P's row fragments, P and T' both split (three passes); each
+//     pair weighted in place by lambda_t^(lev(t, s)) less lambda_t^(7 + lowest set bit of c) on
+//     chunk c >= 1 (lev = bit length of t xor s within the chunk; see the scale walks of
+//     state_walk_kernel, whose outputs on chunk c carry the chunk-local term with that weight),
+//     then split hi + lo into LDS, rows t;
+//  3. out = W V, written transposed as the walks' outputs are (16 columns x 16 tokens per tile,
+//     one 16-byte store per lane and tile): V^T from V's rows by transposed reads, W as row
+//     fragments; two passes (V is exact). Each wave takes DV / 64 column slices of 16.
+// Rows t of every 64-row tile are in the permuted order tok(m, r) of the walks, so that the
+// accumulator pair and fragment conventions are the same.
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+__device__ __forceinline__ int tok_r(int m, int r) { return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3); }
+
+__device__ __forceinline__ void dma16_l(rsrc_t r, void* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4_l(rsrc_t r, void* lds_dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 4, voff, 0, 0, 0);
+}
+
+}  // namespace
+
+constexpr int INTRA_DMA_THREADS = 320;  // four compute waves and the copy wave
+
 template <int DK, int DV>
-__global__ __launch_bounds__(INTRA_THREADS) void loglinear_intra_compact_kernel(
+__global__ __launch_bounds__(INTRA_DMA_THREADS) void loglinear_intra_compact_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint8_t* __restrict__ crec,
     const uint16_t* __restrict__ v, const float* __restrict__ lam, float* __restrict__ out, int T, int H, int nc,
-    int L) {
-  constexpr int BP = CHUNK + 8;  // bf16 pitch of the transposed rows (16-byte aligned)
-  constexpr int WP = CHUNK + 4;  // fp32 pitch of P and W
-  __shared__ __align__(16) uint16_t sTh[CHUNK][BP];  // T'^T, hi and lo
-  __shared__ __align__(16) uint16_t sTl[CHUNK][BP];
-  __shared__ __align__(16) uint16_t sVt[DV][BP];     // V^T
-  __shared__ __align__(16) float sP[CHUNK][WP];
-  __shared__ __align__(16) float sW[CHUNK][WP];
-  __shared__ float sg[CHUNK];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, gq = lane >> 4, ln = lane & 15;
-  const int id = blockIdx.x;
-  const int bh = id / nc, c = id - bh * nc;
-  const int b = bh / H, h = bh - b * H;
-  const int t0 = c * CHUNK;
-  const uint8_t* R = crec + static_cast<size_t>(id) * CREC_BYTES;
-  const int mt = wv & 3;
-  const size_t row0 = (static_cast<size_t>(b) * T + t0) * H + h;  // (b, t0, h) in token-head units
+    int L, int nchunk_all) {
+  using TR = Tr<MODE_BF16>;
+  constexpr int KRB = DK * 2, VRB = DV * 2;            // bytes of a key/query row and a value row
+  constexpr int KBYTES = CHUNK * KRB, VBYTES = CHUNK * VRB;
+  constexpr int K_OFF = 0, Q_OFF = KBYTES, V_OFF = 2 * KBYTES, R_OFF = V_OFF + VBYTES;
+  constexpr int L_OFF = R_OFF + CREC_BYTES;            // weights [8][64] fp32: levels 0..6, the subtracted one
+  constexpr int BUF = L_OFF + 8 * CHUNK * 4;
+  constexpr int KPR = KRB / 16, KRPB = 1024 / KRB, VPR = VRB / 16, VRPB = 1024 / VRB;
+  constexpr int NSL = DV / 64;                         // 16-column slices per compute wave
+  static_assert(BUF % 256 == 0 && R_OFF % 256 == 0, "buffers and records on the 256-byte bank period");
+  __shared__ __align__(256) uint8_t lds0[BUF];
+  __shared__ __align__(256) uint8_t lds1[BUF];
+  __shared__ __align__(256) uint8_t ldsP[CREC_EG_OFF];  // P, hi and lo, in the record's layout
+  __shared__ __align__(256) uint8_t ldsW[CREC_EG_OFF];  // weighted W, likewise
 
-  // Every global load first, so that they are all in flight together: the query row 16 mt + ln
-  // and the key rows 16 nt + ln of this wave's tiles (mt, nt), nt = wv / 4 + 2 u, columns
-  // 32 kb + 8 gq + 0..7 (zero past T); T' (transposed below) and V
-  u32x4 qa[DK / 32], ka[2][DK / 32];
-  {
-    const int tq = 16 * mt + ln;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gq = lane >> 4, ln = lane & 15;
+  const int first = blockIdx.x, step = gridDim.x;
+  const int nmine = first < nchunk_all ? (nchunk_all - 1 - first) / step + 1 : 0;
+
+  if (wu == 4) {  // the copy wave
+    auto copy_chunk = [&](int n, uint8_t* B) __attribute__((always_inline)) {
+      const int bh = n / nc, c = n - bh * nc;
+      const int b = bh / H, h = bh - b * H;
+      const int t0 = c * CHUNK;
+      const rsrc_t rr = make_rsrc_wu(crec + static_cast<size_t>(n) * CREC_BYTES, CREC_BYTES);
 #pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb) {
-      qa[kb] = u32x4{0u, 0u, 0u, 0u};
-      if (t0 + tq < T) qa[kb] = *reinterpret_cast<const u32x4*>(q + (row0 + static_cast<size_t>(tq) * H) * DK + 32 * kb + 8 * gq);
-    }
+      for (int m = 0; m < CREC_BYTES / 1024; ++m) dma16_l(rr, B + R_OFF + 1024 * m, 1024 * m + 16 * lane);
+      if (lane < (CREC_BYTES % 1024) / 16)
+        dma16_l(rr, B + R_OFF + (CREC_BYTES / 1024) * 1024, (CREC_BYTES / 1024) * 1024 + 16 * lane);
+      const size_t row0 = (static_cast<size_t>(b) * T + t0) * H + h;  // token-head row of token t0
+      const long long left = T - t0;
+      const rsrc_t rk = make_rsrc_wu(k + row0 * DK, left * H * KRB - static_cast<long long>(h) * KRB);
+      const rsrc_t rq = make_rsrc_wu(q + row0 * DK, left * H * KRB - static_cast<long long>(h) * KRB);
+      const rsrc_t rv = make_rsrc_wu(v + row0 * DV, left * H * VRB - static_cast<long long>(h) * VRB);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int nt = (wv >> 2) + 2 * u;
-      const int tk = 16 * nt + ln;
-#pragma unroll
-      for (int kb = 0; kb < DK / 32; ++kb) {
-        ka[u][kb] = u32x4{0u, 0u, 0u, 0u};
-        if (nt <= mt && t0 + tk < T)
-          ka[u][kb] = *reinterpret_cast<const u32x4*>(k + (row0 + static_cast<size_t>(tk) * H) * DK + 32 * kb + 8 * gq);
+      for (int blk = 0; blk < KBYTES / 1024; ++blk) {
+        const int row = blk * KRPB + lane / KPR;
+        const int off = row * H * KRB + 16 * ((lane % KPR) ^ swz<KRB>(row));
+        dma16_l(rk, B + K_OFF + 1024 * blk, off);
+        dma16_l(rq, B + Q_OFF + 1024 * blk, off);
       }
+#pragma unroll
+      for (int blk = 0; blk < VBYTES / 1024; ++blk) {
+        const int row = blk * VRPB + lane / VPR;
+        dma16_l(rv, B + V_OFF + 1024 * blk, row * H * VRB + 16 * ((lane % VPR) ^ swz<VRB>(row)));
+      }
+      // weights of levels 0..6 and of 7 + (lowest set bit of c), one dword per lane and level
+      const int HL = H * L;
+      const rsrc_t rl = make_rsrc_wu(lam + row0 * L, (left - 1) * HL * 4 + static_cast<long long>(L) * 4);
+      const int low = c > 0 ? 7 + __builtin_ctz(static_cast<unsigned>(c)) : 0;
+#pragma unroll
+      for (int l = 0; l < 7; ++l) dma4_l(rl, B + L_OFF + 256 * l, (lane * HL + l) * 4);
+      dma4_l(rl, B + L_OFF + 256 * 7, (lane * HL + low) * 4);
+    };
+    if (nmine > 0) copy_chunk(first, lds0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int j = 0; j < nmine; ++j) {
+      if (j + 1 < nmine) copy_chunk(first + (j + 1) * step, ((j + 1) & 1) ? lds1 : lds0);
+      asm volatile("s_barrier\n\ts_barrier" ::: "memory");  // the P and the W barriers
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    return;
   }
-  // T' from the compact record: rows 0..31 hold columns 0..31 (128-byte rows), rows 32..63 all
-  // 64 (256-byte rows); consecutive lanes take consecutive rows
-  const bool top = tid < 32 * 4;
-  const int tr = top ? (tid & 31) : 32 + ((tid - 128) & 31);
-  const int tcb = top ? (tid >> 5) : ((tid - 128) >> 5);
-  u32x4 thi = {0u, 0u, 0u, 0u}, tlo = {0u, 0u, 0u, 0u};
-  if (tid < 32 * 4 + 32 * 8) {
-    thi = *reinterpret_cast<const u32x4*>(top ? R + CREC_TOP_OFF + swz_off<128>(tr, 16 * tcb)
-                                              : R + CREC_BOT_OFF + swz_off<256>(tr - 32, 16 * tcb));
-    tlo = *reinterpret_cast<const u32x4*>(top ? R + CREC_TOP_OFF + swz_off<128>(tr, 16 * (tcb + 4))
-                                              : R + CREC_BOT_OFF + swz_off<256>(tr - 32, 16 * (tcb + 8)));
-  }
-  constexpr int NVL = CHUNK * DV / 8 / INTRA_THREADS;
-  u32x4 vx[NVL];
-#pragma unroll
-  for (int u = 0; u < NVL; ++u) {
-    const int e = tid + INTRA_THREADS * u, tt = e & 63, pc = e >> 6;
-    vx[u] = u32x4{0u, 0u, 0u, 0u};
-    if (t0 + tt < T) vx[u] = *reinterpret_cast<const u32x4*>(v + (row0 + static_cast<size_t>(tt) * H) * DV + 8 * pc);
-  }
-  // Q K^T on the bf16 MFMA (exact products, fp32 sums)
-  f32x4 qk[2] = {zero4(), zero4()};
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if ((wv >> 2) + 2 * u > mt) continue;
-#pragma unroll
-    for (int kb = 0; kb < DK / 32; ++kb)
-      qk[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[kb]),
-                                                      __builtin_bit_cast(bf16x8, ka[u][kb]), qk[u], 0, 0, 0);
-  }
-  // T' and V transposed into LDS
-  if (tid < 32 * 4 + 32 * 8) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sTh[8 * tcb + j][tr] = static_cast<uint16_t>((j & 1) ? thi[j >> 1] >> 16 : thi[j >> 1] & 0xFFFFu);
-      sTl[8 * tcb + j][tr] = static_cast<uint16_t>((j & 1) ? tlo[j >> 1] >> 16 : tlo[j >> 1] & 0xFFFFu);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < NVL; ++u) {
-    const int e = tid + INTRA_THREADS * u, tt = e & 63, pc = e >> 6;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      sVt[8 * pc + j][tt] = static_cast<uint16_t>((j & 1) ? vx[u][j >> 1] >> 16 : vx[u][j >> 1] & 0xFFFFu);
-  }
-  if (tid < CHUNK) sg[tid] = reinterpret_cast<const float*>(R + CREC_G_OFF)[tid];
-  __syncthreads();
-  // P = e^{g_t - g_r} Q K^T on and below the diagonal, zero above
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int nt = (wv >> 2) + 2 * u;
-    const int r = 16 * nt + ln;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * mt + 4 * gq + e;
-      sP[t][r] = r <= t ? __expf(sg[t] - sg[r]) * qk[u][e] : 0.f;
-    }
-  }
-  __syncthreads();
 
-  // W = P T' on tiles (mt, nt) with P split hi + lo (three passes); the contraction needs only
-  // 16 nt <= r <= 16 mt + 15
+  // compute waves 0..3
+  const int w = wu;
+  int oK[DK / 32], oRt[2], oRb[2][2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int nt = (wv >> 2) + 2 * u;
-    f32x4 acc = zero4();
-    if (nt <= mt) {
+  for (int kb = 0; kb < DK / 32; ++kb) oK[kb] = swz_off<KRB>(tok_r(0, ln), 64 * kb + 16 * gq);
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl) {
+    oRt[hl] = CREC_TOP_OFF + swz_off<128>(tok_r(0, ln), 64 * hl + 16 * gq);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) oRb[kb][hl] = CREC_BOT_OFF + swz_off<256>(tok_r(0, ln), 128 * hl + 64 * kb + 16 * gq);
+  }
+  auto mrow = [](int m) { return 32 * (m >> 1) + 4 * (m & 1); };
+  auto fragK = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(X + oK[kb] + mrow(m) * KRB));
+  };
+  // hi and lo of row tok(m, ln) of a lower-triangular matrix in the record's layout, columns
+  // 32 kb + 8 gq + 0..7 (kb = 0 when m < 2)
+  auto fragR = [&](const uint8_t* X, int m, int kb) __attribute__((always_inline)) {
+    const uint8_t* p = m < 2 ? X + oRt[0] + 4 * (m & 1) * 128 : X + oRb[kb][0] + 4 * (m & 1) * 256;
+    const int lo = m < 2 ? oRt[1] - oRt[0] : oRb[kb][1] - oRb[kb][0];
+    S8 r;
+    r.h = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+    r.l = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + lo));
+    return r;
+  };
+  // T'^T operand: lane (gq, ln) receives T'[32 kb + 8 gq + j][16 nt + ln], j = 0..7, hi and lo
+  // (ds_read_b64_tr_b16: it supplies the 8-byte block of row 32 kb + 8 gq + 4 hf + (ln >> 2),
+  // columns 16 nt + 4 (ln & 3) + 0..3; kb = 0 only with nt < 2, the top rows' columns)
+  auto fragTT = [&](const uint8_t* X, int nt, int kb) __attribute__((always_inline)) {
+    const int cb = 2 * (16 * nt + 4 * (ln & 3));
+    i16x4 hv[2], lv[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 32 * kb + 8 * gq + 4 * hf + (ln >> 2);
+      const int oh = kb == 0 ? CREC_TOP_OFF + swz_off<128>(row, cb) : CREC_BOT_OFF + swz_off<256>(row - 32, cb);
+      const int ol = kb == 0 ? CREC_TOP_OFF + swz_off<128>(row, 64 + cb) : CREC_BOT_OFF + swz_off<256>(row - 32, 128 + cb);
+      hv[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + oh));
+      lv[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(X + ol));
+    }
+    S8 r;
+    r.h = __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    r.l = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lv[0], lv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    return r;
+  };
+  // V^T operand: lane (gq, ln) receives V[32 a + 8 gq + j][16 cs + ln], j = 0..7
+  auto fragVT = [&](const uint8_t* X, int cs, int a) __attribute__((always_inline)) {
+    const uint8_t* p = X + swz_off<VRB>(8 * gq + (ln >> 2), 2 * (16 * cs + 4 * (ln & 3))) + 32 * a * VRB;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * VRB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // this wave's W tiles (m_t, nt): four tile-contractions each
+  constexpr int WT[4][4][2] = {{{2, 0}, {2, 1}, {-1, 0}, {-1, 0}},
+                               {{3, 0}, {3, 1}, {-1, 0}, {-1, 0}},
+                               {{0, 0}, {0, 1}, {2, 2}, {2, 3}},
+                               {{1, 0}, {1, 1}, {3, 2}, {3, 3}}};
+
+  asm volatile("s_barrier" ::: "memory");  // the first chunk has landed
+  for (int j = 0; j < nmine; ++j) {
+    const int n = first + j * step;
+    const int bh = n / nc, c = n - bh * nc;
+    const int b = bh / H, h = bh - b * H;
+    const int t0 = c * CHUNK;
+    const uint8_t* B = (j & 1) ? lds1 : lds0;
+    const uint8_t* sK = B + K_OFF;
+    const uint8_t* sQ = B + Q_OFF;
+    const uint8_t* sV = B + V_OFF;
+    const uint8_t* sR = B + R_OFF;
+    const float* sL = reinterpret_cast<const float*>(B + L_OFF);
+    const float* sG = reinterpret_cast<const float*>(sR + CREC_G_OFF);
+    // 1. this wave's three P tiles (rows r of tile mj, columns i of tile mi, i <= r)
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) {
+      const int mi = (w >> 1) + (jj == 2 ? 2 : 0), mj = (w & 1) + (jj >= 1 ? 2 : 0);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < DK / 32; ++kb) acc = mfma_bf16(fragK(sK, mi, kb), fragK(sQ, mj, kb), acc);
+      const int r = tok_r(mj, ln), i0 = tok_r(mi, 4 * gq);
+      const float gr = sG[r];
+      const f32x4 gi = *reinterpret_cast<const f32x4*>(sG + i0);
+      f32x4 pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = __expf(gr - gi[e]) * acc[e];
+        pv[e] = (jj == 1 || i0 + e <= r) ? x : 0.f;
+      }
+      const u32x2 hw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv, bf16x4));
+      f32x4 hf;
+      hf[0] = __uint_as_float(hw[0] << 16);
+      hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
+      hf[2] = __uint_as_float(hw[1] << 16);
+      hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
+      const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(pv - hf, bf16x4));
+      const int oh = jj == 0 ? CREC_TOP_OFF + swz_off<128>(r, 2 * i0) : CREC_BOT_OFF + swz_off<256>(r - 32, 2 * i0);
+      const int ol = jj == 0 ? CREC_TOP_OFF + swz_off<128>(r, 64 + 2 * i0)
+                             : CREC_BOT_OFF + swz_off<256>(r - 32, 128 + 2 * i0);
+      *reinterpret_cast<u32x2*>(ldsP + oh) = hw;
+      *reinterpret_cast<u32x2*>(ldsP + ol) = lw;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // 2. W^T tiles: rows s = 16 nt + 4 gq + e, columns t = tok(m_t, ln); contraction over
+    // i in [s, t]: i < 32 when s < 32, i >= 32 when t >= 32
+    const float sub_on = c > 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int mt = WT[w][u][0], nt = WT[w][u][1];
+      if (mt < 0) continue;
+      f32x4 x = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (32 * kb > 16 * mt + 15 || 32 * kb + 31 < 16 * nt) continue;
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&sP[16 * mt + ln][32 * kb + 8 * gq]);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&sP[16 * mt + ln][32 * kb + 8 * gq + 4]);
-        const S8 ps = split8(frag_from_acc(p0, p1));
-        const bf16x8 th = *reinterpret_cast<const bf16x8*>(&sTh[16 * nt + ln][32 * kb + 8 * gq]);
-        const bf16x8 tl = *reinterpret_cast<const bf16x8*>(&sTl[16 * nt + ln][32 * kb + 8 * gq]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps.h, th, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps.h, tl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ps.l, th, acc, 0, 0, 0);
+        if ((kb == 0 && nt >= 2) || (kb == 1 && mt < 2)) continue;
+        x = TR::mma_dd(x, fragTT(sR, nt, kb), fragR(ldsP, mt, kb));
+      }
+      const int t = tok_r(mt, ln);
+      const float sub = sub_on * sL[7 * CHUNK + t];
+      f32x4 xw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 16 * nt + 4 * gq + e;
+        const int lev = 32 - __clz(t ^ s);  // 0 when s == t
+        xw[e] = s <= t ? x[e] * (sL[(lev > 6 ? 6 : lev) * CHUNK + t] - sub) : 0.f;
+      }
+      const u32x2 hw = __builtin_bit_cast(u32x2, __builtin_convertvector(xw, bf16x4));
+      f32x4 hf;
+      hf[0] = __uint_as_float(hw[0] << 16);
+      hf[1] = __uint_as_float(hw[0] & 0xFFFF0000u);
+      hf[2] = __uint_as_float(hw[1] << 16);
+      hf[3] = __uint_as_float(hw[1] & 0xFFFF0000u);
+      const u32x2 lw = __builtin_bit_cast(u32x2, __builtin_convertvector(xw - hf, bf16x4));
+      const int col = 2 * (16 * nt + 4 * gq);
+      const int oh = t < 32 ? CREC_TOP_OFF + swz_off<128>(t, col) : CREC_BOT_OFF + swz_off<256>(t - 32, col);
+      const int ol = t < 32 ? CREC_TOP_OFF + swz_off<128>(t, 64 + col) : CREC_BOT_OFF + swz_off<256>(t - 32, 128 + col);
+      *reinterpret_cast<u32x2*>(ldsW + oh) = hw;
+      *reinterpret_cast<u32x2*>(ldsW + ol) = lw;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // 3. out = W V on this wave's column slices, stored transposed (rows: 4 columns per lane)
+    const rsrc_t ro = make_rsrc_wu(out + ((static_cast<size_t>(b) * T + t0) * H + h) * DV,
+                                   (static_cast<long long>(T - t0) * H - h) * DV * 4);
+#pragma unroll
+    for (int u = 0; u < NSL; ++u) {
+      const int cs = w * NSL + u;
+      const bf16x8 va0 = fragVT(sV, cs, 0);
+      const bf16x8 va1 = fragVT(sV, cs, 1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4 acc = TR::mma_xd(zero4(), va0, fragR(ldsW, mt, 0));
+        if (mt >= 2) acc = TR::mma_xd(acc, va1, fragR(ldsW, mt, 1));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro,
+                                               (tok_r(mt, ln) * H * DV + 16 * cs + 4 * gq) * 4, 0, 0);
       }
     }
-    const int s = 16 * nt + ln;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * mt + 4 * gq + e;
-      float wgt = 0.f;
-      if (s <= t && t0 + t < T) {
-        const int lev = s == t ? 0 : 32 - __clz(static_cast<unsigned>(t ^ s));
-        const float* lp = lam + (row0 + static_cast<size_t>(t) * H) * L;
-        wgt = acc[e] * (c > 0 ? lp[lev] - lp[7 + __builtin_ctz(static_cast<unsigned>(c))] : lp[lev]);
-      }
-      sW[t][s] = wgt;
-    }
-  }
-  __syncthreads();
-
-  // out = W V, W split hi + lo, V exact (two passes); row tiles 0 and 1 need only 32 tokens
-#pragma unroll
-  for (int u = 0; u < DV / 32; ++u) {
-    const int nt = (wv >> 2) + 2 * u;
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb == 1 && mt < 2) continue;
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sW[16 * mt + ln][32 * kb + 8 * gq]);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sW[16 * mt + ln][32 * kb + 8 * gq + 4]);
-      const S8 ws = split8(frag_from_acc(w0, w1));
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&sVt[16 * nt + ln][32 * kb + 8 * gq]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws.h, vb, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws.l, vb, acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tt = 16 * mt + 4 * gq + e;
-      if (t0 + tt < T) out[(row0 + static_cast<size_t>(tt) * H) * DV + 16 * nt + ln] = acc[e];
-    }
+    // past the end barrier, P and W may be overwritten, and the next chunk has landed
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
 hipError_t launch_loglinear_intra_compact(const Dims& d, const void* q, const void* k, const uint8_t* crec,
                                           const void* v, const float* lam, int L, float* out, hipStream_t stream) {
-  const dim3 grid(d.B * d.H * d.nc), block(INTRA_THREADS);
+  const int nchunk = d.B * d.H * d.nc;
+  if (nchunk == 0) return hipSuccess;
+  const dim3 grid(nchunk < 256 ? nchunk : 256), block(INTRA_DMA_THREADS);
   const auto* qb = static_cast<const uint16_t*>(q);
   const auto* kb = static_cast<const uint16_t*>(k);
   const auto* vb = static_cast<const uint16_t*>(v);
 #define KLA_LLI_CASE(DKV, DVV)                                                                                   \
   if (d.dk == DKV && d.dv == DVV)                                                                                \
     return launch_kernel(loglinear_intra_compact_kernel<DKV, DVV>, grid, block, stream, qb, kb, crec, vb, lam, out, \
-                         d.T, d.H, d.nc, L);
+                         d.T, d.H, d.nc, L, nchunk);
   KLA_LLI_CASE(64, 64)
   KLA_LLI_CASE(64, 128)
   KLA_LLI_CASE(128, 64)

@@ -342,8 +342,8 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
 //  * the recurrence wave (waves 0..3) runs the chain. It hands U, split hi/lo, to the output
 //    wave through LDS, and at the end of each chunk the hi/lo split of the new S, which it
 //    keeps in registers for its own next chunk;
-//  * the output wave (waves 4..7) computes its three P tiles and Q S from that split of S while
-//    the recurrence wave computes U, then P U, and stores its output tiles;
+//  * the output wave (waves 4..7) computes its three P tiles and reads that split of S while the
+//    recurrence wave computes U, then Q S, P U, and stores its output tiles;
 //  * the copy wave (wave 8) copies chunk c+1's rows of K and Q and its record into the other
 //    half of a double-buffered LDS area while chunk c is computed. V rows are read only by the
 //    recurrence wave, before the mid-chunk barrier, so they have one buffer, which the copy
@@ -759,6 +759,10 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
           Sb[kb].h = __builtin_bit_cast(bf16x8, ldsSb[sl][kb][0][lane]);
           Sb[kb].l = __builtin_bit_cast(bf16x8, ldsSb[sl][kb][1][lane]);
         }
+        // the split of S is read before the mid-chunk barrier (past it the recurrence wave may
+        // overwrite it) and used after it: Q S off the first half, where the P tiles already
+        // keep this wave longer than the recurrence wave takes to publish U
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const float* sEG = reinterpret_cast<const float*>(sR + CREC_EG_OFF);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -772,7 +776,6 @@ __global__ __launch_bounds__(WALK_THREADS) void state_walk_kernel(StateDmaArgs a
           Oacc[mt] = acc * sEG[tok(mt, ln)];
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       // LL: nothing below may be hoisted above the barrier; the scheduler would otherwise move
       // the weights' arithmetic up and with it a wait for the loads of this chunk's weights
       if constexpr (LL) __builtin_amdgcn_sched_barrier(0);
