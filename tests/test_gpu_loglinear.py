@@ -172,6 +172,34 @@ def test_loglinear_prefill_unit_weights_equal_kla():
     assert_close(o, o_k.cpu().numpy(), TOL["bf16"] / 10, "out")
 
 
+def _recurrent_reference(wl, lam, b, h, L):
+    """One head by the oracle's recurrent form over every token."""
+    dk, dv = wl.q.shape[-1], wl.v.shape[-1]
+    S = np.zeros((1, 1, L, dk, dv))
+    ref = np.zeros((wl.T, dv))
+    for t in range(wl.T):
+        pick = lambda a: a[b, t, h][None, None]
+        o_t, S = loglinear.decode_step_loglinear(S, t, pick(wl.q), pick(wl.k), pick(wl.v),
+                                                 wl.log_alpha[b, t, h][None, None], wl.eta[b, t, h][None, None],
+                                                 lam[b, t, h][None, None], wl.eps)
+        ref[t] = o_t[0, 0]
+    return ref
+
+
+def test_loglinear_prefill_uneven_work_per_workgroup():
+    """24 heads over 52 chunks less a ragged 17 tokens: the intra-chunk kernel's workgroups take four or five chunks
+    each, and the scale walks share a head's half-blocks out in runs of unequal length (five, then one, at the
+    lowest scale). Two heads against the recurrent form over every token."""
+    B, T, H, L = 1, 64 * 52 - 17, 24, 13
+    log(f"loglinear prefill uneven work B={B} T={T} H={H} L={L}")
+    wl = W.make_prefill("lm_layer_4k", seed=21, B=B, T=T, H=H)
+    lam = np.random.default_rng(22).uniform(0.2, 1.5, (B, T, H, L)).astype(np.float32)
+    o = _run_prefill(wl, lam)
+    for b, h in [(0, 0), (0, 23)]:
+        e = assert_close(o[b, :, h], _recurrent_reference(wl, lam, b, h, L), TOL["bf16"] / 10, f"head {(b, h)}")
+        log(f"loglinear prefill uneven work head {(b, h)}: {e:.2e}")
+
+
 def test_loglinear_prefill_full_size_sampled():
     """The LM-layer shape (B=8, T=4096, H=16, dk=dv=128) with 13 levels, sampled heads against
     the oracle's recurrent form over all 4096 tokens."""
