@@ -118,7 +118,12 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   static_assert((KCB & (KCB - 1)) == 0 && (VCB & (VCB - 1)) == 0, "shape");
 
   __shared__ __align__(16) in_t sK[CHUNK * LDK];
-  __shared__ __align__(16) in_t sKt[DK * LDT];
+  // K^T for the state update. bf16 features read K's rows transposed instead (ds_read_b64_tr_b16):
+  // the map walk at dk = 256 then fits two workgroups per CU and the walks do fewer vector
+  // transposes (host-lifted PSD step 5% faster). With the fused lift the transposed copy is kept:
+  // without it that step measured 2% slower.
+  constexpr bool KT_TR = MODE == MODE_BF16 && !LIFT;
+  __shared__ __align__(16) in_t sKt[KT_TR ? VEC : DK * LDT];
   __shared__ __align__(16) in_t sQ[WITH_OUT ? CHUNK * LDK : VEC];
   __shared__ __align__(16) in_t sVt[NCOLS * LDT];
   __shared__ __align__(16) uint8_t sTP[CHUNK * DROW_BYTES];
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
           *reinterpret_cast<u32x4*>(sK + (4 * rb + u4) * LDK + VEC * cb) = pk[u][u4];
           if constexpr (WITH_OUT) *reinterpret_cast<u32x4*>(sQ + (4 * rb + u4) * LDK + VEC * cb) = pq[u][u4];
         }
-        store_transposed(sKt, pk[u], VEC * cb, 4 * rb);
+        if constexpr (!KT_TR) store_transposed(sKt, pk[u], VEC * cb, 4 * rb);
       }
     }
 #pragma unroll
@@ -439,11 +444,26 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
     DF Ud[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Ud[kb] = TR::mk(frag_from_acc(U[2 * kb], U[2 * kb + 1]));
+    // KT_TR: lane (gq, ln) takes K[32 kb + kslot(gq, j)][16 mt + ln], j = 0..7, from two transposed reads
+    // of four consecutive token rows each: it supplies the 8-byte block of row 32 kb + 4 gq (+ 16) +
+    // (ln >> 2), keys 16 mt + 4 (ln & 3) + 0..3
+    auto ldKT = [&](int mt, int kb) __attribute__((always_inline)) {
+      if constexpr (KT_TR) {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const in_t* p = sK + (32 * kb + 4 * gq + (ln >> 2)) * LDK + 16 * mt + 4 * (ln & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * LDK));
+        return __builtin_bit_cast(typename TR::XF, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        return TR::ldx(sKt, LDT, 16 * mt, 32 * kb, lane);
+      }
+    };
 #pragma unroll
     for (int mt = 0; mt < DK / 16; ++mt) {
       S[mt] *= gC;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], TR::ldx(sKt, LDT, 16 * mt, 32 * kb, lane), Ud[kb]);
+      for (int kb = 0; kb < 2; ++kb) S[mt] = TR::mma_xd(S[mt], ldKT(mt, kb), Ud[kb]);
     }
     // Both barriers guard LDS only: the output stores and the next chunk's prefetch loads stay
     // in flight (store_lds waits for the loads it consumes, not for the stores issued after them).
