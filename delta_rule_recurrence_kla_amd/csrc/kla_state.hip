@@ -95,7 +95,10 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t lo, uint32_t hi, int ha
 }
 
 template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT, bool ACC>
-__global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
+// The bf16 map walk at dk = 256 (61 KB of LDS without a transposed copy of K) is held to the
+// registers of two workgroups per CU: two map chains per SIMD, a few values spilled outside the
+// chunk loop (map walk 389 -> 353 us on the PSD workload).
+__global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIFT) ? 2 : 1) void state_kernel(StateArgs a) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
   using DF = typename TR::DF;
@@ -120,8 +123,9 @@ __global__ __launch_bounds__(256) void state_kernel(StateArgs a) {
   __shared__ __align__(16) in_t sK[CHUNK * LDK];
   // K^T for the state update. bf16 features read K's rows transposed instead (ds_read_b64_tr_b16):
   // the map walk at dk = 256 then fits two workgroups per CU and the walks do fewer vector
-  // transposes (host-lifted PSD step 5% faster). With the fused lift the transposed copy is kept:
-  // without it that step measured 2% slower.
+  // transposes (host-lifted PSD step 5% faster, 9% with the two workgroups). With the fused lift
+  // the transposed copy is kept: without it that step measured 2% slower, 5% with the map walk at
+  // two workgroups per CU.
   constexpr bool KT_TR = MODE == MODE_BF16 && !LIFT;
   __shared__ __align__(16) in_t sKt[KT_TR ? VEC : DK * LDT];
   __shared__ __align__(16) in_t sQ[WITH_OUT ? CHUNK * LDK : VEC];
