@@ -123,10 +123,10 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
   __shared__ __align__(16) in_t sK[CHUNK * LDK];
   // K^T for the state update. bf16 features read K's rows transposed instead (ds_read_b64_tr_b16):
   // the map walk at dk = 256 then fits two workgroups per CU and the walks do fewer vector
-  // transposes (host-lifted PSD step 5% faster, 9% with the two workgroups). With the fused lift
-  // the transposed copy is kept: without it that step measured 2% slower, 5% with the map walk at
-  // two workgroups per CU.
-  constexpr bool KT_TR = MODE == MODE_BF16 && !LIFT;
+  // transposes (host-lifted PSD step 5% faster, 9% with the two workgroups). The fused lift's map
+  // walk keeps the transposed copy: without it that walk measured 7% slower (9% at two workgroups
+  // per CU); its walk with outputs reads K^T transposed like the others.
+  constexpr bool KT_TR = MODE == MODE_BF16 && (!LIFT || WITH_OUT);
   __shared__ __align__(16) in_t sKt[KT_TR ? VEC : DK * LDT];
   __shared__ __align__(16) in_t sQ[WITH_OUT ? CHUNK * LDK : VEC];
   __shared__ __align__(16) in_t sVt[NCOLS * LDT];
