@@ -182,7 +182,9 @@ struct Plan {
   kla_path path;
   int segs;        // scan segments (1 for sequential)
   int seg_chunks;  // chunks per segment
-  size_t rec_off, rec_bytes, maps_off, maps_bytes, starts_off, starts_bytes, total;
+  size_t rec_off, rec_bytes, maps_off, maps_bytes, starts_off, starts_bytes;
+  size_t lift_off, lift_bytes;  // PSD lift: the lifted query rows, then the key rows (0 bytes without the lift)
+  size_t total;
 };
 
 Plan make_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, kla_path path, int segments, int cus) {
@@ -245,8 +247,16 @@ Plan make_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, kla_path pa
   p.maps_bytes = chosen == KLA_PATH_SCAN ? align256(static_cast<size_t>(bh) * (segs - 1) * dk * (dk + dv) * 4) : 0;
   p.starts_off = p.maps_off + p.maps_bytes;
   p.starts_bytes = chosen == KLA_PATH_SCAN ? align256(static_cast<size_t>(bh) * segs * dk * dv * 4) : 0;
-  p.total = p.starts_off + p.starts_bytes;
+  p.lift_off = p.starts_off + p.starts_bytes;
+  p.lift_bytes = 0;
+  p.total = p.lift_off;
   return p;
+}
+
+// Room for the lifted query and key rows of a PSD call (dk bf16 features per row).
+void plan_lift(Plan& p, int B, int T, int H, int dk) {
+  p.lift_bytes = align256(static_cast<size_t>(B) * T * H * dk * 2);
+  p.total = p.lift_off + 2 * p.lift_bytes;
 }
 
 kla_status hip_fail(hipError_t e, const char* what) {
@@ -287,13 +297,24 @@ hipError_t chunk_fwd_enqueue(const Plan& p, kla_dtype dtype, kla_beta_mode beta_
                              const void* v, const float* log_alpha, const float* eta, float eps,
                              const float* init_state, float* out, float* final_state, int B, int T, int H, int dk,
                              int dv, int lift, uint8_t* base, hipStream_t stream) {
-  const kla::Dims d{B, T, H, dk, dv, (T + kChunk - 1) / kChunk, lift};
+  const kla::Dims dp{B, T, H, dk, dv, (T + kChunk - 1) / kChunk, lift};
+  const kla::Dims d{B, T, H, dk, dv, (T + kChunk - 1) / kChunk, 0};
   const int mode = dtype == KLA_DTYPE_BF16 ? 0 : 1;
   uint8_t* rec = base + p.rec_off;
   float* maps = reinterpret_cast<float*>(base + p.maps_off);
   float* starts = reinterpret_cast<float*>(base + p.starts_off);
   const int direct = beta_mode == KLA_BETA_DIRECT;
-  hipError_t e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, rec, stream); });
+  // PSD lift: prep forms its fragments from the u rows and writes the lifted rows, which the
+  // walks read in their place
+  void* fq = lift ? base + p.lift_off : nullptr;
+  void* fk = lift ? base + p.lift_off + p.lift_bytes : nullptr;
+  hipError_t e = timed("kla_prep", stream, [&] {
+    return kla::launch_prep(mode, dp, q, k, log_alpha, eta, eps, direct, rec, stream, fq, fk);
+  });
+  if (lift) {
+    q = fq;
+    k = fk;
+  }
   if (e == hipSuccess) {
     if (p.path == KLA_PATH_SEQUENTIAL) {
       e = timed("kla_state_seq", stream, [&] {
@@ -323,7 +344,8 @@ kla_status chunk_fwd_impl(kla_dtype dtype, kla_beta_mode beta_mode, const void* 
   if (st != KLA_OK) return st;
   if (T == 0) return chunk_fwd_empty(init_state, final_state, static_cast<size_t>(B) * H * dk * dv, stream);
 
-  const Plan p = make_plan(dtype, B, T, H, dk, dv, path, segments, device_cus());
+  Plan p = make_plan(dtype, B, T, H, dk, dv, path, segments, device_cus());
+  if (lift) plan_lift(p, B, T, H, dk);
   void* ws = nullptr;
   st = workspace_alloc(&ws, p.total, stream);
   if (st != KLA_OK) return st;

@@ -38,14 +38,16 @@ constexpr int LIFT_P_HOST = 16;
 struct Dims {
   int B, T, H, dk, dv;
   int nc;        // number of 64-token chunks, ceil(T / 64)
-  int lift = 0;  // q and k hold 16-wide u rows; the kernels form the dk = 256 PSD features
+  int lift = 0;  // prep only: q and k hold 16-wide u rows, and prep forms the dk = 256 PSD features
   int full_rec = 0;  // prep writes the full record (T' and P) whatever the dtype and dk
 };
 
 // Chunk prep: one wavefront per (b, h, chunk); writes one record per chunk. `direct` takes
-// beta = eta as given instead of the Kaczmarz step eta / (||k||^2 + eps).
+// beta = eta as given instead of the Kaczmarz step eta / (||k||^2 + eps). With d.lift, q and k
+// are u rows and prep also writes the lifted query and key rows ([B, T, H, dk] bf16) to fq, fk.
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
-                       const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream);
+                       const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream,
+                       void* fq = nullptr, void* fk = nullptr);
 
 // Sequential inter-chunk state + output: one workgroup per (b, h, 64-column group of dv).
 // init may be null (zero state); fin may be null (not written).

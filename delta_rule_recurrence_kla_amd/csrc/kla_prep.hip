@@ -73,7 +73,8 @@ template <int MODE, int DK, bool COMPACT, bool LIFT>
 __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, const void* __restrict__ kv,
                                                    const float* __restrict__ log_alpha,
                                                    const float* __restrict__ eta, float eps, int direct,
-                                                   uint8_t* __restrict__ rec, int T, int H, int nc, int nchunks) {
+                                                   uint8_t* __restrict__ rec, int T, int H, int nc, int nchunks,
+                                                   void* __restrict__ fq, void* __restrict__ fk) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
   using XF = typename TR::XF;
@@ -106,6 +107,12 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
   const long long avail = static_cast<long long>(T - t0) * rowK;
   const rsrc_t rk = make_rsrc_wu(static_cast<const uint8_t*>(kv) + chunk_off, avail);
   const rsrc_t rq = make_rsrc_wu(static_cast<const uint8_t*>(qv) + chunk_off, avail);
+  // LIFT: the lifted query and key rows ([B, T, H, DK] bf16) that the state walks read
+  const int rowF = H * DK * 2;
+  const size_t fchunk_off = (static_cast<size_t>(b) * T + t0) * rowF;
+  const long long favail = LIFT ? static_cast<long long>(T - t0) * rowF : 0;
+  const rsrc_t wq = make_rsrc_wu(LIFT ? static_cast<uint8_t*>(fq) + fchunk_off : nullptr, favail);
+  const rsrc_t wk = make_rsrc_wu(LIFT ? static_cast<uint8_t*>(fk) + fchunk_off : nullptr, favail);
   // gates first: their loads then overlap the key loads
   const int t = t0 + lane;
   float la = 0.f, et = 0.f;
@@ -168,8 +175,14 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
         const uint32_t qw = *reinterpret_cast<const uint32_t*>(uqr + 4 * kb);
         const u32x4 kbv = *reinterpret_cast<const u32x4*>(ukr + 16 * (gq & 1));
         const u32x4 qbv = *reinterpret_cast<const u32x4*>(uqr + 16 * (gq & 1));
-        kf[x] = __builtin_bit_cast(bf16x8, lift8(lift_pick(kw, odd), kbv));
-        qf[x] = __builtin_bit_cast(bf16x8, lift8(lift_pick(qw, odd), qbv));
+        const u32x4 kl = lift8(lift_pick(kw, odd), kbv), ql = lift8(lift_pick(qw, odd), qbv);
+        kf[x] = __builtin_bit_cast(bf16x8, kl);
+        qf[x] = __builtin_bit_cast(bf16x8, ql);
+        // every feature of the chunk passes through exactly one lane here: store it for the walks
+        // (rows past T fall outside the buffer range and are dropped)
+        const int foff = (16 * x + ln) * rowF + (h * DK + 32 * kb + 8 * gq) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(kl, wk, foff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(ql, wq, foff, 0, 0);
       } else if constexpr (MODE == MODE_BF16) {
         const int off8 = (16 * x + ln) * rowK + h * DK * SZ + (32 * kb + 8 * gq) * SZ;  // as in the preload
         kf[x] = __builtin_bit_cast(bf16x8, bload16(rk, off8));
@@ -389,35 +402,36 @@ __global__ __launch_bounds__(64) void prep_kernel(const void* __restrict__ qv, c
 
 template <int MODE, int DK, bool LIFT = false>
 static hipError_t launch_prep_t(const Dims& d, const void* q, const void* k, const float* la, const float* eta,
-                                float eps, int direct, uint8_t* rec, hipStream_t stream) {
+                                float eps, int direct, uint8_t* rec, void* fq, void* fk, hipStream_t stream) {
   const int nchunks = d.B * d.H * d.nc;
   if (!LIFT && !d.full_rec && state_dma_supported(MODE, DK))
     return launch_kernel(prep_kernel<MODE, DK, true, false>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
-                         direct, rec, d.T, d.H, d.nc, nchunks);
+                         direct, rec, d.T, d.H, d.nc, nchunks, fq, fk);
   return launch_kernel(prep_kernel<MODE, DK, false, LIFT>, dim3(nchunks), dim3(64), stream, q, k, la, eta, eps,
-                       direct, rec, d.T, d.H, d.nc, nchunks);
+                       direct, rec, d.T, d.H, d.nc, nchunks, fq, fk);
 }
 
 int record_bytes(int mode, int dk) { return state_dma_supported(mode, dk) ? CREC_BYTES : REC_BYTES; }
 int full_record_bytes() { return REC_BYTES; }
 
 hipError_t launch_prep(int mode, const Dims& d, const void* q, const void* k, const float* log_alpha,
-                       const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream) {
+                       const float* eta, float eps, int direct, uint8_t* rec, hipStream_t stream, void* fq,
+                       void* fk) {
   if (d.lift) {
-    if (mode == MODE_BF16 && d.dk == LIFT_DK)
-      return launch_prep_t<MODE_BF16, LIFT_DK, true>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
+    if (mode == MODE_BF16 && d.dk == LIFT_DK && fq && fk)
+      return launch_prep_t<MODE_BF16, LIFT_DK, true>(d, q, k, log_alpha, eta, eps, direct, rec, fq, fk, stream);
     return hipErrorInvalidValue;
   }
   if (mode == MODE_BF16) {
     switch (d.dk) {
-      case 64: return launch_prep_t<MODE_BF16, 64>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
-      case 128: return launch_prep_t<MODE_BF16, 128>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
-      case 256: return launch_prep_t<MODE_BF16, 256>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
+      case 64: return launch_prep_t<MODE_BF16, 64>(d, q, k, log_alpha, eta, eps, direct, rec, nullptr, nullptr, stream);
+      case 128: return launch_prep_t<MODE_BF16, 128>(d, q, k, log_alpha, eta, eps, direct, rec, nullptr, nullptr, stream);
+      case 256: return launch_prep_t<MODE_BF16, 256>(d, q, k, log_alpha, eta, eps, direct, rec, nullptr, nullptr, stream);
     }
   } else {
     switch (d.dk) {
-      case 64: return launch_prep_t<MODE_F32, 64>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
-      case 128: return launch_prep_t<MODE_F32, 128>(d, q, k, log_alpha, eta, eps, direct, rec, stream);
+      case 64: return launch_prep_t<MODE_F32, 64>(d, q, k, log_alpha, eta, eps, direct, rec, nullptr, nullptr, stream);
+      case 128: return launch_prep_t<MODE_F32, 128>(d, q, k, log_alpha, eta, eps, direct, rec, nullptr, nullptr, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -23,12 +23,6 @@
 // pass composes the maps of all segments into each segment's true start state, and
 // a final walk per segment produces the outputs.
 //
-// With LIFT = true the queries and keys arrive as the 16-wide vectors u of the KATA page's
-// rank-one PSD feature (section 2.2) and the kernel forms the 256 features u_a u_b (rounded
-// to bf16) in the prefetch registers, in the middle of the previous chunk's products, before
-// they move into LDS. Everything after LDS is the dk = 256 kernel unchanged; the rows read
-// from memory shrink 16-fold.
-//
 // The log-linear prefill (Log-Linear page, "Mathematical formalization") uses three more
 // options: a segment stride (seg_mul, seg_add: every other half-block of a scale), walks
 // with no values (v null: value loads go through a zero-size buffer range and read as
@@ -94,11 +88,11 @@ __device__ __forceinline__ uint32_t pack_halves(uint32_t lo, uint32_t hi, int ha
   return __builtin_amdgcn_perm(hi, lo, half ? 0x07060302u : 0x05040100u);
 }
 
-template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT, bool ACC>
+template <int MODE, int DK, bool WITH_OUT, bool AUG, bool ACC>
 // The bf16 map walk at dk = 256 (61 KB of LDS without a transposed copy of K) is held to the
 // registers of two workgroups per CU: two map chains per SIMD, a few values spilled outside the
 // chunk loop (map walk 389 -> 353 us on the PSD workload).
-__global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIFT) ? 2 : 1) void state_kernel(StateArgs a) {
+__global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG) ? 2 : 1) void state_kernel(StateArgs a) {
   using TR = Tr<MODE>;
   using in_t = typename TR::in_t;
   using DF = typename TR::DF;
@@ -116,17 +110,13 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
   constexpr int VPT = (VBLK + NT - 1) / NT;
   constexpr int TPT = CHUNK * 16 / NT;         // T' (and P) vectors per thread
   static_assert(!AUG || DK % NCOLS == 0, "identity/value columns must not share a workgroup");
-  static_assert(!LIFT || (MODE == MODE_BF16 && DK == LIFT_DK), "the lift makes 256 bf16 features");
-  constexpr int KIN = LIFT ? LIFT_P : DK;      // elements of a query/key row in memory
   static_assert((KCB & (KCB - 1)) == 0 && (VCB & (VCB - 1)) == 0, "shape");
 
   __shared__ __align__(16) in_t sK[CHUNK * LDK];
   // K^T for the state update. bf16 features read K's rows transposed instead (ds_read_b64_tr_b16):
   // the map walk at dk = 256 then fits two workgroups per CU and the walks do fewer vector
-  // transposes (host-lifted PSD step 5% faster, 9% with the two workgroups). The fused lift's map
-  // walk keeps the transposed copy: without it that walk measured 7% slower (9% at two workgroups
-  // per CU); its walk with outputs reads K^T transposed like the others.
-  constexpr bool KT_TR = MODE == MODE_BF16 && (!LIFT || WITH_OUT);
+  // transposes (PSD step 5% faster, 9% with the two workgroups).
+  constexpr bool KT_TR = MODE == MODE_BF16;
   __shared__ __align__(16) in_t sKt[KT_TR ? VEC : DK * LDT];
   __shared__ __align__(16) in_t sQ[WITH_OUT ? CHUNK * LDK : VEC];
   __shared__ __align__(16) in_t sVt[NCOLS * LDT];
@@ -167,7 +157,7 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
   const int c_end = min(a.nc, c_begin + seg_chunks);
 
   // byte strides between consecutive tokens, and this batch's first rows
-  const int rowK = H * KIN * SZ, rowV = H * DV * SZ, rowO = H * DV * 4;
+  const int rowK = H * DK * SZ, rowV = H * DV * SZ, rowO = H * DV * 4;
   const uint8_t* kb_ = static_cast<const uint8_t*>(a.k) + static_cast<size_t>(b) * T * rowK;
   const uint8_t* qb_ = static_cast<const uint8_t*>(a.q) + static_cast<size_t>(b) * T * rowK;
   const uint8_t* vb_ = static_cast<const uint8_t*>(a.v) + static_cast<size_t>(b) * T * rowV;
@@ -186,10 +176,6 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
   // ---- prefetch registers: the next chunk's inputs, loaded while the current one is computed ----
   u32x4 pk[KPT][4];
   u32x4 pq[WITH_OUT ? KPT : 1][4];
-  // lifted rows: pk/pq hold u_{b0} .. u_{b0+7} and pka/pqa the word holding u_a of the same
-  // row, for the features 16a + b0 .. 16a + b0 + 7 of the thread's 16-byte block
-  uint32_t pka[LIFT ? KPT : 1][4];
-  uint32_t pqa[LIFT && WITH_OUT ? KPT : 1][4];
   u32x4 pv[VPT][4];
   u32x4 pt[TPT];
   u32x4 pp[WITH_OUT ? TPT : 1];
@@ -207,27 +193,11 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
       const int blk = tid + NT * u;
       int rb, cb;
       kblk(blk, rb, cb);
-      if constexpr (LIFT) {
-        // features 8cb .. 8cb + 7 = 16a + b0 + 0..7 with a = cb >> 1, b0 = 8 (cb & 1)
-        const int base = 4 * rb * rowK + h * LIFT_P * 2;
-        const int offb = blk < KBLK ? base + 16 * (cb & 1) : BUF_OOB;
-        const int offa = blk < KBLK ? base + 4 * (cb >> 2) : BUF_OOB;
+      const int off = blk < KBLK ? 4 * rb * rowK + h * DK * SZ + 16 * cb : BUF_OOB;
 #pragma unroll
-        for (int u4 = 0; u4 < 4; ++u4) {
-          pk[u][u4] = bload16(rk, offb + u4 * rowK);
-          pka[u][u4] = bload4(rk, offa + u4 * rowK);
-          if constexpr (WITH_OUT) {
-            pq[u][u4] = bload16(rq, offb + u4 * rowK);
-            pqa[u][u4] = bload4(rq, offa + u4 * rowK);
-          }
-        }
-      } else {
-        const int off = blk < KBLK ? 4 * rb * rowK + h * DK * SZ + 16 * cb : BUF_OOB;
-#pragma unroll
-        for (int u4 = 0; u4 < 4; ++u4) {
-          pk[u][u4] = bload16(rk, off + u4 * rowK);
-          if constexpr (WITH_OUT) pq[u][u4] = bload16(rq, off + u4 * rowK);
-        }
+      for (int u4 = 0; u4 < 4; ++u4) {
+        pk[u][u4] = bload16(rk, off + u4 * rowK);
+        if constexpr (WITH_OUT) pq[u][u4] = bload16(rq, off + u4 * rowK);
       }
     }
 #pragma unroll
@@ -298,25 +268,6 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
     if (tid < 3 * CHUNK / 4) reinterpret_cast<u32x4*>(sTail)[tid] = ptail;
   };
 
-  // Lifted rows: turns the prefetched u pieces into their eight features per block, in place.
-  // Called in the middle of a chunk's products, where its vector work fills the waits on the
-  // MFMA chain instead of sitting between the end-of-chunk barriers.
-  auto lift_regs = [&]() __attribute__((always_inline)) {
-    if constexpr (LIFT) {
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        int rb, cb;
-        kblk(tid + NT * u, rb, cb);
-        const bool odd = (cb >> 1) & 1;  // u_a is the high half of its word
-#pragma unroll
-        for (int u4 = 0; u4 < 4; ++u4) {
-          pk[u][u4] = lift8(lift_pick(pka[u][u4], odd), pk[u][u4]);
-          if constexpr (WITH_OUT) pq[u][u4] = lift8(lift_pick(pqa[u][u4], odd), pq[u][u4]);
-        }
-      }
-    }
-  };
-
   // start state
   f32x4 S[DK / 16];
 #pragma unroll
@@ -336,7 +287,6 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
 
   if (c_begin < c_end) {
     issue_loads(c_begin);
-    lift_regs();
     store_lds();
   }
   __syncthreads();
@@ -406,8 +356,6 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG && !LIF
       for (int kb = 0; kb < 2; ++kb)
         if (kb == 0 || mt >= 2) U[mt] = TR::mma_dd(U[mt], TR::ldd(sTP, 16 * mt, 32 * kb, lane), Rb[kb]);
     }
-    // the next chunk's prefetched u pieces (after the last chunk they are stale and never stored)
-    lift_regs();
 
     // ---- O = diag(e^g) Q S + P U ----
     if constexpr (WITH_OUT) {
@@ -549,17 +497,13 @@ __global__ void copy_or_zero_kernel(const float* __restrict__ src, float* __rest
 // ---------------------------------------------------------------------------
 constexpr int NCOLS_STATE = 64;  // state columns per workgroup (4 waves x 16)
 
-template <int MODE, int DK, bool WITH_OUT, bool AUG, bool LIFT = false, bool ACC = false>
+template <int MODE, int DK, bool WITH_OUT, bool AUG, bool ACC = false>
 static hipError_t launch_state_t(int nwg, const StateArgs& a, hipStream_t stream) {
-  return launch_kernel(state_kernel<MODE, DK, WITH_OUT, AUG, LIFT, ACC>, dim3(nwg), dim3(256), stream, a);
+  return launch_kernel(state_kernel<MODE, DK, WITH_OUT, AUG, ACC>, dim3(nwg), dim3(256), stream, a);
 }
 
 template <bool WITH_OUT, bool AUG>
-static hipError_t dispatch_state(int mode, int dk, bool lift, int nwg, const StateArgs& a, hipStream_t stream) {
-  if (lift) {
-    if (mode == MODE_BF16 && dk == LIFT_DK) return launch_state_t<MODE_BF16, LIFT_DK, WITH_OUT, AUG, true>(nwg, a, stream);
-    return hipErrorInvalidValue;
-  }
+static hipError_t dispatch_state(int mode, int dk, int nwg, const StateArgs& a, hipStream_t stream) {
   if (mode == MODE_BF16) {
     switch (dk) {
       case 64: return launch_state_t<MODE_BF16, 64, WITH_OUT, AUG>(nwg, a, stream);
@@ -579,22 +523,22 @@ hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* 
                             const uint8_t* rec, const float* init, float* out, float* fin,
                             hipStream_t stream) {
   const int ncg = d.dv / NCOLS_STATE;
-  if (!d.lift && state_dma_supported(mode, d.dk))
+  if (state_dma_supported(mode, d.dk))
     return launch_state_dma(true, false, d.dk, ncg * d.B * d.H, q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out,
                             fin, d.dv, 1, 0, ncg, 1, stream);
   StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, d.nc, init, 1, out, fin, d.dv, 1, 0, ncg, 1};
-  return dispatch_state<true, false>(mode, d.dk, d.lift, ncg * d.B * d.H, a, stream);
+  return dispatch_state<true, false>(mode, d.dk, ncg * d.B * d.H, a, stream);
 }
 
 hipError_t launch_scan_maps(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
                             int seg_chunks, int segs, float* maps, hipStream_t stream) {
   const int ncg = (d.dk + d.dv) / NCOLS_STATE;
-  if (!d.lift && state_dma_supported(mode, d.dk))
+  if (state_dma_supported(mode, d.dk))
     return launch_state_dma(false, true, d.dk, ncg * (segs - 1) * d.B * d.H, nullptr, k, v, rec, d.T, d.H, d.dv, d.nc,
                             seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv, segs - 1, 0, ncg, segs - 1, stream);
   StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv,
               segs - 1, 0, ncg, segs - 1};
-  return dispatch_state<false, true>(mode, d.dk, d.lift, ncg * (segs - 1) * d.B * d.H, a, stream);
+  return dispatch_state<false, true>(mode, d.dk, ncg * (segs - 1) * d.B * d.H, a, stream);
 }
 
 hipError_t launch_scan_starts(const Dims& d, const float* maps, const float* init, int segs, float* starts,
@@ -612,11 +556,11 @@ hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void*
                              const uint8_t* rec, int seg_chunks, int segs, const float* starts, float* out,
                              float* fin, hipStream_t stream) {
   const int ncg = d.dv / NCOLS_STATE;
-  if (!d.lift && state_dma_supported(mode, d.dk))
+  if (state_dma_supported(mode, d.dk))
     return launch_state_dma(true, false, d.dk, ncg * segs * d.B * d.H, q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks,
                             starts, segs, out, fin, d.dv, 1, 1, ncg, segs, stream);
   StateArgs a{q, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, starts, segs, out, fin, d.dv, 1, 1, ncg, segs};
-  return dispatch_state<true, false>(mode, d.dk, d.lift, ncg * segs * d.B * d.H, a, stream);
+  return dispatch_state<true, false>(mode, d.dk, ncg * segs * d.B * d.H, a, stream);
 }
 
 // Log-linear prefill, one scale: half-blocks of `half` chunks, left ones (even) and right ones (odd).
@@ -624,14 +568,14 @@ template <bool WITH_OUT, bool ACC>
 static hipError_t dispatch_scale(int mode, int dk, int nwg, const StateArgs& a, hipStream_t stream) {
   if (mode == MODE_BF16) {
     switch (dk) {
-      case 64: return launch_state_t<MODE_BF16, 64, WITH_OUT, false, false, ACC>(nwg, a, stream);
-      case 128: return launch_state_t<MODE_BF16, 128, WITH_OUT, false, false, ACC>(nwg, a, stream);
-      case 256: return launch_state_t<MODE_BF16, 256, WITH_OUT, false, false, ACC>(nwg, a, stream);
+      case 64: return launch_state_t<MODE_BF16, 64, WITH_OUT, false, ACC>(nwg, a, stream);
+      case 128: return launch_state_t<MODE_BF16, 128, WITH_OUT, false, ACC>(nwg, a, stream);
+      case 256: return launch_state_t<MODE_BF16, 256, WITH_OUT, false, ACC>(nwg, a, stream);
     }
   } else {
     switch (dk) {
-      case 64: return launch_state_t<MODE_F32, 64, WITH_OUT, false, false, ACC>(nwg, a, stream);
-      case 128: return launch_state_t<MODE_F32, 128, WITH_OUT, false, false, ACC>(nwg, a, stream);
+      case 64: return launch_state_t<MODE_F32, 64, WITH_OUT, false, ACC>(nwg, a, stream);
+      case 128: return launch_state_t<MODE_F32, 128, WITH_OUT, false, ACC>(nwg, a, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -169,9 +169,11 @@ kla_status kla_chunk_fwd_noalloc(kla_dtype dtype, kla_beta_mode beta_mode, const
  * the queries and the keys instead of the p*p features; the kernels form
  *     q_t[a*p + b] = bf16(uq_t[a] * uq_t[b]),   k_t[a*p + b] = bf16(uk_t[a] * uk_t[b])
  * (the exact product of two bf16 values rounded to the nearest bf16, ties to
- * even) as they load each chunk, and compute exactly what kla_chunk_fwd_ex does
- * on those features with dk = p*p. Query and key rows read from memory shrink
- * from p*p to p elements.
+ * even), and compute exactly what kla_chunk_fwd_ex does on those features with
+ * dk = p*p. Chunk prep forms its fragments from u as it loads them and writes
+ * the lifted query and key rows, which the state walks read, into the
+ * workspace; it grows by 2 * B*T*H*p*p*2 bytes over kla_chunk_fwd_ex's (taken
+ * and released like it, stream-ordered on `stream`).
  *
  *   uq, uk      bf16 device arrays [B,T,H,p]; only p == 16 (dk = 256) is supported
  *   v, gates, eps, init_state, out, final_state, B, T, H, dv, chunk, path,
