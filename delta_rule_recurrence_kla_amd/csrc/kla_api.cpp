@@ -195,9 +195,12 @@ Plan make_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, kla_path pa
   kla_path chosen = path;
   int segs = 1;
   if (nc >= 2 && path != KLA_PATH_SEQUENTIAL) {
-    // cost in chunk steps: rounds of workgroups (one per CU) times chunks per walk
-    auto rounds = [cus](long long wgs) { return (wgs + cus - 1) / cus; };
-    const double seq_cost = static_cast<double>(rounds(seq_wgs)) * nc;
+    // cost in chunk steps: rounds of workgroups times chunks per walk. A walk with outputs runs one
+    // workgroup per CU; the bf16 map walks run two (the copy-wave map walk in 76 KB of LDS, the
+    // dk = 256 one held to the registers of two).
+    auto rounds = [cus](long long wgs, int per_cu) { return (wgs + per_cu * cus - 1) / (per_cu * cus); };
+    const int maps_per_cu = dtype == KLA_DTYPE_BF16 ? 2 : 1;
+    const double seq_cost = static_cast<double>(rounds(seq_wgs, 1)) * nc;
     double best = 1e300;
     int best_g = 1;
     const int gmax = std::min(nc, 256);
@@ -207,8 +210,9 @@ Plan make_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, kla_path pa
       if (G < 2) continue;
       const long long wg1 = bh * (G - 1) * ((dk + dv) / 64);
       const long long wg3 = bh * G * (dv / 64);
-      // a map walk skips the output products (about 0.6 of an output walk), plus the serial fold
-      const double cost = 0.6 * rounds(wg1) * L + rounds(wg3) * L + 0.25 * G;
+      // a map walk skips the output products (about 0.6 of an output walk); each step of the
+      // serial fold of the maps costs about two chunk steps (measured at dk = 128 and 256)
+      const double cost = 0.6 * rounds(wg1, maps_per_cu) * L + rounds(wg3, 1) * L + 2.0 * (G - 1);
       if (cost < best) {
         best = cost;
         best_g = G;
