@@ -208,7 +208,8 @@ Plan make_plan(kla_dtype dtype, int B, int T, int H, int dk, int dv, kla_path pa
       const int L = (nc + g - 1) / g;
       const int G = (nc + L - 1) / L;
       if (G < 2) continue;
-      const long long wg1 = bh * (G - 1) * ((dk + dv) / 64);
+      // (calls without an initial state: segment 0's identity columns are not walked)
+      const long long wg1 = bh * ((G - 1) * ((dk + dv) / 64) - dk / 64);
       const long long wg3 = bh * G * (dv / 64);
       // a map walk skips the output products (about 0.6 of an output walk); each step of the
       // serial fold of the maps costs about two chunk steps (measured at dk = 128 and 256)
@@ -326,7 +327,7 @@ hipError_t chunk_fwd_enqueue(const Plan& p, kla_dtype dtype, kla_beta_mode beta_
       });
     } else {
       e = timed("kla_scan_maps", stream, [&] {
-        return kla::launch_scan_maps(mode, d, k, v, rec, p.seg_chunks, p.segs, maps, stream);
+        return kla::launch_scan_maps(mode, d, k, v, rec, p.seg_chunks, p.segs, maps, init_state == nullptr, stream);
       });
       if (e == hipSuccess)
         e = timed("kla_scan_starts", stream, [&] { return kla::launch_scan_starts(d, maps, init_state, p.segs, starts, stream); });
@@ -682,7 +683,7 @@ kla_status kla_chunk_bwd(kla_dtype dtype, kla_beta_mode beta_mode, const void* q
     if (e == hipSuccess)
       e = timed("kla_prep", stream, [&] { return kla::launch_prep(mode, d, q, k, log_alpha, eta, eps, direct, crec, stream); });
     if (e == hipSuccess)
-      e = timed("kla_scan_maps", stream, [&] { return kla::launch_scan_maps(mode, d, k, v, crec, segc, segs, maps_f, stream); });
+      e = timed("kla_scan_maps", stream, [&] { return kla::launch_scan_maps(mode, d, k, v, crec, segc, segs, maps_f, init_state == nullptr, stream); });
     if (e == hipSuccess)
       e = timed("kla_scan_starts", stream, [&] { return kla::launch_scan_starts(d, maps_f, init_state, segs, starts, stream); });
     if (e == hipSuccess)

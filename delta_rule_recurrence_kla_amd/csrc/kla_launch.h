@@ -59,8 +59,10 @@ hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* 
 //  phase 1: affine map [M | N] of each of the first `segs - 1` segments of `seg_chunks` chunks
 //  phase 2: start state of every segment, sequentially over segments
 //  phase 3: state + output inside every segment from its start state
+// zero_start: the scan starts from a zero state (no init), so segment 0's M is not needed; the
+// map walk skips it and launch_scan_starts (given init = null) never reads it.
 hipError_t launch_scan_maps(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
-                            int seg_chunks, int segs, float* maps, hipStream_t stream);
+                            int seg_chunks, int segs, float* maps, bool zero_start, hipStream_t stream);
 hipError_t launch_scan_starts(const Dims& d, const float* maps, const float* init, int segs,
                               float* starts, hipStream_t stream);
 hipError_t launch_scan_apply(int mode, const Dims& d, const void* q, const void* k, const void* v,
@@ -77,7 +79,8 @@ int full_record_bytes();  // T' and P in full, for the kernels that read both
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
-                            int ncg, int nseg, hipStream_t stream, int seg_mul = 1, int seg_add = 0);
+                            int ncg, int nseg, hipStream_t stream, int seg_mul = 1, int seg_add = 0,
+                            int skip_ident0 = 0);
 // Log-linear prefill on compact records (bf16, dk in {64, 128}, DV a multiple of 64): the walk of
 // chunk scale s (level 7 + s of L) over its nright right half-blocks of 2^s chunks per head, each
 // from the state [B*H][nright][dk][DV] in init (written by scale s - 1; scale 0 starts every

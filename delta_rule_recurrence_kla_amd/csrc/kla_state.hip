@@ -66,6 +66,9 @@ struct StateArgs {
   int scale_half[kMaxScales] = {};
   int scale_nseg[kMaxScales] = {};
   long long scale_fin_off[kMaxScales] = {};
+  // Map walks of a scan from a zero start: segment 0's identity columns are not walked (the
+  // fold never reads M_0 then, since it multiplies a zero state), and their workgroups exit.
+  int skip_ident0 = 0;
 };
 
 // Workgroup id -> (column group, unit), unit = bh * nseg + seg. The column groups of one
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(256, (MODE == MODE_BF16 && DK == 256 && AUG) ? 2 : 
   const int col0 = cg * NCOLS;            // first (augmented) column of the workgroup
   const int col = col0 + 16 * w + ln;     // this lane's column
   const bool ident = AUG && col0 < DK;    // identity part of [M | N]
+  if (AUG && ident && seg == 0 && a.skip_ident0) return;  // uniform over the workgroup, before any barrier
   const int vcol0 = AUG ? col0 - DK : col0;
   const int vcol = vcol0 + 16 * w + ln;
   const int c_begin = (seg * a.seg_mul + a.seg_add) * seg_chunks;
@@ -473,12 +477,15 @@ __global__ __launch_bounds__(256) void scan_starts_kernel(const float* __restric
       for (int i = 0; i < 4; ++i) acc[i] = M[static_cast<size_t>(16 * mt + 4 * gq + i) * LDM + DK + c0 + ln];  // N
       const float* Mrow = M + static_cast<size_t>(16 * mt + ln) * LDM + 4 * gq;
       const float* Xrow = X + ln * XP + 4 * gq;
+      // from a zero start, X_1 = N_0: M_0 is never computed (the map walk skips it) or read
+      if (init || s > 0) {
 #pragma unroll 4
-      for (int kk = 0; kk < DK / 16; ++kk) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(Mrow + 16 * kk);
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(Xrow + 16 * kk);
+        for (int kk = 0; kk < DK / 16; ++kk) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(Mrow + 16 * kk);
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(Xrow + 16 * kk);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[q], b4[q], acc, 0, 0, 0);
+          for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[q], b4[q], acc, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[static_cast<size_t>(16 * mt + 4 * gq + i) * DV + c0 + ln] = acc[i];
@@ -531,13 +538,15 @@ hipError_t launch_state_seq(int mode, const Dims& d, const void* q, const void* 
 }
 
 hipError_t launch_scan_maps(int mode, const Dims& d, const void* k, const void* v, const uint8_t* rec,
-                            int seg_chunks, int segs, float* maps, hipStream_t stream) {
+                            int seg_chunks, int segs, float* maps, bool zero_start, hipStream_t stream) {
   const int ncg = (d.dk + d.dv) / NCOLS_STATE;
   if (state_dma_supported(mode, d.dk))
     return launch_state_dma(false, true, d.dk, ncg * (segs - 1) * d.B * d.H, nullptr, k, v, rec, d.T, d.H, d.dv, d.nc,
-                            seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv, segs - 1, 0, ncg, segs - 1, stream);
+                            seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv, segs - 1, 0, ncg, segs - 1, stream, 1, 0,
+                            zero_start ? 1 : 0);
   StateArgs a{nullptr, k, v, rec, d.T, d.H, d.dv, d.nc, seg_chunks, nullptr, 1, nullptr, maps, d.dk + d.dv,
               segs - 1, 0, ncg, segs - 1};
+  a.skip_ident0 = zero_start ? 1 : 0;
   return dispatch_state<false, true>(mode, d.dk, ncg * (segs - 1) * d.B * d.H, a, stream);
 }
 

@@ -73,6 +73,9 @@ struct StateDmaArgs {
   int lam_L;
   int lam_level;
   int wg_segs;
+  // Map walks of a scan from a zero start: the workgroups of segment 0's identity columns exit
+  // (the fold never reads M_0 then).
+  int skip_ident0;
 };
 
 namespace {
@@ -141,6 +144,7 @@ __global__ __launch_bounds__(MAP_THREADS) void state_map_kernel(StateDmaArgs a) 
   const int col0 = cg * NCOLS;
   const int col = col0 + 16 * w + ln;
   const bool ident = AUG && col0 < DK;  // identity columns (they carry M), else value columns (N)
+  if (AUG && ident && seg == 0 && a.skip_ident0) return;  // uniform over the workgroup, before any barrier
   const int vcol0 = AUG ? col0 - DK : col0;
   const int c_begin = (seg * a.seg_mul + a.seg_add) * seg_chunks;
   const int c_end = min(a.nc, c_begin + seg_chunks);
@@ -832,9 +836,9 @@ bool state_dma_supported(int mode, int dk) { return mode == MODE_BF16 && (dk == 
 hipError_t launch_state_dma(bool with_out, bool aug, int dk, int nwg, const void* q, const void* k, const void* v,
                             const uint8_t* rec, int T, int H, int DV, int nc, int seg_chunks, const float* init,
                             int init_segs, float* out, float* fin, int fin_ld, int fin_segs, int fin_last_only,
-                            int ncg, int nseg, hipStream_t stream, int seg_mul, int seg_add) {
+                            int ncg, int nseg, hipStream_t stream, int seg_mul, int seg_add, int skip_ident0) {
   const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, seg_chunks, init, init_segs, out, fin, fin_ld, fin_segs,
-                       fin_last_only, ncg, nseg, seg_mul, seg_add, nullptr, 0, 0, 1};
+                       fin_last_only, ncg, nseg, seg_mul, seg_add, nullptr, 0, 0, 1, skip_ident0};
   if (with_out && aug) return hipErrorInvalidValue;  // a walk with outputs carries the plain state
   if (dk == 64) {
     if (with_out) return launch_kernel(state_walk_kernel<64, WALK_PLAIN>, dim3(nwg), dim3(WALK_THREADS), stream, a);
@@ -862,7 +866,7 @@ hipError_t launch_loglinear_scale_dma(int dk, const void* q, const void* k, cons
   const int wg_segs = (nright + groups - 1) / groups;
   const int ngrp = (nright + wg_segs - 1) / wg_segs;
   const StateDmaArgs a{q, k, v, rec, T, H, DV, nc, 1 << s, init, nright, out, fin, DV, fin_segs, 0, ncg, nright,
-                       2, 1, lam, L, 7 + s, wg_segs};
+                       2, 1, lam, L, 7 + s, wg_segs, 0};
   const dim3 grid(units * ngrp), block(WALK_THREADS);
   if (dk == 64)
     return s == 0 ? launch_kernel(state_walk_kernel<64, WALK_LL_PAIRS>, grid, block, stream, a)
