@@ -178,6 +178,11 @@ def test_plan_paths():
     # long context with 16 heads under-fills the chip -> scan with several segments
     p, s, w = kla.plan(1, 131072, 16, 128, 128, num_cus=256)
     assert p == "scan" and 4 <= s <= 64
+    # the segment counts that measured fastest on 256 CUs (sweeps over 2..32 segments): 8 for the
+    # 131K-token shape; 4 for the PSD shape, whose map walk then fits one round at two
+    # workgroups per CU once segment 0's identity columns are skipped
+    assert kla.plan(1, 131072, 16, 128, 128, num_cus=256)[:2] == ("scan", 8)
+    assert kla.plan(4, 8192, 8, 256, 128, num_cus=256)[:2] == ("scan", 4)
     # explicit choices are honoured; segments are clamped so that none is empty
     assert kla.plan(1, 131072, 16, 128, 128, path="sequential", num_cus=256)[:2] == ("sequential", 1)
     p, s, _ = kla.plan(1, 64 * 10, 1, 64, 64, path="scan", segments=4, num_cus=256)
