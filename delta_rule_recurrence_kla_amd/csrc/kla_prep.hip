@@ -34,7 +34,8 @@
 // With LIFT = true, q and k arrive as the 16-wide vectors u of the KATA page's rank-one PSD
 // feature (section 2.2) and each key/query fragment is formed from them as it is loaded:
 // feature 16a + b is u_a u_b, rounded to bf16, so the products below see exactly the 256
-// features the unfused path would read.
+// features the unfused path would read. Each feature passes through one lane exactly once, and
+// that lane also stores it: prep writes the lifted query and key rows that the state walks read.
 //
 // Tokens past T in the last chunk enter as identity steps: k = q = 0, log_alpha = 0,
 // eta = 0, so their rows and columns of T' and P are zero.

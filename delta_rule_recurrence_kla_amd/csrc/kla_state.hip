@@ -21,7 +21,8 @@
 // S_end = M S_start + N. Running the walk on the augmented state [I | 0] with value
 // columns zero in the identity part yields [M | N] (AUG = true). A short sequential
 // pass composes the maps of all segments into each segment's true start state, and
-// a final walk per segment produces the outputs.
+// a final walk per segment produces the outputs. From a zero start the first segment's
+// start is known (X_1 = N_0), so its identity columns are not walked.
 //
 // The log-linear prefill (Log-Linear page, "Mathematical formalization") uses three more
 // options: a segment stride (seg_mul, seg_add: every other half-block of a scale), walks
