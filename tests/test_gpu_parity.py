@@ -323,6 +323,24 @@ def test_sequential_equals_scan():
         assert_close(S2, S1, 1e-3, f"scan({segs}) state")
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (256, 128), (64, 64)])
+def test_scan_zero_start_equals_explicit_zero_init(dk, dv):
+    """Without an initial state the scan does not form segment 0's M (its map walk skips the
+    identity columns and the fold skips the product). Passing an all-zero initial state takes
+    the full route (M_0 formed, M_0 times zero added), so both must agree bit for bit; the
+    no-init run must also match the oracle."""
+    wl = W.make_prefill("long_131k", seed=8, B=2, T=64 * 23 + 17, H=2, dk=dk, dv=dv)
+    log(f"case: zero-start scan dk={dk} dv={dv} T={wl.T}")
+    zero = torch.zeros((wl.B, wl.H, dk, dv), dtype=torch.float32, device="cuda")
+    for segs in (2, 4, 7):
+        o1, S1 = run_prefill(wl, path="scan", segments=segs)
+        o2, S2 = run_prefill(wl, path="scan", segments=segs, init=zero)
+        assert np.array_equal(o1, o2) and np.array_equal(S1, S2), f"segments={segs}"
+    o_ref, S_ref = oracle_prefill(wl)
+    assert_close(o1, o_ref, TOL["bf16"], "out")
+    assert_close(S1, S_ref, TOL["bf16"], "state")
+
+
 def test_causality_and_determinism():
     wl = W.make_prefill("lm_layer_4k", seed=7, B=1, T=500, H=2)
     q, k, v, la, eta, _ = upload_prefill(wl)
